@@ -1,0 +1,252 @@
+"""Oracle functions (float64 numpy).  Test infrastructure only; see the package docstring.
+
+Every array is float64.  Per-(batch, head) functions take token-major arrays:
+q, k [T, dk], v [T, dv], beta, alpha [T]; the math state S is [dv, dk].
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# Readings of the pages that no printed value can confirm (reported as parity unpinned).
+PARITY_UNPINNED = (
+    "router score pooling is log-MEAN-exp (HLA Overview) rather than log-sum-exp "
+    "(HLA Methodology paragraph 2); the two differ by log(n_rep)",
+    "representatives are the history chunk's raw keys (the learned window pooler needs "
+    "trained weights)",
+    "the decode-time gate query is the token's own q; the prefill gate query is the mean "
+    "of q over the query chunk",
+    "gates are per (batch, head)",
+)
+
+
+# --------------------------------------------------------------------------- O1
+def gdn_recurrent(q, k, v, beta, alpha, S0=None):
+    """Token-by-token gated delta rule.
+
+    For each token t:  S <- alpha_t * S (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+    then o_t = S q_t (the read sees token t's own write).  [HLA] Methodology paragraph 1:
+    decay and edit the old state, then add the key-value write.
+
+    Leading batch dimensions are allowed: q [..., T, dk], beta [..., T], S0 [..., dv, dk].
+    Returns (o [..., T, dv], S_final [..., dv, dk]).  q may be None (state only).
+    """
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    T, dk = k.shape[-2], k.shape[-1]
+    dv = v.shape[-1]
+    batch = k.shape[:-2]
+    S = np.zeros(batch + (dv, dk)) if S0 is None else np.array(S0, np.float64, copy=True)
+    o = None if q is None else np.zeros(batch + (T, dv))
+    for t in range(T):
+        kt = k[..., t, :]
+        vt = v[..., t, :]
+        bt = np.asarray(beta)[..., t][..., None, None]
+        at = np.asarray(alpha)[..., t][..., None, None]
+        Sk = np.einsum("...ij,...j->...i", S, kt)                  # S k_t  [dv]
+        S = at * (S - bt * Sk[..., :, None] * kt[..., None, :]) + bt * vt[..., :, None] * kt[..., None, :]
+        if q is not None:
+            o[..., t, :] = np.einsum("...ij,...j->...i", S, q[..., t, :])
+    return o, S
+
+
+# --------------------------------------------------------------------------- chunks
+def chunk_bounds(T, C):
+    """Chunks start at token 0 of the processed range; the last one may be partial."""
+    return [(s, min(s + C, T)) for s in range(0, T, C)]
+
+
+def chunk_transition(k, v, beta, alpha):
+    """Exact affine map of one chunk, built token by token (never through UT/WY).
+
+    [HLA] Methodology paragraph 1 and Key Contributions 2: because the per-token updates
+    are affine, a whole chunk is one affine map S -> S A + B.  A is the product of the
+    per-token linear parts alpha_t (I - beta_t k_t k_t^T) in token order; B is the state
+    the chunk produces from a zero start.  Returns (A [dk, dk], B [dv, dk]).
+    """
+    dk = k.shape[-1]
+    A = np.eye(dk)
+    for t in range(k.shape[0]):
+        kt = k[t]
+        A = alpha[t] * (A - beta[t] * np.outer(A @ kt, kt))
+    _, B = gdn_recurrent(None, k, v, beta, alpha)
+    return A, B
+
+
+def chunk_transitions(k, v, beta, alpha, C):
+    """(A [N, dk, dk], B [N, dv, dk]) for every chunk of one (batch, head) sequence."""
+    A, B = [], []
+    for s, e in chunk_bounds(k.shape[0], C):
+        a, b = chunk_transition(k[s:e], v[s:e], beta[s:e], alpha[s:e])
+        A.append(a)
+        B.append(b)
+    return np.stack(A), np.stack(B)
+
+
+# --------------------------------------------------------------------------- O3 router
+def log_mean_exp(s, axis=-1):
+    """log(mean(exp(s))) computed with the max shifted out."""
+    m = np.max(s, axis=axis, keepdims=True)
+    return np.squeeze(m, axis) + np.log(np.mean(np.exp(s - m), axis=axis))
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def n_eff(g):
+    """Order-2 effective number of accessed chunks, (sum g)^2 / sum g^2 ([HLA] Key
+    Contributions 3, Methodology paragraph 4: inverse sum of squares); 0 if all are 0."""
+    g = np.asarray(g, np.float64)
+    den = np.sum(g * g, axis=-1)
+    num = np.sum(g, axis=-1) ** 2
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), 0.0)
+
+
+def router_gates(q, reps, n_rep, C, tau, gates_in=None):
+    """Query-chunk x history-chunk gates for one (batch, head) sequence.
+
+    q [T, dk]; reps [(N-1) * n_rep or more, dk]: chunk j's representatives are rows
+    [j n_rep, (j + 1) n_rep).  [HLA] Overview (log-mean-exp pooled routing gates) and
+    Methodology paragraphs 2-4:
+      * query of chunk i = mean of q over the chunk's tokens;
+      * l_ij = log-mean-exp over chunk j's representatives r of (qbar_i . r) / sqrt(dk);
+      * g_ij = sigmoid(l_ij) for j < i, independent (no normalisation over j);
+      * the current chunk has weight 1, future chunks are masked (weight 0);
+      * a history gate below tau is set to zero without renormalisation.  The skip is
+        decided in float32 (the kernel's precision): keep iff float32(g) >= float32(tau).
+    ``gates_in`` [N, N] replaces the computed history gates (entries j < i).
+    Returns dict(gates [N,N], mask [N,N] bool (history only), ghat [N,N], active (list of
+    ascending index arrays), count [N], n_eff [N]).
+    """
+    T, dk = q.shape
+    bounds = chunk_bounds(T, C)
+    N = len(bounds)
+    g = np.zeros((N, N))
+    if gates_in is None:
+        qbar = np.stack([q[s:e].mean(axis=0) for s, e in bounds])
+        for i in range(N):
+            for j in range(i):
+                r = reps[j * n_rep:(j + 1) * n_rep]
+                g[i, j] = _sigmoid(log_mean_exp(r @ qbar[i] / math.sqrt(dk)))
+    else:
+        g = np.tril(np.asarray(gates_in, np.float64), -1)
+    np.fill_diagonal(g, 1.0)
+    hist = np.tril(np.ones((N, N), bool), -1)
+    mask = hist & (g.astype(np.float32) >= np.float32(tau))
+    ghat = np.where(mask, g, 0.0)
+    active = [np.nonzero(mask[i])[0] for i in range(N)]
+    return dict(gates=g, mask=mask, ghat=ghat, active=active,
+                count=mask.sum(axis=1), n_eff=n_eff(ghat))
+
+
+# --------------------------------------------------------------------------- O4 / O5
+def routed_states(A, B, ghat, mask, S0=None):
+    """Initial state of every query chunk i, composed chronologically over history chunks.
+
+    [HLA] Methodology paragraph 3: the gate interpolates the chunk's full transition with
+    the identity, S -> g (S A_j + B_j) + (1 - g) S, so g = 1 applies the chunk and g = 0
+    leaves the state untouched; chunks compose in time order ([HLA] Methodology paragraph
+    1: affine maps compose).  Masked chunks are skipped.  Returns [N, dv, dk].
+    """
+    N, dv, dk = B.shape
+    out = np.zeros((N, dv, dk))
+    for i in range(N):
+        S = np.zeros((dv, dk)) if S0 is None else np.array(S0, np.float64)
+        for j in range(i):
+            if mask[i, j]:
+                S = ghat[i, j] * (S @ A[j] + B[j]) + (1.0 - ghat[i, j]) * S
+        out[i] = S
+    return out
+
+
+def routed_states_by_replay(k, v, beta, alpha, C, ghat, mask, S0=None):
+    """Same as ``routed_states`` but applies chunk j by replaying its tokens (no A, B)."""
+    bounds = chunk_bounds(k.shape[0], C)
+    N, dv, dk = len(bounds), v.shape[1], k.shape[1]
+    out = np.zeros((N, dv, dk))
+    for i in range(N):
+        S = np.zeros((dv, dk)) if S0 is None else np.array(S0, np.float64)
+        for j in range(i):
+            if mask[i, j]:
+                s, e = bounds[j]
+                _, Sj = gdn_recurrent(None, k[s:e], v[s:e], beta[s:e], alpha[s:e], S0=S)
+                S = ghat[i, j] * Sj + (1.0 - ghat[i, j]) * S
+        out[i] = S
+    return out
+
+
+def routed_outputs(q, k, v, beta, alpha, C, S_routed):
+    """Outputs of every chunk i: the plain recurrence over chunk i's own tokens started
+    from its routed state (the current chunk has weight one).  Returns o [T, dv]."""
+    o = np.zeros((q.shape[0], v.shape[1]))
+    for i, (s, e) in enumerate(chunk_bounds(q.shape[0], C)):
+        o[s:e], _ = gdn_recurrent(q[s:e], k[s:e], v[s:e], beta[s:e], alpha[s:e], S0=S_routed[i])
+    return o
+
+
+def hla_prefill(q, k, v, beta, alpha, C, tau, reps=None, n_rep=None, gates_in=None, S0=None):
+    """Whole routed prefill for one (batch, head): transitions, gates, states, outputs."""
+    if reps is None:
+        reps, n_rep = k, C
+    A, B = chunk_transitions(k, v, beta, alpha, C)
+    r = router_gates(q, reps, n_rep, C, tau, gates_in=gates_in)
+    S = routed_states(A, B, r["ghat"], r["mask"], S0=S0)
+    o = routed_outputs(q, k, v, beta, alpha, C, S)
+    return dict(A=A, B=B, S_routed=S, o=o, **r)
+
+
+# --------------------------------------------------------------------------- O6 decode
+def decode_step(q, k, v, beta, alpha, B_cur, A_cur, cache_A, cache_B, cache_reps, tau,
+                gates_in=None, commit=False):
+    """One single-token decode step for one (sequence, head).
+
+    [HLA] Key Contributions 3 (dynamic autoregressive decoding) with Methodology
+    paragraphs 2-4.  The live chunk is the affine map (A_cur, B_cur) of the tokens since
+    the last cached chunk; this token extends it.  Gates over the cached chunks use the
+    token's own q.  The routed state S~ composes the gated cached chunks from zero; the
+    output reads the live chunk applied after it: o = (S~ A_cur + B_cur) q.
+    ``A_cur is None`` selects native GDN: B_cur is the full-prefix state, o = B_cur q.
+    cache_A [Nc, dk, dk], cache_B [Nc, dv, dk], cache_reps [Nc, n_rep, dk].
+    Returns dict(o, B_cur, A_cur, gates, ghat, cache_A, cache_B) after the step (and the
+    optional commit, which appends the live chunk and resets it to (I, 0)).
+    """
+    dk = k.shape[0]
+    lin = alpha * (np.eye(dk) - beta * np.outer(k, k))
+    B_cur = B_cur @ lin + beta * np.outer(v, k)
+    if A_cur is None:
+        return dict(o=B_cur @ q, B_cur=B_cur, A_cur=None)
+    A_cur = A_cur @ lin
+    Nc = cache_A.shape[0]
+    g = np.zeros(Nc)
+    for j in range(Nc):
+        if gates_in is None:
+            g[j] = _sigmoid(log_mean_exp(cache_reps[j] @ q / math.sqrt(dk)))
+        else:
+            g[j] = gates_in[j]
+    keep = g.astype(np.float32) >= np.float32(tau)
+    ghat = np.where(keep, g, 0.0)
+    S = np.zeros_like(B_cur)
+    for j in range(Nc):
+        if keep[j]:
+            S = ghat[j] * (S @ cache_A[j] + cache_B[j]) + (1.0 - ghat[j]) * S
+    o = (S @ A_cur + B_cur) @ q
+    out = dict(o=o, gates=g, ghat=ghat, S_routed=S)
+    if commit:
+        cache_A = np.concatenate([cache_A, A_cur[None]])
+        cache_B = np.concatenate([cache_B, B_cur[None]])
+        A_cur, B_cur = np.eye(dk), np.zeros_like(B_cur)
+    out.update(B_cur=B_cur, A_cur=A_cur, cache_A=cache_A, cache_B=cache_B)
+    return out
+
+
+# --------------------------------------------------------------------------- O7
+def tail_replay(k, v, beta, alpha, L):
+    """[TR]: rebuild the recurrent state of a T-token prefix by replaying only its last L
+    tokens from a zero state.  Returns (S_replay, S_full), both [..., dv, dk]."""
+    T = k.shape[-2]
+    _, S_rep = gdn_recurrent(None, k[..., T - L:, :], v[..., T - L:, :],
+                             beta[..., T - L:], alpha[..., T - L:])
+    _, S_full = gdn_recurrent(None, k, v, beta, alpha)
+    return S_rep, S_full
