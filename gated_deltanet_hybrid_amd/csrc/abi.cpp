@@ -1,0 +1,206 @@
+// C ABI of libhla.so: argument validation, workspace layout and dispatch.
+// Every check runs before anything is enqueued, so an invalid call returns its status
+// with the stream untouched (and without touching the GPU at all).
+#include "../../include/hla.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int64_t kMaxGrid = 0x7fffffffLL;
+constexpr int32_t kMaxCacheSlots = 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t n_chunks(const hla_dims_t* d) { return (d->T + d->C - 1) / d->C; }
+
+int64_t dtype_bytes(int32_t dt) { return dt == HLA_BF16 ? 2 : 4; }
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+hla_status_t check_dims(const hla_dims_t* d) {
+  if (!d) return HLA_ERR_NULL_ARG;
+  if (d->dtype != HLA_F32 && d->dtype != HLA_BF16) return HLA_ERR_BAD_DTYPE;
+  if (d->B < 1 || d->H < 1 || d->T < 1 || d->ld_T < d->T) return HLA_ERR_BAD_SHAPE;
+  if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128)) return HLA_ERR_BAD_SHAPE;
+  if (d->C != 64) return HLA_ERR_BAD_SHAPE;
+  // element counts must stay far from int64 overflow, grids within 2^31 blocks
+  const double elems = (double)d->B * (double)d->ld_T * (double)d->H * 128.0;
+  if (elems > 4.0e18) return HLA_ERR_BAD_SHAPE;
+  const int64_t N = n_chunks(d);
+  if ((double)d->B * (double)d->H * (double)N > (double)kMaxGrid) return HLA_ERR_BAD_SHAPE;
+  if ((double)d->B * d->H * (double)N * (double)N > 4.0e18) return HLA_ERR_BAD_SHAPE;
+  return HLA_OK;
+}
+
+template <class... P>
+bool all_aligned(P... p) {
+  return (aligned16(p) && ...);
+}
+
+// Workspace of the native prefill: transitions (dtype) then, when outputs are wanted, the
+// float32 state at the start of every chunk.
+struct PrefillWs {
+  int64_t at_off, bc_off, st_off, total_ab, total;
+};
+PrefillWs prefill_ws(const hla_dims_t* d) {
+  const int64_t N = n_chunks(d), BHN = d->B * d->H * N, e = dtype_bytes(d->dtype);
+  PrefillWs w;
+  w.at_off = 0;
+  w.bc_off = round_up(BHN * d->dk * d->dk * e, 256);
+  w.total_ab = w.bc_off + round_up(BHN * d->dk * d->dv * e, 256);
+  w.st_off = w.total_ab;
+  w.total = w.st_off + round_up(BHN * d->dk * d->dv * 4, 256);
+  return w;
+}
+
+int64_t route_ws(const hla_dims_t* d) { return round_up(d->B * d->H * n_chunks(d) * d->dk * 4, 256); }
+
+hla_status_t hip_status(hipError_t e) { return e == hipSuccess ? HLA_OK : HLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t hla_abi_version(void) { return HLA_ABI_VERSION; }
+
+const char* hla_status_string(int32_t s) {
+  switch (s) {
+    case HLA_OK: return "ok";
+    case HLA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case HLA_ERR_BAD_SHAPE: return "a size is out of range or inconsistent";
+    case HLA_ERR_BAD_DTYPE: return "dtype must be HLA_F32 or HLA_BF16";
+    case HLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case HLA_ERR_HIP: return "a HIP kernel launch failed";
+    case HLA_ERR_UNSUPPORTED: return "unsupported combination of arguments";
+    case HLA_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+    case HLA_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep, size_t* out) {
+  if (!out) return HLA_ERR_NULL_ARG;
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  (void)n_rep;
+  switch (fn) {
+    case HLA_FN_CHUNK_TRANSITIONS: *out = 0; return HLA_OK;
+    case HLA_FN_GDN_PREFILL: *out = (size_t)prefill_ws(d).total; return HLA_OK;
+    case HLA_FN_ROUTE_MIX: *out = (size_t)route_ws(d); return HLA_OK;
+    default: return HLA_ERR_UNSUPPORTED;
+  }
+}
+
+hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const void* v, const float* beta,
+                                   const float* alpha, void* At, void* Bc, hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (!k || !v || !beta || !alpha || !At || !Bc) return HLA_ERR_NULL_ARG;
+  if (!all_aligned(k, v, beta, alpha, At, Bc)) return HLA_ERR_ALIGN;
+  hla::ChunkArgs a{};
+  a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
+  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)n_chunks(d);
+  a.At = At; a.Bc = Bc;
+  return hip_status(hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream));
+}
+
+hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                             const float* beta, const float* alpha, const float* S0, const float* chunk_init,
+                             float* o, float* S_final, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (!k || !v || !beta || !alpha) return HLA_ERR_NULL_ARG;
+  if (!o && !S_final) return HLA_ERR_NULL_ARG;
+  if (o && !q) return HLA_ERR_NULL_ARG;
+  if (!all_aligned(q, k, v, beta, alpha, S0, chunk_init, o, S_final, ws)) return HLA_ERR_ALIGN;
+  const int32_t N = (int32_t)n_chunks(d);
+  hla::ChunkArgs a{};
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
+  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = N;
+  if (chunk_init) {
+    // routed: every chunk starts from its own given state
+    if (S0 || S_final) return HLA_ERR_UNSUPPORTED;
+    a.chunk_init = chunk_init;
+    a.o = o;
+    return hip_status(hla::launch_chunk(a, d->dtype, d->dk, d->dv, false, true, stream));
+  }
+  const PrefillWs w = prefill_ws(d);
+  const int64_t need = o ? w.total : w.total_ab;
+  if (!ws || (int64_t)ws_bytes < need) return HLA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  a.At = base + w.at_off;
+  a.Bc = base + w.bc_off;
+  hipError_t e = hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  hla::ScanArgs s{};
+  s.At = a.At; s.Bc = a.Bc; s.S0 = S0;
+  s.states = o ? reinterpret_cast<float*>(base + w.st_off) : nullptr;
+  s.S_final = S_final;
+  s.B = d->B; s.H = d->H; s.N = N;
+  e = hla::launch_scan(s, d->dtype, d->dk, d->dv, stream);
+  if (e != hipSuccess || !o) return hip_status(e);
+  hla::ChunkArgs b = a;
+  b.At = nullptr; b.Bc = nullptr;
+  b.chunk_init = s.states;
+  b.o = o;
+  return hip_status(hla::launch_chunk(b, d->dtype, d->dk, d->dv, false, true, stream));
+}
+
+hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps, int32_t n_rep, int64_t ld_R,
+                           const void* At, const void* Bc, const float* S0, const float* gates_in, float tau,
+                           float* gates, uint8_t* mask, int32_t* active_idx, int32_t* active_cnt, float* n_eff,
+                           float* S_routed, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  const int64_t N = n_chunks(d);
+  if (!At || !Bc || !gates || !mask || !active_idx || !active_cnt || !S_routed) return HLA_ERR_NULL_ARG;
+  const bool computed = !gates_in && N > 1;
+  if (computed && (!q || !reps)) return HLA_ERR_NULL_ARG;
+  if (computed && (n_rep < 1 || ld_R < (N - 1) * (int64_t)n_rep)) return HLA_ERR_BAD_SHAPE;
+  if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
+  if (!all_aligned(q, reps, At, Bc, S0, gates_in, gates, S_routed, ws)) return HLA_ERR_ALIGN;
+  if (computed && (!ws || (int64_t)ws_bytes < route_ws(d))) return HLA_ERR_WORKSPACE;
+  hla::RouteArgs a{};
+  a.q = q; a.reps = reps; a.n_rep = n_rep; a.ld_R = ld_R; a.At = At; a.Bc = Bc; a.S0 = S0;
+  a.gates_in = gates_in; a.tau = tau; a.gates = gates; a.mask = mask; a.active_idx = active_idx;
+  a.active_cnt = active_cnt; a.n_eff = n_eff; a.S_routed = S_routed; a.qbar = static_cast<float*>(ws);
+  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)N;
+  return hip_status(hla::launch_route(a, d->dtype, d->dk, d->dv, stream));
+}
+
+hla_status_t hla_gdn_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q,
+                            const void* k, const void* v, const float* beta, const float* alpha, float* S_cur,
+                            float* At_cur, void* At_cache, void* Bc_cache, const void* reps_cache, int32_t n_rep,
+                            int32_t* n_cache, int32_t n_cap, const float* gates_in, float tau, float* o,
+                            float* gates_out, int32_t commit, hipStream_t stream) {
+  if (dtype != HLA_F32 && dtype != HLA_BF16) return HLA_ERR_BAD_DTYPE;
+  if (Bs < 1 || H < 1 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return HLA_ERR_BAD_SHAPE;
+  if ((double)Bs * (double)H > (double)kMaxGrid) return HLA_ERR_BAD_SHAPE;
+  if (!q || !k || !v || !beta || !alpha || !S_cur || !o) return HLA_ERR_NULL_ARG;
+  if (commit != 0 && commit != 1) return HLA_ERR_BAD_SHAPE;
+  if (!At_cur) {
+    if (commit) return HLA_ERR_UNSUPPORTED;
+  } else {
+    if (!n_cache || !At_cache || !Bc_cache) return HLA_ERR_NULL_ARG;
+    if (n_cap < 0 || n_cap > kMaxCacheSlots) return HLA_ERR_BAD_SHAPE;
+    if (!gates_in && n_cap > 0) {
+      if (!reps_cache) return HLA_ERR_NULL_ARG;
+      if (n_rep < 1) return HLA_ERR_BAD_SHAPE;
+    }
+    if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
+  }
+  if (!all_aligned(q, k, v, beta, alpha, S_cur, At_cur, At_cache, Bc_cache, reps_cache, gates_in, o, gates_out))
+    return HLA_ERR_ALIGN;
+  hla::DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.alpha = alpha; a.S_cur = S_cur; a.At_cur = At_cur;
+  a.At_cache = At_cache; a.Bc_cache = Bc_cache; a.reps_cache = reps_cache; a.n_rep = n_rep; a.n_cache = n_cache;
+  a.n_cap = n_cap; a.gates_in = gates_in; a.tau = tau; a.o = o; a.gates_out = gates_out; a.commit = commit;
+  a.Bs = Bs; a.H = H;
+  return hip_status(hla::launch_decode(a, dtype, dk, dv, stream));
+}
+
+}  // extern "C"

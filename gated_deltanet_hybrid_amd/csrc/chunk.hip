@@ -1,0 +1,397 @@
+// Per-chunk kernel: the UT form of one chunk of the gated delta rule.
+//
+// [HLA] Methodology paragraph 1 / Key Contributions 2: a chunk is summarised exactly by the
+// affine map M -> At M + Bc (state orientation M = S^T [dk, dv]).  Within a chunk of n <= 64
+// tokens (local t, padded to 64 with beta = 0, alpha = 1, which is the identity map):
+//   g_t = sum_{s<=t} log alpha_s,  gamma_t = exp(g_t),  Gamma_ts = exp(g_t - g_s) (s <= t)
+//   L   = strictly_lower(diag(beta) (K K^T) o Gamma),  X = (I + L)^-1
+//   W   = X diag(beta gamma) K,  U = X diag(beta) V,  D_s = exp(g_63 - g_s)
+//   At  = gamma_63 I - K^T diag(D) W,   Bc = K^T diag(D) U
+//   P   = (Q K^T) o Gamma (lower, with diagonal),  Qp = diag(gamma) Q - P W,  O_intra = P U
+//   O   = O_intra + Qp M0 for a chunk that starts from state M0.
+// Every decay is the exp of a difference of per-chunk log-decays (never exp(-g)), so nothing
+// overflows when the product of alphas underflows.
+//
+// One 256/512-thread workgroup per (b, h, chunk).  Products run on MFMA (bf16 inputs with
+// fp32 accumulation, or fp32 MFMA for fp32 inputs).  The inverse is blocked (16 x 16
+// diagonal blocks by substitution, then block rows) in fp32; its bf16 use is split into
+// hi + lo parts so W and U keep ~16 mantissa bits.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace hla {
+
+template <class T, int DK, int DV, int NW, bool WANT_AB, bool WANT_O>
+__global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
+  using MM = Mma<T>;
+  constexpr int C = kChunk;
+  constexpr int E = sizeof(T);
+  constexpr int PAD = 16 / E;
+  constexpr int PK = DK + PAD;  // pitch of [t][dk] rows (elements)
+  constexpr int PT = C + PAD;   // pitch of [d][t] rows
+  constexpr int PX = C + 4;     // fp32 pitch of L and X
+  constexpr int NCT = (DK + DV) / 32;
+  constexpr int NT = NW * 64;
+  constexpr int R1a = (WANT_O ? 2 : 1) * C * PK * E;
+  constexpr int R1b = 2 * C * PX * 4;
+  constexpr int R1 = R1a > R1b ? R1a : R1b;
+  constexpr int R2 = (DK + DV) * PT * E;
+  constexpr int R3 = WANT_O ? C * PT * E : 16;
+  static_assert(!WANT_O || DV * PK * E <= R2, "S~^T staging must fit in R2");
+  static_assert(!WANT_O || C * PK * E <= R1, "Qp staging must fit in R1");
+  static_assert(NCT <= 2 * NW, "at most two column tiles per wave");
+
+  __shared__ __attribute__((aligned(16))) char sm1[R1];
+  __shared__ __attribute__((aligned(16))) char sm2[R2];
+  __shared__ __attribute__((aligned(16))) char sm3[R3];
+  __shared__ float s_beta[C], s_bg[C], s_g[C], s_gam[C], s_D[C];
+
+  T* Kp = reinterpret_cast<T*>(sm1);
+  T* Qp = Kp + C * PK;
+  float* Lb = reinterpret_cast<float*>(sm1);
+  float* Xb = Lb + C * PX;
+  T* KT = reinterpret_cast<T*>(sm2);
+  T* VT = KT + DK * PT;
+  T* Pb = reinterpret_cast<T*>(sm3);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, c32 = lane & 31;
+  const int64_t id = blockIdx.x;
+  const int c = (int)(id % a.N);
+  const int64_t bh = id / a.N;
+  const int64_t h = bh % a.H, b = bh / a.H;
+  const int64_t t0 = (int64_t)c * C;
+  const int n = (int)((a.T - t0) < C ? (a.T - t0) : C);
+  const int64_t row0 = (b * a.ld_T + t0) * a.H + h;  // token-row of (b, t0, h)
+  const T* kg = reinterpret_cast<const T*>(a.k) + row0 * DK;
+  const T* vg = reinterpret_cast<const T*>(a.v) + row0 * DV;
+  const T* qg = WANT_O ? reinterpret_cast<const T*>(a.q) + row0 * DK : nullptr;
+  const int64_t kstride = a.H * DK, vstride = a.H * DV;
+
+  // ---- 1. stage K (row-major and transposed), V (transposed), Q (row-major)
+  {
+    constexpr int VK = DK / PAD;
+    for (int i = tid; i < C * VK; i += NT) {
+      const int t = i / VK, cc = i % VK;
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (t < n) val = *reinterpret_cast<const uint4*>(kg + t * kstride + cc * PAD);
+      *reinterpret_cast<uint4*>(Kp + t * PK + cc * PAD) = val;
+      const T* ev = reinterpret_cast<const T*>(&val);
+#pragma unroll
+      for (int e = 0; e < PAD; ++e) KT[(cc * PAD + e) * PT + t] = ev[e];
+      if constexpr (WANT_O) {
+        uint4 qv = make_uint4(0u, 0u, 0u, 0u);
+        if (t < n) qv = *reinterpret_cast<const uint4*>(qg + t * kstride + cc * PAD);
+        *reinterpret_cast<uint4*>(Qp + t * PK + cc * PAD) = qv;
+      }
+    }
+    constexpr int VV = DV / PAD;
+    for (int i = tid; i < C * VV; i += NT) {
+      const int t = i / VV, cc = i % VV;
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (t < n) val = *reinterpret_cast<const uint4*>(vg + t * vstride + cc * PAD);
+      const T* ev = reinterpret_cast<const T*>(&val);
+#pragma unroll
+      for (int e = 0; e < PAD; ++e) VT[(cc * PAD + e) * PT + t] = ev[e];
+    }
+    if (tid < C) {
+      float bt = 0.f, la = 0.f;
+      if (tid < n) {
+        const int64_t idx = row0 + (int64_t)tid * a.H;
+        bt = a.beta[idx];
+        la = logf(a.alpha[idx]);
+      }
+      float x = la;  // inclusive prefix sum over the 64 lanes of wave 0
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      const float gn = __shfl(x, 63, 64);
+      const float gam = expf(x);
+      s_beta[tid] = bt;
+      s_bg[tid] = bt * gam;
+      s_g[tid] = x;
+      s_gam[tid] = gam;
+      s_D[tid] = expf(gn - x);
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. K K^T and Q K^T tiles (64 x 64 each, 32 x 32 tiles)
+  f32x16 kk = zero16(), qk = zero16();
+  int kk_tile = -1, qk_tile = -1;
+  if (NW == 8) {
+    if (w < 4) kk_tile = w; else qk_tile = WANT_O ? w - 4 : -1;
+  } else {
+    kk_tile = w;
+    qk_tile = WANT_O ? w : -1;
+  }
+  if (kk_tile >= 0 && (kk_tile & 1) <= (kk_tile >> 1)) {
+    const T* ar = Kp + ((kk_tile >> 1) * 32 + c32) * PK;
+    const T* br = Kp + ((kk_tile & 1) * 32 + c32) * PK;
+#pragma unroll
+    for (int ks = 0; ks < DK / MM::KS; ++ks) kk = MM::mma(MM::load_plain(ar, ks, hh), MM::load_plain(br, ks, hh), kk);
+  }
+  if constexpr (WANT_O) {
+    if (qk_tile >= 0 && (qk_tile & 1) <= (qk_tile >> 1)) {
+      const T* ar = Qp + ((qk_tile >> 1) * 32 + c32) * PK;
+      const T* br = Kp + ((qk_tile & 1) * 32 + c32) * PK;
+#pragma unroll
+      for (int ks = 0; ks < DK / MM::KS; ++ks) qk = MM::mma(MM::load_plain(ar, ks, hh), MM::load_plain(br, ks, hh), qk);
+    }
+  }
+  __syncthreads();  // Kp and Qp are dead: R1 now holds L and X
+  if (kk_tile >= 0) {
+    const int tm = kk_tile >> 1, tn = kk_tile & 1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int t = tm * 32 + acc_row(e, hh), s = tn * 32 + c32;
+      Lb[t * PX + s] = (s < t) ? s_beta[t] * expf(s_g[t] - s_g[s]) * kk[e] : 0.f;
+    }
+  }
+  if constexpr (WANT_O) {
+    if (qk_tile >= 0) {
+      const int tm = qk_tile >> 1, tn = qk_tile & 1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = tm * 32 + acc_row(e, hh), s = tn * 32 + c32;
+        Pb[t * PT + s] = from_f<T>((s <= t) ? expf(s_g[t] - s_g[s]) * qk[e] : 0.f);
+      }
+    }
+  }
+  for (int i = tid; i < C * PX; i += NT) Xb[i] = 0.f;
+  __syncthreads();
+
+  // ---- 3. X = (I + L)^-1, blocked by 16
+  if (tid < 64) {
+    const int bi = tid >> 4, cc = tid & 15, base = bi * 16;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+      for (int q2 = 0; q2 < r; ++q2) s -= Lb[(base + r) * PX + base + q2] * x[q2];
+      x[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Xb[(base + r) * PX + base + cc] = x[r];
+  }
+  __syncthreads();
+  for (int ib = 1; ib < 4; ++ib) {
+    // Y_{ib,jb} = sum_{kb=jb}^{ib-1} L_{ib,kb} X_{kb,jb}, written into block (ib, jb) of X
+    for (int e = tid; e < ib * 256; e += NT) {
+      const int jb = e >> 8, r = (e >> 4) & 15, cc = e & 15;
+      float s = 0.f;
+      for (int kb = jb; kb < ib; ++kb)
+#pragma unroll
+        for (int q2 = 0; q2 < 16; ++q2) s += Lb[(ib * 16 + r) * PX + kb * 16 + q2] * Xb[(kb * 16 + q2) * PX + jb * 16 + cc];
+      Xb[(ib * 16 + r) * PX + jb * 16 + cc] = s;
+    }
+    __syncthreads();
+    // X_{ib,jb} = -X_{ib,ib} Y_{ib,jb}
+    float y[3] = {0.f, 0.f, 0.f};
+    for (int e = tid, m = 0; e < ib * 256; e += NT, ++m) {
+      const int jb = e >> 8, r = (e >> 4) & 15, cc = e & 15;
+      float s = 0.f;
+#pragma unroll
+      for (int q2 = 0; q2 < 16; ++q2) s -= Xb[(ib * 16 + r) * PX + ib * 16 + q2] * Xb[(ib * 16 + q2) * PX + jb * 16 + cc];
+      y[m] = s;
+    }
+    __syncthreads();
+    for (int e = tid, m = 0; e < ib * 256; e += NT, ++m) {
+      const int jb = e >> 8, r = (e >> 4) & 15, cc = e & 15;
+      Xb[(ib * 16 + r) * PX + jb * 16 + cc] = y[m];
+    }
+    __syncthreads();
+  }
+
+  // ---- 4. [W | U] = X diag(beta gamma | beta) [K | V]; wave w owns column tiles w, w + NW
+  f32x16 wu[2][2];
+  int my_ct[2];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    const int ct = w + NW * sl;
+    my_ct[sl] = ct < NCT ? ct : -1;
+    wu[sl][0] = zero16();
+    wu[sl][1] = zero16();
+    if (ct >= NCT) continue;
+    const bool isw = ct * 32 < DK;
+    const int col0 = isw ? ct * 32 : ct * 32 - DK;
+    const T* brow = (isw ? KT : VT) + (col0 + c32) * PT;
+    const float* scale = isw ? s_bg : s_beta;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      f32x16 acc = zero16();
+      const float* xrow = Xb + (tt * 32 + c32) * PX;
+#pragma unroll
+      for (int ks = 0; ks < C / MM::KS; ++ks) {
+        const auto bf = MM::load_plain(brow, ks, hh);
+        if constexpr (sizeof(T) == 2) {
+          bf16x8 ahi, alo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int s = ks * 16 + hh * 8 + e;
+            const float x = xrow[s] * scale[s];
+            const bf16 hv = (bf16)x;
+            ahi[e] = hv;
+            alo[e] = (bf16)(x - (float)hv);
+          }
+          acc = MM::mma(ahi, bf, acc);
+          acc = MM::mma(alo, bf, acc);
+        } else {
+          const int s = ks * 2 + hh;
+          acc = MM::mma(xrow[s] * scale[s], bf, acc);
+        }
+      }
+      wu[sl][tt] = acc;
+    }
+  }
+
+  // ---- 5. transitions: At = gamma_63 I - K^T D W,  Bc = K^T D U
+  if constexpr (WANT_AB) {
+    const float gam_n = s_gam[C - 1];
+    const int64_t cidx = (b * a.H + h) * a.N + c;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int ct = my_ct[sl];
+      if (ct < 0) continue;
+      const bool isw = ct * 32 < DK;
+      const int col0 = isw ? ct * 32 : ct * 32 - DK;
+      typename MM::Frag bfr[C / MM::KS];
+#pragma unroll
+      for (int ks = 0; ks < C / MM::KS; ++ks) {
+        const int tt = (MM::KS == 16) ? (ks >> 1) : (ks >> 4);
+        if constexpr (sizeof(T) == 2) {
+          bf16x8 f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int ai = (ks & 1) * 8 + e;
+            f[e] = (bf16)(wu[sl][tt][ai] * s_D[tt * 32 + acc_row(ai, hh)]);
+          }
+          bfr[ks] = f;
+        } else {
+          const int ai = ks & 15;
+          bfr[ks] = wu[sl][tt][ai] * s_D[tt * 32 + acc_row(ai, hh)];
+        }
+      }
+      T* out = isw ? reinterpret_cast<T*>(a.At) + cidx * DK * DK : reinterpret_cast<T*>(a.Bc) + cidx * DK * DV;
+      const int ld = isw ? DK : DV;
+#pragma unroll
+      for (int rt = 0; rt < DK / 32; ++rt) {
+        f32x16 acc = zero16();
+        const T* arow = KT + (rt * 32 + c32) * PT;
+#pragma unroll
+        for (int ks = 0; ks < C / MM::KS; ++ks) acc = MM::mma(MM::load_clayout(arow, ks, hh), bfr[ks], acc);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = rt * 32 + acc_row(e, hh), col = col0 + c32;
+          const float val = isw ? ((row == col ? gam_n : 0.f) - acc[e]) : acc[e];
+          out[row * ld + col] = from_f<T>(val);
+        }
+      }
+    }
+  }
+
+  // ---- 6. outputs: Qp = diag(gamma) Q - P W, O_intra = P U, O = O_intra + Qp M0
+  if constexpr (WANT_O) {
+    f32x16 res[2][2];
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int ct = my_ct[sl];
+      res[sl][0] = zero16();
+      res[sl][1] = zero16();
+      if (ct < 0) continue;
+      typename MM::Frag bfr[C / MM::KS];
+#pragma unroll
+      for (int ks = 0; ks < C / MM::KS; ++ks) {
+        const int tt = (MM::KS == 16) ? (ks >> 1) : (ks >> 4);
+        bfr[ks] = MM::from_acc(wu[sl][tt], ks, 1.f);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x16 acc = zero16();
+        const T* arow = Pb + (tt * 32 + c32) * PT;
+#pragma unroll
+        for (int ks = 0; ks < C / MM::KS; ++ks) acc = MM::mma(MM::load_clayout(arow, ks, hh), bfr[ks], acc);
+        res[sl][tt] = acc;
+      }
+    }
+    __syncthreads();  // every wave is past its reads of X, KT, VT and P
+    T* Qb = reinterpret_cast<T*>(sm1);   // [C][PK]
+    T* STb = reinterpret_cast<T*>(sm2);  // [DV][PK]: S~ transposed
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int ct = my_ct[sl];
+      if (ct < 0 || ct * 32 >= DK) continue;
+      const int col0 = ct * 32;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int t = tt * 32 + acc_row(e, hh);
+          const float qv = t < n ? to_f<T>(qg[t * kstride + col0 + c32]) : 0.f;
+          Qb[t * PK + col0 + c32] = from_f<T>(s_gam[t] * qv - res[sl][tt][e]);
+        }
+    }
+    const float* S0 = a.chunk_init + ((b * a.H + h) * a.N + c) * (int64_t)DK * DV;
+    for (int i = tid; i < DK * DV / 4; i += NT) {
+      const int dk = i / (DV / 4), dv = (i % (DV / 4)) * 4;
+      const float4 val = *reinterpret_cast<const float4*>(S0 + dk * DV + dv);
+      STb[(dv + 0) * PK + dk] = from_f<T>(val.x);
+      STb[(dv + 1) * PK + dk] = from_f<T>(val.y);
+      STb[(dv + 2) * PK + dk] = from_f<T>(val.z);
+      STb[(dv + 3) * PK + dk] = from_f<T>(val.w);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int ct = my_ct[sl];
+      if (ct < 0 || ct * 32 < DK) continue;
+      const int col0 = ct * 32 - DK;
+      const T* brow = STb + (col0 + c32) * PK;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x16 acc = res[sl][tt];
+        const T* arow = Qb + (tt * 32 + c32) * PK;
+#pragma unroll
+        for (int ks = 0; ks < DK / MM::KS; ++ks) acc = MM::mma(MM::load_plain(arow, ks, hh), MM::load_plain(brow, ks, hh), acc);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int t = tt * 32 + acc_row(e, hh);
+          if (t < n) a.o[((b * a.T + t0 + t) * a.H + h) * DV + col0 + c32] = acc[e];
+        }
+      }
+    }
+  }
+}
+
+template <class T, int DK, int DV, bool WANT_AB, bool WANT_O>
+static hipError_t launch_chunk_t(const ChunkArgs& a, int64_t nblocks, hipStream_t s) {
+  constexpr int NCT = (DK + DV) / 32;
+  constexpr int NW = NCT >= 8 ? 8 : 4;
+  hipLaunchKernelGGL((chunk_kernel<T, DK, DV, NW, WANT_AB, WANT_O>), dim3((unsigned)nblocks), dim3(NW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class T, bool WANT_AB, bool WANT_O>
+static hipError_t launch_chunk_d(const ChunkArgs& a, int dk, int dv, int64_t nb, hipStream_t s) {
+  if (dk == 64 && dv == 64) return launch_chunk_t<T, 64, 64, WANT_AB, WANT_O>(a, nb, s);
+  if (dk == 64 && dv == 128) return launch_chunk_t<T, 64, 128, WANT_AB, WANT_O>(a, nb, s);
+  if (dk == 128 && dv == 64) return launch_chunk_t<T, 128, 64, WANT_AB, WANT_O>(a, nb, s);
+  return launch_chunk_t<T, 128, 128, WANT_AB, WANT_O>(a, nb, s);
+}
+
+hipError_t launch_chunk(const ChunkArgs& a, int dtype, int dk, int dv, bool want_ab, bool want_o, hipStream_t s) {
+  const int64_t nb = a.B * a.H * (int64_t)a.N;
+  if (nb == 0) return hipSuccess;
+  if (dtype == 1) {
+    if (want_ab && !want_o) return launch_chunk_d<bf16, true, false>(a, dk, dv, nb, s);
+    if (!want_ab && want_o) return launch_chunk_d<bf16, false, true>(a, dk, dv, nb, s);
+    return hipErrorInvalidValue;
+  }
+  if (want_ab && !want_o) return launch_chunk_d<float, true, false>(a, dk, dv, nb, s);
+  if (!want_ab && want_o) return launch_chunk_d<float, false, true>(a, dk, dv, nb, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hla

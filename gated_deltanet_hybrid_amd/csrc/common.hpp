@@ -1,0 +1,149 @@
+// Device helpers shared by the gfx950 kernels: MFMA traits, fragment loaders that match
+// the 32x32 accumulator layout, bf16 packing and wave reductions.
+//
+// 32x32 MFMA lane layout (64-wide wavefront, lane l, half h = l / 32, c = l % 32):
+//   accumulator (16 floats)   : acc[a] is element (row (a/4)*8 + h*4 + a%4, col c)
+//   A operand (rows x K)      : row c; bf16 32x32x16 gives 8 k-slots h*8 + e,
+//                               f32 32x32x2 gives 1 k-slot h
+//   B operand (K x cols)      : col c; same k-slots as A.
+// A contraction only needs the two operands to agree on which k each slot holds.  Two
+// slot->k maps are used:
+//   plain   : bf16 slot s of k-step ks is k = ks*16 + s;  f32 slot h is k = ks*2 + h.
+//   clayout : the k order in which an accumulator tile already sits in a lane, so the
+//             result of one product feeds the next as its B operand without leaving the
+//             lane.  bf16 k-step ks, slot h*8 + e is k = ks*16 + (e/4)*8 + h*4 + e%4, and
+//             the B fragment is acc[8*(ks%2) .. 8*(ks%2)+7] of the tile holding rows
+//             32*(ks/2) ...;  f32 k-step ks, slot h is k = (ks/16)*32 + ((ks%16)/4)*8 +
+//             h*4 + ks%4 and the B fragment is acc[ks%16].
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hla {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kChunk = 64;  // tokens per chunk
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Row of accumulator element a for lane half h.
+__device__ __forceinline__ int acc_row(int a, int h) { return (a >> 2) * 8 + h * 4 + (a & 3); }
+
+template <class T> struct Mma;
+
+template <> struct Mma<bf16> {
+  static constexpr int KS = 16;
+  using Frag = bf16x8;
+  __device__ __forceinline__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // plain k order: 8 contiguous elements
+  __device__ __forceinline__ static Frag load_plain(const bf16* row, int ks, int h) {
+    return *reinterpret_cast<const bf16x8*>(row + ks * 16 + h * 8);
+  }
+  // clayout k order: two runs of 4
+  __device__ __forceinline__ static Frag load_clayout(const bf16* row, int ks, int h) {
+    bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + ks * 16 + h * 4);
+    bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + ks * 16 + 8 + h * 4);
+    Frag f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f[e] = lo[e]; f[e + 4] = hi[e]; }
+    return f;
+  }
+  // B fragment for k-step ks from an accumulator tile that holds rows 32*(ks/2)..
+  __device__ __forceinline__ static Frag from_acc(const f32x16& acc, int ks, float scale) {
+    Frag f;
+    const int b = (ks & 1) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)(acc[b + e] * scale);
+    return f;
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int KS = 2;
+  using Frag = float;
+  __device__ __forceinline__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static Frag load_plain(const float* row, int ks, int h) { return row[ks * 2 + h]; }
+  __device__ __forceinline__ static int clayout_k(int ks, int h) {
+    const int kl = ks & 15;
+    return (ks >> 4) * 32 + (kl >> 2) * 8 + h * 4 + (kl & 3);
+  }
+  __device__ __forceinline__ static Frag load_clayout(const float* row, int ks, int h) {
+    return row[clayout_k(ks, h)];
+  }
+  __device__ __forceinline__ static Frag from_acc(const f32x16& acc, int ks, float scale) {
+    return acc[ks & 15] * scale;
+  }
+};
+
+// k index of plain slot (ks, h, e) -- used to build elementwise-scaled A fragments.
+template <class T> __device__ __forceinline__ int plain_k(int ks, int h, int e);
+template <> __device__ __forceinline__ int plain_k<bf16>(int ks, int h, int e) { return ks * 16 + h * 8 + e; }
+template <> __device__ __forceinline__ int plain_k<float>(int ks, int h, int) { return ks * 2 + h; }
+
+// k index of clayout slot (ks, h, e).
+template <class T> __device__ __forceinline__ int clayout_k(int ks, int h, int e);
+template <> __device__ __forceinline__ int clayout_k<bf16>(int ks, int h, int e) {
+  return ks * 16 + (e >> 2) * 8 + h * 4 + (e & 3);
+}
+template <> __device__ __forceinline__ int clayout_k<float>(int ks, int h, int) { return Mma<float>::clayout_k(ks, h); }
+
+// Number of elements a fragment holds per lane.
+template <class T> struct FragLen;
+template <> struct FragLen<bf16> { static constexpr int n = 8; };
+template <> struct FragLen<float> { static constexpr int n = 1; };
+
+template <class T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
+template <class T> __device__ __forceinline__ T from_f(float x) { return (T)x; }
+
+// Diagonal B fragment: value g where the slot's k (plain order) equals the lane's column.
+template <class T> __device__ __forceinline__ typename Mma<T>::Frag diag_frag(int ks, int lane, float g);
+template <> __device__ __forceinline__ bf16x8 diag_frag<bf16>(int ks, int lane, float g) {
+  bf16x8 f;
+  const int col = lane & 31, h = lane >> 5;
+  const bf16 gb = (bf16)g, z = (bf16)0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (ks * 16 + h * 8 + e == col) ? gb : z;
+  return f;
+}
+template <> __device__ __forceinline__ float diag_frag<float>(int ks, int lane, float g) {
+  const int col = lane & 31, h = lane >> 5;
+  return (ks * 2 + h == col) ? g : 0.f;
+}
+
+// Sum over the 64 lanes of a wavefront (fixed order: deterministic).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+__device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// 16-byte global -> LDS copy of `bytes` (multiple of 16) by the whole block.
+__device__ __forceinline__ void block_copy16(void* lds, const void* g, int bytes, int tid, int nthreads) {
+  const uint4* src = reinterpret_cast<const uint4*>(g);
+  uint4* dst = reinterpret_cast<uint4*>(lds);
+  for (int i = tid; i < bytes / 16; i += nthreads) dst[i] = src[i];
+}
+
+}  // namespace hla

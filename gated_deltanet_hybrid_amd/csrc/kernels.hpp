@@ -1,0 +1,84 @@
+// Internal launchers of libhla.so (host side).  Arguments are validated by abi.cpp before
+// any of these is called; every launcher only enqueues work on the given stream.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hla {
+
+struct ChunkArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* alpha;
+  int64_t B, T, H, ld_T;
+  int32_t N;
+  void* At;                // out [B,H,N,dk,dk] (dtype) when transitions are wanted
+  void* Bc;                // out [B,H,N,dk,dv]
+  const float* chunk_init; // [B,H,N,dk,dv] start state of every chunk (outputs wanted)
+  float* o;                // out [B,T,H,dv]
+};
+
+// Either the transitions (want_ab) or the outputs from chunk_init (want_o).
+hipError_t launch_chunk(const ChunkArgs& a, int dtype, int dk, int dv, bool want_ab, bool want_o,
+                        hipStream_t s);
+
+struct ScanArgs {
+  const void* At;     // [B,H,N,dk,dk]
+  const void* Bc;     // [B,H,N,dk,dv]
+  const float* S0;    // [B,H,dk,dv] or null
+  float* states;      // out [B,H,N,dk,dv]: state at the start of every chunk, or null
+  float* S_final;     // out [B,H,dk,dv] or null
+  int64_t B, H;
+  int32_t N;
+};
+// Sequential chunk scan M_{c+1} = At_c M_c + Bc_c.
+hipError_t launch_scan(const ScanArgs& a, int dtype, int dk, int dv, hipStream_t s);
+
+struct RouteArgs {
+  const void* q;        // [B,ld_T,H,dk]
+  const void* reps;     // [B,ld_R,H,dk]
+  int32_t n_rep;
+  int64_t ld_R;
+  const void* At;       // [B,H,N,dk,dk]
+  const void* Bc;       // [B,H,N,dk,dv]
+  const float* S0;      // [B,H,dk,dv] or null
+  const float* gates_in;// [B,H,N,N] or null
+  float tau;
+  float* gates;         // [B,H,N,N]
+  uint8_t* mask;        // [B,H,N,N]
+  int32_t* active_idx;  // [B,H,N,N]
+  int32_t* active_cnt;  // [B,H,N]
+  float* n_eff;         // [B,H,N] or null
+  float* S_routed;      // [B,H,N,dk,dv]
+  float* qbar;          // workspace [B,H,N,dk] float32
+  int64_t B, T, H, ld_T;
+  int32_t N;
+};
+hipError_t launch_route(const RouteArgs& a, int dtype, int dk, int dv, hipStream_t s);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* alpha;
+  float* S_cur;
+  float* At_cur;
+  void* At_cache;
+  void* Bc_cache;
+  const void* reps_cache;
+  int32_t n_rep;
+  int32_t* n_cache;
+  int32_t n_cap;
+  const float* gates_in;
+  float tau;
+  float* o;
+  float* gates_out;
+  int32_t commit;
+  int64_t Bs, H;
+};
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int dk, int dv, hipStream_t s);
+
+}  // namespace hla

@@ -1,0 +1,269 @@
+"""Thin Python binding of libhla.so (ctypes).
+
+Argument marshalling only: every function checks tensor shapes, dtypes and strides,
+then calls the C entry point of the same name with raw device pointers and torch's
+current stream.  All arithmetic runs in the HIP kernels; there is no fallback.  Loading
+fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhla.so")
+_lib = None
+
+HLA_F32, HLA_BF16 = 0, 1
+FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX = 0, 1, 2
+CHUNK = 64
+MAX_CACHE_SLOTS = 1024
+
+
+class HlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {library().hla_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64), ("ld_T", ctypes.c_int64),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("C", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "hla_abi_version": (ctypes.c_int32, []),
+    "hla_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
+    "hla_workspace_bytes": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(Dims), ctypes.c_int32,
+                                             ctypes.POINTER(ctypes.c_size_t)]),
+    "hla_chunk_transitions": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P]),
+    "hla_gdn_prefill": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_size_t, _P]),
+    "hla_route_mix": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
+                                       _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "hla_gdn_decode": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
+                                        ctypes.c_int32, _P, ctypes.c_float, _P, _P, ctypes.c_int32, _P]),
+}
+
+
+def library(path: str | None = None) -> ctypes.CDLL:
+    """Load libhla.so (once).  Raises if it is missing: there is no fallback path."""
+    global _lib
+    if _lib is None:
+        p = path or _LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it with `python -m gated_deltanet_hybrid_amd.build`")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise HlaError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HLA_BF16
+    if t.dtype == torch.float32:
+        return HLA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _token_view(t: torch.Tensor, name: str):
+    """[B, T, H, d] tensor whose rows may be a window of a longer allocation.
+    Returns (B, T, H, d, ld_T)."""
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, T, H, d]")
+    B, T, H, d = t.shape
+    s = t.stride()
+    if s[3] != 1 or s[2] != d or s[1] != H * d or s[0] % (H * d) != 0 or s[0] // (H * d) < T:
+        raise ValueError(f"{name} must be row-major within a batch row (a token window of [B, ld_T, H, d])")
+    return B, T, H, d, s[0] // (H * d)
+
+
+def _scalar_view(t: torch.Tensor, B, T, H, ld_T, name):
+    if t.dtype != torch.float32 or tuple(t.shape) != (B, T, H):
+        raise ValueError(f"{name} must be float32 [B, T, H]")
+    s = t.stride()
+    if s[2] != 1 or s[1] != H or s[0] != ld_T * H:
+        raise ValueError(f"{name} must share the token window layout of k")
+
+
+def _need(t, shape, dtype, name):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
+def make_dims(B, T, H, ld_T, dk, dv, dtype_code) -> Dims:
+    return Dims(B, T, H, ld_T, dk, dv, CHUNK, dtype_code)
+
+
+def workspace_bytes(fn: int, dims: Dims, n_rep: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(library().hla_workspace_bytes(fn, ctypes.byref(dims), n_rep, ctypes.byref(out)), "hla_workspace_bytes")
+    return out.value
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device) if nbytes else None
+
+
+def _inputs(k, v, beta, alpha, q=None):
+    B, T, H, dk, ld_T = _token_view(k, "k")
+    Bv, Tv, Hv, dv, ldv = _token_view(v, "v")
+    if (Bv, Tv, Hv, ldv) != (B, T, H, ld_T) or v.dtype != k.dtype:
+        raise ValueError("v must match k's batch, tokens, heads, row length and dtype")
+    if q is not None:
+        Bq, Tq, Hq, dq, ldq = _token_view(q, "q")
+        if (Bq, Tq, Hq, dq, ldq) != (B, T, H, dk, ld_T) or q.dtype != k.dtype:
+            raise ValueError("q must match k")
+    _scalar_view(beta, B, T, H, ld_T, "beta")
+    _scalar_view(alpha, B, T, H, ld_T, "alpha")
+    return make_dims(B, T, H, ld_T, dk, dv, _dtype_code(k))
+
+
+def chunk_transitions(k, v, beta, alpha, At=None, Bc=None):
+    """Exact affine map (At, Bc) of every 64-token chunk: M_end = At M_start + Bc."""
+    d = _inputs(k, v, beta, alpha)
+    N = math.ceil(d.T / CHUNK)
+    At = torch.empty((d.B, d.H, N, d.dk, d.dk), dtype=k.dtype, device=k.device) if At is None else At
+    Bc = torch.empty((d.B, d.H, N, d.dk, d.dv), dtype=k.dtype, device=k.device) if Bc is None else Bc
+    _need(At, (d.B, d.H, N, d.dk, d.dk), k.dtype, "At")
+    _need(Bc, (d.B, d.H, N, d.dk, d.dv), k.dtype, "Bc")
+    _check(library().hla_chunk_transitions(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(At),
+                                           _ptr(Bc), _stream(k.device)), "hla_chunk_transitions")
+    return At, Bc
+
+
+def gdn_prefill(q, k, v, beta, alpha, S0=None, chunk_init=None, want_o=True, want_state=True, o=None,
+                S_final=None, ws=None):
+    """Chunkwise gated delta rule prefill.  Returns (o [B,T,H,dv] or None, S_final or None)."""
+    d = _inputs(k, v, beta, alpha, q if want_o else None)
+    N = math.ceil(d.T / CHUNK)
+    dev = k.device
+    if want_o and o is None:
+        o = torch.empty((d.B, d.T, d.H, d.dv), dtype=torch.float32, device=dev)
+    if not want_o:
+        o = None
+    if chunk_init is not None:
+        want_state = False
+    if want_state and S_final is None:
+        S_final = torch.empty((d.B, d.H, d.dk, d.dv), dtype=torch.float32, device=dev)
+    if not want_state:
+        S_final = None
+    _need(o, (d.B, d.T, d.H, d.dv), torch.float32, "o")
+    _need(S0, (d.B, d.H, d.dk, d.dv), torch.float32, "S0")
+    _need(chunk_init, (d.B, d.H, N, d.dk, d.dv), torch.float32, "chunk_init")
+    _need(S_final, (d.B, d.H, d.dk, d.dv), torch.float32, "S_final")
+    if ws is None and chunk_init is None:
+        ws = _workspace(workspace_bytes(FN_GDN_PREFILL, d), dev)
+    _check(library().hla_gdn_prefill(ctypes.byref(d), _ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(beta),
+                                     _ptr(alpha), _ptr(S0), _ptr(chunk_init), _ptr(o), _ptr(S_final), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(dev)), "hla_gdn_prefill")
+    return o, S_final
+
+
+def route_mix(q, reps, At, Bc, n_rep=CHUNK, tau=1e-3, S0=None, gates_in=None, T=None, out=None, ws=None):
+    """Router gates, skip mask, active lists, n_eff and the routed per-chunk states.
+
+    q [B, T, H, dk] (token window), reps [B, R, H, dk] (token window, chunk j's
+    representatives are rows [j n_rep, (j+1) n_rep)), At/Bc from chunk_transitions.
+    Returns a dict of gates, mask, active_idx, active_cnt, n_eff, S_routed.
+    """
+    B, H, N, dk, _ = At.shape
+    dv = Bc.shape[-1]
+    dev = At.device
+    if q is not None:
+        Bq, Tq, Hq, dq, ld_T = _token_view(q, "q")
+        if (Bq, Hq, dq) != (B, H, dk) or math.ceil(Tq / CHUNK) != N:
+            raise ValueError("q does not match the transitions")
+        T = Tq
+    else:
+        ld_T = T = T if T is not None else N * CHUNK
+    ld_R = 0
+    if reps is not None:
+        Br, Rr, Hr, dr, ld_R = _token_view(reps, "reps")
+        if (Br, Hr, dr) != (B, H, dk) or reps.dtype != At.dtype:
+            raise ValueError("reps must be [B, R, H, dk] in the transitions' dtype")
+    d = make_dims(B, T, H, ld_T, dk, dv, _dtype_code(At))
+    _need(At, (B, H, N, dk, dk), At.dtype, "At")
+    _need(Bc, (B, H, N, dk, dv), At.dtype, "Bc")
+    _need(S0, (B, H, dk, dv), torch.float32, "S0")
+    _need(gates_in, (B, H, N, N), torch.float32, "gates_in")
+    o = out or {}
+    gates = o.get("gates") if o.get("gates") is not None else torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+    mask = o.get("mask") if o.get("mask") is not None else torch.empty((B, H, N, N), dtype=torch.uint8, device=dev)
+    aidx = o.get("active_idx") if o.get("active_idx") is not None else torch.empty((B, H, N, N), dtype=torch.int32, device=dev)
+    acnt = o.get("active_cnt") if o.get("active_cnt") is not None else torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    neff = o.get("n_eff") if o.get("n_eff") is not None else torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    Sr = o.get("S_routed") if o.get("S_routed") is not None else torch.empty((B, H, N, dk, dv), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(workspace_bytes(FN_ROUTE_MIX, d, n_rep), dev)
+    _check(library().hla_route_mix(ctypes.byref(d), _ptr(q), _ptr(reps), n_rep, ld_R, _ptr(At), _ptr(Bc), _ptr(S0),
+                                   _ptr(gates_in), ctypes.c_float(tau), _ptr(gates), _ptr(mask), _ptr(aidx),
+                                   _ptr(acnt), _ptr(neff), _ptr(Sr), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(dev)), "hla_route_mix")
+    return dict(gates=gates, mask=mask, active_idx=aidx, active_cnt=acnt, n_eff=neff, S_routed=Sr)
+
+
+def hla_prefill(q, k, v, beta, alpha, tau=1e-3, gates_in=None, S0=None):
+    """The routed prefill as three calls: transitions, routing, outputs from routed states."""
+    At, Bc = chunk_transitions(k, v, beta, alpha)
+    r = route_mix(q, k, At, Bc, n_rep=CHUNK, tau=tau, S0=S0, gates_in=gates_in)
+    o, _ = gdn_prefill(q, k, v, beta, alpha, chunk_init=r["S_routed"], want_state=False)
+    r.update(At=At, Bc=Bc, o=o)
+    return r
+
+
+def gdn_decode(q, k, v, beta, alpha, S_cur, At_cur=None, At_cache=None, Bc_cache=None, reps_cache=None,
+               n_cache=None, gates_in=None, tau=1e-3, o=None, gates_out=None, commit=False):
+    """One decode step.  q, k [Bs, H, dk], v [Bs, H, dv]; S_cur/At_cur are updated in place."""
+    Bs, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(k)
+    dev = k.device
+    _need(q, (Bs, H, dk), k.dtype, "q")
+    _need(v, (Bs, H, dv), k.dtype, "v")
+    _need(beta, (Bs, H), torch.float32, "beta")
+    _need(alpha, (Bs, H), torch.float32, "alpha")
+    _need(S_cur, (Bs, H, dk, dv), torch.float32, "S_cur")
+    n_cap, n_rep = 0, 0
+    if At_cur is not None:
+        _need(At_cur, (Bs, H, dk, dk), torch.float32, "At_cur")
+        n_cap = At_cache.shape[2]
+        _need(At_cache, (Bs, H, n_cap, dk, dk), k.dtype, "At_cache")
+        _need(Bc_cache, (Bs, H, n_cap, dk, dv), k.dtype, "Bc_cache")
+        _need(n_cache, (Bs,), torch.int32, "n_cache")
+        if reps_cache is not None:
+            n_rep = reps_cache.shape[3]
+            _need(reps_cache, (Bs, H, n_cap, n_rep, dk), k.dtype, "reps_cache")
+        _need(gates_in, (Bs, H, n_cap), torch.float32, "gates_in")
+        _need(gates_out, (Bs, H, n_cap), torch.float32, "gates_out")
+    if o is None:
+        o = torch.empty((Bs, H, dv), dtype=torch.float32, device=dev)
+    _need(o, (Bs, H, dv), torch.float32, "o")
+    _check(library().hla_gdn_decode(Bs, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+                                    _ptr(S_cur), _ptr(At_cur), _ptr(At_cache), _ptr(Bc_cache), _ptr(reps_cache),
+                                    n_rep, _ptr(n_cache), n_cap, _ptr(gates_in), ctypes.c_float(tau), _ptr(o),
+                                    _ptr(gates_out), 1 if commit else 0, _stream(dev)), "hla_gdn_decode")
+    return o

@@ -1,0 +1,199 @@
+/*
+ * hla.h -- C ABI of libhla.so: the Gated DeltaNet + HLA hot path on MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [HLA]  "HLA: Expressive Hybrid Linear Attention via Chunk-Wise Dynamic Mixing"
+ *          (ai.info AI-summary page): Overview, Key Contributions, Methodology in Plain
+ *          English paragraphs 1-4, Authors' abstract.
+ *   [TR]   Tail-Replay abstract (second abstract on the thelatestinai.com page listed
+ *          under the same HLA title).
+ *   The per-token update is the gated delta rule of Gated DeltaNet, the affine update
+ *   [HLA] Methodology paragraph 1 describes in words:
+ *       S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t.
+ *
+ * Orientation and layouts (all tensors dense, row-major, no hidden padding):
+ *   - The math state S is [dv, dk]; the library stores M = S^T as [dk, dv] float32.
+ *   - A chunk's exact affine map ([HLA] Methodology paragraph 1) S -> S A_c + B_c is
+ *     stored in the state orientation as the pair (At, Bc) with
+ *         M_end = At @ M_start + Bc,   At = A_c^T [dk, dk],   Bc = B_c^T [dk, dv].
+ *   - Per-token inputs: q, k [B, ld_T, H, dk]; v [B, ld_T, H, dv]; beta, alpha
+ *     [B, ld_T, H] float32.  Only tokens [0, T) of each batch row are read, so a suffix
+ *     view (Tail-Replay) passes base pointers offset to the suffix start and ld_T = the
+ *     allocated row length.
+ *   - Chunk c covers tokens [c C, min((c + 1) C, T)); N = ceil(T / C); the last chunk may
+ *     be partial and its transition is the product over its own tokens.
+ *   - q, k, v, reps and the transitions use the call's dtype (float32 or bfloat16);
+ *     states, outputs, gates and every accumulation are float32.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless marked "host".  Base pointers must be 16-byte
+ *     aligned.  The caller allocates and owns every buffer, including the workspace; the
+ *     library never allocates or frees device memory and keeps no pointer after return.
+ *   - Calls only enqueue work on `stream`; nothing synchronises.  Calls that overlap on
+ *     the same buffers race; calls on separate buffers are independent and reentrant.
+ *   - Arguments are validated before anything is enqueued.  On an error the call returns a
+ *     non-zero status and enqueues nothing.  A failed launch returns HLA_ERR_HIP.
+ *     Asynchronous device faults surface at the caller's next synchronisation.
+ *   - Every output element is overwritten, so results never depend on prior contents.
+ */
+#ifndef HLA_H_
+#define HLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HLA_ABI_VERSION 1
+
+typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype_t;
+
+typedef enum {
+  HLA_OK = 0,
+  HLA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                              */
+  HLA_ERR_BAD_SHAPE = 2,    /* a size is out of range or inconsistent                  */
+  HLA_ERR_BAD_DTYPE = 3,    /* dtype is not HLA_F32 / HLA_BF16                         */
+  HLA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than hla_workspace_bytes() */
+  HLA_ERR_HIP = 5,          /* a kernel launch failed                                  */
+  HLA_ERR_UNSUPPORTED = 6,  /* a valid but unsupported combination of arguments        */
+  HLA_ERR_ALIGN = 7,        /* a base pointer is not 16-byte aligned                   */
+  HLA_ERR_INTERNAL = 8      /* an unexpected host-side failure                         */
+} hla_status_t;
+
+/* Problem sizes.  B batch rows, T tokens processed per row, H heads, ld_T >= T tokens
+ * allocated per row; dk, dv in {64, 128}; C = 64 tokens per chunk. */
+typedef struct {
+  int64_t B, T, H, ld_T;
+  int32_t dk, dv, C;
+  int32_t dtype; /* hla_dtype_t */
+} hla_dims_t;
+
+/* Which entry point a workspace size is asked for (hla_workspace_bytes). */
+typedef enum { HLA_FN_CHUNK_TRANSITIONS = 0, HLA_FN_GDN_PREFILL = 1, HLA_FN_ROUTE_MIX = 2 } hla_fn_t;
+
+/*
+ * hla_chunk_transitions -- the exact affine map of every chunk.
+ * [HLA] Methodology paragraph 1 (affine maps compose, so a chunk is summarised exactly by
+ * one affine map) and Key Contributions 2 (exact chunk-wise affine transitions).
+ * Computed per (b, h, chunk) through the UT form of the chunk: the strictly lower matrix
+ * diag(beta)(K K^T o decay) is inverted per chunk instead of running the token loop.
+ *   k, v, beta, alpha : inputs as in the header notes (q is not needed).
+ *   At [B, H, N, dk, dk], Bc [B, H, N, dk, dv] (out, dtype): M_end = At M_start + Bc.
+ * Errors: HLA_ERR_NULL_ARG, HLA_ERR_BAD_SHAPE, HLA_ERR_BAD_DTYPE, HLA_ERR_ALIGN, HLA_ERR_HIP.
+ */
+hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const void* v,
+                                   const float* beta, const float* alpha, void* At, void* Bc,
+                                   hipStream_t stream);
+
+/*
+ * hla_gdn_prefill -- chunkwise Gated DeltaNet prefill.
+ * [HLA] Methodology paragraph 1 (the per-token affine recurrence and its chunk form);
+ * [TR] (state rebuild by replaying a suffix from a zero state: pass o = NULL).
+ * Modes:
+ *   native  (chunk_init == NULL): states run through the chunks in order starting from S0
+ *           (NULL = zero state); o_t = S_t q_t; S_final = state after token T-1.
+ *   routed  (chunk_init != NULL): chunk c starts from chunk_init[b, h, c] (the routed
+ *           states of hla_route_mix; the current chunk has weight one, [HLA]
+ *           Methodology paragraph 3); no state is carried between chunks.  S0 and S_final
+ *           must be NULL.
+ *   state-only (o == NULL): only S_final is produced; q may be NULL (Tail-Replay).
+ *   q, k, v, beta, alpha : per-token inputs.
+ *   S0         [B, H, dk, dv] float32 or NULL.
+ *   chunk_init [B, H, N, dk, dv] float32 or NULL.
+ *   o          [B, T, H, dv] float32 (out) or NULL.
+ *   S_final    [B, H, dk, dv] float32 (out) or NULL.  At least one of o, S_final.
+ *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_GDN_PREFILL) bytes
+ *           (zero in routed mode).
+ * Errors: as hla_chunk_transitions, plus HLA_ERR_WORKSPACE, HLA_ERR_UNSUPPORTED.
+ */
+hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                             const float* beta, const float* alpha, const float* S0,
+                             const float* chunk_init, float* o, float* S_final, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hla_route_mix -- HLA router gates and the gated composition of chunk transitions.
+ * [HLA] Overview (log-mean-exp pooled routing gates), Methodology paragraphs 2-4,
+ * Key Contributions 3 and the abstract (effective support):
+ *   qbar_i   = mean of q over query chunk i's tokens;
+ *   l_ij     = log( (1/n_rep) sum_r exp(qbar_i . r / sqrt(dk)) ) over chunk j's
+ *              representatives r;  g_ij = sigmoid(l_ij) for j < i (independent gates);
+ *   g_ii = 1 (current chunk), g_ij = 0 for j > i (future masked);
+ *   mask_ij  = (j < i) and (g_ij >= tau)   [skip below tau without renormalisation,
+ *              decided in float32];  ghat = g * mask;
+ *   n_eff_i  = (sum_j ghat_ij)^2 / sum_j ghat_ij^2 over j < i (0 when all are skipped);
+ *   S~_i     = chronological composition over j < i with mask_ij of
+ *              M -> M + ghat_ij (At_j M + Bc_j - M), starting from S0 (NULL = zero).
+ *   q          per-token queries (read only when gates_in == NULL).
+ *   reps       [B, ld_R, H, dk] (dtype): chunk j's representatives are rows
+ *              [j n_rep, (j + 1) n_rep); rows are read for j < N - 1 only, so
+ *              ld_R >= (N - 1) n_rep.  Passing k with n_rep = C, ld_R = ld_T uses the
+ *              chunk's raw keys.
+ *   At, Bc     [B, H, N, dk, dk] / [B, H, N, dk, dv] (dtype), from hla_chunk_transitions.
+ *   gates_in   [B, H, N, N] float32 caller gates (entries j < i are read) or NULL.
+ *   gates      [B, H, N, N] float32 out (full matrix, diagonal 1, upper 0).
+ *   mask       [B, H, N, N] uint8 out (1 = composed).
+ *   active_idx [B, H, N, N] int32 out: ascending j with mask_ij, then -1.
+ *   active_cnt [B, H, N] int32 out.   n_eff [B, H, N] float32 out or NULL.
+ *   S_routed   [B, H, N, dk, dv] float32 out.
+ * Errors: as hla_gdn_prefill.
+ */
+hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps, int32_t n_rep,
+                           int64_t ld_R, const void* At, const void* Bc, const float* S0,
+                           const float* gates_in, float tau, float* gates, uint8_t* mask,
+                           int32_t* active_idx, int32_t* active_cnt, float* n_eff,
+                           float* S_routed, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hla_gdn_decode -- one single-token decode step for Bs sequences x H heads.
+ * [HLA] Key Contributions 3 (dynamic autoregressive decoding) with Methodology
+ * paragraphs 2-4.  Per (sequence b, head h):
+ *   live chunk : S_cur (= M of the tokens since the last cached chunk) and its
+ *                transition At_cur are extended by this token:
+ *                M <- alpha (I - beta k k^T) M + beta k v^T,  At <- alpha (I - beta k k^T) At.
+ *   gates      : g_j = sigmoid(log-mean-exp_r (q . r / sqrt(dk))) over cached chunk j's
+ *                representatives, using the token's own q (or gates_in);
+ *                ghat_j = g_j if g_j >= tau else 0.
+ *   output     : o = (S~ A_cur + B_cur) q in math orientation, where S~ composes the
+ *                gated cached chunks j < n_cache[b] from zero in time order.
+ *   native     : At_cur == NULL: S_cur is the full-prefix state and o = S_cur^T q.
+ *   q, k [Bs, H, dk], v [Bs, H, dv] (dtype); beta, alpha [Bs, H] float32.
+ *   S_cur   [Bs, H, dk, dv] float32 in/out.   At_cur [Bs, H, dk, dk] float32 in/out or NULL.
+ *   At_cache [Bs, H, n_cap, dk, dk], Bc_cache [Bs, H, n_cap, dk, dv] (dtype) in/out.
+ *   reps_cache [Bs, H, n_cap, n_rep, dk] (dtype); may be NULL when gates_in is given.
+ *   n_cache [Bs] int32 in/out (device): cached chunks per sequence; values above n_cap
+ *           are clamped to n_cap.
+ *   gates_in [Bs, H, n_cap] float32 or NULL;  gates_out [Bs, H, n_cap] float32 or NULL
+ *           (entries j >= n_cache[b] are written as 0).
+ *   o [Bs, H, dv] float32 out.
+ *   commit: 1 = after the step append (At_cur, S_cur), cast to dtype, at slot n_cache[b],
+ *           reset At_cur = I, S_cur = 0 and increment n_cache[b].  A full cache
+ *           (n_cache[b] == n_cap) is left unchanged.  The caller writes that chunk's
+ *           representatives.
+ * Errors: HLA_ERR_NULL_ARG, HLA_ERR_BAD_SHAPE, HLA_ERR_BAD_DTYPE, HLA_ERR_ALIGN, HLA_ERR_HIP.
+ */
+hla_status_t hla_gdn_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32_t dtype,
+                            const void* q, const void* k, const void* v, const float* beta,
+                            const float* alpha, float* S_cur, float* At_cur, void* At_cache,
+                            void* Bc_cache, const void* reps_cache, int32_t n_rep,
+                            int32_t* n_cache, int32_t n_cap, const float* gates_in, float tau,
+                            float* o, float* gates_out, int32_t commit, hipStream_t stream);
+
+/* Workspace bytes that entry point `fn` needs for dims `d` (n_rep is used by
+ * HLA_FN_ROUTE_MIX).  `out` is a host pointer. */
+hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep, size_t* out);
+
+/* Static description of a status code (never NULL). */
+const char* hla_status_string(int32_t status);
+
+/* HLA_ABI_VERSION of the loaded library. */
+int32_t hla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLA_H_ */

@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+entry point include/hla.h declares, sizes its workspaces, and rejects invalid arguments
+with the documented status before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_hybrid_amd import hla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hla.h")
+
+OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, WORKSPACE, HIP, UNSUPPORTED, ALIGN = 0, 1, 2, 3, 4, 5, 6, 7
+P = 0x10000          # a 16-byte aligned placeholder address; never dereferenced
+PU = 0x10008         # a misaligned one
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hla.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:hla_status_t|const char\*|int32_t)\s+(hla_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"hla_chunk_transitions", "hla_gdn_prefill", "hla_route_mix", "hla_gdn_decode"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.hla_abi_version() == 1
+    for s in range(0, 9):
+        assert lib.hla_status_string(s)
+    assert lib.hla_status_string(99) == b"unknown status"
+
+
+def dims(B=1, T=256, H=2, ld_T=None, dk=128, dv=128, C=64, dtype=1):
+    return hla.Dims(B, T, H, T if ld_T is None else ld_T, dk, dv, C, dtype)
+
+
+def test_workspace_sizes(lib):
+    d = dims(B=2, T=130, H=3, dk=128, dv=64, dtype=1)  # N = 3 chunks
+    BHN = 2 * 3 * 3
+    assert hla.workspace_bytes(hla.FN_CHUNK_TRANSITIONS, d) == 0
+    ab = BHN * 128 * 128 * 2 + BHN * 128 * 64 * 2
+    st = BHN * 128 * 64 * 4
+    assert hla.workspace_bytes(hla.FN_GDN_PREFILL, d) == ab + st
+    assert hla.workspace_bytes(hla.FN_ROUTE_MIX, d) == 2 * 3 * 3 * 128 * 4
+    out = ctypes.c_size_t()
+    assert lib.hla_workspace_bytes(7, ctypes.byref(d), 0, ctypes.byref(out)) == UNSUPPORTED
+    assert lib.hla_workspace_bytes(0, ctypes.byref(d), 0, None) == NULL_ARG
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=96), BAD_SHAPE), (dict(dv=32), BAD_SHAPE), (dict(C=128), BAD_SHAPE), (dict(T=0), BAD_SHAPE),
+    (dict(ld_T=100), BAD_SHAPE), (dict(B=0), BAD_SHAPE), (dict(H=0), BAD_SHAPE), (dict(dtype=2), BAD_DTYPE),
+])
+def test_chunk_transitions_rejects_bad_dims(lib, kw, code):
+    d = dims(**kw)
+    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, None) == code
+
+
+def test_chunk_transitions_rejects_null_and_misaligned(lib):
+    d = dims()
+    assert lib.hla_chunk_transitions(None, P, P, P, P, P, P, None) == NULL_ARG
+    for i in range(6):
+        args = [P] * 6
+        args[i] = None
+        assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None) == NULL_ARG
+        args[i] = PU
+        assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None) == ALIGN
+
+
+def test_prefill_validation(lib):
+    d = dims()
+    pre = lib.hla_gdn_prefill
+    # neither o nor S_final
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, None, None, P, 1 << 30, None) == NULL_ARG
+    # o without q
+    assert pre(ctypes.byref(d), None, P, P, P, P, None, None, P, None, P, 1 << 30, None) == NULL_ARG
+    # routed mode with S0 or S_final
+    assert pre(ctypes.byref(d), P, P, P, P, P, P, P, P, None, None, 0, None) == UNSUPPORTED
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, P, P, P, None, 0, None) == UNSUPPORTED
+    # native mode without enough workspace
+    need = hla.workspace_bytes(hla.FN_GDN_PREFILL, d)
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, P, P, P, need - 1, None) == WORKSPACE
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, P, P, None, 0, None) == WORKSPACE
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, P, P, PU, need, None) == ALIGN
+
+
+def test_route_mix_validation(lib):
+    d = dims(T=256)  # N = 4
+    rm = lib.hla_route_mix
+    outs = [P, P, P, P, P, P]  # gates, mask, active_idx, active_cnt, n_eff, S_routed
+    ws = hla.workspace_bytes(hla.FN_ROUTE_MIX, d)
+    # computed gates need q and reps
+    assert rm(ctypes.byref(d), None, P, 64, 256, P, P, None, None, 1e-3, *outs, P, ws, None) == NULL_ARG
+    assert rm(ctypes.byref(d), P, None, 64, 256, P, P, None, None, 1e-3, *outs, P, ws, None) == NULL_ARG
+    # reps rows: (N - 1) * n_rep must fit in ld_R
+    assert rm(ctypes.byref(d), P, P, 64, 191, P, P, None, None, 1e-3, *outs, P, ws, None) == BAD_SHAPE
+    assert rm(ctypes.byref(d), P, P, 0, 256, P, P, None, None, 1e-3, *outs, P, ws, None) == BAD_SHAPE
+    assert rm(ctypes.byref(d), P, P, 64, 256, P, P, None, None, float("nan"), *outs, P, ws, None) == BAD_SHAPE
+    assert rm(ctypes.byref(d), P, P, 64, 256, P, P, None, None, 1e-3, *outs, P, ws - 1, None) == WORKSPACE
+    bad = list(outs)
+    bad[5] = None
+    assert rm(ctypes.byref(d), P, P, 64, 256, P, P, None, None, 1e-3, *bad, P, ws, None) == NULL_ARG
+
+
+def test_decode_validation(lib):
+    dec = lib.hla_gdn_decode
+    base = [P, P, P, P, P, P]  # q, k, v, beta, alpha, S_cur
+    # (Bs, H, dk, dv, dtype, q, k, v, beta, alpha, S_cur, At_cur, At_cache, Bc_cache, reps, n_rep, n_cache,
+    #  n_cap, gates_in, tau, o, gates_out, commit, stream)
+    assert dec(0, 1, 128, 128, 1, *base, None, None, None, None, 0, None, 0, None, 0.0, P, None, 0, None) == BAD_SHAPE
+    assert dec(1, 1, 128, 128, 5, *base, None, None, None, None, 0, None, 0, None, 0.0, P, None, 0, None) == BAD_DTYPE
+    assert dec(1, 1, 128, 128, 1, *base, None, None, None, None, 0, None, 0, None, 0.0, None, None, 0, None) == NULL_ARG
+    # commit needs a live transition
+    assert dec(1, 1, 128, 128, 1, *base, None, None, None, None, 0, None, 0, None, 0.0, P, None, 1, None) == UNSUPPORTED
+    # routed: cache arrays and n_cache required; n_cap bounded; reps unless caller gates
+    assert dec(1, 1, 128, 128, 1, *base, P, None, P, P, 64, P, 4, None, 0.0, P, None, 0, None) == NULL_ARG
+    assert dec(1, 1, 128, 128, 1, *base, P, P, P, P, 64, P, 1025, None, 0.0, P, None, 0, None) == BAD_SHAPE
+    assert dec(1, 1, 128, 128, 1, *base, P, P, P, None, 64, P, 4, None, 0.0, P, None, 0, None) == NULL_ARG
+    assert dec(1, 1, 128, 128, 1, *base, P, P, P, P, 0, P, 4, None, 0.0, P, None, 0, None) == BAD_SHAPE
+    assert dec(1, 1, 128, 128, 1, *base, P, P, P, P, 64, P, 4, None, 0.0, PU, None, 0, None) == ALIGN
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = hla._lib
+    try:
+        hla._lib = None
+        with pytest.raises(RuntimeError, match="missing"):
+            hla.library(str(tmp_path / "nope.so"))
+    finally:
+        hla._lib = saved
