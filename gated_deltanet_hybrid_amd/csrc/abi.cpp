@@ -14,6 +14,7 @@ constexpr int64_t kMaxGrid = 0x7fffffffLL;
 constexpr int32_t kMaxCacheSlots = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int64_t n_chunks(const hla_dims_t* d) { return (d->T + d->C - 1) / d->C; }
 
@@ -36,9 +37,15 @@ hla_status_t check_dims(const hla_dims_t* d) {
   return HLA_OK;
 }
 
+// Tensors read or written in 16-byte vectors need 16-byte alignment; per-token scalars,
+// gates and element-wise outputs need only 4-byte alignment.
 template <class... P>
 bool all_aligned(P... p) {
   return (aligned16(p) && ...);
+}
+template <class... P>
+bool all_aligned4(P... p) {
+  return (aligned4(p) && ...);
 }
 
 // Workspace of the native prefill: transitions (dtype) then, when outputs are wanted, the
@@ -100,7 +107,7 @@ hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const voi
   hla_status_t st = check_dims(d);
   if (st != HLA_OK) return st;
   if (!k || !v || !beta || !alpha || !At || !Bc) return HLA_ERR_NULL_ARG;
-  if (!all_aligned(k, v, beta, alpha, At, Bc)) return HLA_ERR_ALIGN;
+  if (!all_aligned(k, v, At, Bc) || !all_aligned4(beta, alpha)) return HLA_ERR_ALIGN;
   hla::ChunkArgs a{};
   a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
   a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)n_chunks(d);
@@ -116,7 +123,7 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
   if (!k || !v || !beta || !alpha) return HLA_ERR_NULL_ARG;
   if (!o && !S_final) return HLA_ERR_NULL_ARG;
   if (o && !q) return HLA_ERR_NULL_ARG;
-  if (!all_aligned(q, k, v, beta, alpha, S0, chunk_init, o, S_final, ws)) return HLA_ERR_ALIGN;
+  if (!all_aligned(q, k, v, S0, chunk_init, S_final, ws) || !all_aligned4(beta, alpha, o)) return HLA_ERR_ALIGN;
   const int32_t N = (int32_t)n_chunks(d);
   hla::ChunkArgs a{};
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
@@ -162,7 +169,8 @@ hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps,
   if (computed && (!q || !reps)) return HLA_ERR_NULL_ARG;
   if (computed && (n_rep < 1 || ld_R < (N - 1) * (int64_t)n_rep)) return HLA_ERR_BAD_SHAPE;
   if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
-  if (!all_aligned(q, reps, At, Bc, S0, gates_in, gates, S_routed, ws)) return HLA_ERR_ALIGN;
+  if (!all_aligned(q, reps, At, Bc, S0, S_routed, ws) || !all_aligned4(gates_in, gates, active_idx, active_cnt, n_eff))
+    return HLA_ERR_ALIGN;
   if (computed && (!ws || (int64_t)ws_bytes < route_ws(d))) return HLA_ERR_WORKSPACE;
   hla::RouteArgs a{};
   a.q = q; a.reps = reps; a.n_rep = n_rep; a.ld_R = ld_R; a.At = At; a.Bc = Bc; a.S0 = S0;
@@ -193,7 +201,8 @@ hla_status_t hla_gdn_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32
     }
     if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
   }
-  if (!all_aligned(q, k, v, beta, alpha, S_cur, At_cur, At_cache, Bc_cache, reps_cache, gates_in, o, gates_out))
+  if (!all_aligned(S_cur, At_cur, At_cache, Bc_cache, reps_cache) ||
+      !all_aligned4(q, k, v, beta, alpha, gates_in, o, gates_out))
     return HLA_ERR_ALIGN;
   hla::DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.alpha = alpha; a.S_cur = S_cur; a.At_cur = At_cur;

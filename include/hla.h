@@ -26,8 +26,11 @@
  *     states, outputs, gates and every accumulation are float32.
  *
  * Conventions for every entry point:
- *   - Pointers are device pointers unless marked "host".  Base pointers must be 16-byte
- *     aligned.  The caller allocates and owns every buffer, including the workspace; the
+ *   - Pointers are device pointers unless marked "host".  Base pointers of tensors moved in
+ *     16-byte vectors (q, k, v and reps of the prefill calls, transitions, states, chunk
+ *     inits, caches and the workspace) must be 16-byte aligned; per-token scalars (beta,
+ *     alpha), gates, counts, element-wise outputs (o) and the decode token vectors need
+ *     4-byte alignment (2 bytes for bf16 decode tokens).  The caller allocates and owns every buffer, including the workspace; the
  *     library never allocates or frees device memory and keeps no pointer after return.
  *   - Calls only enqueue work on `stream`; nothing synchronises.  Calls that overlap on
  *     the same buffers race; calls on separate buffers are independent and reentrant.

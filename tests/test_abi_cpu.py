@@ -74,7 +74,8 @@ def test_chunk_transitions_rejects_null_and_misaligned(lib):
         args = [P] * 6
         args[i] = None
         assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None) == NULL_ARG
-        args[i] = PU
+        # vector-loaded tensors need 16 bytes, the per-token scalars (beta, alpha) 4
+        args[i] = P + 2 if i in (2, 3) else PU
         assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None) == ALIGN
 
 
@@ -128,7 +129,8 @@ def test_decode_validation(lib):
     assert dec(1, 1, 128, 128, 1, *base, P, P, P, P, 64, P, 1025, None, 0.0, P, None, 0, None) == BAD_SHAPE
     assert dec(1, 1, 128, 128, 1, *base, P, P, P, None, 64, P, 4, None, 0.0, P, None, 0, None) == NULL_ARG
     assert dec(1, 1, 128, 128, 1, *base, P, P, P, P, 0, P, 4, None, 0.0, P, None, 0, None) == BAD_SHAPE
-    assert dec(1, 1, 128, 128, 1, *base, P, P, P, P, 64, P, 4, None, 0.0, PU, None, 0, None) == ALIGN
+    assert dec(1, 1, 128, 128, 1, *base, P, P, P, P, 64, P, 4, None, 0.0, P + 2, None, 0, None) == ALIGN
+    assert dec(1, 1, 128, 128, 1, P, P, P, P, P, PU, P, P, P, P, 64, P, 4, None, 0.0, P, None, 0, None) == ALIGN
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
