@@ -64,7 +64,13 @@ PrefillWs prefill_ws(const hla_dims_t* d) {
   return w;
 }
 
-int64_t route_ws(const hla_dims_t* d) { return round_up(d->B * d->H * n_chunks(d) * d->dk * 4, 256); }
+// Workspace of hla_route_mix: float32 query-chunk means, then (bf16 only) the reordered
+// copy of At - I that the composition streams.
+int64_t route_qbar_bytes(const hla_dims_t* d) { return round_up(d->B * d->H * n_chunks(d) * d->dk * 4, 256); }
+int64_t route_ws(const hla_dims_t* d) {
+  const int64_t prep = d->dtype == HLA_BF16 ? round_up(d->B * d->H * n_chunks(d) * d->dk * d->dk * 2, 256) : 0;
+  return route_qbar_bytes(d) + prep;
+}
 
 hla_status_t hip_status(hipError_t e) { return e == hipSuccess ? HLA_OK : HLA_ERR_HIP; }
 
@@ -171,11 +177,12 @@ hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps,
   if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
   if (!all_aligned(q, reps, At, Bc, S0, S_routed, ws) || !all_aligned4(gates_in, gates, active_idx, active_cnt, n_eff))
     return HLA_ERR_ALIGN;
-  if (computed && (!ws || (int64_t)ws_bytes < route_ws(d))) return HLA_ERR_WORKSPACE;
+  if (!ws || (int64_t)ws_bytes < route_ws(d)) return HLA_ERR_WORKSPACE;
   hla::RouteArgs a{};
   a.q = q; a.reps = reps; a.n_rep = n_rep; a.ld_R = ld_R; a.At = At; a.Bc = Bc; a.S0 = S0;
   a.gates_in = gates_in; a.tau = tau; a.gates = gates; a.mask = mask; a.active_idx = active_idx;
   a.active_cnt = active_cnt; a.n_eff = n_eff; a.S_routed = S_routed; a.qbar = static_cast<float*>(ws);
+  a.At_prep = static_cast<char*>(ws) + route_qbar_bytes(d);
   a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)N;
   return hip_status(hla::launch_route(a, d->dtype, d->dk, d->dv, stream));
 }

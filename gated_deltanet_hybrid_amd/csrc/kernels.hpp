@@ -53,10 +53,13 @@ struct RouteArgs {
   float* n_eff;         // [B,H,N] or null
   float* S_routed;      // [B,H,N,dk,dv]
   float* qbar;          // workspace [B,H,N,dk] float32
+  void* At_prep;        // workspace [B,H,N,dk,dk] bf16: (At - I) reordered for the composition
   int64_t B, T, H, ld_T;
   int32_t N;
 };
 hipError_t launch_route(const RouteArgs& a, int dtype, int dk, int dv, hipStream_t s);
+// bf16 gated composition (the routed prefill's hot loop); gates and mask must be final.
+hipError_t launch_compose_bf16(const RouteArgs& a, int dk, int dv, hipStream_t s);
 
 struct DecodeArgs {
   const void* q;

@@ -142,6 +142,8 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
  *   active_idx [B, H, N, N] int32 out: ascending j with mask_ij, then -1.
  *   active_cnt [B, H, N] int32 out.   n_eff [B, H, N] float32 out or NULL.
  *   S_routed   [B, H, N, dk, dv] float32 out.
+ *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_ROUTE_MIX) bytes (the
+ *              query-chunk means and a reordered copy of At - I for the composition).
  * Errors: as hla_gdn_prefill.
  */
 hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps, int32_t n_rep,
