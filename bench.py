@@ -1,0 +1,377 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet + HLA hot path on one MI355X.
+
+Headline: routed GDN+HLA prefill at T = 32768 (B = 1, H = 16, d = 128, C = 64, bf16 inputs,
+float32 states), one step = hla_chunk_transitions -> hla_route_mix -> hla_gdn_prefill
+(chunk_init = routed states).  Reports tokens/s, whole-step MFMA utilisation, a roofline
+record of the dominant kernel (the gated composition) timed with HIP events on its own
+stream, and the CPU oracle's throughput on a bounded sample.  Secondary records (same
+JSON line): decode step tokens/s with HBM GB/s, native chunkwise prefill, Tail-Replay
+state rebuild.  All inputs are seeded synthetic tensors of the workloads' shapes.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s (GDN+HLA, T=32K) with MFMA util %; decode tokens/s with HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+C = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- FLOP / byte models
+def flops_transitions(n_chunks, dk, dv):
+    """UT chunk form per chunk: K K^T, the W/U products, the K^T D [W|U] product."""
+    return n_chunks * (2 * C * C * dk + 2 * C * C * (dk + dv) + 2 * C * dk * (dk + dv))
+
+
+def flops_routed_output(n_chunks, dk, dv):
+    """Per chunk: Q K^T, P [W|U], Qp S~ (plus the transition-side K K^T and W/U)."""
+    return n_chunks * (2 * C * C * dk * 2 + 2 * C * C * (dk + dv) * 2 + 2 * C * dk * dv)
+
+
+def flops_gates(pairs, n_rep, dk):
+    return pairs * 2 * n_rep * dk
+
+
+def flops_compose(pairs, dk, dv):
+    """One gated composition step: S (dv x dk) times A (dk x dk)."""
+    return pairs * 2 * dk * dk * dv
+
+
+def sha_of(*paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_key, sources):
+    """HBM bytes per launch from the committed counter summary, or None when the kernel
+    source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha") != sha_of(*sources):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- helpers
+def to_dev(storage, dtype, torch):
+    import numpy as np
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(storage).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(storage, dtype=np.float32)).cuda()
+
+
+def timed(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+# ----------------------------------------------------------------------------- routed prefill
+def bench_routed_prefill(args, torch, hla, inputs):
+    W = inputs.WORKLOADS["routed_prefill"]
+    N = W.N
+    log(f"[routed_prefill] generating inputs B={W.B} T={W.T} H={W.H} d={W.dk}")
+    x = inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["routed_prefill"],
+                          plant_period=W.plant_period)
+    q, k, v = (to_dev(a, W.dtype, torch) for a in (x.q, x.k, x.v))
+    beta, alpha = to_dev(x.beta, "f32", torch), to_dev(x.alpha, "f32", torch)
+    dev = k.device
+    At = torch.empty((W.B, W.H, N, W.dk, W.dk), dtype=k.dtype, device=dev)
+    Bc = torch.empty((W.B, W.H, N, W.dk, W.dv), dtype=k.dtype, device=dev)
+    d = hla.make_dims(W.B, W.T, W.H, W.T, W.dk, W.dv, hla.HLA_BF16)
+    ws = torch.empty(hla.workspace_bytes(hla.FN_ROUTE_MIX, d, C), dtype=torch.uint8, device=dev)
+    out = dict(gates=torch.empty((W.B, W.H, N, N), dtype=torch.float32, device=dev),
+               mask=torch.empty((W.B, W.H, N, N), dtype=torch.uint8, device=dev),
+               active_idx=torch.empty((W.B, W.H, N, N), dtype=torch.int32, device=dev),
+               active_cnt=torch.empty((W.B, W.H, N), dtype=torch.int32, device=dev),
+               n_eff=torch.empty((W.B, W.H, N), dtype=torch.float32, device=dev),
+               S_routed=torch.empty((W.B, W.H, N, W.dk, W.dv), dtype=torch.float32, device=dev))
+    o = torch.empty((W.B, W.T, W.H, W.dv), dtype=torch.float32, device=dev)
+
+    def step():
+        hla.chunk_transitions(k, v, beta, alpha, At=At, Bc=Bc)
+        hla.route_mix(q, k, At, Bc, n_rep=C, tau=W.tau, out=out, ws=ws)
+        hla.gdn_prefill(q, k, v, beta, alpha, chunk_init=out["S_routed"], want_state=False, o=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    pairs = int(out["active_cnt"].sum().item())
+    hla.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    comp_ms, comp_n = hla.timing_read(hla.KERNEL_COMPOSE)
+    per_kernel = {name: hla.timing_read(kid) for name, kid in
+                  (("chunk", hla.KERNEL_CHUNK), ("gates", hla.KERNEL_GATES), ("compose", hla.KERNEL_COMPOSE))}
+    hla.timing_enable(False)
+
+    n_chunks = W.B * W.H * N
+    fl_comp = flops_compose(pairs, W.dk, W.dv)
+    fl_total = (fl_comp + flops_transitions(n_chunks, W.dk, W.dv) + flops_gates(pairs, C, W.dk)
+                + flops_routed_output(n_chunks, W.dk, W.dv))
+    comp_avg_s = comp_ms / comp_n / 1e3
+    achieved = fl_comp / comp_avg_s / 1e12
+    traffic = read_traffic("compose_routed_prefill", ["gated_deltanet_hybrid_amd/csrc/compose.hip"])
+    tokens = W.B * W.T
+    res = dict(
+        value=tokens / dt, ms_per_step=dt * 1e3,
+        mfma_util_pct=100.0 * fl_total / dt / (PEAK_BF16_TFLOPS * 1e12),
+        step_tflops=fl_total / dt / 1e12, active_pairs=pairs,
+        kernel_ms={kname: round(ms / max(n, 1), 4) for kname, (ms, n) in per_kernel.items()},
+        roofline=dict(kernel="compose_bf16_kernel", bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
+                      unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic,
+                      flops_per_launch=fl_comp, avg_launch_ms=round(comp_avg_s * 1e3, 4), launches=comp_n),
+    )
+    log(f"[routed_prefill] {dt*1e3:.3f} ms/step, {tokens/dt/1e6:.3f} M tok/s, compose {comp_avg_s*1e3:.3f} ms "
+        f"({achieved:.0f} TFLOP/s), step MFMA util {res['mfma_util_pct']:.1f}%")
+    del q, k, v, At, Bc, out, o, ws
+    torch.cuda.empty_cache()
+    return res, x
+
+
+# ----------------------------------------------------------------------------- decode
+def bench_decode(args, torch, hla, inputs):
+    W = inputs.WORKLOADS["decode"]
+    Bs, H, dk, dv, n_cap = W.B, W.H, W.dk, W.dv, W.n_cache
+    log(f"[decode] generating {n_cap} cached chunks per sequence for Bs={Bs} H={H}")
+    hist = inputs.gen_tokens(Bs, n_cap * C, H, dk, dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["decode"],
+                             with_q=False)
+    k = to_dev(hist.k, W.dtype, torch)
+    v = to_dev(hist.v, W.dtype, torch)
+    beta, alpha = to_dev(hist.beta, "f32", torch), to_dev(hist.alpha, "f32", torch)
+    del hist
+    At_cache, Bc_cache = hla.chunk_transitions(k, v, beta, alpha)        # [Bs, H, n_cap, dk, dk|dv]
+    reps = k.view(Bs, n_cap, C, H, dk).permute(0, 3, 1, 2, 4).contiguous()  # chunk keys as representatives
+    del k, v, beta, alpha
+    n_cache = torch.full((Bs,), n_cap, dtype=torch.int32, device="cuda")
+    S = torch.zeros((Bs, H, dk, dv), dtype=torch.float32, device="cuda")
+    A = torch.eye(dk, dtype=torch.float32, device="cuda").repeat(Bs, H, 1, 1).contiguous()
+    o = torch.empty((Bs, H, dv), dtype=torch.float32, device="cuda")
+    n_tok = 32  # distinct token sets, cycled over the timed steps
+    toks = [inputs.gen_decode_tokens(Bs, H, dk, dv, step=s, dtype=W.dtype, seed=0, stream=inputs.STREAM["decode"])
+            for s in range(n_tok)]
+    toks = [{kk: to_dev(vv, W.dtype if kk in ("q", "k", "v") else "f32", torch) for kk, vv in t.items()} for t in toks]
+    it = [0]
+
+    def step():
+        t = toks[it[0] % n_tok]
+        it[0] += 1
+        hla.gdn_decode(t["q"], t["k"], t["v"], t["beta"], t["alpha"], S, At_cur=A, At_cache=At_cache,
+                       Bc_cache=Bc_cache, reps_cache=reps, n_cache=n_cache, tau=W.tau, o=o)
+
+    steps = args.decode_steps
+    for _ in range(8):
+        step()
+    torch.cuda.synchronize()
+    hla.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    dec_ms, dec_n = hla.timing_read(hla.KERNEL_DECODE)
+    hla.timing_enable(False)
+    e = 2  # bf16 bytes
+    per_seqhead = (2 * dk * dv * 4 + 2 * dk * dk * 4 + n_cap * (dk * dk + dk * dv) * e + n_cap * C * dk * e
+                   + (2 * dk + dv) * e + 2 * 4 + dv * 4)
+    bytes_step = Bs * H * per_seqhead
+    kern_s = dec_ms / dec_n / 1e3
+    res = dict(workload="decode", Bs=Bs, H=H, cached_chunks=n_cap, steps=steps, ms_per_step=dt * 1e3,
+               tokens_per_s=Bs / dt, hbm_gbs=bytes_step / kern_s / 1e9,
+               roofline=dict(kernel="decode_kernel", bound="hbm", achieved=round(bytes_step / kern_s / 1e9, 1),
+                             peak=PEAK_HBM_GBS, unit="GB/s", frac=round(bytes_step / kern_s / 1e9 / PEAK_HBM_GBS, 4),
+                             bytes_per_launch=bytes_step, avg_launch_ms=round(kern_s * 1e3, 4)),
+               note="no commit while timing; live chunk extends past 64 tokens so every step does the same work")
+    log(f"[decode] {dt*1e3:.3f} ms/step, {Bs/dt:.0f} tok/s, kernel {kern_s*1e3:.3f} ms, "
+        f"{bytes_step/kern_s/1e9:.0f} GB/s")
+    del At_cache, Bc_cache, reps, S, A, toks
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- native prefill
+def bench_native_prefill(args, torch, hla, inputs):
+    W = inputs.WORKLOADS["native_prefill"]
+    x = inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["native_prefill"])
+    q, k, v = (to_dev(a, W.dtype, torch) for a in (x.q, x.k, x.v))
+    beta, alpha = to_dev(x.beta, "f32", torch), to_dev(x.alpha, "f32", torch)
+    d = hla.make_dims(W.B, W.T, W.H, W.T, W.dk, W.dv, hla.HLA_BF16)
+    ws = torch.empty(hla.workspace_bytes(hla.FN_GDN_PREFILL, d), dtype=torch.uint8, device="cuda")
+    o = torch.empty((W.B, W.T, W.H, W.dv), dtype=torch.float32, device="cuda")
+    S = torch.empty((W.B, W.H, W.dk, W.dv), dtype=torch.float32, device="cuda")
+    dt = timed(lambda: hla.gdn_prefill(q, k, v, beta, alpha, o=o, S_final=S, ws=ws), 20, 3, torch)
+    bytes_alg = W.B * W.T * W.H * (2 * W.dk * 2 + W.dv * 2 + 2 * 4 + W.dv * 4) + W.B * W.H * W.dk * W.dv * 4
+    res = dict(workload="native_prefill", B=W.B, T=W.T, H=W.H, ms_per_step=dt * 1e3, tokens_per_s=W.B * W.T / dt,
+               algorithmic_gbs=bytes_alg / dt / 1e9, hbm_frac=round(bytes_alg / dt / 1e9 / PEAK_HBM_GBS, 4))
+    log(f"[native_prefill] {dt*1e3:.3f} ms, {W.B*W.T/dt/1e6:.2f} M tok/s, {bytes_alg/dt/1e9:.0f} GB/s algorithmic")
+    return res
+
+
+# ----------------------------------------------------------------------------- Tail-Replay
+def bench_tail_replay(args, torch, hla, inputs):
+    W = inputs.WORKLOADS["tail_replay"]
+    L = W.replay
+    log(f"[tail_replay] generating B={W.B} T={W.T} H={W.H} (replay {L})")
+    x = inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["tail_replay"],
+                          with_q=False)
+    k, v = to_dev(x.k, W.dtype, torch), to_dev(x.v, W.dtype, torch)
+    beta, alpha = to_dev(x.beta, "f32", torch), to_dev(x.alpha, "f32", torch)
+    del x
+    ks, vs, bs, als = k[:, -L:], v[:, -L:], beta[:, -L:], alpha[:, -L:]
+    S = torch.empty((W.B, W.H, W.dk, W.dv), dtype=torch.float32, device="cuda")
+    d_rep = hla.make_dims(W.B, L, W.H, W.T, W.dk, W.dv, hla.HLA_BF16)
+    ws_rep = torch.empty(hla.workspace_bytes(hla.FN_GDN_PREFILL, d_rep), dtype=torch.uint8, device="cuda")
+    dt_rep = timed(lambda: hla.gdn_prefill(None, ks, vs, bs, als, want_o=False, S_final=S, ws=ws_rep), 20, 3, torch)
+    d_full = hla.make_dims(W.B, W.T, W.H, W.T, W.dk, W.dv, hla.HLA_BF16)
+    ws_full = torch.empty(hla.workspace_bytes(hla.FN_GDN_PREFILL, d_full), dtype=torch.uint8, device="cuda")
+    S2 = torch.empty_like(S)
+    dt_full = timed(lambda: hla.gdn_prefill(None, k, v, beta, alpha, want_o=False, S_final=S2, ws=ws_full), 5, 1, torch)
+    res = dict(workload="tail_replay", B=W.B, H=W.H, prefix=W.T, replay=L, ms_replay=dt_rep * 1e3,
+               ms_full_prefix_state=dt_full * 1e3, speedup_vs_full=dt_full / dt_rep,
+               replay_tokens_per_s=W.B * L / dt_rep)
+    log(f"[tail_replay] replay {dt_rep*1e3:.3f} ms vs full-prefix state {dt_full*1e3:.3f} ms "
+        f"({dt_full/dt_rep:.1f}x)")
+    del k, v, beta, alpha, ws_rep, ws_full
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- CPU oracle
+def cpu_baseline(x, n_query_chunks):
+    """The oracle (as is) on the routed prefill of the first n_query_chunks chunks of head 0,
+    each stage extrapolated to the full workload by its own work ratio."""
+    import numpy as np
+
+    import oracle
+    from gated_deltanet_hybrid_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    W = inputs.WORKLOADS["routed_prefill"]
+    Tn = n_query_chunks * C
+    q, k, v = (x.f64(n)[0, :Tn, 0] for n in ("q", "k", "v"))
+    beta, alpha = x.f64("beta")[0, :Tn, 0], x.f64("alpha")[0, :Tn, 0]
+    t0 = time.perf_counter()
+    A, B = oracle.chunk_transitions(k, v, beta, alpha, C)
+    t1 = time.perf_counter()
+    r = oracle.router_gates(q, k, C, C, W.tau)
+    t2 = time.perf_counter()
+    S = oracle.routed_states(A, B, r["ghat"], r["mask"])
+    t3 = time.perf_counter()
+    oracle.routed_outputs(q, k, v, beta, alpha, C, S)
+    t4 = time.perf_counter()
+    N = W.N
+    pairs_s, pairs_f = n_query_chunks * (n_query_chunks - 1) / 2, N * (N - 1) / 2
+    per_head = ((t1 - t0) * N / n_query_chunks + (t2 - t1) * pairs_f / pairs_s + (t3 - t2) * pairs_f / pairs_s
+                + (t4 - t3) * N / n_query_chunks)
+    full = per_head * W.H * W.B
+    return dict(value=W.B * W.T / full, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"routed prefill of the first {Tn} tokens ({n_query_chunks} chunks) of head 0, "
+                       f"{t4 - t0:.1f} s; stages extrapolated to B={W.B}, H={W.H}, T={W.T} by chunk count "
+                       f"(transitions, outputs) or chunk-pair count (gates, composition)",
+                sample_seconds=round(t4 - t0, 2), extrapolated_seconds=round(full, 1),
+                host_cpus=os.cpu_count())
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=512)
+    ap.add_argument("--no-secondary", action="store_true", help="only the headline routed prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oracle-chunks", type=int, default=512, help="query chunks of the oracle sample (512 = all of head 0)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: every (batch, head) of this path is independent, so --gpus {args.gpus} "
+              "would only shard heads without communication; only --gpus 1 is measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_deltanet_hybrid_amd import hla, inputs
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    hla.library()
+    torch.cuda.set_device(0)
+
+    head, x = bench_routed_prefill(args, torch, hla, inputs)
+    secondary = {}
+    if not args.no_secondary:
+        secondary["decode"] = bench_decode(args, torch, hla, inputs)
+        secondary["native_prefill"] = bench_native_prefill(args, torch, hla, inputs)
+        secondary["tail_replay"] = bench_tail_replay(args, torch, hla, inputs)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[cpu_baseline] oracle on {args.oracle_chunks} chunks of one head")
+        cpu = cpu_baseline(x, args.oracle_chunks)
+        log(f"[cpu_baseline] {cpu['value']:.1f} tokens/s (sample {cpu['sample_seconds']} s)")
+
+    W = inputs.WORKLOADS["routed_prefill"]
+    line = {
+        "metric": METRIC,
+        "value": round(head["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "routed_prefill (GDN + HLA, T=32K)", "B": W.B, "T": W.T, "H": W.H, "dk": W.dk,
+                   "dv": W.dv, "C": W.C, "tau": W.tau, "parallelism": "single GPU"},
+        "mfma_util_pct": round(head["mfma_util_pct"], 2),
+        "step_tflops": round(head["step_tflops"], 1),
+        "kernel_ms": head["kernel_ms"],
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,6 +18,7 @@
 // hi + lo parts so W and U keep ~16 mantissa bits.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "timing.hpp"
 
 namespace hla {
 
@@ -369,6 +370,7 @@ template <class T, int DK, int DV, bool WANT_AB, bool WANT_O>
 static hipError_t launch_chunk_t(const ChunkArgs& a, int64_t nblocks, hipStream_t s) {
   constexpr int NCT = (DK + DV) / 32;
   constexpr int NW = NCT >= 8 ? 8 : 4;
+  TimedLaunch tl(HLA_KERNEL_CHUNK, s);
   hipLaunchKernelGGL((chunk_kernel<T, DK, DV, NW, WANT_AB, WANT_O>), dim3((unsigned)nblocks), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }

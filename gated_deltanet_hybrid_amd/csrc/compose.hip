@@ -26,6 +26,7 @@
 //     together sweep the same history chunks of the same heads (L2 reuse of At_j, Bc_j).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "timing.hpp"
 
 namespace hla {
 
@@ -263,6 +264,7 @@ static hipError_t launch_compose_bf16_t(const RouteArgs& a, hipStream_t s) {
   constexpr int QG = NW * SPW / (DV / 32);
   const int64_t ng = (a.N + QG - 1) / QG;
   const int64_t nb = ng * a.B * a.H;
+  TimedLaunch tl(HLA_KERNEL_COMPOSE, s);
   hipLaunchKernelGGL((compose_bf16_kernel<DK, DV, NW, SPW, NBUF>), dim3((unsigned)nb), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }

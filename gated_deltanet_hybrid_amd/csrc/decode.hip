@@ -16,6 +16,7 @@
 // [HLA] Methodology paragraph 4).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "timing.hpp"
 
 namespace hla {
 
@@ -286,7 +287,10 @@ template <class T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const int64_t nb = a.Bs * a.H;
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)nb), dim3(256), 0, s, a);
+  {
+    TimedLaunch tl(HLA_KERNEL_DECODE, s);
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)nb), dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(a.commit && a.At_cur)) return e;
   hipLaunchKernelGGL(advance_cache_kernel, dim3((unsigned)((a.Bs + 255) / 256)), dim3(256), 0, s, a.n_cache,

@@ -12,6 +12,7 @@
 // core as a bf16 operand, and g Bc_j is one more MFMA against g I.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "timing.hpp"
 
 namespace hla {
 
@@ -321,6 +322,7 @@ static hipError_t launch_compose_t(const RouteArgs& a, hipStream_t s) {
   constexpr int QG = 8 / (DV / 32);
   const int64_t ng = (a.N + QG - 1) / QG;
   const int64_t nb = ng * a.B * a.H;
+  TimedLaunch tl(HLA_KERNEL_COMPOSE, s);
   hipLaunchKernelGGL((compose_kernel<T, DK, DV, NBUF>), dim3((unsigned)nb), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -329,12 +331,15 @@ template <class T, int DK, int DV>
 static hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
   const int64_t BH = a.B * a.H;
   if (BH == 0 || a.N == 0) return hipSuccess;
-  if (!a.gates_in && a.N > 1) {
-    hipLaunchKernelGGL((qbar_kernel<T, DK>), dim3((unsigned)(BH * a.N)), dim3(DK), 0, s, a);
-    const int64_t nqt = (a.N + 31) / 32, njs = (a.N + 63) / 64;
-    hipLaunchKernelGGL((gate_kernel<T, DK>), dim3((unsigned)(BH * nqt * njs)), dim3(256), 0, s, a);
+  {
+    TimedLaunch tl(HLA_KERNEL_GATES, s);
+    if (!a.gates_in && a.N > 1) {
+      hipLaunchKernelGGL((qbar_kernel<T, DK>), dim3((unsigned)(BH * a.N)), dim3(DK), 0, s, a);
+      const int64_t nqt = (a.N + 31) / 32, njs = (a.N + 63) / 64;
+      hipLaunchKernelGGL((gate_kernel<T, DK>), dim3((unsigned)(BH * nqt * njs)), dim3(256), 0, s, a);
+    }
+    hipLaunchKernelGGL(lists_kernel, dim3((unsigned)(BH * a.N)), dim3(64), 0, s, a);
   }
-  hipLaunchKernelGGL(lists_kernel, dim3((unsigned)(BH * a.N)), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (sizeof(T) == 2) return launch_compose_bf16(a, DK, DV, s);

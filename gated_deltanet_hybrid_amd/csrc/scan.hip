@@ -11,6 +11,7 @@
 // At and Bc are prefetched into registers while the current chunk computes.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "timing.hpp"
 
 namespace hla {
 
@@ -136,6 +137,7 @@ static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
   constexpr bool PF = (NA + NB) <= 48;
   const int64_t nb = a.B * a.H * (DV / 32);
   if (nb == 0) return hipSuccess;
+  TimedLaunch tl(HLA_KERNEL_SCAN, s);
   hipLaunchKernelGGL((scan_kernel<T, DK, DV, PF>), dim3((unsigned)nb), dim3(64), 0, s, a);
   return hipGetLastError();
 }

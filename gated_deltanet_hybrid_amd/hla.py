@@ -17,6 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhla.so"
 _lib = None
 
 HLA_F32, HLA_BF16 = 0, 1
+KERNEL_CHUNK, KERNEL_SCAN, KERNEL_GATES, KERNEL_COMPOSE, KERNEL_DECODE = 0, 1, 2, 3, 4
 FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX = 0, 1, 2
 CHUNK = 64
 MAX_CACHE_SLOTS = 1024
@@ -44,6 +45,8 @@ _SIGS = {
                                          ctypes.c_size_t, _P]),
     "hla_route_mix": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
                                        _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "hla_timing_enable": (ctypes.c_int32, [ctypes.c_int32]),
+    "hla_timing_read": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "hla_gdn_decode": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
                                         ctypes.c_int32, _P, ctypes.c_float, _P, _P, ctypes.c_int32, _P]),
@@ -267,3 +270,15 @@ def gdn_decode(q, k, v, beta, alpha, S_cur, At_cur=None, At_cache=None, Bc_cache
                                     n_rep, _ptr(n_cache), n_cap, _ptr(gates_in), ctypes.c_float(tau), _ptr(o),
                                     _ptr(gates_out), 1 if commit else 0, _stream(dev)), "hla_gdn_decode")
     return o
+
+
+def timing_enable(on: bool = True) -> None:
+    """Start (or stop) per-kernel HIP-event timing inside the library; clears records."""
+    _check(library().hla_timing_enable(1 if on else 0), "hla_timing_enable")
+
+
+def timing_read(which: int) -> tuple[float, int]:
+    """(summed milliseconds, launches) of one kernel kind since timing_enable()."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(library().hla_timing_read(which, ctypes.byref(ms), ctypes.byref(n)), "hla_timing_read")
+    return ms.value, n.value

@@ -191,6 +191,27 @@ hla_status_t hla_gdn_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32
  * HLA_FN_ROUTE_MIX).  `out` is a host pointer. */
 hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep, size_t* out);
 
+/* Kernel kinds that hla_timing_read() reports. */
+typedef enum {
+  HLA_KERNEL_CHUNK = 0,    /* per-chunk UT kernel (transitions, chunk outputs)        */
+  HLA_KERNEL_SCAN = 1,     /* sequential chunk scan of the native prefill             */
+  HLA_KERNEL_GATES = 2,    /* router: query-chunk means, gate scores, mask and lists  */
+  HLA_KERNEL_COMPOSE = 3,  /* gated composition of chunk transitions                  */
+  HLA_KERNEL_DECODE = 4,   /* single-token decode step                                */
+  HLA_KERNEL_COUNT = 5
+} hla_kernel_t;
+
+/*
+ * Optional per-kernel timing (profiling aid; off by default).  hla_timing_enable(1) clears
+ * earlier records and starts bracketing every launch of the kernels above with two HIP
+ * events recorded on that launch's own stream; hla_timing_enable(0) stops and clears.
+ * hla_timing_read() waits for the recorded events of one kernel kind and returns the
+ * summed elapsed milliseconds and the number of launches (host pointers).  Timing is
+ * process-global: enable it only while one thread issues work.
+ */
+hla_status_t hla_timing_enable(int32_t on);
+hla_status_t hla_timing_read(int32_t which, double* total_ms, int64_t* launches);
+
 /* Static description of a status code (never NULL). */
 const char* hla_status_string(int32_t status);
 
