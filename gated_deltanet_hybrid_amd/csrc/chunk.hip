@@ -45,7 +45,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) char sm1[R1];
   __shared__ __attribute__((aligned(16))) char sm2[R2];
   __shared__ __attribute__((aligned(16))) char sm3[R3];
-  __shared__ float s_beta[C], s_bg[C], s_g[C], s_gam[C], s_D[C];
+  __shared__ float s_beta[C], s_g[C], s_gam[C];
 
   T* Kp = reinterpret_cast<T*>(sm1);
   T* Qp = Kp + C * PK;
@@ -107,13 +107,9 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
         const float y = __shfl_up(x, off, 64);
         if (lane >= off) x += y;
       }
-      const float gn = __shfl(x, 63, 64);
-      const float gam = expf(x);
       s_beta[tid] = bt;
-      s_bg[tid] = bt * gam;
       s_g[tid] = x;
-      s_gam[tid] = gam;
-      s_D[tid] = expf(gn - x);
+      s_gam[tid] = expf(x);
     }
   }
   __syncthreads();
@@ -219,7 +215,6 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
     const bool isw = ct * 32 < DK;
     const int col0 = isw ? ct * 32 : ct * 32 - DK;
     const T* brow = (isw ? KT : VT) + (col0 + c32) * PT;
-    const float* scale = isw ? s_bg : s_beta;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       f32x16 acc = zero16();
@@ -232,7 +227,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int s = ks * 16 + hh * 8 + e;
-            const float x = xrow[s] * scale[s];
+            const float x = xrow[s] * (isw ? s_beta[s] * s_gam[s] : s_beta[s]);
             const bf16 hv = (bf16)x;
             ahi[e] = hv;
             alo[e] = (bf16)(x - (float)hv);
@@ -241,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
           acc = MM::mma(alo, bf, acc);
         } else {
           const int s = ks * 2 + hh;
-          acc = MM::mma(xrow[s] * scale[s], bf, acc);
+          acc = MM::mma(xrow[s] * (isw ? s_beta[s] * s_gam[s] : s_beta[s]), bf, acc);
         }
       }
       wu[sl][tt] = acc;
@@ -250,7 +245,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
 
   // ---- 5. transitions: At = gamma_63 I - K^T D W,  Bc = K^T D U
   if constexpr (WANT_AB) {
-    const float gam_n = s_gam[C - 1];
+    const float gam_n = s_gam[C - 1], g_n = s_g[C - 1];
     const int64_t cidx = (b * a.H + h) * a.N + c;
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
@@ -267,12 +262,12 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int ai = (ks & 1) * 8 + e;
-            f[e] = (bf16)(wu[sl][tt][ai] * s_D[tt * 32 + acc_row(ai, hh)]);
+            f[e] = (bf16)(wu[sl][tt][ai] * expf(g_n - s_g[tt * 32 + acc_row(ai, hh)]));
           }
           bfr[ks] = f;
         } else {
           const int ai = ks & 15;
-          bfr[ks] = wu[sl][tt][ai] * s_D[tt * 32 + acc_row(ai, hh)];
+          bfr[ks] = wu[sl][tt][ai] * expf(g_n - s_g[tt * 32 + acc_row(ai, hh)]);
         }
       }
       T* out = isw ? reinterpret_cast<T*>(a.At) + cidx * DK * DK : reinterpret_cast<T*>(a.Bc) + cidx * DK * DV;

@@ -55,8 +55,8 @@ __global__ __launch_bounds__(256) void prep_at_kernel(const bf16* __restrict__ A
   *reinterpret_cast<bf16x8*>(Ap + u * 8) = o;
 }
 
-template <int DK, int DV, int NW, int SPW, int NBUF>
-__global__ __launch_bounds__(NW * 64, NBUF == 1 ? 2 : 1) void compose_bf16_kernel(RouteArgs a) {
+template <int DK, int DV, int NW, int SPW, int NBUF, bool BCG>
+__global__ __launch_bounds__(NW * 64, (NBUF == 1 || BCG) ? 2 : 1) void compose_bf16_kernel(RouteArgs a) {
   constexpr int NCTV = DV / 32;
   constexpr int QG = NW * SPW / NCTV;
   constexpr int NRT = DK / 32, NKS = DK / 16;
@@ -65,10 +65,12 @@ __global__ __launch_bounds__(NW * 64, NBUF == 1 ? 2 : 1) void compose_bf16_kerne
   // Two separate LDS variables (not one array indexed by the step parity): the copy into
   // one buffer can then be proven not to alias reads of the other, so the compiler does
   // not wait for the copy before the multiplications that overlap it.
+  // BCG: Bc fragments come from global memory into registers (prefetched one history
+  // chunk ahead) and only At is staged in LDS, halving the LDS of a workgroup.
   __shared__ __attribute__((aligned(16))) bf16 sA0[DK * DK];
-  __shared__ __attribute__((aligned(16))) bf16 sB0[DK * DV];
+  __shared__ __attribute__((aligned(16))) bf16 sB0[BCG ? 8 : DK * DV];
   __shared__ __attribute__((aligned(16))) bf16 sA1[NBUF == 2 ? DK * DK : 8];
-  __shared__ __attribute__((aligned(16))) bf16 sB1[NBUF == 2 ? DK * DV : 8];
+  __shared__ __attribute__((aligned(16))) bf16 sB1[(NBUF == 2 && !BCG) ? DK * DV : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, c32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -112,10 +114,22 @@ __global__ __launch_bounds__(NW * 64, NBUF == 1 ? 2 : 1) void compose_bf16_kerne
     for (int m = 0; m < NIA / NW; ++m)
       __builtin_amdgcn_global_load_lds(as + (uint32_t)((offA + m * NW * 512) * 2), (lds_void_t*)&dA[(w + m * NW) * 512],
                                        16, 0, 0);
+    if constexpr (!BCG) {
 #pragma unroll
-    for (int m = 0; m < NIB / NW; ++m)
-      __builtin_amdgcn_global_load_lds(bs + (uint32_t)((offB + m * NW * 512) * 2), (lds_void_t*)&dB[(w + m * NW) * 512],
-                                       16, 0, 0);
+      for (int m = 0; m < NIB / NW; ++m)
+        __builtin_amdgcn_global_load_lds(bs + (uint32_t)((offB + m * NW * 512) * 2),
+                                         (lds_void_t*)&dB[(w + m * NW) * 512], 16, 0, 0);
+    }
+  };
+  // Bc A fragments of history chunk j straight from global memory: row rt*32 + c32,
+  // the 8 columns ct*32 + kd*16 + hh*8 ..
+  bf16x8 bcf[NRT][2];
+  auto load_bc = [&](int j) {
+    const bf16* bs = Bg + (int64_t)j * DK * DV + c32 * DV + ct * 32 + hh * 8;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int kd = 0; kd < 2; ++kd) bcf[rt][kd] = *reinterpret_cast<const bf16x8*>(bs + rt * 32 * DV + kd * 16);
   };
   auto wait_copies = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -191,6 +205,7 @@ __global__ __launch_bounds__(NW * 64, NBUF == 1 ? 2 : 1) void compose_bf16_kerne
       any |= (g[s] != 0.f);
     }
     if (NBUF == 2 && j + 1 < nsteps) issue(j + 1, nA, nB);
+    if (BCG && !any && j + 1 < nsteps) load_bc(j + 1);
     if (any) {
       // B operand bf16(g M) straight from the accumulator rows this lane holds
       bf16x8 bfr[SPW][NKS];
@@ -198,6 +213,26 @@ __global__ __launch_bounds__(NW * 64, NBUF == 1 ? 2 : 1) void compose_bf16_kerne
       for (int s = 0; s < SPW; ++s)
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) bfr[s][ks] = Mma<bf16>::from_acc(M[s][ks >> 1], ks, g[s]);
+      if constexpr (BCG) {
+#pragma unroll
+        for (int kd = 0; kd < 2; ++kd) {
+          bf16x8 dg[SPW];
+#pragma unroll
+          for (int s = 0; s < SPW; ++s) {
+            const uint32_t gb = (uint32_t)__builtin_bit_cast(unsigned short, (bf16)g[s]);
+            const uint32_t g2 = gb | (gb << 16);
+            uint32_t d4[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) d4[d] = pat[kd][d] & g2;
+            dg[s] = __builtin_bit_cast(bf16x8, d4);
+          }
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) M[s][rt] = Mma<bf16>::mma(bcf[rt][kd], dg[s], M[s][rt]);
+        }
+      }
+      if (BCG && j + 1 < nsteps) load_bc(j + 1);  // bcf was consumed at issue above
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -209,6 +244,7 @@ __global__ __launch_bounds__(NW * 64, NBUF == 1 ? 2 : 1) void compose_bf16_kerne
           for (int s = 0; s < SPW; ++s) M[s][rt] = Mma<bf16>::mma(af, bfr[s][ks], M[s][rt]);
         }
       }
+if constexpr (!BCG) {
 #pragma unroll
       for (int kd = 0; kd < 2; ++kd) {
         bf16x8 dg[SPW];
@@ -230,6 +266,7 @@ __global__ __launch_bounds__(NW * 64, NBUF == 1 ? 2 : 1) void compose_bf16_kerne
           for (int s = 0; s < SPW; ++s) M[s][rt] = Mma<bf16>::mma(af, dg[s], M[s][rt]);
         }
       }
+}
     }
 #pragma unroll
     for (int s = 0; s < SPW; ++s)
@@ -246,6 +283,7 @@ __global__ __launch_bounds__(NW * 64, NBUF == 1 ? 2 : 1) void compose_bf16_kerne
 
   if (nsteps > 0) {
     issue(0, sA0, sB0);
+    if constexpr (BCG) load_bc(0);
     wait_copies();
     __syncthreads();
   }
@@ -259,13 +297,13 @@ __global__ __launch_bounds__(NW * 64, NBUF == 1 ? 2 : 1) void compose_bf16_kerne
   }
 }
 
-template <int DK, int DV, int NW, int SPW, int NBUF>
+template <int DK, int DV, int NW, int SPW, int NBUF, bool BCG>
 static hipError_t launch_compose_bf16_t(const RouteArgs& a, hipStream_t s) {
   constexpr int QG = NW * SPW / (DV / 32);
   const int64_t ng = (a.N + QG - 1) / QG;
   const int64_t nb = ng * a.B * a.H;
   TimedLaunch tl(HLA_KERNEL_COMPOSE, s);
-  hipLaunchKernelGGL((compose_bf16_kernel<DK, DV, NW, SPW, NBUF>), dim3((unsigned)nb), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((compose_bf16_kernel<DK, DV, NW, SPW, NBUF, BCG>), dim3((unsigned)nb), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -283,7 +321,7 @@ hipError_t launch_compose_bf16(const RouteArgs& a, int dk, int dv, hipStream_t s
     if (e != hipSuccess) return e;
   }
 #ifndef HLA_COMPOSE_SHAPE
-#define HLA_COMPOSE_SHAPE 8, 2, 2
+#define HLA_COMPOSE_SHAPE 8, 2, 2, false
 #endif
   if (dk == 64 && dv == 64) return launch_compose_bf16_t<64, 64, HLA_COMPOSE_SHAPE>(a, s);
   if (dk == 64 && dv == 128) return launch_compose_bf16_t<64, 128, HLA_COMPOSE_SHAPE>(a, s);

@@ -17,41 +17,71 @@
 namespace hla {
 
 // ---------------------------------------------------------------- query-chunk means
+// One 256-thread workgroup per (b, h, chunk i): 16 token groups x 16 lanes of 16 bytes.
 template <class T, int DK>
-__global__ __launch_bounds__(DK) void qbar_kernel(RouteArgs a) {
+__global__ __launch_bounds__(256) void qbar_kernel(RouteArgs a) {
+  constexpr int PAD = 16 / sizeof(T), UPR = DK / PAD;  // 16-byte units per token row
+  constexpr int TG = 256 / UPR;                        // token groups
+  __shared__ float part[TG][DK];
   const int64_t id = blockIdx.x;  // (b, h, i)
   const int i = (int)(id % a.N);
   const int64_t bh = id / a.N, h = bh % a.H, b = bh / a.H;
   const int64_t t0 = (int64_t)i * kChunk;
   const int n = (int)((a.T - t0) < kChunk ? (a.T - t0) : kChunk);
-  const T* q = reinterpret_cast<const T*>(a.q) + ((b * a.ld_T + t0) * a.H + h) * DK + threadIdx.x;
-  float s = 0.f;
-  for (int t = 0; t < n; ++t) s += to_f<T>(q[(int64_t)t * a.H * DK]);
-  a.qbar[id * DK + threadIdx.x] = s / (float)n;
+  const int u = threadIdx.x % UPR, tg = threadIdx.x / UPR;
+  const T* q = reinterpret_cast<const T*>(a.q) + ((b * a.ld_T + t0) * a.H + h) * DK + u * PAD;
+  float acc[PAD];
+#pragma unroll
+  for (int e = 0; e < PAD; ++e) acc[e] = 0.f;
+  for (int t = tg; t < n; t += TG) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(q + (int64_t)t * a.H * DK);
+    const T* ev = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < PAD; ++e) acc[e] += to_f<T>(ev[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < PAD; ++e) part[tg][u * PAD + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < DK) {
+    float s = 0.f;
+    for (int g = 0; g < TG; ++g) s += part[g][threadIdx.x];
+    a.qbar[id * DK + threadIdx.x] = s / (float)n;
+  }
 }
 
 // ---------------------------------------------------------------- gate scores
-// Workgroup = (b, h, 32-query tile, segment of 64 history chunks); each wave scores 16
-// history chunks against the 32 query-chunk means.  Keys are the MFMA rows, queries the
-// columns, so the pooling over a chunk's representatives is lane-local plus one
-// cross-half exchange.
+// Workgroup = (b, h, segment of 64 history chunks, group of 4 query tiles of 32 chunks);
+// wave w scores query tile 4 g + w.  Each history chunk's representatives (the MFMA rows)
+// are staged once in LDS with coalesced loads and shared by the four waves; the next
+// chunk's rows are prefetched into registers while the current one is scored.  Queries
+// are the columns, so pooling over representatives is lane-local plus one exchange
+// between the lane halves.
 template <class T, int DK>
 __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
   using MM = Mma<T>;
   constexpr int JSEG = 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, c32 = lane & 31;
-  const int nqt = (a.N + 31) / 32, njs = (a.N + JSEG - 1) / JSEG;
+  constexpr int PAD = 16 / sizeof(T), UPR = DK / PAD;
+  constexpr int RT = 32;                  // representatives staged per round
+  constexpr int PR = DK + PAD;            // LDS row pitch (elements)
+  constexpr int NU = RT * UPR / 256;      // 16-byte units per thread per round
+  static_assert(NU >= 1 && (RT * UPR) % 256 == 0, "staging split");
+  __shared__ __attribute__((aligned(16))) T sR[2][RT * PR];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, c32 = lane & 31;
+  const int nqt = (a.N + 31) / 32, nqg = (nqt + 3) / 4, njs = (a.N + JSEG - 1) / JSEG;
   int64_t id = blockIdx.x;
   const int js = (int)(id % njs);
   id /= njs;
-  const int qt = (int)(id % nqt);
-  const int64_t bh = id / nqt, h = bh % a.H, b = bh / a.H;
-  const int i_max = qt * 32 + 31 < a.N - 1 ? qt * 32 + 31 : a.N - 1;
-  const int j_lo = js * JSEG;
-  if (j_lo >= i_max) return;  // every j in this segment is >= every query in the tile
-
-  // B operand: query-chunk means (fp32 split into bf16 hi + lo for the bf16 path)
+  const int qg = (int)(id % nqg);
+  const int64_t bh = id / nqg, h = bh % a.H, b = bh / a.H;
+  const int qt = qg * 4 + w;
   const int qi = qt * 32 + c32;
+  const int grp_imax = (qg * 4 + 3) * 32 + 31 < a.N - 1 ? (qg * 4 + 3) * 32 + 31 : a.N - 1;
+  const int wave_imax = qt * 32 + 31 < a.N - 1 ? qt * 32 + 31 : a.N - 1;
+  const int j_lo = js * JSEG;
+  const int j_hi = (j_lo + JSEG < grp_imax ? j_lo + JSEG : grp_imax);  // exclusive; j < i <= grp_imax
+  if (j_lo >= j_hi) return;
+
+  // B operand: query-chunk means (fp32 split into bf16 hi + lo on the bf16 path)
   const float* qb = a.qbar + (bh * a.N + (qi < a.N ? qi : 0)) * DK;
   constexpr int NKS = DK / MM::KS;
   typename MM::Frag bhi[NKS], blo[NKS];
@@ -74,29 +104,52 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
     }
   }
   const float scale = 1.f / sqrtf((float)DK);
-  const int nkt = (a.n_rep + 31) / 32;
   const T* reps = reinterpret_cast<const T*>(a.reps);
-  for (int jj = 0; jj < JSEG / 4; ++jj) {
-    const int j = j_lo + w * (JSEG / 4) + jj;
-    if (j >= i_max || j >= a.N - 1) break;
-    // streaming log-mean-exp over the representatives this lane holds (rows of the tile)
-    float m = -INFINITY, ssum = 0.f;
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int r = kt * 32 + c32;
-      const bool valid = r < a.n_rep;
-      const T* arow = reps + ((b * a.ld_R + (int64_t)j * a.n_rep + (valid ? r : 0)) * a.H + h) * DK;
+  const int nkt = (a.n_rep + RT - 1) / RT;
+  // rounds = (history chunk, key tile of 32 representatives), staged in order
+  const int nrounds = (j_hi - j_lo) * nkt;
+  uint4 pf[NU];
+  auto load_round = [&](int rd) {
+    const int j = j_lo + rd / nkt, kt = rd % nkt;
+#pragma unroll
+    for (int m = 0; m < NU; ++m) {
+      const int uu = tid + 256 * m, r = uu / UPR, cu = uu % UPR;
+      const int rr = kt * RT + r;
+      pf[m] = make_uint4(0u, 0u, 0u, 0u);
+      if (rr < a.n_rep)
+        pf[m] = *reinterpret_cast<const uint4*>(reps + ((b * a.ld_R + (int64_t)j * a.n_rep + rr) * a.H + h) * DK +
+                                                cu * PAD);
+    }
+  };
+  auto store_round = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < NU; ++m) {
+      const int uu = tid + 256 * m, r = uu / UPR, cu = uu % UPR;
+      *reinterpret_cast<uint4*>(&sR[buf][r * PR + cu * PAD]) = pf[m];
+    }
+  };
+  load_round(0);
+  store_round(0);
+  __syncthreads();
+  float m = -INFINITY, ssum = 0.f;
+  for (int rd = 0; rd < nrounds; ++rd) {
+    const int buf = rd & 1;
+    const int j = j_lo + rd / nkt, kt = rd % nkt;
+    if (rd + 1 < nrounds) load_round(rd + 1);
+    if (j < wave_imax) {
+      const T* arow = &sR[buf][c32 * PR];
       f32x16 acc = zero16();
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        typename MM::Frag af = MM::load_plain(arow, ks, hh);
-        if (!valid) af = typename MM::Frag{};
+        const auto af = MM::load_plain(arow, ks, hh);
         acc = MM::mma(af, bhi[ks], acc);
         if constexpr (sizeof(T) == 2) acc = MM::mma(af, blo[ks], acc);
       }
+      // streaming log-mean-exp over the representatives this lane holds
       float sv[16], tmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int rr = kt * 32 + acc_row(e, hh);
+        const int rr = kt * RT + acc_row(e, hh);
         sv[e] = rr < a.n_rep ? acc[e] * scale : -INFINITY;
         tmax = fmaxf(tmax, sv[e]);
       }
@@ -108,14 +161,22 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
         ssum = (m > -INFINITY ? ssum * __expf(m - mn) : 0.f) + add;
         m = mn;
       }
+      if (kt == nkt - 1) {
+        // the other lane half holds the remaining rows of the same query column
+        const float mo = __shfl_xor(m, 32, 64), so = __shfl_xor(ssum, 32, 64);
+        const float mall = fmaxf(m, mo);
+        const float stot = (m > -INFINITY ? ssum * __expf(m - mall) : 0.f) + (mo > -INFINITY ? so * __expf(mo - mall) : 0.f);
+        const float l = mall + logf(stot / (float)a.n_rep);
+        const float g = 1.f / (1.f + expf(-l));
+        if (hh == 0 && qi < a.N && j < qi) a.gates[(bh * a.N + qi) * a.N + j] = g;
+        m = -INFINITY;
+        ssum = 0.f;
+      }
     }
-    // the other lane half holds the remaining rows of the same query column
-    const float mo = __shfl_xor(m, 32, 64), so = __shfl_xor(ssum, 32, 64);
-    const float mall = fmaxf(m, mo);
-    const float stot = (m > -INFINITY ? ssum * __expf(m - mall) : 0.f) + (mo > -INFINITY ? so * __expf(mo - mall) : 0.f);
-    const float l = mall + logf(stot / (float)a.n_rep);
-    const float g = 1.f / (1.f + expf(-l));
-    if (hh == 0 && qi < a.N && j < qi) a.gates[(bh * a.N + qi) * a.N + j] = g;
+    if (rd + 1 < nrounds) {
+      store_round(buf ^ 1);
+      __syncthreads();
+    }
   }
 }
 
@@ -334,9 +395,9 @@ static hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
   {
     TimedLaunch tl(HLA_KERNEL_GATES, s);
     if (!a.gates_in && a.N > 1) {
-      hipLaunchKernelGGL((qbar_kernel<T, DK>), dim3((unsigned)(BH * a.N)), dim3(DK), 0, s, a);
-      const int64_t nqt = (a.N + 31) / 32, njs = (a.N + 63) / 64;
-      hipLaunchKernelGGL((gate_kernel<T, DK>), dim3((unsigned)(BH * nqt * njs)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((qbar_kernel<T, DK>), dim3((unsigned)(BH * a.N)), dim3(256), 0, s, a);
+      const int64_t nqt = (a.N + 31) / 32, nqg = (nqt + 3) / 4, njs = (a.N + 63) / 64;
+      hipLaunchKernelGGL((gate_kernel<T, DK>), dim3((unsigned)(BH * nqg * njs)), dim3(256), 0, s, a);
     }
     hipLaunchKernelGGL(lists_kernel, dim3((unsigned)(BH * a.N)), dim3(64), 0, s, a);
   }
