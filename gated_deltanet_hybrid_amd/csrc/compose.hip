@@ -14,12 +14,12 @@
 //     without leaving the lane (the k order of the accumulator rows is matched by how At
 //     is read);
 //   * g Bc_j is one more pair of MFMAs per row tile: Bc_j as the A operand against g I;
-//   * (At_j, Bc_j) of the next history chunk are copied global -> LDS asynchronously
-//     (global_load_lds, 16 bytes per lane) while the current one is multiplied; the LDS
-//     rows are XOR-swizzled in 16-byte units so fragment reads are bank-conflict free;
-//   * a prep pass writes (At_j - I) with each 16-wide k block reordered so that one lane's
-//     8 k values of a k-step are 16 contiguous bytes: every A fragment is a single
-//     conflict-free 16-byte LDS read;
+//   * (At_j - I, Bc_j) of the next history chunk are copied global -> LDS asynchronously
+//     (global_load_lds, 16 bytes per lane, every instruction a contiguous 1 KiB source)
+//     while the current one is multiplied;
+//   * a prep pass writes (At_j - I) in the exact byte order of its LDS image: every A
+//     fragment is one conflict-free 16-byte LDS read at a lane-constant address plus a
+//     compile-time offset, which leaves registers for a ring of fragment reads in flight;
 //   * gates sit in one register per query chunk (64 history chunks per refill) and are
 //     broadcast with readlane, so the loop touches no other memory;
 //   * groups are dispatched longest chain first, head-fastest, so the workgroups running
@@ -32,50 +32,75 @@ namespace hla {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// (At_j - I) in the k order the composition reads: within every 16-wide k block the two
-// middle groups of four are swapped, so the 8 k values one lane needs for a k-step
-// (ks*16 + {h*4 .. h*4+3, 8 + h*4 .. 8 + h*4+3}) are 16 contiguous bytes at unit 2 ks + h.
+// (At_j - I) written in the exact byte order of the composition's LDS image of it, so the
+// copy into LDS is a plain contiguous 1 KiB block per instruction.  The image: the columns
+// are cut into 16-wide k blocks stored one after the other (DK rows x 32 bytes each);
+// within a block the 16 columns are reordered so that the 8 k values one lane needs for a
+// k-step (ks*16 + {h*4 .. h*4+3, 8 + h*4 .. 8 + h*4+3}) form the 16-byte half h, and the
+// two halves of row r are swapped when bit 2 of r is set.  Copy block m (1 KiB) holds k
+// block m / (DK/32) for rows 32 (m % (DK/32)) .. + 31, two 16-byte units per row.
 template <int DK>
-__global__ __launch_bounds__(256) void prep_at_kernel(const bf16* __restrict__ At, bf16* __restrict__ Ap, int64_t n_units) {
-  const int64_t u = blockIdx.x * (int64_t)256 + threadIdx.x;  // output 16-byte unit
-  if (u >= n_units) return;
-  constexpr int UPR = DK / 8;
-  const int64_t row_all = u / UPR;  // row over all (b, h, j, r)
-  const int U = (int)(u % UPR), r = (int)(row_all % DK);
-  const bf16* src = At + row_all * DK;
-  const int q0 = 4 * (U >> 1) + (U & 1), q1 = q0 + 2;  // source groups of four
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(src + q0 * 4);
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(src + q1 * 4);
-  bf16x8 o;
+__global__ __launch_bounds__(256) void prep_at_kernel(const bf16* __restrict__ At, bf16* __restrict__ Ap, int64_t n_pairs) {
+  // one thread per (row, k block): reads the row's 32 contiguous bytes of the block
+  // (consecutive threads walk along a row, so the reads are fully coalesced) and writes
+  // the two 16-byte halves to their adjacent places in the image.
+  const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
+  if (t >= n_pairs) return;
+  constexpr int KB = DK / 16, NRT = DK / 32;
+  const int kb = (int)(t % KB);
+  const int64_t row_all = t / KB;  // row over all (b, h, j, r)
+  const int r = (int)(row_all % DK);
+  const int64_t chunk = row_all / DK;
+  const bf16* src = At + row_all * DK + kb * 16;
+  const bf16x8 lo = *reinterpret_cast<const bf16x8*>(src);      // groups of four 0, 1
+  const bf16x8 hi = *reinterpret_cast<const bf16x8*>(src + 8);  // groups 2, 3
+  bf16x8 h0, h1;  // logical halves: groups (0, 2) and (1, 3)
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    o[e] = (q0 * 4 + e == r) ? (bf16)((float)a[e] - 1.f) : a[e];
-    o[e + 4] = (q1 * 4 + e == r) ? (bf16)((float)b[e] - 1.f) : b[e];
+    h0[e] = lo[e];
+    h0[e + 4] = hi[e];
+    h1[e] = lo[e + 4];
+    h1[e + 4] = hi[e + 4];
   }
-  *reinterpret_cast<bf16x8*>(Ap + u * 8) = o;
+  const int d = r - kb * 16;  // the diagonal entry of this row, if it falls in the block
+  if (d >= 0 && d < 16) {
+    const int half = (d >> 2) & 1, e = (d & 3) + ((d >> 3) << 2);
+    if (half == 0)
+      h0[e] = (bf16)((float)h0[e] - 1.f);
+    else
+      h1[e] = (bf16)((float)h1[e] - 1.f);
+  }
+  const int m = kb * NRT + (r >> 5);
+  bf16* dst = Ap + chunk * DK * DK + m * 512 + (r & 31) * 16;
+  const bool swap = (r >> 2) & 1;
+  *reinterpret_cast<bf16x8*>(dst) = swap ? h1 : h0;
+  *reinterpret_cast<bf16x8*>(dst + 8) = swap ? h0 : h1;
 }
 
-template <int DK, int DV, int NW, int SPW, int NBUF, bool BCG>
-__global__ __launch_bounds__(NW * 64, (NBUF == 1 || BCG) ? 2 : 1) void compose_bf16_kernel(RouteArgs a) {
+template <int DK, int DV, int NW, int SPW, int PF>
+__global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
   constexpr int NCTV = DV / 32;
-  constexpr int QG = NW * SPW / NCTV;
   constexpr int NRT = DK / 32, NKS = DK / 16;
-  constexpr int UA = DK / 8, UB = DV / 8;  // 16-byte units per LDS row
-  constexpr int NIA = DK * UA / 64, NIB = DK * UB / 64;
-  // Two separate LDS variables (not one array indexed by the step parity): the copy into
-  // one buffer can then be proven not to alias reads of the other, so the compiler does
-  // not wait for the copy before the multiplications that overlap it.
-  // BCG: Bc fragments come from global memory into registers (prefetched one history
-  // chunk ahead) and only At is staged in LDS, halving the LDS of a workgroup.
+  constexpr int BLK = DK * 32;                     // bytes of one 16-wide k block in LDS
+  constexpr int NDA = (DK / 16) * NRT, NDB = (DV / 16) * NRT;  // 1 KiB copy blocks
+  static_assert(NDA % NW == 0 && NDB % NW == 0, "copy blocks split evenly");
+  // LDS images: (At_j - I) as the prep pass laid it out (k blocks of DK rows x 32 bytes,
+  // every fragment read is one lane-constant address plus a compile-time offset); Bc_j row
+  // by row, 16-byte unit p of row r holding unit p ^ (r mod units-per-row), so both the
+  // copy (whole rows) and the column-block reads are bank-conflict free.  Two separate LDS
+  // variables per operand (not one array indexed by the step parity): the copy into one
+  // buffer can then be proven not to alias reads of the other, so the compiler does not
+  // wait for the copy before the multiplications that overlap it.
   __shared__ __attribute__((aligned(16))) bf16 sA0[DK * DK];
-  __shared__ __attribute__((aligned(16))) bf16 sB0[BCG ? 8 : DK * DV];
-  __shared__ __attribute__((aligned(16))) bf16 sA1[NBUF == 2 ? DK * DK : 8];
-  __shared__ __attribute__((aligned(16))) bf16 sB1[(NBUF == 2 && !BCG) ? DK * DV : 8];
+  __shared__ __attribute__((aligned(16))) bf16 sB0[DK * DV];
+  __shared__ __attribute__((aligned(16))) bf16 sA1[DK * DK];
+  __shared__ __attribute__((aligned(16))) bf16 sB1[DK * DV];
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, c32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = a.N;
   const int64_t BH = a.B * a.H;
+  constexpr int QG = NW * SPW / NCTV;
   const int ng = (N + QG - 1) / QG;
   const int64_t id = blockIdx.x;
   const int64_t bh = id % BH;
@@ -91,47 +116,48 @@ __global__ __launch_bounds__(NW * 64, (NBUF == 1 || BCG) ? 2 : 1) void compose_b
   const bf16* Bg = reinterpret_cast<const bf16*>(a.Bc) + bh * N * (int64_t)DK * DV;
   const float* gts = a.gates + bh * (int64_t)N * N;
   const uint8_t* msk = a.mask + bh * (int64_t)N * N;
-  static_assert((DK * UA / 64) % NW == 0 && (DK * UB / 64) % NW == 0, "copy blocks split evenly");
   float* Sout = a.S_routed + bh * (int64_t)N * DK * DV;
 
-  // async copy of (At_j, Bc_j) into LDS buffer `buf`; LDS unit p of row r holds global
-  // unit p ^ (r mod units-per-row).  Wave w copies 1 KiB blocks w, w + NW, ...; because NW
-  // is a multiple of 4 the swizzle of a lane is the same in all of its blocks, so one
-  // offset per lane serves every block.
-  static_assert(NW % 4 == 0, "one swizzle per lane needs NW % 4 == 0");
-  const int offA = [&] {
-    const int u = w * 64 + lane, r = u / UA, p = u % UA;
-    return r * DK + ((p ^ (r & (UA - 1))) * 8);
-  }();
-  const int offB = [&] {
-    const int u = w * 64 + lane, r = u / UB, p = u % UB;
-    return r * DV + ((p ^ (r & (UB - 1))) * 8);
+  // Async copy of (At_j, Bc_j) into LDS, 1 KiB blocks m = w, w + NW, ... per wave.  Bc
+  // block m is UPB = 1024 / (2 DV) whole rows; its lane -> source unit permutation depends
+  // on m only through m mod (units-per-row / UPB), which is fixed per wave because NW is a
+  // multiple of it, so one offset per lane serves every block.
+  constexpr int UB = DV / 8, RPB = 1024 / (2 * DV);  // units per Bc row, rows per block
+  static_assert(NW % (UB / RPB) == 0, "Bc swizzle fixed per wave");
+  const int srcB = [&] {
+    const int r = w * RPB + lane / UB, p = lane % UB;
+    return (lane / UB) * DV * 2 + ((p ^ (r & (UB - 1))) << 4);
   }();
   auto issue = [&](int j, bf16* dA, bf16* dB) {
     const char* as = reinterpret_cast<const char*>(Ag + (int64_t)j * DK * DK);  // uniform base
     const char* bs = reinterpret_cast<const char*>(Bg + (int64_t)j * DK * DV);
 #pragma unroll
-    for (int m = 0; m < NIA / NW; ++m)
-      __builtin_amdgcn_global_load_lds(as + (uint32_t)((offA + m * NW * 512) * 2), (lds_void_t*)&dA[(w + m * NW) * 512],
-                                       16, 0, 0);
-    if constexpr (!BCG) {
+    for (int i = 0; i < NDA / NW; ++i) {
+      const int m = w + i * NW;
+      __builtin_amdgcn_global_load_lds(as + m * 1024 + lane * 16,
+                                       (lds_void_t*)(reinterpret_cast<char*>(dA) + m * 1024), 16, 0, 0);
+    }
 #pragma unroll
-      for (int m = 0; m < NIB / NW; ++m)
-        __builtin_amdgcn_global_load_lds(bs + (uint32_t)((offB + m * NW * 512) * 2),
-                                         (lds_void_t*)&dB[(w + m * NW) * 512], 16, 0, 0);
+    for (int i = 0; i < NDB / NW; ++i) {
+      const int m = w + i * NW;
+      __builtin_amdgcn_global_load_lds(bs + m * 1024 + srcB,
+                                       (lds_void_t*)(reinterpret_cast<char*>(dB) + m * 1024), 16, 0, 0);
     }
   };
-  // Bc A fragments of history chunk j straight from global memory: row rt*32 + c32,
-  // the 8 columns ct*32 + kd*16 + hh*8 ..
-  bf16x8 bcf[NRT][2];
-  auto load_bc = [&](int j) {
-    const bf16* bs = Bg + (int64_t)j * DK * DV + c32 * DV + ct * 32 + hh * 8;
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int kd = 0; kd < 2; ++kd) bcf[rt][kd] = *reinterpret_cast<const bf16x8*>(bs + rt * 32 * DV + kd * 16);
-  };
   auto wait_copies = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // fragment reads: row rt*32 + c32, logical half hh of k block kb (At); Bc columns
+  // 32 ct + 16 kd + 8 hh .. (unit 4 ct + 2 kd + hh of the row)
+  const int rd = c32 * 32 + ((hh ^ ((c32 >> 2) & 1)) << 4);
+  const int rdB0 = c32 * DV * 2 + (((4 * ct + hh) ^ (c32 & (UB - 1))) << 4);
+  const int rdB1 = c32 * DV * 2 + (((4 * ct + 2 + hh) ^ (c32 & (UB - 1))) << 4);
+  constexpr int NFA = NKS * NRT, NF = NFA + 2 * NRT;
+  auto frag = [&](const bf16* cA, const bf16* cB, int f) -> bf16x8 {
+    if (f < NFA)
+      return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(cA) + rd + (f / NRT) * BLK + (f % NRT) * 1024);
+    const int fb = f - NFA;
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(cB) + (fb / NRT ? rdB1 : rdB0) +
+                                            (fb % NRT) * 32 * DV * 2);
+  };
 
   f32x16 M[SPW][NRT];
 #pragma unroll
@@ -204,19 +230,26 @@ __global__ __launch_bounds__(NW * 64, (NBUF == 1 || BCG) ? 2 : 1) void compose_b
       g[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(greg[s]), j & 63));
       any |= (g[s] != 0.f);
     }
-    if (NBUF == 2 && j + 1 < nsteps) issue(j + 1, nA, nB);
-    if (BCG && !any && j + 1 < nsteps) load_bc(j + 1);
+    if (j + 1 < nsteps) issue(j + 1, nA, nB);
     if (any) {
+      // the first PF fragment reads are in flight while the B operands are converted
+      bf16x8 ring[PF];
+#pragma unroll
+      for (int p = 0; p < PF; ++p) ring[p] = frag(cA, cB, p);
       // B operand bf16(g M) straight from the accumulator rows this lane holds
       bf16x8 bfr[SPW][NKS];
 #pragma unroll
       for (int s = 0; s < SPW; ++s)
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) bfr[s][ks] = Mma<bf16>::from_acc(M[s][ks >> 1], ks, g[s]);
-      if constexpr (BCG) {
+      bf16x8 dg[SPW];
 #pragma unroll
-        for (int kd = 0; kd < 2; ++kd) {
-          bf16x8 dg[SPW];
+      for (int f = 0; f < NF; ++f) {
+        const bf16x8 af = ring[f % PF];
+        if (f + PF < NF) ring[f % PF] = frag(cA, cB, f + PF);
+        const int rt = (f < NFA ? f : f - NFA) % NRT;
+        if (f >= NFA && (f - NFA) % NRT == 0) {
+          const int kd = (f - NFA) / NRT;
 #pragma unroll
           for (int s = 0; s < SPW; ++s) {
             const uint32_t gb = (uint32_t)__builtin_bit_cast(unsigned short, (bf16)g[s]);
@@ -226,56 +259,16 @@ __global__ __launch_bounds__(NW * 64, (NBUF == 1 || BCG) ? 2 : 1) void compose_b
             for (int d = 0; d < 4; ++d) d4[d] = pat[kd][d] & g2;
             dg[s] = __builtin_bit_cast(bf16x8, d4);
           }
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-            for (int s = 0; s < SPW; ++s) M[s][rt] = Mma<bf16>::mma(bcf[rt][kd], dg[s], M[s][rt]);
         }
+#pragma unroll
+        for (int s = 0; s < SPW; ++s)
+          M[s][rt] = Mma<bf16>::mma(af, f < NFA ? bfr[s][f / NRT] : dg[s], M[s][rt]);
       }
-      if (BCG && j + 1 < nsteps) load_bc(j + 1);  // bcf was consumed at issue above
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-          const int r = rt * 32 + c32;
-          const bf16x8 af =
-              *reinterpret_cast<const bf16x8*>(cA + r * DK + (((2 * ks + hh) ^ (r & (UA - 1))) * 8));
-#pragma unroll
-          for (int s = 0; s < SPW; ++s) M[s][rt] = Mma<bf16>::mma(af, bfr[s][ks], M[s][rt]);
-        }
-      }
-if constexpr (!BCG) {
-#pragma unroll
-      for (int kd = 0; kd < 2; ++kd) {
-        bf16x8 dg[SPW];
-#pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-          const uint32_t gb = (uint32_t)__builtin_bit_cast(unsigned short, (bf16)g[s]);
-          const uint32_t g2 = gb | (gb << 16);
-          uint32_t d4[4];
-#pragma unroll
-          for (int d = 0; d < 4; ++d) d4[d] = pat[kd][d] & g2;
-          dg[s] = __builtin_bit_cast(bf16x8, d4);
-        }
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-          const int r = rt * 32 + c32;
-          const int unit = 4 * ct + 2 * kd + hh;
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(cB + r * DV + ((unit ^ (r & (UB - 1))) * 8));
-#pragma unroll
-          for (int s = 0; s < SPW; ++s) M[s][rt] = Mma<bf16>::mma(af, dg[s], M[s][rt]);
-        }
-      }
-}
     }
 #pragma unroll
     for (int s = 0; s < SPW; ++s)
       if (qi[s] == j + 1 && qi[s] < N) write_state(s);
     if (j + 1 < nsteps) {
-      if (NBUF == 1) {
-        __syncthreads();  // every wave is done reading the single buffer
-        issue(j + 1, nA, nB);
-      }
       wait_copies();
       __syncthreads();
     }
@@ -283,45 +276,40 @@ if constexpr (!BCG) {
 
   if (nsteps > 0) {
     issue(0, sA0, sB0);
-    if constexpr (BCG) load_bc(0);
     wait_copies();
     __syncthreads();
   }
-  if constexpr (NBUF == 2) {
-    for (int j = 0; j < nsteps; j += 2) {
-      step(j, sA0, sB0, sA1, sB1);
-      if (j + 1 < nsteps) step(j + 1, sA1, sB1, sA0, sB0);
-    }
-  } else {
-    for (int j = 0; j < nsteps; ++j) step(j, sA0, sB0, sA0, sB0);
+  for (int j = 0; j < nsteps; j += 2) {
+    step(j, sA0, sB0, sA1, sB1);
+    if (j + 1 < nsteps) step(j + 1, sA1, sB1, sA0, sB0);
   }
 }
 
-template <int DK, int DV, int NW, int SPW, int NBUF, bool BCG>
+template <int DK, int DV, int NW, int SPW, int PF>
 static hipError_t launch_compose_bf16_t(const RouteArgs& a, hipStream_t s) {
   constexpr int QG = NW * SPW / (DV / 32);
   const int64_t ng = (a.N + QG - 1) / QG;
   const int64_t nb = ng * a.B * a.H;
   TimedLaunch tl(HLA_KERNEL_COMPOSE, s);
-  hipLaunchKernelGGL((compose_bf16_kernel<DK, DV, NW, SPW, NBUF, BCG>), dim3((unsigned)nb), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((compose_bf16_kernel<DK, DV, NW, SPW, PF>), dim3((unsigned)nb), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_compose_bf16(const RouteArgs& a, int dk, int dv, hipStream_t s) {
-  const int64_t n_units = a.B * a.H * (int64_t)a.N * dk * (dk / 8);
-  if (n_units > 0) {
-    const unsigned nb = (unsigned)((n_units + 255) / 256);
+  const int64_t n_pairs = a.B * a.H * (int64_t)a.N * dk * (dk / 16);
+  if (n_pairs > 0) {
+    const unsigned nb = (unsigned)((n_pairs + 255) / 256);
     if (dk == 64)
       hipLaunchKernelGGL(prep_at_kernel<64>, dim3(nb), dim3(256), 0, s, reinterpret_cast<const bf16*>(a.At),
-                         reinterpret_cast<bf16*>(a.At_prep), n_units);
+                         reinterpret_cast<bf16*>(a.At_prep), n_pairs);
     else
       hipLaunchKernelGGL(prep_at_kernel<128>, dim3(nb), dim3(256), 0, s, reinterpret_cast<const bf16*>(a.At),
-                         reinterpret_cast<bf16*>(a.At_prep), n_units);
+                         reinterpret_cast<bf16*>(a.At_prep), n_pairs);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
 #ifndef HLA_COMPOSE_SHAPE
-#define HLA_COMPOSE_SHAPE 8, 2, 2, false
+#define HLA_COMPOSE_SHAPE 8, 2, 4
 #endif
   if (dk == 64 && dv == 64) return launch_compose_bf16_t<64, 64, HLA_COMPOSE_SHAPE>(a, s);
   if (dk == 64 && dv == 128) return launch_compose_bf16_t<64, 128, HLA_COMPOSE_SHAPE>(a, s);
