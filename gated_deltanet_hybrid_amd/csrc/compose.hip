@@ -37,8 +37,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // are cut into 16-wide k blocks stored one after the other (DK rows x 32 bytes each);
 // within a block the 16 columns are reordered so that the 8 k values one lane needs for a
 // k-step (ks*16 + {h*4 .. h*4+3, 8 + h*4 .. 8 + h*4+3}) form the 16-byte half h, and the
-// two halves of row r are swapped when bit 2 of r is set.  Copy block m (1 KiB) holds k
-// block m / (DK/32) for rows 32 (m % (DK/32)) .. + 31, two 16-byte units per row.
+// two halves of row r are swapped when bits 2 and 3 of r differ, so that rows r, r + 4,
+// r + 8 and r + 12 start on distinct bank groups and a read phase of 8 or of 16 lanes is
+// conflict free.  Copy block m (1 KiB) holds k block m / (DK/32) for rows
+// 32 (m % (DK/32)) .. + 31, two 16-byte units per row.
 template <int DK>
 __global__ __launch_bounds__(256) void prep_at_kernel(const bf16* __restrict__ At, bf16* __restrict__ Ap, int64_t n_pairs) {
   // one thread per (row, k block): reads the row's 32 contiguous bytes of the block
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void prep_at_kernel(const bf16* __restrict__ A
   }
   const int m = kb * NRT + (r >> 5);
   bf16* dst = Ap + chunk * DK * DK + m * 512 + (r & 31) * 16;
-  const bool swap = (r >> 2) & 1;
+  const bool swap = ((r >> 2) ^ (r >> 3)) & 1;
   *reinterpret_cast<bf16x8*>(dst) = swap ? h1 : h0;
   *reinterpret_cast<bf16x8*>(dst + 8) = swap ? h0 : h1;
 }
@@ -84,6 +86,7 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
   constexpr int BLK = DK * 32;                     // bytes of one 16-wide k block in LDS
   constexpr int NDA = (DK / 16) * NRT, NDB = (DV / 16) * NRT;  // 1 KiB copy blocks
   static_assert(NDA % NW == 0 && NDB % NW == 0, "copy blocks split evenly");
+  static_assert(NDA / NW + NDB / NW <= NKS * NRT, "at most one copy per A fragment");
   // LDS images: (At_j - I) as the prep pass laid it out (k blocks of DK rows x 32 bytes,
   // every fragment read is one lane-constant address plus a compile-time offset); Bc_j row
   // by row, 16-byte unit p of row r holding unit p ^ (r mod units-per-row), so both the
@@ -128,26 +131,29 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
     const int r = w * RPB + lane / UB, p = lane % UB;
     return (lane / UB) * DV * 2 + ((p ^ (r & (UB - 1))) << 4);
   }();
-  auto issue = [&](int j, bf16* dA, bf16* dB) {
-    const char* as = reinterpret_cast<const char*>(Ag + (int64_t)j * DK * DK);  // uniform base
-    const char* bs = reinterpret_cast<const char*>(Bg + (int64_t)j * DK * DV);
-#pragma unroll
-    for (int i = 0; i < NDA / NW; ++i) {
-      const int m = w + i * NW;
+  // copy instruction d (0 .. NDW-1) of this wave for history chunk j
+  constexpr int NDW = NDA / NW + NDB / NW;
+  auto issue_one = [&](int j, int d, bf16* dA, bf16* dB) {
+    if (d < NDA / NW) {
+      const int m = w + d * NW;
+      const char* as = reinterpret_cast<const char*>(Ag + (int64_t)j * DK * DK);  // uniform base
       __builtin_amdgcn_global_load_lds(as + m * 1024 + lane * 16,
                                        (lds_void_t*)(reinterpret_cast<char*>(dA) + m * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NDB / NW; ++i) {
-      const int m = w + i * NW;
+    } else {
+      const int m = w + (d - NDA / NW) * NW;
+      const char* bs = reinterpret_cast<const char*>(Bg + (int64_t)j * DK * DV);
       __builtin_amdgcn_global_load_lds(bs + m * 1024 + srcB,
                                        (lds_void_t*)(reinterpret_cast<char*>(dB) + m * 1024), 16, 0, 0);
     }
   };
+  auto issue = [&](int j, bf16* dA, bf16* dB) {
+#pragma unroll
+    for (int d = 0; d < NDW; ++d) issue_one(j, d, dA, dB);
+  };
   auto wait_copies = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   // fragment reads: row rt*32 + c32, logical half hh of k block kb (At); Bc columns
   // 32 ct + 16 kd + 8 hh .. (unit 4 ct + 2 kd + hh of the row)
-  const int rd = c32 * 32 + ((hh ^ ((c32 >> 2) & 1)) << 4);
+  const int rd = c32 * 32 + ((hh ^ (((c32 >> 2) ^ (c32 >> 3)) & 1)) << 4);
   const int rdB0 = c32 * DV * 2 + (((4 * ct + hh) ^ (c32 & (UB - 1))) << 4);
   const int rdB1 = c32 * DV * 2 + (((4 * ct + 2 + hh) ^ (c32 & (UB - 1))) << 4);
   constexpr int NFA = NKS * NRT, NF = NFA + 2 * NRT;
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
       g[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(greg[s]), j & 63));
       any |= (g[s] != 0.f);
     }
-    if (j + 1 < nsteps) issue(j + 1, nA, nB);
+    const bool more = j + 1 < nsteps;
     if (any) {
       // the first PF fragment reads are in flight while the B operands are converted
       bf16x8 ring[PF];
@@ -245,6 +251,21 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
       bf16x8 dg[SPW];
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
+        // the copies of chunk j + 1 are spread over the products, so the address unit
+        // drains them in the background instead of stalling every wave at once (after
+        // the last step this copies chunk nsteps <= N - 1 into the idle buffer: in
+        // bounds, never read, and waited for before the kernel ends)
+#pragma unroll
+        for (int d = 0; d < NDW; ++d)
+          if (f == d * NFA / NDW) {
+#ifdef HLA_SPREAD_MASK
+            __builtin_amdgcn_sched_barrier(HLA_SPREAD_MASK);
+#endif
+            issue_one(j + 1, d, nA, nB);
+#ifdef HLA_SPREAD_MASK
+            __builtin_amdgcn_sched_barrier(HLA_SPREAD_MASK);
+#endif
+          }
         const bf16x8 af = ring[f % PF];
         if (f + PF < NF) ring[f % PF] = frag(cA, cB, f + PF);
         const int rt = (f < NFA ? f : f - NFA) % NRT;
@@ -264,11 +285,27 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
         for (int s = 0; s < SPW; ++s)
           M[s][rt] = Mma<bf16>::mma(af, f < NFA ? bfr[s][f / NRT] : dg[s], M[s][rt]);
       }
+#ifdef HLA_SGB
+      // instruction order of the block: the ring prologue, then per fragment its SPW
+      // products followed by the refill of its ring slot, with the copy instructions
+      // spread evenly in front of the fragments they were placed at
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+#pragma unroll
+        for (int d = 0; d < NDW; ++d)
+          if (f == d * NFA / NDW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, SPW, 0);
+        if (f + PF < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#endif
+    } else if (more) {
+      issue(j + 1, nA, nB);
     }
 #pragma unroll
     for (int s = 0; s < SPW; ++s)
       if (qi[s] == j + 1 && qi[s] < N) write_state(s);
-    if (j + 1 < nsteps) {
+    if (more) {
       wait_copies();
       __syncthreads();
     }
@@ -283,6 +320,7 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
     step(j, sA0, sB0, sA1, sB1);
     if (j + 1 < nsteps) step(j + 1, sA1, sB1, sA0, sB0);
   }
+  wait_copies();
 }
 
 template <int DK, int DV, int NW, int SPW, int PF>
