@@ -76,23 +76,61 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
       uint4 val = make_uint4(0u, 0u, 0u, 0u);
       if (t < n) val = *reinterpret_cast<const uint4*>(kg + t * kstride + cc * PAD);
       *reinterpret_cast<uint4*>(Kp + t * PK + cc * PAD) = val;
-      const T* ev = reinterpret_cast<const T*>(&val);
+      if constexpr (sizeof(T) == 4) {
+        const T* ev = reinterpret_cast<const T*>(&val);
 #pragma unroll
-      for (int e = 0; e < PAD; ++e) KT[(cc * PAD + e) * PT + t] = ev[e];
+        for (int e = 0; e < PAD; ++e) KT[(cc * PAD + e) * PT + t] = ev[e];
+      }
       if constexpr (WANT_O) {
         uint4 qv = make_uint4(0u, 0u, 0u, 0u);
         if (t < n) qv = *reinterpret_cast<const uint4*>(qg + t * kstride + cc * PAD);
         *reinterpret_cast<uint4*>(Qp + t * PK + cc * PAD) = qv;
       }
     }
-    constexpr int VV = DV / PAD;
-    for (int i = tid; i < C * VV; i += NT) {
-      const int t = i / VV, cc = i % VV;
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (t < n) val = *reinterpret_cast<const uint4*>(vg + t * vstride + cc * PAD);
-      const T* ev = reinterpret_cast<const T*>(&val);
+    if constexpr (sizeof(T) == 4) {
+      constexpr int VV = DV / PAD;
+      for (int i = tid; i < C * VV; i += NT) {
+        const int t = i / VV, cc = i % VV;
+        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        if (t < n) val = *reinterpret_cast<const uint4*>(vg + t * vstride + cc * PAD);
+        const T* ev = reinterpret_cast<const T*>(&val);
 #pragma unroll
-      for (int e = 0; e < PAD; ++e) VT[(cc * PAD + e) * PT + t] = ev[e];
+        for (int e = 0; e < PAD; ++e) VT[(cc * PAD + e) * PT + t] = ev[e];
+      }
+    } else {
+      // K^T and V^T by 8 x 8 register transposes: task (token block tb, column block db)
+      // loads 8 tokens x 8 columns and writes 8 rows of 8 tokens.  tb runs fastest, so the
+      // 8 lanes of a write phase hit rows (8 db + e) at token blocks 0..7: 16-byte units
+      // e * (PT / 8) + tb, distinct modulo 8 because PT / 8 is odd.
+      static_assert((PT / 8) % 2 == 1, "odd row pitch in 16-byte units");
+      constexpr int NTB = C / 8, NDK = DK / 8, NDV = DV / 8;
+      for (int i = tid; i < NTB * (NDK + NDV); i += NT) {
+        const int tb = i % NTB, dball = i / NTB;
+        const bool isk = dball < NDK;
+        const int db = isk ? dball : dball - NDK;
+        const T* src = (isk ? kg + db * 8 : vg + db * 8);
+        const int64_t stride = isk ? kstride : vstride;
+        uint4 in[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int t = tb * 8 + r;
+          in[r] = t < n ? *reinterpret_cast<const uint4*>(src + t * stride) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        T* dst = (isk ? KT : VT) + db * 8 * PT + tb * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // tokens (2m, 2m + 1) of column e: the 16-bit half e & 1 of word e / 2
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const int wd = e >> 1;
+          auto word = [&](const uint4& u) { return wd == 0 ? u.x : wd == 1 ? u.y : wd == 2 ? u.z : u.w; };
+          uint4 o;
+          o.x = __builtin_amdgcn_perm(word(in[1]), word(in[0]), sel);
+          o.y = __builtin_amdgcn_perm(word(in[3]), word(in[2]), sel);
+          o.z = __builtin_amdgcn_perm(word(in[5]), word(in[4]), sel);
+          o.w = __builtin_amdgcn_perm(word(in[7]), word(in[6]), sel);
+          *reinterpret_cast<uint4*>(dst + e * PT) = o;
+        }
+      }
     }
     if (tid < C) {
       float bt = 0.f, la = 0.f;
@@ -330,13 +368,36 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
         }
     }
     const float* S0 = a.chunk_init + ((b * a.H + h) * a.N + c) * (int64_t)DK * DV;
-    for (int i = tid; i < DK * DV / 4; i += NT) {
-      const int dk = i / (DV / 4), dv = (i % (DV / 4)) * 4;
-      const float4 val = *reinterpret_cast<const float4*>(S0 + dk * DV + dv);
-      STb[(dv + 0) * PK + dk] = from_f<T>(val.x);
-      STb[(dv + 1) * PK + dk] = from_f<T>(val.y);
-      STb[(dv + 2) * PK + dk] = from_f<T>(val.z);
-      STb[(dv + 3) * PK + dk] = from_f<T>(val.w);
+    if constexpr (sizeof(T) == 4) {
+      for (int i = tid; i < DK * DV / 4; i += NT) {
+        const int dk = i / (DV / 4), dv = (i % (DV / 4)) * 4;
+        const float4 val = *reinterpret_cast<const float4*>(S0 + dk * DV + dv);
+        STb[(dv + 0) * PK + dk] = from_f<T>(val.x);
+        STb[(dv + 1) * PK + dk] = from_f<T>(val.y);
+        STb[(dv + 2) * PK + dk] = from_f<T>(val.z);
+        STb[(dv + 3) * PK + dk] = from_f<T>(val.w);
+      }
+    } else {
+      // S~ transposed to bf16 by register blocks: task (row block rb of 8 dk, column group
+      // cg of 4 dv) loads 8 float4 and writes 4 rows of 8 dk.  rb runs fastest, so the 8
+      // lanes of a write phase hit 16-byte units (4 cg + j) (PK / 8) + rb, distinct modulo
+      // 8 because PK / 8 is odd.
+      static_assert((PK / 8) % 2 == 1, "odd row pitch in 16-byte units");
+      constexpr int NRB = DK / 8, NCG = DV / 4;
+      for (int i = tid; i < NRB * NCG; i += NT) {
+        const int rb = i % NRB, cg = i / NRB;
+        const float* src = S0 + rb * 8 * DV + cg * 4;
+        float4 in[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) in[r] = *reinterpret_cast<const float4*>(src + r * DV);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x8 o;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) o[r] = (bf16)(j == 0 ? in[r].x : j == 1 ? in[r].y : j == 2 ? in[r].z : in[r].w);
+          *reinterpret_cast<bf16x8*>(STb + (cg * 4 + j) * PK + rb * 8) = o;
+        }
+      }
     }
     __syncthreads();
 #pragma unroll
