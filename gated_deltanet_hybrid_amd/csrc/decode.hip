@@ -27,11 +27,11 @@ constexpr int kMaxCache = 1024;  // largest n_cap a decode call accepts
 //   state      (IS_STATE): mat' = alpha mat + beta k (v - alpha u)^T,  out = q^T mat'
 //   transition (else)    : mat' = alpha mat - alpha beta k u^T,        out = q^T mat'
 // With `commit`, mat' goes to the cache slot (cast to T) and mat is reset (0, or I).
-template <class T, int DK, int W, bool IS_STATE>
-__device__ void live_pass(float* mat, T* cache_out, bool commit, float alpha, float beta, float qk,
+template <class T, int DK, int W, bool IS_STATE, int NT>
+__device__ __forceinline__ void live_pass(float* mat, T* cache_out, bool commit, float alpha, float beta, float qk,
                           const float* s_q, const float* s_k, const float* s_v, float* red0, float* red1,
                           int red_size, float* s_u, float* out) {
-  constexpr int NT = 256, CPR = W / 4, RPP = NT / CPR, NP = DK / RPP;
+  constexpr int CPR = W / 4, RPP = NT / CPR, NP = DK / RPP;
   const int tid = threadIdx.x;
   const int col = (tid % CPR) * 4, r0 = tid / CPR;
   float4 m[NP];
@@ -86,9 +86,17 @@ __device__ void live_pass(float* mat, T* cache_out, bool commit, float alpha, fl
   __syncthreads();
 }
 
-template <class T, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-  constexpr int NT = 256;
+// 512 threads per (sequence, head) and a two-deep register prefetch of the cached chunks
+// fit in ~121 VGPRs, so two workgroups share a CU; every phase is a short dependent chain
+// of loads and reductions, and the second workgroup keeps HBM busy meanwhile.
+#ifndef HLA_DECODE_WGS_PER_CU
+#define HLA_DECODE_WGS_PER_CU 1
+#endif
+#ifndef HLA_DECODE_NT
+#define HLA_DECODE_NT 512
+#endif
+template <class T, int DK, int DV, int NT, int WPC>
+__global__ __launch_bounds__(NT, WPC) void decode_kernel(DecodeArgs a) {
   constexpr int E = sizeof(T), PAD = 16 / E;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t bh = blockIdx.x;
@@ -134,14 +142,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   T* Acache = reinterpret_cast<T*>(a.At_cache);
   T* Bcache = reinterpret_cast<T*>(a.Bc_cache);
   const int64_t slot = bh * a.n_cap + nc;
-  live_pass<T, DK, DV, true>(a.S_cur + bh * (int64_t)DK * DV, commit ? Bcache + slot * DK * DV : nullptr, commit,
+  live_pass<T, DK, DV, true, NT>(a.S_cur + bh * (int64_t)DK * DV, commit ? Bcache + slot * DK * DV : nullptr, commit,
                             alpha, beta, s_qk, s_q, s_k, s_v, &s_red[0][0][0], &s_red[1][0][0], RMAX * WMAX, s_u,
                             s_o);
   if (!a.At_cur) {
     if (tid < DV) a.o[bh * DV + tid] = s_o[tid];
     return;
   }
-  live_pass<T, DK, DK, false>(a.At_cur + bh * (int64_t)DK * DK, commit ? Acache + slot * DK * DK : nullptr, commit,
+  live_pass<T, DK, DK, false, NT>(a.At_cur + bh * (int64_t)DK * DK, commit ? Acache + slot * DK * DK : nullptr, commit,
                               alpha, beta, s_qk, s_q, s_k, s_v, &s_red[0][0][0], &s_red[1][0][0], RMAX * WMAX,
                               s_u, s_y);
 
@@ -149,7 +157,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ float s_g[kMaxCache];
   __shared__ int s_keep[kMaxCache];
   const int ncap = a.n_cap;
-  for (int j = w; j < nc; j += 4) {
+  for (int j = w; j < nc; j += NT / 64) {
     float g;
     if (a.gates_in) {
       g = a.gates_in[bh * ncap + j];
@@ -160,6 +168,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const T* rep = reinterpret_cast<const T*>(a.reps_cache) + (bh * ncap + j) * (int64_t)a.n_rep * DK;
       float m = -INFINITY, ssum = 0.f;
       const float scale = 1.f / sqrtf((float)DK);
+#pragma unroll 4
       for (int r0 = 0; r0 < a.n_rep; r0 += RPI) {
         const int r = r0 + grp;
         float part = 0.f;
@@ -259,6 +268,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
   };
+#if HLA_DECODE_WGS_PER_CU >= 2
+  // with a tighter register bound: one chunk in flight per workgroup
+  for (int j = next_active(nc); j >= 0; j = next_active(j)) {
+    load_chunk(j, ra0, rb0);
+    process(j, ra0, rb0);
+  }
+#else
   int j = next_active(nc);
   if (j >= 0) load_chunk(j, ra0, rb0);
   while (j >= 0) {
@@ -272,6 +288,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     process(j, ra1, rb1);
     j = jn;
   }
+#endif
   if (tid < DV) a.o[bh * DV + tid] = s_o[tid];
 }
 
@@ -289,7 +306,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   if (nb == 0) return hipSuccess;
   {
     TimedLaunch tl(HLA_KERNEL_DECODE, s);
-    hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)nb), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV, HLA_DECODE_NT, HLA_DECODE_WGS_PER_CU>), dim3((unsigned)nb),
+                       dim3(HLA_DECODE_NT), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(a.commit && a.At_cur)) return e;
