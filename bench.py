@@ -10,6 +10,15 @@ JSON line): decode step tokens/s with HBM GB/s, native chunkwise prefill, Tail-R
 state rebuild.  All inputs are seeded synthetic tensors of the workloads' shapes.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
+
+HBM traffic of the composition kernel (the roofline record's ``traffic``), from two counter
+passes over one routed-prefill step plus a 1 GiB calibration copy:
+
+    cd /tmp && rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d <f> -o t -- \
+        python3 <repo>/bench.py --traffic-run
+    cd /tmp && rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d <w> -o t -- \
+        python3 <repo>/bench.py --traffic-run
+    python3 bench.py --traffic-write <f>/t_counter_collection.csv <w>/t_counter_collection.csv
 """
 from __future__ import annotations
 
@@ -146,7 +155,7 @@ def bench_routed_prefill(args, torch, hla, inputs):
                 + flops_routed_output(n_chunks, W.dk, W.dv))
     comp_avg_s = comp_ms / comp_n / 1e3
     achieved = fl_comp / comp_avg_s / 1e12
-    traffic = read_traffic("compose_routed_prefill", ["gated_deltanet_hybrid_amd/csrc/compose.hip"])
+    traffic = read_traffic(TRAFFIC_KEY, TRAFFIC_SOURCES)
     tokens = W.B * W.T
     res = dict(
         value=tokens / dt, ms_per_step=dt * 1e3,
@@ -310,6 +319,78 @@ def cpu_baseline(x, n_query_chunks):
                 host_cpus=os.cpu_count())
 
 
+# ----------------------------------------------------------------------------- HBM traffic
+TRAFFIC_KEY = "compose_routed_prefill"
+TRAFFIC_SOURCES = ["gated_deltanet_hybrid_amd/csrc/compose.hip"]
+CALIB_BYTES = 1 << 30
+
+
+def traffic_run(torch, hla, inputs):
+    """One warm-up and one timed routed-prefill step, then a plain 1 GiB device copy (read
+    1 GiB, write 1 GiB) that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    args = argparse.Namespace(steps=1, warmup=1)
+    bench_routed_prefill(args, torch, hla, inputs)
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("[traffic] done")
+
+
+def _per_dispatch(csv_path, counter):
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"], int(r["Grid_Size"]))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def _mean_of(per, pred):
+    """Mean counter value over the dispatches whose kernel name passes ``pred`` and whose
+    grid is the largest among those (the calibration copy, not incidental small copies)."""
+    sel = [(g, v) for (_, name, g), v in per.items() if pred(name)]
+    if not sel:
+        return None, 0
+    gmax = max(g for g, _ in sel)
+    vals = [v for g, v in sel if g == gmax]
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_write(fetch_csv, write_csv):
+    """HBM bytes per composition launch from the two counter passes (KiB per dispatch),
+    each scaled by the same counter's reading for the calibration copy of known size."""
+    is_copy = lambda n: "copy" in n.lower() and "hla::" not in n
+    is_comp = lambda n: "compose_bf16_kernel" in n
+    f, w = _per_dispatch(fetch_csv, "FETCH_SIZE"), _per_dispatch(write_csv, "WRITE_SIZE")
+    f_copy, n_fc = _mean_of(f, is_copy)
+    w_copy, n_wc = _mean_of(w, is_copy)
+    f_comp, n_f = _mean_of(f, is_comp)
+    w_comp, n_w = _mean_of(w, is_comp)
+    if None in (f_copy, w_copy, f_comp, w_comp):
+        sys.exit("traffic: a calibration copy or composition dispatch is missing from the counter files")
+    k_fetch = CALIB_BYTES / (f_copy * 1024.0)
+    k_write = CALIB_BYTES / (w_copy * 1024.0)
+    fetch_b = f_comp * 1024.0 * k_fetch
+    write_b = w_comp * 1024.0 * k_write
+    rec = dict(source_sha=sha_of(*TRAFFIC_SOURCES), hbm_bytes_per_launch=round(fetch_b + write_b),
+               fetch_bytes=round(fetch_b), write_bytes=round(write_b), fetch_kib_raw=round(f_comp, 1),
+               write_kib_raw=round(w_comp, 1), calib_fetch_factor=round(k_fetch, 4),
+               calib_write_factor=round(k_write, 4), calib_copy_bytes=CALIB_BYTES, launches=[n_f, n_w],
+               kernel="compose_bf16_kernel", workload="routed_prefill B=1 H=16 T=32768 d=128 C=64 bf16")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    allrec = json.load(open(path)) if os.path.exists(path) else {}
+    allrec[TRAFFIC_KEY] = rec
+    with open(path, "w") as fh:
+        json.dump(allrec, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 # ----------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -320,7 +401,13 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="only the headline routed prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-chunks", type=int, default=512, help="query chunks of the oracle sample (512 = all of head 0)")
+    ap.add_argument("--traffic-run", action="store_true", help="one routed-prefill step plus a calibration copy (under rocprofv3 --pmc)")
+    ap.add_argument("--traffic-write", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from the two counter passes")
     args = ap.parse_args()
+    if args.traffic_write:
+        traffic_write(*args.traffic_write)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: every (batch, head) of this path is independent, so --gpus {args.gpus} "
               "would only shard heads without communication; only --gpus 1 is measured here.", file=sys.stderr)
@@ -334,6 +421,9 @@ def main():
         sys.exit(1)
     hla.library()
     torch.cuda.set_device(0)
+    if args.traffic_run:
+        traffic_run(torch, hla, inputs)
+        return
 
     head, x = bench_routed_prefill(args, torch, hla, inputs)
     secondary = {}

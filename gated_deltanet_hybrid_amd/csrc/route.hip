@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void compose_kernel(RouteArgs a) {
         for (int e = 0; e < 16; ++e) M[s][rt][e] = s0[(rt * 32 + acc_row(e, hh)) * DV + ct * 32 + c32];
       }
     }
-  auto write_state = [&](int s) {
+  auto write_state = [&](int s) __attribute__((always_inline)) {
     float* dst = Sout + (int64_t)qi[s] * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void compose_kernel(RouteArgs a) {
   const int nsteps = i_hi;  // history chunks j = 0 .. i_hi - 1
 
   uint4 pf[NU];
-  auto load_step = [&](int j) {
+  auto load_step = [&](int j) __attribute__((always_inline)) {
     const uint4* asrc = reinterpret_cast<const uint4*>(Ag + (int64_t)j * DK * DK);
     const uint4* bsrc = reinterpret_cast<const uint4*>(Bg + (int64_t)j * DK * DV);
 #pragma unroll
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void compose_kernel(RouteArgs a) {
       pf[u] = idx < DK * UA ? asrc[idx] : bsrc[idx - DK * UA];
     }
   };
-  auto store_step = [&](int buf) {
+  auto store_step = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int idx = tid + 256 * u;
