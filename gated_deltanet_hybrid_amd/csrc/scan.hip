@@ -130,6 +130,87 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
   }
 }
 
+// bf16 transitions: one workgroup per (b, h, 32-column block) with one wave per 32-row
+// tile.  Wave rt keeps rows [32 rt, 32 rt + 32) of the state block in its accumulators and
+// needs only those rows of At: its A fragments (row 32 rt + lane%32, 8 consecutive k) come
+// straight from global memory into registers, one chunk ahead.  The B operand is the whole
+// 128 x 32 state block in bf16; every wave writes its tile into an LDS image laid out
+// [column][k] (so a B fragment is one 16-byte read) and one barrier per chunk publishes it.
+// The image is double-buffered: buffer c % 2 is rewritten only after the next barrier, when
+// every wave has read it.  Bc seeds the accumulator (fp32), so no extra products are needed.
+template <int DK, int DV>
+__global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
+  constexpr int NCT = DV / 32, NKS = DK / 16;
+  constexpr int PB = DK + 8;  // bf16 pitch of an image row (one row per state column)
+  __shared__ __attribute__((aligned(16))) bf16 sB0[32 * PB];
+  __shared__ __attribute__((aligned(16))) bf16 sB1[32 * PB];
+
+  const int lane = threadIdx.x & 63, hh = lane >> 5, c32 = lane & 31;
+  const int rt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t id = blockIdx.x;
+  const int ct = (int)(id % NCT);
+  const int64_t bh = id / NCT;
+  const int N = a.N;
+  const bf16* arow = reinterpret_cast<const bf16*>(a.At) + bh * N * (int64_t)DK * DK + (rt * 32 + c32) * DK + hh * 8;
+  const bf16* bcol = reinterpret_cast<const bf16*>(a.Bc) + bh * N * (int64_t)DK * DV + rt * 32 * DV + ct * 32 + c32;
+  // accumulator element e of this lane: row 32 rt + (e / 4) 8 + 4 hh + e % 4, column 32 ct + c32
+  auto row_of = [&](int e) { return (e >> 2) * 8 + hh * 4 + (e & 3); };
+
+  f32x16 M = zero16();
+  if (a.S0) {
+    const float* s0 = a.S0 + bh * (int64_t)DK * DV + rt * 32 * DV + ct * 32 + c32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) M[e] = s0[row_of(e) * DV];
+  }
+  bf16x8 af[NKS];
+  bf16 bcv[16];
+  auto load = [&](int c) __attribute__((always_inline)) {
+    const bf16* ap = arow + (int64_t)c * DK * DK;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(ap + ks * 16);
+    const bf16* bp = bcol + (int64_t)c * DK * DV;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bcv[e] = bp[row_of(e) * DV];
+  };
+  auto store_state = [&](float* dst) __attribute__((always_inline)) {
+    float* p = dst + rt * 32 * DV + ct * 32 + c32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) p[row_of(e) * DV] = M[e];
+  };
+  if (N > 0) load(0);
+  for (int c = 0; c < N; ++c) {
+    if (a.states) store_state(a.states + (bh * N + c) * (int64_t)DK * DV);
+    bf16* img = (c & 1) ? sB1 : sB0;
+    // this wave's rows of bf16(M) into the image: 4 runs of 4 consecutive k per lane
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)M[g * 4 + e];
+      *reinterpret_cast<bf16x4*>(img + c32 * PB + rt * 32 + g * 8 + hh * 4) = v;
+    }
+    __syncthreads();
+    f32x16 acc0, acc1 = zero16();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc0[e] = (float)bcv[e];
+    bf16x8 cur[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) cur[ks] = af[ks];
+    if (c + 1 < N) load(c + 1);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(img + c32 * PB + ks * 16 + hh * 8);
+      if (ks & 1)
+        acc1 = Mma<bf16>::mma(cur[ks], bfr, acc1);
+      else
+        acc0 = Mma<bf16>::mma(cur[ks], bfr, acc0);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) M[e] = acc0[e] + acc1[e];
+  }
+  if (a.S_final) store_state(a.S_final + bh * (int64_t)DK * DV);
+}
+
 template <class T, int DK, int DV>
 static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
   constexpr int E = sizeof(T), PAD = 16 / E;
@@ -150,8 +231,23 @@ static hipError_t launch_scan_d(const ScanArgs& a, int dk, int dv, hipStream_t s
   return launch_scan_t<T, 128, 128>(a, s);
 }
 
+template <int DK, int DV>
+static hipError_t launch_scan_bf16_t(const ScanArgs& a, hipStream_t s) {
+  const int64_t nb = a.B * a.H * (DV / 32);
+  if (nb == 0) return hipSuccess;
+  TimedLaunch tl(HLA_KERNEL_SCAN, s);
+  hipLaunchKernelGGL((scan_bf16_kernel<DK, DV>), dim3((unsigned)nb), dim3(DK / 32 * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const ScanArgs& a, int dtype, int dk, int dv, hipStream_t s) {
-  return dtype == 1 ? launch_scan_d<bf16>(a, dk, dv, s) : launch_scan_d<float>(a, dk, dv, s);
+  if (dtype == 1) {
+    if (dk == 64 && dv == 64) return launch_scan_bf16_t<64, 64>(a, s);
+    if (dk == 64 && dv == 128) return launch_scan_bf16_t<64, 128>(a, s);
+    if (dk == 128 && dv == 64) return launch_scan_bf16_t<128, 64>(a, s);
+    return launch_scan_bf16_t<128, 128>(a, s);
+  }
+  return launch_scan_d<float>(a, dk, dv, s);
 }
 
 }  // namespace hla
