@@ -22,8 +22,8 @@
 //     compile-time offset, which leaves registers for a ring of fragment reads in flight;
 //   * gates sit in one register per query chunk (64 history chunks per refill) and are
 //     broadcast with readlane, so the loop touches no other memory;
-//   * groups are dispatched longest chain first, head-fastest, so the workgroups running
-//     together sweep the same history chunks of the same heads (L2 reuse of At_j, Bc_j).
+//   * each XCD works through its heads one at a time, longest chain first, so the 32
+//     workgroups running on an XCD sweep the same head's history (L2 reuse of At_j, Bc_j).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
@@ -106,8 +106,20 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
   constexpr int QG = NW * SPW / NCTV;
   const int ng = (N + QG - 1) / QG;
   const int64_t id = blockIdx.x;
-  const int64_t bh = id % BH;
-  const int grp = ng - 1 - (int)(id / BH);
+  // Workgroup ids go to XCDs round-robin (id % 8).  When the heads split evenly over the 8
+  // XCDs, the k-th workgroup of an XCD takes the XCD's heads one at a time, each longest
+  // chain first: all 32 CUs of an XCD then sweep the history of one head and share its
+  // chunks in that XCD's L2.  Otherwise heads run fastest, longest chains first.
+  int64_t bh;
+  int grp;
+  if (BH % 8 == 0) {
+    const int64_t xcd = id % 8, k = id / 8;
+    bh = xcd + 8 * (k / ng);
+    grp = ng - 1 - (int)(k % ng);
+  } else {
+    bh = id % BH;
+    grp = ng - 1 - (int)(id / BH);
+  }
   const int i0 = grp * QG;
   const int nsteps = (i0 + QG < N ? i0 + QG : N) - 1;  // history chunks 0 .. nsteps-1
   const int ct = w % NCTV;
