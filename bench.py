@@ -46,12 +46,12 @@ def log(*a):
 
 # ----------------------------------------------------------------------------- FLOP / byte models
 def flops_transitions(n_chunks, dk, dv):
-    """UT chunk form per chunk: K K^T, the W/U products, the K^T D [W|U] product."""
+    """UT chunk form per 64-token piece: K K^T, the W/U products, the K^T D [W|U] product."""
     return n_chunks * (2 * C * C * dk + 2 * C * C * (dk + dv) + 2 * C * dk * (dk + dv))
 
 
 def flops_routed_output(n_chunks, dk, dv):
-    """Per chunk: Q K^T, P [W|U], Qp S~ (plus the transition-side K K^T and W/U)."""
+    """Per 64-token piece: Q K^T, P [W|U], Qp S~ (plus the transition-side K K^T and W/U)."""
     return n_chunks * (2 * C * C * dk * 2 + 2 * C * C * (dk + dv) * 2 + 2 * C * dk * dv)
 
 
@@ -107,19 +107,26 @@ def timed(fn, steps, warmup, torch):
 
 
 # ----------------------------------------------------------------------------- routed prefill
-def bench_routed_prefill(args, torch, hla, inputs):
+def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None, x=None, tag="routed_prefill"):
+    """The routed prefill step at chunk size Cw (64-token pieces underneath), with the
+    router's computed gates or caller gates."""
     W = inputs.WORKLOADS["routed_prefill"]
-    N = W.N
-    log(f"[routed_prefill] generating inputs B={W.B} T={W.T} H={W.H} d={W.dk}")
-    x = inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["routed_prefill"],
-                          plant_period=W.plant_period)
+    tau = W.tau if tau is None else tau
+    N = math.ceil(W.T / Cw)
+    if x is None:
+        log(f"[{tag}] generating inputs B={W.B} T={W.T} H={W.H} d={W.dk}")
+        x = inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=0,
+                              stream=inputs.STREAM["routed_prefill"], plant_period=W.plant_period)
     q, k, v = (to_dev(a, W.dtype, torch) for a in (x.q, x.k, x.v))
     beta, alpha = to_dev(x.beta, "f32", torch), to_dev(x.alpha, "f32", torch)
     dev = k.device
     At = torch.empty((W.B, W.H, N, W.dk, W.dk), dtype=k.dtype, device=dev)
     Bc = torch.empty((W.B, W.H, N, W.dk, W.dv), dtype=k.dtype, device=dev)
-    d = hla.make_dims(W.B, W.T, W.H, W.T, W.dk, W.dv, hla.HLA_BF16)
-    ws = torch.empty(hla.workspace_bytes(hla.FN_ROUTE_MIX, d, C), dtype=torch.uint8, device=dev)
+    d = hla.make_dims(W.B, W.T, W.H, W.T, W.dk, W.dv, hla.HLA_BF16, Cw)
+    ws = torch.empty(hla.workspace_bytes(hla.FN_ROUTE_MIX, d, Cw), dtype=torch.uint8, device=dev)
+    ws_t = hla._workspace(hla.workspace_bytes(hla.FN_CHUNK_TRANSITIONS, d), dev)
+    ws_p = hla._workspace(hla.workspace_bytes(hla.FN_GDN_PREFILL, d), dev) if Cw != C else None
+    g_in = None if gates_in is None else torch.from_numpy(gates_in).to(dev)
     out = dict(gates=torch.empty((W.B, W.H, N, N), dtype=torch.float32, device=dev),
                mask=torch.empty((W.B, W.H, N, N), dtype=torch.uint8, device=dev),
                active_idx=torch.empty((W.B, W.H, N, N), dtype=torch.int32, device=dev),
@@ -129,9 +136,9 @@ def bench_routed_prefill(args, torch, hla, inputs):
     o = torch.empty((W.B, W.T, W.H, W.dv), dtype=torch.float32, device=dev)
 
     def step():
-        hla.chunk_transitions(k, v, beta, alpha, At=At, Bc=Bc)
-        hla.route_mix(q, k, At, Bc, n_rep=C, tau=W.tau, out=out, ws=ws)
-        hla.gdn_prefill(q, k, v, beta, alpha, chunk_init=out["S_routed"], want_state=False, o=o)
+        hla.chunk_transitions(k, v, beta, alpha, At=At, Bc=Bc, C=Cw, ws=ws_t)
+        hla.route_mix(q, k, At, Bc, n_rep=Cw, tau=tau, gates_in=g_in, out=out, ws=ws, C=Cw)
+        hla.gdn_prefill(q, k, v, beta, alpha, chunk_init=out["S_routed"], want_state=False, o=o, ws=ws_p, C=Cw)
 
     for _ in range(args.warmup):
         step()
@@ -149,10 +156,12 @@ def bench_routed_prefill(args, torch, hla, inputs):
                   (("chunk", hla.KERNEL_CHUNK), ("gates", hla.KERNEL_GATES), ("compose", hla.KERNEL_COMPOSE))}
     hla.timing_enable(False)
 
-    n_chunks = W.B * W.H * N
+    n_pieces = W.B * W.H * math.ceil(W.T / C)
     fl_comp = flops_compose(pairs, W.dk, W.dv)
-    fl_total = (fl_comp + flops_transitions(n_chunks, W.dk, W.dv) + flops_gates(pairs, C, W.dk)
-                + flops_routed_output(n_chunks, W.dk, W.dv))
+    fl_total = (fl_comp + flops_transitions(n_pieces, W.dk, W.dv) + flops_routed_output(n_pieces, W.dk, W.dv)
+                + (flops_gates(pairs, Cw, W.dk) if gates_in is None else 0))
+    if Cw != C:  # composing the C / 64 piece maps of every chunk: [I|0] through C/64 pieces
+        fl_total += W.B * W.H * N * (Cw // C) * 2 * W.dk * W.dk * (W.dk + W.dv)
     comp_avg_s = comp_ms / comp_n / 1e3
     achieved = fl_comp / comp_avg_s / 1e12
     traffic = read_traffic(TRAFFIC_KEY, TRAFFIC_SOURCES)
@@ -166,11 +175,34 @@ def bench_routed_prefill(args, torch, hla, inputs):
                       unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic,
                       flops_per_launch=fl_comp, avg_launch_ms=round(comp_avg_s * 1e3, 4), launches=comp_n),
     )
-    log(f"[routed_prefill] {dt*1e3:.3f} ms/step, {tokens/dt/1e6:.3f} M tok/s, compose {comp_avg_s*1e3:.3f} ms "
-        f"({achieved:.0f} TFLOP/s), step MFMA util {res['mfma_util_pct']:.1f}%")
-    del q, k, v, At, Bc, out, o, ws
+    log(f"[{tag}] {dt*1e3:.3f} ms/step, {tokens/dt/1e6:.3f} M tok/s, compose {comp_avg_s*1e3:.3f} ms "
+        f"({achieved:.0f} TFLOP/s), step MFMA util {res['mfma_util_pct']:.1f}%, active pairs {pairs}")
+    del q, k, v, At, Bc, out, o, ws, ws_t, ws_p, g_in
     torch.cuda.empty_cache()
     return res, x
+
+
+def bench_routed_variants(args, torch, hla, inputs, x):
+    """Secondary routed-prefill lines: the pages' default chunk size (C = 256), and C = 64
+    with skip-heavy caller gates at tau = 0.1 (how skipping cuts the composition)."""
+    W = inputs.WORKLOADS["routed_prefill"]
+    sub = argparse.Namespace(steps=max(3, args.steps // 2), warmup=1)
+    out = {}
+    r, _ = bench_routed_prefill(sub, torch, hla, inputs, Cw=256, x=x, tag="routed_prefill_C256")
+    out["routed_prefill_C256"] = dict(workload="routed_prefill C=256", C=256, tau=W.tau,
+                                      ms_per_step=r["ms_per_step"], tokens_per_s=r["value"],
+                                      mfma_util_pct=r["mfma_util_pct"], active_pairs=r["active_pairs"],
+                                      compose_ms=r["roofline"]["avg_launch_ms"])
+    N = math.ceil(W.T / C)
+    G = inputs.gen_gates(W.B, W.H, N, seed=0, stream=inputs.STREAM["routed_prefill"], mode="skip_heavy")
+    r, _ = bench_routed_prefill(sub, torch, hla, inputs, Cw=C, gates_in=G, tau=0.1, x=x, tag="routed_prefill_skip")
+    dense_pairs = W.B * W.H * N * (N - 1) // 2
+    out["routed_prefill_skip"] = dict(workload="routed_prefill C=64, caller gates sigmoid(N(-4, 3)), tau=0.1",
+                                      C=C, tau=0.1, ms_per_step=r["ms_per_step"], tokens_per_s=r["value"],
+                                      active_pairs=r["active_pairs"], active_frac=r["active_pairs"] / dense_pairs,
+                                      compose_ms=r["roofline"]["avg_launch_ms"],
+                                      compose_tflops_active=r["roofline"]["achieved"])
+    return out
 
 
 # ----------------------------------------------------------------------------- decode
@@ -428,6 +460,7 @@ def main():
     head, x = bench_routed_prefill(args, torch, hla, inputs)
     secondary = {}
     if not args.no_secondary:
+        secondary.update(bench_routed_variants(args, torch, hla, inputs, x))
         secondary["decode"] = bench_decode(args, torch, hla, inputs)
         secondary["native_prefill"] = bench_native_prefill(args, torch, hla, inputs)
         secondary["tail_replay"] = bench_tail_replay(args, torch, hla, inputs)

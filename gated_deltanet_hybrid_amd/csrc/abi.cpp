@@ -17,6 +17,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int64_t n_chunks(const hla_dims_t* d) { return (d->T + d->C - 1) / d->C; }
+// the kernels work on 64-token pieces; a chunk of C tokens is C / 64 consecutive pieces
+constexpr int32_t kPiece = 64;
+int64_t n_pieces(const hla_dims_t* d) { return (d->T + kPiece - 1) / kPiece; }
 
 int64_t dtype_bytes(int32_t dt) { return dt == HLA_BF16 ? 2 : 4; }
 
@@ -27,11 +30,12 @@ hla_status_t check_dims(const hla_dims_t* d) {
   if (d->dtype != HLA_F32 && d->dtype != HLA_BF16) return HLA_ERR_BAD_DTYPE;
   if (d->B < 1 || d->H < 1 || d->T < 1 || d->ld_T < d->T) return HLA_ERR_BAD_SHAPE;
   if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128)) return HLA_ERR_BAD_SHAPE;
-  if (d->C != 64) return HLA_ERR_BAD_SHAPE;
+  if (d->C != 64 && d->C != 128 && d->C != 256) return HLA_ERR_BAD_SHAPE;
+  if (d->C != kPiece && d->dtype != HLA_BF16) return HLA_ERR_UNSUPPORTED;
   // element counts must stay far from int64 overflow, grids within 2^31 blocks
   const double elems = (double)d->B * (double)d->ld_T * (double)d->H * 128.0;
   if (elems > 4.0e18) return HLA_ERR_BAD_SHAPE;
-  const int64_t N = n_chunks(d);
+  const int64_t N = n_pieces(d);
   if ((double)d->B * (double)d->H * (double)N > (double)kMaxGrid) return HLA_ERR_BAD_SHAPE;
   if ((double)d->B * d->H * (double)N * (double)N > 4.0e18) return HLA_ERR_BAD_SHAPE;
   return HLA_OK;
@@ -48,13 +52,14 @@ bool all_aligned4(P... p) {
   return (aligned4(p) && ...);
 }
 
-// Workspace of the native prefill: transitions (dtype) then, when outputs are wanted, the
-// float32 state at the start of every chunk.
+// Workspace of the prefill: transitions of the 64-token pieces (dtype) then, when outputs
+// are wanted, the float32 state at the start of every piece.  The native prefill uses it;
+// a routed prefill with C > 64 uses it to run each chunk's pieces from its routed state.
 struct PrefillWs {
   int64_t at_off, bc_off, st_off, total_ab, total;
 };
 PrefillWs prefill_ws(const hla_dims_t* d) {
-  const int64_t N = n_chunks(d), BHN = d->B * d->H * N, e = dtype_bytes(d->dtype);
+  const int64_t N = n_pieces(d), BHN = d->B * d->H * N, e = dtype_bytes(d->dtype);
   PrefillWs w;
   w.at_off = 0;
   w.bc_off = round_up(BHN * d->dk * d->dk * e, 256);
@@ -101,7 +106,7 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
   if (st != HLA_OK) return st;
   (void)n_rep;
   switch (fn) {
-    case HLA_FN_CHUNK_TRANSITIONS: *out = 0; return HLA_OK;
+    case HLA_FN_CHUNK_TRANSITIONS: *out = d->C == kPiece ? 0 : (size_t)prefill_ws(d).total_ab; return HLA_OK;
     case HLA_FN_GDN_PREFILL: *out = (size_t)prefill_ws(d).total; return HLA_OK;
     case HLA_FN_ROUTE_MIX: *out = (size_t)route_ws(d); return HLA_OK;
     default: return HLA_ERR_UNSUPPORTED;
@@ -109,16 +114,31 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
 }
 
 hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const void* v, const float* beta,
-                                   const float* alpha, void* At, void* Bc, hipStream_t stream) {
+                                   const float* alpha, void* At, void* Bc, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
   hla_status_t st = check_dims(d);
   if (st != HLA_OK) return st;
   if (!k || !v || !beta || !alpha || !At || !Bc) return HLA_ERR_NULL_ARG;
-  if (!all_aligned(k, v, At, Bc) || !all_aligned4(beta, alpha)) return HLA_ERR_ALIGN;
+  if (!all_aligned(k, v, At, Bc, ws) || !all_aligned4(beta, alpha)) return HLA_ERR_ALIGN;
+  const PrefillWs w = prefill_ws(d);
+  if (d->C != kPiece && (!ws || (int64_t)ws_bytes < w.total_ab)) return HLA_ERR_WORKSPACE;
   hla::ChunkArgs a{};
   a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
-  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)n_chunks(d);
-  a.At = At; a.Bc = Bc;
-  return hip_status(hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream));
+  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)n_pieces(d);
+  if (d->C == kPiece) {
+    a.At = At; a.Bc = Bc;
+    return hip_status(hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream));
+  }
+  // pieces of 64 tokens, then the composite map of every C / 64 consecutive pieces
+  char* base = static_cast<char*>(ws);
+  a.At = base + w.at_off;
+  a.Bc = base + w.bc_off;
+  hipError_t e = hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  hla::ScanArgs s{};
+  s.At = a.At; s.Bc = a.Bc; s.B = d->B; s.H = d->H; s.N = a.N;
+  s.seg = d->C / kPiece; s.seg_At = At; s.seg_Bc = Bc;
+  return hip_status(hla::launch_combine_segments(s, d->dk, d->dv, stream));
 }
 
 hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, const void* v,
@@ -130,18 +150,37 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
   if (!o && !S_final) return HLA_ERR_NULL_ARG;
   if (o && !q) return HLA_ERR_NULL_ARG;
   if (!all_aligned(q, k, v, S0, chunk_init, S_final, ws) || !all_aligned4(beta, alpha, o)) return HLA_ERR_ALIGN;
-  const int32_t N = (int32_t)n_chunks(d);
+  const int32_t N = (int32_t)n_pieces(d);
   hla::ChunkArgs a{};
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
   a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = N;
+  const PrefillWs w = prefill_ws(d);
   if (chunk_init) {
     // routed: every chunk starts from its own given state
-    if (S0 || S_final) return HLA_ERR_UNSUPPORTED;
-    a.chunk_init = chunk_init;
+    if (S0 || S_final || !o) return HLA_ERR_UNSUPPORTED;
     a.o = o;
-    return hip_status(hla::launch_chunk(a, d->dtype, d->dk, d->dv, false, true, stream));
+    if (d->C == kPiece) {
+      a.chunk_init = chunk_init;
+      return hip_status(hla::launch_chunk(a, d->dtype, d->dk, d->dv, false, true, stream));
+    }
+    // C > 64: the start state of every 64-token piece from its chunk's routed state
+    if (!ws || (int64_t)ws_bytes < w.total) return HLA_ERR_WORKSPACE;
+    char* base = static_cast<char*>(ws);
+    a.At = base + w.at_off;
+    a.Bc = base + w.bc_off;
+    hipError_t e = hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+    hla::ScanArgs s{};
+    s.At = a.At; s.Bc = a.Bc; s.B = d->B; s.H = d->H; s.N = N;
+    s.seg = d->C / kPiece; s.seg_init = chunk_init;
+    s.states = reinterpret_cast<float*>(base + w.st_off);
+    e = hla::launch_scan_segments(s, d->dk, d->dv, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+    hla::ChunkArgs b = a;
+    b.At = nullptr; b.Bc = nullptr;
+    b.chunk_init = s.states;
+    return hip_status(hla::launch_chunk(b, d->dtype, d->dk, d->dv, false, true, stream));
   }
-  const PrefillWs w = prefill_ws(d);
   const int64_t need = o ? w.total : w.total_ab;
   if (!ws || (int64_t)ws_bytes < need) return HLA_ERR_WORKSPACE;
   char* base = static_cast<char*>(ws);
@@ -183,7 +222,7 @@ hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps,
   a.gates_in = gates_in; a.tau = tau; a.gates = gates; a.mask = mask; a.active_idx = active_idx;
   a.active_cnt = active_cnt; a.n_eff = n_eff; a.S_routed = S_routed; a.qbar = static_cast<float*>(ws);
   a.At_prep = static_cast<char*>(ws) + route_qbar_bytes(d);
-  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)N;
+  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)N; a.C = d->C;
   return hip_status(hla::launch_route(a, d->dtype, d->dk, d->dv, stream));
 }
 

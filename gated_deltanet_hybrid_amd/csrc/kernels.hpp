@@ -32,9 +32,18 @@ struct ScanArgs {
   float* S_final;     // out [B,H,dk,dv] or null
   int64_t B, H;
   int32_t N;
+  // Segmented forms (bf16 only): segments of `seg` consecutive chunks, NS = ceil(N / seg).
+  int32_t seg;
+  const float* seg_init;  // [B,H,NS,dk,dv]: start state of every segment (states are written)
+  void* seg_At;           // out [B,H,NS,dk,dk] (bf16): composite map of every segment
+  void* seg_Bc;           // out [B,H,NS,dk,dv] (bf16)
 };
-// Sequential chunk scan M_{c+1} = At_c M_c + Bc_c.
+// Sequential chunk scan M_{c+1} = At_c M_c + Bc_c (S0, states, S_final).
 hipError_t launch_scan(const ScanArgs& a, int dtype, int dk, int dv, hipStream_t s);
+// Per segment, the start state of every chunk from seg_init (states; bf16).
+hipError_t launch_scan_segments(const ScanArgs& a, int dk, int dv, hipStream_t s);
+// Per segment, the composite map (seg_At, seg_Bc) of its chunks (bf16).
+hipError_t launch_combine_segments(const ScanArgs& a, int dk, int dv, hipStream_t s);
 
 struct RouteArgs {
   const void* q;        // [B,ld_T,H,dk]
@@ -52,6 +61,7 @@ struct RouteArgs {
   int32_t* active_cnt;  // [B,H,N]
   float* n_eff;         // [B,H,N] or null
   float* S_routed;      // [B,H,N,dk,dv]
+  int32_t C;            // tokens per chunk
   float* qbar;          // workspace [B,H,N,dk] float32
   void* At_prep;        // workspace [B,H,N,dk,dk] bf16: (At - I) reordered for the composition
   int64_t B, T, H, ld_T;

@@ -26,8 +26,8 @@ __global__ __launch_bounds__(256) void qbar_kernel(RouteArgs a) {
   const int64_t id = blockIdx.x;  // (b, h, i)
   const int i = (int)(id % a.N);
   const int64_t bh = id / a.N, h = bh % a.H, b = bh / a.H;
-  const int64_t t0 = (int64_t)i * kChunk;
-  const int n = (int)((a.T - t0) < kChunk ? (a.T - t0) : kChunk);
+  const int64_t t0 = (int64_t)i * a.C;
+  const int n = (int)((a.T - t0) < a.C ? (a.T - t0) : a.C);
   const int u = threadIdx.x % UPR, tg = threadIdx.x / UPR;
   const T* q = reinterpret_cast<const T*>(a.q) + ((b * a.ld_T + t0) * a.H + h) * DK + u * PAD;
   float acc[PAD];
@@ -50,16 +50,17 @@ __global__ __launch_bounds__(256) void qbar_kernel(RouteArgs a) {
 }
 
 // ---------------------------------------------------------------- gate scores
-// Workgroup = (b, h, segment of 64 history chunks, group of 4 query tiles of 32 chunks);
+// Workgroup = (b, h, segment of 32 history chunks, group of 4 query tiles of 32 chunks);
 // wave w scores query tile 4 g + w.  Each history chunk's representatives (the MFMA rows)
 // are staged once in LDS with coalesced loads and shared by the four waves; the next
 // chunk's rows are prefetched into registers while the current one is scored.  Queries
 // are the columns, so pooling over representatives is lane-local plus one exchange
 // between the lane halves.
+constexpr int kGateSeg = 32;  // history chunks per workgroup: 2x the workgroups of 64, fewer rounds each
 template <class T, int DK>
 __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
   using MM = Mma<T>;
-  constexpr int JSEG = 64;
+  constexpr int JSEG = kGateSeg;
   constexpr int PAD = 16 / sizeof(T), UPR = DK / PAD;
   constexpr int RT = 32;                  // representatives staged per round
   constexpr int PR = DK + PAD;            // LDS row pitch (elements)
@@ -396,7 +397,7 @@ static hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
     TimedLaunch tl(HLA_KERNEL_GATES, s);
     if (!a.gates_in && a.N > 1) {
       hipLaunchKernelGGL((qbar_kernel<T, DK>), dim3((unsigned)(BH * a.N)), dim3(256), 0, s, a);
-      const int64_t nqt = (a.N + 31) / 32, nqg = (nqt + 3) / 4, njs = (a.N + 63) / 64;
+      const int64_t nqt = (a.N + 31) / 32, nqg = (nqt + 3) / 4, njs = (a.N + kGateSeg - 1) / kGateSeg;
       hipLaunchKernelGGL((gate_kernel<T, DK>), dim3((unsigned)(BH * nqg * njs)), dim3(256), 0, s, a);
     }
     hipLaunchKernelGGL(lists_kernel, dim3((unsigned)(BH * a.N)), dim3(64), 0, s, a);

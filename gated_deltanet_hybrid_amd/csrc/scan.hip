@@ -138,9 +138,18 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
 // [column][k] (so a B fragment is one 16-byte read) and one barrier per chunk publishes it.
 // The image is double-buffered: buffer c % 2 is rewritten only after the next barrier, when
 // every wave has read it.  Bc seeds the accumulator (fp32), so no extra products are needed.
-template <int DK, int DV>
+//
+// MODE 0: one scan over all N chunks from S0 (states, S_final).
+// MODE 1: independent segments of `seg` chunks, each starting from its seg_init state; the
+//         start state of every chunk is written to `states` (a chunk of C = 64 seg tokens
+//         seen as seg chunks of 64).
+// MODE 2: the composite map of every segment: the scan runs over the augmented state
+//         [At_seg | Bc_seg] (dk x (dk + dv)) from [I | 0], the additive term being [0 | Bc]
+//         ([HLA] Methodology paragraph 1: affine maps compose; the map of a chunk of C tokens
+//         is the composition of the maps of its 64-token pieces).
+template <int DK, int DV, int MODE>
 __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
-  constexpr int NCT = DV / 32, NKS = DK / 16;
+  constexpr int NCT = (MODE == 2 ? DK + DV : DV) / 32, NKS = DK / 16;
   constexpr int PB = DK + 8;  // bf16 pitch of an image row (one row per state column)
   __shared__ __attribute__((aligned(16))) bf16 sB0[32 * PB];
   __shared__ __attribute__((aligned(16))) bf16 sB1[32 * PB];
@@ -149,18 +158,41 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
   const int rt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t id = blockIdx.x;
   const int ct = (int)(id % NCT);
-  const int64_t bh = id / NCT;
+  const int64_t rest = id / NCT;
   const int N = a.N;
-  const bf16* arow = reinterpret_cast<const bf16*>(a.At) + bh * N * (int64_t)DK * DK + (rt * 32 + c32) * DK + hh * 8;
-  const bf16* bcol = reinterpret_cast<const bf16*>(a.Bc) + bh * N * (int64_t)DK * DV + rt * 32 * DV + ct * 32 + c32;
+  int64_t bh = rest;
+  int NS = 1, g = 0, c0 = 0, nsub = N;
+  if (MODE != 0) {
+    NS = (N + a.seg - 1) / a.seg;
+    g = (int)(rest % NS);
+    bh = rest / NS;
+    c0 = g * a.seg;
+    nsub = N - c0 < a.seg ? N - c0 : a.seg;
+  }
+  // MODE 2: column blocks [0, DK/32) are the At part (additive term 0), the rest the Bc part
+  const bool apart = MODE == 2 && ct < DK / 32;
+  const int bcolumn = MODE == 2 ? (apart ? 0 : (ct - DK / 32) * 32) : ct * 32;
+  const bf16* arow = reinterpret_cast<const bf16*>(a.At) + (bh * N + c0) * (int64_t)DK * DK + (rt * 32 + c32) * DK +
+                     hh * 8;
+  const bf16* bcol =
+      reinterpret_cast<const bf16*>(a.Bc) + (bh * N + c0) * (int64_t)DK * DV + rt * 32 * DV + bcolumn + c32;
   // accumulator element e of this lane: row 32 rt + (e / 4) 8 + 4 hh + e % 4, column 32 ct + c32
   auto row_of = [&](int e) { return (e >> 2) * 8 + hh * 4 + (e & 3); };
 
   f32x16 M = zero16();
-  if (a.S0) {
+  if (MODE == 0 && a.S0) {
     const float* s0 = a.S0 + bh * (int64_t)DK * DV + rt * 32 * DV + ct * 32 + c32;
 #pragma unroll
     for (int e = 0; e < 16; ++e) M[e] = s0[row_of(e) * DV];
+  }
+  if (MODE == 1) {
+    const float* s0 = a.seg_init + (bh * NS + g) * (int64_t)DK * DV + rt * 32 * DV + ct * 32 + c32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) M[e] = s0[row_of(e) * DV];
+  }
+  if (apart) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) M[e] = (rt * 32 + row_of(e) == ct * 32 + c32) ? 1.f : 0.f;
   }
   bf16x8 af[NKS];
   bf16 bcv[16];
@@ -168,35 +200,37 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
     const bf16* ap = arow + (int64_t)c * DK * DK;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(ap + ks * 16);
-    const bf16* bp = bcol + (int64_t)c * DK * DV;
+    if (!apart) {
+      const bf16* bp = bcol + (int64_t)c * DK * DV;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) bcv[e] = bp[row_of(e) * DV];
+      for (int e = 0; e < 16; ++e) bcv[e] = bp[row_of(e) * DV];
+    }
   };
   auto store_state = [&](float* dst) __attribute__((always_inline)) {
     float* p = dst + rt * 32 * DV + ct * 32 + c32;
 #pragma unroll
     for (int e = 0; e < 16; ++e) p[row_of(e) * DV] = M[e];
   };
-  if (N > 0) load(0);
-  for (int c = 0; c < N; ++c) {
-    if (a.states) store_state(a.states + (bh * N + c) * (int64_t)DK * DV);
+  if (nsub > 0) load(0);
+  for (int c = 0; c < nsub; ++c) {
+    if (MODE != 2 && a.states) store_state(a.states + (bh * N + c0 + c) * (int64_t)DK * DV);
     bf16* img = (c & 1) ? sB1 : sB0;
     // this wave's rows of bf16(M) into the image: 4 runs of 4 consecutive k per lane
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int gq = 0; gq < 4; ++gq) {
       bf16x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (bf16)M[g * 4 + e];
-      *reinterpret_cast<bf16x4*>(img + c32 * PB + rt * 32 + g * 8 + hh * 4) = v;
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)M[gq * 4 + e];
+      *reinterpret_cast<bf16x4*>(img + c32 * PB + rt * 32 + gq * 8 + hh * 4) = v;
     }
     __syncthreads();
     f32x16 acc0, acc1 = zero16();
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc0[e] = (float)bcv[e];
+    for (int e = 0; e < 16; ++e) acc0[e] = apart ? 0.f : (float)bcv[e];
     bf16x8 cur[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) cur[ks] = af[ks];
-    if (c + 1 < N) load(c + 1);
+    if (c + 1 < nsub) load(c + 1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(img + c32 * PB + ks * 16 + hh * 8);
@@ -208,7 +242,19 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) M[e] = acc0[e] + acc1[e];
   }
-  if (a.S_final) store_state(a.S_final + bh * (int64_t)DK * DV);
+  if (MODE == 0 && a.S_final) store_state(a.S_final + bh * (int64_t)DK * DV);
+  if (MODE == 2) {
+    const int64_t sidx = bh * NS + g;
+    if (apart) {
+      bf16* p = reinterpret_cast<bf16*>(a.seg_At) + sidx * DK * DK + rt * 32 * DK + ct * 32 + c32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p[row_of(e) * DK] = (bf16)M[e];
+    } else {
+      bf16* p = reinterpret_cast<bf16*>(a.seg_Bc) + sidx * DK * DV + rt * 32 * DV + bcolumn + c32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p[row_of(e) * DV] = (bf16)M[e];
+    }
+  }
 }
 
 template <class T, int DK, int DV>
@@ -231,23 +277,36 @@ static hipError_t launch_scan_d(const ScanArgs& a, int dk, int dv, hipStream_t s
   return launch_scan_t<T, 128, 128>(a, s);
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int MODE>
 static hipError_t launch_scan_bf16_t(const ScanArgs& a, hipStream_t s) {
-  const int64_t nb = a.B * a.H * (DV / 32);
+  constexpr int NCT = (MODE == 2 ? DK + DV : DV) / 32;
+  const int64_t ns = MODE == 0 ? 1 : (a.N + a.seg - 1) / a.seg;
+  const int64_t nb = a.B * a.H * ns * NCT;
   if (nb == 0) return hipSuccess;
   TimedLaunch tl(HLA_KERNEL_SCAN, s);
-  hipLaunchKernelGGL((scan_bf16_kernel<DK, DV>), dim3((unsigned)nb), dim3(DK / 32 * 64), 0, s, a);
+  hipLaunchKernelGGL((scan_bf16_kernel<DK, DV, MODE>), dim3((unsigned)nb), dim3(DK / 32 * 64), 0, s, a);
   return hipGetLastError();
 }
 
+template <int MODE>
+static hipError_t launch_scan_bf16(const ScanArgs& a, int dk, int dv, hipStream_t s) {
+  if (dk == 64 && dv == 64) return launch_scan_bf16_t<64, 64, MODE>(a, s);
+  if (dk == 64 && dv == 128) return launch_scan_bf16_t<64, 128, MODE>(a, s);
+  if (dk == 128 && dv == 64) return launch_scan_bf16_t<128, 64, MODE>(a, s);
+  return launch_scan_bf16_t<128, 128, MODE>(a, s);
+}
+
 hipError_t launch_scan(const ScanArgs& a, int dtype, int dk, int dv, hipStream_t s) {
-  if (dtype == 1) {
-    if (dk == 64 && dv == 64) return launch_scan_bf16_t<64, 64>(a, s);
-    if (dk == 64 && dv == 128) return launch_scan_bf16_t<64, 128>(a, s);
-    if (dk == 128 && dv == 64) return launch_scan_bf16_t<128, 64>(a, s);
-    return launch_scan_bf16_t<128, 128>(a, s);
-  }
+  if (dtype == 1) return launch_scan_bf16<0>(a, dk, dv, s);
   return launch_scan_d<float>(a, dk, dv, s);
+}
+
+hipError_t launch_scan_segments(const ScanArgs& a, int dk, int dv, hipStream_t s) {
+  return launch_scan_bf16<1>(a, dk, dv, s);
+}
+
+hipError_t launch_combine_segments(const ScanArgs& a, int dk, int dv, hipStream_t s) {
+  return launch_scan_bf16<2>(a, dk, dv, s);
 }
 
 }  // namespace hla

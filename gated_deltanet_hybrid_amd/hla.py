@@ -40,7 +40,8 @@ _SIGS = {
     "hla_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "hla_workspace_bytes": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(Dims), ctypes.c_int32,
                                              ctypes.POINTER(ctypes.c_size_t)]),
-    "hla_chunk_transitions": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P]),
+    "hla_chunk_transitions": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                               _P]),
     "hla_gdn_prefill": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]),
     "hla_route_mix": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
@@ -117,8 +118,8 @@ def _need(t, shape, dtype, name):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
 
 
-def make_dims(B, T, H, ld_T, dk, dv, dtype_code) -> Dims:
-    return Dims(B, T, H, ld_T, dk, dv, CHUNK, dtype_code)
+def make_dims(B, T, H, ld_T, dk, dv, dtype_code, C=CHUNK) -> Dims:
+    return Dims(B, T, H, ld_T, dk, dv, C, dtype_code)
 
 
 def workspace_bytes(fn: int, dims: Dims, n_rep: int = 0) -> int:
@@ -131,7 +132,7 @@ def _workspace(nbytes: int, device) -> torch.Tensor | None:
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device) if nbytes else None
 
 
-def _inputs(k, v, beta, alpha, q=None):
+def _inputs(k, v, beta, alpha, q=None, C=CHUNK):
     B, T, H, dk, ld_T = _token_view(k, "k")
     Bv, Tv, Hv, dv, ldv = _token_view(v, "v")
     if (Bv, Tv, Hv, ldv) != (B, T, H, ld_T) or v.dtype != k.dtype:
@@ -142,27 +143,31 @@ def _inputs(k, v, beta, alpha, q=None):
             raise ValueError("q must match k")
     _scalar_view(beta, B, T, H, ld_T, "beta")
     _scalar_view(alpha, B, T, H, ld_T, "alpha")
-    return make_dims(B, T, H, ld_T, dk, dv, _dtype_code(k))
+    return make_dims(B, T, H, ld_T, dk, dv, _dtype_code(k), C)
 
 
-def chunk_transitions(k, v, beta, alpha, At=None, Bc=None):
-    """Exact affine map (At, Bc) of every 64-token chunk: M_end = At M_start + Bc."""
-    d = _inputs(k, v, beta, alpha)
-    N = math.ceil(d.T / CHUNK)
+def chunk_transitions(k, v, beta, alpha, At=None, Bc=None, C=CHUNK, ws=None):
+    """Exact affine map (At, Bc) of every C-token chunk: M_end = At M_start + Bc."""
+    d = _inputs(k, v, beta, alpha, C=C)
+    N = math.ceil(d.T / C)
     At = torch.empty((d.B, d.H, N, d.dk, d.dk), dtype=k.dtype, device=k.device) if At is None else At
     Bc = torch.empty((d.B, d.H, N, d.dk, d.dv), dtype=k.dtype, device=k.device) if Bc is None else Bc
     _need(At, (d.B, d.H, N, d.dk, d.dk), k.dtype, "At")
     _need(Bc, (d.B, d.H, N, d.dk, d.dv), k.dtype, "Bc")
+    if ws is None:
+        ws = _workspace(workspace_bytes(FN_CHUNK_TRANSITIONS, d), k.device)
     _check(library().hla_chunk_transitions(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(At),
-                                           _ptr(Bc), _stream(k.device)), "hla_chunk_transitions")
+                                           _ptr(Bc), _ptr(ws), 0 if ws is None else ws.numel(), _stream(k.device)),
+           "hla_chunk_transitions")
     return At, Bc
 
 
 def gdn_prefill(q, k, v, beta, alpha, S0=None, chunk_init=None, want_o=True, want_state=True, o=None,
-                S_final=None, ws=None):
-    """Chunkwise gated delta rule prefill.  Returns (o [B,T,H,dv] or None, S_final or None)."""
-    d = _inputs(k, v, beta, alpha, q if want_o else None)
-    N = math.ceil(d.T / CHUNK)
+                S_final=None, ws=None, C=CHUNK):
+    """Chunkwise gated delta rule prefill.  Returns (o [B,T,H,dv] or None, S_final or None).
+    C is the chunk size of chunk_init (routed mode); native results do not depend on it."""
+    d = _inputs(k, v, beta, alpha, q if want_o else None, C=C)
+    N = math.ceil(d.T / C)
     dev = k.device
     if want_o and o is None:
         o = torch.empty((d.B, d.T, d.H, d.dv), dtype=torch.float32, device=dev)
@@ -178,7 +183,7 @@ def gdn_prefill(q, k, v, beta, alpha, S0=None, chunk_init=None, want_o=True, wan
     _need(S0, (d.B, d.H, d.dk, d.dv), torch.float32, "S0")
     _need(chunk_init, (d.B, d.H, N, d.dk, d.dv), torch.float32, "chunk_init")
     _need(S_final, (d.B, d.H, d.dk, d.dv), torch.float32, "S_final")
-    if ws is None and chunk_init is None:
+    if ws is None and (chunk_init is None or C != CHUNK):
         ws = _workspace(workspace_bytes(FN_GDN_PREFILL, d), dev)
     _check(library().hla_gdn_prefill(ctypes.byref(d), _ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(beta),
                                      _ptr(alpha), _ptr(S0), _ptr(chunk_init), _ptr(o), _ptr(S_final), _ptr(ws),
@@ -186,7 +191,8 @@ def gdn_prefill(q, k, v, beta, alpha, S0=None, chunk_init=None, want_o=True, wan
     return o, S_final
 
 
-def route_mix(q, reps, At, Bc, n_rep=CHUNK, tau=1e-3, S0=None, gates_in=None, T=None, out=None, ws=None):
+def route_mix(q, reps, At, Bc, n_rep=CHUNK, tau=1e-3, S0=None, gates_in=None, T=None, out=None, ws=None,
+              C=CHUNK):
     """Router gates, skip mask, active lists, n_eff and the routed per-chunk states.
 
     q [B, T, H, dk] (token window), reps [B, R, H, dk] (token window, chunk j's
@@ -198,17 +204,17 @@ def route_mix(q, reps, At, Bc, n_rep=CHUNK, tau=1e-3, S0=None, gates_in=None, T=
     dev = At.device
     if q is not None:
         Bq, Tq, Hq, dq, ld_T = _token_view(q, "q")
-        if (Bq, Hq, dq) != (B, H, dk) or math.ceil(Tq / CHUNK) != N:
+        if (Bq, Hq, dq) != (B, H, dk) or math.ceil(Tq / C) != N:
             raise ValueError("q does not match the transitions")
         T = Tq
     else:
-        ld_T = T = T if T is not None else N * CHUNK
+        ld_T = T = T if T is not None else N * C
     ld_R = 0
     if reps is not None:
         Br, Rr, Hr, dr, ld_R = _token_view(reps, "reps")
         if (Br, Hr, dr) != (B, H, dk) or reps.dtype != At.dtype:
             raise ValueError("reps must be [B, R, H, dk] in the transitions' dtype")
-    d = make_dims(B, T, H, ld_T, dk, dv, _dtype_code(At))
+    d = make_dims(B, T, H, ld_T, dk, dv, _dtype_code(At), C)
     _need(At, (B, H, N, dk, dk), At.dtype, "At")
     _need(Bc, (B, H, N, dk, dv), At.dtype, "Bc")
     _need(S0, (B, H, dk, dv), torch.float32, "S0")
@@ -229,11 +235,12 @@ def route_mix(q, reps, At, Bc, n_rep=CHUNK, tau=1e-3, S0=None, gates_in=None, T=
     return dict(gates=gates, mask=mask, active_idx=aidx, active_cnt=acnt, n_eff=neff, S_routed=Sr)
 
 
-def hla_prefill(q, k, v, beta, alpha, tau=1e-3, gates_in=None, S0=None):
-    """The routed prefill as three calls: transitions, routing, outputs from routed states."""
-    At, Bc = chunk_transitions(k, v, beta, alpha)
-    r = route_mix(q, k, At, Bc, n_rep=CHUNK, tau=tau, S0=S0, gates_in=gates_in)
-    o, _ = gdn_prefill(q, k, v, beta, alpha, chunk_init=r["S_routed"], want_state=False)
+def hla_prefill(q, k, v, beta, alpha, tau=1e-3, gates_in=None, S0=None, C=CHUNK):
+    """The routed prefill as three calls: transitions, routing, outputs from routed states.
+    Representatives are each chunk's raw keys (n_rep = C)."""
+    At, Bc = chunk_transitions(k, v, beta, alpha, C=C)
+    r = route_mix(q, k, At, Bc, n_rep=C, tau=tau, S0=S0, gates_in=gates_in, C=C)
+    o, _ = gdn_prefill(q, k, v, beta, alpha, chunk_init=r["S_routed"], want_state=False, C=C)
     r.update(At=At, Bc=Bc, o=o)
     return r
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define HLA_ABI_VERSION 1
+#define HLA_ABI_VERSION 2
 
 typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype_t;
 
@@ -67,7 +67,9 @@ typedef enum {
 } hla_status_t;
 
 /* Problem sizes.  B batch rows, T tokens processed per row, H heads, ld_T >= T tokens
- * allocated per row; dk, dv in {64, 128}; C = 64 tokens per chunk. */
+ * allocated per row; dk, dv in {64, 128}; C in {64, 128, 256} tokens per chunk (C > 64
+ * needs dtype HLA_BF16, else HLA_ERR_UNSUPPORTED).  The kernels work on 64-token pieces;
+ * a chunk of C tokens is C / 64 consecutive pieces, and its map is their composition. */
 typedef struct {
   int64_t B, T, H, ld_T;
   int32_t dk, dv, C;
@@ -85,11 +87,15 @@ typedef enum { HLA_FN_CHUNK_TRANSITIONS = 0, HLA_FN_GDN_PREFILL = 1, HLA_FN_ROUT
  * diag(beta)(K K^T o decay) is inverted per chunk instead of running the token loop.
  *   k, v, beta, alpha : inputs as in the header notes (q is not needed).
  *   At [B, H, N, dk, dk], Bc [B, H, N, dk, dv] (out, dtype): M_end = At M_start + Bc.
- * Errors: HLA_ERR_NULL_ARG, HLA_ERR_BAD_SHAPE, HLA_ERR_BAD_DTYPE, HLA_ERR_ALIGN, HLA_ERR_HIP.
+ *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_CHUNK_TRANSITIONS)
+ *           bytes (zero for C = 64; for C > 64 it holds the maps of the 64-token pieces,
+ *           which are then composed C / 64 at a time: [HLA] Methodology paragraph 1).
+ * Errors: HLA_ERR_NULL_ARG, HLA_ERR_BAD_SHAPE, HLA_ERR_BAD_DTYPE, HLA_ERR_ALIGN,
+ *         HLA_ERR_WORKSPACE, HLA_ERR_UNSUPPORTED, HLA_ERR_HIP.
  */
 hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const void* v,
                                    const float* beta, const float* alpha, void* At, void* Bc,
-                                   hipStream_t stream);
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * hla_gdn_prefill -- chunkwise Gated DeltaNet prefill.
@@ -109,7 +115,9 @@ hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const voi
  *   o          [B, T, H, dv] float32 (out) or NULL.
  *   S_final    [B, H, dk, dv] float32 (out) or NULL.  At least one of o, S_final.
  *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_GDN_PREFILL) bytes
- *           (zero in routed mode).
+ *           (none in routed mode with C = 64; in routed mode with C > 64 every chunk's
+ *           64-token pieces start from states scanned from its routed state).  The
+ *           native outputs do not depend on C: the prefill runs on 64-token pieces.
  * Errors: as hla_chunk_transitions, plus HLA_ERR_WORKSPACE, HLA_ERR_UNSUPPORTED.
  */
 hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, const void* v,

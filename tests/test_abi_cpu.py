@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hla_abi_version() == 1
+    assert lib.hla_abi_version() == 2
     for s in range(0, 9):
         assert lib.hla_status_string(s)
     assert lib.hla_status_string(99) == b"unknown status"
@@ -59,25 +59,49 @@ def test_workspace_sizes(lib):
     assert lib.hla_workspace_bytes(0, ctypes.byref(d), 0, None) == NULL_ARG
 
 
+def test_workspace_sizes_larger_chunks(lib):
+    # C = 256 over T = 700: 3 chunks of 256 tokens, 11 pieces of 64
+    d = dims(B=1, T=700, H=2, dk=128, dv=128, C=256, dtype=1)
+    pieces = 1 * 2 * 11
+    ab = pieces * 128 * 128 * 2 + pieces * 128 * 128 * 2
+    # the transitions of the 64-token pieces are composed four at a time
+    assert hla.workspace_bytes(hla.FN_CHUNK_TRANSITIONS, d) == ab
+    # the prefill runs on pieces whatever C is
+    assert hla.workspace_bytes(hla.FN_GDN_PREFILL, d) == ab + pieces * 128 * 128 * 4
+    assert hla.workspace_bytes(hla.FN_ROUTE_MIX, d) == 2 * 3 * 128 * 4 + 2 * 3 * 128 * 128 * 2
+
+
 @pytest.mark.parametrize("kw,code", [
-    (dict(dk=96), BAD_SHAPE), (dict(dv=32), BAD_SHAPE), (dict(C=128), BAD_SHAPE), (dict(T=0), BAD_SHAPE),
-    (dict(ld_T=100), BAD_SHAPE), (dict(B=0), BAD_SHAPE), (dict(H=0), BAD_SHAPE), (dict(dtype=2), BAD_DTYPE),
+    (dict(dk=96), BAD_SHAPE), (dict(dv=32), BAD_SHAPE), (dict(C=96), BAD_SHAPE), (dict(C=512), BAD_SHAPE),
+    (dict(T=0), BAD_SHAPE), (dict(ld_T=100), BAD_SHAPE), (dict(B=0), BAD_SHAPE), (dict(H=0), BAD_SHAPE),
+    (dict(dtype=2), BAD_DTYPE), (dict(C=128, dtype=0), UNSUPPORTED),
 ])
 def test_chunk_transitions_rejects_bad_dims(lib, kw, code):
     d = dims(**kw)
-    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, None) == code
+    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, None, 0, None) == code
+
+
+def test_larger_chunks_need_workspace(lib):
+    d = dims(C=128)
+    need = hla.workspace_bytes(hla.FN_CHUNK_TRANSITIONS, d)
+    assert need > 0
+    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, None, 0, None) == WORKSPACE
+    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, P, need - 1, None) == WORKSPACE
+    # routed outputs with C > 64 scan the pieces of every chunk from its routed state
+    pre = lib.hla_gdn_prefill
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, P, P, None, None, 0, None) == WORKSPACE
 
 
 def test_chunk_transitions_rejects_null_and_misaligned(lib):
     d = dims()
-    assert lib.hla_chunk_transitions(None, P, P, P, P, P, P, None) == NULL_ARG
+    assert lib.hla_chunk_transitions(None, P, P, P, P, P, P, None, 0, None) == NULL_ARG
     for i in range(6):
         args = [P] * 6
         args[i] = None
-        assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None) == NULL_ARG
+        assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None, 0, None) == NULL_ARG
         # vector-loaded tensors need 16 bytes, the per-token scalars (beta, alpha) 4
         args[i] = P + 2 if i in (2, 3) else PU
-        assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None) == ALIGN
+        assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None, 0, None) == ALIGN
 
 
 def test_prefill_validation(lib):
