@@ -190,10 +190,21 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) M[e] = s0[row_of(e) * DV];
   }
-  if (apart) {
+  // MODE 2 starts from the first piece's own map ([I | 0] through piece 0 is [At_0 | Bc_0])
+  int cstart = 0;
+  if (MODE == 2 && nsub > 0) {
+    cstart = 1;
+    if (apart) {
+      const bf16* p0 = reinterpret_cast<const bf16*>(a.At) + (bh * N + c0) * (int64_t)DK * DK + rt * 32 * DK + ct * 32 + c32;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) M[e] = (rt * 32 + row_of(e) == ct * 32 + c32) ? 1.f : 0.f;
+      for (int e = 0; e < 16; ++e) M[e] = (float)p0[row_of(e) * DK];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) M[e] = (float)bcol[row_of(e) * DV];
+    }
   }
+  // MODE 1 never needs the end state of a segment's last piece
+  const int nmul = MODE == 1 ? nsub - 1 : nsub;
   bf16x8 af[NKS];
   bf16 bcv[16];
   auto load = [&](int c) __attribute__((always_inline)) {
@@ -211,9 +222,10 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) p[row_of(e) * DV] = M[e];
   };
-  if (nsub > 0) load(0);
-  for (int c = 0; c < nsub; ++c) {
+  if (cstart < nmul) load(cstart);
+  for (int c = cstart; c < nsub; ++c) {
     if (MODE != 2 && a.states) store_state(a.states + (bh * N + c0 + c) * (int64_t)DK * DV);
+    if (c >= nmul) break;
     bf16* img = (c & 1) ? sB1 : sB0;
     // this wave's rows of bf16(M) into the image: 4 runs of 4 consecutive k per lane
 #pragma unroll
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
     bf16x8 cur[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) cur[ks] = af[ks];
-    if (c + 1 < nsub) load(c + 1);
+    if (c + 1 < nmul) load(c + 1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(img + c32 * PB + ks * 16 + hh * 8);
