@@ -51,8 +51,8 @@ def flops_transitions(n_chunks, dk, dv):
 
 
 def flops_routed_output(n_chunks, dk, dv):
-    """Per 64-token piece: Q K^T, P [W|U], Qp S~ (plus the transition-side K K^T and W/U)."""
-    return n_chunks * (2 * C * C * dk * 2 + 2 * C * C * (dk + dv) * 2 + 2 * C * dk * dv)
+    """Per 64-token piece: Q K^T, P [W|U], Qp S~ (W|U come from the transitions pass)."""
+    return n_chunks * (2 * C * C * dk + 2 * C * C * (dk + dv) + 2 * C * dk * dv)
 
 
 def flops_gates(pairs, n_rep, dk):
@@ -107,9 +107,11 @@ def timed(fn, steps, warmup, torch):
 
 
 # ----------------------------------------------------------------------------- routed prefill
-def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None, x=None, tag="routed_prefill"):
+def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None, x=None, tag="routed_prefill",
+                         handoff=True):
     """The routed prefill step at chunk size Cw (64-token pieces underneath), with the
-    router's computed gates or caller gates."""
+    router's computed gates or caller gates; handoff passes W | U from the transitions
+    call to the output call."""
     W = inputs.WORKLOADS["routed_prefill"]
     tau = W.tau if tau is None else tau
     N = math.ceil(W.T / Cw)
@@ -126,6 +128,7 @@ def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None
     ws = torch.empty(hla.workspace_bytes(hla.FN_ROUTE_MIX, d, Cw), dtype=torch.uint8, device=dev)
     ws_t = hla._workspace(hla.workspace_bytes(hla.FN_CHUNK_TRANSITIONS, d), dev)
     ws_p = hla._workspace(hla.workspace_bytes(hla.FN_GDN_PREFILL, d), dev) if Cw != C else None
+    wu = hla._workspace(hla.workspace_bytes(hla.FN_WU_HANDOFF, d), dev) if handoff else None
     g_in = None if gates_in is None else torch.from_numpy(gates_in).to(dev)
     out = dict(gates=torch.empty((W.B, W.H, N, N), dtype=torch.float32, device=dev),
                mask=torch.empty((W.B, W.H, N, N), dtype=torch.uint8, device=dev),
@@ -136,9 +139,10 @@ def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None
     o = torch.empty((W.B, W.T, W.H, W.dv), dtype=torch.float32, device=dev)
 
     def step():
-        hla.chunk_transitions(k, v, beta, alpha, At=At, Bc=Bc, C=Cw, ws=ws_t)
+        hla.chunk_transitions(k, v, beta, alpha, At=At, Bc=Bc, C=Cw, ws=ws_t, wu=wu)
         hla.route_mix(q, k, At, Bc, n_rep=Cw, tau=tau, gates_in=g_in, out=out, ws=ws, C=Cw)
-        hla.gdn_prefill(q, k, v, beta, alpha, chunk_init=out["S_routed"], want_state=False, o=o, ws=ws_p, C=Cw)
+        hla.gdn_prefill(q, k, v, beta, alpha, chunk_init=out["S_routed"], want_state=False, o=o, ws=ws_p, C=Cw,
+                        wu=wu)
 
     for _ in range(args.warmup):
         step()

@@ -52,11 +52,23 @@ bool all_aligned4(P... p) {
   return (aligned4(p) && ...);
 }
 
-// Workspace of the prefill: transitions of the 64-token pieces (dtype) then, when outputs
-// are wanted, the float32 state at the start of every piece.  The native prefill uses it;
-// a routed prefill with C > 64 uses it to run each chunk's pieces from its routed state.
+// The transitions pass of a prefill hands W | U of every piece to its output pass through
+// the workspace (bf16 only) instead of the output pass inverting the chunk matrix again.
+#ifndef HLA_WU_HANDOFF
+#define HLA_WU_HANDOFF 1
+#endif
+
+// Bytes of the W | U image of every 64-token piece (bf16; float32 takes no hand-off).
+int64_t wu_bytes(const hla_dims_t* d) {
+  return d->dtype == HLA_BF16 ? d->B * d->H * n_pieces(d) * hla::aux_chunk_bytes(d->dk, d->dv) : 0;
+}
+
+// Workspace of the prefill: transitions of the 64-token pieces (dtype), then, when outputs
+// are wanted, the W | U hand-off (bf16) and the float32 state at the start of every piece.
+// The native prefill uses it; a routed prefill with C > 64 uses it to run each chunk's
+// pieces from its routed state.
 struct PrefillWs {
-  int64_t at_off, bc_off, st_off, total_ab, total;
+  int64_t at_off, bc_off, wu_off, st_off, total_ab, total;
 };
 PrefillWs prefill_ws(const hla_dims_t* d) {
   const int64_t N = n_pieces(d), BHN = d->B * d->H * N, e = dtype_bytes(d->dtype);
@@ -64,7 +76,8 @@ PrefillWs prefill_ws(const hla_dims_t* d) {
   w.at_off = 0;
   w.bc_off = round_up(BHN * d->dk * d->dk * e, 256);
   w.total_ab = w.bc_off + round_up(BHN * d->dk * d->dv * e, 256);
-  w.st_off = w.total_ab;
+  w.wu_off = w.total_ab;
+  w.st_off = w.wu_off + (HLA_WU_HANDOFF ? round_up(wu_bytes(d), 256) : 0);
   w.total = w.st_off + round_up(BHN * d->dk * d->dv * 4, 256);
   return w;
 }
@@ -78,6 +91,12 @@ int64_t route_ws(const hla_dims_t* d) {
 }
 
 hla_status_t hip_status(hipError_t e) { return e == hipSuccess ? HLA_OK : HLA_ERR_HIP; }
+
+// Where a prefill's own transitions pass writes W | U: nowhere when the caller supplies
+// them (or for float32), else the workspace region.
+void* wu_internal(const hla_dims_t* d, const void* wu, void* region) {
+  return (wu || !HLA_WU_HANDOFF || d->dtype != HLA_BF16) ? nullptr : region;
+}
 
 }  // namespace
 
@@ -109,21 +128,24 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
     case HLA_FN_CHUNK_TRANSITIONS: *out = d->C == kPiece ? 0 : (size_t)prefill_ws(d).total_ab; return HLA_OK;
     case HLA_FN_GDN_PREFILL: *out = (size_t)prefill_ws(d).total; return HLA_OK;
     case HLA_FN_ROUTE_MIX: *out = (size_t)route_ws(d); return HLA_OK;
+    case HLA_FN_WU_HANDOFF: *out = (size_t)wu_bytes(d); return HLA_OK;
     default: return HLA_ERR_UNSUPPORTED;
   }
 }
 
 hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const void* v, const float* beta,
-                                   const float* alpha, void* At, void* Bc, void* ws, size_t ws_bytes,
+                                   const float* alpha, void* At, void* Bc, void* wu, void* ws, size_t ws_bytes,
                                    hipStream_t stream) {
   hla_status_t st = check_dims(d);
   if (st != HLA_OK) return st;
   if (!k || !v || !beta || !alpha || !At || !Bc) return HLA_ERR_NULL_ARG;
-  if (!all_aligned(k, v, At, Bc, ws) || !all_aligned4(beta, alpha)) return HLA_ERR_ALIGN;
+  if (!all_aligned(k, v, At, Bc, wu, ws) || !all_aligned4(beta, alpha)) return HLA_ERR_ALIGN;
+  if (wu && d->dtype != HLA_BF16) return HLA_ERR_UNSUPPORTED;
   const PrefillWs w = prefill_ws(d);
   if (d->C != kPiece && (!ws || (int64_t)ws_bytes < w.total_ab)) return HLA_ERR_WORKSPACE;
   hla::ChunkArgs a{};
   a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
+  a.aux_out = wu;
   a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)n_pieces(d);
   if (d->C == kPiece) {
     a.At = At; a.Bc = Bc;
@@ -143,13 +165,15 @@ hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const voi
 
 hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, const void* v,
                              const float* beta, const float* alpha, const float* S0, const float* chunk_init,
-                             float* o, float* S_final, void* ws, size_t ws_bytes, hipStream_t stream) {
+                             const void* wu, float* o, float* S_final, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
   hla_status_t st = check_dims(d);
   if (st != HLA_OK) return st;
   if (!k || !v || !beta || !alpha) return HLA_ERR_NULL_ARG;
   if (!o && !S_final) return HLA_ERR_NULL_ARG;
   if (o && !q) return HLA_ERR_NULL_ARG;
-  if (!all_aligned(q, k, v, S0, chunk_init, S_final, ws) || !all_aligned4(beta, alpha, o)) return HLA_ERR_ALIGN;
+  if (!all_aligned(q, k, v, S0, chunk_init, wu, S_final, ws) || !all_aligned4(beta, alpha, o)) return HLA_ERR_ALIGN;
+  if (wu && d->dtype != HLA_BF16) return HLA_ERR_UNSUPPORTED;
   const int32_t N = (int32_t)n_pieces(d);
   hla::ChunkArgs a{};
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
@@ -161,6 +185,7 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
     a.o = o;
     if (d->C == kPiece) {
       a.chunk_init = chunk_init;
+      a.aux_in = wu;
       return hip_status(hla::launch_chunk(a, d->dtype, d->dk, d->dv, false, true, stream));
     }
     // C > 64: the start state of every 64-token piece from its chunk's routed state
@@ -168,6 +193,7 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
     char* base = static_cast<char*>(ws);
     a.At = base + w.at_off;
     a.Bc = base + w.bc_off;
+    a.aux_out = wu_internal(d, wu, base + w.wu_off);
     hipError_t e = hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream);
     if (e != hipSuccess) return HLA_ERR_HIP;
     hla::ScanArgs s{};
@@ -177,7 +203,8 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
     e = hla::launch_scan_segments(s, d->dk, d->dv, stream);
     if (e != hipSuccess) return HLA_ERR_HIP;
     hla::ChunkArgs b = a;
-    b.At = nullptr; b.Bc = nullptr;
+    b.At = nullptr; b.Bc = nullptr; b.aux_out = nullptr;
+    b.aux_in = wu ? wu : a.aux_out;
     b.chunk_init = s.states;
     return hip_status(hla::launch_chunk(b, d->dtype, d->dk, d->dv, false, true, stream));
   }
@@ -186,6 +213,7 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
   char* base = static_cast<char*>(ws);
   a.At = base + w.at_off;
   a.Bc = base + w.bc_off;
+  if (o) a.aux_out = wu_internal(d, wu, base + w.wu_off);
   hipError_t e = hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;
   hla::ScanArgs s{};
@@ -196,7 +224,8 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
   e = hla::launch_scan(s, d->dtype, d->dk, d->dv, stream);
   if (e != hipSuccess || !o) return hip_status(e);
   hla::ChunkArgs b = a;
-  b.At = nullptr; b.Bc = nullptr;
+  b.At = nullptr; b.Bc = nullptr; b.aux_out = nullptr;
+  b.aux_in = wu ? wu : a.aux_out;
   b.chunk_init = s.states;
   b.o = o;
   return hip_status(hla::launch_chunk(b, d->dtype, d->dk, d->dv, false, true, stream));

@@ -22,8 +22,10 @@
 
 namespace hla {
 
-template <class T, int DK, int DV, int NW, bool WANT_AB, bool WANT_O>
+template <class T, int DK, int DV, int NW, bool WANT_AB, bool WANT_O, bool AUXIN>
 __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
+  // AUXIN: the output pass takes W | U from a.aux_in and skips the UT transform
+  static_assert(!AUXIN || (WANT_O && !WANT_AB && sizeof(T) == 2), "W | U hand-off is an output-pass, bf16 option");
   using MM = Mma<T>;
   constexpr int C = kChunk;
   constexpr int E = sizeof(T);
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
         for (int e = 0; e < PAD; ++e) VT[(cc * PAD + e) * PT + t] = ev[e];
       }
-    } else {
+    } else if constexpr (!AUXIN) {
       // K^T and V^T by 8 x 8 register transposes: task (token block tb, column block db)
       // loads 8 tokens x 8 columns and writes 8 rows of 8 tokens.  tb runs fastest, so the
       // 8 lanes of a write phase hit rows (8 db + e) at token blocks 0..7: 16-byte units
@@ -155,7 +157,9 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
   // ---- 2. K K^T and Q K^T tiles (64 x 64 each, 32 x 32 tiles)
   f32x16 kk = zero16(), qk = zero16();
   int kk_tile = -1, qk_tile = -1;
-  if (NW == 8) {
+  if (AUXIN) {
+    qk_tile = w < 4 ? w : -1;
+  } else if (NW == 8) {
     if (w < 4) kk_tile = w; else qk_tile = WANT_O ? w - 4 : -1;
   } else {
     kk_tile = w;
@@ -194,10 +198,12 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
       }
     }
   }
-  for (int i = tid; i < C * PX; i += NT) Xb[i] = 0.f;
+  if constexpr (!AUXIN)
+    for (int i = tid; i < C * PX; i += NT) Xb[i] = 0.f;
   __syncthreads();
 
   // ---- 3. X = (I + L)^-1, blocked by 16
+  if constexpr (!AUXIN) {
   if (tid < 64) {
     const int bi = tid >> 4, cc = tid & 15, base = bi * 16;
     float x[16];
@@ -239,6 +245,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
     }
     __syncthreads();
   }
+  }  // !AUXIN
 
   // ---- 4. [W | U] = X diag(beta gamma | beta) [K | V]; wave w owns column tiles w, w + NW
   f32x16 wu[2][2];
@@ -249,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
     my_ct[sl] = ct < NCT ? ct : -1;
     wu[sl][0] = zero16();
     wu[sl][1] = zero16();
-    if (ct >= NCT) continue;
+    if (AUXIN || ct >= NCT) continue;
     const bool isw = ct * 32 < DK;
     const int col0 = isw ? ct * 32 : ct * 32 - DK;
     const T* brow = (isw ? KT : VT) + (col0 + c32) * PT;
@@ -278,6 +285,23 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
         }
       }
       wu[sl][tt] = acc;
+    }
+  }
+
+  // W | U fragment image of this chunk for a later output pass: fragment (ct, ks) is the
+  // B operand bf16 rows 16 ks .. of columns 32 ct .., 16 bytes per lane, lanes in order
+  constexpr int NKC = C / 16;
+  if constexpr (WANT_AB && sizeof(T) == 2) {
+    if (a.aux_out) {
+      bf16* ax = reinterpret_cast<bf16*>(a.aux_out) + ((b * a.H + h) * a.N + c) * (int64_t)C * (DK + DV);
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const int ct = my_ct[sl];
+        if (ct < 0) continue;
+#pragma unroll
+        for (int ks = 0; ks < NKC; ++ks)
+          *reinterpret_cast<bf16x8*>(ax + ((ct * NKC + ks) * 64 + lane) * 8) = MM::from_acc(wu[sl][ks >> 1], ks, 1.f);
+      }
     }
   }
 
@@ -336,10 +360,17 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
       res[sl][1] = zero16();
       if (ct < 0) continue;
       typename MM::Frag bfr[C / MM::KS];
+      if constexpr (AUXIN) {
+        const bf16* ax = reinterpret_cast<const bf16*>(a.aux_in) + ((b * a.H + h) * a.N + c) * (int64_t)C * (DK + DV);
 #pragma unroll
-      for (int ks = 0; ks < C / MM::KS; ++ks) {
-        const int tt = (MM::KS == 16) ? (ks >> 1) : (ks >> 4);
-        bfr[ks] = MM::from_acc(wu[sl][tt], ks, 1.f);
+        for (int ks = 0; ks < C / MM::KS; ++ks)
+          bfr[ks] = *reinterpret_cast<const bf16x8*>(ax + ((ct * (C / 16) + ks) * 64 + lane) * 8);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < C / MM::KS; ++ks) {
+          const int tt = (MM::KS == 16) ? (ks >> 1) : (ks >> 4);
+          bfr[ks] = MM::from_acc(wu[sl][tt], ks, 1.f);
+        }
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -427,7 +458,15 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, int64_t nblocks, hipStream_
   constexpr int NCT = (DK + DV) / 32;
   constexpr int NW = NCT >= 8 ? 8 : 4;
   TimedLaunch tl(HLA_KERNEL_CHUNK, s);
-  hipLaunchKernelGGL((chunk_kernel<T, DK, DV, NW, WANT_AB, WANT_O>), dim3((unsigned)nblocks), dim3(NW * 64), 0, s, a);
+  if constexpr (WANT_O && !WANT_AB && sizeof(T) == 2) {
+    if (a.aux_in) {
+      hipLaunchKernelGGL((chunk_kernel<T, DK, DV, NW, WANT_AB, WANT_O, true>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
+                         s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((chunk_kernel<T, DK, DV, NW, WANT_AB, WANT_O, false>), dim3((unsigned)nblocks), dim3(NW * 64), 0, s,
+                     a);
   return hipGetLastError();
 }
 

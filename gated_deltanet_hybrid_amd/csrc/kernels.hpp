@@ -18,11 +18,18 @@ struct ChunkArgs {
   void* Bc;                // out [B,H,N,dk,dv]
   const float* chunk_init; // [B,H,N,dk,dv] start state of every chunk (outputs wanted)
   float* o;                // out [B,T,H,dv]
+  // W | U of every chunk in the output pass's B-operand fragment order (bf16 only):
+  // written by the transitions pass when aux_out is set, read by the output pass (which
+  // then skips the UT transform) when aux_in is set.  [B,H,N, (dk+dv)/32, 4, 64 lanes, 8].
+  void* aux_out;
+  const void* aux_in;
 };
 
 // Either the transitions (want_ab) or the outputs from chunk_init (want_o).
 hipError_t launch_chunk(const ChunkArgs& a, int dtype, int dk, int dv, bool want_ab, bool want_o,
                         hipStream_t s);
+// bytes of the W | U fragment image of one chunk
+constexpr int64_t aux_chunk_bytes(int dk, int dv) { return (int64_t)64 * (dk + dv) * 2; }
 
 struct ScanArgs {
   const void* At;     // [B,H,N,dk,dk]

@@ -18,7 +18,7 @@ _lib = None
 
 HLA_F32, HLA_BF16 = 0, 1
 KERNEL_CHUNK, KERNEL_SCAN, KERNEL_GATES, KERNEL_COMPOSE, KERNEL_DECODE = 0, 1, 2, 3, 4
-FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX = 0, 1, 2
+FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX, FN_WU_HANDOFF = 0, 1, 2, 3
 CHUNK = 64
 MAX_CACHE_SLOTS = 1024
 
@@ -40,9 +40,9 @@ _SIGS = {
     "hla_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "hla_workspace_bytes": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(Dims), ctypes.c_int32,
                                              ctypes.POINTER(ctypes.c_size_t)]),
-    "hla_chunk_transitions": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
-                                               _P]),
-    "hla_gdn_prefill": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+    "hla_chunk_transitions": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P,
+                                               ctypes.c_size_t, _P]),
+    "hla_gdn_prefill": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]),
     "hla_route_mix": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
                                        _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -146,8 +146,15 @@ def _inputs(k, v, beta, alpha, q=None, C=CHUNK):
     return make_dims(B, T, H, ld_T, dk, dv, _dtype_code(k), C)
 
 
-def chunk_transitions(k, v, beta, alpha, At=None, Bc=None, C=CHUNK, ws=None):
-    """Exact affine map (At, Bc) of every C-token chunk: M_end = At M_start + Bc."""
+def wu_buffer(k, v, beta, alpha, C=CHUNK):
+    """A buffer for the W | U hand-off from chunk_transitions to gdn_prefill (bf16), else None."""
+    n = workspace_bytes(FN_WU_HANDOFF, _inputs(k, v, beta, alpha, C=C))
+    return torch.empty(n, dtype=torch.uint8, device=k.device) if n else None
+
+
+def chunk_transitions(k, v, beta, alpha, At=None, Bc=None, C=CHUNK, ws=None, wu=None):
+    """Exact affine map (At, Bc) of every C-token chunk: M_end = At M_start + Bc.
+    wu (from wu_buffer) also receives every piece's W | U for a later gdn_prefill."""
     d = _inputs(k, v, beta, alpha, C=C)
     N = math.ceil(d.T / C)
     At = torch.empty((d.B, d.H, N, d.dk, d.dk), dtype=k.dtype, device=k.device) if At is None else At
@@ -157,15 +164,16 @@ def chunk_transitions(k, v, beta, alpha, At=None, Bc=None, C=CHUNK, ws=None):
     if ws is None:
         ws = _workspace(workspace_bytes(FN_CHUNK_TRANSITIONS, d), k.device)
     _check(library().hla_chunk_transitions(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(At),
-                                           _ptr(Bc), _ptr(ws), 0 if ws is None else ws.numel(), _stream(k.device)),
-           "hla_chunk_transitions")
+                                           _ptr(Bc), _ptr(wu), _ptr(ws), 0 if ws is None else ws.numel(),
+                                           _stream(k.device)), "hla_chunk_transitions")
     return At, Bc
 
 
 def gdn_prefill(q, k, v, beta, alpha, S0=None, chunk_init=None, want_o=True, want_state=True, o=None,
-                S_final=None, ws=None, C=CHUNK):
+                S_final=None, ws=None, C=CHUNK, wu=None):
     """Chunkwise gated delta rule prefill.  Returns (o [B,T,H,dv] or None, S_final or None).
-    C is the chunk size of chunk_init (routed mode); native results do not depend on it."""
+    C is the chunk size of chunk_init (routed mode); native results do not depend on it.
+    wu: a buffer chunk_transitions filled from the same inputs, or None."""
     d = _inputs(k, v, beta, alpha, q if want_o else None, C=C)
     N = math.ceil(d.T / C)
     dev = k.device
@@ -186,8 +194,8 @@ def gdn_prefill(q, k, v, beta, alpha, S0=None, chunk_init=None, want_o=True, wan
     if ws is None and (chunk_init is None or C != CHUNK):
         ws = _workspace(workspace_bytes(FN_GDN_PREFILL, d), dev)
     _check(library().hla_gdn_prefill(ctypes.byref(d), _ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(beta),
-                                     _ptr(alpha), _ptr(S0), _ptr(chunk_init), _ptr(o), _ptr(S_final), _ptr(ws),
-                                     0 if ws is None else ws.numel(), _stream(dev)), "hla_gdn_prefill")
+                                     _ptr(alpha), _ptr(S0), _ptr(chunk_init), _ptr(wu), _ptr(o), _ptr(S_final),
+                                     _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)), "hla_gdn_prefill")
     return o, S_final
 
 
@@ -235,12 +243,14 @@ def route_mix(q, reps, At, Bc, n_rep=CHUNK, tau=1e-3, S0=None, gates_in=None, T=
     return dict(gates=gates, mask=mask, active_idx=aidx, active_cnt=acnt, n_eff=neff, S_routed=Sr)
 
 
-def hla_prefill(q, k, v, beta, alpha, tau=1e-3, gates_in=None, S0=None, C=CHUNK):
+def hla_prefill(q, k, v, beta, alpha, tau=1e-3, gates_in=None, S0=None, C=CHUNK, handoff=True):
     """The routed prefill as three calls: transitions, routing, outputs from routed states.
-    Representatives are each chunk's raw keys (n_rep = C)."""
-    At, Bc = chunk_transitions(k, v, beta, alpha, C=C)
+    Representatives are each chunk's raw keys (n_rep = C).  handoff passes W | U from the
+    first call to the last (bf16)."""
+    wu = wu_buffer(k, v, beta, alpha, C=C) if handoff else None
+    At, Bc = chunk_transitions(k, v, beta, alpha, C=C, wu=wu)
     r = route_mix(q, k, At, Bc, n_rep=C, tau=tau, S0=S0, gates_in=gates_in, C=C)
-    o, _ = gdn_prefill(q, k, v, beta, alpha, chunk_init=r["S_routed"], want_state=False, C=C)
+    o, _ = gdn_prefill(q, k, v, beta, alpha, chunk_init=r["S_routed"], want_state=False, C=C, wu=wu)
     r.update(At=At, Bc=Bc, o=o)
     return r
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define HLA_ABI_VERSION 2
+#define HLA_ABI_VERSION 3
 
 typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype_t;
 
@@ -77,7 +77,14 @@ typedef struct {
 } hla_dims_t;
 
 /* Which entry point a workspace size is asked for (hla_workspace_bytes). */
-typedef enum { HLA_FN_CHUNK_TRANSITIONS = 0, HLA_FN_GDN_PREFILL = 1, HLA_FN_ROUTE_MIX = 2 } hla_fn_t;
+typedef enum {
+  HLA_FN_CHUNK_TRANSITIONS = 0,
+  HLA_FN_GDN_PREFILL = 1,
+  HLA_FN_ROUTE_MIX = 2,
+  HLA_FN_WU_HANDOFF = 3 /* size of the optional wu buffer of hla_chunk_transitions and
+                           hla_gdn_prefill: B H ceil(T / 64) 64 (dk + dv) bf16 values;
+                           0 for float32, which takes no hand-off */
+} hla_fn_t;
 
 /*
  * hla_chunk_transitions -- the exact affine map of every chunk.
@@ -87,6 +94,13 @@ typedef enum { HLA_FN_CHUNK_TRANSITIONS = 0, HLA_FN_GDN_PREFILL = 1, HLA_FN_ROUT
  * diag(beta)(K K^T o decay) is inverted per chunk instead of running the token loop.
  *   k, v, beta, alpha : inputs as in the header notes (q is not needed).
  *   At [B, H, N, dk, dk], Bc [B, H, N, dk, dv] (out, dtype): M_end = At M_start + Bc.
+ *   wu     (out, optional, bf16 only): hla_workspace_bytes(HLA_FN_WU_HANDOFF) bytes, or
+ *           NULL.  Receives, for every 64-token piece, the UT-transformed keys and values
+ *           W = X diag(beta gamma) K and U = X diag(beta) V (X the inverted strictly lower
+ *           part plus identity) in the library's own fragment order, so that
+ *           hla_gdn_prefill on the same inputs can take them instead of recomputing the
+ *           inverse.  The layout is private to this library version.  A non-NULL wu
+ *           with float32 inputs is HLA_ERR_UNSUPPORTED.
  *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_CHUNK_TRANSITIONS)
  *           bytes (zero for C = 64; for C > 64 it holds the maps of the 64-token pieces,
  *           which are then composed C / 64 at a time: [HLA] Methodology paragraph 1).
@@ -95,7 +109,7 @@ typedef enum { HLA_FN_CHUNK_TRANSITIONS = 0, HLA_FN_GDN_PREFILL = 1, HLA_FN_ROUT
  */
 hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const void* v,
                                    const float* beta, const float* alpha, void* At, void* Bc,
-                                   void* ws, size_t ws_bytes, hipStream_t stream);
+                                   void* wu, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * hla_gdn_prefill -- chunkwise Gated DeltaNet prefill.
@@ -112,6 +126,9 @@ hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const voi
  *   q, k, v, beta, alpha : per-token inputs.
  *   S0         [B, H, dk, dv] float32 or NULL.
  *   chunk_init [B, H, N, dk, dv] float32 or NULL.
+ *   wu         (optional, bf16 only): a buffer that hla_chunk_transitions filled from the
+ *           same k, v, beta, alpha and dims, or NULL.  Given, the output pass reads W and U
+ *           from it instead of recomputing them; results are identical.
  *   o          [B, T, H, dv] float32 (out) or NULL.
  *   S_final    [B, H, dk, dv] float32 (out) or NULL.  At least one of o, S_final.
  *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_GDN_PREFILL) bytes
@@ -122,8 +139,8 @@ hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const voi
  */
 hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, const void* v,
                              const float* beta, const float* alpha, const float* S0,
-                             const float* chunk_init, float* o, float* S_final, void* ws,
-                             size_t ws_bytes, hipStream_t stream);
+                             const float* chunk_init, const void* wu, float* o, float* S_final,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * hla_route_mix -- HLA router gates and the gated composition of chunk transitions.

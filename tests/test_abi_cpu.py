@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hla_abi_version() == 2
+    assert lib.hla_abi_version() == 3
     for s in range(0, 9):
         assert lib.hla_status_string(s)
     assert lib.hla_status_string(99) == b"unknown status"
@@ -50,8 +50,14 @@ def test_workspace_sizes(lib):
     BHN = 2 * 3 * 3
     assert hla.workspace_bytes(hla.FN_CHUNK_TRANSITIONS, d) == 0
     ab = BHN * 128 * 128 * 2 + BHN * 128 * 64 * 2
+    wu = BHN * 64 * (128 + 64) * 2  # W | U of every piece, bf16
     st = BHN * 128 * 64 * 4
-    assert hla.workspace_bytes(hla.FN_GDN_PREFILL, d) == ab + st
+    assert hla.workspace_bytes(hla.FN_GDN_PREFILL, d) == ab + wu + st
+    assert hla.workspace_bytes(hla.FN_WU_HANDOFF, d) == wu
+    # float32 takes no hand-off
+    d32 = dims(B=2, T=130, H=3, dk=128, dv=64, dtype=0)
+    assert hla.workspace_bytes(hla.FN_WU_HANDOFF, d32) == 0
+    assert hla.workspace_bytes(hla.FN_GDN_PREFILL, d32) == 2 * ab + st
     # float32 query-chunk means, then the reordered bf16 copy of At - I
     assert hla.workspace_bytes(hla.FN_ROUTE_MIX, d) == 2 * 3 * 3 * 128 * 4 + BHN * 128 * 128 * 2
     out = ctypes.c_size_t()
@@ -67,7 +73,8 @@ def test_workspace_sizes_larger_chunks(lib):
     # the transitions of the 64-token pieces are composed four at a time
     assert hla.workspace_bytes(hla.FN_CHUNK_TRANSITIONS, d) == ab
     # the prefill runs on pieces whatever C is
-    assert hla.workspace_bytes(hla.FN_GDN_PREFILL, d) == ab + pieces * 128 * 128 * 4
+    assert hla.workspace_bytes(hla.FN_GDN_PREFILL, d) == ab + pieces * 64 * 256 * 2 + pieces * 128 * 128 * 4
+    assert hla.workspace_bytes(hla.FN_WU_HANDOFF, d) == pieces * 64 * 256 * 2
     assert hla.workspace_bytes(hla.FN_ROUTE_MIX, d) == 2 * 3 * 128 * 4 + 2 * 3 * 128 * 128 * 2
 
 
@@ -78,47 +85,53 @@ def test_workspace_sizes_larger_chunks(lib):
 ])
 def test_chunk_transitions_rejects_bad_dims(lib, kw, code):
     d = dims(**kw)
-    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, None, 0, None) == code
+    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, None, None, 0, None) == code
 
 
 def test_larger_chunks_need_workspace(lib):
     d = dims(C=128)
     need = hla.workspace_bytes(hla.FN_CHUNK_TRANSITIONS, d)
     assert need > 0
-    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, None, 0, None) == WORKSPACE
-    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, P, need - 1, None) == WORKSPACE
+    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, None, None, 0, None) == WORKSPACE
+    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, None, P, need - 1, None) == WORKSPACE
     # routed outputs with C > 64 scan the pieces of every chunk from its routed state
     pre = lib.hla_gdn_prefill
-    assert pre(ctypes.byref(d), P, P, P, P, P, None, P, P, None, None, 0, None) == WORKSPACE
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, P, None, P, None, None, 0, None) == WORKSPACE
 
 
 def test_chunk_transitions_rejects_null_and_misaligned(lib):
     d = dims()
-    assert lib.hla_chunk_transitions(None, P, P, P, P, P, P, None, 0, None) == NULL_ARG
+    assert lib.hla_chunk_transitions(None, P, P, P, P, P, P, None, None, 0, None) == NULL_ARG
     for i in range(6):
         args = [P] * 6
         args[i] = None
-        assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None, 0, None) == NULL_ARG
+        assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None, None, 0, None) == NULL_ARG
         # vector-loaded tensors need 16 bytes, the per-token scalars (beta, alpha) 4
         args[i] = P + 2 if i in (2, 3) else PU
-        assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None, 0, None) == ALIGN
+        assert lib.hla_chunk_transitions(ctypes.byref(d), *args, None, None, 0, None) == ALIGN
 
 
 def test_prefill_validation(lib):
     d = dims()
     pre = lib.hla_gdn_prefill
     # neither o nor S_final
-    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, None, None, P, 1 << 30, None) == NULL_ARG
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, None, None, None, P, 1 << 30, None) == NULL_ARG
     # o without q
-    assert pre(ctypes.byref(d), None, P, P, P, P, None, None, P, None, P, 1 << 30, None) == NULL_ARG
+    assert pre(ctypes.byref(d), None, P, P, P, P, None, None, None, P, None, P, 1 << 30, None) == NULL_ARG
     # routed mode with S0 or S_final
-    assert pre(ctypes.byref(d), P, P, P, P, P, P, P, P, None, None, 0, None) == UNSUPPORTED
-    assert pre(ctypes.byref(d), P, P, P, P, P, None, P, P, P, None, 0, None) == UNSUPPORTED
+    assert pre(ctypes.byref(d), P, P, P, P, P, P, P, None, P, None, None, 0, None) == UNSUPPORTED
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, P, None, P, P, None, 0, None) == UNSUPPORTED
     # native mode without enough workspace
     need = hla.workspace_bytes(hla.FN_GDN_PREFILL, d)
-    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, P, P, P, need - 1, None) == WORKSPACE
-    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, P, P, None, 0, None) == WORKSPACE
-    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, P, P, PU, need, None) == ALIGN
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, None, P, P, P, need - 1, None) == WORKSPACE
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, None, P, P, None, 0, None) == WORKSPACE
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, None, P, P, PU, need, None) == ALIGN
+    # the W | U hand-off: 16-byte aligned, bf16 only
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, P, PU, P, None, None, 0, None) == ALIGN
+    d32 = dims(dtype=0)
+    assert pre(ctypes.byref(d32), P, P, P, P, P, None, P, P, P, None, None, 0, None) == UNSUPPORTED
+    assert lib.hla_chunk_transitions(ctypes.byref(d32), P, P, P, P, P, P, P, None, 0, None) == UNSUPPORTED
+    assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, PU, None, 0, None) == ALIGN
 
 
 def test_route_mix_validation(lib):
