@@ -30,7 +30,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 SEGMENT = 4096
-_TENSOR_ID = {"q": 1, "k": 2, "v": 3, "beta": 4, "alpha": 5, "gates": 6, "At": 7, "Bc": 8, "S0": 9}
+_TENSOR_ID = {"q": 1, "k": 2, "v": 3, "beta": 4, "alpha": 5, "gates": 6, "At": 7, "Bc": 8, "S0": 9,
+              "Wq": 10, "Wk": 11, "Wv": 12, "Wp": 13, "Wr": 14}
 
 
 # --------------------------------------------------------------------------- rounding
@@ -222,6 +223,20 @@ def gen_transitions(B, H, N, dk, dv, dtype="bf16", seed=0, stream=0, norm=0.95, 
     rng2 = _rng(seed, stream, "Bc", B, H, N, dv)
     Bc = b_scale * rng2.standard_normal((B, H, N, dk, dv))
     return to_storage(At, dtype), to_storage(Bc, dtype)
+
+
+def gen_pooler_weights(H, dk, dtype="bf16", seed=0, stream=0, shared=False, qk_scale=1.0) -> dict:
+    """Seeded weights of the chunk-representative pooler and the router query projection,
+    each [H, dk, dk] (or [1, dk, dk] when ``shared``) in storage form, layout [out, in].
+    Wq, Wk ~ N(0, qk_scale^2), so the window's attention scores are of order one; Wv, Wp,
+    Wr ~ N(0, 1 / dk), so they roughly preserve vector norms."""
+    nh = 1 if shared else H
+    out = {}
+    for name in ("Wq", "Wk", "Wv", "Wp", "Wr"):
+        rng = _rng(seed, stream, name, nh, dk)
+        sd = qk_scale if name in ("Wq", "Wk") else 1.0 / math.sqrt(dk)
+        out[name] = to_storage(sd * rng.standard_normal((nh, dk, dk)), dtype)
+    return out
 
 
 def gen_state(B, H, dk, dv, seed=0, stream=0, scale=0.5) -> np.ndarray:

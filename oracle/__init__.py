@@ -30,6 +30,8 @@ from .gdn import (  # noqa: F401
     chunk_transition,
     chunk_transitions,
     log_mean_exp,
+    window_rep,
+    window_reps,
     router_gates,
     routed_states,
     routed_states_by_replay,

@@ -13,8 +13,10 @@ import numpy as np
 PARITY_UNPINNED = (
     "router score pooling is log-MEAN-exp (HLA Overview) rather than log-sum-exp "
     "(HLA Methodology paragraph 2); the two differ by log(n_rep)",
-    "representatives are the history chunk's raw keys (the learned window pooler needs "
-    "trained weights)",
+    "representatives are the history chunk's raw keys, or (window_reps) the learned "
+    "pooler with seeded random weights: trained weights are not on the pages",
+    "the pooler's self-attention is one head, scaled by 1/sqrt(dk), over the keys of the "
+    "window, with no causal mask inside a completed window; every projection is dk x dk",
     "the decode-time gate query is the token's own q; the prefill gate query is the mean "
     "of q over the query chunk",
     "gates are per (batch, head)",
@@ -104,13 +106,48 @@ def n_eff(g):
     return np.where(den > 0, num / np.where(den > 0, den, 1.0), 0.0)
 
 
-def router_gates(q, reps, n_rep, C, tau, gates_in=None):
+def window_rep(X, Wq, Wk, Wv, Wp):
+    """One representative from the keys X [n, dk] of one pooling window ([HLA] Methodology
+    paragraph 2): self-attention inside the window, mean-pool of its token outputs, then a
+    learned projection.  Weights are [out, in]: a row vector x maps to W @ x.
+      Q = X Wq^T, K = X Wk^T, V = X Wv^T
+      P = row-softmax(Q K^T / sqrt(dk))      (every token attends to the whole window)
+      O = P V;   rep = Wp (mean over the n token rows of O)."""
+    n, dk = X.shape
+    Q, K, V = X @ Wq.T, X @ Wk.T, X @ Wv.T
+    s = Q @ K.T / math.sqrt(dk)
+    s = s - s.max(axis=1, keepdims=True)
+    P = np.exp(s) / np.exp(s).sum(axis=1, keepdims=True)
+    O = P @ V
+    return Wp @ O.mean(axis=0)
+
+
+def window_reps(k, C, window, Wq, Wk, Wv, Wp):
+    """Representatives of every chunk for one (batch, head) sequence: chunk c is split into
+    C / window pooling windows of consecutive tokens, one representative each, rows
+    [c n_rep, (c + 1) n_rep) with n_rep = C / window.  A window cut by the end of the
+    sequence pools the tokens it has; one with no tokens gets a zero row."""
+    T, dk = k.shape
+    assert C % window == 0
+    n_rep = C // window
+    bounds = chunk_bounds(T, C)
+    reps = np.zeros((len(bounds) * n_rep, dk))
+    for c, (s, e) in enumerate(bounds):
+        for w in range(n_rep):
+            lo, hi = s + w * window, min(s + (w + 1) * window, e)
+            if hi > lo:
+                reps[c * n_rep + w] = window_rep(k[lo:hi], Wq, Wk, Wv, Wp)
+    return reps
+
+
+def router_gates(q, reps, n_rep, C, tau, gates_in=None, Wr=None):
     """Query-chunk x history-chunk gates for one (batch, head) sequence.
 
     q [T, dk]; reps [(N-1) * n_rep or more, dk]: chunk j's representatives are rows
     [j n_rep, (j + 1) n_rep).  [HLA] Overview (log-mean-exp pooled routing gates) and
     Methodology paragraphs 2-4:
-      * query of chunk i = mean of q over the chunk's tokens;
+      * query of chunk i = mean of q over the chunk's tokens, then projected by Wr
+        [dk, dk] when given (the router's learned query projection);
       * l_ij = log-mean-exp over chunk j's representatives r of (qbar_i . r) / sqrt(dk);
       * g_ij = sigmoid(l_ij) for j < i, independent (no normalisation over j);
       * the current chunk has weight 1, future chunks are masked (weight 0);
@@ -126,6 +163,8 @@ def router_gates(q, reps, n_rep, C, tau, gates_in=None):
     g = np.zeros((N, N))
     if gates_in is None:
         qbar = np.stack([q[s:e].mean(axis=0) for s, e in bounds])
+        if Wr is not None:
+            qbar = qbar @ Wr.T
         for i in range(N):
             for j in range(i):
                 r = reps[j * n_rep:(j + 1) * n_rep]
@@ -186,12 +225,12 @@ def routed_outputs(q, k, v, beta, alpha, C, S_routed):
     return o
 
 
-def hla_prefill(q, k, v, beta, alpha, C, tau, reps=None, n_rep=None, gates_in=None, S0=None):
+def hla_prefill(q, k, v, beta, alpha, C, tau, reps=None, n_rep=None, gates_in=None, S0=None, Wr=None):
     """Whole routed prefill for one (batch, head): transitions, gates, states, outputs."""
     if reps is None:
         reps, n_rep = k, C
     A, B = chunk_transitions(k, v, beta, alpha, C)
-    r = router_gates(q, reps, n_rep, C, tau, gates_in=gates_in)
+    r = router_gates(q, reps, n_rep, C, tau, gates_in=gates_in, Wr=Wr)
     S = routed_states(A, B, r["ghat"], r["mask"], S0=S0)
     o = routed_outputs(q, k, v, beta, alpha, C, S)
     return dict(A=A, B=B, S_routed=S, o=o, **r)
@@ -199,7 +238,7 @@ def hla_prefill(q, k, v, beta, alpha, C, tau, reps=None, n_rep=None, gates_in=No
 
 # --------------------------------------------------------------------------- O6 decode
 def decode_step(q, k, v, beta, alpha, B_cur, A_cur, cache_A, cache_B, cache_reps, tau,
-                gates_in=None, commit=False):
+                gates_in=None, commit=False, Wr=None):
     """One single-token decode step for one (sequence, head).
 
     [HLA] Key Contributions 3 (dynamic autoregressive decoding) with Methodology
@@ -208,7 +247,8 @@ def decode_step(q, k, v, beta, alpha, B_cur, A_cur, cache_A, cache_B, cache_reps
     token's own q.  The routed state S~ composes the gated cached chunks from zero; the
     output reads the live chunk applied after it: o = (S~ A_cur + B_cur) q.
     ``A_cur is None`` selects native GDN: B_cur is the full-prefix state, o = B_cur q.
-    cache_A [Nc, dk, dk], cache_B [Nc, dv, dk], cache_reps [Nc, n_rep, dk].
+    cache_A [Nc, dk, dk], cache_B [Nc, dv, dk], cache_reps [Nc, n_rep, dk].  Wr [dk, dk]
+    projects the gate query when given.
     Returns dict(o, B_cur, A_cur, gates, ghat, cache_A, cache_B) after the step (and the
     optional commit, which appends the live chunk and resets it to (I, 0)).
     """
@@ -220,9 +260,10 @@ def decode_step(q, k, v, beta, alpha, B_cur, A_cur, cache_A, cache_B, cache_reps
     A_cur = A_cur @ lin
     Nc = cache_A.shape[0]
     g = np.zeros(Nc)
+    qr = q if Wr is None else Wr @ q
     for j in range(Nc):
         if gates_in is None:
-            g[j] = _sigmoid(log_mean_exp(cache_reps[j] @ q / math.sqrt(dk)))
+            g[j] = _sigmoid(log_mean_exp(cache_reps[j] @ qr / math.sqrt(dk)))
         else:
             g[j] = gates_in[j]
     keep = g.astype(np.float32) >= np.float32(tau)
