@@ -55,6 +55,16 @@ def flops_routed_output(n_chunks, dk, dv):
     return n_chunks * (2 * C * C * dk + 2 * C * C * (dk + dv) + 2 * C * dk * dv)
 
 
+def flops_reps_pool(n_windows, window, dk):
+    """Learned representatives, pooling pass, per window: Q, K, V projections of its tokens,
+    the in-window scores and P V (the mean over rows is additions)."""
+    return n_windows * (3 * 2 * window * dk * dk + 2 * 2 * window * window * dk)
+
+
+def flops_reps_project(n_windows, dk, with_wr=True):
+    return n_windows * 2 * dk * dk * (2 if with_wr else 1)
+
+
 def flops_gates(pairs, n_rep, dk):
     return pairs * 2 * n_rep * dk
 
@@ -108,10 +118,11 @@ def timed(fn, steps, warmup, torch):
 
 # ----------------------------------------------------------------------------- routed prefill
 def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None, x=None, tag="routed_prefill",
-                         handoff=True):
+                         handoff=True, pooler=None, window=32):
     """The routed prefill step at chunk size Cw (64-token pieces underneath), with the
     router's computed gates or caller gates; handoff passes W | U from the transitions
-    call to the output call."""
+    call to the output call.  With ``pooler`` (seeded weights) the step also computes the
+    learned window representatives (hla_chunk_reps) that the router scores."""
     W = inputs.WORKLOADS["routed_prefill"]
     tau = W.tau if tau is None else tau
     N = math.ceil(W.T / Cw)
@@ -130,6 +141,11 @@ def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None
     ws_p = hla._workspace(hla.workspace_bytes(hla.FN_GDN_PREFILL, d), dev) if Cw != C else None
     wu = hla._workspace(hla.workspace_bytes(hla.FN_WU_HANDOFF, d), dev) if handoff else None
     g_in = None if gates_in is None else torch.from_numpy(gates_in).to(dev)
+    n_rep = Cw if pooler is None else Cw // window
+    if pooler is not None:
+        Wd = {n: to_dev(a, W.dtype, torch) for n, a in pooler.items()}
+        reps = torch.empty((W.B, N * n_rep, W.H, W.dk), dtype=k.dtype, device=dev)
+        ws_r = hla._workspace(hla.workspace_bytes(hla.FN_CHUNK_REPS, d, n_rep), dev)
     out = dict(gates=torch.empty((W.B, W.H, N, N), dtype=torch.float32, device=dev),
                mask=torch.empty((W.B, W.H, N, N), dtype=torch.uint8, device=dev),
                active_idx=torch.empty((W.B, W.H, N, N), dtype=torch.int32, device=dev),
@@ -140,7 +156,10 @@ def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None
 
     def step():
         hla.chunk_transitions(k, v, beta, alpha, At=At, Bc=Bc, C=Cw, ws=ws_t, wu=wu)
-        hla.route_mix(q, k, At, Bc, n_rep=Cw, tau=tau, gates_in=g_in, out=out, ws=ws, C=Cw)
+        r_in = k
+        if pooler is not None:
+            r_in = hla.chunk_reps(k, Wd, window=window, C=Cw, out=reps, ws=ws_r)
+        hla.route_mix(q, r_in, At, Bc, n_rep=n_rep, tau=tau, gates_in=g_in, out=out, ws=ws, C=Cw)
         hla.gdn_prefill(q, k, v, beta, alpha, chunk_init=out["S_routed"], want_state=False, o=o, ws=ws_p, C=Cw,
                         wu=wu)
 
@@ -157,13 +176,17 @@ def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None
     dt = (time.perf_counter() - t0) / args.steps
     comp_ms, comp_n = hla.timing_read(hla.KERNEL_COMPOSE)
     per_kernel = {name: hla.timing_read(kid) for name, kid in
-                  (("chunk", hla.KERNEL_CHUNK), ("gates", hla.KERNEL_GATES), ("compose", hla.KERNEL_COMPOSE))}
+                  (("chunk", hla.KERNEL_CHUNK), ("gates", hla.KERNEL_GATES), ("compose", hla.KERNEL_COMPOSE),
+                   ("reps", hla.KERNEL_REPS))}
     hla.timing_enable(False)
 
     n_pieces = W.B * W.H * math.ceil(W.T / C)
     fl_comp = flops_compose(pairs, W.dk, W.dv)
     fl_total = (fl_comp + flops_transitions(n_pieces, W.dk, W.dv) + flops_routed_output(n_pieces, W.dk, W.dv)
-                + (flops_gates(pairs, Cw, W.dk) if gates_in is None else 0))
+                + (flops_gates(pairs, n_rep, W.dk) if gates_in is None else 0))
+    n_windows = W.B * W.H * N * n_rep
+    if pooler is not None:
+        fl_total += flops_reps_pool(n_windows, window, W.dk) + flops_reps_project(n_windows, W.dk)
     if Cw != C:  # composing the C / 64 piece maps of every chunk: [I|0] through C/64 pieces
         fl_total += W.B * W.H * N * (Cw // C) * 2 * W.dk * W.dk * (W.dk + W.dv)
     comp_avg_s = comp_ms / comp_n / 1e3
@@ -174,11 +197,18 @@ def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None
         value=tokens / dt, ms_per_step=dt * 1e3,
         mfma_util_pct=100.0 * fl_total / dt / (PEAK_BF16_TFLOPS * 1e12),
         step_tflops=fl_total / dt / 1e12, active_pairs=pairs,
-        kernel_ms={kname: round(ms / max(n, 1), 4) for kname, (ms, n) in per_kernel.items()},
+        kernel_ms={kname: round(ms / n, 4) for kname, (ms, n) in per_kernel.items() if n > 0},
         roofline=dict(kernel="compose_bf16_kernel", bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
                       unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic,
                       flops_per_launch=fl_comp, avg_launch_ms=round(comp_avg_s * 1e3, 4), launches=comp_n),
     )
+    if pooler is not None:
+        rms, rn = per_kernel["reps"]
+        r_ach = flops_reps_pool(n_windows, window, W.dk) / (rms / rn / 1e3) / 1e12
+        res["reps_pool"] = dict(kernel="reps_pool_kernel", bound="mfma", window=window, n_rep=n_rep,
+                                avg_launch_ms=round(rms / rn, 4), achieved=round(r_ach, 2), peak=PEAK_BF16_TFLOPS,
+                                unit="TFLOP/s", frac=round(r_ach / PEAK_BF16_TFLOPS, 4),
+                                flops_per_launch=flops_reps_pool(n_windows, window, W.dk))
     log(f"[{tag}] {dt*1e3:.3f} ms/step, {tokens/dt/1e6:.3f} M tok/s, compose {comp_avg_s*1e3:.3f} ms "
         f"({achieved:.0f} TFLOP/s), step MFMA util {res['mfma_util_pct']:.1f}%, active pairs {pairs}")
     del q, k, v, At, Bc, out, o, ws, ws_t, ws_p, g_in
@@ -187,8 +217,9 @@ def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None
 
 
 def bench_routed_variants(args, torch, hla, inputs, x):
-    """Secondary routed-prefill lines: the pages' default chunk size (C = 256), and C = 64
-    with skip-heavy caller gates at tau = 0.1 (how skipping cuts the composition)."""
+    """Secondary routed-prefill lines: the pages' default chunk size (C = 256), C = 64 with
+    skip-heavy caller gates at tau = 0.1 (how skipping cuts the composition), and C = 64
+    with learned window representatives."""
     W = inputs.WORKLOADS["routed_prefill"]
     sub = argparse.Namespace(steps=max(3, args.steps // 2), warmup=1)
     out = {}
@@ -206,6 +237,13 @@ def bench_routed_variants(args, torch, hla, inputs, x):
                                       active_pairs=r["active_pairs"], active_frac=r["active_pairs"] / dense_pairs,
                                       compose_ms=r["roofline"]["avg_launch_ms"],
                                       compose_tflops_active=r["roofline"]["achieved"])
+    pooler = inputs.gen_pooler_weights(W.H, W.dk, dtype=W.dtype, seed=0, stream=inputs.STREAM["routed_prefill"])
+    r, _ = bench_routed_prefill(sub, torch, hla, inputs, Cw=C, x=x, tag="routed_prefill_learned_reps", pooler=pooler,
+                                window=32)
+    out["routed_prefill_learned_reps"] = dict(
+        workload="routed_prefill C=64, learned representatives (window 32, 2 per chunk), seeded weights",
+        C=C, tau=W.tau, ms_per_step=r["ms_per_step"], tokens_per_s=r["value"], mfma_util_pct=r["mfma_util_pct"],
+        active_pairs=r["active_pairs"], kernel_ms=r["kernel_ms"], reps_pool=r["reps_pool"])
     return out
 
 

@@ -90,6 +90,11 @@ int64_t route_ws(const hla_dims_t* d) {
   return route_qbar_bytes(d) + prep;
 }
 
+// Workspace of hla_chunk_reps: float32 window means [B,H,N*n_rep,dk].
+int64_t reps_ws(const hla_dims_t* d, int32_t n_rep) {
+  return round_up(d->B * d->H * n_chunks(d) * n_rep * d->dk * 4, 256);
+}
+
 hla_status_t hip_status(hipError_t e) { return e == hipSuccess ? HLA_OK : HLA_ERR_HIP; }
 
 // Where a prefill's own transitions pass writes W | U: nowhere when the caller supplies
@@ -123,12 +128,15 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
   if (!out) return HLA_ERR_NULL_ARG;
   hla_status_t st = check_dims(d);
   if (st != HLA_OK) return st;
-  (void)n_rep;
   switch (fn) {
     case HLA_FN_CHUNK_TRANSITIONS: *out = d->C == kPiece ? 0 : (size_t)prefill_ws(d).total_ab; return HLA_OK;
     case HLA_FN_GDN_PREFILL: *out = (size_t)prefill_ws(d).total; return HLA_OK;
     case HLA_FN_ROUTE_MIX: *out = (size_t)route_ws(d); return HLA_OK;
     case HLA_FN_WU_HANDOFF: *out = (size_t)wu_bytes(d); return HLA_OK;
+    case HLA_FN_CHUNK_REPS:
+      if (n_rep < 1 || d->C % n_rep != 0) return HLA_ERR_BAD_SHAPE;
+      *out = (size_t)reps_ws(d, n_rep);
+      return HLA_OK;
     default: return HLA_ERR_UNSUPPORTED;
   }
 }
@@ -229,6 +237,28 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
   b.chunk_init = s.states;
   b.o = o;
   return hip_status(hla::launch_chunk(b, d->dtype, d->dk, d->dv, false, true, stream));
+}
+
+hla_status_t hla_chunk_reps(const hla_dims_t* d, const void* k, int32_t window, const void* Wq, const void* Wk,
+                            const void* Wv, const void* Wp, const void* Wr, int64_t w_hstride, void* reps, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (!k || !Wq || !Wk || !Wv || !Wp || !reps) return HLA_ERR_NULL_ARG;
+  if (window != 8 && window != 16 && window != 32) return HLA_ERR_BAD_SHAPE;
+  const int64_t wsz = (int64_t)d->dk * d->dk;
+  if (w_hstride != 0 && w_hstride < wsz) return HLA_ERR_BAD_SHAPE;
+  if ((w_hstride * dtype_bytes(d->dtype)) % 16 != 0) return HLA_ERR_ALIGN;
+  if (!all_aligned(k, Wq, Wk, Wv, Wp, Wr, reps, ws)) return HLA_ERR_ALIGN;
+  const int32_t n_rep = d->C / window;
+  if (!ws || (int64_t)ws_bytes < reps_ws(d, n_rep)) return HLA_ERR_WORKSPACE;
+  hla::RepsArgs a{};
+  a.k = k; a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T;
+  a.C = d->C; a.window = window; a.N = (int32_t)n_chunks(d);
+  a.Wq = Wq; a.Wk = Wk; a.Wv = Wv; a.Wp = Wp; a.Wr = Wr; a.w_hstride = w_hstride;
+  a.pooled = static_cast<float*>(ws);
+  a.reps = reps;
+  return hip_status(hla::launch_reps(a, d->dtype, d->dk, stream));
 }
 
 hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps, int32_t n_rep, int64_t ld_R,

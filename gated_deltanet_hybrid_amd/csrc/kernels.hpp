@@ -101,4 +101,21 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int dk, int dv, hipStream_t s);
 
+struct RepsArgs {
+  const void* k;          // [B,ld_T,H,dk]
+  int64_t B, T, H, ld_T;
+  int32_t C, window, N;   // N chunks of C tokens, C / window representatives each
+  const void* Wq;         // [*, dk, dk] (out, in) in dtype; head h at + h * w_hstride
+  const void* Wk;
+  const void* Wv;
+  const void* Wp;
+  const void* Wr;         // query projection folded into the representatives, or null
+  int64_t w_hstride;      // elements between the heads' weights (0: shared)
+  float* pooled;          // workspace [B,H,N*C/window,dk] float32: window means
+  void* reps;             // out [B,N*C/window,H,dk] (dtype)
+  int32_t groups;         // set by the launcher: workgroups per (b, h) of the pooling pass
+};
+// Learned chunk representatives: window self-attention, mean-pool, projections.
+hipError_t launch_reps(const RepsArgs& a, int dtype, int dk, hipStream_t s);
+
 }  // namespace hla

@@ -17,8 +17,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhla.so"
 _lib = None
 
 HLA_F32, HLA_BF16 = 0, 1
-KERNEL_CHUNK, KERNEL_SCAN, KERNEL_GATES, KERNEL_COMPOSE, KERNEL_DECODE = 0, 1, 2, 3, 4
-FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX, FN_WU_HANDOFF = 0, 1, 2, 3
+KERNEL_CHUNK, KERNEL_SCAN, KERNEL_GATES, KERNEL_COMPOSE, KERNEL_DECODE, KERNEL_REPS = 0, 1, 2, 3, 4, 5
+FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX, FN_WU_HANDOFF, FN_CHUNK_REPS = 0, 1, 2, 3, 4
 CHUNK = 64
 MAX_CACHE_SLOTS = 1024
 
@@ -44,6 +44,8 @@ _SIGS = {
                                                ctypes.c_size_t, _P]),
     "hla_gdn_prefill": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]),
+    "hla_chunk_reps": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                        ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]),
     "hla_route_mix": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
                                        _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "hla_timing_enable": (ctypes.c_int32, [ctypes.c_int32]),
@@ -199,6 +201,30 @@ def gdn_prefill(q, k, v, beta, alpha, S0=None, chunk_init=None, want_o=True, wan
     return o, S_final
 
 
+def chunk_reps(k, W, window=32, C=CHUNK, out=None, ws=None):
+    """Learned representatives of every C-token chunk: [B, N * C/window, H, dk] in k's dtype.
+
+    W: dict of Wq, Wk, Wv, Wp and optionally Wr, each [H, dk, dk] or [1, dk, dk] ([out, in],
+    k's dtype); Wr (the router's query projection) is folded into the result."""
+    B, T, H, dk, ld_T = _token_view(k, "k")
+    d = make_dims(B, T, H, ld_T, dk, dk, _dtype_code(k), C)
+    N = math.ceil(T / C)
+    n_rep = C // window
+    ws_ = [W[n] for n in ("Wq", "Wk", "Wv", "Wp")] + ([W["Wr"]] if W.get("Wr") is not None else [])
+    nh = ws_[0].shape[0]
+    for t in ws_:
+        if t.shape != (nh, dk, dk) or nh not in (1, H) or t.dtype != k.dtype or not t.is_contiguous():
+            raise ValueError("weights must be contiguous [H or 1, dk, dk] in k's dtype")
+    out = torch.empty((B, N * n_rep, H, dk), dtype=k.dtype, device=k.device) if out is None else out
+    _need(out, (B, N * n_rep, H, dk), k.dtype, "out")
+    if ws is None:
+        ws = _workspace(workspace_bytes(FN_CHUNK_REPS, d, n_rep), k.device)
+    _check(library().hla_chunk_reps(ctypes.byref(d), _ptr(k), window, _ptr(W["Wq"]), _ptr(W["Wk"]), _ptr(W["Wv"]),
+                                    _ptr(W["Wp"]), _ptr(W.get("Wr")), 0 if nh == 1 else dk * dk, _ptr(out),
+                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(k.device)), "hla_chunk_reps")
+    return out
+
+
 def route_mix(q, reps, At, Bc, n_rep=CHUNK, tau=1e-3, S0=None, gates_in=None, T=None, out=None, ws=None,
               C=CHUNK):
     """Router gates, skip mask, active lists, n_eff and the routed per-chunk states.
@@ -243,15 +269,21 @@ def route_mix(q, reps, At, Bc, n_rep=CHUNK, tau=1e-3, S0=None, gates_in=None, T=
     return dict(gates=gates, mask=mask, active_idx=aidx, active_cnt=acnt, n_eff=neff, S_routed=Sr)
 
 
-def hla_prefill(q, k, v, beta, alpha, tau=1e-3, gates_in=None, S0=None, C=CHUNK, handoff=True):
+def hla_prefill(q, k, v, beta, alpha, tau=1e-3, gates_in=None, S0=None, C=CHUNK, handoff=True, pooler=None,
+                window=32):
     """The routed prefill as three calls: transitions, routing, outputs from routed states.
-    Representatives are each chunk's raw keys (n_rep = C).  handoff passes W | U from the
-    first call to the last (bf16)."""
+    Representatives are each chunk's raw keys (n_rep = C), or with ``pooler`` (weights for
+    chunk_reps) the learned window representatives (n_rep = C / window).  handoff passes
+    W | U from the first call to the last (bf16)."""
     wu = wu_buffer(k, v, beta, alpha, C=C) if handoff else None
     At, Bc = chunk_transitions(k, v, beta, alpha, C=C, wu=wu)
-    r = route_mix(q, k, At, Bc, n_rep=C, tau=tau, S0=S0, gates_in=gates_in, C=C)
+    if pooler is None:
+        reps, n_rep = k, C
+    else:
+        reps, n_rep = chunk_reps(k, pooler, window=window, C=C), C // window
+    r = route_mix(q, reps, At, Bc, n_rep=n_rep, tau=tau, S0=S0, gates_in=gates_in, C=C)
     o, _ = gdn_prefill(q, k, v, beta, alpha, chunk_init=r["S_routed"], want_state=False, C=C, wu=wu)
-    r.update(At=At, Bc=Bc, o=o)
+    r.update(At=At, Bc=Bc, o=o, reps=reps)
     return r
 
 

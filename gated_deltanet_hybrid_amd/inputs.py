@@ -225,16 +225,19 @@ def gen_transitions(B, H, N, dk, dv, dtype="bf16", seed=0, stream=0, norm=0.95, 
     return to_storage(At, dtype), to_storage(Bc, dtype)
 
 
-def gen_pooler_weights(H, dk, dtype="bf16", seed=0, stream=0, shared=False, qk_scale=1.0) -> dict:
+def gen_pooler_weights(H, dk, dtype="bf16", seed=0, stream=0, shared=False, qk_scale=1.0, r_scale=None) -> dict:
     """Seeded weights of the chunk-representative pooler and the router query projection,
     each [H, dk, dk] (or [1, dk, dk] when ``shared``) in storage form, layout [out, in].
-    Wq, Wk ~ N(0, qk_scale^2), so the window's attention scores are of order one; Wv, Wp,
-    Wr ~ N(0, 1 / dk), so they roughly preserve vector norms."""
+    Wq, Wk ~ N(0, qk_scale^2), so the window's attention scores are of order one; Wv, Wp
+    ~ N(0, 1 / dk), so they roughly preserve vector norms; Wr ~ N(0, r_scale^2) (default
+    1 / sqrt(dk)); a large r_scale spreads the router's gates away from one half."""
     nh = 1 if shared else H
     out = {}
     for name in ("Wq", "Wk", "Wv", "Wp", "Wr"):
         rng = _rng(seed, stream, name, nh, dk)
         sd = qk_scale if name in ("Wq", "Wk") else 1.0 / math.sqrt(dk)
+        if name == "Wr" and r_scale is not None:
+            sd = r_scale
         out[name] = to_storage(sd * rng.standard_normal((nh, dk, dk)), dtype)
     return out
 

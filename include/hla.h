@@ -81,9 +81,10 @@ typedef enum {
   HLA_FN_CHUNK_TRANSITIONS = 0,
   HLA_FN_GDN_PREFILL = 1,
   HLA_FN_ROUTE_MIX = 2,
-  HLA_FN_WU_HANDOFF = 3 /* size of the optional wu buffer of hla_chunk_transitions and
-                           hla_gdn_prefill: B H ceil(T / 64) 64 (dk + dv) bf16 values;
-                           0 for float32, which takes no hand-off */
+  HLA_FN_WU_HANDOFF = 3, /* size of the optional wu buffer of hla_chunk_transitions and
+                            hla_gdn_prefill: B H ceil(T / 64) 64 (dk + dv) bf16 values;
+                            0 for float32, which takes no hand-off */
+  HLA_FN_CHUNK_REPS = 4  /* workspace of hla_chunk_reps; n_rep = C / window */
 } hla_fn_t;
 
 /*
@@ -141,6 +142,36 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
                              const float* beta, const float* alpha, const float* S0,
                              const float* chunk_init, const void* wu, float* o, float* S_final,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hla_chunk_reps -- learned representatives of every chunk.
+ * [HLA] Methodology paragraph 2: each chunk is cut into pooling windows of `window`
+ * consecutive tokens; one-head self-attention runs inside every window over its keys
+ * (scores scaled by 1/sqrt(dk), every token sees the whole window), the token outputs are
+ * mean-pooled and a learned projection gives one representative per window.  The router's
+ * learned query projection Wr is folded in: the output row is r' = Wr^T Wp pooled, so
+ * hla_route_mix and hla_gdn_decode, which score the plain query q against r', compute
+ * (Wr q) . (Wp pooled).  A window cut by the end of the sequence pools the tokens it has;
+ * a window with no tokens gets a zero row.
+ *   k      : [B, ld_T, H, dk] keys (dims d; dv is not used).
+ *   window : 8, 16 or 32 tokens (C / window representatives per chunk).
+ *   Wq, Wk, Wv, Wp : [dk, dk] weights in the dims' dtype, row-major [out, in] (a row
+ *           vector x maps to W x); head h's matrices start w_hstride elements after head
+ *           h-1's (w_hstride = 0: one set shared by all heads; else >= dk*dk).
+ *   Wr     : [dk, dk] query projection [out, in], same head stride, or NULL (identity).
+ *   reps   : [B, N * (C / window), H, dk] (out, dtype): chunk j's representatives are rows
+ *           [j n_rep, (j + 1) n_rep) with n_rep = C / window -- the reps argument of
+ *           hla_route_mix with that n_rep and ld_R = N n_rep.
+ *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_CHUNK_REPS, d,
+ *           C / window) bytes (float32 window means).
+ * Errors: HLA_ERR_NULL_ARG, HLA_ERR_BAD_SHAPE (window, w_hstride), HLA_ERR_BAD_DTYPE,
+ *         HLA_ERR_ALIGN (every pointer 16-byte aligned, head strides 16-byte multiples),
+ *         HLA_ERR_WORKSPACE, HLA_ERR_UNSUPPORTED, HLA_ERR_HIP.
+ */
+hla_status_t hla_chunk_reps(const hla_dims_t* d, const void* k, int32_t window, const void* Wq,
+                            const void* Wk, const void* Wv, const void* Wp, const void* Wr,
+                            int64_t w_hstride, void* reps, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /*
  * hla_route_mix -- HLA router gates and the gated composition of chunk transitions.
@@ -212,8 +243,9 @@ hla_status_t hla_gdn_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32
                             int32_t* n_cache, int32_t n_cap, const float* gates_in, float tau,
                             float* o, float* gates_out, int32_t commit, hipStream_t stream);
 
-/* Workspace bytes that entry point `fn` needs for dims `d` (n_rep is used by
- * HLA_FN_ROUTE_MIX).  `out` is a host pointer. */
+/* Workspace bytes that entry point `fn` needs for dims `d`; n_rep is the number of
+ * representatives per chunk for HLA_FN_CHUNK_REPS (C / window; it must divide C) and is
+ * ignored otherwise.  `out` is a host pointer. */
 hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep, size_t* out);
 
 /* Kernel kinds that hla_timing_read() reports. */
@@ -223,7 +255,8 @@ typedef enum {
   HLA_KERNEL_GATES = 2,    /* router: query-chunk means, gate scores, mask and lists  */
   HLA_KERNEL_COMPOSE = 3,  /* gated composition of chunk transitions                  */
   HLA_KERNEL_DECODE = 4,   /* single-token decode step                                */
-  HLA_KERNEL_COUNT = 5
+  HLA_KERNEL_REPS = 5,     /* learned representatives: window attention and mean-pool */
+  HLA_KERNEL_COUNT = 6
 } hla_kernel_t;
 
 /*

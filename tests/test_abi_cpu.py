@@ -179,3 +179,25 @@ def test_binding_fails_loudly_without_library(tmp_path):
             hla.library(str(tmp_path / "nope.so"))
     finally:
         hla._lib = saved
+
+
+def test_chunk_reps_validation(lib):
+    d = dims(T=256, C=64)  # N = 4 chunks
+    cr = lib.hla_chunk_reps
+    need = hla.workspace_bytes(hla.FN_CHUNK_REPS, d, 2)
+    assert need == 1 * 2 * 4 * 2 * 128 * 4  # float32 window means [B, H, N * n_rep, dk]
+    W = [P, P, P, P]  # Wq, Wk, Wv, Wp
+    ok = (ctypes.byref(d), P, 32, *W, None, 0, P, P, need, None)
+    # (d, k, window, Wq, Wk, Wv, Wp, Wr, w_hstride, reps, ws, ws_bytes, stream)
+    assert cr(ctypes.byref(d), None, 32, *W, None, 0, P, P, need, None) == NULL_ARG
+    assert cr(ctypes.byref(d), P, 32, P, P, None, P, None, 0, P, P, need, None) == NULL_ARG
+    assert cr(ctypes.byref(d), P, 32, *W, None, 0, None, P, need, None) == NULL_ARG
+    for bad_window in (0, 4, 24, 64):
+        assert cr(ctypes.byref(d), P, bad_window, *W, None, 0, P, P, need, None) == BAD_SHAPE
+    assert cr(ctypes.byref(d), P, 32, *W, None, 100, P, P, need, None) == BAD_SHAPE  # overlapping heads
+    assert cr(ctypes.byref(d), P, 32, *W, None, 128 * 128 + 4, P, P, need, None) == ALIGN  # 8-byte head step
+    assert cr(ctypes.byref(d), P, 32, *W, PU, 0, P, P, need, None) == ALIGN
+    assert cr(ctypes.byref(d), P, 32, *W, None, 0, P, P, need - 1, None) == WORKSPACE
+    assert cr(ctypes.byref(d), P, 32, *W, None, 0, P, None, 0, None) == WORKSPACE
+    assert lib.hla_workspace_bytes(hla.FN_CHUNK_REPS, ctypes.byref(d), 3, ctypes.byref(ctypes.c_size_t())) == BAD_SHAPE
+    assert len(ok) == 13
