@@ -42,3 +42,10 @@ from .gdn import (  # noqa: F401
     n_eff,
     PARITY_UNPINNED,
 )
+from .gdn2 import (  # noqa: F401
+    gdn2_recurrent,
+    gdn2_chunk_transition,
+    gdn2_chunk_transitions,
+    gdn2_routed_outputs,
+    gdn2_hla_prefill,
+)

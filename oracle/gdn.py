@@ -20,6 +20,8 @@ PARITY_UNPINNED = (
     "the decode-time gate query is the token's own q; the prefill gate query is the mean "
     "of q over the query chunk",
     "gates are per (batch, head)",
+    "Gated DeltaNet-2: the decay acts before the edit, the read uses k_t and the erase "
+    "is (S' k_t)(b_t o k_t)^T, the write (w_t o v_t) k_t^T (the pages give no formula)",
 )
 
 
