@@ -325,6 +325,80 @@ def bench_native_prefill(args, torch, hla, inputs):
     return res
 
 
+# ----------------------------------------------------------------------------- Gated DeltaNet-2
+# fp32 vector peak without packed-fp32 instructions (this build does not emit them):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flop per FMA x 2.4 GHz
+PEAK_FP32_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+
+
+def flops_gdn2_pass(n_tokens_heads, dk, dv, outputs):
+    """Token-loop chunk pass per token and head: every column of the map [P | Q] (dk + dv
+    columns) or of the state (dv columns) takes k.(D x) (dk FMA), D x (dk mul), the erase
+    (dk FMA) and the write (dk FMA; none for P columns); outputs add q . x (dk FMA)."""
+    if outputs:
+        return n_tokens_heads * dv * dk * (2 + 1 + 2 + 2 + 2)
+    return n_tokens_heads * (dk * dk * (2 + 1 + 2) + dv * dk * (2 + 1 + 2 + 2))
+
+
+def bench_gdn2_routed(args, torch, hla, inputs, x):
+    """The routed prefill step under the Gated DeltaNet-2 recurrence at the long-context
+    shape: GDN-2 chunk maps, the HLA router and composition, GDN-2 chunk outputs."""
+    W = inputs.WORKLOADS["routed_prefill"]
+    log(f"[gdn2_routed_prefill] generating channel-wise gates B={W.B} T={W.T} H={W.H}")
+    g = inputs.gen_gdn2_gates(W.B, W.T, W.H, W.dk, W.dv, seed=0, stream=inputs.STREAM["routed_prefill"])
+    ga, gb, gw = (to_dev(g[n], "f32", torch) for n in ("a", "b", "w"))
+    del g
+    q, k, v = (to_dev(a, W.dtype, torch) for a in (x.q, x.k, x.v))
+    dev = k.device
+    N = math.ceil(W.T / C)
+    d = hla.make_dims(W.B, W.T, W.H, W.T, W.dk, W.dv, hla.HLA_BF16, C)
+    At = torch.empty((W.B, W.H, N, W.dk, W.dk), dtype=k.dtype, device=dev)
+    Bc = torch.empty((W.B, W.H, N, W.dk, W.dv), dtype=k.dtype, device=dev)
+    ws = torch.empty(hla.workspace_bytes(hla.FN_ROUTE_MIX, d, C), dtype=torch.uint8, device=dev)
+    out = dict(gates=torch.empty((W.B, W.H, N, N), dtype=torch.float32, device=dev),
+               mask=torch.empty((W.B, W.H, N, N), dtype=torch.uint8, device=dev),
+               active_idx=torch.empty((W.B, W.H, N, N), dtype=torch.int32, device=dev),
+               active_cnt=torch.empty((W.B, W.H, N), dtype=torch.int32, device=dev),
+               n_eff=torch.empty((W.B, W.H, N), dtype=torch.float32, device=dev),
+               S_routed=torch.empty((W.B, W.H, N, W.dk, W.dv), dtype=torch.float32, device=dev))
+    o = torch.empty((W.B, W.T, W.H, W.dv), dtype=torch.float32, device=dev)
+
+    def step():
+        hla.gdn2_chunk_transitions(k, v, ga, gb, gw, At=At, Bc=Bc)
+        hla.route_mix(q, k, At, Bc, n_rep=C, tau=W.tau, out=out, ws=ws)
+        hla.gdn2_prefill(q, k, v, ga, gb, gw, chunk_init=out["S_routed"], want_state=False, o=o)
+
+    steps = max(3, args.steps // 2)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    hla.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    ch_ms, ch_n = hla.timing_read(hla.KERNEL_CHUNK)
+    cm_ms, cm_n = hla.timing_read(hla.KERNEL_COMPOSE)
+    hla.timing_enable(False)
+    th = W.B * W.T * W.H
+    fl_pass = flops_gdn2_pass(th, W.dk, W.dv, False) + flops_gdn2_pass(th, W.dk, W.dv, True)
+    chunk_s = ch_ms / ch_n / 1e3 * 2  # two chunk passes per step
+    ach = fl_pass / chunk_s / 1e12
+    res = dict(workload="routed_prefill under Gated DeltaNet-2 (channel-wise decay, erase and write gates), "
+                        "B=1 T=32768 H=16 d=128 C=64",
+               ms_per_step=dt * 1e3, tokens_per_s=W.B * W.T / dt, compose_ms=round(cm_ms / cm_n, 4),
+               chunk_passes_ms=round(chunk_s * 1e3, 4),
+               chunk_roofline=dict(kernel="gdn2_chunk_kernel (maps + outputs)", bound="alu", achieved=round(ach, 2),
+                                   peak=round(PEAK_FP32_VALU_TFLOPS, 1), unit="TFLOP/s",
+                                   frac=round(ach / PEAK_FP32_VALU_TFLOPS, 4), flops_per_step=fl_pass))
+    log(f"[gdn2_routed_prefill] {dt*1e3:.3f} ms/step, {W.B*W.T/dt/1e6:.3f} M tok/s, chunk passes "
+        f"{chunk_s*1e3:.3f} ms ({ach:.1f} TFLOP/s fp32 VALU), compose {cm_ms/cm_n:.3f} ms")
+    del q, k, v, ga, gb, gw, At, Bc, out, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 # ----------------------------------------------------------------------------- Tail-Replay
 def bench_tail_replay(args, torch, hla, inputs):
     W = inputs.WORKLOADS["tail_replay"]
@@ -503,6 +577,7 @@ def main():
     secondary = {}
     if not args.no_secondary:
         secondary.update(bench_routed_variants(args, torch, hla, inputs, x))
+        secondary["gdn2_routed_prefill"] = bench_gdn2_routed(args, torch, hla, inputs, x)
         secondary["decode"] = bench_decode(args, torch, hla, inputs)
         secondary["native_prefill"] = bench_native_prefill(args, torch, hla, inputs)
         secondary["tail_replay"] = bench_tail_replay(args, torch, hla, inputs)

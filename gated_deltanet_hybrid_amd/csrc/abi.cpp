@@ -97,10 +97,99 @@ int64_t reps_ws(const hla_dims_t* d, int32_t n_rep) {
 
 hla_status_t hip_status(hipError_t e) { return e == hipSuccess ? HLA_OK : HLA_ERR_HIP; }
 
+// One chunk pass of either recurrence: transitions (want_ab) or outputs from chunk_init.
+hipError_t chunk_pass(const hla::ChunkArgs& a, const hla_dims_t* d, bool want_ab, bool want_o, hipStream_t s) {
+  if (a.variant == 2) return hla::launch_gdn2_chunk(a, d->dtype, d->dk, d->dv, want_o, s);
+  return hla::launch_chunk(a, d->dtype, d->dk, d->dv, want_ab, want_o, s);
+}
+
 // Where a prefill's own transitions pass writes W | U: nowhere when the caller supplies
-// them (or for float32), else the workspace region.
-void* wu_internal(const hla_dims_t* d, const void* wu, void* region) {
-  return (wu || !HLA_WU_HANDOFF || d->dtype != HLA_BF16) ? nullptr : region;
+// them, for float32 or for the Gated DeltaNet-2 pass (which has no UT form), else the
+// workspace region.
+void* wu_internal(const hla_dims_t* d, const hla::ChunkArgs& a, const void* wu, void* region) {
+  return (wu || !HLA_WU_HANDOFF || d->dtype != HLA_BF16 || a.variant != 0) ? nullptr : region;
+}
+
+// Shared body of the transitions entry points (arguments validated by the caller; `a`
+// carries the token inputs of either recurrence).
+hla_status_t transitions_body(const hla_dims_t* d, hla::ChunkArgs a, void* At, void* Bc, void* wu, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  const PrefillWs w = prefill_ws(d);
+  if (d->C != kPiece && (!ws || (int64_t)ws_bytes < w.total_ab)) return HLA_ERR_WORKSPACE;
+  a.aux_out = wu;
+  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)n_pieces(d);
+  if (d->C == kPiece) {
+    a.At = At; a.Bc = Bc;
+    return hip_status(chunk_pass(a, d, true, false, stream));
+  }
+  // pieces of 64 tokens, then the composite map of every C / 64 consecutive pieces
+  char* base = static_cast<char*>(ws);
+  a.At = base + w.at_off;
+  a.Bc = base + w.bc_off;
+  hipError_t e = chunk_pass(a, d, true, false, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  hla::ScanArgs s{};
+  s.At = a.At; s.Bc = a.Bc; s.B = d->B; s.H = d->H; s.N = a.N;
+  s.seg = d->C / kPiece; s.seg_At = At; s.seg_Bc = Bc;
+  return hip_status(hla::launch_combine_segments(s, d->dk, d->dv, stream));
+}
+
+// Shared body of the prefill entry points.
+hla_status_t prefill_body(const hla_dims_t* d, hla::ChunkArgs a, const float* S0, const float* chunk_init,
+                          const void* wu, float* o, float* S_final, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int32_t N = (int32_t)n_pieces(d);
+  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = N;
+  const PrefillWs w = prefill_ws(d);
+  if (chunk_init) {
+    // routed: every chunk starts from its own given state
+    if (S0 || S_final || !o) return HLA_ERR_UNSUPPORTED;
+    a.o = o;
+    if (d->C == kPiece) {
+      a.chunk_init = chunk_init;
+      a.aux_in = wu;
+      return hip_status(chunk_pass(a, d, false, true, stream));
+    }
+    // C > 64: the start state of every 64-token piece from its chunk's routed state
+    if (!ws || (int64_t)ws_bytes < w.total) return HLA_ERR_WORKSPACE;
+    char* base = static_cast<char*>(ws);
+    a.At = base + w.at_off;
+    a.Bc = base + w.bc_off;
+    a.aux_out = wu_internal(d, a, wu, base + w.wu_off);
+    hipError_t e = chunk_pass(a, d, true, false, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+    hla::ScanArgs s{};
+    s.At = a.At; s.Bc = a.Bc; s.B = d->B; s.H = d->H; s.N = N;
+    s.seg = d->C / kPiece; s.seg_init = chunk_init;
+    s.states = reinterpret_cast<float*>(base + w.st_off);
+    e = hla::launch_scan_segments(s, d->dk, d->dv, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+    hla::ChunkArgs b = a;
+    b.At = nullptr; b.Bc = nullptr; b.aux_out = nullptr;
+    b.aux_in = wu ? wu : a.aux_out;
+    b.chunk_init = s.states;
+    return hip_status(chunk_pass(b, d, false, true, stream));
+  }
+  const int64_t need = o ? w.total : w.total_ab;
+  if (!ws || (int64_t)ws_bytes < need) return HLA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  a.At = base + w.at_off;
+  a.Bc = base + w.bc_off;
+  if (o) a.aux_out = wu_internal(d, a, wu, base + w.wu_off);
+  hipError_t e = chunk_pass(a, d, true, false, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  hla::ScanArgs s{};
+  s.At = a.At; s.Bc = a.Bc; s.S0 = S0;
+  s.states = o ? reinterpret_cast<float*>(base + w.st_off) : nullptr;
+  s.S_final = S_final;
+  s.B = d->B; s.H = d->H; s.N = N;
+  e = hla::launch_scan(s, d->dtype, d->dk, d->dv, stream);
+  if (e != hipSuccess || !o) return hip_status(e);
+  hla::ChunkArgs b = a;
+  b.At = nullptr; b.Bc = nullptr; b.aux_out = nullptr;
+  b.aux_in = wu ? wu : a.aux_out;
+  b.chunk_init = s.states;
+  b.o = o;
+  return hip_status(chunk_pass(b, d, false, true, stream));
 }
 
 }  // namespace
@@ -149,26 +238,21 @@ hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const voi
   if (!k || !v || !beta || !alpha || !At || !Bc) return HLA_ERR_NULL_ARG;
   if (!all_aligned(k, v, At, Bc, wu, ws) || !all_aligned4(beta, alpha)) return HLA_ERR_ALIGN;
   if (wu && d->dtype != HLA_BF16) return HLA_ERR_UNSUPPORTED;
-  const PrefillWs w = prefill_ws(d);
-  if (d->C != kPiece && (!ws || (int64_t)ws_bytes < w.total_ab)) return HLA_ERR_WORKSPACE;
   hla::ChunkArgs a{};
   a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
-  a.aux_out = wu;
-  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)n_pieces(d);
-  if (d->C == kPiece) {
-    a.At = At; a.Bc = Bc;
-    return hip_status(hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream));
-  }
-  // pieces of 64 tokens, then the composite map of every C / 64 consecutive pieces
-  char* base = static_cast<char*>(ws);
-  a.At = base + w.at_off;
-  a.Bc = base + w.bc_off;
-  hipError_t e = hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream);
-  if (e != hipSuccess) return HLA_ERR_HIP;
-  hla::ScanArgs s{};
-  s.At = a.At; s.Bc = a.Bc; s.B = d->B; s.H = d->H; s.N = a.N;
-  s.seg = d->C / kPiece; s.seg_At = At; s.seg_Bc = Bc;
-  return hip_status(hla::launch_combine_segments(s, d->dk, d->dv, stream));
+  return transitions_body(d, a, At, Bc, wu, ws, ws_bytes, stream);
+}
+
+hla_status_t hla_gdn2_chunk_transitions(const hla_dims_t* d, const void* k, const void* v, const float* a_decay,
+                                        const float* b_erase, const float* w_write, void* At, void* Bc, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (!k || !v || !a_decay || !b_erase || !w_write || !At || !Bc) return HLA_ERR_NULL_ARG;
+  if (!all_aligned(k, v, At, Bc, ws) || !all_aligned4(a_decay, b_erase, w_write)) return HLA_ERR_ALIGN;
+  hla::ChunkArgs a{};
+  a.k = k; a.v = v; a.ga = a_decay; a.gb = b_erase; a.gw = w_write; a.variant = 2;
+  return transitions_body(d, a, At, Bc, nullptr, ws, ws_bytes, stream);
 }
 
 hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, const void* v,
@@ -182,61 +266,24 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
   if (o && !q) return HLA_ERR_NULL_ARG;
   if (!all_aligned(q, k, v, S0, chunk_init, wu, S_final, ws) || !all_aligned4(beta, alpha, o)) return HLA_ERR_ALIGN;
   if (wu && d->dtype != HLA_BF16) return HLA_ERR_UNSUPPORTED;
-  const int32_t N = (int32_t)n_pieces(d);
   hla::ChunkArgs a{};
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
-  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = N;
-  const PrefillWs w = prefill_ws(d);
-  if (chunk_init) {
-    // routed: every chunk starts from its own given state
-    if (S0 || S_final || !o) return HLA_ERR_UNSUPPORTED;
-    a.o = o;
-    if (d->C == kPiece) {
-      a.chunk_init = chunk_init;
-      a.aux_in = wu;
-      return hip_status(hla::launch_chunk(a, d->dtype, d->dk, d->dv, false, true, stream));
-    }
-    // C > 64: the start state of every 64-token piece from its chunk's routed state
-    if (!ws || (int64_t)ws_bytes < w.total) return HLA_ERR_WORKSPACE;
-    char* base = static_cast<char*>(ws);
-    a.At = base + w.at_off;
-    a.Bc = base + w.bc_off;
-    a.aux_out = wu_internal(d, wu, base + w.wu_off);
-    hipError_t e = hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream);
-    if (e != hipSuccess) return HLA_ERR_HIP;
-    hla::ScanArgs s{};
-    s.At = a.At; s.Bc = a.Bc; s.B = d->B; s.H = d->H; s.N = N;
-    s.seg = d->C / kPiece; s.seg_init = chunk_init;
-    s.states = reinterpret_cast<float*>(base + w.st_off);
-    e = hla::launch_scan_segments(s, d->dk, d->dv, stream);
-    if (e != hipSuccess) return HLA_ERR_HIP;
-    hla::ChunkArgs b = a;
-    b.At = nullptr; b.Bc = nullptr; b.aux_out = nullptr;
-    b.aux_in = wu ? wu : a.aux_out;
-    b.chunk_init = s.states;
-    return hip_status(hla::launch_chunk(b, d->dtype, d->dk, d->dv, false, true, stream));
-  }
-  const int64_t need = o ? w.total : w.total_ab;
-  if (!ws || (int64_t)ws_bytes < need) return HLA_ERR_WORKSPACE;
-  char* base = static_cast<char*>(ws);
-  a.At = base + w.at_off;
-  a.Bc = base + w.bc_off;
-  if (o) a.aux_out = wu_internal(d, wu, base + w.wu_off);
-  hipError_t e = hla::launch_chunk(a, d->dtype, d->dk, d->dv, true, false, stream);
-  if (e != hipSuccess) return HLA_ERR_HIP;
-  hla::ScanArgs s{};
-  s.At = a.At; s.Bc = a.Bc; s.S0 = S0;
-  s.states = o ? reinterpret_cast<float*>(base + w.st_off) : nullptr;
-  s.S_final = S_final;
-  s.B = d->B; s.H = d->H; s.N = N;
-  e = hla::launch_scan(s, d->dtype, d->dk, d->dv, stream);
-  if (e != hipSuccess || !o) return hip_status(e);
-  hla::ChunkArgs b = a;
-  b.At = nullptr; b.Bc = nullptr; b.aux_out = nullptr;
-  b.aux_in = wu ? wu : a.aux_out;
-  b.chunk_init = s.states;
-  b.o = o;
-  return hip_status(hla::launch_chunk(b, d->dtype, d->dk, d->dv, false, true, stream));
+  return prefill_body(d, a, S0, chunk_init, wu, o, S_final, ws, ws_bytes, stream);
+}
+
+hla_status_t hla_gdn2_prefill(const hla_dims_t* d, const void* q, const void* k, const void* v, const float* a_decay,
+                              const float* b_erase, const float* w_write, const float* S0, const float* chunk_init,
+                              float* o, float* S_final, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (!k || !v || !a_decay || !b_erase || !w_write) return HLA_ERR_NULL_ARG;
+  if (!o && !S_final) return HLA_ERR_NULL_ARG;
+  if (o && !q) return HLA_ERR_NULL_ARG;
+  if (!all_aligned(q, k, v, S0, chunk_init, S_final, ws) || !all_aligned4(a_decay, b_erase, w_write, o))
+    return HLA_ERR_ALIGN;
+  hla::ChunkArgs a{};
+  a.q = q; a.k = k; a.v = v; a.ga = a_decay; a.gb = b_erase; a.gw = w_write; a.variant = 2;
+  return prefill_body(d, a, S0, chunk_init, nullptr, o, S_final, ws, ws_bytes, stream);
 }
 
 hla_status_t hla_chunk_reps(const hla_dims_t* d, const void* k, int32_t window, const void* Wq, const void* Wk,

@@ -23,11 +23,20 @@ struct ChunkArgs {
   // then skips the UT transform) when aux_in is set.  [B,H,N, (dk+dv)/32, 4, 64 lanes, 8].
   void* aux_out;
   const void* aux_in;
+  // Gated DeltaNet-2 (variant 2): per-token channel-wise decay ga [B,ld_T,H,dk], erase gate
+  // gb [B,ld_T,H,dk] and write gate gw [B,ld_T,H,dv] (float32) replace beta and alpha.
+  const float* ga;
+  const float* gb;
+  const float* gw;
+  int32_t variant;  // 0: Gated DeltaNet, 2: Gated DeltaNet-2
 };
 
 // Either the transitions (want_ab) or the outputs from chunk_init (want_o).
 hipError_t launch_chunk(const ChunkArgs& a, int dtype, int dk, int dv, bool want_ab, bool want_o,
                         hipStream_t s);
+// Gated DeltaNet-2 chunk pass: maps (At, Bc) of every 64-token piece, or (want_o) the
+// outputs from chunk_init.
+hipError_t launch_gdn2_chunk(const ChunkArgs& a, int dtype, int dk, int dv, bool want_o, hipStream_t s);
 // bytes of the W | U fragment image of one chunk
 constexpr int64_t aux_chunk_bytes(int dk, int dv) { return (int64_t)64 * (dk + dv) * 2; }
 

@@ -44,6 +44,10 @@ _SIGS = {
                                                ctypes.c_size_t, _P]),
     "hla_gdn_prefill": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]),
+    "hla_gdn2_chunk_transitions": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P,
+                                                    ctypes.c_size_t, _P]),
+    "hla_gdn2_prefill": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
     "hla_chunk_reps": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, ctypes.c_int32, _P, _P, _P, _P, _P,
                                         ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]),
     "hla_route_mix": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
@@ -199,6 +203,76 @@ def gdn_prefill(q, k, v, beta, alpha, S0=None, chunk_init=None, want_o=True, wan
                                      _ptr(alpha), _ptr(S0), _ptr(chunk_init), _ptr(wu), _ptr(o), _ptr(S_final),
                                      _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)), "hla_gdn_prefill")
     return o, S_final
+
+
+def _gdn2_gates(d, a_decay, b_erase, w_write):
+    B, T, H, dk, dv = d.B, d.T, d.H, d.dk, d.dv
+    for t, width, name in ((a_decay, dk, "a_decay"), (b_erase, dk, "b_erase"), (w_write, dv, "w_write")):
+        Bx, Tx, Hx, dx, ld = _token_view(t, name)
+        if (Bx, Tx, Hx, dx, ld) != (B, T, H, width, d.ld_T) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [B, T, H, {width}] with k's row layout")
+
+
+def gdn2_chunk_transitions(k, v, a_decay, b_erase, w_write, At=None, Bc=None, C=CHUNK, ws=None):
+    """Exact affine maps of every chunk under the Gated DeltaNet-2 recurrence."""
+    B, T, H, dk, ld_T = _token_view(k, "k")
+    dv = v.shape[-1]
+    d = make_dims(B, T, H, ld_T, dk, dv, _dtype_code(k), C)
+    _gdn2_gates(d, a_decay, b_erase, w_write)
+    N = math.ceil(T / C)
+    At = torch.empty((B, H, N, dk, dk), dtype=k.dtype, device=k.device) if At is None else At
+    Bc = torch.empty((B, H, N, dk, dv), dtype=k.dtype, device=k.device) if Bc is None else Bc
+    _need(At, (B, H, N, dk, dk), k.dtype, "At")
+    _need(Bc, (B, H, N, dk, dv), k.dtype, "Bc")
+    if ws is None:
+        ws = _workspace(workspace_bytes(FN_CHUNK_TRANSITIONS, d), k.device)
+    _check(library().hla_gdn2_chunk_transitions(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(a_decay), _ptr(b_erase),
+                                                _ptr(w_write), _ptr(At), _ptr(Bc), _ptr(ws),
+                                                0 if ws is None else ws.numel(), _stream(k.device)),
+           "hla_gdn2_chunk_transitions")
+    return At, Bc
+
+
+def gdn2_prefill(q, k, v, a_decay, b_erase, w_write, S0=None, chunk_init=None, want_o=True, want_state=True,
+                 o=None, S_final=None, ws=None, C=CHUNK):
+    """Chunkwise Gated DeltaNet-2 prefill (native or routed), as gdn_prefill."""
+    B, T, H, dk, ld_T = _token_view(k, "k")
+    dv = v.shape[-1]
+    d = make_dims(B, T, H, ld_T, dk, dv, _dtype_code(k), C)
+    _gdn2_gates(d, a_decay, b_erase, w_write)
+    N = math.ceil(T / C)
+    dev = k.device
+    if want_o and o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    if not want_o:
+        o = None
+    if chunk_init is not None:
+        want_state = False
+    if want_state and S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if not want_state:
+        S_final = None
+    _need(o, (B, T, H, dv), torch.float32, "o")
+    _need(S0, (B, H, dk, dv), torch.float32, "S0")
+    _need(chunk_init, (B, H, N, dk, dv), torch.float32, "chunk_init")
+    _need(S_final, (B, H, dk, dv), torch.float32, "S_final")
+    if ws is None and (chunk_init is None or C != CHUNK):
+        ws = _workspace(workspace_bytes(FN_GDN_PREFILL, d), dev)
+    _check(library().hla_gdn2_prefill(ctypes.byref(d), _ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(a_decay),
+                                      _ptr(b_erase), _ptr(w_write), _ptr(S0), _ptr(chunk_init), _ptr(o),
+                                      _ptr(S_final), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)),
+           "hla_gdn2_prefill")
+    return o, S_final
+
+
+def gdn2_hla_prefill(q, k, v, a_decay, b_erase, w_write, tau=1e-3, gates_in=None, S0=None, C=CHUNK):
+    """The routed prefill under the Gated DeltaNet-2 recurrence: GDN-2 chunk maps, the HLA
+    router and composition unchanged, GDN-2 chunk outputs from the routed states."""
+    At, Bc = gdn2_chunk_transitions(k, v, a_decay, b_erase, w_write, C=C)
+    r = route_mix(q, k, At, Bc, n_rep=C, tau=tau, S0=S0, gates_in=gates_in, C=C)
+    o, _ = gdn2_prefill(q, k, v, a_decay, b_erase, w_write, chunk_init=r["S_routed"], want_state=False, C=C)
+    r.update(At=At, Bc=Bc, o=o)
+    return r
 
 
 def chunk_reps(k, W, window=32, C=CHUNK, out=None, ws=None):

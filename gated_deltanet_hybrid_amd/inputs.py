@@ -31,7 +31,7 @@ import numpy as np
 
 SEGMENT = 4096
 _TENSOR_ID = {"q": 1, "k": 2, "v": 3, "beta": 4, "alpha": 5, "gates": 6, "At": 7, "Bc": 8, "S0": 9,
-              "Wq": 10, "Wk": 11, "Wv": 12, "Wp": 13, "Wr": 14}
+              "Wq": 10, "Wk": 11, "Wv": 12, "Wp": 13, "Wr": 14, "ga": 15, "gb": 16, "gw": 17}
 
 
 # --------------------------------------------------------------------------- rounding
@@ -239,6 +239,23 @@ def gen_pooler_weights(H, dk, dtype="bf16", seed=0, stream=0, shared=False, qk_s
         if name == "Wr" and r_scale is not None:
             sd = r_scale
         out[name] = to_storage(sd * rng.standard_normal((nh, dk, dk)), dtype)
+    return out
+
+
+def gen_gdn2_gates(B, T, H, dk, dv, seed=0, stream=0, alpha_mode="config", t_range=None) -> dict:
+    """Per-token, per-channel gates of the Gated DeltaNet-2 recurrence, float32:
+    a [B, T, H, dk] = exp(-softplus(x + 2)) (the "slow" variant x - 3), b [B, T, H, dk] =
+    sigmoid(x) and w [B, T, H, dv] = sigmoid(x), x ~ N(0, 1) drawn per (tensor, b, h,
+    4096-token segment) like the token tensors, so any token range regenerates alone."""
+    t0, t1 = (0, T) if t_range is None else t_range
+    shift = -3.0 if alpha_mode == "slow" else 2.0
+    out = {n: np.empty((B, t1 - t0, H, wdt), np.float32) for n, wdt in (("a", dk), ("b", dk), ("w", dv))}
+    for b in range(B):
+        for h in range(H):
+            out["a"][b, :, h] = np.exp(-_softplus(_normal_rows(seed, stream, "ga", b, h, t0, t1, dk).astype(np.float64)
+                                                  + shift))
+            out["b"][b, :, h] = _sigmoid(_normal_rows(seed, stream, "gb", b, h, t0, t1, dk).astype(np.float64))
+            out["w"][b, :, h] = _sigmoid(_normal_rows(seed, stream, "gw", b, h, t0, t1, dv).astype(np.float64))
     return out
 
 

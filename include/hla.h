@@ -144,6 +144,35 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * hla_gdn2_chunk_transitions, hla_gdn2_prefill -- the same two calls for the Gated
+ * DeltaNet-2 recurrence.
+ * [GDN2] the Gated DeltaNet-2 abstract (thelatestinai.com pages): channel-wise decay, a
+ * channel-wise erase gate on the key side and a channel-wise write gate on the value side;
+ * with one scalar for both gates it is Kimi Delta Attention, and with a scalar decay too,
+ * Gated DeltaNet.  The formula taken here (the pages print none): with the math state S
+ * [dv, dk], each token does
+ *     S' = S diag(a_t),   S = S' - (S' k_t)(b_t o k_t)^T + (w_t o v_t) k_t^T,   o_t = S q_t.
+ * Each token is affine in S, so each chunk is one exact affine map and hla_route_mix
+ * composes these maps exactly as it composes Gated DeltaNet's ([HLA] Methodology
+ * paragraph 1).
+ *   a_decay [B, ld_T, H, dk], b_erase [B, ld_T, H, dk], w_write [B, ld_T, H, dv]: float32
+ *           per-token gates (4-byte aligned) in place of beta and alpha.
+ *   Every other argument, output, mode, workspace size and error is as for
+ *           hla_chunk_transitions and hla_gdn_prefill, which have no wu argument here (the
+ *           W | U hand-off belongs to Gated DeltaNet's UT form).
+ * The chunk pass runs each 64-token piece's tokens in float32, so its cost is
+ * O(C dk (dk + dv)) vector arithmetic per piece rather than matrix-core work.
+ */
+hla_status_t hla_gdn2_chunk_transitions(const hla_dims_t* d, const void* k, const void* v,
+                                        const float* a_decay, const float* b_erase,
+                                        const float* w_write, void* At, void* Bc, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
+hla_status_t hla_gdn2_prefill(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                              const float* a_decay, const float* b_erase, const float* w_write,
+                              const float* S0, const float* chunk_init, float* o, float* S_final,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * hla_chunk_reps -- learned representatives of every chunk.
  * [HLA] Methodology paragraph 2: each chunk is cut into pooling windows of `window`
  * consecutive tokens; one-head self-attention runs inside every window over its keys

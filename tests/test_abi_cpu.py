@@ -201,3 +201,25 @@ def test_chunk_reps_validation(lib):
     assert cr(ctypes.byref(d), P, 32, *W, None, 0, P, None, 0, None) == WORKSPACE
     assert lib.hla_workspace_bytes(hla.FN_CHUNK_REPS, ctypes.byref(d), 3, ctypes.byref(ctypes.c_size_t())) == BAD_SHAPE
     assert len(ok) == 13
+
+
+def test_gdn2_validation(lib):
+    d = dims()
+    tr, pre = lib.hla_gdn2_chunk_transitions, lib.hla_gdn2_prefill
+    # (d, k, v, a, b, w, At, Bc, ws, ws_bytes, stream)
+    for i in range(7):
+        args = [P] * 7
+        args[i] = None
+        assert tr(ctypes.byref(d), *args, None, 0, None) == NULL_ARG
+    assert tr(ctypes.byref(d), P, P, P + 2, P, P, P, P, None, 0, None) == ALIGN   # gates need 4 bytes
+    assert tr(ctypes.byref(d), P, P, P + 4, P, P, P, P, None, 0, None) != ALIGN
+    assert tr(ctypes.byref(d), PU, P, P, P, P, P, P, None, 0, None) == ALIGN
+    assert tr(ctypes.byref(dims(C=256)), P, P, P, P, P, P, P, None, 0, None) == WORKSPACE
+    assert tr(ctypes.byref(dims(C=128, dtype=0)), P, P, P, P, P, P, P, None, 0, None) == UNSUPPORTED
+    # (d, q, k, v, a, b, w, S0, chunk_init, o, S_final, ws, ws_bytes, stream)
+    need = hla.workspace_bytes(hla.FN_GDN_PREFILL, d)
+    assert pre(ctypes.byref(d), P, P, P, P, P, P, None, None, None, None, P, need, None) == NULL_ARG
+    assert pre(ctypes.byref(d), None, P, P, P, P, P, None, None, P, None, P, need, None) == NULL_ARG
+    assert pre(ctypes.byref(d), P, P, P, P, P, P, P, P, P, None, None, 0, None) == UNSUPPORTED  # routed with S0
+    assert pre(ctypes.byref(d), P, P, P, P, P, P, None, None, P, P, P, need - 1, None) == WORKSPACE
+    assert pre(ctypes.byref(d), P, P, P, P, None, P, None, None, P, P, P, need, None) == NULL_ARG
