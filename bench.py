@@ -248,8 +248,11 @@ def bench_routed_variants(args, torch, hla, inputs, x):
 
 
 # ----------------------------------------------------------------------------- decode
-def bench_decode(args, torch, hla, inputs):
+def bench_decode(args, torch, hla, inputs, gdn2=False):
+    """Decode at Bs=256, H=16 with 64 cached chunks per sequence; ``gdn2`` runs the Gated
+    DeltaNet-2 live update (channel-wise gates per token) instead of Gated DeltaNet's."""
     W = inputs.WORKLOADS["decode"]
+    tag = "gdn2_decode" if gdn2 else "decode"
     Bs, H, dk, dv, n_cap = W.B, W.H, W.dk, W.dv, W.n_cache
     log(f"[decode] generating {n_cap} cached chunks per sequence for Bs={Bs} H={H}")
     hist = inputs.gen_tokens(Bs, n_cap * C, H, dk, dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["decode"],
@@ -269,13 +272,21 @@ def bench_decode(args, torch, hla, inputs):
     toks = [inputs.gen_decode_tokens(Bs, H, dk, dv, step=s, dtype=W.dtype, seed=0, stream=inputs.STREAM["decode"])
             for s in range(n_tok)]
     toks = [{kk: to_dev(vv, W.dtype if kk in ("q", "k", "v") else "f32", torch) for kk, vv in t.items()} for t in toks]
+    if gdn2:
+        for s_, t in enumerate(toks):
+            g = inputs.gen_gdn2_decode_gates(Bs, H, dk, dv, step=s_, seed=0, stream=inputs.STREAM["decode"])
+            t.update({n: to_dev(g[n], "f32", torch) for n in ("a", "b", "w")})
     it = [0]
 
     def step():
         t = toks[it[0] % n_tok]
         it[0] += 1
-        hla.gdn_decode(t["q"], t["k"], t["v"], t["beta"], t["alpha"], S, At_cur=A, At_cache=At_cache,
-                       Bc_cache=Bc_cache, reps_cache=reps, n_cache=n_cache, tau=W.tau, o=o)
+        if gdn2:
+            hla.gdn2_decode(t["q"], t["k"], t["v"], t["a"], t["b"], t["w"], S, At_cur=A, At_cache=At_cache,
+                            Bc_cache=Bc_cache, reps_cache=reps, n_cache=n_cache, tau=W.tau, o=o)
+        else:
+            hla.gdn_decode(t["q"], t["k"], t["v"], t["beta"], t["alpha"], S, At_cur=A, At_cache=At_cache,
+                           Bc_cache=Bc_cache, reps_cache=reps, n_cache=n_cache, tau=W.tau, o=o)
 
     steps = args.decode_steps
     for _ in range(8):
@@ -291,16 +302,16 @@ def bench_decode(args, torch, hla, inputs):
     hla.timing_enable(False)
     e = 2  # bf16 bytes
     per_seqhead = (2 * dk * dv * 4 + 2 * dk * dk * 4 + n_cap * (dk * dk + dk * dv) * e + n_cap * C * dk * e
-                   + (2 * dk + dv) * e + 2 * 4 + dv * 4)
+                   + (2 * dk + dv) * e + ((2 * dk + dv) * 4 if gdn2 else 2 * 4) + dv * 4)
     bytes_step = Bs * H * per_seqhead
     kern_s = dec_ms / dec_n / 1e3
-    res = dict(workload="decode", Bs=Bs, H=H, cached_chunks=n_cap, steps=steps, ms_per_step=dt * 1e3,
+    res = dict(workload=tag, Bs=Bs, H=H, cached_chunks=n_cap, steps=steps, ms_per_step=dt * 1e3,
                tokens_per_s=Bs / dt, hbm_gbs=bytes_step / kern_s / 1e9,
                roofline=dict(kernel="decode_kernel", bound="hbm", achieved=round(bytes_step / kern_s / 1e9, 1),
                              peak=PEAK_HBM_GBS, unit="GB/s", frac=round(bytes_step / kern_s / 1e9 / PEAK_HBM_GBS, 4),
                              bytes_per_launch=bytes_step, avg_launch_ms=round(kern_s * 1e3, 4)),
                note="no commit while timing; live chunk extends past 64 tokens so every step does the same work")
-    log(f"[decode] {dt*1e3:.3f} ms/step, {Bs/dt:.0f} tok/s, kernel {kern_s*1e3:.3f} ms, "
+    log(f"[{tag}] {dt*1e3:.3f} ms/step, {Bs/dt:.0f} tok/s, kernel {kern_s*1e3:.3f} ms, "
         f"{bytes_step/kern_s/1e9:.0f} GB/s")
     del At_cache, Bc_cache, reps, S, A, toks
     torch.cuda.empty_cache()
@@ -579,6 +590,7 @@ def main():
         secondary.update(bench_routed_variants(args, torch, hla, inputs, x))
         secondary["gdn2_routed_prefill"] = bench_gdn2_routed(args, torch, hla, inputs, x)
         secondary["decode"] = bench_decode(args, torch, hla, inputs)
+        secondary["gdn2_decode"] = bench_decode(args, torch, hla, inputs, gdn2=True)
         secondary["native_prefill"] = bench_native_prefill(args, torch, hla, inputs)
         secondary["tail_replay"] = bench_tail_replay(args, torch, hla, inputs)
     cpu = None

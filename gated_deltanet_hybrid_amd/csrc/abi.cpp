@@ -332,15 +332,15 @@ hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps,
   return hip_status(hla::launch_route(a, d->dtype, d->dk, d->dv, stream));
 }
 
-hla_status_t hla_gdn_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q,
-                            const void* k, const void* v, const float* beta, const float* alpha, float* S_cur,
-                            float* At_cur, void* At_cache, void* Bc_cache, const void* reps_cache, int32_t n_rep,
-                            int32_t* n_cache, int32_t n_cap, const float* gates_in, float tau, float* o,
-                            float* gates_out, int32_t commit, hipStream_t stream) {
+// Shared checks of the two decode entry points (everything but the per-token gates).
+static hla_status_t decode_checks(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q, const void* k,
+                           const void* v, float* S_cur, float* At_cur, void* At_cache, void* Bc_cache,
+                           const void* reps_cache, int32_t n_rep, int32_t* n_cache, int32_t n_cap,
+                           const float* gates_in, float tau, float* o, float* gates_out, int32_t commit) {
   if (dtype != HLA_F32 && dtype != HLA_BF16) return HLA_ERR_BAD_DTYPE;
   if (Bs < 1 || H < 1 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return HLA_ERR_BAD_SHAPE;
   if ((double)Bs * (double)H > (double)kMaxGrid) return HLA_ERR_BAD_SHAPE;
-  if (!q || !k || !v || !beta || !alpha || !S_cur || !o) return HLA_ERR_NULL_ARG;
+  if (!q || !k || !v || !S_cur || !o) return HLA_ERR_NULL_ARG;
   if (commit != 0 && commit != 1) return HLA_ERR_BAD_SHAPE;
   if (!At_cur) {
     if (commit) return HLA_ERR_UNSUPPORTED;
@@ -353,11 +353,43 @@ hla_status_t hla_gdn_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32
     }
     if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
   }
-  if (!all_aligned(S_cur, At_cur, At_cache, Bc_cache, reps_cache) ||
-      !all_aligned4(q, k, v, beta, alpha, gates_in, o, gates_out))
+  if (!all_aligned(S_cur, At_cur, At_cache, Bc_cache, reps_cache) || !all_aligned4(q, k, v, gates_in, o, gates_out))
     return HLA_ERR_ALIGN;
+  return HLA_OK;
+}
+
+hla_status_t hla_gdn_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q,
+                            const void* k, const void* v, const float* beta, const float* alpha, float* S_cur,
+                            float* At_cur, void* At_cache, void* Bc_cache, const void* reps_cache, int32_t n_rep,
+                            int32_t* n_cache, int32_t n_cap, const float* gates_in, float tau, float* o,
+                            float* gates_out, int32_t commit, hipStream_t stream) {
+  hla_status_t st = decode_checks(Bs, H, dk, dv, dtype, q, k, v, S_cur, At_cur, At_cache, Bc_cache, reps_cache, n_rep,
+                                  n_cache, n_cap, gates_in, tau, o, gates_out, commit);
+  if (st != HLA_OK) return st;
+  if (!beta || !alpha) return HLA_ERR_NULL_ARG;
+  if (!all_aligned4(beta, alpha)) return HLA_ERR_ALIGN;
   hla::DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.alpha = alpha; a.S_cur = S_cur; a.At_cur = At_cur;
+  a.At_cache = At_cache; a.Bc_cache = Bc_cache; a.reps_cache = reps_cache; a.n_rep = n_rep; a.n_cache = n_cache;
+  a.n_cap = n_cap; a.gates_in = gates_in; a.tau = tau; a.o = o; a.gates_out = gates_out; a.commit = commit;
+  a.Bs = Bs; a.H = H;
+  return hip_status(hla::launch_decode(a, dtype, dk, dv, stream));
+}
+
+hla_status_t hla_gdn2_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q,
+                             const void* k, const void* v, const float* a_decay, const float* b_erase,
+                             const float* w_write, float* S_cur, float* At_cur, void* At_cache, void* Bc_cache,
+                             const void* reps_cache, int32_t n_rep, int32_t* n_cache, int32_t n_cap,
+                             const float* gates_in, float tau, float* o, float* gates_out, int32_t commit,
+                             hipStream_t stream) {
+  hla_status_t st = decode_checks(Bs, H, dk, dv, dtype, q, k, v, S_cur, At_cur, At_cache, Bc_cache, reps_cache, n_rep,
+                                  n_cache, n_cap, gates_in, tau, o, gates_out, commit);
+  if (st != HLA_OK) return st;
+  if (!a_decay || !b_erase || !w_write) return HLA_ERR_NULL_ARG;
+  if (!all_aligned4(a_decay, b_erase, w_write)) return HLA_ERR_ALIGN;
+  hla::DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v; a.ga = a_decay; a.gb = b_erase; a.gw = w_write; a.variant = 2;
+  a.S_cur = S_cur; a.At_cur = At_cur;
   a.At_cache = At_cache; a.Bc_cache = Bc_cache; a.reps_cache = reps_cache; a.n_rep = n_rep; a.n_cache = n_cache;
   a.n_cap = n_cap; a.gates_in = gates_in; a.tau = tau; a.o = o; a.gates_out = gates_out; a.commit = commit;
   a.Bs = Bs; a.H = H;

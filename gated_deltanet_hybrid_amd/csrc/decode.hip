@@ -22,15 +22,27 @@ namespace hla {
 
 constexpr int kMaxCache = 1024;  // largest n_cap a decode call accepts
 
+// Per-row token vectors of the Gated DeltaNet-2 live update (LDS): ka = k o a, qa = q o a,
+// a, e = b o k; the write vector (w o v) is passed as s_v and qe = q . e.
+struct G2Rows {
+  const float* ka;
+  const float* qa;
+  const float* a;
+  const float* e;
+  float qe;
+};
+
 // One read + write pass over a live [DK][W] matrix `mat` (float32, row-major):
 //   u = k^T mat, z0 = q^T mat
 //   state      (IS_STATE): mat' = alpha mat + beta k (v - alpha u)^T,  out = q^T mat'
 //   transition (else)    : mat' = alpha mat - alpha beta k u^T,        out = q^T mat'
+// Gated DeltaNet-2 (G2): u = (k o a)^T mat, z0 = (q o a)^T mat and
+//   mat' = diag(a) mat - e u^T (+ k (w o v)^T for the state),  out = z0 - qe u (+ qk (w o v)).
 // With `commit`, mat' goes to the cache slot (cast to T) and mat is reset (0, or I).
-template <class T, int DK, int W, bool IS_STATE, int NT>
+template <class T, int DK, int W, bool IS_STATE, int NT, bool G2>
 __device__ __forceinline__ void live_pass(float* mat, T* cache_out, bool commit, float alpha, float beta, float qk,
                           const float* s_q, const float* s_k, const float* s_v, float* red0, float* red1,
-                          int red_size, float* s_u, float* out) {
+                          int red_size, float* s_u, float* out, const G2Rows& g2) {
   constexpr int CPR = W / 4, RPP = NT / CPR, NP = DK / RPP;
   const int tid = threadIdx.x;
   const int col = (tid % CPR) * 4, r0 = tid / CPR;
@@ -40,7 +52,7 @@ __device__ __forceinline__ void live_pass(float* mat, T* cache_out, bool commit,
   for (int p = 0; p < NP; ++p) {
     const int r = p * RPP + r0;
     m[p] = *reinterpret_cast<const float4*>(mat + r * W + col);
-    const float kr = s_k[r], qr = s_q[r];
+    const float kr = G2 ? g2.ka[r] : s_k[r], qr = G2 ? g2.qa[r] : s_q[r];
     pu.x += kr * m[p].x; pu.y += kr * m[p].y; pu.z += kr * m[p].z; pu.w += kr * m[p].w;
     pz.x += qr * m[p].x; pz.y += qr * m[p].y; pz.z += qr * m[p].z; pz.w += qr * m[p].w;
   }
@@ -52,23 +64,33 @@ __device__ __forceinline__ void live_pass(float* mat, T* cache_out, bool commit,
     float u = 0.f, z = 0.f;
     for (int g2 = 0; g2 < RPP; ++g2) { u += red0[g2 * W + tid]; z += red1[g2 * W + tid]; }
     s_u[tid] = u;
-    if (IS_STATE) out[tid] = alpha * z + beta * qk * (s_v[tid] - alpha * u);
+    if constexpr (G2) out[tid] = z - g2.qe * u + (IS_STATE ? qk * s_v[tid] : 0.f);
+    else if (IS_STATE) out[tid] = alpha * z + beta * qk * (s_v[tid] - alpha * u);
     else out[tid] = alpha * z - alpha * beta * qk * u;
   }
   __syncthreads();
   const float4 uu = *reinterpret_cast<const float4*>(&s_u[col]);
   float4 dd;
-  if (IS_STATE) dd = make_float4(s_v[col] - alpha * uu.x, s_v[col + 1] - alpha * uu.y, s_v[col + 2] - alpha * uu.z, s_v[col + 3] - alpha * uu.w);
+  if constexpr (G2) dd = IS_STATE ? *reinterpret_cast<const float4*>(&s_v[col]) : make_float4(0.f, 0.f, 0.f, 0.f);
+  else if (IS_STATE) dd = make_float4(s_v[col] - alpha * uu.x, s_v[col + 1] - alpha * uu.y, s_v[col + 2] - alpha * uu.z, s_v[col + 3] - alpha * uu.w);
   else dd = make_float4(-alpha * uu.x, -alpha * uu.y, -alpha * uu.z, -alpha * uu.w);
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int r = p * RPP + r0;
-    const float bk = beta * s_k[r];
     float4 nm;
-    nm.x = alpha * m[p].x + bk * dd.x;
-    nm.y = alpha * m[p].y + bk * dd.y;
-    nm.z = alpha * m[p].z + bk * dd.z;
-    nm.w = alpha * m[p].w + bk * dd.w;
+    if constexpr (G2) {
+      const float ar = g2.a[r], er = g2.e[r], kr = s_k[r];
+      nm.x = ar * m[p].x - er * uu.x + kr * dd.x;
+      nm.y = ar * m[p].y - er * uu.y + kr * dd.y;
+      nm.z = ar * m[p].z - er * uu.z + kr * dd.z;
+      nm.w = ar * m[p].w - er * uu.w + kr * dd.w;
+    } else {
+      const float bk = beta * s_k[r];
+      nm.x = alpha * m[p].x + bk * dd.x;
+      nm.y = alpha * m[p].y + bk * dd.y;
+      nm.z = alpha * m[p].z + bk * dd.z;
+      nm.w = alpha * m[p].w + bk * dd.w;
+    }
     if (commit) {
       T* cdst = cache_out + r * W + col;
       cdst[0] = from_f<T>(nm.x); cdst[1] = from_f<T>(nm.y); cdst[2] = from_f<T>(nm.z); cdst[3] = from_f<T>(nm.w);
@@ -95,7 +117,7 @@ __device__ __forceinline__ void live_pass(float* mat, T* cache_out, bool commit,
 #ifndef HLA_DECODE_NT
 #define HLA_DECODE_NT 512
 #endif
-template <class T, int DK, int DV, int NT, int WPC>
+template <class T, int DK, int DV, int NT, int WPC, bool G2>
 __global__ __launch_bounds__(NT, WPC) void decode_kernel(DecodeArgs a) {
   constexpr int E = sizeof(T), PAD = 16 / E;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -119,6 +141,19 @@ __global__ __launch_bounds__(NT, WPC) void decode_kernel(DecodeArgs a) {
     s_k[tid] = to_f<T>(kg[tid]);
   }
   if (tid < DV) s_v[tid] = to_f<T>(vg[tid]);
+  // Gated DeltaNet-2 rows: ka = k o a, qa = q o a, a, e = b o k; s_v becomes w o v
+  __shared__ float s_ka[G2 ? DK : 1], s_qa[G2 ? DK : 1], s_a[G2 ? DK : 1], s_e[G2 ? DK : 1];
+  __shared__ float s_qe;
+  if constexpr (G2) {
+    if (tid < DK) {
+      const float av = a.ga[bh * DK + tid], kv = s_k[tid];
+      s_a[tid] = av;
+      s_ka[tid] = kv * av;
+      s_qa[tid] = s_q[tid] * av;
+      s_e[tid] = a.gb[bh * DK + tid] * kv;
+    }
+    if (tid < DV) s_v[tid] *= a.gw[bh * DV + tid];
+  }
   if (tid == 0) {
     int nc = 0;
     if (a.At_cur) {
@@ -134,7 +169,15 @@ __global__ __launch_bounds__(NT, WPC) void decode_kernel(DecodeArgs a) {
     x = wave_sum(x);
     if (lane == 0) s_qk = x;
   }
-  const float alpha = a.alpha[bh], beta = a.beta[bh];
+  if constexpr (G2) {
+    if (w == 1) {
+      float x = 0.f;
+      for (int i = lane; i < DK; i += 64) x += s_q[i] * s_e[i];
+      x = wave_sum(x);
+      if (lane == 0) s_qe = x;
+    }
+  }
+  const float alpha = G2 ? 0.f : a.alpha[bh], beta = G2 ? 0.f : a.beta[bh];
   const int nc = s_nc;
   const bool commit = a.commit && a.At_cur && nc < a.n_cap;
   __syncthreads();
@@ -142,16 +185,17 @@ __global__ __launch_bounds__(NT, WPC) void decode_kernel(DecodeArgs a) {
   T* Acache = reinterpret_cast<T*>(a.At_cache);
   T* Bcache = reinterpret_cast<T*>(a.Bc_cache);
   const int64_t slot = bh * a.n_cap + nc;
-  live_pass<T, DK, DV, true, NT>(a.S_cur + bh * (int64_t)DK * DV, commit ? Bcache + slot * DK * DV : nullptr, commit,
-                            alpha, beta, s_qk, s_q, s_k, s_v, &s_red[0][0][0], &s_red[1][0][0], RMAX * WMAX, s_u,
-                            s_o);
+  const G2Rows g2{s_ka, s_qa, s_a, s_e, G2 ? s_qe : 0.f};
+  live_pass<T, DK, DV, true, NT, G2>(a.S_cur + bh * (int64_t)DK * DV, commit ? Bcache + slot * DK * DV : nullptr,
+                                     commit, alpha, beta, s_qk, s_q, s_k, s_v, &s_red[0][0][0], &s_red[1][0][0],
+                                     RMAX * WMAX, s_u, s_o, g2);
   if (!a.At_cur) {
     if (tid < DV) a.o[bh * DV + tid] = s_o[tid];
     return;
   }
-  live_pass<T, DK, DK, false, NT>(a.At_cur + bh * (int64_t)DK * DK, commit ? Acache + slot * DK * DK : nullptr, commit,
-                              alpha, beta, s_qk, s_q, s_k, s_v, &s_red[0][0][0], &s_red[1][0][0], RMAX * WMAX,
-                              s_u, s_y);
+  live_pass<T, DK, DK, false, NT, G2>(a.At_cur + bh * (int64_t)DK * DK, commit ? Acache + slot * DK * DK : nullptr,
+                                      commit, alpha, beta, s_qk, s_q, s_k, s_v, &s_red[0][0][0], &s_red[1][0][0],
+                                      RMAX * WMAX, s_u, s_y, g2);
 
   // ---- gates over the cached chunks (wave w takes chunks j = w, w + 4, ...)
   __shared__ float s_g[kMaxCache];
@@ -306,8 +350,12 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   if (nb == 0) return hipSuccess;
   {
     TimedLaunch tl(HLA_KERNEL_DECODE, s);
-    hipLaunchKernelGGL((decode_kernel<T, DK, DV, HLA_DECODE_NT, HLA_DECODE_WGS_PER_CU>), dim3((unsigned)nb),
-                       dim3(HLA_DECODE_NT), 0, s, a);
+    if (a.variant == 2)
+      hipLaunchKernelGGL((decode_kernel<T, DK, DV, HLA_DECODE_NT, HLA_DECODE_WGS_PER_CU, true>), dim3((unsigned)nb),
+                         dim3(HLA_DECODE_NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<T, DK, DV, HLA_DECODE_NT, HLA_DECODE_WGS_PER_CU, false>), dim3((unsigned)nb),
+                         dim3(HLA_DECODE_NT), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(a.commit && a.At_cur)) return e;

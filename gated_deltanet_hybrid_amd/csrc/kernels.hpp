@@ -107,6 +107,11 @@ struct DecodeArgs {
   float* gates_out;
   int32_t commit;
   int64_t Bs, H;
+  // Gated DeltaNet-2 (variant 2): ga, gb [Bs,H,dk] and gw [Bs,H,dv] replace alpha and beta
+  const float* ga;
+  const float* gb;
+  const float* gw;
+  int32_t variant;
 };
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int dk, int dv, hipStream_t s);
 

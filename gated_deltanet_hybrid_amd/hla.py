@@ -57,6 +57,9 @@ _SIGS = {
     "hla_gdn_decode": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
                                         ctypes.c_int32, _P, ctypes.c_float, _P, _P, ctypes.c_int32, _P]),
+    "hla_gdn2_decode": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                         _P, ctypes.c_int32, _P, ctypes.c_float, _P, _P, ctypes.c_int32, _P]),
 }
 
 
@@ -365,13 +368,33 @@ def gdn_decode(q, k, v, beta, alpha, S_cur, At_cur=None, At_cache=None, Bc_cache
                n_cache=None, gates_in=None, tau=1e-3, o=None, gates_out=None, commit=False):
     """One decode step.  q, k [Bs, H, dk], v [Bs, H, dv]; S_cur/At_cur are updated in place."""
     Bs, H, dk = k.shape
+    _need(beta, (Bs, H), torch.float32, "beta")
+    _need(alpha, (Bs, H), torch.float32, "alpha")
+    return _decode("hla_gdn_decode", (beta, alpha), q, k, v, S_cur, At_cur, At_cache, Bc_cache, reps_cache, n_cache,
+                   gates_in, tau, o, gates_out, commit)
+
+
+def gdn2_decode(q, k, v, a_decay, b_erase, w_write, S_cur, At_cur=None, At_cache=None, Bc_cache=None,
+                reps_cache=None, n_cache=None, gates_in=None, tau=1e-3, o=None, gates_out=None, commit=False):
+    """One decode step under the Gated DeltaNet-2 recurrence: a_decay, b_erase [Bs, H, dk]
+    and w_write [Bs, H, dv] (float32) replace beta and alpha."""
+    Bs, H, dk = k.shape
+    dv = v.shape[-1]
+    _need(a_decay, (Bs, H, dk), torch.float32, "a_decay")
+    _need(b_erase, (Bs, H, dk), torch.float32, "b_erase")
+    _need(w_write, (Bs, H, dv), torch.float32, "w_write")
+    return _decode("hla_gdn2_decode", (a_decay, b_erase, w_write), q, k, v, S_cur, At_cur, At_cache, Bc_cache,
+                   reps_cache, n_cache, gates_in, tau, o, gates_out, commit)
+
+
+def _decode(fn, gates, q, k, v, S_cur, At_cur, At_cache, Bc_cache, reps_cache, n_cache, gates_in, tau, o, gates_out,
+            commit):
+    Bs, H, dk = k.shape
     dv = v.shape[-1]
     dt = _dtype_code(k)
     dev = k.device
     _need(q, (Bs, H, dk), k.dtype, "q")
     _need(v, (Bs, H, dv), k.dtype, "v")
-    _need(beta, (Bs, H), torch.float32, "beta")
-    _need(alpha, (Bs, H), torch.float32, "alpha")
     _need(S_cur, (Bs, H, dk, dv), torch.float32, "S_cur")
     n_cap, n_rep = 0, 0
     if At_cur is not None:
@@ -388,10 +411,10 @@ def gdn_decode(q, k, v, beta, alpha, S_cur, At_cur=None, At_cache=None, Bc_cache
     if o is None:
         o = torch.empty((Bs, H, dv), dtype=torch.float32, device=dev)
     _need(o, (Bs, H, dv), torch.float32, "o")
-    _check(library().hla_gdn_decode(Bs, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
-                                    _ptr(S_cur), _ptr(At_cur), _ptr(At_cache), _ptr(Bc_cache), _ptr(reps_cache),
-                                    n_rep, _ptr(n_cache), n_cap, _ptr(gates_in), ctypes.c_float(tau), _ptr(o),
-                                    _ptr(gates_out), 1 if commit else 0, _stream(dev)), "hla_gdn_decode")
+    _check(getattr(library(), fn)(Bs, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), *(_ptr(g) for g in gates),
+                                  _ptr(S_cur), _ptr(At_cur), _ptr(At_cache), _ptr(Bc_cache), _ptr(reps_cache), n_rep,
+                                  _ptr(n_cache), n_cap, _ptr(gates_in), ctypes.c_float(tau), _ptr(o),
+                                  _ptr(gates_out), 1 if commit else 0, _stream(dev)), fn)
     return o
 
 

@@ -199,6 +199,18 @@ def gen_decode_tokens(Bs, H, dk, dv, step, dtype="bf16", seed=0, stream=7, alpha
                 alpha=np.exp(-_softplus(xa + shift)).astype(np.float32))
 
 
+def gen_gdn2_decode_gates(Bs, H, dk, dv, step, seed=0, stream=7, alpha_mode="config") -> dict:
+    """Gated DeltaNet-2 gates of one decode token per sequence: a, b [Bs, H, dk] and
+    w [Bs, H, dv], float32, with the distributions of gen_gdn2_gates."""
+    rng = np.random.default_rng([seed, stream, 101, int(step)])
+    shift = -3.0 if alpha_mode == "slow" else 2.0
+    xa = rng.standard_normal((Bs, H, dk), dtype=np.float32).astype(np.float64)
+    xb = rng.standard_normal((Bs, H, dk), dtype=np.float32).astype(np.float64)
+    xw = rng.standard_normal((Bs, H, dv), dtype=np.float32).astype(np.float64)
+    return dict(a=np.exp(-_softplus(xa + shift)).astype(np.float32), b=_sigmoid(xb).astype(np.float32),
+                w=_sigmoid(xw).astype(np.float32))
+
+
 def gen_gates(B, H, N, seed=0, stream=0, mode="skip_heavy") -> np.ndarray:
     """Caller-supplied gates [B, H, N, N] float32 (only entries j < i are read)."""
     rng = _rng(seed, stream, "gates", B, H, N)

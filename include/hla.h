@@ -272,6 +272,22 @@ hla_status_t hla_gdn_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32
                             int32_t* n_cache, int32_t n_cap, const float* gates_in, float tau,
                             float* o, float* gates_out, int32_t commit, hipStream_t stream);
 
+/*
+ * hla_gdn2_decode -- hla_gdn_decode for the Gated DeltaNet-2 recurrence ([GDN2] abstract):
+ * a_decay, b_erase [Bs, H, dk] and w_write [Bs, H, dv] (float32, 4-byte aligned) replace
+ * beta and alpha; the live chunk takes the token as in hla_gdn2_prefill,
+ *     S_cur <- S_cur diag(a) (I - k (b o k)^T) + (w o v) k^T,   A_cur likewise with no write,
+ * and the gates, the routed read over the cache and commit are hla_gdn_decode's.  Every
+ * other argument and error is as for hla_gdn_decode.
+ */
+hla_status_t hla_gdn2_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int32_t dtype,
+                             const void* q, const void* k, const void* v, const float* a_decay,
+                             const float* b_erase, const float* w_write, float* S_cur,
+                             float* At_cur, void* At_cache, void* Bc_cache, const void* reps_cache,
+                             int32_t n_rep, int32_t* n_cache, int32_t n_cap, const float* gates_in,
+                             float tau, float* o, float* gates_out, int32_t commit,
+                             hipStream_t stream);
+
 /* Workspace bytes that entry point `fn` needs for dims `d`; n_rep is the number of
  * representatives per chunk for HLA_FN_CHUNK_REPS (C / window; it must divide C) and is
  * ignored otherwise.  `out` is a host pointer. */

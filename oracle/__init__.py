@@ -48,4 +48,5 @@ from .gdn2 import (  # noqa: F401
     gdn2_chunk_transitions,
     gdn2_routed_outputs,
     gdn2_hla_prefill,
+    gdn2_decode_step,
 )

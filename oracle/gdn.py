@@ -256,10 +256,16 @@ def decode_step(q, k, v, beta, alpha, B_cur, A_cur, cache_A, cache_B, cache_reps
     """
     dk = k.shape[0]
     lin = alpha * (np.eye(dk) - beta * np.outer(k, k))
-    B_cur = B_cur @ lin + beta * np.outer(v, k)
+    return decode_read(q, B_cur @ lin + beta * np.outer(v, k), None if A_cur is None else A_cur @ lin,
+                       cache_A, cache_B, cache_reps, tau, gates_in=gates_in, commit=commit, Wr=Wr)
+
+
+def decode_read(q, B_cur, A_cur, cache_A, cache_B, cache_reps, tau, gates_in=None, commit=False, Wr=None):
+    """The decode step after the live chunk (A_cur, B_cur) has taken the token: gates over
+    the cached chunks, the routed state and the output (see decode_step)."""
+    dk = q.shape[0]
     if A_cur is None:
         return dict(o=B_cur @ q, B_cur=B_cur, A_cur=None)
-    A_cur = A_cur @ lin
     Nc = cache_A.shape[0]
     g = np.zeros(Nc)
     qr = q if Wr is None else Wr @ q

@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .gdn import chunk_bounds, routed_states, router_gates
+from .gdn import chunk_bounds, decode_read, routed_states, router_gates
 
 
 def gdn2_recurrent(q, k, v, alpha, b, w, S0=None):
@@ -77,3 +77,13 @@ def gdn2_hla_prefill(q, k, v, alpha, b, w, C, tau, reps=None, n_rep=None, gates_
     S = routed_states(A, B, r["ghat"], r["mask"], S0=S0)
     o = gdn2_routed_outputs(q, k, v, alpha, b, w, C, S)
     return dict(A=A, B=B, S_routed=S, o=o, **r)
+
+
+def gdn2_decode_step(q, k, v, alpha, b, w, B_cur, A_cur, cache_A, cache_B, cache_reps, tau, gates_in=None,
+                     commit=False, Wr=None):
+    """One decode step under the GDN-2 recurrence: the live chunk takes the token,
+    B_cur <- B_cur diag(alpha)(I - k (b o k)^T) + (w o v) k^T and A_cur likewise without the
+    write; the routed read over the cached chunks is HLA's (decode_step)."""
+    lin = np.diag(alpha) @ (np.eye(k.shape[0]) - np.outer(k, b * k))
+    return decode_read(q, B_cur @ lin + np.outer(w * v, k), None if A_cur is None else A_cur @ lin,
+                       cache_A, cache_B, cache_reps, tau, gates_in=gates_in, commit=commit, Wr=Wr)

@@ -174,3 +174,91 @@ def test_gdn2_full_size_sampled_transitions():
                                              g["w"][0, s, h].astype(np.float64))
         assert_close(host(At[0, h, c]), A.T, W.dtype, f"At h{h} c{c}")
         assert_close(host(Bc[0, h, c]), Bm.T, W.dtype, f"Bc h{h} c{c}")
+
+
+def _tok(t, x, g, dtype):
+    """Token t of every (sequence, head) as decode inputs."""
+    q, k, v = (dev(np.ascontiguousarray(getattr(x, n)[:, t]), dtype) for n in ("q", "k", "v"))
+    return q, k, v, f32(g["a"][:, t]), f32(g["b"][:, t]), f32(g["w"][:, t])
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2]], ids=[IDS[0], IDS[2]])
+def test_gdn2_decode_native_equals_recurrence(case):
+    note(f"gdn2 decode native {case}")
+    dtype, dk, dv = case[:3]
+    Bs, H, T = 2, 2, 40
+    x, g = gen((dtype, dk, dv, T), B=Bs, H=H, seed=90)
+    S0 = inputs.gen_state(Bs, H, dk, dv, seed=91)
+    S = f32(S0)
+    outs = []
+    for t in range(T):
+        outs.append(host(hla().gdn2_decode(*_tok(t, x, g, dtype), S)))
+    torch.cuda.synchronize()
+    for b in range(Bs):
+        for h in range(H):
+            o_ref, S_ref = oracle.gdn2_recurrent(*seq(x, g, b, h), S0=S0[b, h].T.astype(np.float64))
+            assert_close(np.stack([o[b, h] for o in outs]), o_ref, dtype, "decode o")
+            assert_close(host(S)[b, h], S_ref.T, dtype, "decode state")
+
+
+def test_gdn2_decode_routed_with_commits_equals_routed_prefill():
+    # token-by-token decode, committing every C tokens, with the prefill gate rows as caller
+    # gates, reproduces the routed prefill outputs
+    dtype, dk, dv = "bf16", 128, 128
+    note("gdn2 decode routed commits")
+    Bs, H, N = 2, 2, 3
+    T = N * C
+    x, g = gen((dtype, dk, dv, T), B=Bs, H=H, seed=92)
+    G = inputs.gen_gates(Bs, H, N, seed=93, mode="uniform")
+    tau = 0.2
+    S = torch.zeros((Bs, H, dk, dv), dtype=torch.float32, device="cuda")
+    A = torch.eye(dk, dtype=torch.float32, device="cuda").repeat(Bs, H, 1, 1).contiguous()
+    Ac = torch.zeros((Bs, H, N, dk, dk), dtype=torch.bfloat16, device="cuda")
+    Bcc = torch.zeros((Bs, H, N, dk, dv), dtype=torch.bfloat16, device="cuda")
+    nc = torch.zeros((Bs,), dtype=torch.int32, device="cuda")
+    outs = []
+    for t in range(T):
+        i = t // C
+        gin = np.zeros((Bs, H, N), np.float32)
+        gin[:, :, :i] = G[:, :, i, :i]
+        o = hla().gdn2_decode(*_tok(t, x, g, dtype), S, At_cur=A, At_cache=Ac, Bc_cache=Bcc, n_cache=nc,
+                              gates_in=f32(gin), tau=tau, commit=(t % C == C - 1))
+        outs.append(host(o))
+    torch.cuda.synchronize()
+    assert host(nc).tolist() == [N] * Bs
+    got = np.stack(outs, axis=2)  # [Bs, H, T, dv]
+    for b in range(Bs):
+        for h in range(H):
+            ref = oracle.gdn2_hla_prefill(*seq(x, g, b, h), C, tau, gates_in=G[b, h].astype(np.float64))
+            assert_close(got[b, h], ref["o"], dtype, "decode routed o")
+
+
+def test_gdn2_decode_computed_gates():
+    dtype, dk, dv = "bf16", 128, 64
+    note("gdn2 decode computed gates")
+    Bs, H, n_cap, n_rep = 3, 2, 5, 64
+    At_s, Bc_s = inputs.gen_transitions(Bs, H, n_cap, dk, dv, dtype=dtype, seed=94)
+    reps_x = inputs.gen_tokens(Bs, n_cap * n_rep, H, dk, dk, dtype=dtype, seed=95)
+    reps = reps_x.k.reshape(Bs, n_cap, n_rep, H, dk).transpose(0, 3, 1, 2, 4).copy()
+    x, g = gen((dtype, dk, dv, 1), B=Bs, H=H, seed=96)
+    S0 = inputs.gen_state(Bs, H, dk, dv, seed=97)
+    A0 = (np.eye(dk)[None, None] + 0.05 * inputs.gen_state(Bs, H, dk, dk, seed=98)).astype(np.float32)
+    n_cache = np.array([5, 2, 0], np.int32)
+    S, A, nc = f32(S0), f32(A0), torch.from_numpy(n_cache).cuda()
+    go = torch.empty((Bs, H, n_cap), dtype=torch.float32, device="cuda")
+    o = hla().gdn2_decode(*_tok(0, x, g, dtype), S, At_cur=A, At_cache=dev(At_s, dtype), Bc_cache=dev(Bc_s, dtype),
+                          reps_cache=dev(reps, dtype), n_cache=nc, tau=0.3, gates_out=go)
+    torch.cuda.synchronize()
+    Am = inputs.to_f64(At_s, dtype).transpose(0, 1, 2, 4, 3)
+    Bm = inputs.to_f64(Bc_s, dtype).transpose(0, 1, 2, 4, 3)
+    R = inputs.to_f64(reps, dtype)
+    for b in range(Bs):
+        for h in range(H):
+            ncb = n_cache[b]
+            qv, kv, vv, av, bv, wv = (arr[0] for arr in seq(x, g, b, h))
+            r = oracle.gdn2_decode_step(qv, kv, vv, av, bv, wv, S0[b, h].astype(np.float64).T,
+                                        A0[b, h].astype(np.float64).T, Am[b, h, :ncb], Bm[b, h, :ncb], R[b, h, :ncb], 0.3)
+            assert_close(host(o)[b, h], r["o"], dtype, f"o b{b} h{h}")
+            np.testing.assert_allclose(host(go)[b, h, :ncb], r["gates"], atol=2e-5)
+            assert_close(host(S)[b, h], r["B_cur"].T, dtype, "live state")
+            assert_close(host(A)[b, h], r["A_cur"].T, dtype, "live transition")

@@ -129,3 +129,25 @@ def test_routed_prefill_with_all_gates_one_is_the_recurrence():
     r = oracle.gdn2_hla_prefill(q, k, v, alpha, b, w, C, 0.5, gates_in=np.ones((N, N)))
     o_ref, _ = oracle.gdn2_recurrent(q, k, v, alpha, b, w)
     np.testing.assert_allclose(r["o"], o_ref, rtol=1e-11, atol=1e-12)
+
+
+def test_decode_step_collapses_and_follows_the_recurrence():
+    rng = np.random.default_rng(8)
+    dk, dv, Nc = 6, 4, 3
+    q, k, v, alpha, b, w = _seq(rng, 1, dk, dv)
+    B0 = rng.standard_normal((dv, dk))
+    A0 = np.eye(dk) + 0.1 * rng.standard_normal((dk, dk))
+    cA, cB = 0.5 * rng.standard_normal((Nc, dk, dk)), rng.standard_normal((Nc, dv, dk))
+    reps = rng.standard_normal((Nc, 2, dk))
+    # native: the live state follows the token recurrence
+    r = oracle.gdn2_decode_step(q[0], k[0], v[0], alpha[0], b[0], w[0], B0, None, None, None, None, 0.0)
+    o_ref, S_ref = oracle.gdn2_recurrent(q, k, v, alpha, b, w, S0=B0)
+    np.testing.assert_allclose(r["B_cur"], S_ref, rtol=1e-13)
+    np.testing.assert_allclose(r["o"], o_ref[0], rtol=1e-13)
+    # collapsed gates: Gated DeltaNet's decode step, routed read included
+    be, al = 0.6, 0.8
+    r2 = oracle.gdn2_decode_step(q[0], k[0], v[0], np.full(dk, al), np.full(dk, be), np.full(dv, be), B0, A0,
+                                 cA, cB, reps, 0.3)
+    r1 = oracle.decode_step(q[0], k[0], v[0], be, al, B0, A0, cA, cB, reps, 0.3)
+    for key in ("o", "B_cur", "A_cur", "gates"):
+        np.testing.assert_allclose(r2[key], r1[key], rtol=1e-12, atol=1e-14)
