@@ -127,9 +127,7 @@ def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None
     tau = W.tau if tau is None else tau
     N = math.ceil(W.T / Cw)
     if x is None:
-        log(f"[{tag}] generating inputs B={W.B} T={W.T} H={W.H} d={W.dk}")
-        x = inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=0,
-                              stream=inputs.STREAM["routed_prefill"], plant_period=W.plant_period)
+        x = routed_inputs(inputs)
     q, k, v = (to_dev(a, W.dtype, torch) for a in (x.q, x.k, x.v))
     beta, alpha = to_dev(x.beta, "f32", torch), to_dev(x.alpha, "f32", torch)
     dev = k.device
@@ -216,35 +214,63 @@ def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None
     return res, x
 
 
-def bench_routed_variants(args, torch, hla, inputs, x):
-    """Secondary routed-prefill lines: the pages' default chunk size (C = 256), C = 64 with
-    skip-heavy caller gates at tau = 0.1 (how skipping cuts the composition), and C = 64
-    with learned window representatives."""
+def _sub(args):
+    return argparse.Namespace(steps=max(3, args.steps // 2), warmup=1)
+
+
+def bench_routed_c256(args, torch, hla, inputs, x):
+    """The pages' default chunk size, C = 256 (64-token pieces composed four at a time)."""
     W = inputs.WORKLOADS["routed_prefill"]
-    sub = argparse.Namespace(steps=max(3, args.steps // 2), warmup=1)
-    out = {}
-    r, _ = bench_routed_prefill(sub, torch, hla, inputs, Cw=256, x=x, tag="routed_prefill_C256")
-    out["routed_prefill_C256"] = dict(workload="routed_prefill C=256", C=256, tau=W.tau,
-                                      ms_per_step=r["ms_per_step"], tokens_per_s=r["value"],
-                                      mfma_util_pct=r["mfma_util_pct"], active_pairs=r["active_pairs"],
-                                      compose_ms=r["roofline"]["avg_launch_ms"])
+    r, _ = bench_routed_prefill(_sub(args), torch, hla, inputs, Cw=256, x=x, tag="routed_prefill_C256")
+    return dict(workload="routed_prefill C=256", C=256, tau=W.tau, ms_per_step=r["ms_per_step"],
+                tokens_per_s=r["value"], mfma_util_pct=r["mfma_util_pct"], active_pairs=r["active_pairs"],
+                compose_ms=r["roofline"]["avg_launch_ms"])
+
+
+def bench_routed_skip(args, torch, hla, inputs, x):
+    """C = 64 with skip-heavy caller gates at tau = 0.1: how skipping cuts the composition."""
+    W = inputs.WORKLOADS["routed_prefill"]
     N = math.ceil(W.T / C)
     G = inputs.gen_gates(W.B, W.H, N, seed=0, stream=inputs.STREAM["routed_prefill"], mode="skip_heavy")
-    r, _ = bench_routed_prefill(sub, torch, hla, inputs, Cw=C, gates_in=G, tau=0.1, x=x, tag="routed_prefill_skip")
+    r, _ = bench_routed_prefill(_sub(args), torch, hla, inputs, Cw=C, gates_in=G, tau=0.1, x=x,
+                                tag="routed_prefill_skip")
     dense_pairs = W.B * W.H * N * (N - 1) // 2
-    out["routed_prefill_skip"] = dict(workload="routed_prefill C=64, caller gates sigmoid(N(-4, 3)), tau=0.1",
-                                      C=C, tau=0.1, ms_per_step=r["ms_per_step"], tokens_per_s=r["value"],
-                                      active_pairs=r["active_pairs"], active_frac=r["active_pairs"] / dense_pairs,
-                                      compose_ms=r["roofline"]["avg_launch_ms"],
-                                      compose_tflops_active=r["roofline"]["achieved"])
+    return dict(workload="routed_prefill C=64, caller gates sigmoid(N(-4, 3)), tau=0.1",
+                C=C, tau=0.1, ms_per_step=r["ms_per_step"], tokens_per_s=r["value"],
+                active_pairs=r["active_pairs"], active_frac=r["active_pairs"] / dense_pairs,
+                compose_ms=r["roofline"]["avg_launch_ms"], compose_tflops_active=r["roofline"]["achieved"])
+
+
+def bench_routed_learned_reps(args, torch, hla, inputs, x):
+    """C = 64 with learned window representatives (window 32, seeded weights)."""
+    W = inputs.WORKLOADS["routed_prefill"]
     pooler = inputs.gen_pooler_weights(W.H, W.dk, dtype=W.dtype, seed=0, stream=inputs.STREAM["routed_prefill"])
-    r, _ = bench_routed_prefill(sub, torch, hla, inputs, Cw=C, x=x, tag="routed_prefill_learned_reps", pooler=pooler,
-                                window=32)
-    out["routed_prefill_learned_reps"] = dict(
+    r, _ = bench_routed_prefill(_sub(args), torch, hla, inputs, Cw=C, x=x, tag="routed_prefill_learned_reps",
+                                pooler=pooler, window=32)
+    return dict(
         workload="routed_prefill C=64, learned representatives (window 32, 2 per chunk), seeded weights",
         C=C, tau=W.tau, ms_per_step=r["ms_per_step"], tokens_per_s=r["value"], mfma_util_pct=r["mfma_util_pct"],
         active_pairs=r["active_pairs"], kernel_ms=r["kernel_ms"], reps_pool=r["reps_pool"])
-    return out
+
+
+def routed_inputs(inputs):
+    W = inputs.WORKLOADS["routed_prefill"]
+    log(f"[routed_prefill] generating inputs B={W.B} T={W.T} H={W.H} d={W.dk}")
+    return inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["routed_prefill"],
+                             plant_period=W.plant_period)
+
+
+# secondary lines, in the order the default run measures them; each takes the routed inputs
+SECONDARY = {
+    "routed_prefill_C256": bench_routed_c256,
+    "routed_prefill_skip": bench_routed_skip,
+    "routed_prefill_learned_reps": bench_routed_learned_reps,
+    "gdn2_routed_prefill": lambda args, torch, hla, inputs, x: bench_gdn2_routed(args, torch, hla, inputs, x),
+    "decode": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs),
+    "gdn2_decode": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs, gdn2=True),
+    "native_prefill": lambda args, torch, hla, inputs, x: bench_native_prefill(args, torch, hla, inputs),
+    "tail_replay": lambda args, torch, hla, inputs, x: bench_tail_replay(args, torch, hla, inputs),
+}
 
 
 # ----------------------------------------------------------------------------- decode
@@ -563,6 +589,9 @@ def main():
     ap.add_argument("--traffic-run", action="store_true", help="one routed-prefill step plus a calibration copy (under rocprofv3 --pmc)")
     ap.add_argument("--traffic-write", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from the two counter passes")
+    ap.add_argument("--only", metavar="LINES",
+                    help="profiling aid: run only these comma-separated lines (routed_prefill or a secondary "
+                         "name) and print their results as one JSON object instead of the bench line")
     args = ap.parse_args()
     if args.traffic_write:
         traffic_write(*args.traffic_write)
@@ -584,15 +613,25 @@ def main():
         traffic_run(torch, hla, inputs)
         return
 
+    if args.only:
+        names = args.only.split(",")
+        unknown = [n for n in names if n != "routed_prefill" and n not in SECONDARY]
+        if unknown:
+            print(f"unknown lines {unknown}; known: routed_prefill, {', '.join(SECONDARY)}", file=sys.stderr)
+            sys.exit(2)
+        x = routed_inputs(inputs) if any(n.startswith(("routed", "gdn2_routed")) for n in names) else None
+        out = {}
+        for n in names:
+            out[n] = bench_routed_prefill(args, torch, hla, inputs, x=x)[0] if n == "routed_prefill" else \
+                SECONDARY[n](args, torch, hla, inputs, x)
+        print(json.dumps(out), flush=True)
+        return
+
     head, x = bench_routed_prefill(args, torch, hla, inputs)
     secondary = {}
     if not args.no_secondary:
-        secondary.update(bench_routed_variants(args, torch, hla, inputs, x))
-        secondary["gdn2_routed_prefill"] = bench_gdn2_routed(args, torch, hla, inputs, x)
-        secondary["decode"] = bench_decode(args, torch, hla, inputs)
-        secondary["gdn2_decode"] = bench_decode(args, torch, hla, inputs, gdn2=True)
-        secondary["native_prefill"] = bench_native_prefill(args, torch, hla, inputs)
-        secondary["tail_replay"] = bench_tail_replay(args, torch, hla, inputs)
+        for name, fn in SECONDARY.items():
+            secondary[name] = fn(args, torch, hla, inputs, x)
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[cpu_baseline] oracle on {args.oracle_chunks} chunks of one head")
