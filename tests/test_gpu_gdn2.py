@@ -138,6 +138,20 @@ def test_gdn2_tail_replay_state_only():
             assert_close(host(S)[b, h], S_ref.T, dtype, "replayed state")
 
 
+def test_gdn2_native_prefill_many_pieces():
+    # 21 pieces scanned in order from the GDN-2 piece maps
+    dtype, dk, dv, T = "bf16", 128, 128, 20 * C + 3
+    note("gdn2 native many pieces")
+    x, g = gen((dtype, dk, dv, T), B=1, seed=99)
+    q, k, v, _, _ = token_tensors(x)
+    o, S = hla().gdn2_prefill(q, k, v, *gates_dev(g))
+    torch.cuda.synchronize()
+    for h in range(2):
+        o_ref, S_ref = oracle.gdn2_recurrent(*seq(x, g, 0, h))
+        assert_close(host(o)[0, :, h], o_ref, dtype, f"o h{h}")
+        assert_close(host(S)[0, h], S_ref.T, dtype, f"S h{h}")
+
+
 def test_gdn2_collapsed_gates_match_gdn():
     # b = w = beta and a = alpha broadcast: both GPU paths compute the same Gated DeltaNet
     dtype, dk, dv, T = "f32", 64, 64, 150

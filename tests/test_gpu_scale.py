@@ -147,6 +147,26 @@ def test_routed_prefill_full_size_sampled():
             assert_close(host(o[0, s:e, hh]), o_i, W.dtype, f"o h{hh} chunk {i}")
 
 
+@pytest.mark.parametrize("T,with_s0", [(16 * C + 37, True), (40 * C - 5, False)])
+def test_native_prefill_many_pieces(T, with_s0):
+    """17 and 40 pieces of 64 tokens (ragged last piece), outputs and final state, and the
+    state-only call.  Slow decay, so each piece's start state carries its history."""
+    dtype, dk, dv, B, H = "bf16", 128, 64, 1, 2
+    note(f"native prefill T={T} S0={with_s0}")
+    x = inputs.gen_tokens(B, T, H, dk, dv, dtype=dtype, seed=101, alpha_mode="slow")
+    q, k, v, beta, alpha = token_tensors(x)
+    S0 = inputs.gen_state(B, H, dk, dv, seed=102) if with_s0 else None
+    h = hla()
+    o, S = h.gdn_prefill(q, k, v, beta, alpha, S0=None if S0 is None else f32(S0))
+    _, S_only = h.gdn_prefill(None, k, v, beta, alpha, S0=None if S0 is None else f32(S0), want_o=False)
+    torch.cuda.synchronize()
+    for hh in range(H):
+        o_ref, S_ref = oracle.gdn_recurrent(*seq(x, 0, hh), S0=None if S0 is None else S0[0, hh].T.astype(np.float64))
+        assert_close(host(o[0, :, hh]), o_ref, dtype, f"o h{hh}")
+        assert_close(host(S[0, hh]), S_ref.T, dtype, f"S_final h{hh}")
+        assert_close(host(S_only[0, hh]), S_ref.T, dtype, f"state-only S_final h{hh}")
+
+
 def test_native_prefill_full_size_sampled():
     """B=4, H=16, T=4096, d=128, bf16: the benchmark's call, then outputs and final state
     of (b, h) in {(0, 0), (2, 9), (3, 15)} against the sequential recurrence."""
