@@ -12,30 +12,46 @@
 // and takes no write, Q starts at 0.  [HLA] Methodology paragraph 1: the chunk is one
 // exact affine map, which the HLA router and composition consume unchanged.
 //
-// Layout: one workgroup per (b, h, 64-token piece).  A thread holds 4 columns over a
-// quarter of the rows (4 x dk/4 floats); the 4 threads of a column group are adjacent
+// Layout: one workgroup per (b, h, 64-token piece).  A thread holds 2 columns over a
+// quarter of the rows (2 x dk/4 floats); the 4 threads of a column group are adjacent
 // lanes, so the read k . D x is a sum over the thread's rows plus two lane exchanges.
-// Token vectors (k o alpha, alpha, e, k, u, and q for outputs) are staged 16 tokens at a
+// Token vectors (k o alpha, alpha, e, k, u, and q for outputs) are staged 8 tokens at a
 // time in LDS and read as broadcasts.  The work is float32 VALU: per token and column
-// about 4 dk fused multiply-adds (5 dk with the output read).
+// about 4 dk fused multiply-adds (5 dk with the output read).  The layout was chosen by
+// timing: 2 columns x 4 row groups x 8 staged tokens ran the routed step's two passes at
+// 3.6 ms against 5.3 ms for 4 x 4 x 16 (more waves in flight, smaller LDS).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
 
 namespace hla {
 
+#ifndef HLA_GDN2_SHAPE
+#define HLA_GDN2_SHAPE 2, 4, 8  // columns per thread, row groups, tokens per staged block
+#endif
 namespace {
-constexpr int kTB = 16;  // tokens per staged block
+template <int CPT_, int RQ_, int TB_>
+struct G2Shape {
+  static constexpr int CPT = CPT_, RQ = RQ_, TB = TB_;
+};
+using G2 = G2Shape<HLA_GDN2_SHAPE>;
+constexpr int kTB = G2::TB;
+}
+
+// threads of one workgroup: one per (group of CPT columns, row group)
+template <int DK, int DV, bool OUT>
+constexpr int gdn2_threads() {
+  return (OUT ? DV : DK + DV) / G2::CPT * G2::RQ;
 }
 
 template <class T, int DK, int DV, bool OUT>
-__global__ __launch_bounds__(256) void gdn2_chunk_kernel(ChunkArgs a) {
+__global__ __launch_bounds__((gdn2_threads<DK, DV, OUT>())) void gdn2_chunk_kernel(ChunkArgs a) {
   constexpr int C = kChunk;
   constexpr int NCOL = OUT ? DV : DK + DV;
-  constexpr int CPT = 4, RQ = 4, RPT = DK / RQ;
+  constexpr int CPT = G2::CPT, RQ = G2::RQ, RPT = DK / RQ;
   constexpr int NT = NCOL / CPT * RQ;
-  constexpr int PR = DK + 4;  // LDS row pitch: the 4 row quarters start on different banks
-  static_assert(NT <= 256, "one thread per (column group, row quarter)");
+  constexpr int PR = DK + 4;  // LDS row pitch
+  static_assert(NT <= 1024 && RPT % 4 == 0 && (RQ & (RQ - 1)) == 0, "thread layout");
   __shared__ __attribute__((aligned(16))) float s_ka[kTB][PR];
   __shared__ __attribute__((aligned(16))) float s_al[kTB][PR];
   __shared__ __attribute__((aligned(16))) float s_e[kTB][PR];
@@ -44,7 +60,7 @@ __global__ __launch_bounds__(256) void gdn2_chunk_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) float s_u[kTB][DV];
 
   const int tid = threadIdx.x;
-  const int rq = tid & 3, grp = tid >> 2;  // row quarter, column group
+  const int rq = tid % RQ, grp = tid / RQ;  // row group, column group
   const int64_t id = blockIdx.x;
   const int c = (int)(id % a.N);
   const int64_t bh = id / a.N;
@@ -60,10 +76,9 @@ __global__ __launch_bounds__(256) void gdn2_chunk_kernel(ChunkArgs a) {
     if constexpr (OUT) {
       const float* M0 = a.chunk_init + ((b * a.H + h) * a.N + c) * (int64_t)DK * DV;
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const float4 v4 = *reinterpret_cast<const float4*>(M0 + (int64_t)(r0 + i) * DV + grp * CPT);
-        x[0][i] = v4.x; x[1][i] = v4.y; x[2][i] = v4.z; x[3][i] = v4.w;
-      }
+      for (int i = 0; i < RPT; ++i)
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) x[j][i] = M0[(int64_t)(r0 + i) * DV + grp * CPT + j];
     } else {
 #pragma unroll
       for (int j = 0; j < CPT; ++j)
@@ -98,7 +113,9 @@ __global__ __launch_bounds__(256) void gdn2_chunk_kernel(ChunkArgs a) {
     if (!active) continue;
     for (int t = 0; t < nb; ++t) {
       // read of every column: k . D x over this thread's rows, then over the row quarters
-      float s[CPT] = {0.f, 0.f, 0.f, 0.f};
+      float s[CPT];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) s[j] = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; i += 4) {
         const float4 ka = *reinterpret_cast<const float4*>(&s_ka[t][r0 + i]);
@@ -111,10 +128,9 @@ __global__ __launch_bounds__(256) void gdn2_chunk_kernel(ChunkArgs a) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        s[j] += __shfl_xor(s[j], 1, 64);
-        s[j] += __shfl_xor(s[j], 2, 64);
-      }
+      for (int j = 0; j < CPT; ++j)
+#pragma unroll
+        for (int m = 1; m < RQ; m <<= 1) s[j] += __shfl_xor(s[j], m, 64);
       float u[CPT];
 #pragma unroll
       for (int j = 0; j < CPT; ++j) u[j] = writes ? s_u[t][ucol0 + j] : 0.f;
@@ -132,7 +148,9 @@ __global__ __launch_bounds__(256) void gdn2_chunk_kernel(ChunkArgs a) {
         }
       }
       if constexpr (OUT) {
-        float o[CPT] = {0.f, 0.f, 0.f, 0.f};
+        float o[CPT];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) o[j] = 0.f;
 #pragma unroll
         for (int i = 0; i < RPT; i += 4) {
           const float4 qv = *reinterpret_cast<const float4*>(&s_q[t][r0 + i]);
@@ -145,10 +163,9 @@ __global__ __launch_bounds__(256) void gdn2_chunk_kernel(ChunkArgs a) {
           }
         }
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-          o[j] += __shfl_xor(o[j], 1, 64);
-          o[j] += __shfl_xor(o[j], 2, 64);
-        }
+        for (int j = 0; j < CPT; ++j)
+#pragma unroll
+          for (int m = 1; m < RQ; m <<= 1) o[j] += __shfl_xor(o[j], m, 64);
         if (rq == 0) {
           float* orow = a.o + ((b * a.T + t0 + tb + t) * a.H + h) * DV + grp * CPT;
 #pragma unroll
@@ -174,8 +191,7 @@ __global__ __launch_bounds__(256) void gdn2_chunk_kernel(ChunkArgs a) {
 
 template <class T, int DK, int DV, bool OUT>
 static hipError_t launch_gdn2_t(const ChunkArgs& a, hipStream_t s) {
-  constexpr int NCOL = OUT ? DV : DK + DV;
-  constexpr int NT = NCOL / 4 * 4;
+  constexpr int NT = gdn2_threads<DK, DV, OUT>();
   const int64_t nb = a.B * a.H * (int64_t)a.N;
   TimedLaunch tl(HLA_KERNEL_CHUNK, s);
   hipLaunchKernelGGL((gdn2_chunk_kernel<T, DK, DV, OUT>), dim3((unsigned)nb), dim3(NT < 64 ? 64 : NT), 0, s, a);
