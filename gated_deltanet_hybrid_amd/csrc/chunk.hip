@@ -38,7 +38,9 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
   constexpr int R1a = (WANT_O ? 2 : 1) * C * PK * E;
   constexpr int R1b = 2 * C * PX * 4;
   constexpr int R1 = R1a > R1b ? R1a : R1b;
-  constexpr int R2 = (DK + DV) * PT * E;
+  // R2 holds K^T, V^T for the UT transform, then S~^T; an output pass that takes W | U
+  // from the hand-off needs only the latter (two workgroups fit in one CU's LDS)
+  constexpr int R2 = AUXIN ? DV * PK * E : (DK + DV) * PT * E;
   constexpr int R3 = WANT_O ? C * PT * E : 16;
   static_assert(!WANT_O || DV * PK * E <= R2, "S~^T staging must fit in R2");
   static_assert(!WANT_O || C * PK * E <= R1, "Qp staging must fit in R1");
