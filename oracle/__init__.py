@@ -21,8 +21,12 @@ Sources (cited by page title and section):
 Orientation: the math state S has shape [dv, dk] and acts on keys (o = S q).  Chunk
 transitions act on the right: S_end = S_start @ A + B with A [dk, dk], B [dv, dk].
 
-Parity status: every function is pinned by tests/test_oracle_pins.py except the readings
-listed in ``PARITY_UNPINNED`` (no printed number can confirm them).
+Gradients (``oracle.grad``) are those of the same forward, taken by torch.autograd on a
+float64 CPU restatement of it.
+
+Parity status: every function is pinned by tests/test_oracle_pins.py (gradients by
+tests/test_oracle_grad_pins.py) except the readings listed in ``PARITY_UNPINNED`` (no
+printed number can confirm them).
 """
 from .gdn import (  # noqa: F401
     gdn_recurrent,
@@ -41,6 +45,13 @@ from .gdn import (  # noqa: F401
     tail_replay,
     n_eff,
     PARITY_UNPINNED,
+)
+from .grad import (  # noqa: F401
+    routed_states_backward,
+    chunk_outputs_backward,
+    chunk_transitions_backward,
+    router_backward,
+    hla_prefill_backward,
 )
 from .gdn2 import (  # noqa: F401
     gdn2_recurrent,
