@@ -95,6 +95,25 @@ int64_t reps_ws(const hla_dims_t* d, int32_t n_rep) {
   return round_up(d->B * d->H * n_chunks(d) * n_rep * d->dk * 4, 256);
 }
 
+// Workspace of hla_compose_backward: At^T, the states in front of every history step and
+// g lambda of it (N (N - 1) / 2 slots per (b, h), dtype), per-wave gate-gradient parts and
+// the final lambda of every chain.
+struct ComposeBwdWs {
+  int64_t att_off, ms_off, ls_off, dgp_off, le_off, total;
+};
+ComposeBwdWs compose_bwd_ws(const hla_dims_t* d) {
+  const int64_t N = n_chunks(d), BH = d->B * d->H, e = dtype_bytes(d->dtype);
+  const int64_t P = N * (N - 1) / 2;
+  ComposeBwdWs w;
+  w.att_off = 0;
+  w.ms_off = round_up(BH * N * d->dk * d->dk * e, 256);
+  w.ls_off = w.ms_off + round_up(BH * P * d->dk * d->dv * e, 256);
+  w.dgp_off = w.ls_off + round_up(BH * P * d->dk * d->dv * e, 256);
+  w.le_off = w.dgp_off + round_up(BH * N * N * (d->dv / 32) * 4, 256);
+  w.total = w.le_off + round_up(BH * N * d->dk * d->dv * 4, 256);
+  return w;
+}
+
 hla_status_t hip_status(hipError_t e) { return e == hipSuccess ? HLA_OK : HLA_ERR_HIP; }
 
 // One chunk pass of either recurrence: transitions (want_ab) or outputs from chunk_init.
@@ -226,6 +245,7 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
       if (n_rep < 1 || d->C % n_rep != 0) return HLA_ERR_BAD_SHAPE;
       *out = (size_t)reps_ws(d, n_rep);
       return HLA_OK;
+    case HLA_FN_COMPOSE_BACKWARD: *out = (size_t)compose_bwd_ws(d).total; return HLA_OK;
     default: return HLA_ERR_UNSUPPORTED;
   }
 }
@@ -330,6 +350,27 @@ hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps,
   a.At_prep = static_cast<char*>(ws) + route_qbar_bytes(d);
   a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)N; a.C = d->C;
   return hip_status(hla::launch_route(a, d->dtype, d->dk, d->dv, stream));
+}
+
+hla_status_t hla_compose_backward(const hla_dims_t* d, const void* At, const void* Bc, const float* gates,
+                                  const uint8_t* mask, const float* S0, const float* dS_routed, float* dAt,
+                                  float* dBc, float* dgates, float* dS0, float* S_routed, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (!At || !Bc || !gates || !mask || !dS_routed || !dAt || !dBc || !dgates) return HLA_ERR_NULL_ARG;
+  if (!all_aligned(At, Bc, S0, dS_routed, dAt, dBc, dS0, S_routed, ws) || !all_aligned4(gates, dgates))
+    return HLA_ERR_ALIGN;
+  const ComposeBwdWs w = compose_bwd_ws(d);
+  if (!ws || (int64_t)ws_bytes < w.total) return HLA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  hla::ComposeBwdArgs a{};
+  a.At = At; a.Bc = Bc; a.gates = gates; a.mask = mask; a.S0 = S0; a.dS = dS_routed;
+  a.dAt = dAt; a.dBc = dBc; a.dgates = dgates; a.dS0 = dS0; a.S_routed = S_routed;
+  a.AtT = base + w.att_off; a.Msave = base + w.ms_off; a.Lsave = base + w.ls_off;
+  a.dgp = reinterpret_cast<float*>(base + w.dgp_off); a.lam_end = reinterpret_cast<float*>(base + w.le_off);
+  a.B = d->B; a.H = d->H; a.N = (int32_t)n_chunks(d);
+  return hip_status(hla::launch_compose_backward(a, d->dtype, d->dk, d->dv, stream));
 }
 
 // Shared checks of the two decode entry points (everything but the per-token gates).

@@ -132,4 +132,27 @@ struct RepsArgs {
 // Learned chunk representatives: window self-attention, mean-pool, projections.
 hipError_t launch_reps(const RepsArgs& a, int dtype, int dk, hipStream_t s);
 
+struct ComposeBwdArgs {
+  const void* At;        // [B,H,N,dk,dk] (dtype)
+  const void* Bc;        // [B,H,N,dk,dv]
+  const float* gates;    // [B,H,N,N]
+  const uint8_t* mask;   // [B,H,N,N]
+  const float* S0;       // [B,H,dk,dv] or null
+  const float* dS;       // [B,H,N,dk,dv] upstream gradient of the routed states
+  float* dAt;            // out [B,H,N,dk,dk]
+  float* dBc;            // out [B,H,N,dk,dv]
+  float* dgates;         // out [B,H,N,N]
+  float* dS0;            // out [B,H,dk,dv] or null
+  float* S_routed;       // out [B,H,N,dk,dv] or null
+  void* AtT;             // workspace [B,H,N,dk,dk] (dtype)
+  void* Msave;           // workspace [B,H,N(N-1)/2,dk,dv] (dtype): M_{j-1} of pair (i, j)
+  void* Lsave;           // workspace [B,H,N(N-1)/2,dk,dv] (dtype): g lambda_j of pair (i, j)
+  float* dgp;            // workspace [B,H,N,N,dv/32]: per-wave gate-gradient parts
+  float* lam_end;        // workspace [B,H,N,dk,dv]: final lambda of every chain
+  int64_t B, H;
+  int32_t N;
+};
+// Backward of the gated composition (see compose_bwd.hip).
+hipError_t launch_compose_backward(const ComposeBwdArgs& a, int dtype, int dk, int dv, hipStream_t s);
+
 }  // namespace hla

@@ -18,7 +18,9 @@ _lib = None
 
 HLA_F32, HLA_BF16 = 0, 1
 KERNEL_CHUNK, KERNEL_SCAN, KERNEL_GATES, KERNEL_COMPOSE, KERNEL_DECODE, KERNEL_REPS = 0, 1, 2, 3, 4, 5
+KERNEL_BWD_SAVE, KERNEL_BWD_ADJOINT, KERNEL_BWD_REDUCE, KERNEL_BWD_CHUNK, KERNEL_BWD_ROUTER = 6, 7, 8, 9, 10
 FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX, FN_WU_HANDOFF, FN_CHUNK_REPS = 0, 1, 2, 3, 4
+FN_COMPOSE_BACKWARD, FN_PREFILL_BACKWARD = 5, 6
 CHUNK = 64
 MAX_CACHE_SLOTS = 1024
 
@@ -52,6 +54,8 @@ _SIGS = {
                                         ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]),
     "hla_route_mix": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
                                        _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "hla_compose_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              ctypes.c_size_t, _P]),
     "hla_timing_enable": (ctypes.c_int32, [ctypes.c_int32]),
     "hla_timing_read": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "hla_gdn_decode": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -344,6 +348,37 @@ def route_mix(q, reps, At, Bc, n_rep=CHUNK, tau=1e-3, S0=None, gates_in=None, T=
                                    _ptr(acnt), _ptr(neff), _ptr(Sr), _ptr(ws), 0 if ws is None else ws.numel(),
                                    _stream(dev)), "hla_route_mix")
     return dict(gates=gates, mask=mask, active_idx=aidx, active_cnt=acnt, n_eff=neff, S_routed=Sr)
+
+
+def compose_backward(At, Bc, gates, mask, dS_routed, S0=None, want_dS0=True, want_states=False, T=None, C=CHUNK,
+                     ws=None):
+    """Reverse of the gated composition.  At/Bc as given to route_mix, gates/mask as it
+    wrote them, dS_routed [B, H, N, dk, dv] float32.  Returns dict(dAt, dBc, dgates, dS0
+    (or None), S_routed (the recomputed routed states, or None))."""
+    B, H, N, dk, _ = At.shape
+    dv = Bc.shape[-1]
+    dev = At.device
+    T = T if T is not None else N * C
+    d = make_dims(B, T, H, T, dk, dv, _dtype_code(At), C)
+    _need(At, (B, H, N, dk, dk), At.dtype, "At")
+    _need(Bc, (B, H, N, dk, dv), At.dtype, "Bc")
+    _need(gates, (B, H, N, N), torch.float32, "gates")
+    _need(mask, (B, H, N, N), torch.uint8, "mask")
+    _need(dS_routed, (B, H, N, dk, dv), torch.float32, "dS_routed")
+    _need(S0, (B, H, dk, dv), torch.float32, "S0")
+    f32 = dict(dtype=torch.float32, device=dev)
+    dAt = torch.empty((B, H, N, dk, dk), **f32)
+    dBc = torch.empty((B, H, N, dk, dv), **f32)
+    dg = torch.empty((B, H, N, N), **f32)
+    dS0 = torch.empty((B, H, dk, dv), **f32) if want_dS0 else None
+    Sr = torch.empty((B, H, N, dk, dv), **f32) if want_states else None
+    if ws is None:
+        ws = _workspace(workspace_bytes(FN_COMPOSE_BACKWARD, d), dev)
+    _check(library().hla_compose_backward(ctypes.byref(d), _ptr(At), _ptr(Bc), _ptr(gates), _ptr(mask), _ptr(S0),
+                                          _ptr(dS_routed), _ptr(dAt), _ptr(dBc), _ptr(dg), _ptr(dS0), _ptr(Sr),
+                                          _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)),
+           "hla_compose_backward")
+    return dict(dAt=dAt, dBc=dBc, dgates=dg, dS0=dS0, S_routed=Sr)
 
 
 def hla_prefill(q, k, v, beta, alpha, tau=1e-3, gates_in=None, S0=None, C=CHUNK, handoff=True, pooler=None,

@@ -31,7 +31,8 @@ import numpy as np
 
 SEGMENT = 4096
 _TENSOR_ID = {"q": 1, "k": 2, "v": 3, "beta": 4, "alpha": 5, "gates": 6, "At": 7, "Bc": 8, "S0": 9,
-              "Wq": 10, "Wk": 11, "Wv": 12, "Wp": 13, "Wr": 14, "ga": 15, "gb": 16, "gw": 17}
+              "Wq": 10, "Wk": 11, "Wv": 12, "Wp": 13, "Wr": 14, "ga": 15, "gb": 16, "gw": 17,
+              "dO": 18, "dS": 19}
 
 
 # --------------------------------------------------------------------------- rounding
@@ -275,6 +276,13 @@ def gen_state(B, H, dk, dv, seed=0, stream=0, scale=0.5) -> np.ndarray:
     """A float32 initial state [B, H, dk, dv] (state orientation)."""
     rng = _rng(seed, stream, "S0", B, H, dk, dv)
     return (scale * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
+
+
+def gen_cotangent(shape, seed=0, stream=0, name="dO", scale=1.0) -> np.ndarray:
+    """A seeded upstream gradient (a random direction for a vector-Jacobian product):
+    float32 N(0, scale^2) of the given shape."""
+    rng = _rng(seed, stream, name, *shape)
+    return (scale * rng.standard_normal(tuple(shape))).astype(np.float32)
 
 
 # --------------------------------------------------------------------------- workloads

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define HLA_ABI_VERSION 3
+#define HLA_ABI_VERSION 4
 
 typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype_t;
 
@@ -84,7 +84,9 @@ typedef enum {
   HLA_FN_WU_HANDOFF = 3, /* size of the optional wu buffer of hla_chunk_transitions and
                             hla_gdn_prefill: B H ceil(T / 64) 64 (dk + dv) bf16 values;
                             0 for float32, which takes no hand-off */
-  HLA_FN_CHUNK_REPS = 4  /* workspace of hla_chunk_reps; n_rep = C / window */
+  HLA_FN_CHUNK_REPS = 4, /* workspace of hla_chunk_reps; n_rep = C / window */
+  HLA_FN_COMPOSE_BACKWARD = 5, /* workspace of hla_compose_backward */
+  HLA_FN_PREFILL_BACKWARD = 6  /* workspace of hla_prefill_backward */
 } hla_fn_t;
 
 /*
@@ -288,6 +290,38 @@ hla_status_t hla_gdn2_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int3
                              float tau, float* o, float* gates_out, int32_t commit,
                              hipStream_t stream);
 
+/*
+ * hla_compose_backward -- reverse of the gated composition of hla_route_mix.
+ * [HLA] Methodology paragraphs 1, 3 and 4.  Query chunk i's routed state is the chain
+ *     M_j = M_{j-1} + g_ij (At_j - I) M_{j-1} + g_ij Bc_j    over active j < i, M = S0 first,
+ * and given lambda = dL/dS~_i (stored orientation) the reverse of every step is
+ *     dBc_j += g lambda_j,  dAt_j += g lambda_j M_{j-1}^T,
+ *     dg_ij = <lambda_j, (At_j - I) M_{j-1} + Bc_j>,  lambda_{j-1} = lambda_j + g (At_j - I)^T lambda_j.
+ * Skipped pairs (mask 0) pass lambda unchanged and get dg = 0 (the skip is a step function
+ * of g with zero derivative).
+ *   At, Bc     [B, H, N, dk, dk] / [B, H, N, dk, dv] (dtype), as given to hla_route_mix.
+ *   gates, mask [B, H, N, N] float32 / uint8, as hla_route_mix wrote them (entries j < i
+ *              are read).
+ *   S0         [B, H, dk, dv] float32 or NULL (zero).
+ *   dS_routed  [B, H, N, dk, dv] float32: upstream gradient of S_routed.
+ *   dAt, dBc   out [B, H, N, dk, dk] / [B, H, N, dk, dv] float32.
+ *   dgates     out [B, H, N, N] float32: dL/dg_ij for active j < i, 0 elsewhere.
+ *   dS0        out [B, H, dk, dv] float32, or NULL.
+ *   S_routed   out [B, H, N, dk, dv] float32 (the routed states, recomputed), or NULL.
+ *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_COMPOSE_BACKWARD) bytes:
+ *              At^T, and the state in front of every active step and g lambda of it
+ *              (dtype, N (N - 1) / 2 slots of dk x dv per (b, h)), so it grows as N^2.
+ * Computation: bf16 (or float32) matrix-core products with float32 accumulation; sums in a
+ * fixed order (deterministic).
+ * Errors: HLA_ERR_NULL_ARG, HLA_ERR_BAD_SHAPE, HLA_ERR_BAD_DTYPE, HLA_ERR_ALIGN,
+ * HLA_ERR_WORKSPACE, HLA_ERR_HIP.
+ */
+hla_status_t hla_compose_backward(const hla_dims_t* d, const void* At, const void* Bc,
+                                  const float* gates, const uint8_t* mask, const float* S0,
+                                  const float* dS_routed, float* dAt, float* dBc, float* dgates,
+                                  float* dS0, float* S_routed, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /* Workspace bytes that entry point `fn` needs for dims `d`; n_rep is the number of
  * representatives per chunk for HLA_FN_CHUNK_REPS (C / window; it must divide C) and is
  * ignored otherwise.  `out` is a host pointer. */
@@ -301,7 +335,12 @@ typedef enum {
   HLA_KERNEL_COMPOSE = 3,  /* gated composition of chunk transitions                  */
   HLA_KERNEL_DECODE = 4,   /* single-token decode step                                */
   HLA_KERNEL_REPS = 5,     /* learned representatives: window attention and mean-pool */
-  HLA_KERNEL_COUNT = 6
+  HLA_KERNEL_BWD_SAVE = 6,    /* backward: composition replay that keeps the step states */
+  HLA_KERNEL_BWD_ADJOINT = 7, /* backward: adjoint sweep of every composition chain     */
+  HLA_KERNEL_BWD_REDUCE = 8,  /* backward: per-history-chunk sums (dAt, dBc, gates, dS0)  */
+  HLA_KERNEL_BWD_CHUNK = 9,   /* backward: per-chunk reverse token recurrence            */
+  HLA_KERNEL_BWD_ROUTER = 10, /* backward: router gates to queries and keys              */
+  HLA_KERNEL_COUNT = 11
 } hla_kernel_t;
 
 /*
