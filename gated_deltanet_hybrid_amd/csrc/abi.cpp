@@ -114,6 +114,30 @@ ComposeBwdWs compose_bwd_ws(const hla_dims_t* d) {
   return w;
 }
 
+// Workspace of hla_chunk_backward: per-workgroup partial sums of the per-token gradients.
+struct ChunkBwdWs {
+  int64_t k_off, q_off, s_off, v_off, total;
+};
+ChunkBwdWs chunk_bwd_ws(const hla_dims_t* d) {
+  const int64_t BHN = d->B * d->H * n_pieces(d), C = kPiece;
+  const int64_t nb_out = d->dv / 32, nb_all = nb_out + (d->dk + d->dv) / 32;
+  ChunkBwdWs w;
+  w.k_off = 0;
+  w.q_off = round_up(BHN * nb_all * C * d->dk * 4, 256);
+  w.s_off = w.q_off + round_up(BHN * nb_out * C * d->dk * 4, 256);
+  w.v_off = w.s_off + round_up(BHN * nb_all * C * 2 * 4, 256);
+  w.total = w.v_off + round_up(BHN * 2 * C * d->dv * 4, 256);
+  return w;
+}
+
+void set_chunk_bwd_ws(hla::ChunkBwdArgs& a, const ChunkBwdWs& w, void* ws) {
+  char* base = static_cast<char*>(ws);
+  a.part_k = reinterpret_cast<float*>(base + w.k_off);
+  a.part_q = reinterpret_cast<float*>(base + w.q_off);
+  a.part_s = reinterpret_cast<float*>(base + w.s_off);
+  a.part_v = reinterpret_cast<float*>(base + w.v_off);
+}
+
 hla_status_t hip_status(hipError_t e) { return e == hipSuccess ? HLA_OK : HLA_ERR_HIP; }
 
 // One chunk pass of either recurrence: transitions (want_ab) or outputs from chunk_init.
@@ -246,6 +270,10 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
       *out = (size_t)reps_ws(d, n_rep);
       return HLA_OK;
     case HLA_FN_COMPOSE_BACKWARD: *out = (size_t)compose_bwd_ws(d).total; return HLA_OK;
+    case HLA_FN_CHUNK_BACKWARD:
+      if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
+      *out = (size_t)chunk_bwd_ws(d).total;
+      return HLA_OK;
     default: return HLA_ERR_UNSUPPORTED;
   }
 }
@@ -371,6 +399,33 @@ hla_status_t hla_compose_backward(const hla_dims_t* d, const void* At, const voi
   a.dgp = reinterpret_cast<float*>(base + w.dgp_off); a.lam_end = reinterpret_cast<float*>(base + w.le_off);
   a.B = d->B; a.H = d->H; a.N = (int32_t)n_chunks(d);
   return hip_status(hla::launch_compose_backward(a, d->dtype, d->dk, d->dv, stream));
+}
+
+hla_status_t hla_chunk_backward(const hla_dims_t* d, const void* q, const void* k, const void* v, const float* beta,
+                                const float* alpha, const float* chunk_init, const float* dO, const float* dAt,
+                                const float* dBc, float* dq, float* dk, float* dv, float* dbeta, float* dalpha,
+                                float* dchunk_init, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
+  const bool have_out = chunk_init || dO, have_map = dAt || dBc;
+  if (!have_out && !have_map) return HLA_ERR_NULL_ARG;
+  if (have_out && (!chunk_init || !dO || !q || !dchunk_init)) return HLA_ERR_NULL_ARG;
+  if (have_map && (!dAt || !dBc)) return HLA_ERR_NULL_ARG;
+  if (!k || !v || !beta || !alpha || !dq || !dk || !dv || !dbeta || !dalpha) return HLA_ERR_NULL_ARG;
+  if (!all_aligned(q, k, v, chunk_init, dAt, dBc, dchunk_init, ws) ||
+      !all_aligned4(beta, alpha, dO, dq, dk, dv, dbeta, dalpha))
+    return HLA_ERR_ALIGN;
+  const ChunkBwdWs w = chunk_bwd_ws(d);
+  if (!ws || (int64_t)ws_bytes < w.total) return HLA_ERR_WORKSPACE;
+  hla::ChunkBwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
+  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)n_pieces(d);
+  a.have_out = have_out; a.have_map = have_map;
+  a.chunk_init = chunk_init; a.dO = dO; a.dAt = dAt; a.dBc = dBc; a.dchunk_init = dchunk_init;
+  set_chunk_bwd_ws(a, w, ws);
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dalpha = dalpha;
+  return hip_status(hla::launch_chunk_backward(a, d->dtype, d->dk, d->dv, stream));
 }
 
 // Shared checks of the two decode entry points (everything but the per-token gates).

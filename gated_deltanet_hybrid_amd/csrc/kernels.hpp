@@ -155,4 +155,36 @@ struct ComposeBwdArgs {
 // Backward of the gated composition (see compose_bwd.hip).
 hipError_t launch_compose_backward(const ComposeBwdArgs& a, int dtype, int dk, int dv, hipStream_t s);
 
+struct ChunkBwdArgs {
+  const void* q;            // [B,ld_T,H,dk] (dtype)
+  const void* k;
+  const void* v;
+  const float* beta;        // [B,ld_T,H]
+  const float* alpha;
+  int64_t B, T, H, ld_T;
+  int32_t N;                // 64-token chunks
+  int32_t have_out;         // reverse of the outputs from chunk_init
+  int32_t have_map;         // reverse of the chunk maps
+  const float* chunk_init;  // [B,H,N,dk,dv] start state of every chunk (have_out)
+  const float* dO;          // [B,T,H,dv] upstream gradient of the outputs (have_out)
+  const float* dAt;         // [B,H,N,dk,dk] upstream gradient of At (have_map)
+  const float* dBc;         // [B,H,N,dk,dv]
+  float* dchunk_init;       // out [B,H,N,dk,dv] (have_out)
+  // workspace: per-workgroup partial sums
+  float* part_k;            // [B,H,N,(dv + dk + dv)/32,64,dk]
+  float* part_q;            // [B,H,N,dv/32,64,dk]
+  float* part_s;            // [B,H,N,(dv + dk + dv)/32,64,2]: dbeta, dalpha
+  float* part_v;            // [B,H,N,2,64,dv]
+  // router parts added by the finalize pass, or null
+  const float* dqbar;       // [B,H,N,dk] gradient of each chunk's query mean
+  const float* dk_router;   // [B,T,H,dk]
+  float* dq;                // out [B,T,H,dk]
+  float* dk;                // out [B,T,H,dk]
+  float* dv;                // out [B,T,H,dv]
+  float* dbeta;             // out [B,T,H]
+  float* dalpha;            // out [B,T,H]
+};
+// Backward of the chunk outputs and / or the chunk maps, then the per-token sums.
+hipError_t launch_chunk_backward(const ChunkBwdArgs& a, int dtype, int dk, int dv, hipStream_t s);
+
 }  // namespace hla

@@ -20,7 +20,7 @@ HLA_F32, HLA_BF16 = 0, 1
 KERNEL_CHUNK, KERNEL_SCAN, KERNEL_GATES, KERNEL_COMPOSE, KERNEL_DECODE, KERNEL_REPS = 0, 1, 2, 3, 4, 5
 KERNEL_BWD_SAVE, KERNEL_BWD_ADJOINT, KERNEL_BWD_REDUCE, KERNEL_BWD_CHUNK, KERNEL_BWD_ROUTER = 6, 7, 8, 9, 10
 FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX, FN_WU_HANDOFF, FN_CHUNK_REPS = 0, 1, 2, 3, 4
-FN_COMPOSE_BACKWARD, FN_PREFILL_BACKWARD = 5, 6
+FN_COMPOSE_BACKWARD, FN_PREFILL_BACKWARD, FN_CHUNK_BACKWARD = 5, 6, 7
 CHUNK = 64
 MAX_CACHE_SLOTS = 1024
 
@@ -56,6 +56,8 @@ _SIGS = {
                                        _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "hla_compose_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
+    "hla_chunk_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                            _P, _P, _P, ctypes.c_size_t, _P]),
     "hla_timing_enable": (ctypes.c_int32, [ctypes.c_int32]),
     "hla_timing_read": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "hla_gdn_decode": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -379,6 +381,33 @@ def compose_backward(At, Bc, gates, mask, dS_routed, S0=None, want_dS0=True, wan
                                           _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)),
            "hla_compose_backward")
     return dict(dAt=dAt, dBc=dBc, dgates=dg, dS0=dS0, S_routed=Sr)
+
+
+def chunk_backward(q, k, v, beta, alpha, chunk_init=None, dO=None, dAt=None, dBc=None, ws=None):
+    """Reverse of the per-chunk work (64-token chunks): the outputs from chunk_init (with
+    dO [B, T, H, dv] float32) and / or the chunk maps (with dAt, dBc float32).  Returns
+    dict(dq, dk, dv, dbeta, dalpha, dchunk_init (or None)), all float32, [B, T, H, *]."""
+    d = _inputs(k, v, beta, alpha, q=q if chunk_init is not None else None)
+    B, T, H, ld_T, dk, dv = d.B, d.T, d.H, d.ld_T, d.dk, d.dv
+    N = math.ceil(T / CHUNK)
+    dev = k.device
+    _need(chunk_init, (B, H, N, dk, dv), torch.float32, "chunk_init")
+    _need(dO, (B, T, H, dv), torch.float32, "dO")
+    _need(dAt, (B, H, N, dk, dk), torch.float32, "dAt")
+    _need(dBc, (B, H, N, dk, dv), torch.float32, "dBc")
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
+               dv=torch.empty((B, T, H, dv), **f32), dbeta=torch.empty((B, T, H), **f32),
+               dalpha=torch.empty((B, T, H), **f32),
+               dchunk_init=torch.empty((B, H, N, dk, dv), **f32) if chunk_init is not None else None)
+    if ws is None:
+        ws = _workspace(workspace_bytes(FN_CHUNK_BACKWARD, d), dev)
+    _check(library().hla_chunk_backward(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+                                        _ptr(chunk_init), _ptr(dO), _ptr(dAt), _ptr(dBc), _ptr(out["dq"]),
+                                        _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dalpha"]),
+                                        _ptr(out["dchunk_init"]), _ptr(ws), 0 if ws is None else ws.numel(),
+                                        _stream(dev)), "hla_chunk_backward")
+    return out
 
 
 def hla_prefill(q, k, v, beta, alpha, tau=1e-3, gates_in=None, S0=None, C=CHUNK, handoff=True, pooler=None,

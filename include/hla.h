@@ -86,7 +86,8 @@ typedef enum {
                             0 for float32, which takes no hand-off */
   HLA_FN_CHUNK_REPS = 4, /* workspace of hla_chunk_reps; n_rep = C / window */
   HLA_FN_COMPOSE_BACKWARD = 5, /* workspace of hla_compose_backward */
-  HLA_FN_PREFILL_BACKWARD = 6  /* workspace of hla_prefill_backward */
+  HLA_FN_PREFILL_BACKWARD = 6, /* workspace of hla_prefill_backward */
+  HLA_FN_CHUNK_BACKWARD = 7    /* workspace of hla_chunk_backward */
 } hla_fn_t;
 
 /*
@@ -321,6 +322,35 @@ hla_status_t hla_compose_backward(const hla_dims_t* d, const void* At, const voi
                                   const float* dS_routed, float* dAt, float* dBc, float* dgates,
                                   float* dS0, float* S_routed, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/*
+ * hla_chunk_backward -- reverse of the per-chunk work (64-token chunks, C = 64):
+ *   outputs part: the routed outputs of hla_gdn_prefill with chunk_init (every chunk's
+ *     tokens run by the gated delta rule from its own start state, o_t = S_t q_t);
+ *   map part: the chunk maps (At, Bc) of hla_chunk_transitions ([HLA] Methodology
+ *     paragraph 1: the product of the per-token linear parts, and the state from zero).
+ * Every state column follows x <- alpha (x - beta k (k . x)) + beta k u on its own; the
+ * reverse of one token with dx = dL/dx after it is b = k . dx, dv[col] += beta b,
+ * dbeta += b (u - alpha k . x_prev), dalpha += dx . x_prev - beta (k . x_prev) b,
+ * dk += beta u dx - alpha beta ((k . x_prev) dx + b x_prev), dx <- alpha (dx - beta k b).
+ *   q, k, v, beta, alpha: as for hla_gdn_prefill (q is read by the outputs part only).
+ *   chunk_init [B, H, N, dk, dv] float32 and dO [B, T, H, dv] float32: both or neither
+ *              (outputs part).
+ *   dAt [B, H, N, dk, dk], dBc [B, H, N, dk, dv] float32: both or neither (map part).
+ *   dq, dk [B, T, H, dk], dv [B, T, H, dv], dbeta, dalpha [B, T, H]: float32 outputs, the
+ *              sum of both parts (dq is zero without the outputs part).
+ *   dchunk_init [B, H, N, dk, dv] float32 out (required with the outputs part).
+ *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_CHUNK_BACKWARD) bytes
+ *              (per-workgroup partial sums).
+ * Arithmetic is float32 throughout; partial sums are added in a fixed order.
+ * Errors: HLA_ERR_NULL_ARG (no part, or a missing output), HLA_ERR_UNSUPPORTED (C != 64),
+ * and as hla_gdn_prefill.
+ */
+hla_status_t hla_chunk_backward(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                                const float* beta, const float* alpha, const float* chunk_init,
+                                const float* dO, const float* dAt, const float* dBc, float* dq,
+                                float* dk, float* dv, float* dbeta, float* dalpha,
+                                float* dchunk_init, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes that entry point `fn` needs for dims `d`; n_rep is the number of
  * representatives per chunk for HLA_FN_CHUNK_REPS (C / window; it must divide C) and is

@@ -57,3 +57,52 @@ def test_compose_backward(case, mode, tau, with_s0):
             assert_close(dg, ref["dghat"], dtype, "dgates")
             assert np.all(dg[~fw["mask"]] == 0.0)
             assert_close(host(g["dS0"])[b, hh], ref["dS0"].T, dtype, "dS0")
+
+
+def _tok(x, name, b, h):
+    return x.f64(name)[b, :, h]
+
+
+CHUNK_CASES = [("f32", 64, 128, 3 * C + 17), ("bf16", 128, 128, 150), ("bf16", 128, 64, C), ("bf16", 64, 64, 1),
+               ("f32", 128, 128, 2 * C)]
+
+
+@pytest.mark.parametrize("parts", ["out", "map", "both"])
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=[f"{c[0]}-dk{c[1]}-dv{c[2]}-T{c[3]}" for c in CHUNK_CASES])
+def test_chunk_backward(case, parts):
+    dtype, dk, dv, T = case
+    note(f"chunk backward {case} {parts}")
+    B, H = 2, 2
+    N = -(-T // C)
+    x = inputs.gen_tokens(B, T, H, dk, dv, dtype=dtype, seed=41, alpha_mode="slow")
+    q, k, v, beta, alpha = (dev(x.q, dtype), dev(x.k, dtype), dev(x.v, dtype), f32(x.beta), f32(x.alpha))
+    want_out, want_map = parts in ("out", "both"), parts in ("map", "both")
+    init = inputs.gen_cotangent((B, H, N, dk, dv), seed=42, name="S0", scale=0.5) if want_out else None
+    dO = inputs.gen_cotangent((B, T, H, dv), seed=43, name="dO") if want_out else None
+    dAt = inputs.gen_cotangent((B, H, N, dk, dk), seed=44, name="At") if want_map else None
+    dBc = inputs.gen_cotangent((B, H, N, dk, dv), seed=45, name="Bc") if want_map else None
+    g = hla().chunk_backward(q, k, v, beta, alpha, chunk_init=None if init is None else f32(init),
+                             dO=None if dO is None else f32(dO), dAt=None if dAt is None else f32(dAt),
+                             dBc=None if dBc is None else f32(dBc))
+    torch.cuda.synchronize()
+    for b in range(B):
+        for hh in range(H):
+            qq, kk, vv, bb, aa = (_tok(x, n, b, hh) for n in ("q", "k", "v", "beta", "alpha"))
+            ref = {n: 0.0 for n in ("dq", "dk", "dv", "dbeta", "dalpha")}
+            if want_out:
+                ro = oracle.chunk_outputs_backward(qq, kk, vv, bb, aa, C, init[b, hh].astype(np.float64).transpose(0, 2, 1),
+                                                   dO[b, :, hh].astype(np.float64))
+                for n in ref:
+                    ref[n] = ref[n] + ro[n]
+                assert_close(host(g["dchunk_init"])[b, hh], ro["dS_routed"].transpose(0, 2, 1), dtype, "dchunk_init")
+            if want_map:
+                rm = oracle.chunk_transitions_backward(kk, vv, bb, aa, C, dAt[b, hh].astype(np.float64).transpose(0, 2, 1),
+                                                       dBc[b, hh].astype(np.float64).transpose(0, 2, 1))
+                for n in ("dk", "dv", "dbeta", "dalpha"):
+                    ref[n] = ref[n] + rm[n]
+            if want_out:
+                assert_close(host(g["dq"])[b, :, hh], ref["dq"], dtype, "dq")
+            else:
+                assert np.all(host(g["dq"])[b, :, hh] == 0.0)
+            for n, key in (("dk", "dk"), ("dv", "dv"), ("dbeta", "dbeta"), ("dalpha", "dalpha")):
+                assert_close(host(g[key])[b, :, hh], ref[n], dtype, n)
