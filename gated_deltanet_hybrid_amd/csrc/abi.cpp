@@ -138,6 +138,43 @@ void set_chunk_bwd_ws(hla::ChunkBwdArgs& a, const ChunkBwdWs& w, void* ws) {
   a.part_v = reinterpret_cast<float*>(base + w.v_off);
 }
 
+// Workspace of hla_prefill_backward: the forward's transitions, route outputs and routed
+// states, the gradients handed between the passes, then the workspaces of the route, the
+// chunk backward and the composition backward.
+struct PrefillBwdWs {
+  int64_t at_off, bc_off, gates_off, mask_off, aidx_off, acnt_off, sr_off, dsr_off, dat_off, dbc_off, dg_off,
+      qbar_off, dqbar_off, dkr_off, route_off, chunk_off, comp_off, total;
+};
+PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d) {
+  const int64_t N = n_chunks(d), BH = d->B * d->H, BHN = BH * N, e = dtype_bytes(d->dtype);
+  PrefillBwdWs w;
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = o;
+    o += round_up(bytes, 256);
+    return at;
+  };
+  w.at_off = take(BHN * d->dk * d->dk * e);
+  w.bc_off = take(BHN * d->dk * d->dv * e);
+  w.gates_off = take(BH * N * N * 4);
+  w.mask_off = take(BH * N * N);
+  w.aidx_off = take(BH * N * N * 4);
+  w.acnt_off = take(BHN * 4);
+  w.sr_off = take(BHN * d->dk * d->dv * 4);
+  w.dsr_off = take(BHN * d->dk * d->dv * 4);
+  w.dat_off = take(BHN * d->dk * d->dk * 4);
+  w.dbc_off = take(BHN * d->dk * d->dv * 4);
+  w.dg_off = take(BH * N * N * 4);
+  w.qbar_off = take(BHN * d->dk * 4);
+  w.dqbar_off = take(BHN * d->dk * 4);
+  w.dkr_off = take(d->B * d->T * d->H * d->dk * 4);
+  w.route_off = take(route_ws(d));
+  w.chunk_off = take(chunk_bwd_ws(d).total);
+  w.comp_off = take(compose_bwd_ws(d).total);
+  w.total = o;
+  return w;
+}
+
 hla_status_t hip_status(hipError_t e) { return e == hipSuccess ? HLA_OK : HLA_ERR_HIP; }
 
 // One chunk pass of either recurrence: transitions (want_ab) or outputs from chunk_init.
@@ -273,6 +310,10 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
     case HLA_FN_CHUNK_BACKWARD:
       if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
       *out = (size_t)chunk_bwd_ws(d).total;
+      return HLA_OK;
+    case HLA_FN_PREFILL_BACKWARD:
+      if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
+      *out = (size_t)prefill_bwd_ws(d).total;
       return HLA_OK;
     default: return HLA_ERR_UNSUPPORTED;
   }
@@ -425,7 +466,84 @@ hla_status_t hla_chunk_backward(const hla_dims_t* d, const void* q, const void* 
   a.chunk_init = chunk_init; a.dO = dO; a.dAt = dAt; a.dBc = dBc; a.dchunk_init = dchunk_init;
   set_chunk_bwd_ws(a, w, ws);
   a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dalpha = dalpha;
-  return hip_status(hla::launch_chunk_backward(a, d->dtype, d->dk, d->dv, stream));
+  const int stages = (have_out ? hla::kChunkBwdOut : 0) | (have_map ? hla::kChunkBwdMap : 0) | hla::kChunkBwdFinalize;
+  return hip_status(hla::launch_chunk_backward(a, d->dtype, d->dk, d->dv, stages, stream));
+}
+
+hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                                  const float* beta, const float* alpha, const float* S0, const float* gates_in,
+                                  float tau, const float* dO, float* dq, float* dk, float* dv, float* dbeta,
+                                  float* dalpha, float* dS0, float* dgates, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !beta || !alpha || !dO || !dq || !dk || !dv || !dbeta || !dalpha) return HLA_ERR_NULL_ARG;
+  if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
+  if (!all_aligned(q, k, v, S0, dS0, ws) || !all_aligned4(beta, alpha, gates_in, dO, dq, dk, dv, dbeta, dalpha, dgates))
+    return HLA_ERR_ALIGN;
+  const PrefillBwdWs w = prefill_bwd_ws(d);
+  if (!ws || (int64_t)ws_bytes < w.total) return HLA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  const int32_t N = (int32_t)n_chunks(d);
+  auto at = [&](int64_t off) { return static_cast<void*>(base + off); };
+  auto fat = [&](int64_t off) { return reinterpret_cast<float*>(base + off); };
+  // 1. forward: chunk maps, gates and routed states
+  hla::ChunkArgs c{};
+  c.q = q; c.k = k; c.v = v; c.beta = beta; c.alpha = alpha;
+  c.B = d->B; c.T = d->T; c.H = d->H; c.ld_T = d->ld_T; c.N = N;
+  c.At = at(w.at_off); c.Bc = at(w.bc_off);
+  hipError_t e = hla::launch_chunk(c, d->dtype, d->dk, d->dv, true, false, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  hla::RouteArgs r{};
+  r.q = q; r.reps = k; r.n_rep = kPiece; r.ld_R = d->ld_T; r.At = c.At; r.Bc = c.Bc; r.S0 = S0;
+  r.gates_in = gates_in; r.tau = tau; r.gates = fat(w.gates_off);
+  r.mask = reinterpret_cast<uint8_t*>(base + w.mask_off);
+  r.active_idx = reinterpret_cast<int32_t*>(base + w.aidx_off);
+  r.active_cnt = reinterpret_cast<int32_t*>(base + w.acnt_off);
+  r.n_eff = nullptr; r.S_routed = fat(w.sr_off);
+  r.qbar = fat(w.route_off); r.At_prep = base + w.route_off + route_qbar_bytes(d);
+  r.B = d->B; r.T = d->T; r.H = d->H; r.ld_T = d->ld_T; r.N = N; r.C = d->C;
+  e = hla::launch_route(r, d->dtype, d->dk, d->dv, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  // 2. outputs part of the chunk backward: dS~ and the chunk-local partial sums
+  hla::ChunkBwdArgs cb{};
+  cb.q = q; cb.k = k; cb.v = v; cb.beta = beta; cb.alpha = alpha;
+  cb.B = d->B; cb.T = d->T; cb.H = d->H; cb.ld_T = d->ld_T; cb.N = N;
+  cb.have_out = 1; cb.have_map = 1;
+  cb.chunk_init = r.S_routed; cb.dO = dO; cb.dchunk_init = fat(w.dsr_off);
+  cb.dAt = fat(w.dat_off); cb.dBc = fat(w.dbc_off);
+  set_chunk_bwd_ws(cb, chunk_bwd_ws(d), at(w.chunk_off));
+  cb.dq = dq; cb.dk = dk; cb.dv = dv; cb.dbeta = dbeta; cb.dalpha = dalpha;
+  e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdOut, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  // 3. composition backward: dAt, dBc, dgates, dS0
+  float* dg = dgates ? dgates : fat(w.dg_off);
+  const ComposeBwdWs cw = compose_bwd_ws(d);
+  char* cbase = base + w.comp_off;
+  hla::ComposeBwdArgs m{};
+  m.At = c.At; m.Bc = c.Bc; m.gates = r.gates; m.mask = r.mask; m.S0 = S0; m.dS = cb.dchunk_init;
+  m.dAt = fat(w.dat_off); m.dBc = fat(w.dbc_off); m.dgates = dg; m.dS0 = dS0; m.S_routed = nullptr;
+  m.AtT = cbase + cw.att_off; m.Msave = cbase + cw.ms_off; m.Lsave = cbase + cw.ls_off;
+  m.dgp = reinterpret_cast<float*>(cbase + cw.dgp_off); m.lam_end = reinterpret_cast<float*>(cbase + cw.le_off);
+  m.B = d->B; m.H = d->H; m.N = N;
+  e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  // 4. maps part of the chunk backward
+  e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdMap, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  // 5. router (computed gates only), then the per-token sums
+  if (!gates_in && N > 1) {
+    hla::RouterBwdArgs rb{};
+    rb.q = q; rb.k = k; rb.gates = r.gates; rb.dgates = dg;
+    rb.qbar = fat(w.qbar_off); rb.dqbar = fat(w.dqbar_off); rb.dk_router = fat(w.dkr_off);
+    rb.B = d->B; rb.T = d->T; rb.H = d->H; rb.ld_T = d->ld_T; rb.N = N;
+    e = hla::launch_router_backward(rb, d->dtype, d->dk, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+    cb.dqbar = rb.dqbar;
+    cb.dk_router = rb.dk_router;
+  }
+  return hip_status(hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdFinalize, stream));
 }
 
 // Shared checks of the two decode entry points (everything but the per-token gates).

@@ -301,19 +301,19 @@ __global__ __launch_bounds__(256) void chunk_bwd_finalize_kernel(ChunkBwdArgs a)
 }
 
 template <class T, int DK, int DV>
-static hipError_t launch_chunk_bwd_t(const ChunkBwdArgs& a, hipStream_t s) {
+static hipError_t launch_chunk_bwd_t(const ChunkBwdArgs& a, int stages, hipStream_t s) {
   const int64_t BHN = a.B * a.H * (int64_t)a.N;
   constexpr int NT = chunk_bwd_threads<DK>();
-  {
+  if (stages & (kChunkBwdOut | kChunkBwdMap)) {
     TimedLaunch tl(HLA_KERNEL_BWD_CHUNK, s);
-    if (a.have_out)
+    if (stages & kChunkBwdOut)
       hipLaunchKernelGGL((chunk_bwd_kernel<T, DK, DV, true>), dim3((unsigned)(BHN * (DV / 32))), dim3(NT), 0, s, a);
-    if (a.have_map)
+    if (stages & kChunkBwdMap)
       hipLaunchKernelGGL((chunk_bwd_kernel<T, DK, DV, false>), dim3((unsigned)(BHN * ((DK + DV) / 32))), dim3(NT), 0,
                          s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !(stages & kChunkBwdFinalize)) return e;
   constexpr int W = DK > DV ? DK : DV;
   const int64_t total = a.B * a.T * a.H * W;
   hipLaunchKernelGGL((chunk_bwd_finalize_kernel<DK, DV>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
@@ -321,15 +321,15 @@ static hipError_t launch_chunk_bwd_t(const ChunkBwdArgs& a, hipStream_t s) {
 }
 
 template <class T>
-static hipError_t launch_chunk_bwd_d(const ChunkBwdArgs& a, int dk, int dv, hipStream_t s) {
-  if (dk == 64 && dv == 64) return launch_chunk_bwd_t<T, 64, 64>(a, s);
-  if (dk == 64 && dv == 128) return launch_chunk_bwd_t<T, 64, 128>(a, s);
-  if (dk == 128 && dv == 64) return launch_chunk_bwd_t<T, 128, 64>(a, s);
-  return launch_chunk_bwd_t<T, 128, 128>(a, s);
+static hipError_t launch_chunk_bwd_d(const ChunkBwdArgs& a, int dk, int dv, int stages, hipStream_t s) {
+  if (dk == 64 && dv == 64) return launch_chunk_bwd_t<T, 64, 64>(a, stages, s);
+  if (dk == 64 && dv == 128) return launch_chunk_bwd_t<T, 64, 128>(a, stages, s);
+  if (dk == 128 && dv == 64) return launch_chunk_bwd_t<T, 128, 64>(a, stages, s);
+  return launch_chunk_bwd_t<T, 128, 128>(a, stages, s);
 }
 
-hipError_t launch_chunk_backward(const ChunkBwdArgs& a, int dtype, int dk, int dv, hipStream_t s) {
-  return dtype == 1 ? launch_chunk_bwd_d<bf16>(a, dk, dv, s) : launch_chunk_bwd_d<float>(a, dk, dv, s);
+hipError_t launch_chunk_backward(const ChunkBwdArgs& a, int dtype, int dk, int dv, int stages, hipStream_t s) {
+  return dtype == 1 ? launch_chunk_bwd_d<bf16>(a, dk, dv, stages, s) : launch_chunk_bwd_d<float>(a, dk, dv, stages, s);
 }
 
 }  // namespace hla

@@ -184,7 +184,23 @@ struct ChunkBwdArgs {
   float* dbeta;             // out [B,T,H]
   float* dalpha;            // out [B,T,H]
 };
-// Backward of the chunk outputs and / or the chunk maps, then the per-token sums.
-hipError_t launch_chunk_backward(const ChunkBwdArgs& a, int dtype, int dk, int dv, hipStream_t s);
+// Backward of the chunk outputs and / or the chunk maps, then the per-token sums.  `stages`
+// picks what is launched: 1 the outputs part, 2 the maps part, 4 the finalize pass.
+constexpr int kChunkBwdOut = 1, kChunkBwdMap = 2, kChunkBwdFinalize = 4;
+hipError_t launch_chunk_backward(const ChunkBwdArgs& a, int dtype, int dk, int dv, int stages, hipStream_t s);
+
+struct RouterBwdArgs {
+  const void* q;         // [B,ld_T,H,dk] (dtype)
+  const void* k;         // [B,ld_T,H,dk]: the representatives (raw keys, n_rep = 64)
+  const float* gates;    // [B,H,N,N]
+  const float* dgates;   // [B,H,N,N] gradient of the gates (zero for skipped pairs)
+  float* qbar;           // workspace [B,H,N,dk]
+  float* dqbar;          // out [B,H,N,dk]
+  float* dk_router;      // out [B,T,H,dk]
+  int64_t B, T, H, ld_T;
+  int32_t N;
+};
+// Backward of the router gates to the query-chunk means and the keys.
+hipError_t launch_router_backward(const RouterBwdArgs& a, int dtype, int dk, hipStream_t s);
 
 }  // namespace hla

@@ -58,6 +58,8 @@ _SIGS = {
                                               ctypes.c_size_t, _P]),
     "hla_chunk_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                             _P, _P, _P, ctypes.c_size_t, _P]),
+    "hla_prefill_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
+                                              _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "hla_timing_enable": (ctypes.c_int32, [ctypes.c_int32]),
     "hla_timing_read": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "hla_gdn_decode": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -407,6 +409,34 @@ def chunk_backward(q, k, v, beta, alpha, chunk_init=None, dO=None, dAt=None, dBc
                                         _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dalpha"]),
                                         _ptr(out["dchunk_init"]), _ptr(ws), 0 if ws is None else ws.numel(),
                                         _stream(dev)), "hla_chunk_backward")
+    return out
+
+
+def prefill_backward(q, k, v, beta, alpha, dO, tau=1e-3, gates_in=None, S0=None, want_dS0=True, want_dgates=True,
+                     ws=None):
+    """Gradients of the routed prefill (raw-key representatives, 64-token chunks) for the
+    upstream gradient dO [B, T, H, dv] float32.  Returns dict(dq, dk, dv, dbeta, dalpha,
+    dS0, dgates), float32 (dS0 / dgates None unless wanted)."""
+    d = _inputs(k, v, beta, alpha, q=q)
+    B, T, H, dk, dv = d.B, d.T, d.H, d.dk, d.dv
+    N = math.ceil(T / CHUNK)
+    dev = k.device
+    _need(dO, (B, T, H, dv), torch.float32, "dO")
+    _need(S0, (B, H, dk, dv), torch.float32, "S0")
+    _need(gates_in, (B, H, N, N), torch.float32, "gates_in")
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
+               dv=torch.empty((B, T, H, dv), **f32), dbeta=torch.empty((B, T, H), **f32),
+               dalpha=torch.empty((B, T, H), **f32),
+               dS0=torch.empty((B, H, dk, dv), **f32) if want_dS0 else None,
+               dgates=torch.empty((B, H, N, N), **f32) if want_dgates else None)
+    if ws is None:
+        ws = _workspace(workspace_bytes(FN_PREFILL_BACKWARD, d), dev)
+    _check(library().hla_prefill_backward(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+                                          _ptr(S0), _ptr(gates_in), ctypes.c_float(tau), _ptr(dO), _ptr(out["dq"]),
+                                          _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dalpha"]),
+                                          _ptr(out["dS0"]), _ptr(out["dgates"]), _ptr(ws),
+                                          0 if ws is None else ws.numel(), _stream(dev)), "hla_prefill_backward")
     return out
 
 

@@ -352,6 +352,36 @@ hla_status_t hla_chunk_backward(const hla_dims_t* d, const void* q, const void* 
                                 float* dk, float* dv, float* dbeta, float* dalpha,
                                 float* dchunk_init, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * hla_prefill_backward -- gradients of the routed prefill (raw-key representatives, C = 64).
+ * Given dO = dL/do for the outputs of hla_chunk_transitions + hla_route_mix (reps = k,
+ * n_rep = 64) + hla_gdn_prefill with chunk_init = S_routed, the call recomputes that
+ * forward and returns dL/d(q, k, v, beta, alpha), dL/dS0 and dL/dg for the history gates:
+ *   the outputs part of hla_chunk_backward (dS~ and the chunk-local gradients);
+ *   hla_compose_backward (dAt, dBc, dgates, dS0);
+ *   the maps part of hla_chunk_backward;
+ *   the router ([HLA] Overview, Methodology paragraph 2): dl_ij = dg_ij g_ij (1 - g_ij),
+ *     p_ijr = softmax over chunk j's keys of qbar_i . k_r / sqrt(dk),
+ *     dqbar_i = sum_j dl_ij sum_r p_ijr k_r / sqrt(dk) (spread as dqbar_i / n_i over chunk
+ *     i's tokens), dk_r += sum_i dl_ij p_ijr qbar_i / sqrt(dk);
+ * then the per-token sums.  The skip mask is a step function of g: a skipped pair passes
+ * no gradient.  With gates_in the gates are the caller's: dgates is the gradient w.r.t.
+ * them and the router takes no part.
+ *   q, k, v, beta, alpha, S0, gates_in, tau: as for the forward calls.
+ *   dO [B, T, H, dv] float32.
+ *   dq, dk [B, T, H, dk], dv [B, T, H, dv], dbeta, dalpha [B, T, H]: float32 out.
+ *   dS0 [B, H, dk, dv] float32 out or NULL;  dgates [B, H, N, N] float32 out or NULL.
+ *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_PREFILL_BACKWARD)
+ *              bytes; it holds the composition backward's per-pair states, so it grows as
+ *              N^2 dk dv per (b, h).
+ * Errors: HLA_ERR_UNSUPPORTED (C != 64) and as hla_gdn_prefill.
+ */
+hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                                  const float* beta, const float* alpha, const float* S0,
+                                  const float* gates_in, float tau, const float* dO, float* dq,
+                                  float* dk, float* dv, float* dbeta, float* dalpha, float* dS0,
+                                  float* dgates, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes that entry point `fn` needs for dims `d`; n_rep is the number of
  * representatives per chunk for HLA_FN_CHUNK_REPS (C / window; it must divide C) and is
  * ignored otherwise.  `out` is a host pointer. */

@@ -223,3 +223,103 @@ def test_gdn2_validation(lib):
     assert pre(ctypes.byref(d), P, P, P, P, P, P, P, P, P, None, None, 0, None) == UNSUPPORTED  # routed with S0
     assert pre(ctypes.byref(d), P, P, P, P, P, P, None, None, P, P, P, need - 1, None) == WORKSPACE
     assert pre(ctypes.byref(d), P, P, P, P, None, P, None, None, P, P, P, need, None) == NULL_ARG
+
+
+def _r(x):
+    return (x + 255) // 256 * 256
+
+
+def test_backward_workspace_sizes(lib):
+    d = dims(B=2, T=130, H=3, dk=128, dv=64, dtype=1)  # N = 3 chunks, 3 pairs per (b, h)
+    BH, N, P_ = 6, 3, 3
+    comp = (_r(BH * N * 128 * 128 * 2) + 2 * _r(BH * P_ * 128 * 64 * 2) + _r(BH * N * N * 2 * 4)
+            + _r(BH * N * 128 * 64 * 4))
+    assert hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD, d) == comp
+    BHN, nb_out, nb_all = BH * N, 2, 2 + 6
+    chunk = (_r(BHN * nb_all * 64 * 128 * 4) + _r(BHN * nb_out * 64 * 128 * 4) + _r(BHN * nb_all * 64 * 2 * 4)
+             + _r(BHN * 2 * 64 * 64 * 4))
+    assert hla.workspace_bytes(hla.FN_CHUNK_BACKWARD, d) == chunk
+    # the prefill backward holds the composition's per-pair states: it grows as N^2
+    pb = hla.workspace_bytes(hla.FN_PREFILL_BACKWARD, d)
+    assert pb > comp + chunk
+    d4 = dims(B=2, T=130 + 3 * 64, H=3, dk=128, dv=64, dtype=1)  # N = 6: 15 pairs
+    assert hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD, d4) - hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD, d) >= \
+        2 * BH * 12 * 128 * 64 * 2
+    out = ctypes.c_size_t()
+    for fn in (hla.FN_CHUNK_BACKWARD, hla.FN_PREFILL_BACKWARD):
+        assert lib.hla_workspace_bytes(fn, ctypes.byref(dims(C=128)), 0, ctypes.byref(out)) == UNSUPPORTED
+
+
+def test_compose_backward_validation(lib):
+    d = dims()
+    f = lib.hla_compose_backward
+    need = hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD, d)
+    # (d, At, Bc, gates, mask, S0, dS, dAt, dBc, dgates, dS0, S_routed, ws, ws_bytes, stream)
+    req = [0, 1, 2, 3, 5, 6, 7, 8]  # positions of required pointers among the 11
+    for i in req:
+        args = [P] * 11
+        args[i] = None
+        assert f(ctypes.byref(d), *args, P, need, None) == NULL_ARG, i
+    args = [P] * 11
+    assert f(ctypes.byref(d), *args, P, need - 1, None) == WORKSPACE
+    assert f(ctypes.byref(d), *args, None, 0, None) == WORKSPACE
+    bad = list(args)
+    bad[0] = PU
+    assert f(ctypes.byref(d), *bad, P, need, None) == ALIGN
+    bad = list(args)
+    bad[2] = P + 2  # gates need 4 bytes
+    assert f(ctypes.byref(d), *bad, P, need, None) == ALIGN
+    assert f(ctypes.byref(dims(dtype=2)), *args, P, need, None) == BAD_DTYPE
+
+
+def test_chunk_backward_validation(lib):
+    d = dims()
+    f = lib.hla_chunk_backward
+    need = hla.workspace_bytes(hla.FN_CHUNK_BACKWARD, d)
+    # (d, q, k, v, beta, alpha, chunk_init, dO, dAt, dBc, dq, dk, dv, dbeta, dalpha, dinit, ws, ws_bytes, s)
+    full = [P] * 15
+    assert f(ctypes.byref(d), *full, None, 0, None) == WORKSPACE
+    neither = list(full)
+    neither[5:9] = [None] * 4
+    assert f(ctypes.byref(d), *neither, P, need, None) == NULL_ARG   # no part asked for
+    half = list(full)
+    half[6] = None                                                   # chunk_init without dO
+    assert f(ctypes.byref(d), *half, P, need, None) == NULL_ARG
+    half = list(full)
+    half[8] = None                                                   # dAt without dBc
+    assert f(ctypes.byref(d), *half, P, need, None) == NULL_ARG
+    outs_only_map = list(full)
+    outs_only_map[5] = outs_only_map[6] = None
+    outs_only_map[0] = None                                          # q unused by the map part
+    outs_only_map[14] = None                                         # no dchunk_init without outputs
+    assert f(ctypes.byref(d), *outs_only_map, P, need - 1, None) == WORKSPACE
+    for i in range(9, 14):
+        a = list(full)
+        a[i] = None
+        assert f(ctypes.byref(d), *a, P, need, None) == NULL_ARG, i
+    a = list(full)
+    a[3] = P + 2
+    assert f(ctypes.byref(d), *a, P, need, None) == ALIGN
+    assert f(ctypes.byref(dims(C=128)), *full, P, need, None) == UNSUPPORTED
+
+
+def test_prefill_backward_validation(lib):
+    d = dims()
+    f = lib.hla_prefill_backward
+    need = hla.workspace_bytes(hla.FN_PREFILL_BACKWARD, d)
+    # (d, q, k, v, beta, alpha, S0, gates_in, tau, dO, dq, dk, dv, dbeta, dalpha, dS0, dgates, ws, ws_bytes, s)
+    def call(args, tau=1e-3, ws=P, nb=need, dd=d):
+        return f(ctypes.byref(dd), *args[:7], ctypes.c_float(tau), *args[7:], ws, nb, None)
+    full = [P] * 16
+    for i in (0, 1, 2, 3, 4, 7, 8, 9, 10, 11, 12):
+        a = list(full)
+        a[i] = None
+        assert call(a) == NULL_ARG, i
+    opt = list(full)
+    opt[5] = opt[6] = opt[14] = opt[15] = None  # S0, gates_in, dS0, dgates are optional
+    assert call(opt, nb=need - 1) == WORKSPACE
+    assert call(full, tau=float("nan")) == BAD_SHAPE
+    assert call(full, dd=dims(C=256)) == UNSUPPORTED
+    a = list(full)
+    a[0] = PU
+    assert call(a) == ALIGN

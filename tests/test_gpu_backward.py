@@ -106,3 +106,63 @@ def test_chunk_backward(case, parts):
                 assert np.all(host(g["dq"])[b, :, hh] == 0.0)
             for n, key in (("dk", "dk"), ("dv", "dv"), ("dbeta", "dbeta"), ("dalpha", "dalpha")):
                 assert_close(host(g[key])[b, :, hh], ref[n], dtype, n)
+
+
+PREFILL_CASES = [("f32", 64, 128, 4 * C + 9), ("bf16", 128, 128, 5 * C - 3), ("bf16", 64, 64, 3 * C)]
+
+
+def _gap_tau(g, hist):
+    vals = np.sort(g[hist])
+    gaps = np.diff(vals)
+    i = int(np.argmax(gaps))
+    return float(0.5 * (vals[i] + vals[i + 1]))
+
+
+@pytest.mark.parametrize("gates", ["computed", "computed_gap", "caller"])
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[f"{c[0]}-dk{c[1]}-dv{c[2]}-T{c[3]}" for c in PREFILL_CASES])
+def test_prefill_backward(case, gates):
+    """Whole routed-prefill backward against the one-graph autograd oracle."""
+    dtype, dk, dv, T = case
+    note(f"prefill backward {case} {gates}")
+    B, H = 1, 2
+    N = -(-T // C)
+    x = inputs.gen_tokens(B, T, H, dk, dv, dtype=dtype, seed=51, alpha_mode="slow")
+    q, k, v, beta, alpha = (dev(x.q, dtype), dev(x.k, dtype), dev(x.v, dtype), f32(x.beta), f32(x.alpha))
+    S0 = inputs.gen_state(B, H, dk, dv, seed=52)
+    dO = inputs.gen_cotangent((B, T, H, dv), seed=53, name="dO")
+    hist = np.tril(np.ones((N, N), bool), -1)
+    G = None
+    if gates == "caller":
+        G = inputs.gen_gates(B, H, N, seed=54, mode="uniform")
+        taus = [0.3] * H
+    elif gates == "computed":
+        taus = [1e-3] * H
+    else:
+        taus = []
+        for hh in range(H):
+            g = oracle.router_gates(_tok(x, "q", 0, hh), _tok(x, "k", 0, hh), C, C, 0.0)["gates"]
+            taus.append(_gap_tau(g, hist))
+    # one tau per call: the heads share it, so use the first head's and check the masks agree
+    tau = taus[0]
+    skipped = 0
+    g = hla().prefill_backward(q, k, v, beta, alpha, f32(dO), tau=tau, gates_in=None if G is None else f32(G),
+                               S0=f32(S0))
+    torch.cuda.synchronize()
+    for hh in range(H):
+        qq, kk, vv, bb, aa = (_tok(x, n, 0, hh) for n in ("q", "k", "v", "beta", "alpha"))
+        ref = oracle.hla_prefill_backward(qq, kk, vv, bb, aa, C, tau, dO[0, :, hh].astype(np.float64),
+                                          S0=S0[0, hh].astype(np.float64).T,
+                                          gates_in=None if G is None else G[0, hh].astype(np.float64))
+        if gates == "computed_gap" and hh > 0:
+            gg = oracle.router_gates(qq, kk, C, C, 0.0)["gates"][hist]
+            if np.min(np.abs(gg - tau)) < 1e-4:
+                continue  # this head has a gate too close to the shared threshold
+        for n in ("dq", "dk", "dv", "dbeta", "dalpha"):
+            assert_close(host(g[n])[0, :, hh], ref[n], dtype, n)
+        assert_close(host(g["dS0"])[0, hh], ref["dS0"].T, dtype, "dS0")
+        dgg = host(g["dgates"])[0, hh]
+        assert_close(dgg, ref["dgates"], dtype, "dgates")
+        assert np.all(dgg[~ref["mask"]] == 0.0)
+        skipped += int(hist.sum() - ref["mask"][hist].sum())
+    if gates != "computed":
+        assert skipped > 0
