@@ -95,23 +95,35 @@ int64_t reps_ws(const hla_dims_t* d, int32_t n_rep) {
   return round_up(d->B * d->H * n_chunks(d) * n_rep * d->dk * 4, 256);
 }
 
-// Workspace of hla_compose_backward: At^T, the states in front of every history step and
-// g lambda of it (N (N - 1) / 2 slots per (b, h), dtype), per-wave gate-gradient parts and
-// the final lambda of every chain.
+// Workspace of hla_compose_backward: (At - I) and its transpose in the fragment order, Bc in
+// the lane order, then per active pair (N (N - 1) / 2 slots per (b, h), dtype) the state in
+// front of the step, D_j and g lambda, then per-wave gate-gradient parts and the final
+// lambda of every chain.
 struct ComposeBwdWs {
-  int64_t att_off, ms_off, ls_off, dgp_off, le_off, total;
+  int64_t ap_off, apt_off, bl_off, ms_off, ds_off, ls_off, dgp_off, le_off, total;
 };
 ComposeBwdWs compose_bwd_ws(const hla_dims_t* d) {
   const int64_t N = n_chunks(d), BH = d->B * d->H, e = dtype_bytes(d->dtype);
   const int64_t P = N * (N - 1) / 2;
+  const int64_t at = round_up(BH * N * d->dk * d->dk * e, 256), pr = round_up(BH * P * d->dk * d->dv * e, 256);
   ComposeBwdWs w;
-  w.att_off = 0;
-  w.ms_off = round_up(BH * N * d->dk * d->dk * e, 256);
-  w.ls_off = w.ms_off + round_up(BH * P * d->dk * d->dv * e, 256);
-  w.dgp_off = w.ls_off + round_up(BH * P * d->dk * d->dv * e, 256);
+  w.ap_off = 0;
+  w.apt_off = at;
+  w.bl_off = 2 * at;
+  w.ms_off = w.bl_off + round_up(BH * N * d->dk * d->dv * e, 256);
+  w.ds_off = w.ms_off + pr;
+  w.ls_off = w.ds_off + pr;
+  w.dgp_off = w.ls_off + pr;
   w.le_off = w.dgp_off + round_up(BH * N * N * (d->dv / 32) * 4, 256);
   w.total = w.le_off + round_up(BH * N * d->dk * d->dv * 4, 256);
   return w;
+}
+
+void set_compose_bwd_ws(hla::ComposeBwdArgs& a, const ComposeBwdWs& w, void* ws) {
+  char* base = static_cast<char*>(ws);
+  a.Ap = base + w.ap_off; a.ApT = base + w.apt_off; a.Bl = base + w.bl_off;
+  a.Msave = base + w.ms_off; a.Dsave = base + w.ds_off; a.Lsave = base + w.ls_off;
+  a.dgp = reinterpret_cast<float*>(base + w.dgp_off); a.lam_end = reinterpret_cast<float*>(base + w.le_off);
 }
 
 // Workspace of hla_chunk_backward: per-workgroup partial sums of the per-token gradients.
@@ -432,12 +444,10 @@ hla_status_t hla_compose_backward(const hla_dims_t* d, const void* At, const voi
     return HLA_ERR_ALIGN;
   const ComposeBwdWs w = compose_bwd_ws(d);
   if (!ws || (int64_t)ws_bytes < w.total) return HLA_ERR_WORKSPACE;
-  char* base = static_cast<char*>(ws);
   hla::ComposeBwdArgs a{};
   a.At = At; a.Bc = Bc; a.gates = gates; a.mask = mask; a.S0 = S0; a.dS = dS_routed;
   a.dAt = dAt; a.dBc = dBc; a.dgates = dgates; a.dS0 = dS0; a.S_routed = S_routed;
-  a.AtT = base + w.att_off; a.Msave = base + w.ms_off; a.Lsave = base + w.ls_off;
-  a.dgp = reinterpret_cast<float*>(base + w.dgp_off); a.lam_end = reinterpret_cast<float*>(base + w.le_off);
+  set_compose_bwd_ws(a, w, ws);
   a.B = d->B; a.H = d->H; a.N = (int32_t)n_chunks(d);
   return hip_status(hla::launch_compose_backward(a, d->dtype, d->dk, d->dv, stream));
 }
@@ -519,13 +529,10 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   if (e != hipSuccess) return HLA_ERR_HIP;
   // 3. composition backward: dAt, dBc, dgates, dS0
   float* dg = dgates ? dgates : fat(w.dg_off);
-  const ComposeBwdWs cw = compose_bwd_ws(d);
-  char* cbase = base + w.comp_off;
   hla::ComposeBwdArgs m{};
   m.At = c.At; m.Bc = c.Bc; m.gates = r.gates; m.mask = r.mask; m.S0 = S0; m.dS = cb.dchunk_init;
   m.dAt = fat(w.dat_off); m.dBc = fat(w.dbc_off); m.dgates = dg; m.dS0 = dS0; m.S_routed = nullptr;
-  m.AtT = cbase + cw.att_off; m.Msave = cbase + cw.ms_off; m.Lsave = cbase + cw.ls_off;
-  m.dgp = reinterpret_cast<float*>(cbase + cw.dgp_off); m.lam_end = reinterpret_cast<float*>(cbase + cw.le_off);
+  set_compose_bwd_ws(m, compose_bwd_ws(d), at(w.comp_off));
   m.B = d->B; m.H = d->H; m.N = N;
   e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;

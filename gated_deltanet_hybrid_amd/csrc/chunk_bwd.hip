@@ -16,7 +16,8 @@
 //
 // Layout: one workgroup per (b, h, chunk, block of 32 columns); a thread holds 8 rows of one
 // column (the dk / 8 threads of a column are adjacent lanes, so a dot product is a sum over
-// 8 rows plus log2(dk / 8) lane exchanges).  The reverse needs the state in front of every
+// 8 rows plus log2(dk / 8) DPP lane moves, which keeps the token recurrence's critical path
+// short).  The reverse needs the state in front of every
 // token: a forward pass keeps the state in front of every 8-token block in registers (8
 // checkpoints x 8 rows per thread), and each block is replayed from its checkpoint before
 // it is reversed.
@@ -99,9 +100,7 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < kRPT; ++i) s = fmaf(vec[r0 + i], x[i], s);
-#pragma unroll
-    for (int m = 1; m < RG; m <<= 1) s += __shfl_xor(s, m, 64);
-    return s;
+    return group_sum<RG>(s);  // the column's RG threads are one aligned lane group
   };
 
   // ---- forward, keeping the state in front of every 8-token block

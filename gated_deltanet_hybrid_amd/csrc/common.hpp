@@ -137,6 +137,27 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Cross-lane move inside a 16-lane row (DPP), for sums over small lane groups.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+// Sum over aligned groups of G consecutive lanes (G = 2, 4, 8 or 16), every lane of the group
+// receiving it: quad permutations swap lanes 1 and 2 apart, a half-row mirror pairs the two
+// quads of an 8-lane half, and row rotations by 4 and 8 add the other quads of a 16-lane row.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group of 2, 4, 8 or 16 lanes");
+  x += dpp_f<0xB1>(x);  // quad_perm [1, 0, 3, 2]
+  if constexpr (G >= 4) x += dpp_f<0x4E>(x);  // quad_perm [2, 3, 0, 1]
+  if constexpr (G == 8) x += dpp_f<0x141>(x);  // row_half_mirror
+  if constexpr (G == 16) {
+    x += dpp_f<0x124>(x);  // row_ror 4
+    x += dpp_f<0x128>(x);  // row_ror 8
+  }
+  return x;
+}
+
 __device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + __expf(-x)); }
 
 // 16-byte global -> LDS copy of `bytes` (multiple of 16) by the whole block.

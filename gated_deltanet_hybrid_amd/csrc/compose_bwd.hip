@@ -13,12 +13,15 @@
 // and dS0 sums the final lambda of every chain.  Skipped pairs pass lambda through.
 //
 // Passes (one chain per workgroup in the first two, one wave per 32 state columns):
-//   1. compose_save_kernel runs every chain forward and stores the state in front of each
-//      active step (M_{j-1}) in the workspace;
+//   0. prep_bwd_kernel writes (At_j - I) and its transpose with every 16-wide k block in the
+//      order the MFMA fragments read it (one 16-byte load per fragment), and Bc_j in the
+//      accumulator's lane order;
+//   1. compose_save_kernel runs every chain forward: per active step it forms
+//      D_j = (At_j - I) M_{j-1} + Bc_j on the matrix cores, stores M_{j-1} (row-major, for
+//      pass 3) and D_j (in the accumulator's lane order, for pass 2), and sets M += g D_j;
 //   2. compose_adjoint_kernel runs every chain backward: per active step it stores
-//      g lambda_j, forms Y = (At_j - I)^T lambda_j on the matrix cores, takes the gate
-//      gradient as <Y, M_{j-1}> + <lambda_j, Bc_j> (per wave, summed over its 32 columns),
-//      and updates lambda += g Y;
+//      g lambda_j, takes the gate gradient <lambda_j, D_j> (per wave, summed over its 32
+//      columns) and updates lambda += (At_j - I)^T (g lambda) on the matrix cores;
 //   3. compose_grad_reduce_kernel, one workgroup per history chunk j, sums over the query
 //      chunks i > j: dAt_j = sum_i (g lambda)_i M_i^T on the matrix cores, dBc_j = sum_i
 //      (g lambda)_i, and the gate gradients of column j;
@@ -34,37 +37,111 @@ namespace {
 
 __device__ __forceinline__ int64_t pair_index(int i, int j) { return (int64_t)i * (i - 1) / 2 + j; }
 
-// A fragment of (X - I) for row tile rt and k-step ks, X row-major [DK][DK], in the
-// clayout k order that matches from_acc B fragments.
+// A fragment of row tile rt, k-step ks from a prepared (X - I) image (prep_bwd_kernel):
+// bf16 rows hold every 16-wide k block in the clayout slot order, so the fragment is one
+// 16-byte load; float32 rows are plain and the fragment is the clayout element.
 template <class T, int DK>
-__device__ __forceinline__ typename Mma<T>::Frag minus_eye_frag(const T* X, int rt, int ks, int hh, int c32) {
-  const int m = rt * 32 + c32;
-  typename Mma<T>::Frag f = Mma<T>::load_clayout(X + (int64_t)m * DK, ks, hh);
+__device__ __forceinline__ typename Mma<T>::Frag prep_frag(const T* Xp, int rt, int ks, int hh, int c32) {
+  const T* row = Xp + (int64_t)(rt * 32 + c32) * DK;
+  if constexpr (sizeof(T) == 2)
+    return *reinterpret_cast<const bf16x8*>(row + ks * 16 + hh * 8);
+  else
+    return Mma<T>::load_clayout(row, ks, hh);
+}
+
+// Offset of element e of lane `lane` in the accumulator-lane-order image of one dk x dv
+// matrix: [dv/32 column tiles][dk/32 row tiles][64 lanes][16].
+template <int DK>
+__device__ __forceinline__ int64_t lane_off(int ct, int rt, int lane) {
+  return ((int64_t)(ct * (DK / 32) + rt) * 64 + lane) * 16;
+}
+
+// 16 values of one accumulator tile in the lane's order, in T.
+template <class T>
+__device__ __forceinline__ void store16(T* dst, const f32x16& v, float scale) {
   if constexpr (sizeof(T) == 2) {
+    bf16x8 lo, hi;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (clayout_k<T>(ks, hh, e) == m) f[e] = (T)((float)f[e] - 1.f);
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = (bf16)(v[e] * scale);
+      hi[e] = (bf16)(v[e + 8] * scale);
+    }
+    *reinterpret_cast<bf16x8*>(dst) = lo;
+    *reinterpret_cast<bf16x8*>(dst + 8) = hi;
   } else {
-    if (clayout_k<T>(ks, hh, 0) == m) f -= 1.f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4)
+      *reinterpret_cast<float4*>(dst + e) = make_float4(v[e] * scale, v[e + 1] * scale, v[e + 2] * scale, v[e + 3] * scale);
   }
-  return f;
+}
+template <class T>
+__device__ __forceinline__ f32x16 load16(const T* src) {
+  f32x16 v;
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8 lo = *reinterpret_cast<const bf16x8*>(src), hi = *reinterpret_cast<const bf16x8*>(src + 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = (float)lo[e];
+      v[e + 8] = (float)hi[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(src + e);
+      v[e] = f.x; v[e + 1] = f.y; v[e + 2] = f.z; v[e + 3] = f.w;
+    }
+  }
+  return v;
+}
+
+// Position of k within its 16-wide block in the prepared bf16 image: slots 0-3 hold k 0-3,
+// 4-7 hold k 8-11, 8-11 hold k 4-7 and 12-15 hold k 12-15 (the clayout order of the two
+// lane halves).
+__device__ __forceinline__ int prep_pos(int k) {
+  const int b = k & ~15, r = k & 15;
+  const int q = r >> 2;
+  const int qp = q == 1 ? 2 : q == 2 ? 1 : q;
+  return b + qp * 4 + (r & 3);
 }
 
 }  // namespace
 
-// At^T of every chunk (plain transpose through LDS, 32 x 32 tiles).
-template <class T, int DK>
-__global__ __launch_bounds__(256) void transpose_at_kernel(const T* __restrict__ At, T* __restrict__ AtT) {
-  __shared__ T tile[32][33];
-  constexpr int NT = DK / 32;
-  const int64_t chunk = blockIdx.x / (NT * NT);
-  const int tr = (int)(blockIdx.x % (NT * NT)) / NT, tc = (int)(blockIdx.x % NT);
-  const T* src = At + chunk * DK * DK;
-  T* dst = AtT + chunk * DK * DK;
-  const int x = threadIdx.x & 31, y0 = threadIdx.x >> 5;
-  for (int y = y0; y < 32; y += 8) tile[y][x] = src[(int64_t)(tr * 32 + y) * DK + tc * 32 + x];
-  __syncthreads();
-  for (int y = y0; y < 32; y += 8) dst[(int64_t)(tc * 32 + y) * DK + tr * 32 + x] = tile[x][y];
+// Pass 0: (At - I) and (At - I)^T in the fragment order, and Bc in the lane order.  One
+// thread per (chunk, row m, 16-wide k block) for the two At images; consecutive threads
+// take consecutive m, so the transposed reads are coalesced.
+template <class T, int DK, int DV>
+__global__ __launch_bounds__(256) void prep_bwd_kernel(ComposeBwdArgs a, int64_t n_chunks) {
+  const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
+  constexpr int KB = DK / 16;
+  const int64_t n_at = n_chunks * KB * DK;
+  if (t < n_at) {
+    const int m = (int)(t % DK);
+    const int kb = (int)((t / DK) % KB);
+    const int64_t chunk = t / ((int64_t)DK * KB);
+    const T* X = reinterpret_cast<const T*>(a.At) + chunk * DK * DK;
+    T* P = reinterpret_cast<T*>(a.Ap) + chunk * DK * DK + (int64_t)m * DK;
+    T* PT = reinterpret_cast<T*>(a.ApT) + chunk * DK * DK + (int64_t)m * DK;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int k = kb * 16 + r;
+      const int pos = sizeof(T) == 2 ? prep_pos(k) : k;
+      const float d = (k == m) ? 1.f : 0.f;
+      P[pos] = from_f<T>(to_f<T>(X[(int64_t)m * DK + k]) - d);
+      PT[pos] = from_f<T>(to_f<T>(X[(int64_t)k * DK + m]) - d);
+    }
+    return;
+  }
+  const int64_t u = t - n_at;  // Bc: one thread per (chunk, column tile, row tile, lane)
+  constexpr int NRT = DK / 32, NCT = DV / 32;
+  if (u >= n_chunks * NCT * NRT * 64) return;
+  const int lane = (int)(u % 64), rt = (int)((u / 64) % NRT), ct = (int)((u / (64 * NRT)) % NCT);
+  const int64_t chunk = u / (64 * NRT * NCT);
+  const int hh = lane >> 5, c32 = lane & 31;
+  const T* B = reinterpret_cast<const T*>(a.Bc) + chunk * DK * DV;
+  f32x16 v;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = to_f<T>(B[(int64_t)(rt * 32 + acc_row(e, hh)) * DV + ct * 32 + c32]);
+  store16<T>(reinterpret_cast<T*>(a.Bl) + chunk * DK * DV + lane_off<DK>(ct, rt, lane), v, 1.f);
 }
 
 // Pass 1: forward over every chain, storing M_{j-1} of each active step.
@@ -79,8 +156,6 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
   const int N = a.N;
   const int col = ct * 32 + c32;
   const int64_t P = (int64_t)N * (N - 1) / 2;
-  const T* Ab = reinterpret_cast<const T*>(a.At) + bh * N * (int64_t)DK * DK;
-  const T* Bb = reinterpret_cast<const T*>(a.Bc) + bh * N * (int64_t)DK * DV;
   T* Ms = reinterpret_cast<T*>(a.Msave) + bh * P * DK * DV;
 
   f32x16 M[NRT];
@@ -90,28 +165,38 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
     for (int e = 0; e < 16; ++e)
       M[rt][e] = a.S0 ? a.S0[bh * DK * DV + (int64_t)(rt * 32 + acc_row(e, hh)) * DV + col] : 0.f;
 
+  const T* Apb = reinterpret_cast<const T*>(a.Ap) + bh * N * (int64_t)DK * DK;
+  const T* Blb = reinterpret_cast<const T*>(a.Bl) + bh * N * (int64_t)DK * DV;
+  T* Ds = reinterpret_cast<T*>(a.Dsave) + bh * P * DK * DV;
   for (int j = 0; j < i; ++j) {
     const int64_t o = (bh * N + i) * N + j;
     if (!a.mask[o]) continue;
     const float g = a.gates[o];
-    T* dst = Ms + pair_index(i, j) * DK * DV;
+    const int64_t p = pair_index(i, j);
+    // the opaque lane offset keeps the compiler from holding 64 store addresses in
+    // registers across the whole chain
+    int lofs = hh * 4 * DV + col;
+    asm volatile("" : "+v"(lofs));
+    T* dst = Ms + p * DK * DV + lofs;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) dst[(int64_t)(rt * 32 + acc_row(e, hh)) * DV + col] = from_f<T>(M[rt][e]);
+      for (int e = 0; e < 16; ++e) dst[(rt * 32 + (e >> 2) * 8 + (e & 3)) * DV] = from_f<T>(M[rt][e]);
     typename MM::Frag bf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) bf[ks] = MM::from_acc(M[ks / KPT], ks, g);
-    const T* X = Ab + (int64_t)j * DK * DK;
+    for (int ks = 0; ks < NKS; ++ks) bf[ks] = MM::from_acc(M[ks / KPT], ks, 1.f);
+    const T* X = Apb + (int64_t)j * DK * DK;
+    const T* Bl = Blb + (int64_t)j * DK * DV;
+    T* dd = Ds + p * DK * DV;
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+    for (int rt = 0; rt < NRT; ++rt) {
+      f32x16 D = load16<T>(Bl + lane_off<DK>(ct, rt, lane));
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) M[rt] = MM::mma(minus_eye_frag<T, DK>(X, rt, ks, hh, c32), bf[ks], M[rt]);
-    const T* Bj = Bb + (int64_t)j * DK * DV;
+      for (int ks = 0; ks < NKS; ++ks) D = MM::mma(prep_frag<T, DK>(X, rt, ks, hh, c32), bf[ks], D);
+      store16<T>(dd + lane_off<DK>(ct, rt, lane), D, 1.f);
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) M[rt][e] = fmaf(g, to_f<T>(Bj[(int64_t)(rt * 32 + acc_row(e, hh)) * DV + col]), M[rt][e]);
+      for (int e = 0; e < 16; ++e) M[rt][e] = fmaf(g, D[e], M[rt][e]);
+    }
   }
   if (a.S_routed) {
     float* so = a.S_routed + (bh * N + i) * (int64_t)DK * DV;
@@ -134,9 +219,8 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
   const int N = a.N;
   const int col = ct * 32 + c32;
   const int64_t P = (int64_t)N * (N - 1) / 2;
-  const T* ATb = reinterpret_cast<const T*>(a.AtT) + bh * N * (int64_t)DK * DK;
-  const T* Bb = reinterpret_cast<const T*>(a.Bc) + bh * N * (int64_t)DK * DV;
-  const T* Ms = reinterpret_cast<const T*>(a.Msave) + bh * P * DK * DV;
+  const T* ATb = reinterpret_cast<const T*>(a.ApT) + bh * N * (int64_t)DK * DK;
+  const T* Ds = reinterpret_cast<const T*>(a.Dsave) + bh * P * DK * DV;
   T* Ls = reinterpret_cast<T*>(a.Lsave) + bh * P * DK * DV;
 
   f32x16 lam[NRT];
@@ -151,39 +235,33 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
     if (!a.mask[o]) continue;
     const float g = a.gates[o];
     const int64_t p = pair_index(i, j);
-    T* ld = Ls + p * DK * DV;
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) ld[(int64_t)(rt * 32 + acc_row(e, hh)) * DV + col] = from_f<T>(g * lam[rt][e]);
-    typename MM::Frag bf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) bf[ks] = MM::from_acc(lam[ks / KPT], ks, 1.f);
-    const T* XT = ATb + (int64_t)j * DK * DK;
-    f32x16 Y[NRT];
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      Y[rt] = zero16();
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) Y[rt] = MM::mma(minus_eye_frag<T, DK>(XT, rt, ks, hh, c32), bf[ks], Y[rt]);
-    }
-    const T* Mj = Ms + p * DK * DV;
-    const T* Bj = Bb + (int64_t)j * DK * DV;
+    // gate gradient <lambda_j, D_j>, this wave's 32 columns
+    const T* dd = Ds + p * DK * DV;
     float part = 0.f;
 #pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const f32x16 D = load16<T>(dd + lane_off<DK>(ct, rt, lane));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) part = fmaf(lam[rt][e], D[e], part);
+    }
+    int lofs = hh * 4 * DV + col;  // opaque: see compose_save_kernel
+    asm volatile("" : "+v"(lofs));
+    T* ld = Ls + p * DK * DV + lofs;
+#pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t off = (int64_t)(rt * 32 + acc_row(e, hh)) * DV + col;
-        part = fmaf(Y[rt][e], to_f<T>(Mj[off]), part);
-        part = fmaf(lam[rt][e], to_f<T>(Bj[off]), part);
-      }
+      for (int e = 0; e < 16; ++e) ld[(rt * 32 + (e >> 2) * 8 + (e & 3)) * DV] = from_f<T>(g * lam[rt][e]);
+    // lambda += (At_j - I)^T (g lambda)
+    typename MM::Frag bf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) bf[ks] = MM::from_acc(lam[ks / KPT], ks, g);
+    const T* XT = ATb + (int64_t)j * DK * DK;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) lam[rt] = MM::mma(prep_frag<T, DK>(XT, rt, ks, hh, c32), bf[ks], lam[rt]);
     part = wave_sum(part);
     if (lane == 0) a.dgp[o * NCT + ct] = part;
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) lam[rt][e] = fmaf(g, Y[rt][e], lam[rt][e]);
   }
   float* le = a.lam_end + (bh * N + i) * (int64_t)DK * DV;
 #pragma unroll
@@ -281,14 +359,14 @@ static hipError_t launch_compose_bwd_t(const ComposeBwdArgs& a, hipStream_t s) {
   const int64_t BH = a.B * a.H, BHN = BH * a.N;
   {
     TimedLaunch tl(HLA_KERNEL_BWD_SAVE, s);
+    const int64_t nt = BHN * (DK / 16) * DK + BHN * (DV / 32) * (DK / 32) * 64;
+    hipLaunchKernelGGL((prep_bwd_kernel<T, DK, DV>), dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, a, BHN);
     hipLaunchKernelGGL((compose_save_kernel<T, DK, DV>), dim3((unsigned)BHN), dim3(DV / 32 * 64), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     TimedLaunch tl(HLA_KERNEL_BWD_ADJOINT, s);
-    hipLaunchKernelGGL((transpose_at_kernel<T, DK>), dim3((unsigned)(BHN * (DK / 32) * (DK / 32))), dim3(256), 0, s,
-                       reinterpret_cast<const T*>(a.At), reinterpret_cast<T*>(a.AtT));
     hipLaunchKernelGGL((compose_adjoint_kernel<T, DK, DV>), dim3((unsigned)BHN), dim3(DV / 32 * 64), 0, s, a);
   }
   e = hipGetLastError();

@@ -144,8 +144,11 @@ struct ComposeBwdArgs {
   float* dgates;         // out [B,H,N,N]
   float* dS0;            // out [B,H,dk,dv] or null
   float* S_routed;       // out [B,H,N,dk,dv] or null
-  void* AtT;             // workspace [B,H,N,dk,dk] (dtype)
+  void* Ap;              // workspace [B,H,N,dk,dk] (dtype): At - I in the fragment order
+  void* ApT;             // workspace [B,H,N,dk,dk] (dtype): (At - I)^T in the fragment order
+  void* Bl;              // workspace [B,H,N,dk,dv] (dtype): Bc in the accumulator's lane order
   void* Msave;           // workspace [B,H,N(N-1)/2,dk,dv] (dtype): M_{j-1} of pair (i, j)
+  void* Dsave;           // workspace [B,H,N(N-1)/2,dk,dv] (dtype): D_j of pair (i, j), lane order
   void* Lsave;           // workspace [B,H,N(N-1)/2,dk,dv] (dtype): g lambda_j of pair (i, j)
   float* dgp;            // workspace [B,H,N,N,dv/32]: per-wave gate-gradient parts
   float* lam_end;        // workspace [B,H,N,dk,dv]: final lambda of every chain

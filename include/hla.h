@@ -310,8 +310,10 @@ hla_status_t hla_gdn2_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int3
  *   dS0        out [B, H, dk, dv] float32, or NULL.
  *   S_routed   out [B, H, N, dk, dv] float32 (the routed states, recomputed), or NULL.
  *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_COMPOSE_BACKWARD) bytes:
- *              At^T, and the state in front of every active step and g lambda of it
- *              (dtype, N (N - 1) / 2 slots of dk x dv per (b, h)), so it grows as N^2.
+ *              (At - I), its transpose and Bc reordered for the matrix cores, and for
+ *              every active step the state in front of it, (At_j - I) M + Bc_j and
+ *              g lambda (dtype, N (N - 1) / 2 slots of dk x dv each per (b, h)), so it
+ *              grows as N^2.
  * Computation: bf16 (or float32) matrix-core products with float32 accumulation; sums in a
  * fixed order (deterministic).
  * Errors: HLA_ERR_NULL_ARG, HLA_ERR_BAD_SHAPE, HLA_ERR_BAD_DTYPE, HLA_ERR_ALIGN,

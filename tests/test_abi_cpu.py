@@ -232,8 +232,9 @@ def _r(x):
 def test_backward_workspace_sizes(lib):
     d = dims(B=2, T=130, H=3, dk=128, dv=64, dtype=1)  # N = 3 chunks, 3 pairs per (b, h)
     BH, N, P_ = 6, 3, 3
-    comp = (_r(BH * N * 128 * 128 * 2) + 2 * _r(BH * P_ * 128 * 64 * 2) + _r(BH * N * N * 2 * 4)
-            + _r(BH * N * 128 * 64 * 4))
+    # (At - I), its transpose and Bc reordered; per pair M, D and g lambda; gate parts; final lambda
+    comp = (2 * _r(BH * N * 128 * 128 * 2) + _r(BH * N * 128 * 64 * 2) + 3 * _r(BH * P_ * 128 * 64 * 2)
+            + _r(BH * N * N * 2 * 4) + _r(BH * N * 128 * 64 * 4))
     assert hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD, d) == comp
     BHN, nb_out, nb_all = BH * N, 2, 2 + 6
     chunk = (_r(BHN * nb_all * 64 * 128 * 4) + _r(BHN * nb_out * 64 * 128 * 4) + _r(BHN * nb_all * 64 * 2 * 4)
@@ -244,7 +245,7 @@ def test_backward_workspace_sizes(lib):
     assert pb > comp + chunk
     d4 = dims(B=2, T=130 + 3 * 64, H=3, dk=128, dv=64, dtype=1)  # N = 6: 15 pairs
     assert hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD, d4) - hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD, d) >= \
-        2 * BH * 12 * 128 * 64 * 2
+        3 * BH * 12 * 128 * 64 * 2
     out = ctypes.c_size_t()
     for fn in (hla.FN_CHUNK_BACKWARD, hla.FN_PREFILL_BACKWARD):
         assert lib.hla_workspace_bytes(fn, ctypes.byref(dims(C=128)), 0, ctypes.byref(out)) == UNSUPPORTED
