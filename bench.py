@@ -7,7 +7,7 @@ float32 states), one step = hla_chunk_transitions -> hla_route_mix -> hla_gdn_pr
 record of the dominant kernel (the gated composition) timed with HIP events on its own
 stream, and the CPU oracle's throughput on a bounded sample.  Secondary records (same
 JSON line): decode step tokens/s with HBM GB/s, native chunkwise prefill, Tail-Replay
-state rebuild.  All inputs are seeded synthetic tensors of the workloads' shapes.
+state rebuild, the routed prefill's backward pass at T = 8192.  All inputs are seeded synthetic tensors of the workloads' shapes.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
 
@@ -266,6 +266,7 @@ SECONDARY = {
     "routed_prefill_skip": bench_routed_skip,
     "routed_prefill_learned_reps": bench_routed_learned_reps,
     "gdn2_routed_prefill": lambda args, torch, hla, inputs, x: bench_gdn2_routed(args, torch, hla, inputs, x),
+    "routed_prefill_backward": lambda args, torch, hla, inputs, x: bench_prefill_backward(args, torch, hla, inputs, x),
     "decode": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs),
     "gdn2_decode": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs, gdn2=True),
     "native_prefill": lambda args, torch, hla, inputs, x: bench_native_prefill(args, torch, hla, inputs),
@@ -432,6 +433,81 @@ def bench_gdn2_routed(args, torch, hla, inputs, x):
     log(f"[gdn2_routed_prefill] {dt*1e3:.3f} ms/step, {W.B*W.T/dt/1e6:.3f} M tok/s, chunk passes "
         f"{chunk_s*1e3:.3f} ms ({ach:.1f} TFLOP/s fp32 VALU), compose {cm_ms/cm_n:.3f} ms")
     del q, k, v, ga, gb, gw, At, Bc, out, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- backward
+BWD_T = 8192
+
+
+def flops_chunk_bwd(n_tokens_heads, dk, dv):
+    """Algorithmic work of the per-chunk reverse, per token and head: every column runs the
+    forward step once (k . x and the update, 4 dk) and its reverse (k . dx, dx . x_prev, the
+    two-term key gradient and the dx update, 10 dk); the dv state columns add q dO and the
+    query gradient (4 dk).  Map columns: dk + dv; state columns: dv.  The checkpoint replay
+    the kernel adds (a second forward step) is not counted."""
+    return n_tokens_heads * dk * (dv * 18 + (dk + dv) * 14)
+
+
+def flops_router_bwd(pairs, n_rep, dk):
+    """Per history pair: the scores twice (query side and key side) and the two gradient
+    accumulations, 2 n_rep dk each."""
+    return pairs * 4 * 2 * n_rep * dk
+
+
+def bench_prefill_backward(args, torch, hla, inputs, x):
+    """The routed-prefill backward (hla_prefill_backward) at B=1, T=8192, H=16, d=128, C=64,
+    bf16, computed gates at tau = 1e-3: recomputed forward, chunk outputs reverse,
+    composition backward, chunk maps reverse, router backward and the per-token sums."""
+    W = inputs.WORKLOADS["routed_prefill"]
+    T = BWD_T
+    q, k, v = (to_dev(a[:, :T], W.dtype, torch) for a in (x.q, x.k, x.v))
+    beta, alpha = to_dev(x.beta[:, :T], "f32", torch), to_dev(x.alpha[:, :T], "f32", torch)
+    dO = to_dev(inputs.gen_cotangent((W.B, T, W.H, W.dv), seed=0, name="dO"), "f32", torch)
+    dev = k.device
+    N = math.ceil(T / C)
+    d = hla.make_dims(W.B, T, W.H, T, W.dk, W.dv, hla.HLA_BF16, C)
+    ws = torch.empty(hla.workspace_bytes(hla.FN_PREFILL_BACKWARD, d), dtype=torch.uint8, device=dev)
+    log(f"[routed_prefill_backward] T={T}: workspace {ws.numel() / 2**30:.2f} GiB")
+    step = lambda: hla.prefill_backward(q, k, v, beta, alpha, dO, tau=W.tau, ws=ws)
+    g = step()
+    torch.cuda.synchronize()
+    pairs = int((g["dgates"] != 0).sum().item())
+    steps = max(3, args.steps // 4)
+    hla.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    names = (("bwd_chunk", hla.KERNEL_BWD_CHUNK), ("bwd_save", hla.KERNEL_BWD_SAVE),
+             ("bwd_adjoint", hla.KERNEL_BWD_ADJOINT), ("bwd_reduce", hla.KERNEL_BWD_REDUCE),
+             ("bwd_router", hla.KERNEL_BWD_ROUTER), ("fwd_chunk", hla.KERNEL_CHUNK), ("fwd_gates", hla.KERNEL_GATES),
+             ("fwd_compose", hla.KERNEL_COMPOSE))
+    per = {n: hla.timing_read(kid) for n, kid in names}
+    hla.timing_enable(False)
+    ms = {n: tot / steps for n, (tot, cnt) in per.items() if cnt > 0}
+    th = W.B * T * W.H
+    fl_chunk = flops_chunk_bwd(th, W.dk, W.dv)
+    fl_pair = flops_compose(pairs, W.dk, W.dv)
+    ach = fl_chunk / (ms["bwd_chunk"] / 1e3) / 1e12
+    mfma = {n: dict(achieved=round(fl_pair / (ms[n] / 1e3) / 1e12, 1),
+                    frac=round(fl_pair / (ms[n] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+            for n in ("bwd_save", "bwd_adjoint", "bwd_reduce")}
+    res = dict(workload=f"routed prefill backward (GDN + HLA), B={W.B} T={T} H={W.H} d={W.dk} C={C} bf16, "
+                        f"computed gates tau={W.tau}",
+               ms_per_step=round(dt * 1e3, 3), tokens_per_s=round(W.B * T / dt, 1), active_pairs=pairs,
+               kernel_ms={n: round(v, 3) for n, v in ms.items()},
+               roofline=dict(kernel="chunk_bwd_kernel (outputs + maps reverse)", bound="alu", achieved=round(ach, 2),
+                             peak=round(PEAK_FP32_VALU_TFLOPS, 1), unit="TFLOP/s",
+                             frac=round(ach / PEAK_FP32_VALU_TFLOPS, 4), flops_per_step=fl_chunk),
+               composition_mfma=dict(flops_per_pass=fl_pair, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", **mfma),
+               router_tflops=round(flops_router_bwd(pairs, C, W.dk) / (ms["bwd_router"] / 1e3) / 1e12, 2))
+    log(f"[routed_prefill_backward] {dt*1e3:.3f} ms/step, {W.B*T/dt/1e6:.3f} M tok/s; chunk reverse "
+        f"{ms['bwd_chunk']:.3f} ms ({ach:.1f} TFLOP/s fp32 VALU); save {ms['bwd_save']:.3f}, adjoint "
+        f"{ms['bwd_adjoint']:.3f}, reduce {ms['bwd_reduce']:.3f}, router {ms['bwd_router']:.3f} ms")
+    del q, k, v, beta, alpha, dO, ws, g
     torch.cuda.empty_cache()
     return res
 

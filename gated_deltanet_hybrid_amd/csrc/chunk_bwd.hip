@@ -21,8 +21,8 @@
 // token: a forward pass keeps the state in front of every 8-token block in registers (8
 // checkpoints x 8 rows per thread), and each block is replayed from its checkpoint before
 // it is reversed.
-// Sums over columns run through lane exchanges inside a wave and LDS across waves, once
-// per block of 8 tokens; every workgroup writes its own partial sums, which
+// Sums over columns run through DPP row moves and gfx950's permlane swaps inside a wave
+// (no LDS traffic) and through LDS across waves, once per block of 8 tokens; every workgroup writes its own partial sums, which
 // chunk_bwd_finalize_kernel adds in a fixed order (no atomics: deterministic).
 #include "common.hpp"
 #include "kernels.hpp"
@@ -124,14 +124,15 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
     return at;
   };
   float ck[C / kTB][kRPT];
+  // Tokens past the end of a partial chunk are staged as k = 0, beta = 0, alpha = 1, u = 0
+  // and dO = 0: exact identity steps both ways, so every loop runs all 64 tokens without
+  // branches (their partial sums land in slots the finalize pass never reads).
 #pragma unroll
   for (int s = 0; s < C / kTB; ++s) {
 #pragma unroll
     for (int i = 0; i < kRPT; ++i) ck[s][i] = x[i];
-    for (int u = 0; u < kTB; ++u) {
-      const int t = s * kTB + u;
-      if (t < n) step(t, x);
-    }
+#pragma unroll
+    for (int u = 0; u < kTB; ++u) step(s * kTB + u, x);
   }
 
   // ---- reverse, one 8-token block at a time
@@ -146,10 +147,10 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
       dx[i] = isP ? a.dAt[(cc * DK + r0 + i) * DK + colall] : a.dBc[(cc * DK + r0 + i) * DV + vcol];
   }
   float* pv = a.part_v + ((bh * a.N + c) * 2 + (OUT ? 0 : 1)) * (int64_t)C * DV;
-  for (int s = C / kTB - 1; s >= 0; --s) {
+  const int nblk = (n + kTB - 1) / kTB;
+  for (int s = nblk - 1; s >= 0; --s) {
     const int tb = s * kTB;
-    if (tb < n) {  // uniform over the workgroup
-      const int nb = n - tb < kTB ? n - tb : kTB;
+    {
       float xs[kTB][kRPT], av[kTB];
       // the block's checkpoint, picked with compile-time register indices
 #pragma unroll
@@ -160,12 +161,11 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
       for (int u = 0; u < kTB; ++u) {
 #pragma unroll
         for (int i = 0; i < kRPT; ++i) xs[u][i] = x[i];
-        av[u] = 0.f;
-        if (u < nb) av[u] = step(tb + u, x);
+        av[u] = step(tb + u, x);
       }
 #pragma unroll
       for (int u = kTB - 1; u >= 0; --u) {
-        if (u < nb) {
+        {
           const int t = tb + u;
           const float be = s_beta[t], al = s_alpha[t], uu = s_u[t][cl], at = av[u];
           float pq[kRPT];
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
             const float go = s_do[t][cl];
 #pragma unroll
             for (int i = 0; i < kRPT; ++i) {
-              const float xa = (u + 1 < nb) ? xs[u + 1 < kTB ? u + 1 : u][i] : x[i];  // state after token t
+              const float xa = u + 1 < kTB ? xs[u + 1 < kTB ? u + 1 : u][i] : x[i];  // state after token t
               dx[i] = fmaf(s_q[t][r0 + i], go, dx[i]);
               pq[i] = xa * go;
             }
@@ -190,21 +190,13 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
             pk[i] = be * uu * dx[i] - al * be * (at * dx[i] + bd * xp);
             dx[i] = al * (dx[i] - be * s_k[t][r0 + i] * bd);
           }
-          // sums over the wave's columns (lanes with the same row group)
+          // sums over the wave's columns (lanes with the same row group), in the VALU
 #pragma unroll
-          for (int m = RG; m < 64; m <<= 1) {
-#pragma unroll
-            for (int i = 0; i < kRPT; ++i) {
-              pk[i] += __shfl_xor(pk[i], m, 64);
-              if constexpr (OUT) pq[i] += __shfl_xor(pq[i], m, 64);
-            }
+          for (int i = 0; i < kRPT; ++i) {
+            pk[i] = stride_sum<RG>(pk[i]);
+            if constexpr (OUT) pq[i] = stride_sum<RG>(pq[i]);
           }
-          float pab = pa, pbb = pb;
-#pragma unroll
-          for (int m = 1; m < 64; m <<= 1) {
-            pab += __shfl_xor(pab, m, 64);
-            pbb += __shfl_xor(pbb, m, 64);
-          }
+          const float pab = wave_sum_valu(pa), pbb = wave_sum_valu(pb);
           if (lane < RG) {
 #pragma unroll
             for (int i = 0; i < kRPT; ++i) {
@@ -221,7 +213,7 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
       __syncthreads();
       // sums over the waves, written as this workgroup's partial sums
       const int64_t slot = ((bh * a.N + c) * NB_ALL + blk) * (int64_t)C;
-      for (int i = tid; i < nb * NRED; i += NTH) {
+      for (int i = tid; i < kTB * NRED; i += NTH) {
         const int u = i / NRED, e = i % NRED;
         float sum = 0.f;
 #pragma unroll
@@ -233,7 +225,7 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
       }
       if constexpr (OUT) {
         const int64_t qslot = ((bh * a.N + c) * NB_OUT + cb) * (int64_t)C;
-        for (int i = tid; i < nb * DK; i += NTH) {
+        for (int i = tid; i < kTB * DK; i += NTH) {
           const int u = i / DK, e = i % DK;
           float sum = 0.f;
 #pragma unroll

@@ -158,6 +158,32 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// x plus the value of the lane 16 (swap16) or 32 (swap32) apart, every lane receiving the
+// sum: gfx950's permlane swaps exchange 16-lane rows between two registers in the VALU,
+// with no LDS traffic.  Both registers hold x, so the two halves of the result are the
+// lane's own value and its partner's.
+__device__ __forceinline__ float swap16_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+// Sum over the lanes that agree with this one in the lane-index bits below G (G = 8, 16 or
+// 32): the lanes G, 2G, ... apart.
+template <int G>
+__device__ __forceinline__ float stride_sum(float x) {
+  static_assert(G == 8 || G == 16 || G == 32, "stride of 8, 16 or 32 lanes");
+  if constexpr (G == 8) x += dpp_f<0x128>(x);  // row_ror 8: the lane 8 apart in its row
+  if constexpr (G <= 16) x = swap16_sum(x);
+  return swap32_sum(x);
+}
+// Sum over all 64 lanes without LDS traffic.
+__device__ __forceinline__ float wave_sum_valu(float x) { return stride_sum<16>(group_sum<16>(x)); }
+
 __device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + __expf(-x)); }
 
 // 16-byte global -> LDS copy of `bytes` (multiple of 16) by the whole block.
