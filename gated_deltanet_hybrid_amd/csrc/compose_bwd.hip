@@ -16,7 +16,9 @@
 //   0. prep_bwd_kernel writes (At_j - I) and its transpose with every 16-wide k block in the
 //      order the MFMA fragments read it (one 16-byte load per fragment), and Bc_j in the
 //      accumulator's lane order;
-//   1. compose_save_kernel runs every chain forward: per active step it forms
+//   1. compose_save_kernel runs every chain forward (one chain per workgroup; the step's
+//      (At_j - I) staged in LDS and shared by the column waves, the next one loaded while
+//      the current one is multiplied): per active step it forms
 //      D_j = (At_j - I) M_{j-1} + Bc_j on the matrix cores, stores M_{j-1} (row-major, for
 //      pass 3) and D_j (in the accumulator's lane order, for pass 2), and sets M += g D_j;
 //   2. compose_adjoint_kernel runs every chain backward: per active step it stores
@@ -36,18 +38,6 @@ namespace hla {
 namespace {
 
 __device__ __forceinline__ int64_t pair_index(int i, int j) { return (int64_t)i * (i - 1) / 2 + j; }
-
-// A fragment of row tile rt, k-step ks from a prepared (X - I) image (prep_bwd_kernel):
-// bf16 rows hold every 16-wide k block in the clayout slot order, so the fragment is one
-// 16-byte load; float32 rows are plain and the fragment is the clayout element.
-template <class T, int DK>
-__device__ __forceinline__ typename Mma<T>::Frag prep_frag(const T* Xp, int rt, int ks, int hh, int c32) {
-  const T* row = Xp + (int64_t)(rt * 32 + c32) * DK;
-  if constexpr (sizeof(T) == 2)
-    return *reinterpret_cast<const bf16x8*>(row + ks * 16 + hh * 8);
-  else
-    return Mma<T>::load_clayout(row, ks, hh);
-}
 
 // Offset of element e of lane `lane` in the accumulator-lane-order image of one dk x dv
 // matrix: [dv/32 column tiles][dk/32 row tiles][64 lanes][16].
@@ -144,12 +134,59 @@ __global__ __launch_bounds__(256) void prep_bwd_kernel(ComposeBwdArgs a, int64_t
   store16<T>(reinterpret_cast<T*>(a.Bl) + chunk * DK * DV + lane_off<DK>(ct, rt, lane), v, 1.f);
 }
 
-// Pass 1: forward over every chain, storing M_{j-1} of each active step.
+// (At - I) images of one history chunk staged in LDS, shared by the workgroup's waves: rows
+// padded by 16 bytes so that a 16-lane read phase of fragment rows hits distinct banks.
+template <class T, int DK>
+struct StagedA {
+  static constexpr int PAD = 16 / (int)sizeof(T), PP = DK + PAD;  // row pitch (elements)
+  static constexpr int BYTES = DK * PP * (int)sizeof(T);
+};
+
+template <class T, int DK>
+__device__ __forceinline__ typename Mma<T>::Frag lds_frag(const T* sA, int rt, int ks, int hh, int c32) {
+  const T* row = sA + (rt * 32 + c32) * StagedA<T, DK>::PP;
+  if constexpr (sizeof(T) == 2)
+    return *reinterpret_cast<const bf16x8*>(row + ks * 16 + hh * 8);
+  else
+    return Mma<T>::load_clayout(row, ks, hh);
+}
+
+// Copy of one prepared (At - I) image (global, rows of DK elements) into registers, then into
+// padded LDS rows: NCP 16-byte pieces per thread.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <class T, int DK, int NTH>
+struct AStage {
+  static constexpr int EPP = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  static constexpr int NCP = DK * DK / EPP / NTH;
+  static_assert(NCP * EPP * NTH == DK * DK, "pieces split evenly");
+};
+template <class T, int DK, int NTH, int NC>
+__device__ __forceinline__ void stage_load(u32x4 (&r)[NC], const T* src, int tid) {
+  static_assert(NC == AStage<T, DK, NTH>::NCP, "piece count");
+#pragma unroll
+  for (int c = 0; c < NC; ++c) r[c] = reinterpret_cast<const u32x4*>(src)[tid + c * NTH];
+}
+template <class T, int DK, int NTH, int NC>
+__device__ __forceinline__ void stage_store(const u32x4 (&r)[NC], T* sA, int tid) {
+  constexpr int EPP = AStage<T, DK, NTH>::EPP;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int e0 = (tid + c * NTH) * EPP;
+    *reinterpret_cast<u32x4*>(sA + (e0 / DK) * StagedA<T, DK>::PP + e0 % DK) = r[c];
+  }
+}
+
+// Pass 1: forward over every chain, storing M_{j-1} and D_j of each active step.  One
+// chain per workgroup: (At_j - I) of the next active step is loaded into registers while
+// the current one is multiplied from LDS, then written to the other LDS buffer.
 template <class T, int DK, int DV>
 __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdArgs a) {
   using MM = Mma<T>;
-  constexpr int NRT = DK / 32, NKS = DK / MM::KS, KPT = 32 / MM::KS;
-  const int lane = threadIdx.x & 63, ct = threadIdx.x >> 6, hh = lane >> 5, c32 = lane & 31;
+  constexpr int NRT = DK / 32, NKS = DK / MM::KS, KPT = 32 / MM::KS, NTH = DV / 32 * 64;
+  __shared__ __attribute__((aligned(16))) char smem[2 * StagedA<T, DK>::BYTES];
+  auto sbuf = [&](int b) { return reinterpret_cast<T*>(smem + b * StagedA<T, DK>::BYTES); };
+  const int tid = threadIdx.x, lane = tid & 63, ct = tid >> 6, hh = lane >> 5, c32 = lane & 31;
   const int64_t BH = a.B * a.H;
   const int64_t bh = blockIdx.x % BH;
   const int i = a.N - 1 - (int)(blockIdx.x / BH);  // longest chains first
@@ -157,6 +194,11 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
   const int col = ct * 32 + c32;
   const int64_t P = (int64_t)N * (N - 1) / 2;
   T* Ms = reinterpret_cast<T*>(a.Msave) + bh * P * DK * DV;
+  T* Ds = reinterpret_cast<T*>(a.Dsave) + bh * P * DK * DV;
+  const T* Apb = reinterpret_cast<const T*>(a.Ap) + bh * N * (int64_t)DK * DK;
+  const T* Blb = reinterpret_cast<const T*>(a.Bl) + bh * N * (int64_t)DK * DV;
+  const uint8_t* mrow = a.mask + (bh * N + i) * (int64_t)N;
+  const float* grow = a.gates + (bh * N + i) * (int64_t)N;
 
   f32x16 M[NRT];
 #pragma unroll
@@ -165,13 +207,22 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
     for (int e = 0; e < 16; ++e)
       M[rt][e] = a.S0 ? a.S0[bh * DK * DV + (int64_t)(rt * 32 + acc_row(e, hh)) * DV + col] : 0.f;
 
-  const T* Apb = reinterpret_cast<const T*>(a.Ap) + bh * N * (int64_t)DK * DK;
-  const T* Blb = reinterpret_cast<const T*>(a.Bl) + bh * N * (int64_t)DK * DV;
-  T* Ds = reinterpret_cast<T*>(a.Dsave) + bh * P * DK * DV;
-  for (int j = 0; j < i; ++j) {
-    const int64_t o = (bh * N + i) * N + j;
-    if (!a.mask[o]) continue;
-    const float g = a.gates[o];
+  auto next_active = [&](int j) {
+    while (j < i && !mrow[j]) ++j;
+    return j;
+  };
+  u32x4 pre[AStage<T, DK, NTH>::NCP];
+  int j = next_active(0);
+  int buf = 0;
+  if (j < i) {
+    stage_load<T, DK, NTH>(pre, Apb + (int64_t)j * DK * DK, tid);
+    stage_store<T, DK, NTH>(pre, sbuf(0), tid);
+    __syncthreads();
+  }
+  while (j < i) {
+    const int jn = next_active(j + 1);
+    if (jn < i) stage_load<T, DK, NTH>(pre, Apb + (int64_t)jn * DK * DK, tid);
+    const float g = grow[j];
     const int64_t p = pair_index(i, j);
     // the opaque lane offset keeps the compiler from holding 64 store addresses in
     // registers across the whole chain
@@ -185,18 +236,25 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
     typename MM::Frag bf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) bf[ks] = MM::from_acc(M[ks / KPT], ks, 1.f);
-    const T* X = Apb + (int64_t)j * DK * DK;
+    const T* sA = sbuf(buf);
     const T* Bl = Blb + (int64_t)j * DK * DV;
     T* dd = Ds + p * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      f32x16 D = load16<T>(Bl + lane_off<DK>(ct, rt, lane));
+      f32x16 D = zero16();
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) D = MM::mma(prep_frag<T, DK>(X, rt, ks, hh, c32), bf[ks], D);
+      for (int ks = 0; ks < NKS; ++ks) D = MM::mma(lds_frag<T, DK>(sA, rt, ks, hh, c32), bf[ks], D);
+      const f32x16 b = load16<T>(Bl + lane_off<DK>(ct, rt, lane));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) D[e] += b[e];
       store16<T>(dd + lane_off<DK>(ct, rt, lane), D, 1.f);
 #pragma unroll
       for (int e = 0; e < 16; ++e) M[rt][e] = fmaf(g, D[e], M[rt][e]);
     }
+    if (jn < i) stage_store<T, DK, NTH>(pre, sbuf(buf ^ 1), tid);
+    __syncthreads();
+    buf ^= 1;
+    j = jn;
   }
   if (a.S_routed) {
     float* so = a.S_routed + (bh * N + i) * (int64_t)DK * DV;
@@ -207,12 +265,14 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
   }
 }
 
-// Pass 2: backward over every chain.
+// Pass 2: backward over every chain, staged like pass 1 with (At_j - I)^T.
 template <class T, int DK, int DV>
 __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBwdArgs a) {
   using MM = Mma<T>;
-  constexpr int NRT = DK / 32, NKS = DK / MM::KS, KPT = 32 / MM::KS, NCT = DV / 32;
-  const int lane = threadIdx.x & 63, ct = threadIdx.x >> 6, hh = lane >> 5, c32 = lane & 31;
+  constexpr int NRT = DK / 32, NKS = DK / MM::KS, KPT = 32 / MM::KS, NCT = DV / 32, NTH = NCT * 64;
+  __shared__ __attribute__((aligned(16))) char smem[2 * StagedA<T, DK>::BYTES];
+  auto sbuf = [&](int b) { return reinterpret_cast<T*>(smem + b * StagedA<T, DK>::BYTES); };
+  const int tid = threadIdx.x, lane = tid & 63, ct = tid >> 6, hh = lane >> 5, c32 = lane & 31;
   const int64_t BH = a.B * a.H;
   const int64_t bh = blockIdx.x % BH;
   const int i = a.N - 1 - (int)(blockIdx.x / BH);
@@ -222,6 +282,8 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
   const T* ATb = reinterpret_cast<const T*>(a.ApT) + bh * N * (int64_t)DK * DK;
   const T* Ds = reinterpret_cast<const T*>(a.Dsave) + bh * P * DK * DV;
   T* Ls = reinterpret_cast<T*>(a.Lsave) + bh * P * DK * DV;
+  const uint8_t* mrow = a.mask + (bh * N + i) * (int64_t)N;
+  const float* grow = a.gates + (bh * N + i) * (int64_t)N;
 
   f32x16 lam[NRT];
   const float* dS = a.dS + (bh * N + i) * (int64_t)DK * DV;
@@ -230,20 +292,27 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
 #pragma unroll
     for (int e = 0; e < 16; ++e) lam[rt][e] = dS[(int64_t)(rt * 32 + acc_row(e, hh)) * DV + col];
 
-  for (int j = i - 1; j >= 0; --j) {
-    const int64_t o = (bh * N + i) * N + j;
-    if (!a.mask[o]) continue;
-    const float g = a.gates[o];
+  auto prev_active = [&](int j) {
+    while (j >= 0 && !mrow[j]) --j;
+    return j;
+  };
+  u32x4 pre[AStage<T, DK, NTH>::NCP];
+  int j = prev_active(i - 1);
+  int buf = 0;
+  if (j >= 0) {
+    stage_load<T, DK, NTH>(pre, ATb + (int64_t)j * DK * DK, tid);
+    stage_store<T, DK, NTH>(pre, sbuf(0), tid);
+    __syncthreads();
+  }
+  while (j >= 0) {
+    const int jn = prev_active(j - 1);
+    if (jn >= 0) stage_load<T, DK, NTH>(pre, ATb + (int64_t)jn * DK * DK, tid);
+    const float g = grow[j];
     const int64_t p = pair_index(i, j);
-    // gate gradient <lambda_j, D_j>, this wave's 32 columns
     const T* dd = Ds + p * DK * DV;
-    float part = 0.f;
+    f32x16 D[NRT];
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const f32x16 D = load16<T>(dd + lane_off<DK>(ct, rt, lane));
-#pragma unroll
-      for (int e = 0; e < 16; ++e) part = fmaf(lam[rt][e], D[e], part);
-    }
+    for (int rt = 0; rt < NRT; ++rt) D[rt] = load16<T>(dd + lane_off<DK>(ct, rt, lane));
     int lofs = hh * 4 * DV + col;  // opaque: see compose_save_kernel
     asm volatile("" : "+v"(lofs));
     T* ld = Ls + p * DK * DV + lofs;
@@ -251,17 +320,34 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) ld[(rt * 32 + (e >> 2) * 8 + (e & 3)) * DV] = from_f<T>(g * lam[rt][e]);
-    // lambda += (At_j - I)^T (g lambda)
+    // Y = (At_j - I)^T (g lambda), in accumulators of its own so lambda_j stays for dg
     typename MM::Frag bf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) bf[ks] = MM::from_acc(lam[ks / KPT], ks, g);
-    const T* XT = ATb + (int64_t)j * DK * DK;
+    const T* sA = sbuf(buf);
+    f32x16 Y[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      Y[rt] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) Y[rt] = MM::mma(lds_frag<T, DK>(sA, rt, ks, hh, c32), bf[ks], Y[rt]);
+    }
+    // gate gradient <lambda_j, D_j>, this wave's 32 columns
+    float part = 0.f;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) lam[rt] = MM::mma(prep_frag<T, DK>(XT, rt, ks, hh, c32), bf[ks], lam[rt]);
+      for (int e = 0; e < 16; ++e) part = fmaf(lam[rt][e], D[rt][e], part);
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lam[rt][e] += Y[rt][e];
     part = wave_sum(part);
-    if (lane == 0) a.dgp[o * NCT + ct] = part;
+    if (lane == 0) a.dgp[((bh * N + i) * N + j) * NCT + ct] = part;
+    if (jn >= 0) stage_store<T, DK, NTH>(pre, sbuf(buf ^ 1), tid);
+    __syncthreads();
+    buf ^= 1;
+    j = jn;
   }
   float* le = a.lam_end + (bh * N + i) * (int64_t)DK * DV;
 #pragma unroll

@@ -166,3 +166,25 @@ def test_prefill_backward(case, gates):
         skipped += int(hist.sum() - ref["mask"][hist].sum())
     if gates != "computed":
         assert skipped > 0
+
+
+def test_prefill_backward_bench_launch_shape():
+    """The bench's launch configuration (H = 16, d = 128, bf16, computed gates, tau = 1e-3)
+    at T = 1024 (16 chunks, 120 pairs per head); two of the sixteen heads against the
+    oracle, the others checked for finiteness."""
+    dtype, dk, dv, T, H = "bf16", 128, 128, 1024, 16
+    note("prefill backward, bench launch shape")
+    x = inputs.gen_tokens(1, T, H, dk, dv, dtype=dtype, seed=61)
+    q, k, v, beta, alpha = (dev(x.q, dtype), dev(x.k, dtype), dev(x.v, dtype), f32(x.beta), f32(x.alpha))
+    dO = inputs.gen_cotangent((1, T, H, dv), seed=62, name="dO")
+    g = hla().prefill_backward(q, k, v, beta, alpha, f32(dO), tau=1e-3)
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv", "dbeta", "dalpha", "dgates"):
+        assert np.all(np.isfinite(host(g[n]))), n
+    for hh in (0, 11):
+        qq, kk, vv, bb, aa = (_tok(x, n, 0, hh) for n in ("q", "k", "v", "beta", "alpha"))
+        ref = oracle.hla_prefill_backward(qq, kk, vv, bb, aa, C, 1e-3, dO[0, :, hh].astype(np.float64))
+        for n in ("dq", "dk", "dv", "dbeta", "dalpha"):
+            assert_close(host(g[n])[0, :, hh], ref[n], dtype, f"{n} head {hh}")
+        assert_close(host(g["dgates"])[0, hh], ref["dgates"], dtype, f"dgates head {hh}")
+        assert_close(host(g["dS0"])[0, hh], ref["dS0"].T, dtype, f"dS0 head {hh}")
