@@ -113,14 +113,13 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
 #pragma unroll
     for (int i = 0; i < kRPT; ++i) x[i] = (isP && r0 + i == colall) ? 1.f : 0.f;
   }
+  // x <- alpha (x - beta k a) + beta k u  =  alpha x + c k  with  c = beta (u - alpha a)
   auto step = [&](int t, float* xx) {
     const float at = rowdot(s_k[t], xx);
     const float be = s_beta[t], al = s_alpha[t], u = s_u[t][cl];
+    const float cc = be * fmaf(-al, at, u);
 #pragma unroll
-    for (int i = 0; i < kRPT; ++i) {
-      const float kr = s_k[t][r0 + i];
-      xx[i] = al * fmaf(-be * kr, at, xx[i]) + be * kr * u;
-    }
+    for (int i = 0; i < kRPT; ++i) xx[i] = fmaf(cc, s_k[t][r0 + i], al * xx[i]);
     return at;
   };
   float ck[C / kTB][kRPT];
@@ -182,13 +181,15 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
           if (writes && rg == 0) pv[(int64_t)t * DV + vcol] = be * bd;
           float pa = rg == 0 ? -be * at * bd : 0.f;
           const float pb = rg == 0 ? bd * (uu - al * at) : 0.f;
+          // dk partial = beta (u - alpha a) dx - alpha beta b x_prev;  dx <- alpha dx - alpha beta b k
+          const float c1 = be * fmaf(-al, at, uu), c2 = -al * be * bd;
           float pk[kRPT];
 #pragma unroll
           for (int i = 0; i < kRPT; ++i) {
             const float xp = xs[u][i];
             pa = fmaf(dx[i], xp, pa);
-            pk[i] = be * uu * dx[i] - al * be * (at * dx[i] + bd * xp);
-            dx[i] = al * (dx[i] - be * s_k[t][r0 + i] * bd);
+            pk[i] = fmaf(c2, xp, c1 * dx[i]);
+            dx[i] = fmaf(c2, s_k[t][r0 + i], al * dx[i]);
           }
           // sums over the wave's columns (lanes with the same row group), in the VALU
 #pragma unroll

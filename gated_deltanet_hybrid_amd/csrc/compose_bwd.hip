@@ -37,6 +37,8 @@ namespace hla {
 
 namespace {
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ int64_t pair_index(int i, int j) { return (int64_t)i * (i - 1) / 2 + j; }
 
 // Offset of element e of lane `lane` in the accumulator-lane-order image of one dk x dv
@@ -109,15 +111,24 @@ __global__ __launch_bounds__(256) void prep_bwd_kernel(ComposeBwdArgs a, int64_t
     const int kb = (int)((t / DK) % KB);
     const int64_t chunk = t / ((int64_t)DK * KB);
     const T* X = reinterpret_cast<const T*>(a.At) + chunk * DK * DK;
-    T* P = reinterpret_cast<T*>(a.Ap) + chunk * DK * DK + (int64_t)m * DK;
-    T* PT = reinterpret_cast<T*>(a.ApT) + chunk * DK * DK + (int64_t)m * DK;
+    // the 16 values of this block, row m of (At - I) and of its transpose, placed in the
+    // fragment order in registers, then written as whole 16-byte pieces
+    T vp[16], vt[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int k = kb * 16 + r;
-      const int pos = sizeof(T) == 2 ? prep_pos(k) : k;
+      const int pos = sizeof(T) == 2 ? prep_pos(k) - kb * 16 : r;
       const float d = (k == m) ? 1.f : 0.f;
-      P[pos] = from_f<T>(to_f<T>(X[(int64_t)m * DK + k]) - d);
-      PT[pos] = from_f<T>(to_f<T>(X[(int64_t)k * DK + m]) - d);
+      vp[pos] = from_f<T>(to_f<T>(X[(int64_t)m * DK + k]) - d);
+      vt[pos] = from_f<T>(to_f<T>(X[(int64_t)k * DK + m]) - d);
+    }
+    u32x4* P = reinterpret_cast<u32x4*>(reinterpret_cast<T*>(a.Ap) + chunk * DK * DK + (int64_t)m * DK + kb * 16);
+    u32x4* PT = reinterpret_cast<u32x4*>(reinterpret_cast<T*>(a.ApT) + chunk * DK * DK + (int64_t)m * DK + kb * 16);
+    constexpr int NP = 16 * (int)sizeof(T) / 16;
+#pragma unroll
+    for (int c = 0; c < NP; ++c) {
+      P[c] = reinterpret_cast<const u32x4*>(vp)[c];
+      PT[c] = reinterpret_cast<const u32x4*>(vt)[c];
     }
     return;
   }
@@ -153,8 +164,6 @@ __device__ __forceinline__ typename Mma<T>::Frag lds_frag(const T* sA, int rt, i
 
 // Copy of one prepared (At - I) image (global, rows of DK elements) into registers, then into
 // padded LDS rows: NCP 16-byte pieces per thread.
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
 template <class T, int DK, int NTH>
 struct AStage {
   static constexpr int EPP = 16 / (int)sizeof(T);  // elements per 16-byte piece
@@ -356,13 +365,20 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
     for (int e = 0; e < 16; ++e) le[(int64_t)(rt * 32 + acc_row(e, hh)) * DV + col] = lam[rt][e];
 }
 
-// Pass 3: per history chunk j, the sums over the query chunks that keep it.
+// Pass 3: per history chunk j, the sums over the query chunks that keep it.  Each active
+// chain's g lambda and M (row-major) are staged in padded LDS rows shared by the four
+// waves; the next active chain's are loaded into registers while the current ones are
+// multiplied, and dBc_j accumulates straight from those registers.
 template <class T, int DK, int DV>
 __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs a) {
   using MM = Mma<T>;
   constexpr int NRT = DK / 32, NTILE = NRT * NRT, TPW = NTILE / 4, NKS = DV / MM::KS, NCT = DV / 32;
   static_assert(NTILE % 4 == 0, "four waves share the dAt tiles");
-  constexpr int NV8 = DK * DV / 8 / 256;  // 8-element groups of dBc per thread
+  constexpr int EPP = 16 / (int)sizeof(T), PP = DV + EPP;  // elements per piece, LDS row pitch
+  constexpr int NPC = DK * DV / EPP / 256;                  // 16-byte pieces per thread and matrix
+  static_assert(NPC * EPP * 256 == DK * DV, "pieces split evenly");
+  __shared__ __attribute__((aligned(16))) T sL[DK * PP];
+  __shared__ __attribute__((aligned(16))) T sM[DK * PP];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, c32 = lane & 31;
   const int64_t BH = a.B * a.H;
   const int64_t bh = blockIdx.x % BH;
@@ -371,36 +387,57 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
   const int64_t P = (int64_t)N * (N - 1) / 2;
   const T* Ms = reinterpret_cast<const T*>(a.Msave) + bh * P * DK * DV;
   const T* Ls = reinterpret_cast<const T*>(a.Lsave) + bh * P * DK * DV;
+  auto active = [&](int i) { return a.mask[(bh * N + i) * (int64_t)N + j] != 0; };
+  auto next_active = [&](int i) {
+    while (i < N && !active(i)) ++i;
+    return i;
+  };
 
   f32x16 acc[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) acc[u] = zero16();
-  float sb[NV8][8];
+  float sb[NPC][EPP];
 #pragma unroll
-  for (int v = 0; v < NV8; ++v)
+  for (int c = 0; c < NPC; ++c)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sb[v][e] = 0.f;
-
-  for (int i = j + 1; i < N; ++i) {
-    const int64_t o = (bh * N + i) * N + j;
-    if (!a.mask[o]) continue;
+    for (int e = 0; e < EPP; ++e) sb[c][e] = 0.f;
+  u32x4 preL[NPC], preM[NPC];
+  auto prefetch = [&](int i) {
     const int64_t p = pair_index(i, j);
-    const T* L = Ls + p * DK * DV;
-    const T* Mi = Ms + p * DK * DV;
+    const u32x4* L = reinterpret_cast<const u32x4*>(Ls + p * DK * DV);
+    const u32x4* Mi = reinterpret_cast<const u32x4*>(Ms + p * DK * DV);
+#pragma unroll
+    for (int c = 0; c < NPC; ++c) {
+      preL[c] = L[tid + c * 256];
+      preM[c] = Mi[tid + c * 256];
+    }
+  };
+
+  int i = next_active(j + 1);
+  if (i < N) prefetch(i);
+  while (i < N) {
+    __syncthreads();  // the previous chain's LDS reads are done
+#pragma unroll
+    for (int c = 0; c < NPC; ++c) {
+      const int e0 = (tid + c * 256) * EPP;
+      *reinterpret_cast<u32x4*>(sL + (e0 / DV) * PP + e0 % DV) = preL[c];
+      *reinterpret_cast<u32x4*>(sM + (e0 / DV) * PP + e0 % DV) = preM[c];
+      const T* v = reinterpret_cast<const T*>(&preL[c]);
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) sb[c][e] += to_f<T>(v[e]);
+    }
+    __syncthreads();
+    const int in = next_active(i + 1);
+    if (in < N) prefetch(in);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int t = w * TPW + u, rt = t / NRT, st = t % NRT;
-      const T* ar = L + (int64_t)(rt * 32 + c32) * DV;
-      const T* br = Mi + (int64_t)(st * 32 + c32) * DV;
+      const T* ar = sL + (rt * 32 + c32) * PP;
+      const T* br = sM + (st * 32 + c32) * PP;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) acc[u] = MM::mma(MM::load_plain(ar, ks, hh), MM::load_plain(br, ks, hh), acc[u]);
     }
-#pragma unroll
-    for (int v = 0; v < NV8; ++v) {
-      const int64_t base = (int64_t)(v * 256 + tid) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sb[v][e] += to_f<T>(L[base + e]);
-    }
+    i = in;
   }
   float* dA = a.dAt + (bh * N + j) * (int64_t)DK * DK;
 #pragma unroll
@@ -411,20 +448,20 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
   }
   float* dB = a.dBc + (bh * N + j) * (int64_t)DK * DV;
 #pragma unroll
-  for (int v = 0; v < NV8; ++v) {
-    const int64_t base = (int64_t)(v * 256 + tid) * 8;
+  for (int c = 0; c < NPC; ++c) {
+    const int64_t e0 = (int64_t)(tid + c * 256) * EPP;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dB[base + e] = sb[v][e];
+    for (int e = 0; e < EPP; ++e) dB[e0 + e] = sb[c][e];
   }
   // gate gradients of column j (zero for skipped, diagonal and future pairs)
-  for (int i = tid; i < N; i += 256) {
-    const int64_t o = (bh * N + i) * N + j;
-    float s = 0.f;
-    if (i > j && a.mask[o]) {
+  for (int ii = tid; ii < N; ii += 256) {
+    const int64_t o = (bh * N + ii) * N + j;
+    float sg = 0.f;
+    if (ii > j && a.mask[o]) {
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) s += a.dgp[o * NCT + c];
+      for (int c = 0; c < NCT; ++c) sg += a.dgp[o * NCT + c];
     }
-    a.dgates[o] = s;
+    a.dgates[o] = sg;
   }
 }
 
