@@ -14,7 +14,7 @@
 //
 // Layout: one workgroup per (b, h, 64-token piece).  A thread holds 2 columns over a
 // quarter of the rows (2 x dk/4 floats); the 4 threads of a column group are adjacent
-// lanes, so the read k . D x is a sum over the thread's rows plus two lane exchanges.
+// lanes, so the read k . D x is a sum over the thread's rows plus two DPP quad moves.
 // Token vectors (k o alpha, alpha, e, k, u, and q for outputs) are staged 8 tokens at a
 // time in LDS and read as broadcasts.  The work is float32 VALU: per token and column
 // about 4 dk fused multiply-adds (5 dk with the output read).  The layout was chosen by
@@ -128,9 +128,7 @@ __global__ __launch_bounds__((gdn2_threads<DK, DV, OUT>())) void gdn2_chunk_kern
         }
       }
 #pragma unroll
-      for (int j = 0; j < CPT; ++j)
-#pragma unroll
-        for (int m = 1; m < RQ; m <<= 1) s[j] += __shfl_xor(s[j], m, 64);
+      for (int j = 0; j < CPT; ++j) s[j] = group_sum<RQ>(s[j]);  // the RQ row groups are adjacent lanes
       float u[CPT];
 #pragma unroll
       for (int j = 0; j < CPT; ++j) u[j] = writes ? s_u[t][ucol0 + j] : 0.f;
@@ -163,9 +161,7 @@ __global__ __launch_bounds__((gdn2_threads<DK, DV, OUT>())) void gdn2_chunk_kern
           }
         }
 #pragma unroll
-        for (int j = 0; j < CPT; ++j)
-#pragma unroll
-          for (int m = 1; m < RQ; m <<= 1) o[j] += __shfl_xor(o[j], m, 64);
+        for (int j = 0; j < CPT; ++j) o[j] = group_sum<RQ>(o[j]);
         if (rq == 0) {
           float* orow = a.o + ((b * a.T + t0 + tb + t) * a.H + h) * DV + grp * CPT;
 #pragma unroll
