@@ -183,6 +183,19 @@ __device__ __forceinline__ float stride_sum(float x) {
 }
 // Sum over all 64 lanes without LDS traffic.
 __device__ __forceinline__ float wave_sum_valu(float x) { return stride_sum<16>(group_sum<16>(x)); }
+// Maximum over all 64 lanes without LDS traffic (the same lane moves as wave_sum_valu).
+__device__ __forceinline__ float wave_max_valu(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x124>(x));
+  x = fmaxf(x, dpp_f<0x128>(x));
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  u = __builtin_bit_cast(unsigned, x);
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
 
 __device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + __expf(-x)); }
 
