@@ -191,18 +191,28 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
             pk[i] = fmaf(c2, xp, c1 * dx[i]);
             dx[i] = fmaf(c2, s_k[t][r0 + i], al * dx[i]);
           }
-          // sums over the wave's columns (lanes with the same row group), in the VALU
-#pragma unroll
-          for (int i = 0; i < kRPT; ++i) {
-            pk[i] = stride_sum<RG>(pk[i]);
-            if constexpr (OUT) pq[i] = stride_sum<RG>(pq[i]);
-          }
-          const float pab = wave_sum_valu(pa), pbb = wave_sum_valu(pb);
-          if (lane < RG) {
+          // sums over the wave's columns (lanes with the same row group), in the VALU: with
+          // 8-lane row groups the two columns of a 16-lane row are added first; then
+          // rows_sum8 leaves row rho with the totals of rows r0 + rho and r0 + 4 + rho
+          static_assert(kRPT == 8, "rows_sum8 takes the thread's 8 rows");
+          if constexpr (RG == 8) {
 #pragma unroll
             for (int i = 0; i < kRPT; ++i) {
-              s_red[u][wv][r0 + i] = pk[i];
-              if constexpr (OUT) s_redq[u][wv][r0 + i] = pq[i];
+              pk[i] += dpp_f<0x128>(pk[i]);  // row_ror 8: the other column of the row
+              if constexpr (OUT) pq[i] += dpp_f<0x128>(pq[i]);
+            }
+          }
+          float ka, kb2, qa = 0.f, qb2 = 0.f;
+          rows_sum8(pk, ka, kb2);
+          if constexpr (OUT) rows_sum8(pq, qa, qb2);
+          const float pab = wave_sum_valu(pa), pbb = wave_sum_valu(pb);
+          const int rho = lane >> 4;
+          if (RG == 16 || ((lane >> 3) & 1) == 0) {
+            s_red[u][wv][r0 + rho] = ka;
+            s_red[u][wv][r0 + 4 + rho] = kb2;
+            if constexpr (OUT) {
+              s_redq[u][wv][r0 + rho] = qa;
+              s_redq[u][wv][r0 + 4 + rho] = qb2;
             }
           }
           if (lane == 0) {

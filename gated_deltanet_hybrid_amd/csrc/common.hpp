@@ -181,6 +181,28 @@ __device__ __forceinline__ float stride_sum(float x) {
   if constexpr (G <= 16) x = swap16_sum(x);
   return swap32_sum(x);
 }
+// Sums of 8 values over the four 16-lane rows of a wave, with the result spread over the
+// rows instead of replicated: permlane16_swap of two different values adds each to its
+// partner row's copy (rows 0 and 2 keep the first value's pair sums, rows 1 and 3 the
+// second's), and permlane32_swap of two such results finishes the four-row sums.  On
+// return row rho holds the total of v[rho] in `ra` and of v[4 + rho] in `rb`: 12
+// instructions instead of a full all-reduce per value.
+__device__ __forceinline__ void rows_sum8(const float (&v)[8], float& ra, float& rb) {
+  float l1[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v[2 * m]),
+                                                    __builtin_bit_cast(unsigned, v[2 * m + 1]), false, false);
+    l1[m] = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  }
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, l1[0]), __builtin_bit_cast(unsigned, l1[1]),
+                                            false, false);
+  ra = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, l1[2]), __builtin_bit_cast(unsigned, l1[3]),
+                                       false, false);
+  rb = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 // Sum over all 64 lanes without LDS traffic.
 __device__ __forceinline__ float wave_sum_valu(float x) { return stride_sum<16>(group_sum<16>(x)); }
 // Maximum over all 64 lanes without LDS traffic (the same lane moves as wave_sum_valu).
