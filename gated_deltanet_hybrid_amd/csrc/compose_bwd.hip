@@ -274,11 +274,15 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
   }
 }
 
-// Pass 2: backward over every chain, staged like pass 1 with (At_j - I)^T.
+// Pass 2: backward over every chain, staged like pass 1 with (At_j - I)^T.  D_j of the next
+// active step is loaded into registers (raw, in the storage type) during the current one,
+// so the gate gradient <lambda_j, D_j> can be taken before the products and lambda can be
+// updated in place.
 template <class T, int DK, int DV>
 __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBwdArgs a) {
   using MM = Mma<T>;
   constexpr int NRT = DK / 32, NKS = DK / MM::KS, KPT = 32 / MM::KS, NCT = DV / 32, NTH = NCT * 64;
+  constexpr int DPC = 16 * (int)sizeof(T) / 16;  // 16-byte pieces of one lane's tile values
   __shared__ __attribute__((aligned(16))) char smem[2 * StagedA<T, DK>::BYTES];
   auto sbuf = [&](int b) { return reinterpret_cast<T*>(smem + b * StagedA<T, DK>::BYTES); };
   const int tid = threadIdx.x, lane = tid & 63, ct = tid >> 6, hh = lane >> 5, c32 = lane & 31;
@@ -306,54 +310,62 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
     return j;
   };
   u32x4 pre[AStage<T, DK, NTH>::NCP];
+  u32x4 dcur[NRT][DPC], dnext[NRT][DPC];
+  auto load_d = [&](u32x4 (&dst)[NRT][DPC], int j) {
+    const T* dd = Ds + pair_index(i, j) * DK * DV;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int c = 0; c < DPC; ++c) dst[rt][c] = reinterpret_cast<const u32x4*>(dd + lane_off<DK>(ct, rt, lane))[c];
+  };
   int j = prev_active(i - 1);
   int buf = 0;
   if (j >= 0) {
     stage_load<T, DK, NTH>(pre, ATb + (int64_t)j * DK * DK, tid);
+    load_d(dcur, j);
     stage_store<T, DK, NTH>(pre, sbuf(0), tid);
     __syncthreads();
   }
   while (j >= 0) {
     const int jn = prev_active(j - 1);
-    if (jn >= 0) stage_load<T, DK, NTH>(pre, ATb + (int64_t)jn * DK * DK, tid);
+    if (jn >= 0) {
+      stage_load<T, DK, NTH>(pre, ATb + (int64_t)jn * DK * DK, tid);
+      load_d(dnext, jn);
+    }
     const float g = grow[j];
-    const int64_t p = pair_index(i, j);
-    const T* dd = Ds + p * DK * DV;
-    f32x16 D[NRT];
+    // gate gradient <lambda_j, D_j>, this wave's 32 columns
+    float part = 0.f;
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) D[rt] = load16<T>(dd + lane_off<DK>(ct, rt, lane));
+    for (int rt = 0; rt < NRT; ++rt) {
+      const T* dv = reinterpret_cast<const T*>(dcur[rt]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) part = fmaf(lam[rt][e], to_f<T>(dv[e]), part);
+    }
     int lofs = hh * 4 * DV + col;  // opaque: see compose_save_kernel
     asm volatile("" : "+v"(lofs));
-    T* ld = Ls + p * DK * DV + lofs;
+    T* ld = Ls + pair_index(i, j) * DK * DV + lofs;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) ld[(rt * 32 + (e >> 2) * 8 + (e & 3)) * DV] = from_f<T>(g * lam[rt][e]);
-    // Y = (At_j - I)^T (g lambda), in accumulators of its own so lambda_j stays for dg
+    // lambda += (At_j - I)^T (g lambda), accumulated in place
     typename MM::Frag bf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) bf[ks] = MM::from_acc(lam[ks / KPT], ks, g);
     const T* sA = sbuf(buf);
-    f32x16 Y[NRT];
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      Y[rt] = zero16();
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) Y[rt] = MM::mma(lds_frag<T, DK>(sA, rt, ks, hh, c32), bf[ks], Y[rt]);
-    }
-    // gate gradient <lambda_j, D_j>, this wave's 32 columns
-    float part = 0.f;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) part = fmaf(lam[rt][e], D[rt][e], part);
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) lam[rt][e] += Y[rt][e];
+      for (int ks = 0; ks < NKS; ++ks) lam[rt] = MM::mma(lds_frag<T, DK>(sA, rt, ks, hh, c32), bf[ks], lam[rt]);
     part = wave_sum(part);
     if (lane == 0) a.dgp[((bh * N + i) * N + j) * NCT + ct] = part;
-    if (jn >= 0) stage_store<T, DK, NTH>(pre, sbuf(buf ^ 1), tid);
+    if (jn >= 0) {
+      stage_store<T, DK, NTH>(pre, sbuf(buf ^ 1), tid);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int c = 0; c < DPC; ++c) dcur[rt][c] = dnext[rt][c];
+    }
     __syncthreads();
     buf ^= 1;
     j = jn;
