@@ -205,6 +205,13 @@ __device__ __forceinline__ void rows_sum8(const float (&v)[8], float& ra, float&
 
 // Sum over all 64 lanes without LDS traffic.
 __device__ __forceinline__ float wave_sum_valu(float x) { return stride_sum<16>(group_sum<16>(x)); }
+// Sum over aligned groups of G consecutive lanes (G = 2 .. 64), every lane receiving it.
+template <int G>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  if constexpr (G <= 16) return group_sum<G>(x);
+  else if constexpr (G == 32) return swap16_sum(group_sum<16>(x));
+  else return wave_sum_valu(x);
+}
 // Maximum over all 64 lanes without LDS traffic (the same lane moves as wave_sum_valu).
 __device__ __forceinline__ float wave_max_valu(float x) {
   x = fmaxf(x, dpp_f<0xB1>(x));

@@ -222,8 +222,7 @@ __global__ __launch_bounds__(NT, WPC) void decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int e = 0; e < PAD; ++e) part += to_f<T>(ev[e]) * s_q[sub * PAD + e];
         }
-#pragma unroll
-        for (int off = TPR / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+        part = lane_group_sum<TPR>(part);  // the TPR lanes of a row are an aligned group
         if (r < a.n_rep) {
           const float s = part * scale;
           const float mn = fmaxf(m, s);
@@ -231,13 +230,25 @@ __global__ __launch_bounds__(NT, WPC) void decode_kernel(DecodeArgs a) {
           m = mn;
         }
       }
-      // combine the row groups of the wave (lanes with equal sub hold the same values)
-#pragma unroll
-      for (int off = TPR; off < 64; off <<= 1) {
-        const float mo = __shfl_xor(m, off, 64), so = __shfl_xor(ssum, off, 64);
-        const float mn = fmaxf(m, mo);
-        ssum = (m > -INFINITY ? ssum * __expf(m - mn) : 0.f) + (mo > -INFINITY ? so * __expf(mo - mn) : 0.f);
+      // combine the row groups of the wave (lanes with equal sub hold the same values); the
+      // combine is symmetric, so each level takes the two values a lane move delivers
+      auto combine = [&](float m1, float s1, float m2, float s2) {
+        const float mn = fmaxf(m1, m2);
+        ssum = (m1 > -INFINITY ? s1 * __expf(m1 - mn) : 0.f) + (m2 > -INFINITY ? s2 * __expf(m2 - mn) : 0.f);
         m = mn;
+      };
+      if constexpr (TPR <= 8) combine(m, ssum, dpp_f<0x128>(m), dpp_f<0x128>(ssum));  // 8 lanes apart
+      if constexpr (TPR <= 16) {
+        const auto rm = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, m), __builtin_bit_cast(unsigned, m), false, false);
+        const auto rs = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, ssum), __builtin_bit_cast(unsigned, ssum), false, false);
+        combine(__builtin_bit_cast(float, (unsigned)rm[0]), __builtin_bit_cast(float, (unsigned)rs[0]),
+                __builtin_bit_cast(float, (unsigned)rm[1]), __builtin_bit_cast(float, (unsigned)rs[1]));
+      }
+      {
+        const auto rm = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, m), __builtin_bit_cast(unsigned, m), false, false);
+        const auto rs = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, ssum), __builtin_bit_cast(unsigned, ssum), false, false);
+        combine(__builtin_bit_cast(float, (unsigned)rm[0]), __builtin_bit_cast(float, (unsigned)rs[0]),
+                __builtin_bit_cast(float, (unsigned)rm[1]), __builtin_bit_cast(float, (unsigned)rs[1]));
       }
       g = 1.f / (1.f + expf(-(m + logf(ssum / (float)a.n_rep))));
     }
