@@ -188,3 +188,26 @@ def test_prefill_backward_bench_launch_shape():
             assert_close(host(g[n])[0, :, hh], ref[n], dtype, f"{n} head {hh}")
         assert_close(host(g["dgates"])[0, hh], ref["dgates"], dtype, f"dgates head {hh}")
         assert_close(host(g["dS0"])[0, hh], ref["dS0"].T, dtype, f"dS0 head {hh}")
+
+
+def test_prefill_backward_batch_and_token_window():
+    """B = 2 with inputs that are a token window of a longer allocation (ld_T > T), no S0,
+    a ragged last chunk: the kernels read rows through ld_T and write gradients [B, T, H]."""
+    dtype, dk, dv, H, T, ld = "bf16", 64, 128, 2, 2 * C + 22, 2 * C + 70
+    note("prefill backward, batch and token window")
+    x = inputs.gen_tokens(2, ld, H, dk, dv, dtype=dtype, seed=71, alpha_mode="slow")
+    full = (dev(x.q, dtype), dev(x.k, dtype), dev(x.v, dtype), f32(x.beta), f32(x.alpha))
+    off = 30  # the window starts 30 tokens into each row
+    q, k, v, beta, alpha = (t[:, off:off + T] for t in full)
+    dO = inputs.gen_cotangent((2, T, H, dv), seed=72, name="dO")
+    g = hla().prefill_backward(q, k, v, beta, alpha, f32(dO), tau=1e-3, want_dS0=True)
+    torch.cuda.synchronize()
+    for b in range(2):
+        for hh in range(H):
+            sl = slice(off, off + T)
+            qq, kk, vv, bb, aa = (x.f64(n)[b, sl, hh] for n in ("q", "k", "v", "beta", "alpha"))
+            ref = oracle.hla_prefill_backward(qq, kk, vv, bb, aa, C, 1e-3, dO[b, :, hh].astype(np.float64))
+            for n in ("dq", "dk", "dv", "dbeta", "dalpha"):
+                assert_close(host(g[n])[b, :, hh], ref[n], dtype, f"{n} b{b} h{hh}")
+            assert_close(host(g["dgates"])[b, hh], ref["dgates"], dtype, "dgates")
+            assert_close(host(g["dS0"])[b, hh], ref["dS0"].T, dtype, "dS0")
