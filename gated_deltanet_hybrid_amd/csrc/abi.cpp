@@ -449,7 +449,8 @@ hla_status_t hla_compose_backward(const hla_dims_t* d, const void* At, const voi
   a.dAt = dAt; a.dBc = dBc; a.dgates = dgates; a.dS0 = dS0; a.S_routed = S_routed;
   set_compose_bwd_ws(a, w, ws);
   a.B = d->B; a.H = d->H; a.N = (int32_t)n_chunks(d);
-  return hip_status(hla::launch_compose_backward(a, d->dtype, d->dk, d->dv, stream));
+  return hip_status(hla::launch_compose_backward(a, d->dtype, d->dk, d->dv,
+                                                 hla::kComposeBwdSave | hla::kComposeBwdReverse, stream));
 }
 
 hla_status_t hla_chunk_backward(const hla_dims_t* d, const void* q, const void* k, const void* v, const float* beta,
@@ -498,7 +499,8 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   const int32_t N = (int32_t)n_chunks(d);
   auto at = [&](int64_t off) { return static_cast<void*>(base + off); };
   auto fat = [&](int64_t off) { return reinterpret_cast<float*>(base + off); };
-  // 1. forward: chunk maps, gates and routed states
+  // 1. forward: chunk maps, then gates, mask and lists (the routed states come from the
+  //    composition backward's forward replay in step 2)
   hla::ChunkArgs c{};
   c.q = q; c.k = k; c.v = v; c.beta = beta; c.alpha = alpha;
   c.B = d->B; c.T = d->T; c.H = d->H; c.ld_T = d->ld_T; c.N = N;
@@ -511,32 +513,35 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   r.mask = reinterpret_cast<uint8_t*>(base + w.mask_off);
   r.active_idx = reinterpret_cast<int32_t*>(base + w.aidx_off);
   r.active_cnt = reinterpret_cast<int32_t*>(base + w.acnt_off);
-  r.n_eff = nullptr; r.S_routed = fat(w.sr_off);
+  r.n_eff = nullptr; r.S_routed = nullptr;
   r.qbar = fat(w.route_off); r.At_prep = base + w.route_off + route_qbar_bytes(d);
   r.B = d->B; r.T = d->T; r.H = d->H; r.ld_T = d->ld_T; r.N = N; r.C = d->C;
   e = hla::launch_route(r, d->dtype, d->dk, d->dv, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;
-  // 2. outputs part of the chunk backward: dS~ and the chunk-local partial sums
+  // 2. composition backward, first stage: replay every chain, keeping the step states and
+  //    writing the routed states
+  float* dg = dgates ? dgates : fat(w.dg_off);
+  hla::ComposeBwdArgs m{};
+  m.At = c.At; m.Bc = c.Bc; m.gates = r.gates; m.mask = r.mask; m.S0 = S0; m.dS = fat(w.dsr_off);
+  m.dAt = fat(w.dat_off); m.dBc = fat(w.dbc_off); m.dgates = dg; m.dS0 = dS0; m.S_routed = fat(w.sr_off);
+  set_compose_bwd_ws(m, compose_bwd_ws(d), at(w.comp_off));
+  m.B = d->B; m.H = d->H; m.N = N;
+  e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdSave, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  // 3. outputs part of the chunk backward: dS~ and the chunk-local partial sums
   hla::ChunkBwdArgs cb{};
   cb.q = q; cb.k = k; cb.v = v; cb.beta = beta; cb.alpha = alpha;
   cb.B = d->B; cb.T = d->T; cb.H = d->H; cb.ld_T = d->ld_T; cb.N = N;
   cb.have_out = 1; cb.have_map = 1;
-  cb.chunk_init = r.S_routed; cb.dO = dO; cb.dchunk_init = fat(w.dsr_off);
-  cb.dAt = fat(w.dat_off); cb.dBc = fat(w.dbc_off);
+  cb.chunk_init = m.S_routed; cb.dO = dO; cb.dchunk_init = fat(w.dsr_off);
+  cb.dAt = m.dAt; cb.dBc = m.dBc;
   set_chunk_bwd_ws(cb, chunk_bwd_ws(d), at(w.chunk_off));
   cb.dq = dq; cb.dk = dk; cb.dv = dv; cb.dbeta = dbeta; cb.dalpha = dalpha;
   e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdOut, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;
-  // 3. composition backward: dAt, dBc, dgates, dS0
-  float* dg = dgates ? dgates : fat(w.dg_off);
-  hla::ComposeBwdArgs m{};
-  m.At = c.At; m.Bc = c.Bc; m.gates = r.gates; m.mask = r.mask; m.S0 = S0; m.dS = cb.dchunk_init;
-  m.dAt = fat(w.dat_off); m.dBc = fat(w.dbc_off); m.dgates = dg; m.dS0 = dS0; m.S_routed = nullptr;
-  set_compose_bwd_ws(m, compose_bwd_ws(d), at(w.comp_off));
-  m.B = d->B; m.H = d->H; m.N = N;
-  e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, stream);
+  // 4. composition backward, second stage: dAt, dBc, dgates, dS0; then the maps part
+  e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdReverse, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;
-  // 4. maps part of the chunk backward
   e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdMap, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;
   // 5. router (computed gates only), then the per-token sums

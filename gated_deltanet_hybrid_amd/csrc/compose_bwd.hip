@@ -490,16 +490,16 @@ __global__ __launch_bounds__(256) void chain_sum_kernel(const float* __restrict_
 }
 
 template <class T, int DK, int DV>
-static hipError_t launch_compose_bwd_t(const ComposeBwdArgs& a, hipStream_t s) {
+static hipError_t launch_compose_bwd_t(const ComposeBwdArgs& a, int stages, hipStream_t s) {
   const int64_t BH = a.B * a.H, BHN = BH * a.N;
-  {
+  if (stages & kComposeBwdSave) {
     TimedLaunch tl(HLA_KERNEL_BWD_SAVE, s);
     const int64_t nt = BHN * (DK / 16) * DK + BHN * (DV / 32) * (DK / 32) * 64;
     hipLaunchKernelGGL((prep_bwd_kernel<T, DK, DV>), dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, a, BHN);
     hipLaunchKernelGGL((compose_save_kernel<T, DK, DV>), dim3((unsigned)BHN), dim3(DV / 32 * 64), 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !(stages & kComposeBwdReverse)) return e;
   {
     TimedLaunch tl(HLA_KERNEL_BWD_ADJOINT, s);
     hipLaunchKernelGGL((compose_adjoint_kernel<T, DK, DV>), dim3((unsigned)BHN), dim3(DV / 32 * 64), 0, s, a);
@@ -519,15 +519,16 @@ static hipError_t launch_compose_bwd_t(const ComposeBwdArgs& a, hipStream_t s) {
 }
 
 template <class T>
-static hipError_t launch_compose_bwd_d(const ComposeBwdArgs& a, int dk, int dv, hipStream_t s) {
-  if (dk == 64 && dv == 64) return launch_compose_bwd_t<T, 64, 64>(a, s);
-  if (dk == 64 && dv == 128) return launch_compose_bwd_t<T, 64, 128>(a, s);
-  if (dk == 128 && dv == 64) return launch_compose_bwd_t<T, 128, 64>(a, s);
-  return launch_compose_bwd_t<T, 128, 128>(a, s);
+static hipError_t launch_compose_bwd_d(const ComposeBwdArgs& a, int dk, int dv, int stages, hipStream_t s) {
+  if (dk == 64 && dv == 64) return launch_compose_bwd_t<T, 64, 64>(a, stages, s);
+  if (dk == 64 && dv == 128) return launch_compose_bwd_t<T, 64, 128>(a, stages, s);
+  if (dk == 128 && dv == 64) return launch_compose_bwd_t<T, 128, 64>(a, stages, s);
+  return launch_compose_bwd_t<T, 128, 128>(a, stages, s);
 }
 
-hipError_t launch_compose_backward(const ComposeBwdArgs& a, int dtype, int dk, int dv, hipStream_t s) {
-  return dtype == 1 ? launch_compose_bwd_d<bf16>(a, dk, dv, s) : launch_compose_bwd_d<float>(a, dk, dv, s);
+hipError_t launch_compose_backward(const ComposeBwdArgs& a, int dtype, int dk, int dv, int stages, hipStream_t s) {
+  return dtype == 1 ? launch_compose_bwd_d<bf16>(a, dk, dv, stages, s)
+                    : launch_compose_bwd_d<float>(a, dk, dv, stages, s);
 }
 
 }  // namespace hla

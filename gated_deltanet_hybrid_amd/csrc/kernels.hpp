@@ -76,7 +76,7 @@ struct RouteArgs {
   int32_t* active_idx;  // [B,H,N,N]
   int32_t* active_cnt;  // [B,H,N]
   float* n_eff;         // [B,H,N] or null
-  float* S_routed;      // [B,H,N,dk,dv]
+  float* S_routed;      // [B,H,N,dk,dv]; null: gates, mask and lists only (internal use)
   int32_t C;            // tokens per chunk
   float* qbar;          // workspace [B,H,N,dk] float32
   void* At_prep;        // workspace [B,H,N,dk,dk] bf16: (At - I) reordered for the composition
@@ -155,8 +155,11 @@ struct ComposeBwdArgs {
   int64_t B, H;
   int32_t N;
 };
-// Backward of the gated composition (see compose_bwd.hip).
-hipError_t launch_compose_backward(const ComposeBwdArgs& a, int dtype, int dk, int dv, hipStream_t s);
+// Backward of the gated composition (see compose_bwd.hip).  `stages`: 1 the forward replay
+// that keeps the step states (and writes S_routed when asked), 2 the adjoint sweep and the
+// sums (dAt, dBc, dgates, dS0).
+constexpr int kComposeBwdSave = 1, kComposeBwdReverse = 2;
+hipError_t launch_compose_backward(const ComposeBwdArgs& a, int dtype, int dk, int dv, int stages, hipStream_t s);
 
 struct ChunkBwdArgs {
   const void* q;            // [B,ld_T,H,dk] (dtype)

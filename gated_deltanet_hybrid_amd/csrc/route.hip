@@ -403,7 +403,7 @@ static hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(lists_kernel, dim3((unsigned)(BH * a.N)), dim3(64), 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !a.S_routed) return e;  // no S_routed: gates, mask and lists only
   if constexpr (sizeof(T) == 2) return launch_compose_bf16(a, DK, DV, s);
   return launch_compose_t<T, DK, DV>(a, s);
 }
