@@ -113,7 +113,8 @@ __global__ __launch_bounds__(256) void prep_bwd_kernel(ComposeBwdArgs a, int64_t
     const T* X = reinterpret_cast<const T*>(a.At) + chunk * DK * DK;
     // the 16 values of this block, row m of (At - I) and of its transpose, placed in the
     // fragment order in registers, then written as whole 16-byte pieces
-    T vp[16], vt[16];
+    alignas(16) T vp[16];
+    alignas(16) T vt[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int k = kb * 16 + r;
