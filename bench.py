@@ -273,6 +273,13 @@ SECONDARY = {
     "tail_replay": lambda args, torch, hla, inputs, x: bench_tail_replay(args, torch, hla, inputs),
 }
 
+# lines run only when named with --only: the backward at the full 32768 tokens needs about
+# 200 GiB of workspace (three per-pair states of the composition backward grow as N^2)
+ONLY_LINES = {
+    "routed_prefill_backward_T32K": lambda args, torch, hla, inputs, x: bench_prefill_backward(
+        args, torch, hla, inputs, x, T=inputs.WORKLOADS["routed_prefill"].T),
+}
+
 
 # ----------------------------------------------------------------------------- decode
 def bench_decode(args, torch, hla, inputs, gdn2=False):
@@ -456,12 +463,12 @@ def flops_router_bwd(pairs, n_rep, dk):
     return pairs * 4 * 2 * n_rep * dk
 
 
-def bench_prefill_backward(args, torch, hla, inputs, x):
-    """The routed-prefill backward (hla_prefill_backward) at B=1, T=8192, H=16, d=128, C=64,
-    bf16, computed gates at tau = 1e-3: recomputed forward, chunk outputs reverse,
-    composition backward, chunk maps reverse, router backward and the per-token sums."""
+def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T):
+    """The routed-prefill backward (hla_prefill_backward) at B=1, T tokens (8192 by default),
+    H=16, d=128, C=64, bf16, computed gates at tau = 1e-3: recomputed chunk maps and gates,
+    composition replay, chunk outputs reverse, composition adjoint and sums, chunk maps
+    reverse, router backward and the per-token sums."""
     W = inputs.WORKLOADS["routed_prefill"]
-    T = BWD_T
     q, k, v = (to_dev(a[:, :T], W.dtype, torch) for a in (x.q, x.k, x.v))
     beta, alpha = to_dev(x.beta[:, :T], "f32", torch), to_dev(x.alpha[:, :T], "f32", torch)
     dO = to_dev(inputs.gen_cotangent((W.B, T, W.H, W.dv), seed=0, name="dO"), "f32", torch)
@@ -472,8 +479,12 @@ def bench_prefill_backward(args, torch, hla, inputs, x):
     log(f"[routed_prefill_backward] T={T}: workspace {ws.numel() / 2**30:.2f} GiB")
     step = lambda: hla.prefill_backward(q, k, v, beta, alpha, dO, tau=W.tau, ws=ws)
     g = step()
+    # active pairs from the router's own mask (a gate gradient can underflow to zero far
+    # back in a long chain, so it does not count them)
+    At, Bc = hla.chunk_transitions(k, v, beta, alpha)
+    pairs = int(hla.route_mix(q, k, At, Bc, tau=W.tau)["active_cnt"].sum().item())
+    del At, Bc
     torch.cuda.synchronize()
-    pairs = int((g["dgates"] != 0).sum().item())
     steps = max(3, args.steps // 4)
     hla.timing_enable(True)
     t0 = time.perf_counter()
@@ -495,16 +506,27 @@ def bench_prefill_backward(args, torch, hla, inputs, x):
     mfma = {n: dict(achieved=round(fl_pair / (ms[n] / 1e3) / 1e12, 1),
                     frac=round(fl_pair / (ms[n] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4))
             for n in ("bwd_save", "bwd_adjoint", "bwd_reduce")}
+    # roofline record of the kernel that takes the most time: the chunk reverse (fp32 VALU)
+    # or one of the composition passes (bf16 matrix cores)
+    kernels = {"bwd_chunk": ("chunk_bwd_kernel (outputs + maps reverse)", "alu", fl_chunk, PEAK_FP32_VALU_TFLOPS),
+               "bwd_save": ("compose_save_kernel (+ prep_bwd_kernel)", "mfma", fl_pair, PEAK_BF16_TFLOPS),
+               "bwd_adjoint": ("compose_adjoint_kernel", "mfma", fl_pair, PEAK_BF16_TFLOPS),
+               "bwd_reduce": ("compose_grad_reduce_kernel (+ chain_sum_kernel)", "mfma", fl_pair, PEAK_BF16_TFLOPS)}
+    dom = max(kernels, key=lambda n: ms[n])
+    kname, bound, fl_dom, peak = kernels[dom]
+    ach_dom = fl_dom / (ms[dom] / 1e3) / 1e12
     res = dict(workload=f"routed prefill backward (GDN + HLA), B={W.B} T={T} H={W.H} d={W.dk} C={C} bf16, "
                         f"computed gates tau={W.tau}",
                ms_per_step=round(dt * 1e3, 3), tokens_per_s=round(W.B * T / dt, 1), active_pairs=pairs,
                kernel_ms={n: round(v, 3) for n, v in ms.items()},
-               roofline=dict(kernel="chunk_bwd_kernel (outputs + maps reverse)", bound="alu", achieved=round(ach, 2),
-                             peak=round(PEAK_FP32_VALU_TFLOPS, 1), unit="TFLOP/s",
-                             frac=round(ach / PEAK_FP32_VALU_TFLOPS, 4), flops_per_step=fl_chunk),
+               roofline=dict(kernel=kname, bound=bound, achieved=round(ach_dom, 2), peak=round(peak, 1),
+                             unit="TFLOP/s", frac=round(ach_dom / peak, 4), flops_per_launch=fl_dom,
+                             avg_launch_ms=round(ms[dom], 4)),
+               chunk_reverse=dict(bound="alu", achieved=round(ach, 2), peak=round(PEAK_FP32_VALU_TFLOPS, 1),
+                                  unit="TFLOP/s", frac=round(ach / PEAK_FP32_VALU_TFLOPS, 4), flops_per_step=fl_chunk),
                composition_mfma=dict(flops_per_pass=fl_pair, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", **mfma),
                router_tflops=round(flops_router_bwd(pairs, C, W.dk) / (ms["bwd_router"] / 1e3) / 1e12, 2))
-    log(f"[routed_prefill_backward] {dt*1e3:.3f} ms/step, {W.B*T/dt/1e6:.3f} M tok/s; chunk reverse "
+    log(f"[routed_prefill_backward T={T}] {dt*1e3:.3f} ms/step, {W.B*T/dt/1e6:.3f} M tok/s; chunk reverse "
         f"{ms['bwd_chunk']:.3f} ms ({ach:.1f} TFLOP/s fp32 VALU); save {ms['bwd_save']:.3f}, adjoint "
         f"{ms['bwd_adjoint']:.3f}, reduce {ms['bwd_reduce']:.3f}, router {ms['bwd_router']:.3f} ms")
     del q, k, v, beta, alpha, dO, ws, g
@@ -691,15 +713,16 @@ def main():
 
     if args.only:
         names = args.only.split(",")
-        unknown = [n for n in names if n != "routed_prefill" and n not in SECONDARY]
+        extra = {**SECONDARY, **ONLY_LINES}
+        unknown = [n for n in names if n != "routed_prefill" and n not in extra]
         if unknown:
-            print(f"unknown lines {unknown}; known: routed_prefill, {', '.join(SECONDARY)}", file=sys.stderr)
+            print(f"unknown lines {unknown}; known: routed_prefill, {', '.join(extra)}", file=sys.stderr)
             sys.exit(2)
         x = routed_inputs(inputs) if any(n.startswith(("routed", "gdn2_routed")) for n in names) else None
         out = {}
         for n in names:
             out[n] = bench_routed_prefill(args, torch, hla, inputs, x=x)[0] if n == "routed_prefill" else \
-                SECONDARY[n](args, torch, hla, inputs, x)
+                extra[n](args, torch, hla, inputs, x)
         print(json.dumps(out), flush=True)
         return
 
