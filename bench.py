@@ -274,10 +274,11 @@ SECONDARY = {
 }
 
 # lines run only when named with --only: the backward at the full 32768 tokens needs about
-# 200 GiB of workspace (three per-pair states of the composition backward grow as N^2)
+# 200 GiB of workspace in one pass (three per-pair states of the composition backward grow
+# as N^2); the line also times it in query-chunk groups within 64 GiB
 ONLY_LINES = {
     "routed_prefill_backward_T32K": lambda args, torch, hla, inputs, x: bench_prefill_backward(
-        args, torch, hla, inputs, x, T=inputs.WORKLOADS["routed_prefill"].T),
+        args, torch, hla, inputs, x, T=inputs.WORKLOADS["routed_prefill"].T, grouped_gib=64),
 }
 
 
@@ -463,11 +464,12 @@ def flops_router_bwd(pairs, n_rep, dk):
     return pairs * 4 * 2 * n_rep * dk
 
 
-def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T):
+def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, grouped_gib=None):
     """The routed-prefill backward (hla_prefill_backward) at B=1, T tokens (8192 by default),
     H=16, d=128, C=64, bf16, computed gates at tau = 1e-3: recomputed chunk maps and gates,
     composition replay, chunk outputs reverse, composition adjoint and sums, chunk maps
-    reverse, router backward and the per-token sums."""
+    reverse, router backward and the per-token sums.  With `grouped_gib` the step is also
+    timed with a workspace of that many GiB, which runs the query chunks in groups."""
     W = inputs.WORKLOADS["routed_prefill"]
     q, k, v = (to_dev(a[:, :T], W.dtype, torch) for a in (x.q, x.k, x.v))
     beta, alpha = to_dev(x.beta[:, :T], "f32", torch), to_dev(x.alpha[:, :T], "f32", torch)
@@ -529,6 +531,26 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T):
     log(f"[routed_prefill_backward T={T}] {dt*1e3:.3f} ms/step, {W.B*T/dt/1e6:.3f} M tok/s; chunk reverse "
         f"{ms['bwd_chunk']:.3f} ms ({ach:.1f} TFLOP/s fp32 VALU); save {ms['bwd_save']:.3f}, adjoint "
         f"{ms['bwd_adjoint']:.3f}, reduce {ms['bwd_reduce']:.3f}, router {ms['bwd_router']:.3f} ms")
+    res["workspace_gib"] = round(ws.numel() / 2**30, 2)
+    if grouped_gib is not None and grouped_gib * 2**30 < ws.numel():
+        del ws, g
+        torch.cuda.empty_cache()
+        ws = torch.empty(int(grouped_gib * 2**30), dtype=torch.uint8, device=dev)
+        g = step()
+        torch.cuda.synchronize()
+        hla.timing_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        dtg = (time.perf_counter() - t0) / steps
+        groups = hla.timing_read(hla.KERNEL_BWD_SAVE)[1] // steps  # one save launch per group
+        hla.timing_enable(False)
+        res["grouped"] = dict(workspace_gib=grouped_gib, groups=groups, ms_per_step=round(dtg * 1e3, 3),
+                              tokens_per_s=round(W.B * T / dtg, 1),
+                              min_workspace_gib=round(hla.workspace_bytes(hla.FN_PREFILL_BACKWARD_MIN, d) / 2**30, 2))
+        log(f"[routed_prefill_backward T={T}] in {groups} query-chunk groups within {grouped_gib} GiB: "
+            f"{dtg*1e3:.3f} ms/step")
     del q, k, v, beta, alpha, dO, ws, g
     torch.cuda.empty_cache()
     return res

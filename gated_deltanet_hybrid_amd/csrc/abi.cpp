@@ -5,6 +5,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <utility>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -96,27 +98,57 @@ int64_t reps_ws(const hla_dims_t* d, int32_t n_rep) {
 }
 
 // Workspace of hla_compose_backward: (At - I) and its transpose in the fragment order, Bc in
-// the lane order, then per active pair (N (N - 1) / 2 slots per (b, h), dtype) the state in
-// front of the step, D_j and g lambda, then per-wave gate-gradient parts and the final
-// lambda of every chain.
+// the lane order, per-wave gate-gradient parts and the final lambda of every chain, then
+// `slots` pair slots per (b, h) (dtype) for each of the state in front of a step, D_j and
+// lambda.  With N (N - 1) / 2 slots every pair has its own and the chains run in one group;
+// with fewer, the chains run in consecutive groups whose pairs fit (at least N - 1 slots,
+// the longest chain's pairs).
 struct ComposeBwdWs {
-  int64_t ap_off, apt_off, bl_off, ms_off, ds_off, ls_off, dgp_off, le_off, total;
+  int64_t ap_off, apt_off, bl_off, dgp_off, le_off, ms_off, ds_off, ls_off, total;
 };
-ComposeBwdWs compose_bwd_ws(const hla_dims_t* d) {
+int64_t all_pairs(const hla_dims_t* d) {
+  const int64_t N = n_chunks(d);
+  return N * (N - 1) / 2;
+}
+int64_t min_pairs(const hla_dims_t* d) { return n_chunks(d) > 1 ? n_chunks(d) - 1 : 0; }
+int64_t pair_bytes(const hla_dims_t* d) { return d->B * d->H * d->dk * d->dv * dtype_bytes(d->dtype); }
+ComposeBwdWs compose_bwd_ws(const hla_dims_t* d, int64_t slots) {
   const int64_t N = n_chunks(d), BH = d->B * d->H, e = dtype_bytes(d->dtype);
-  const int64_t P = N * (N - 1) / 2;
-  const int64_t at = round_up(BH * N * d->dk * d->dk * e, 256), pr = round_up(BH * P * d->dk * d->dv * e, 256);
+  const int64_t at = round_up(BH * N * d->dk * d->dk * e, 256), pr = round_up(slots * pair_bytes(d), 256);
   ComposeBwdWs w;
   w.ap_off = 0;
   w.apt_off = at;
   w.bl_off = 2 * at;
-  w.ms_off = w.bl_off + round_up(BH * N * d->dk * d->dv * e, 256);
+  w.dgp_off = w.bl_off + round_up(BH * N * d->dk * d->dv * e, 256);
+  w.le_off = w.dgp_off + round_up(BH * N * N * (d->dv / 32) * 4, 256);
+  w.ms_off = w.le_off + round_up(BH * N * d->dk * d->dv * 4, 256);
   w.ds_off = w.ms_off + pr;
   w.ls_off = w.ds_off + pr;
-  w.dgp_off = w.ls_off + pr;
-  w.le_off = w.dgp_off + round_up(BH * N * N * (d->dv / 32) * 4, 256);
-  w.total = w.le_off + round_up(BH * N * d->dk * d->dv * 4, 256);
+  w.total = w.ls_off + pr;
   return w;
+}
+
+// Pair slots per (b, h) that `bytes` of composition workspace hold (all pairs at most), or
+// -1 when they hold fewer than the longest chain needs.
+int64_t slots_for(const hla_dims_t* d, int64_t bytes) {
+  const int64_t fixed = compose_bwd_ws(d, 0).total, per = 3 * pair_bytes(d);
+  const int64_t slots = bytes < fixed ? -1 : (bytes - fixed) / per;
+  if (slots < min_pairs(d)) return -1;
+  return slots < all_pairs(d) ? slots : all_pairs(d);
+}
+
+// Consecutive chain groups [i0, i1) whose pairs (i (i - 1) / 2 before chain i) fit `slots`,
+// each as long as it can be.
+std::vector<std::pair<int32_t, int32_t>> chain_groups(int32_t N, int64_t slots) {
+  std::vector<std::pair<int32_t, int32_t>> g;
+  auto before = [](int64_t i) { return i * (i - 1) / 2; };
+  for (int32_t i0 = 0; i0 < N;) {
+    int32_t i1 = i0 + 1;
+    while (i1 < N && before(i1 + 1) - before(i0) <= slots) ++i1;
+    g.emplace_back(i0, i1);
+    i0 = i1;
+  }
+  return g;
 }
 
 void set_compose_bwd_ws(hla::ComposeBwdArgs& a, const ComposeBwdWs& w, void* ws) {
@@ -152,12 +184,13 @@ void set_chunk_bwd_ws(hla::ChunkBwdArgs& a, const ChunkBwdWs& w, void* ws) {
 
 // Workspace of hla_prefill_backward: the forward's transitions, route outputs and routed
 // states, the gradients handed between the passes, then the workspaces of the route, the
-// chunk backward and the composition backward.
+// chunk backward and the composition backward (with `slots` pair slots, last, so that
+// what a caller's workspace holds beyond the rest becomes pair slots).
 struct PrefillBwdWs {
   int64_t at_off, bc_off, gates_off, mask_off, aidx_off, acnt_off, sr_off, dsr_off, dat_off, dbc_off, dg_off,
       qbar_off, dqbar_off, dkr_off, route_off, chunk_off, comp_off, total;
 };
-PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d) {
+PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d, int64_t slots) {
   const int64_t N = n_chunks(d), BH = d->B * d->H, BHN = BH * N, e = dtype_bytes(d->dtype);
   PrefillBwdWs w;
   int64_t o = 0;
@@ -182,7 +215,7 @@ PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d) {
   w.dkr_off = take(d->B * d->T * d->H * d->dk * 4);
   w.route_off = take(route_ws(d));
   w.chunk_off = take(chunk_bwd_ws(d).total);
-  w.comp_off = take(compose_bwd_ws(d).total);
+  w.comp_off = take(compose_bwd_ws(d, slots).total);
   w.total = o;
   return w;
 }
@@ -318,14 +351,16 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
       if (n_rep < 1 || d->C % n_rep != 0) return HLA_ERR_BAD_SHAPE;
       *out = (size_t)reps_ws(d, n_rep);
       return HLA_OK;
-    case HLA_FN_COMPOSE_BACKWARD: *out = (size_t)compose_bwd_ws(d).total; return HLA_OK;
+    case HLA_FN_COMPOSE_BACKWARD: *out = (size_t)compose_bwd_ws(d, all_pairs(d)).total; return HLA_OK;
+    case HLA_FN_COMPOSE_BACKWARD_MIN: *out = (size_t)compose_bwd_ws(d, min_pairs(d)).total; return HLA_OK;
     case HLA_FN_CHUNK_BACKWARD:
       if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
       *out = (size_t)chunk_bwd_ws(d).total;
       return HLA_OK;
     case HLA_FN_PREFILL_BACKWARD:
+    case HLA_FN_PREFILL_BACKWARD_MIN:
       if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
-      *out = (size_t)prefill_bwd_ws(d).total;
+      *out = (size_t)prefill_bwd_ws(d, fn == HLA_FN_PREFILL_BACKWARD ? all_pairs(d) : min_pairs(d)).total;
       return HLA_OK;
     default: return HLA_ERR_UNSUPPORTED;
   }
@@ -442,15 +477,20 @@ hla_status_t hla_compose_backward(const hla_dims_t* d, const void* At, const voi
   if (!At || !Bc || !gates || !mask || !dS_routed || !dAt || !dBc || !dgates) return HLA_ERR_NULL_ARG;
   if (!all_aligned(At, Bc, S0, dS_routed, dAt, dBc, dS0, S_routed, ws) || !all_aligned4(gates, dgates))
     return HLA_ERR_ALIGN;
-  const ComposeBwdWs w = compose_bwd_ws(d);
-  if (!ws || (int64_t)ws_bytes < w.total) return HLA_ERR_WORKSPACE;
+  const int64_t slots = ws ? slots_for(d, (int64_t)ws_bytes) : -1;
+  if (slots < 0) return HLA_ERR_WORKSPACE;
   hla::ComposeBwdArgs a{};
   a.At = At; a.Bc = Bc; a.gates = gates; a.mask = mask; a.S0 = S0; a.dS = dS_routed;
   a.dAt = dAt; a.dBc = dBc; a.dgates = dgates; a.dS0 = dS0; a.S_routed = S_routed;
-  set_compose_bwd_ws(a, w, ws);
+  set_compose_bwd_ws(a, compose_bwd_ws(d, slots), ws);
   a.B = d->B; a.H = d->H; a.N = (int32_t)n_chunks(d);
-  return hip_status(hla::launch_compose_backward(a, d->dtype, d->dk, d->dv,
-                                                 hla::kComposeBwdSave | hla::kComposeBwdReverse, stream));
+  for (const auto& g : chain_groups(a.N, slots)) {
+    a.i0 = g.first; a.i1 = g.second; a.accumulate = g.first > 0;
+    const hipError_t e = hla::launch_compose_backward(a, d->dtype, d->dk, d->dv,
+                                                      hla::kComposeBwdSave | hla::kComposeBwdReverse, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+  }
+  return HLA_OK;
 }
 
 hla_status_t hla_chunk_backward(const hla_dims_t* d, const void* q, const void* k, const void* v, const float* beta,
@@ -473,6 +513,7 @@ hla_status_t hla_chunk_backward(const hla_dims_t* d, const void* q, const void* 
   hla::ChunkBwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
   a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)n_pieces(d);
+  a.c0 = 0; a.c1 = a.N;
   a.have_out = have_out; a.have_map = have_map;
   a.chunk_init = chunk_init; a.dO = dO; a.dAt = dAt; a.dBc = dBc; a.dchunk_init = dchunk_init;
   set_chunk_bwd_ws(a, w, ws);
@@ -493,8 +534,10 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
   if (!all_aligned(q, k, v, S0, dS0, ws) || !all_aligned4(beta, alpha, gates_in, dO, dq, dk, dv, dbeta, dalpha, dgates))
     return HLA_ERR_ALIGN;
-  const PrefillBwdWs w = prefill_bwd_ws(d);
-  if (!ws || (int64_t)ws_bytes < w.total) return HLA_ERR_WORKSPACE;
+  const PrefillBwdWs w0 = prefill_bwd_ws(d, 0);
+  const int64_t slots = ws ? slots_for(d, (int64_t)ws_bytes - w0.comp_off) : -1;
+  if (slots < 0) return HLA_ERR_WORKSPACE;
+  const PrefillBwdWs w = prefill_bwd_ws(d, slots);
   char* base = static_cast<char*>(ws);
   const int32_t N = (int32_t)n_chunks(d);
   auto at = [&](int64_t off) { return static_cast<void*>(base + off); };
@@ -518,17 +561,12 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   r.B = d->B; r.T = d->T; r.H = d->H; r.ld_T = d->ld_T; r.N = N; r.C = d->C;
   e = hla::launch_route(r, d->dtype, d->dk, d->dv, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;
-  // 2. composition backward, first stage: replay every chain, keeping the step states and
-  //    writing the routed states
   float* dg = dgates ? dgates : fat(w.dg_off);
   hla::ComposeBwdArgs m{};
   m.At = c.At; m.Bc = c.Bc; m.gates = r.gates; m.mask = r.mask; m.S0 = S0; m.dS = fat(w.dsr_off);
   m.dAt = fat(w.dat_off); m.dBc = fat(w.dbc_off); m.dgates = dg; m.dS0 = dS0; m.S_routed = fat(w.sr_off);
-  set_compose_bwd_ws(m, compose_bwd_ws(d), at(w.comp_off));
+  set_compose_bwd_ws(m, compose_bwd_ws(d, slots), at(w.comp_off));
   m.B = d->B; m.H = d->H; m.N = N;
-  e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdSave, stream);
-  if (e != hipSuccess) return HLA_ERR_HIP;
-  // 3. outputs part of the chunk backward: dS~ and the chunk-local partial sums
   hla::ChunkBwdArgs cb{};
   cb.q = q; cb.k = k; cb.v = v; cb.beta = beta; cb.alpha = alpha;
   cb.B = d->B; cb.T = d->T; cb.H = d->H; cb.ld_T = d->ld_T; cb.N = N;
@@ -537,11 +575,25 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   cb.dAt = m.dAt; cb.dBc = m.dBc;
   set_chunk_bwd_ws(cb, chunk_bwd_ws(d), at(w.chunk_off));
   cb.dq = dq; cb.dk = dk; cb.dv = dv; cb.dbeta = dbeta; cb.dalpha = dalpha;
-  e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdOut, stream);
-  if (e != hipSuccess) return HLA_ERR_HIP;
-  // 4. composition backward, second stage: dAt, dBc, dgates, dS0; then the maps part
-  e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdReverse, stream);
-  if (e != hipSuccess) return HLA_ERR_HIP;
+  // 2-4 per group of query chunks (one group when the workspace holds every pair):
+  for (const auto& g : chain_groups(N, slots)) {
+    m.i0 = g.first; m.i1 = g.second; m.accumulate = g.first > 0;
+    // 2. composition backward, first stage: replay the group's chains, keeping the step
+    //    states and writing their routed states
+    e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdSave, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+    // 3. outputs part of the chunk backward for the group's chunks: dS~ and the chunk-local
+    //    partial sums
+    cb.c0 = g.first; cb.c1 = g.second;
+    e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdOut, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+    // 4. composition backward, second stage: the group's parts of dAt, dBc, dgates (dS0
+    //    after the last group)
+    e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdReverse, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+  }
+  // then the maps part of the chunk backward
+  cb.c0 = 0; cb.c1 = N;
   e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdMap, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;
   // 5. router (computed gates only), then the per-token sums

@@ -57,8 +57,8 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
   const int64_t id = blockIdx.x;
   const int cb = (int)(id % NB);
   const int64_t rest = id / NB;
-  const int c = (int)(rest % a.N);
-  const int64_t bh = rest / a.N;
+  const int c = a.c0 + (int)(rest % (a.c1 - a.c0));
+  const int64_t bh = rest / (a.c1 - a.c0);
   const int64_t h = bh % a.H, b = bh / a.H;
   const int64_t t0 = (int64_t)c * C;
   const int n = (int)((a.T - t0) < C ? (a.T - t0) : C);
@@ -304,9 +304,9 @@ __global__ __launch_bounds__(256) void chunk_bwd_finalize_kernel(ChunkBwdArgs a)
 
 template <class T, int DK, int DV>
 static hipError_t launch_chunk_bwd_t(const ChunkBwdArgs& a, int stages, hipStream_t s) {
-  const int64_t BHN = a.B * a.H * (int64_t)a.N;
+  const int64_t BHN = a.B * a.H * (int64_t)(a.c1 - a.c0);
   constexpr int NT = chunk_bwd_threads<DK>();
-  if (stages & (kChunkBwdOut | kChunkBwdMap)) {
+  if ((stages & (kChunkBwdOut | kChunkBwdMap)) && BHN > 0) {
     TimedLaunch tl(HLA_KERNEL_BWD_CHUNK, s);
     if (stages & kChunkBwdOut)
       hipLaunchKernelGGL((chunk_bwd_kernel<T, DK, DV, true>), dim3((unsigned)(BHN * (DV / 32))), dim3(NT), 0, s, a);

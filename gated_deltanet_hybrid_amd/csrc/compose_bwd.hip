@@ -28,6 +28,10 @@
 //      chunks i > j: dAt_j = sum_i (g lambda)_i M_i^T on the matrix cores, dBc_j = sum_i
 //      (g lambda)_i, and the gate gradients of column j;
 //   4. chain_sum_kernel: dS0 = sum over chains of the final lambda.
+// Passes 1 and 2 take the chains i0 <= i < i1 of one group, and pass 3 sums over that
+// group's chains only (adding to the sums of the earlier groups), so a caller with less
+// memory than every pair's states runs the chains in several groups, each group's pairs
+// stored in the same slots.
 // Every reduction runs in a fixed order (no atomics): results are deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -40,6 +44,12 @@ namespace {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int64_t pair_index(int i, int j) { return (int64_t)i * (i - 1) / 2 + j; }
+
+// Slot of pair (i, j) among the pairs of the chains i0 <= i < i1 (per (b, h)), and their count.
+__device__ __forceinline__ int64_t pair_slot(const ComposeBwdArgs& a, int i, int j) {
+  return pair_index(i, j) - pair_index(a.i0, 0);
+}
+__device__ __forceinline__ int64_t group_pairs(const ComposeBwdArgs& a) { return pair_index(a.i1, 0) - pair_index(a.i0, 0); }
 
 // Offset of element e of lane `lane` in the accumulator-lane-order image of one dk x dv
 // matrix: [dv/32 column tiles][dk/32 row tiles][64 lanes][16].
@@ -199,10 +209,10 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
   const int tid = threadIdx.x, lane = tid & 63, ct = tid >> 6, hh = lane >> 5, c32 = lane & 31;
   const int64_t BH = a.B * a.H;
   const int64_t bh = blockIdx.x % BH;
-  const int i = a.N - 1 - (int)(blockIdx.x / BH);  // longest chains first
+  const int i = a.i1 - 1 - (int)(blockIdx.x / BH);  // longest chains first
   const int N = a.N;
   const int col = ct * 32 + c32;
-  const int64_t P = (int64_t)N * (N - 1) / 2;
+  const int64_t P = group_pairs(a);
   T* Ms = reinterpret_cast<T*>(a.Msave) + bh * P * DK * DV;
   T* Ds = reinterpret_cast<T*>(a.Dsave) + bh * P * DK * DV;
   const T* Apb = reinterpret_cast<const T*>(a.Ap) + bh * N * (int64_t)DK * DK;
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
     const int jn = next_active(j + 1);
     if (jn < i) stage_load<T, DK, NTH>(pre, Apb + (int64_t)jn * DK * DK, tid);
     const float g = grow[j];
-    const int64_t p = pair_index(i, j);
+    const int64_t p = pair_slot(a, i, j);
     // the opaque lane offset keeps the compiler from holding 64 store addresses in
     // registers across the whole chain
     int lofs = hh * 4 * DV + col;
@@ -289,10 +299,10 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
   const int tid = threadIdx.x, lane = tid & 63, ct = tid >> 6, hh = lane >> 5, c32 = lane & 31;
   const int64_t BH = a.B * a.H;
   const int64_t bh = blockIdx.x % BH;
-  const int i = a.N - 1 - (int)(blockIdx.x / BH);
+  const int i = a.i1 - 1 - (int)(blockIdx.x / BH);
   const int N = a.N;
   const int col = ct * 32 + c32;
-  const int64_t P = (int64_t)N * (N - 1) / 2;
+  const int64_t P = group_pairs(a);
   const T* ATb = reinterpret_cast<const T*>(a.ApT) + bh * N * (int64_t)DK * DK;
   const T* Ds = reinterpret_cast<const T*>(a.Dsave) + bh * P * DK * DV;
   T* Ls = reinterpret_cast<T*>(a.Lsave) + bh * P * DK * DV;
@@ -313,7 +323,7 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
   u32x4 pre[AStage<T, DK, NTH>::NCP];
   u32x4 dcur[NRT][DPC], dnext[NRT][DPC];
   auto load_d = [&](u32x4 (&dst)[NRT][DPC], int j) {
-    const T* dd = Ds + pair_index(i, j) * DK * DV;
+    const T* dd = Ds + pair_slot(a, i, j) * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
@@ -344,7 +354,7 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
     }
     int lofs = hh * 4 * DV + col;  // opaque: see compose_save_kernel
     asm volatile("" : "+v"(lofs));
-    T* ld = Ls + pair_index(i, j) * DK * DV + lofs;
+    T* ld = Ls + pair_slot(a, i, j) * DK * DV + lofs;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
@@ -397,12 +407,12 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
   const int64_t bh = blockIdx.x % BH;
   const int j = (int)(blockIdx.x / BH);  // most query chunks first
   const int N = a.N;
-  const int64_t P = (int64_t)N * (N - 1) / 2;
+  const int64_t P = group_pairs(a);
   const T* Ms = reinterpret_cast<const T*>(a.Msave) + bh * P * DK * DV;
   const T* Ls = reinterpret_cast<const T*>(a.Lsave) + bh * P * DK * DV;
   auto active = [&](int i) { return a.mask[(bh * N + i) * (int64_t)N + j] != 0; };
-  auto next_active = [&](int i) {
-    while (i < N && !active(i)) ++i;
+  auto next_active = [&](int i) {  // the group's chains only
+    while (i < a.i1 && !active(i)) ++i;
     return i;
   };
 
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
     for (int e = 0; e < EPP; ++e) sb[c][e] = 0.f;
   u32x4 preL[NPC], preM[NPC];
   auto prefetch = [&](int i) {
-    const int64_t p = pair_index(i, j);
+    const int64_t p = pair_slot(a, i, j);
     const u32x4* L = reinterpret_cast<const u32x4*>(Ls + p * DK * DV);
     const u32x4* Mi = reinterpret_cast<const u32x4*>(Ms + p * DK * DV);
 #pragma unroll
@@ -426,9 +436,10 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
     }
   };
 
-  int i = next_active(j + 1);
-  if (i < N) prefetch(i);
-  while (i < N) {
+  int i = next_active(j + 1 > a.i0 ? j + 1 : a.i0);
+  const bool any = i < a.i1;
+  if (i < a.i1) prefetch(i);
+  while (i < a.i1) {
     __syncthreads();  // the previous chain's LDS reads are done
 #pragma unroll
     for (int c = 0; c < NPC; ++c) {
@@ -441,7 +452,7 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
     }
     __syncthreads();
     const int in = next_active(i + 1);
-    if (in < N) prefetch(in);
+    if (in < a.i1) prefetch(in);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int t = w * TPW + u, rt = t / NRT, st = t % NRT;
@@ -452,22 +463,29 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
     }
     i = in;
   }
-  float* dA = a.dAt + (bh * N + j) * (int64_t)DK * DK;
+  // the first group writes dAt_j and dBc_j, later groups add theirs (if they have a chain)
+  if (!a.accumulate || any) {
+    float* dA = a.dAt + (bh * N + j) * (int64_t)DK * DK;
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int t = w * TPW + u, rt = t / NRT, st = t % NRT;
+    for (int u = 0; u < TPW; ++u) {
+      const int t = w * TPW + u, rt = t / NRT, st = t % NRT;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dA[(int64_t)(rt * 32 + acc_row(e, hh)) * DK + st * 32 + c32] = acc[u][e];
+      for (int e = 0; e < 16; ++e) {
+        float* d = dA + (int64_t)(rt * 32 + acc_row(e, hh)) * DK + st * 32 + c32;
+        *d = a.accumulate ? *d + acc[u][e] : acc[u][e];
+      }
+    }
+    float* dB = a.dBc + (bh * N + j) * (int64_t)DK * DV;
+#pragma unroll
+    for (int c = 0; c < NPC; ++c) {
+      const int64_t e0 = (int64_t)(tid + c * 256) * EPP;
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) dB[e0 + e] = a.accumulate ? dB[e0 + e] + sb[c][e] : sb[c][e];
+    }
   }
-  float* dB = a.dBc + (bh * N + j) * (int64_t)DK * DV;
-#pragma unroll
-  for (int c = 0; c < NPC; ++c) {
-    const int64_t e0 = (int64_t)(tid + c * 256) * EPP;
-#pragma unroll
-    for (int e = 0; e < EPP; ++e) dB[e0 + e] = sb[c][e];
-  }
-  // gate gradients of column j (zero for skipped, diagonal and future pairs)
-  for (int ii = tid; ii < N; ii += 256) {
+  // gate gradients of column j in the group's rows (zero for skipped, diagonal and future
+  // pairs)
+  for (int ii = a.i0 + tid; ii < a.i1; ii += 256) {
     const int64_t o = (bh * N + ii) * N + j;
     float sg = 0.f;
     if (ii > j && a.mask[o]) {
@@ -492,25 +510,29 @@ __global__ __launch_bounds__(256) void chain_sum_kernel(const float* __restrict_
 
 template <class T, int DK, int DV>
 static hipError_t launch_compose_bwd_t(const ComposeBwdArgs& a, int stages, hipStream_t s) {
-  const int64_t BH = a.B * a.H, BHN = BH * a.N;
+  const int64_t BH = a.B * a.H, BHN = BH * a.N, BHG = BH * (a.i1 - a.i0);
   if (stages & kComposeBwdSave) {
     TimedLaunch tl(HLA_KERNEL_BWD_SAVE, s);
-    const int64_t nt = BHN * (DK / 16) * DK + BHN * (DV / 32) * (DK / 32) * 64;
-    hipLaunchKernelGGL((prep_bwd_kernel<T, DK, DV>), dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, a, BHN);
-    hipLaunchKernelGGL((compose_save_kernel<T, DK, DV>), dim3((unsigned)BHN), dim3(DV / 32 * 64), 0, s, a);
+    if (a.i0 == 0) {  // the reordered maps serve every group
+      const int64_t nt = BHN * (DK / 16) * DK + BHN * (DV / 32) * (DK / 32) * 64;
+      hipLaunchKernelGGL((prep_bwd_kernel<T, DK, DV>), dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, a, BHN);
+    }
+    if (BHG > 0)
+      hipLaunchKernelGGL((compose_save_kernel<T, DK, DV>), dim3((unsigned)BHG), dim3(DV / 32 * 64), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(stages & kComposeBwdReverse)) return e;
   {
     TimedLaunch tl(HLA_KERNEL_BWD_ADJOINT, s);
-    hipLaunchKernelGGL((compose_adjoint_kernel<T, DK, DV>), dim3((unsigned)BHN), dim3(DV / 32 * 64), 0, s, a);
+    if (BHG > 0)
+      hipLaunchKernelGGL((compose_adjoint_kernel<T, DK, DV>), dim3((unsigned)BHG), dim3(DV / 32 * 64), 0, s, a);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     TimedLaunch tl(HLA_KERNEL_BWD_REDUCE, s);
     hipLaunchKernelGGL((compose_grad_reduce_kernel<T, DK, DV>), dim3((unsigned)BHN), dim3(256), 0, s, a);
-    if (a.dS0) {
+    if (a.dS0 && a.i1 == a.N) {  // after the last group
       const int64_t per = (int64_t)DK * DV, total = BH * per;
       hipLaunchKernelGGL(chain_sum_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.lam_end, a.dS0,
                          a.N, per, total);

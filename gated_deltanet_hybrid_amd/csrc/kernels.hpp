@@ -154,6 +154,9 @@ struct ComposeBwdArgs {
   float* lam_end;        // workspace [B,H,N,dk,dv]: final lambda of every chain
   int64_t B, H;
   int32_t N;
+  // the group of chains (query chunks) i0 <= i < i1 this launch takes; its pairs fill the
+  // slots of Msave, Dsave and Lsave.  accumulate: add to dAt, dBc (a group after the first)
+  int32_t i0, i1, accumulate;
 };
 // Backward of the gated composition (see compose_bwd.hip).  `stages`: 1 the forward replay
 // that keeps the step states (and writes S_routed when asked), 2 the adjoint sweep and the
@@ -169,6 +172,7 @@ struct ChunkBwdArgs {
   const float* alpha;
   int64_t B, T, H, ld_T;
   int32_t N;                // 64-token chunks
+  int32_t c0, c1;           // the chunks c0 <= c < c1 that the outputs and maps parts take
   int32_t have_out;         // reverse of the outputs from chunk_init
   int32_t have_map;         // reverse of the chunk maps
   const float* chunk_init;  // [B,H,N,dk,dv] start state of every chunk (have_out)

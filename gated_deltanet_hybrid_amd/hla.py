@@ -21,6 +21,7 @@ KERNEL_CHUNK, KERNEL_SCAN, KERNEL_GATES, KERNEL_COMPOSE, KERNEL_DECODE, KERNEL_R
 KERNEL_BWD_SAVE, KERNEL_BWD_ADJOINT, KERNEL_BWD_REDUCE, KERNEL_BWD_CHUNK, KERNEL_BWD_ROUTER = 6, 7, 8, 9, 10
 FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX, FN_WU_HANDOFF, FN_CHUNK_REPS = 0, 1, 2, 3, 4
 FN_COMPOSE_BACKWARD, FN_PREFILL_BACKWARD, FN_CHUNK_BACKWARD = 5, 6, 7
+FN_COMPOSE_BACKWARD_MIN, FN_PREFILL_BACKWARD_MIN = 8, 9  # smallest workspaces (query chunks in groups)
 CHUNK = 64
 MAX_CACHE_SLOTS = 1024
 
@@ -416,7 +417,9 @@ def prefill_backward(q, k, v, beta, alpha, dO, tau=1e-3, gates_in=None, S0=None,
                      ws=None):
     """Gradients of the routed prefill (raw-key representatives, 64-token chunks) for the
     upstream gradient dO [B, T, H, dv] float32.  Returns dict(dq, dk, dv, dbeta, dalpha,
-    dS0, dgates), float32 (dS0 / dgates None unless wanted)."""
+    dS0, dgates), float32 (dS0 / dgates None unless wanted).  `ws` (uint8, device) may be
+    smaller than workspace_bytes(FN_PREFILL_BACKWARD) down to FN_PREFILL_BACKWARD_MIN's size:
+    the query chunks then run in groups whose per-pair states fit."""
     d = _inputs(k, v, beta, alpha, q=q)
     B, T, H, dk, dv = d.B, d.T, d.H, d.dk, d.dv
     N = math.ceil(T / CHUNK)

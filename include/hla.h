@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define HLA_ABI_VERSION 4
+#define HLA_ABI_VERSION 5
 
 typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype_t;
 
@@ -85,9 +85,11 @@ typedef enum {
                             hla_gdn_prefill: B H ceil(T / 64) 64 (dk + dv) bf16 values;
                             0 for float32, which takes no hand-off */
   HLA_FN_CHUNK_REPS = 4, /* workspace of hla_chunk_reps; n_rep = C / window */
-  HLA_FN_COMPOSE_BACKWARD = 5, /* workspace of hla_compose_backward */
-  HLA_FN_PREFILL_BACKWARD = 6, /* workspace of hla_prefill_backward */
-  HLA_FN_CHUNK_BACKWARD = 7    /* workspace of hla_chunk_backward */
+  HLA_FN_COMPOSE_BACKWARD = 5, /* workspace of hla_compose_backward (one pass) */
+  HLA_FN_PREFILL_BACKWARD = 6, /* workspace of hla_prefill_backward (one pass) */
+  HLA_FN_CHUNK_BACKWARD = 7,   /* workspace of hla_chunk_backward */
+  HLA_FN_COMPOSE_BACKWARD_MIN = 8, /* smallest workspace hla_compose_backward accepts */
+  HLA_FN_PREFILL_BACKWARD_MIN = 9  /* smallest workspace hla_prefill_backward accepts */
 } hla_fn_t;
 
 /*
@@ -309,11 +311,16 @@ hla_status_t hla_gdn2_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int3
  *   dgates     out [B, H, N, N] float32: dL/dg_ij for active j < i, 0 elsewhere.
  *   dS0        out [B, H, dk, dv] float32, or NULL.
  *   S_routed   out [B, H, N, dk, dv] float32 (the routed states, recomputed), or NULL.
- *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_COMPOSE_BACKWARD) bytes:
- *              (At - I), its transpose and Bc reordered for the matrix cores, and for
- *              every active step the state in front of it, (At_j - I) M + Bc_j and
- *              g lambda (dtype, N (N - 1) / 2 slots of dk x dv each per (b, h)), so it
- *              grows as N^2.
+ *   ws, ws_bytes: workspace: (At - I), its transpose and Bc reordered for the matrix
+ *              cores, and slots for the state in front of an active step, (At_j - I) M
+ *              + Bc_j and g lambda (dtype, dk x dv each).  With
+ *              hla_workspace_bytes(HLA_FN_COMPOSE_BACKWARD) bytes every pair j < i has
+ *              its slots (N (N - 1) / 2 per (b, h), so it grows as N^2) and the query
+ *              chunks run in one pass.  A smaller workspace, down to
+ *              hla_workspace_bytes(HLA_FN_COMPOSE_BACKWARD_MIN) (N - 1 slots: the
+ *              longest chain's pairs), runs consecutive groups of query chunks whose
+ *              pairs fit, as few as it can; the results agree up to the order of float32
+ *              sums over the groups.
  * Computation: bf16 (or float32) matrix-core products with float32 accumulation; sums in a
  * fixed order (deterministic).
  * Errors: HLA_ERR_NULL_ARG, HLA_ERR_BAD_SHAPE, HLA_ERR_BAD_DTYPE, HLA_ERR_ALIGN,
@@ -373,9 +380,11 @@ hla_status_t hla_chunk_backward(const hla_dims_t* d, const void* q, const void* 
  *   dO [B, T, H, dv] float32.
  *   dq, dk [B, T, H, dk], dv [B, T, H, dv], dbeta, dalpha [B, T, H]: float32 out.
  *   dS0 [B, H, dk, dv] float32 out or NULL;  dgates [B, H, N, N] float32 out or NULL.
- *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_PREFILL_BACKWARD)
- *              bytes; it holds the composition backward's per-pair states, so it grows as
- *              N^2 dk dv per (b, h).
+ *   ws, ws_bytes: workspace; it holds the composition backward's per-pair states.  With
+ *              hla_workspace_bytes(HLA_FN_PREFILL_BACKWARD) bytes (growing as N^2 dk dv
+ *              per (b, h)) all query chunks run in one pass; any size down to
+ *              hla_workspace_bytes(HLA_FN_PREFILL_BACKWARD_MIN) runs them in groups, as
+ *              for hla_compose_backward.
  * Errors: HLA_ERR_UNSUPPORTED (C != 64) and as hla_gdn_prefill.
  */
 hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void* k, const void* v,

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hla_abi_version() == 4
+    assert lib.hla_abi_version() == 5
     for s in range(0, 9):
         assert lib.hla_status_string(s)
     assert lib.hla_status_string(99) == b"unknown status"
@@ -247,8 +247,21 @@ def test_backward_workspace_sizes(lib):
     assert hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD, d4) - hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD, d) >= \
         3 * BH * 12 * 128 * 64 * 2
     out = ctypes.c_size_t()
-    for fn in (hla.FN_CHUNK_BACKWARD, hla.FN_PREFILL_BACKWARD):
+    for fn in (hla.FN_CHUNK_BACKWARD, hla.FN_PREFILL_BACKWARD, hla.FN_PREFILL_BACKWARD_MIN):
         assert lib.hla_workspace_bytes(fn, ctypes.byref(dims(C=128)), 0, ctypes.byref(out)) == UNSUPPORTED
+
+
+def test_backward_minimum_workspace(lib):
+    """The smallest workspaces hold the longest chain's pairs (N - 1 slots per (b, h)) of
+    each of the three per-pair arrays; everything else is as for one pass."""
+    for T, N in ((130, 3), (130 + 3 * 64, 6), (64, 1)):
+        d = dims(B=2, T=T, H=3, dk=128, dv=64, dtype=1)
+        BH, P_ = 6, N * (N - 1) // 2
+        slot = BH * 128 * 64 * 2
+        full, mn = hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD, d), hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD_MIN, d)
+        assert full - mn == 3 * slot * (P_ - max(N - 1, 0))
+        pf, pm = hla.workspace_bytes(hla.FN_PREFILL_BACKWARD, d), hla.workspace_bytes(hla.FN_PREFILL_BACKWARD_MIN, d)
+        assert pf - pm == full - mn
 
 
 def test_compose_backward_validation(lib):
@@ -262,7 +275,9 @@ def test_compose_backward_validation(lib):
         args[i] = None
         assert f(ctypes.byref(d), *args, P, need, None) == NULL_ARG, i
     args = [P] * 11
-    assert f(ctypes.byref(d), *args, P, need - 1, None) == WORKSPACE
+    mn = hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD_MIN, d)
+    assert mn < need  # N = 4 chunks: 3 slots per (b, h) instead of 6
+    assert f(ctypes.byref(d), *args, P, mn - 1, None) == WORKSPACE
     assert f(ctypes.byref(d), *args, None, 0, None) == WORKSPACE
     bad = list(args)
     bad[0] = PU
@@ -311,14 +326,17 @@ def test_prefill_backward_validation(lib):
     # (d, q, k, v, beta, alpha, S0, gates_in, tau, dO, dq, dk, dv, dbeta, dalpha, dS0, dgates, ws, ws_bytes, s)
     def call(args, tau=1e-3, ws=P, nb=need, dd=d):
         return f(ctypes.byref(dd), *args[:7], ctypes.c_float(tau), *args[7:], ws, nb, None)
-    full = [P] * 16
+    full = [P] * 15  # q .. gates_in (7), then dO .. dgates (8)
     for i in (0, 1, 2, 3, 4, 7, 8, 9, 10, 11, 12):
         a = list(full)
         a[i] = None
         assert call(a) == NULL_ARG, i
     opt = list(full)
-    opt[5] = opt[6] = opt[14] = opt[15] = None  # S0, gates_in, dS0, dgates are optional
-    assert call(opt, nb=need - 1) == WORKSPACE
+    opt[5] = opt[6] = opt[13] = opt[14] = None  # S0, gates_in, dS0, dgates are optional
+    mn = hla.workspace_bytes(hla.FN_PREFILL_BACKWARD_MIN, d)
+    assert mn < need
+    assert call(opt, nb=mn - 1) == WORKSPACE
+    assert call(opt, ws=None, nb=need) == WORKSPACE
     assert call(full, tau=float("nan")) == BAD_SHAPE
     assert call(full, dd=dims(C=256)) == UNSUPPORTED
     a = list(full)

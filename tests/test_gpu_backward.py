@@ -211,3 +211,75 @@ def test_prefill_backward_batch_and_token_window():
                 assert_close(host(g[n])[b, :, hh], ref[n], dtype, f"{n} b{b} h{hh}")
             assert_close(host(g["dgates"])[b, hh], ref["dgates"], dtype, "dgates")
             assert_close(host(g["dS0"])[b, hh], ref["dS0"].T, dtype, "dS0")
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_compose_backward_grouped(dtype):
+    """A workspace below the one-pass size runs the query chunks in groups (here the
+    smallest, one slot row per chain, and a third of the pairs): per-chain results (routed
+    states, gate gradients, dS0) are bit-identical to one pass; dAt and dBc differ only by
+    the order of the float32 sums over the groups."""
+    dk, dv, N, B, H = 128, 64, 11, 2, 2
+    note(f"compose backward, grouped, {dtype}")
+    At_s, Bc_s = inputs.gen_transitions(B, H, N, dk, dv, dtype=dtype, seed=81)
+    G = inputs.gen_gates(B, H, N, seed=82, mode="skip_heavy")
+    dS = inputs.gen_cotangent((B, H, N, dk, dv), seed=83, name="dS")
+    S0 = inputs.gen_state(B, H, dk, dv, seed=84)
+    h = hla()
+    At, Bc = dev(At_s, dtype), dev(Bc_s, dtype)
+    r = h.route_mix(None, None, At, Bc, tau=0.1, gates_in=f32(G), T=N * C, S0=f32(S0))
+    d = h.make_dims(B, N * C, H, N * C, dk, dv, 0 if dtype == "f32" else 1, C)
+    full, mn = h.workspace_bytes(h.FN_COMPOSE_BACKWARD, d), h.workspace_bytes(h.FN_COMPOSE_BACKWARD_MIN, d)
+    one = h.compose_backward(At, Bc, r["gates"], r["mask"], f32(dS), S0=f32(S0), want_states=True)
+    for size in (mn, mn + (full - mn) // 3):
+        ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+        g = h.compose_backward(At, Bc, r["gates"], r["mask"], f32(dS), S0=f32(S0), want_states=True, ws=ws)
+        torch.cuda.synchronize()
+        for n in ("S_routed", "dgates", "dS0"):
+            assert torch.equal(g[n], one[n]), (size, n)
+        for n in ("dAt", "dBc"):
+            assert _rel(host(g[n]), host(one[n])) <= 1e-5, (size, n)
+    A = inputs.to_f64(At_s, dtype).transpose(0, 1, 2, 4, 3)
+    Bm = inputs.to_f64(Bc_s, dtype).transpose(0, 1, 2, 4, 3)
+    fw = oracle.router_gates(np.zeros((N * C, dk)), np.zeros((N * C, dk)), C, C, 0.1, gates_in=G[1, 1].astype(np.float64))
+    ref = oracle.routed_states_backward(A[1, 1], Bm[1, 1], fw["ghat"], fw["mask"],
+                                        dS[1, 1].astype(np.float64).transpose(0, 2, 1),
+                                        S0=S0[1, 1].astype(np.float64).T)
+    assert_close(host(g["dAt"])[1, 1], ref["dA"].transpose(0, 2, 1), dtype, "dAt (grouped)")
+    assert_close(host(g["dBc"])[1, 1], ref["dB"].transpose(0, 2, 1), dtype, "dBc (grouped)")
+
+
+def test_prefill_backward_grouped():
+    """The whole backward with the smallest workspace (query chunks in many groups) and
+    with a third of the pairs' slots: against one pass and against the oracle."""
+    dtype, dk, dv, B, H, T = "bf16", 128, 64, 2, 2, 9 * C - 11
+    note("prefill backward, grouped")
+    x = inputs.gen_tokens(B, T, H, dk, dv, dtype=dtype, seed=91, alpha_mode="slow")
+    q, k, v, beta, alpha = (dev(x.q, dtype), dev(x.k, dtype), dev(x.v, dtype), f32(x.beta), f32(x.alpha))
+    S0 = inputs.gen_state(B, H, dk, dv, seed=92)
+    dO = inputs.gen_cotangent((B, T, H, dv), seed=93, name="dO")
+    h = hla()
+    d = h.make_dims(B, T, H, T, dk, dv, 1, C)
+    full, mn = h.workspace_bytes(h.FN_PREFILL_BACKWARD, d), h.workspace_bytes(h.FN_PREFILL_BACKWARD_MIN, d)
+    assert mn < full
+    one = h.prefill_backward(q, k, v, beta, alpha, f32(dO), tau=1e-3, S0=f32(S0))
+    names = ("dq", "dk", "dv", "dbeta", "dalpha", "dS0", "dgates")
+    for size in (mn, mn + (full - mn) // 3):
+        ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+        g = h.prefill_backward(q, k, v, beta, alpha, f32(dO), tau=1e-3, S0=f32(S0), ws=ws)
+        torch.cuda.synchronize()
+        for n in names:
+            assert _rel(host(g[n]), host(one[n])) <= 1e-5, (size, n)
+    b, hh = 1, 0
+    qq, kk, vv, bb, aa = (x.f64(n)[b, :, hh] for n in ("q", "k", "v", "beta", "alpha"))
+    ref = oracle.hla_prefill_backward(qq, kk, vv, bb, aa, C, 1e-3, dO[b, :, hh].astype(np.float64),
+                                      S0=S0[b, hh].astype(np.float64).T)
+    for n in ("dq", "dk", "dv", "dbeta", "dalpha"):
+        assert_close(host(g[n])[b, :, hh], ref[n], dtype, f"{n} (grouped)")
+    assert_close(host(g["dgates"])[b, hh], ref["dgates"], dtype, "dgates (grouped)")
+    assert_close(host(g["dS0"])[b, hh], ref["dS0"].T, dtype, "dS0 (grouped)")
