@@ -235,6 +235,16 @@ void* wu_internal(const hla_dims_t* d, const hla::ChunkArgs& a, const void* wu, 
   return (wu || !HLA_WU_HANDOFF || d->dtype != HLA_BF16 || a.variant != 0) ? nullptr : region;
 }
 
+// Maps that the library writes for its own scans (never a caller's buffer) carry Bc in the
+// scan's lane order, and the scan then hands the chunk start states on as the bf16 image the
+// output pass multiplies with (bf16 Gated DeltaNet; the Gated DeltaNet-2 pass and float32
+// keep the row-major forms).
+int32_t own_lanes(const hla_dims_t* d, const hla::ChunkArgs& a) { return d->dtype == HLA_BF16 && a.variant != 2; }
+void set_states(hla::ScanArgs& s, char* region) {
+  if (s.lanes) s.states_t = region;
+  else s.states = reinterpret_cast<float*>(region);
+}
+
 // Shared body of the transitions entry points (arguments validated by the caller; `a`
 // carries the token inputs of either recurrence).
 hla_status_t transitions_body(const hla_dims_t* d, hla::ChunkArgs a, void* At, void* Bc, void* wu, void* ws,
@@ -251,10 +261,11 @@ hla_status_t transitions_body(const hla_dims_t* d, hla::ChunkArgs a, void* At, v
   char* base = static_cast<char*>(ws);
   a.At = base + w.at_off;
   a.Bc = base + w.bc_off;
+  a.lanes = own_lanes(d, a);
   hipError_t e = chunk_pass(a, d, true, false, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;
   hla::ScanArgs s{};
-  s.At = a.At; s.Bc = a.Bc; s.B = d->B; s.H = d->H; s.N = a.N;
+  s.At = a.At; s.Bc = a.Bc; s.B = d->B; s.H = d->H; s.N = a.N; s.lanes = a.lanes;
   s.seg = d->C / kPiece; s.seg_At = At; s.seg_Bc = Bc;
   return hip_status(hla::launch_combine_segments(s, d->dk, d->dv, stream));
 }
@@ -280,18 +291,20 @@ hla_status_t prefill_body(const hla_dims_t* d, hla::ChunkArgs a, const float* S0
     a.At = base + w.at_off;
     a.Bc = base + w.bc_off;
     a.aux_out = wu_internal(d, a, wu, base + w.wu_off);
+    a.lanes = own_lanes(d, a);
     hipError_t e = chunk_pass(a, d, true, false, stream);
     if (e != hipSuccess) return HLA_ERR_HIP;
     hla::ScanArgs s{};
-    s.At = a.At; s.Bc = a.Bc; s.B = d->B; s.H = d->H; s.N = N;
+    s.At = a.At; s.Bc = a.Bc; s.B = d->B; s.H = d->H; s.N = N; s.lanes = a.lanes;
     s.seg = d->C / kPiece; s.seg_init = chunk_init;
-    s.states = reinterpret_cast<float*>(base + w.st_off);
+    set_states(s, base + w.st_off);
     e = hla::launch_scan_segments(s, d->dk, d->dv, stream);
     if (e != hipSuccess) return HLA_ERR_HIP;
     hla::ChunkArgs b = a;
-    b.At = nullptr; b.Bc = nullptr; b.aux_out = nullptr;
+    b.At = nullptr; b.Bc = nullptr; b.aux_out = nullptr; b.lanes = 0;
     b.aux_in = wu ? wu : a.aux_out;
     b.chunk_init = s.states;
+    b.chunk_init_t = s.states_t;
     return hip_status(chunk_pass(b, d, false, true, stream));
   }
   const int64_t need = o ? w.total : w.total_ab;
@@ -300,19 +313,21 @@ hla_status_t prefill_body(const hla_dims_t* d, hla::ChunkArgs a, const float* S0
   a.At = base + w.at_off;
   a.Bc = base + w.bc_off;
   if (o) a.aux_out = wu_internal(d, a, wu, base + w.wu_off);
+  a.lanes = own_lanes(d, a);
   hipError_t e = chunk_pass(a, d, true, false, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;
   hla::ScanArgs s{};
-  s.At = a.At; s.Bc = a.Bc; s.S0 = S0;
-  s.states = o ? reinterpret_cast<float*>(base + w.st_off) : nullptr;
+  s.At = a.At; s.Bc = a.Bc; s.S0 = S0; s.lanes = a.lanes;
+  if (o) set_states(s, base + w.st_off);
   s.S_final = S_final;
   s.B = d->B; s.H = d->H; s.N = N;
   e = hla::launch_scan(s, d->dtype, d->dk, d->dv, stream);
   if (e != hipSuccess || !o) return hip_status(e);
   hla::ChunkArgs b = a;
-  b.At = nullptr; b.Bc = nullptr; b.aux_out = nullptr;
+  b.At = nullptr; b.Bc = nullptr; b.aux_out = nullptr; b.lanes = 0;
   b.aux_in = wu ? wu : a.aux_out;
   b.chunk_init = s.states;
+  b.chunk_init_t = s.states_t;
   b.o = o;
   return hip_status(chunk_pass(b, d, false, true, stream));
 }

@@ -342,6 +342,21 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
         const T* arow = KT + (rt * 32 + c32) * PT;
 #pragma unroll
         for (int ks = 0; ks < C / MM::KS; ++ks) acc = MM::mma(MM::load_clayout(arow, ks, hh), bfr[ks], acc);
+        if constexpr (sizeof(T) == 2) {
+          if (!isw && a.lanes) {
+            // the scan's lane order: [chunk][dv/32 column tile][dk/32 row tile][64 lanes][16]
+            bf16* bl = reinterpret_cast<bf16*>(a.Bc) + (((cidx * (DV / 32) + col0 / 32) * (DK / 32) + rt) * 64 + lane) * 16;
+            bf16x8 lo, hi;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              lo[e] = (bf16)acc[e];
+              hi[e] = (bf16)acc[e + 8];
+            }
+            *reinterpret_cast<bf16x8*>(bl) = lo;
+            *reinterpret_cast<bf16x8*>(bl + 8) = hi;
+            continue;
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = rt * 32 + acc_row(e, hh), col = col0 + c32;
@@ -400,8 +415,15 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
           Qb[t * PK + col0 + c32] = from_f<T>(s_gam[t] * qv - res[sl][tt][e]);
         }
     }
-    const float* S0 = a.chunk_init + ((b * a.H + h) * a.N + c) * (int64_t)DK * DV;
-    if constexpr (sizeof(T) == 4) {
+    const float* S0 = a.chunk_init ? a.chunk_init + ((b * a.H + h) * a.N + c) * (int64_t)DK * DV : nullptr;
+    if (sizeof(T) == 2 && a.chunk_init_t) {
+      // the scan's bf16 image [dv][dk] of the start state: straight copies into padded rows
+      const bf16* src = reinterpret_cast<const bf16*>(a.chunk_init_t) + ((b * a.H + h) * a.N + c) * (int64_t)DV * DK;
+      for (int i = tid; i < DV * DK / 8; i += NT) {
+        const int r = i / (DK / 8), u = i % (DK / 8);
+        *reinterpret_cast<uint4*>(STb + r * PK + u * 8) = *reinterpret_cast<const uint4*>(src + r * DK + u * 8);
+      }
+    } else if constexpr (sizeof(T) == 4) {
       for (int i = tid; i < DK * DV / 4; i += NT) {
         const int dk = i / (DV / 4), dv = (i % (DV / 4)) * 4;
         const float4 val = *reinterpret_cast<const float4*>(S0 + dk * DV + dv);

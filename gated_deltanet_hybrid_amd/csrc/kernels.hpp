@@ -17,6 +17,8 @@ struct ChunkArgs {
   void* At;                // out [B,H,N,dk,dk] (dtype) when transitions are wanted
   void* Bc;                // out [B,H,N,dk,dv]
   const float* chunk_init; // [B,H,N,dk,dv] start state of every chunk (outputs wanted)
+  const void* chunk_init_t;  // or (bf16) the same states as bf16 [B,H,N,dv,dk], from the scan
+  int32_t lanes;           // transitions: write Bc in the scan's lane order (bf16)
   float* o;                // out [B,T,H,dv]
   // W | U of every chunk in the output pass's B-operand fragment order (bf16 only):
   // written by the transitions pass when aux_out is set, read by the output pass (which
@@ -53,6 +55,11 @@ struct ScanArgs {
   const float* seg_init;  // [B,H,NS,dk,dv]: start state of every segment (states are written)
   void* seg_At;           // out [B,H,NS,dk,dk] (bf16): composite map of every segment
   void* seg_Bc;           // out [B,H,NS,dk,dv] (bf16)
+  // bf16 maps from the library's own transitions pass (lanes != 0): Bc in the
+  // accumulator's lane order [B,H,N, dv/32, dk/32, 64, 16], and the start states written
+  // to states_t as bf16 [B,H,N,dv,dk] instead of to states
+  int32_t lanes;
+  void* states_t;
 };
 // Sequential chunk scan M_{c+1} = At_c M_c + Bc_c (S0, states, S_final).
 hipError_t launch_scan(const ScanArgs& a, int dtype, int dk, int dv, hipStream_t s);

@@ -133,23 +133,34 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
 // bf16 transitions: one workgroup per (b, h, 32-column block) with one wave per 32-row
 // tile.  Wave rt keeps rows [32 rt, 32 rt + 32) of the state block in its accumulators and
 // needs only those rows of At: its A fragments (row 32 rt + lane%32, 8 consecutive k) come
-// straight from global memory into registers, one chunk ahead.  The B operand is the whole
-// 128 x 32 state block in bf16; every wave writes its tile into an LDS image laid out
-// [column][k] (so a B fragment is one 16-byte read) and one barrier per chunk publishes it.
-// The image is double-buffered: buffer c % 2 is rewritten only after the next barrier, when
-// every wave has read it.  Bc seeds the accumulator (fp32), so no extra products are needed.
+// straight from global memory into registers.  The B operand is the whole 128 x 32 state
+// block in bf16; every wave writes its tile into an LDS image laid out [column][k] (so a B
+// fragment is one 16-byte read) and one barrier per chunk publishes it.  The image is
+// double-buffered: buffer c % 2 is rewritten only after the next barrier, when every wave
+// has read it.  Bc seeds the accumulator (fp32), so no extra products are needed.
+//
+// LANES (maps written by the library's own transitions pass): Bc comes in the accumulator's
+// lane order, [chunk][dv/32 column tile][dk/32 row tile][64 lanes][16], two 16-byte loads
+// per lane, and the At rows and Bc of the next kScanDepth chunks are in flight in a
+// register ring (a step is a few products and one barrier, far shorter than a load from
+// HBM).  The start state of every chunk is written as the bf16 image [dv][dk] that the
+// output pass multiplies with (it rounds the state to bf16 there in any case).  Without
+// LANES, Bc is row-major, one chunk is loaded ahead and the states are float32 [dk][dv].
 //
 // MODE 0: one scan over all N chunks from S0 (states, S_final).
 // MODE 1: independent segments of `seg` chunks, each starting from its seg_init state; the
-//         start state of every chunk is written to `states` (a chunk of C = 64 seg tokens
-//         seen as seg chunks of 64).
+//         start state of every chunk is written (a chunk of C = 64 seg tokens seen as seg
+//         chunks of 64).
 // MODE 2: the composite map of every segment: the scan runs over the augmented state
 //         [At_seg | Bc_seg] (dk x (dk + dv)) from [I | 0], the additive term being [0 | Bc]
 //         ([HLA] Methodology paragraph 1: affine maps compose; the map of a chunk of C tokens
 //         is the composition of the maps of its 64-token pieces).
-template <int DK, int DV, int MODE>
+constexpr int kScanDepth = 3;
+
+template <int DK, int DV, int MODE, bool LANES>
 __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
-  constexpr int NCT = (MODE == 2 ? DK + DV : DV) / 32, NKS = DK / 16;
+  constexpr int NCT = (MODE == 2 ? DK + DV : DV) / 32, NKS = DK / 16, NRT = DK / 32;
+  constexpr int DEPTH = LANES ? kScanDepth : 1;
   constexpr int PB = DK + 8;  // bf16 pitch of an image row (one row per state column)
   __shared__ __attribute__((aligned(16))) bf16 sB0[32 * PB];
   __shared__ __attribute__((aligned(16))) bf16 sB1[32 * PB];
@@ -171,11 +182,15 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
   }
   // MODE 2: column blocks [0, DK/32) are the At part (additive term 0), the rest the Bc part
   const bool apart = MODE == 2 && ct < DK / 32;
-  const int bcolumn = MODE == 2 ? (apart ? 0 : (ct - DK / 32) * 32) : ct * 32;
+  const int ctv = MODE == 2 ? (apart ? 0 : ct - DK / 32) : ct;  // column tile of Bc
   const bf16* arow = reinterpret_cast<const bf16*>(a.At) + (bh * N + c0) * (int64_t)DK * DK + (rt * 32 + c32) * DK +
                      hh * 8;
-  const bf16* bcol =
-      reinterpret_cast<const bf16*>(a.Bc) + (bh * N + c0) * (int64_t)DK * DV + rt * 32 * DV + bcolumn + c32;
+  // this lane's Bc values of chunk c: 16 rows (row_of) of one column, row-major or lane order
+  const bf16* bbase = reinterpret_cast<const bf16*>(a.Bc) + (bh * N + c0) * (int64_t)DK * DV;
+  auto bc_ptr = [&](int c) {
+    return LANES ? bbase + (int64_t)c * DK * DV + (((int64_t)ctv * NRT + rt) * 64 + lane) * 16
+                 : bbase + (int64_t)c * DK * DV + rt * 32 * DV + ctv * 32 + c32;
+  };
   // accumulator element e of this lane: row 32 rt + (e / 4) 8 + 4 hh + e % 4, column 32 ct + c32
   auto row_of = [&](int e) { return (e >> 2) * 8 + hh * 4 + (e & 3); };
 
@@ -198,63 +213,109 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
       const bf16* p0 = reinterpret_cast<const bf16*>(a.At) + (bh * N + c0) * (int64_t)DK * DK + rt * 32 * DK + ct * 32 + c32;
 #pragma unroll
       for (int e = 0; e < 16; ++e) M[e] = (float)p0[row_of(e) * DK];
-    } else {
+    } else if (LANES) {
+      const bf16x8* p = reinterpret_cast<const bf16x8*>(bc_ptr(0));
+      const bf16x8 lo = p[0], hi = p[1];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) M[e] = (float)bcol[row_of(e) * DV];
+      for (int e = 0; e < 8; ++e) {
+        M[e] = (float)lo[e];
+        M[e + 8] = (float)hi[e];
+      }
+    } else {
+      const bf16* p = bc_ptr(0);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) M[e] = (float)p[row_of(e) * DV];
     }
   }
   // MODE 1 never needs the end state of a segment's last piece
   const int nmul = MODE == 1 ? nsub - 1 : nsub;
-  bf16x8 af[NKS];
-  bf16 bcv[16];
-  auto load = [&](int c) __attribute__((always_inline)) {
+  bf16x8 af[DEPTH][NKS];
+  bf16x8 bl[DEPTH][2];   // LANES: 16 Bc values in lane order
+  bf16 bcv[DEPTH][16];   // otherwise: 16 Bc values, one load each
+  // the loads of one ring slot; the At part of MODE 2 has no additive term (its Bc loads
+  // read the first column tile and are not used, so every slot's loads are unconditional)
+  auto load = [&](int slot, int c) __attribute__((always_inline)) {
     const bf16* ap = arow + (int64_t)c * DK * DK;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(ap + ks * 16);
-    if (!apart) {
-      const bf16* bp = bcol + (int64_t)c * DK * DV;
+    for (int ks = 0; ks < NKS; ++ks) af[slot][ks] = *reinterpret_cast<const bf16x8*>(ap + ks * 16);
+    if constexpr (LANES) {
+      const bf16x8* p = reinterpret_cast<const bf16x8*>(bc_ptr(c));
+      bl[slot][0] = p[0];
+      bl[slot][1] = p[1];
+    } else {
+      const bf16* p = bc_ptr(c);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) bcv[e] = bp[row_of(e) * DV];
+      for (int e = 0; e < 16; ++e) bcv[slot][e] = p[row_of(e) * DV];
     }
   };
-  auto store_state = [&](float* dst) __attribute__((always_inline)) {
-    float* p = dst + rt * 32 * DV + ct * 32 + c32;
+  auto store_state = [&](int c) __attribute__((always_inline)) {
+    if constexpr (LANES) {
+      // bf16 image [dv][dk]: this lane's column is one row of it, 4 runs of 4 consecutive k
+      bf16* p = reinterpret_cast<bf16*>(a.states_t) + ((bh * N + c0 + c) * (int64_t)DV + ct * 32 + c32) * DK +
+                rt * 32 + hh * 4;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)M[gq * 4 + e];
+        *reinterpret_cast<bf16x4*>(p + gq * 8) = v;
+      }
+    } else {
+      float* p = a.states + (bh * N + c0 + c) * (int64_t)DK * DV + rt * 32 * DV + ct * 32 + c32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p[row_of(e) * DV] = M[e];
+    }
+  };
+  const bool want_states = MODE != 2 && (LANES ? a.states_t != nullptr : a.states != nullptr);
+#pragma unroll
+  for (int sl = 0; sl < DEPTH; ++sl)
+    if (cstart + sl < nmul) load(sl, cstart + sl);
+  for (int cb = cstart; cb < nsub; cb += DEPTH) {
+#pragma unroll
+    for (int sl = 0; sl < DEPTH; ++sl) {  // unrolled: every ring slot index is static
+      const int c = cb + sl;
+      if (c >= nsub) break;
+      if (want_states) store_state(c);
+      if (c >= nmul) break;
+      bf16* img = (c & 1) ? sB1 : sB0;
+      // this wave's rows of bf16(M) into the image: 4 runs of 4 consecutive k per lane
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)M[gq * 4 + e];
+        *reinterpret_cast<bf16x4*>(img + c32 * PB + rt * 32 + gq * 8 + hh * 4) = v;
+      }
+      __syncthreads();
+      f32x16 acc0, acc1 = zero16();
+      if constexpr (LANES) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc0[e] = apart ? 0.f : (float)bl[sl][0][e];
+          acc0[e + 8] = apart ? 0.f : (float)bl[sl][1][e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc0[e] = apart ? 0.f : (float)bcv[sl][e];
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(img + c32 * PB + ks * 16 + hh * 8);
+        if (ks & 1)
+          acc1 = Mma<bf16>::mma(af[sl][ks], bfr, acc1);
+        else
+          acc0 = Mma<bf16>::mma(af[sl][ks], bfr, acc0);
+      }
+      if (c + DEPTH < nmul) load(sl, c + DEPTH);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) M[e] = acc0[e] + acc1[e];
+    }
+  }
+  if (MODE == 0 && a.S_final) {
+    float* p = a.S_final + bh * (int64_t)DK * DV + rt * 32 * DV + ct * 32 + c32;
 #pragma unroll
     for (int e = 0; e < 16; ++e) p[row_of(e) * DV] = M[e];
-  };
-  if (cstart < nmul) load(cstart);
-  for (int c = cstart; c < nsub; ++c) {
-    if (MODE != 2 && a.states) store_state(a.states + (bh * N + c0 + c) * (int64_t)DK * DV);
-    if (c >= nmul) break;
-    bf16* img = (c & 1) ? sB1 : sB0;
-    // this wave's rows of bf16(M) into the image: 4 runs of 4 consecutive k per lane
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      bf16x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (bf16)M[gq * 4 + e];
-      *reinterpret_cast<bf16x4*>(img + c32 * PB + rt * 32 + gq * 8 + hh * 4) = v;
-    }
-    __syncthreads();
-    f32x16 acc0, acc1 = zero16();
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc0[e] = apart ? 0.f : (float)bcv[e];
-    bf16x8 cur[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) cur[ks] = af[ks];
-    if (c + 1 < nmul) load(c + 1);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(img + c32 * PB + ks * 16 + hh * 8);
-      if (ks & 1)
-        acc1 = Mma<bf16>::mma(cur[ks], bfr, acc1);
-      else
-        acc0 = Mma<bf16>::mma(cur[ks], bfr, acc0);
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) M[e] = acc0[e] + acc1[e];
   }
-  if (MODE == 0 && a.S_final) store_state(a.S_final + bh * (int64_t)DK * DV);
   if (MODE == 2) {
     const int64_t sidx = bh * NS + g;
     if (apart) {
@@ -262,7 +323,7 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) p[row_of(e) * DK] = (bf16)M[e];
     } else {
-      bf16* p = reinterpret_cast<bf16*>(a.seg_Bc) + sidx * DK * DV + rt * 32 * DV + bcolumn + c32;
+      bf16* p = reinterpret_cast<bf16*>(a.seg_Bc) + sidx * DK * DV + rt * 32 * DV + ctv * 32 + c32;
 #pragma unroll
       for (int e = 0; e < 16; ++e) p[row_of(e) * DV] = (bf16)M[e];
     }
@@ -296,7 +357,10 @@ static hipError_t launch_scan_bf16_t(const ScanArgs& a, hipStream_t s) {
   const int64_t nb = a.B * a.H * ns * NCT;
   if (nb == 0) return hipSuccess;
   TimedLaunch tl(HLA_KERNEL_SCAN, s);
-  hipLaunchKernelGGL((scan_bf16_kernel<DK, DV, MODE>), dim3((unsigned)nb), dim3(DK / 32 * 64), 0, s, a);
+  if (a.lanes)
+    hipLaunchKernelGGL((scan_bf16_kernel<DK, DV, MODE, true>), dim3((unsigned)nb), dim3(DK / 32 * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((scan_bf16_kernel<DK, DV, MODE, false>), dim3((unsigned)nb), dim3(DK / 32 * 64), 0, s, a);
   return hipGetLastError();
 }
 
