@@ -144,8 +144,11 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
 // per lane, and the At rows and Bc of the next kScanDepth chunks are in flight in a
 // register ring (a step is a few products and one barrier, far shorter than a load from
 // HBM).  The start state of every chunk is written as the bf16 image [dv][dk] that the
-// output pass multiplies with (it rounds the state to bf16 there in any case).  Without
-// LANES, Bc is row-major, one chunk is loaded ahead and the states are float32 [dk][dv].
+// output pass multiplies with (it rounds the state to bf16 there in any case): the LDS
+// image of the step is that state already, and one more wave copies it out.  That wave
+// issues every global store of the loop, so the product waves issue only loads and their
+// waits for the ring never also wait for stores.  Without LANES, Bc is row-major, one
+// chunk is loaded ahead and the product waves store the float32 states [dk][dv].
 //
 // MODE 0: one scan over all N chunks from S0 (states, S_final).
 // MODE 1: independent segments of `seg` chunks, each starting from its seg_init state; the
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
 constexpr int kScanDepth = 3;
 
 template <int DK, int DV, int MODE, bool LANES>
-__global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
+__global__ __launch_bounds__(DK / 32 * 64 + (LANES ? 64 : 0)) void scan_bf16_kernel(ScanArgs a) {
   constexpr int NCT = (MODE == 2 ? DK + DV : DV) / 32, NKS = DK / 16, NRT = DK / 32;
   constexpr int DEPTH = LANES ? kScanDepth : 1;
   constexpr int PB = DK + 8;  // bf16 pitch of an image row (one row per state column)
@@ -179,6 +182,28 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
     bh = rest / NS;
     c0 = g * a.seg;
     nsub = N - c0 < a.seg ? N - c0 : a.seg;
+  }
+  // MODE 1 never needs the end state of a segment's last piece
+  const int nmul = MODE == 1 ? nsub - 1 : nsub;
+  const bool want_states = MODE != 2 && (LANES ? a.states_t != nullptr : a.states != nullptr);
+  if (LANES && rt == NRT) {
+    // the writer wave: after each step's barrier, the image of the chunk's start state goes
+    // out to states_t (row ct * 32 + r of the [dv][dk] image is image row r); the barrier
+    // sequence is the product waves'
+    const int nstep = want_states ? nsub : nmul;
+    for (int c = (MODE == 2 && nsub > 0) ? 1 : 0; c < nstep; ++c) {
+      __syncthreads();
+      if (want_states) {
+        const bf16* img = (c & 1) ? sB1 : sB0;
+        bf16* dst = reinterpret_cast<bf16*>(a.states_t) + ((bh * N + c0 + c) * (int64_t)DV + ct * 32) * DK;
+#pragma unroll
+        for (int i = lane; i < 32 * (DK / 8); i += 64) {
+          const int r = i / (DK / 8), u = i % (DK / 8);
+          *reinterpret_cast<uint4*>(dst + r * DK + u * 8) = *reinterpret_cast<const uint4*>(img + r * PB + u * 8);
+        }
+      }
+    }
+    return;
   }
   // MODE 2: column blocks [0, DK/32) are the At part (additive term 0), the rest the Bc part
   const bool apart = MODE == 2 && ct < DK / 32;
@@ -227,8 +252,6 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
       for (int e = 0; e < 16; ++e) M[e] = (float)p[row_of(e) * DV];
     }
   }
-  // MODE 1 never needs the end state of a segment's last piece
-  const int nmul = MODE == 1 ? nsub - 1 : nsub;
   bf16x8 af[DEPTH][NKS];
   bf16x8 bl[DEPTH][2];   // LANES: 16 Bc values in lane order
   bf16 bcv[DEPTH][16];   // otherwise: 16 Bc values, one load each
@@ -248,25 +271,11 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
       for (int e = 0; e < 16; ++e) bcv[slot][e] = p[row_of(e) * DV];
     }
   };
-  auto store_state = [&](int c) __attribute__((always_inline)) {
-    if constexpr (LANES) {
-      // bf16 image [dv][dk]: this lane's column is one row of it, 4 runs of 4 consecutive k
-      bf16* p = reinterpret_cast<bf16*>(a.states_t) + ((bh * N + c0 + c) * (int64_t)DV + ct * 32 + c32) * DK +
-                rt * 32 + hh * 4;
+  auto store_state = [&](int c) __attribute__((always_inline)) {  // float32 states (not LANES)
+    float* p = a.states + (bh * N + c0 + c) * (int64_t)DK * DV + rt * 32 * DV + ct * 32 + c32;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)M[gq * 4 + e];
-        *reinterpret_cast<bf16x4*>(p + gq * 8) = v;
-      }
-    } else {
-      float* p = a.states + (bh * N + c0 + c) * (int64_t)DK * DV + rt * 32 * DV + ct * 32 + c32;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) p[row_of(e) * DV] = M[e];
-    }
+    for (int e = 0; e < 16; ++e) p[row_of(e) * DV] = M[e];
   };
-  const bool want_states = MODE != 2 && (LANES ? a.states_t != nullptr : a.states != nullptr);
 #pragma unroll
   for (int sl = 0; sl < DEPTH; ++sl)
     if (cstart + sl < nmul) load(sl, cstart + sl);
@@ -275,8 +284,10 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
     for (int sl = 0; sl < DEPTH; ++sl) {  // unrolled: every ring slot index is static
       const int c = cb + sl;
       if (c >= nsub) break;
-      if (want_states) store_state(c);
-      if (c >= nmul) break;
+      if (!LANES && want_states) store_state(c);
+      // the last piece of a MODE 1 segment needs no product: only (LANES) its image, for
+      // the writer wave
+      if (c >= nmul && !(LANES && want_states)) break;
       bf16* img = (c & 1) ? sB1 : sB0;
       // this wave's rows of bf16(M) into the image: 4 runs of 4 consecutive k per lane
 #pragma unroll
@@ -287,6 +298,7 @@ __global__ __launch_bounds__(DK / 32 * 64) void scan_bf16_kernel(ScanArgs a) {
         *reinterpret_cast<bf16x4*>(img + c32 * PB + rt * 32 + gq * 8 + hh * 4) = v;
       }
       __syncthreads();
+      if (c >= nmul) break;
       f32x16 acc0, acc1 = zero16();
       if constexpr (LANES) {
 #pragma unroll
@@ -358,7 +370,7 @@ static hipError_t launch_scan_bf16_t(const ScanArgs& a, hipStream_t s) {
   if (nb == 0) return hipSuccess;
   TimedLaunch tl(HLA_KERNEL_SCAN, s);
   if (a.lanes)
-    hipLaunchKernelGGL((scan_bf16_kernel<DK, DV, MODE, true>), dim3((unsigned)nb), dim3(DK / 32 * 64), 0, s, a);
+    hipLaunchKernelGGL((scan_bf16_kernel<DK, DV, MODE, true>), dim3((unsigned)nb), dim3(DK / 32 * 64 + 64), 0, s, a);
   else
     hipLaunchKernelGGL((scan_bf16_kernel<DK, DV, MODE, false>), dim3((unsigned)nb), dim3(DK / 32 * 64), 0, s, a);
   return hipGetLastError();
