@@ -49,7 +49,9 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) char sm1[R1];
   __shared__ __attribute__((aligned(16))) char sm2[R2];
   __shared__ __attribute__((aligned(16))) char sm3[R3];
-  __shared__ float s_beta[C], s_g[C], s_gam[C];
+  // per token: beta, cumulative log decay g, gamma = exp(g), beta gamma, D = exp(g_63 - g)
+  __shared__ __attribute__((aligned(16))) float s_beta[C], s_g[C], s_gam[C], s_bg[C];
+  __shared__ float s_d[WANT_AB ? C : 1];  // (an output pass keeps two workgroups per CU)
 
   T* Kp = reinterpret_cast<T*>(sm1);
   T* Qp = Kp + C * PK;
@@ -149,9 +151,12 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
         const float y = __shfl_up(x, off, 64);
         if (lane >= off) x += y;
       }
+      const float gam = expf(x), g_end = __shfl(x, 63, 64);
       s_beta[tid] = bt;
       s_g[tid] = x;
-      s_gam[tid] = expf(x);
+      s_gam[tid] = gam;
+      s_bg[tid] = bt * gam;
+      if constexpr (WANT_AB) s_d[tid] = expf(g_end - x);
     }
   }
   __syncthreads();
@@ -266,15 +271,22 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
     for (int tt = 0; tt < 2; ++tt) {
       f32x16 acc = zero16();
       const float* xrow = Xb + (tt * 32 + c32) * PX;
+      const float* fac = isw ? s_bg : s_beta;  // column factor: beta gamma for W, beta for U
 #pragma unroll
       for (int ks = 0; ks < C / MM::KS; ++ks) {
         const auto bf = MM::load_plain(brow, ks, hh);
         if constexpr (sizeof(T) == 2) {
+          // 8 consecutive entries of this lane's X row and their factors, 16-byte reads
+          const int s0 = ks * 16 + hh * 8;
+          float xv[8], fv[8];
+          *reinterpret_cast<float4*>(xv) = *reinterpret_cast<const float4*>(xrow + s0);
+          *reinterpret_cast<float4*>(xv + 4) = *reinterpret_cast<const float4*>(xrow + s0 + 4);
+          *reinterpret_cast<float4*>(fv) = *reinterpret_cast<const float4*>(fac + s0);
+          *reinterpret_cast<float4*>(fv + 4) = *reinterpret_cast<const float4*>(fac + s0 + 4);
           bf16x8 ahi, alo;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int s = ks * 16 + hh * 8 + e;
-            const float x = xrow[s] * (isw ? s_beta[s] * s_gam[s] : s_beta[s]);
+            const float x = xv[e] * fv[e];
             const bf16 hv = (bf16)x;
             ahi[e] = hv;
             alo[e] = (bf16)(x - (float)hv);
@@ -283,7 +295,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
           acc = MM::mma(alo, bf, acc);
         } else {
           const int s = ks * 2 + hh;
-          acc = MM::mma(xrow[s] * (isw ? s_beta[s] * s_gam[s] : s_beta[s]), bf, acc);
+          acc = MM::mma(xrow[s] * fac[s], bf, acc);
         }
       }
       wu[sl][tt] = acc;
@@ -309,7 +321,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
 
   // ---- 5. transitions: At = gamma_63 I - K^T D W,  Bc = K^T D U
   if constexpr (WANT_AB) {
-    const float gam_n = s_gam[C - 1], g_n = s_g[C - 1];
+    const float gam_n = s_gam[C - 1];
     const int64_t cidx = (b * a.H + h) * a.N + c;
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
@@ -326,12 +338,12 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int ai = (ks & 1) * 8 + e;
-            f[e] = (bf16)(wu[sl][tt][ai] * expf(g_n - s_g[tt * 32 + acc_row(ai, hh)]));
+            f[e] = (bf16)(wu[sl][tt][ai] * s_d[tt * 32 + acc_row(ai, hh)]);
           }
           bfr[ks] = f;
         } else {
           const int ai = ks & 15;
-          bfr[ks] = wu[sl][tt][ai] * expf(g_n - s_g[tt * 32 + acc_row(ai, hh)]);
+          bfr[ks] = wu[sl][tt][ai] * s_d[tt * 32 + acc_row(ai, hh)];
         }
       }
       T* out = isw ? reinterpret_cast<T*>(a.At) + cidx * DK * DK : reinterpret_cast<T*>(a.Bc) + cidx * DK * DV;
