@@ -423,7 +423,9 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int t = tt * 32 + acc_row(e, hh);
-          const float qv = t < n ? to_f<T>(qg[t * kstride + col0 + c32]) : 0.f;
+          // with the hand-off nothing overwrote the staged Q (zero past n); otherwise L and X
+          // did, and q is read again
+          const float qv = AUXIN ? to_f<T>(Qp[t * PK + col0 + c32]) : (t < n ? to_f<T>(qg[t * kstride + col0 + c32]) : 0.f);
           Qb[t * PK + col0 + c32] = from_f<T>(s_gam[t] * qv - res[sl][tt][e]);
         }
     }
