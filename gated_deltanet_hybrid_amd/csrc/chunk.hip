@@ -346,8 +346,11 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
           bfr[ks] = wu[sl][tt][ai] * s_d[tt * 32 + acc_row(ai, hh)];
         }
       }
-      T* out = isw ? reinterpret_cast<T*>(a.At) + cidx * DK * DK : reinterpret_cast<T*>(a.Bc) + cidx * DK * DV;
-      const int ld = isw ? DK : DV;
+      // row-major stores: one base address per lane (row 32 rt + 4 hh, column col0 + c32)
+      // and compile-time strides, so the 16 stores of a tile differ only in their offsets;
+      // gamma_63 is added on the diagonal of At's diagonal tiles only
+      T* const base = isw ? reinterpret_cast<T*>(a.At) + cidx * DK * DK + (hh * 4) * DK + col0 + c32
+                          : reinterpret_cast<T*>(a.Bc) + cidx * DK * DV + (hh * 4) * DV + col0 + c32;
 #pragma unroll
       for (int rt = 0; rt < DK / 32; ++rt) {
         f32x16 acc = zero16();
@@ -369,11 +372,21 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
             continue;
           }
         }
+        if (isw) {
+          if (rt * 32 == col0) {  // diagonal tile: row == column where acc_row(e) == c32
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = rt * 32 + acc_row(e, hh), col = col0 + c32;
-          const float val = isw ? ((row == col ? gam_n : 0.f) - acc[e]) : acc[e];
-          out[row * ld + col] = from_f<T>(val);
+            for (int e = 0; e < 16; ++e) acc[e] = (acc_row(e, hh) == c32 ? gam_n : 0.f) - acc[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = -acc[e];
+          }
+          T* o = base + rt * 32 * DK;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[((e >> 2) * 8 + (e & 3)) * DK] = from_f<T>(acc[e]);
+        } else {
+          T* o = base + rt * 32 * DV;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[((e >> 2) * 8 + (e & 3)) * DV] = from_f<T>(acc[e]);
         }
       }
     }
