@@ -494,10 +494,16 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
         const T* arow = Qb + (tt * 32 + c32) * PK;
 #pragma unroll
         for (int ks = 0; ks < DK / MM::KS; ++ks) acc = MM::mma(MM::load_plain(arow, ks, hh), MM::load_plain(brow, ks, hh), acc);
+        // token t = 32 tt + acc_row(e): rows of o are H DV floats apart
+        const int64_t ostride = a.H * DV;
+        float* ob = a.o + ((b * a.T + t0 + tt * 32 + hh * 4) * a.H + h) * DV + col0 + c32;
+        if (n == C) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int t = tt * 32 + acc_row(e, hh);
-          if (t < n) a.o[((b * a.T + t0 + t) * a.H + h) * DV + col0 + c32] = acc[e];
+          for (int e = 0; e < 16; ++e) ob[((e >> 2) * 8 + (e & 3)) * ostride] = acc[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (tt * 32 + acc_row(e, hh) < n) ob[((e >> 2) * 8 + (e & 3)) * ostride] = acc[e];
         }
       }
     }
