@@ -429,10 +429,11 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
     const int64_t p = pair_slot(a, i, j);
     const u32x4* L = reinterpret_cast<const u32x4*>(Ls + p * DK * DV);
     const u32x4* Mi = reinterpret_cast<const u32x4*>(Ms + p * DK * DV);
+    // the last read of a pair's states: non-temporal loads, which leave the caches to data read again
 #pragma unroll
     for (int c = 0; c < NPC; ++c) {
-      preL[c] = L[tid + c * 256];
-      preM[c] = Mi[tid + c * 256];
+      preL[c] = __builtin_nontemporal_load(L + tid + c * 256);
+      preM[c] = __builtin_nontemporal_load(Mi + tid + c * 256);
     }
   };
 

@@ -154,9 +154,10 @@ struct ComposeBwdArgs {
   void* Ap;              // workspace [B,H,N,dk,dk] (dtype): At - I in the fragment order
   void* ApT;             // workspace [B,H,N,dk,dk] (dtype): (At - I)^T in the fragment order
   void* Bl;              // workspace [B,H,N,dk,dv] (dtype): Bc in the accumulator's lane order
-  void* Msave;           // workspace [B,H,N(N-1)/2,dk,dv] (dtype): M_{j-1} of pair (i, j)
-  void* Dsave;           // workspace [B,H,N(N-1)/2,dk,dv] (dtype): D_j of pair (i, j), lane order
-  void* Lsave;           // workspace [B,H,N(N-1)/2,dk,dv] (dtype): g lambda_j of pair (i, j)
+  // per-pair slots of the chain group's pairs ([B,H,slots,dk,dv], dtype each):
+  void* Msave;           // M_{j-1} of pair (i, j)
+  void* Dsave;           // D_j of pair (i, j), lane order
+  void* Lsave;           // g lambda_j of pair (i, j)
   float* dgp;            // workspace [B,H,N,N,dv/32]: per-wave gate-gradient parts
   float* lam_end;        // workspace [B,H,N,dk,dv]: final lambda of every chain
   int64_t B, H;
