@@ -22,6 +22,14 @@ namespace hla {
 
 constexpr int kMaxCache = 1024;  // largest n_cap a decode call accepts
 
+// A 16-byte non-temporal load.  The cached chunk maps are read once per step and the whole
+// cache is far larger than L2 and the MALL, so the stream is kept from allocating there.
+typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Per-row token vectors of the Gated DeltaNet-2 live update (LDS): ka = k o a, qa = q o a,
 // a, e = b o k; the write vector (w o v) is passed as s_v and qe = q . e.
 struct G2Rows {
@@ -272,9 +280,9 @@ __global__ __launch_bounds__(NT, WPC) void decode_kernel(DecodeArgs a) {
     const uint4* ap = reinterpret_cast<const uint4*>(Acache + (bh * ncap + j) * (int64_t)DK * DK);
     const uint4* bp = reinterpret_cast<const uint4*>(Bcache + (bh * ncap + j) * (int64_t)DK * DV);
 #pragma unroll
-    for (int p = 0; p < NPA; ++p) ra[p] = ap[p * NT + tid];
+    for (int p = 0; p < NPA; ++p) ra[p] = load_stream(ap + p * NT + tid);
 #pragma unroll
-    for (int p = 0; p < NPB; ++p) rb[p] = bp[p * NT + tid];
+    for (int p = 0; p < NPB; ++p) rb[p] = load_stream(bp + p * NT + tid);
   };
   auto next_active = [&](int j) {
     --j;
