@@ -29,6 +29,17 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// The live state and transition of every (sequence, head) are read and written once per
+// step, 1 GiB in all at the decode workload: non-temporal too.
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const nt_f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(float* p, const float4& x) {
+  const nt_f32x4 v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<nt_f32x4*>(p));
+}
 
 // Per-row token vectors of the Gated DeltaNet-2 live update (LDS): ka = k o a, qa = q o a,
 // a, e = b o k; the write vector (w o v) is passed as s_v and qe = q . e.
@@ -59,7 +70,7 @@ __device__ __forceinline__ void live_pass(float* mat, T* cache_out, bool commit,
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int r = p * RPP + r0;
-    m[p] = *reinterpret_cast<const float4*>(mat + r * W + col);
+    m[p] = load_stream(mat + r * W + col);
     const float kr = G2 ? g2.ka[r] : s_k[r], qr = G2 ? g2.qa[r] : s_q[r];
     pu.x += kr * m[p].x; pu.y += kr * m[p].y; pu.z += kr * m[p].z; pu.w += kr * m[p].w;
     pz.x += qr * m[p].x; pz.y += qr * m[p].y; pz.z += qr * m[p].z; pz.w += qr * m[p].w;
@@ -111,7 +122,7 @@ __device__ __forceinline__ void live_pass(float* mat, T* cache_out, bool commit,
       }
       nm = rs;
     }
-    *reinterpret_cast<float4*>(mat + r * W + col) = nm;
+    store_stream(mat + r * W + col, nm);
   }
   __syncthreads();
 }
