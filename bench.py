@@ -372,7 +372,7 @@ def bench_native_prefill(args, torch, hla, inputs):
 
 
 # ----------------------------------------------------------------------------- Gated DeltaNet-2
-# fp32 vector peak without packed-fp32 instructions (this build does not emit them):
+# fp32 vector peak without packed-fp32 instructions (the library is compiled without them):
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flop per FMA x 2.4 GHz
 PEAK_FP32_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 
