@@ -14,8 +14,8 @@
 //
 // One 256/512-thread workgroup per (b, h, chunk).  Products run on MFMA (bf16 inputs with
 // fp32 accumulation, or fp32 MFMA for fp32 inputs).  The inverse is blocked (16 x 16
-// diagonal blocks by substitution, then block rows) in fp32; its bf16 use is split into
-// hi + lo parts so W and U keep ~16 mantissa bits.
+// diagonal blocks by substitution, then the blocks below them by sub-diagonal) in fp32; its
+// bf16 use is split into hi + lo parts so W and U keep ~16 mantissa bits.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
@@ -225,30 +225,30 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
     for (int r = 0; r < 16; ++r) Xb[(base + r) * PX + base + cc] = x[r];
   }
   __syncthreads();
-  for (int ib = 1; ib < 4; ++ib) {
-    // Y_{ib,jb} = sum_{kb=jb}^{ib-1} L_{ib,kb} X_{kb,jb}, written into block (ib, jb) of X
-    for (int e = tid; e < ib * 256; e += NT) {
-      const int jb = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      float s = 0.f;
-      for (int kb = jb; kb < ib; ++kb)
+  // Off-diagonal blocks, from (I + L) X = I by blocks: X_ik = -X_ii sum_{m=k}^{i-1} L_im X_mk
+  // = sum_m Z_im X_mk with Z_im = -X_ii L_im.  Z of the six blocks below the diagonal comes
+  // first (all at once), into L's block (m, i) above the diagonal, which nothing reads;
+  // then X by sub-diagonal d = i - k, each from the ones before it.
 #pragma unroll
-        for (int q2 = 0; q2 < 16; ++q2) s += Lb[(ib * 16 + r) * PX + kb * 16 + q2] * Xb[(kb * 16 + q2) * PX + jb * 16 + cc];
-      Xb[(ib * 16 + r) * PX + jb * 16 + cc] = s;
-    }
-    __syncthreads();
-    // X_{ib,jb} = -X_{ib,ib} Y_{ib,jb}
-    float y[3] = {0.f, 0.f, 0.f};
-    for (int e = tid, m = 0; e < ib * 256; e += NT, ++m) {
-      const int jb = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      float s = 0.f;
+  for (int e = tid; e < 6 * 256; e += NT) {
+    const int bz = e >> 8, r = (e >> 4) & 15, cc = e & 15;
+    const int i = bz < 1 ? 1 : (bz < 3 ? 2 : 3), m = bz - i * (i - 1) / 2;  // block (i, m), m < i
+    float z = 0.f;
 #pragma unroll
-      for (int q2 = 0; q2 < 16; ++q2) s -= Xb[(ib * 16 + r) * PX + ib * 16 + q2] * Xb[(ib * 16 + q2) * PX + jb * 16 + cc];
-      y[m] = s;
-    }
-    __syncthreads();
-    for (int e = tid, m = 0; e < ib * 256; e += NT, ++m) {
-      const int jb = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      Xb[(ib * 16 + r) * PX + jb * 16 + cc] = y[m];
+    for (int q2 = 0; q2 < 16; ++q2) z -= Xb[(i * 16 + r) * PX + i * 16 + q2] * Lb[(i * 16 + q2) * PX + m * 16 + cc];
+    Lb[(m * 16 + r) * PX + i * 16 + cc] = z;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+#pragma unroll
+    for (int e = tid; e < (4 - d) * 256; e += NT) {
+      const int k = e >> 8, i = k + d, r = (e >> 4) & 15, cc = e & 15;
+      float x = 0.f;
+      for (int m = k; m < i; ++m)
+#pragma unroll
+        for (int q2 = 0; q2 < 16; ++q2) x += Lb[(m * 16 + r) * PX + i * 16 + q2] * Xb[(m * 16 + q2) * PX + k * 16 + cc];
+      Xb[(i * 16 + r) * PX + k * 16 + cc] = x;
     }
     __syncthreads();
   }
