@@ -49,7 +49,8 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) char sm1[R1];
   __shared__ __attribute__((aligned(16))) char sm2[R2];
   __shared__ __attribute__((aligned(16))) char sm3[R3];
-  // per token: beta, cumulative log decay g, gamma = exp(g), beta gamma, D = exp(g_63 - g)
+  // per token: beta, cumulative log decay g (in log2 units: pairwise decays are one exp2),
+  // gamma = exp(g), beta gamma, D = exp(g_63 - g)
   __shared__ __attribute__((aligned(16))) float s_beta[C], s_g[C], s_gam[C], s_bg[C];
   __shared__ float s_d[WANT_AB ? C : 1];  // (an output pass keeps two workgroups per CU)
 
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
       }
       const float gam = expf(x), g_end = __shfl(x, 63, 64);
       s_beta[tid] = bt;
-      s_g[tid] = x;
+      s_g[tid] = x * 1.4426950408889634f;  // log2(e)
       s_gam[tid] = gam;
       s_bg[tid] = bt * gam;
       if constexpr (WANT_AB) s_d[tid] = expf(g_end - x);
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int t = tm * 32 + acc_row(e, hh), s = tn * 32 + c32;
-      Lb[t * PX + s] = (s < t) ? s_beta[t] * expf(s_g[t] - s_g[s]) * kk[e] : 0.f;
+      Lb[t * PX + s] = (s < t) ? s_beta[t] * __builtin_amdgcn_exp2f(s_g[t] - s_g[s]) * kk[e] : 0.f;
     }
   }
   if constexpr (WANT_O) {
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int t = tm * 32 + acc_row(e, hh), s = tn * 32 + c32;
-        Pb[t * PT + s] = from_f<T>((s <= t) ? expf(s_g[t] - s_g[s]) * qk[e] : 0.f);
+        Pb[t * PT + s] = from_f<T>((s <= t) ? __builtin_amdgcn_exp2f(s_g[t] - s_g[s]) * qk[e] : 0.f);
       }
     }
   }
