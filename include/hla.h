@@ -30,8 +30,9 @@
  *     16-byte vectors (q, k, v and reps of the prefill calls, transitions, states, chunk
  *     inits, caches and the workspace) must be 16-byte aligned; per-token scalars (beta,
  *     alpha), gates, counts, element-wise outputs (o) and the decode token vectors need
- *     4-byte alignment (2 bytes for bf16 decode tokens).  The caller allocates and owns every buffer, including the workspace; the
- *     library never allocates or frees device memory and keeps no pointer after return.
+ *     4-byte alignment (2 bytes for bf16 decode tokens).  The caller allocates and owns
+ *     every buffer, including the workspace; the library never allocates or frees device
+ *     memory and keeps no pointer after return.
  *   - Calls only enqueue work on `stream`; nothing synchronises.  Calls that overlap on
  *     the same buffers race; calls on separate buffers are independent and reentrant.
  *   - Arguments are validated before anything is enqueued.  On an error the call returns a
