@@ -58,7 +58,8 @@ __device__ __forceinline__ int64_t lane_off(int ct, int rt, int lane) {
   return ((int64_t)(ct * (DK / 32) + rt) * 64 + lane) * 16;
 }
 
-// 16 values of one accumulator tile in the lane's order, in T.
+// 16 values of one accumulator tile in the lane's order, in T.  bf16 pieces go out as
+// non-temporal stores: whole 16-byte pieces of a stream far larger than the caches.
 template <class T>
 __device__ __forceinline__ void store16(T* dst, const f32x16& v, float scale) {
   if constexpr (sizeof(T) == 2) {
@@ -68,8 +69,8 @@ __device__ __forceinline__ void store16(T* dst, const f32x16& v, float scale) {
       lo[e] = (bf16)(v[e] * scale);
       hi[e] = (bf16)(v[e + 8] * scale);
     }
-    *reinterpret_cast<bf16x8*>(dst) = lo;
-    *reinterpret_cast<bf16x8*>(dst + 8) = hi;
+    __builtin_nontemporal_store(lo, reinterpret_cast<bf16x8*>(dst));
+    __builtin_nontemporal_store(hi, reinterpret_cast<bf16x8*>(dst + 8));
   } else {
 #pragma unroll
     for (int e = 0; e < 16; e += 4)
