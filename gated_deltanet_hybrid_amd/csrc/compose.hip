@@ -192,7 +192,9 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
       }
     }
   // Store a finished state slice.  The opaque lane offset keeps the compiler from holding
-  // 64 precomputed store addresses across the whole chain.
+  // 64 precomputed store addresses across the whole chain.  The stores are non-temporal:
+  // the routed states are read once, later, and the L2 is better left to the transitions
+  // that other workgroups still read.
   auto write_state = [&](int s) {
     int lofs = hh * 4 * DV + ct * 32 + c32;
     asm volatile("" : "+v"(lofs));
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) dst[(rt * 32 + (e >> 2) * 8 + (e & 3)) * DV] = M[s][rt][e];
+      for (int e = 0; e < 16; ++e) __builtin_nontemporal_store(M[s][rt][e], &dst[(rt * 32 + (e >> 2) * 8 + (e & 3)) * DV]);
   };
 #pragma unroll
   for (int s = 0; s < SPW; ++s)
