@@ -495,16 +495,17 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
         const T* arow = Qb + (tt * 32 + c32) * PK;
 #pragma unroll
         for (int ks = 0; ks < DK / MM::KS; ++ks) acc = MM::mma(MM::load_plain(arow, ks, hh), MM::load_plain(brow, ks, hh), acc);
-        // token t = 32 tt + acc_row(e): rows of o are H DV floats apart
+        // token t = 32 tt + acc_row(e): rows of o are H DV floats apart.  o is the pass's
+        // final output, written in whole 128-byte rows of 32 lanes: non-temporal stores
         const int64_t ostride = a.H * DV;
         float* ob = a.o + ((b * a.T + t0 + tt * 32 + hh * 4) * a.H + h) * DV + col0 + c32;
         if (n == C) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) ob[((e >> 2) * 8 + (e & 3)) * ostride] = acc[e];
+          for (int e = 0; e < 16; ++e) __builtin_nontemporal_store(acc[e], &ob[((e >> 2) * 8 + (e & 3)) * ostride]);
         } else {
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            if (tt * 32 + acc_row(e, hh) < n) ob[((e >> 2) * 8 + (e & 3)) * ostride] = acc[e];
+            if (tt * 32 + acc_row(e, hh) < n) __builtin_nontemporal_store(acc[e], &ob[((e >> 2) * 8 + (e & 3)) * ostride]);
         }
       }
     }
