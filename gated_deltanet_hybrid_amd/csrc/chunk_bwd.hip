@@ -272,15 +272,19 @@ __global__ __launch_bounds__(256) void chunk_bwd_finalize_kernel(ChunkBwdArgs a)
   const int64_t bh = b * a.H + h;
   const int64_t base = (bh * a.N + c) * NB_ALL;
   const int b0 = a.have_out ? 0 : NB_OUT, b1 = a.have_map ? NB_ALL : NB_OUT;
+  // every partial sum is read once, here: non-temporal loads, all of a thread's in flight
   if (e < DK) {
     float sk = 0.f;
-    for (int k = b0; k < b1; ++k) sk += a.part_k[((base + k) * C + u) * DK + e];
+#pragma unroll
+    for (int k = 0; k < NB_ALL; ++k)
+      if (k >= b0 && k < b1) sk += __builtin_nontemporal_load(a.part_k + ((base + k) * C + u) * DK + e);
     if (a.dk_router) sk += a.dk_router[bth * DK + e];
     a.dk[bth * DK + e] = sk;
     float sq = 0.f;
     if (a.have_out) {
       const int64_t qb = (bh * a.N + c) * NB_OUT;
-      for (int k = 0; k < NB_OUT; ++k) sq += a.part_q[((qb + k) * C + u) * DK + e];
+#pragma unroll
+      for (int k = 0; k < NB_OUT; ++k) sq += __builtin_nontemporal_load(a.part_q + ((qb + k) * C + u) * DK + e);
     }
     if (a.dqbar) {
       const int64_t t0 = (int64_t)c * C;
