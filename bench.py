@@ -105,6 +105,14 @@ def to_dev(storage, dtype, torch):
     return torch.from_numpy(np.ascontiguousarray(storage, dtype=np.float32)).cuda()
 
 
+def rel_err(got, ref):
+    """max|got - ref| / max|ref| (a comparison of two results, not part of the method)."""
+    import numpy as np
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    scale = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(got - ref))) / scale if scale > 0 else float(np.max(np.abs(got)))
+
+
 def timed(fn, steps, warmup, torch):
     for _ in range(warmup):
         fn()
@@ -270,7 +278,8 @@ SECONDARY = {
     "decode": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs),
     "gdn2_decode": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs, gdn2=True),
     "native_prefill": lambda args, torch, hla, inputs, x: bench_native_prefill(args, torch, hla, inputs),
-    "tail_replay": lambda args, torch, hla, inputs, x: bench_tail_replay(args, torch, hla, inputs),
+    "tail_replay": lambda args, torch, hla, inputs, x: _tail_replay_line(args, torch, hla, inputs),
+    "decode_skip": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs, skip=True),
 }
 
 # lines run only when named with --only: the backward at the full 32768 tokens needs about
@@ -283,11 +292,15 @@ ONLY_LINES = {
 
 
 # ----------------------------------------------------------------------------- decode
-def bench_decode(args, torch, hla, inputs, gdn2=False):
+def bench_decode(args, torch, hla, inputs, gdn2=False, skip=False):
     """Decode at Bs=256, H=16 with 64 cached chunks per sequence; ``gdn2`` runs the Gated
-    DeltaNet-2 live update (channel-wise gates per token) instead of Gated DeltaNet's."""
+    DeltaNet-2 live update (channel-wise gates per token) instead of Gated DeltaNet's.
+    ``skip``: skip-heavy caller gates (sigmoid(N(-4, 3)) per cached chunk) at tau = 0.1, the
+    pages' threshold, so that skipped chunks are never read ([HLA] Methodology paragraph 4:
+    thresholding cuts memory traffic)."""
     W = inputs.WORKLOADS["decode"]
-    tag = "gdn2_decode" if gdn2 else "decode"
+    tag = "gdn2_decode" if gdn2 else ("decode_skip" if skip else "decode")
+    tau = 0.1 if skip else W.tau
     Bs, H, dk, dv, n_cap = W.B, W.H, W.dk, W.dv, W.n_cache
     log(f"[decode] generating {n_cap} cached chunks per sequence for Bs={Bs} H={H}")
     hist = inputs.gen_tokens(Bs, n_cap * C, H, dk, dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["decode"],
@@ -312,16 +325,23 @@ def bench_decode(args, torch, hla, inputs, gdn2=False):
             g = inputs.gen_gdn2_decode_gates(Bs, H, dk, dv, step=s_, seed=0, stream=inputs.STREAM["decode"])
             t.update({n: to_dev(g[n], "f32", torch) for n in ("a", "b", "w")})
     it = [0]
+    g_in, n_active = None, Bs * H * n_cap
+    if skip:
+        import numpy as np
+        G = inputs.gen_gates(Bs, H, n_cap, seed=0, stream=inputs.STREAM["decode"], mode="skip_heavy")[:, :, -1, :]
+        G = np.ascontiguousarray(G)
+        n_active = int((G >= np.float32(tau)).sum())
+        g_in = torch.from_numpy(G).cuda()
 
     def step():
         t = toks[it[0] % n_tok]
         it[0] += 1
         if gdn2:
             hla.gdn2_decode(t["q"], t["k"], t["v"], t["a"], t["b"], t["w"], S, At_cur=A, At_cache=At_cache,
-                            Bc_cache=Bc_cache, reps_cache=reps, n_cache=n_cache, tau=W.tau, o=o)
+                            Bc_cache=Bc_cache, reps_cache=reps, n_cache=n_cache, tau=tau, o=o)
         else:
             hla.gdn_decode(t["q"], t["k"], t["v"], t["beta"], t["alpha"], S, At_cur=A, At_cache=At_cache,
-                           Bc_cache=Bc_cache, reps_cache=reps, n_cache=n_cache, tau=W.tau, o=o)
+                           Bc_cache=Bc_cache, reps_cache=reps, n_cache=n_cache, tau=tau, o=o, gates_in=g_in)
 
     steps = args.decode_steps
     for _ in range(8):
@@ -336,19 +356,27 @@ def bench_decode(args, torch, hla, inputs, gdn2=False):
     dec_ms, dec_n = hla.timing_read(hla.KERNEL_DECODE)
     hla.timing_enable(False)
     e = 2  # bf16 bytes
-    per_seqhead = (2 * dk * dv * 4 + 2 * dk * dk * 4 + n_cap * (dk * dk + dk * dv) * e + n_cap * C * dk * e
-                   + (2 * dk + dv) * e + ((2 * dk + dv) * 4 if gdn2 else 2 * 4) + dv * 4)
-    bytes_step = Bs * H * per_seqhead
+    # per (sequence, head): live state and live transition read and written, the token
+    # vectors and gates, the output; the representatives (computed gates) or the caller's
+    # gates; and every active cached chunk's (At_j, Bc_j), read once
+    per_seqhead = (2 * dk * dv * 4 + 2 * dk * dk * 4 + (2 * dk + dv) * e + ((2 * dk + dv) * 4 if gdn2 else 2 * 4)
+                   + dv * 4 + (n_cap * 4 if skip else n_cap * C * dk * e))
+    bytes_step = Bs * H * per_seqhead + n_active * (dk * dk + dk * dv) * e
+    bytes_dense = Bs * H * (per_seqhead + n_cap * (dk * dk + dk * dv) * e)  # the same call, every chunk kept
     kern_s = dec_ms / dec_n / 1e3
-    res = dict(workload=tag, Bs=Bs, H=H, cached_chunks=n_cap, steps=steps, ms_per_step=dt * 1e3,
+    res = dict(workload=tag, Bs=Bs, H=H, cached_chunks=n_cap, steps=steps, ms_per_step=dt * 1e3, tau=tau,
                tokens_per_s=Bs / dt, hbm_gbs=bytes_step / kern_s / 1e9,
                roofline=dict(kernel="decode_kernel", bound="hbm", achieved=round(bytes_step / kern_s / 1e9, 1),
                              peak=PEAK_HBM_GBS, unit="GB/s", frac=round(bytes_step / kern_s / 1e9 / PEAK_HBM_GBS, 4),
                              bytes_per_launch=bytes_step, avg_launch_ms=round(kern_s * 1e3, 4)),
                note="no commit while timing; live chunk extends past 64 tokens so every step does the same work")
+    if skip:
+        res.update(active_chunk_frac=n_active / (Bs * H * n_cap), bytes_per_step=bytes_step,
+                   dense_bytes_per_step=bytes_dense, bytes_frac_of_dense=bytes_step / bytes_dense,
+                   gates="caller gates sigmoid(N(-4, 3)) per cached chunk")
     log(f"[{tag}] {dt*1e3:.3f} ms/step, {Bs/dt:.0f} tok/s, kernel {kern_s*1e3:.3f} ms, "
         f"{bytes_step/kern_s/1e9:.0f} GB/s")
-    del At_cache, Bc_cache, reps, S, A, toks
+    del At_cache, Bc_cache, reps, S, A, toks, g_in
     torch.cuda.empty_cache()
     return res
 
@@ -562,6 +590,10 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, grouped_gib=Non
 
 # ----------------------------------------------------------------------------- Tail-Replay
 def bench_tail_replay(args, torch, hla, inputs):
+    """[TR]: the state of a 32768-token prefix rebuilt from its last 3277 tokens alone (a
+    suffix view of the allocation, state-only), against the full-prefix state-only prefill
+    on the GPU.  Returns the record and the two states of TAIL_PAIRS on the host, for the
+    oracle leg."""
     W = inputs.WORKLOADS["tail_replay"]
     L = W.replay
     log(f"[tail_replay] generating B={W.B} T={W.T} H={W.H} (replay {L})")
@@ -573,39 +605,67 @@ def bench_tail_replay(args, torch, hla, inputs):
     ks, vs, bs, als = k[:, -L:], v[:, -L:], beta[:, -L:], alpha[:, -L:]
     S = torch.empty((W.B, W.H, W.dk, W.dv), dtype=torch.float32, device="cuda")
     d_rep = hla.make_dims(W.B, L, W.H, W.T, W.dk, W.dv, hla.HLA_BF16)
-    ws_rep = torch.empty(hla.workspace_bytes(hla.FN_GDN_PREFILL, d_rep), dtype=torch.uint8, device="cuda")
+    ws_rep = hla._workspace(hla.workspace_bytes(hla.FN_GDN_PREFILL, d_rep), "cuda")
     dt_rep = timed(lambda: hla.gdn_prefill(None, ks, vs, bs, als, want_o=False, S_final=S, ws=ws_rep), 20, 3, torch)
     d_full = hla.make_dims(W.B, W.T, W.H, W.T, W.dk, W.dv, hla.HLA_BF16)
-    ws_full = torch.empty(hla.workspace_bytes(hla.FN_GDN_PREFILL, d_full), dtype=torch.uint8, device="cuda")
+    ws_full = hla._workspace(hla.workspace_bytes(hla.FN_GDN_PREFILL, d_full), "cuda")
     S2 = torch.empty_like(S)
     dt_full = timed(lambda: hla.gdn_prefill(None, k, v, beta, alpha, want_o=False, S_final=S2, ws=ws_full), 5, 1, torch)
+    Sh, S2h = S.cpu().numpy(), S2.cpu().numpy()
+    bytes_alg = W.B * L * W.H * (W.dk * 2 + W.dv * 2 + 2 * 4) + W.B * W.H * W.dk * W.dv * 4
     res = dict(workload="tail_replay", B=W.B, H=W.H, prefix=W.T, replay=L, ms_replay=dt_rep * 1e3,
                ms_full_prefix_state=dt_full * 1e3, speedup_vs_full=dt_full / dt_rep,
-               replay_tokens_per_s=W.B * L / dt_rep)
+               replay_tokens_per_s=W.B * L / dt_rep, algorithmic_gbs=bytes_alg / dt_rep / 1e9,
+               hbm_frac=round(bytes_alg / dt_rep / 1e9 / PEAK_HBM_GBS, 4),
+               rel_err_vs_gpu_full_prefix=rel_err(Sh, S2h),
+               note="rel_err_vs_gpu_full_prefix compares the rebuilt states of all sequences with the GPU's "
+                    "full-prefix states; the oracle leg adds both against the oracle and the P11 bound")
     log(f"[tail_replay] replay {dt_rep*1e3:.3f} ms vs full-prefix state {dt_full*1e3:.3f} ms "
-        f"({dt_full/dt_rep:.1f}x)")
+        f"({dt_full/dt_rep:.1f}x), rebuilt vs full-prefix state {res['rel_err_vs_gpu_full_prefix']:.2e}")
     del k, v, beta, alpha, ws_rep, ws_full
     torch.cuda.empty_cache()
+    states = (Sh[[b for b, _ in TAIL_PAIRS], [h for _, h in TAIL_PAIRS]],
+              S2h[[b for b, _ in TAIL_PAIRS], [h for _, h in TAIL_PAIRS]])
+    return res, states
+
+
+_TAIL_STATES = {}
+
+
+def _tail_replay_line(args, torch, hla, inputs):
+    res, _TAIL_STATES["states"] = bench_tail_replay(args, torch, hla, inputs)
     return res
 
 
 # ----------------------------------------------------------------------------- CPU oracle
-def cpu_baseline(x, n_query_chunks):
-    """The oracle (as is) on the routed prefill of the first n_query_chunks chunks of head 0,
-    each stage extrapolated to the full workload by its own work ratio."""
+TAIL_PAIRS = [(0, 0), (0, 1)]  # (b, h) of the Tail-Replay workload the oracle checks and times
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        return 1
+
+
+def oracle_samples(n_query_chunks, small=False, tail_states=None):
+    """The oracle (as it stands, never tuned) timed on a bounded sample of every workload
+    the GPU lines measure, each stage extrapolated to the full workload by its own work
+    ratio.  ``small`` shrinks the samples (the single-thread run).  ``tail_states``: the
+    GPU's rebuilt and full-prefix states of TAIL_PAIRS, compared with the oracle's."""
     import numpy as np
 
     import oracle
     from gated_deltanet_hybrid_amd import inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    out = {}
+    # routed prefill (the headline): the first n_query_chunks chunks of head 0
     W = inputs.WORKLOADS["routed_prefill"]
     Tn = n_query_chunks * C
-    q, k, v = (x.f64(n)[0, :Tn, 0] for n in ("q", "k", "v"))
-    beta, alpha = x.f64("beta")[0, :Tn, 0], x.f64("alpha")[0, :Tn, 0]
+    x = inputs.gen_tokens(1, W.T, 1, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["routed_prefill"],
+                          plant_period=W.plant_period, t_range=(0, Tn))
+    q, k, v = (x.f64(n)[0, :, 0] for n in ("q", "k", "v"))
+    beta, alpha = x.f64("beta")[0, :, 0], x.f64("alpha")[0, :, 0]
     t0 = time.perf_counter()
     A, B = oracle.chunk_transitions(k, v, beta, alpha, C)
     t1 = time.perf_counter()
@@ -620,12 +680,110 @@ def cpu_baseline(x, n_query_chunks):
     per_head = ((t1 - t0) * N / n_query_chunks + (t2 - t1) * pairs_f / pairs_s + (t3 - t2) * pairs_f / pairs_s
                 + (t4 - t3) * N / n_query_chunks)
     full = per_head * W.H * W.B
-    return dict(value=W.B * W.T / full, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"routed prefill of the first {Tn} tokens ({n_query_chunks} chunks) of head 0, "
-                       f"{t4 - t0:.1f} s; stages extrapolated to B={W.B}, H={W.H}, T={W.T} by chunk count "
-                       f"(transitions, outputs) or chunk-pair count (gates, composition)",
-                sample_seconds=round(t4 - t0, 2), extrapolated_seconds=round(full, 1),
-                host_cpus=os.cpu_count())
+    out["routed_prefill"] = dict(
+        value=W.B * W.T / full, unit="tokens/s",
+        sample=f"routed prefill of the first {Tn} tokens ({n_query_chunks} chunks) of head 0, {t4 - t0:.1f} s; "
+               f"stages extrapolated to B={W.B}, H={W.H}, T={W.T} by chunk count (transitions, outputs) or "
+               f"chunk-pair count (gates, composition)",
+        sample_seconds=round(t4 - t0, 2), extrapolated_seconds=round(full, 1))
+    # native prefill: a few heads of batch row 0, whole sequence, outputs and final state
+    W = inputs.WORKLOADS["native_prefill"]
+    nh = 2 if small else 4
+    x = inputs.gen_tokens(1, W.T, nh, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["native_prefill"])
+    t0 = time.perf_counter()
+    oracle.gdn_recurrent(*(x.f64(n)[0].swapaxes(0, 1) for n in ("q", "k", "v", "beta", "alpha")))
+    dt = time.perf_counter() - t0
+    full = dt * W.B * W.H / nh
+    out["native_prefill"] = dict(value=W.B * W.T / full, unit="tokens/s",
+                                 sample=f"{nh} of {W.B * W.H} (batch row, head) sequences of {W.T} tokens, "
+                                        f"{dt:.1f} s, extrapolated by sequence count",
+                                 sample_seconds=round(dt, 2), extrapolated_seconds=round(full, 1))
+    # decode: one step of a few (sequence, head) pairs, each composing its 64 cached chunks
+    W = inputs.WORKLOADS["decode"]
+    ns = 4 if small else 8
+    At_s, Bc_s = inputs.gen_transitions(1, ns, W.n_cache, W.dk, W.dv, dtype=W.dtype, seed=31)
+    reps = inputs.gen_tokens(1, W.n_cache * C, ns, W.dk, W.dk, dtype=W.dtype, seed=32, with_q=False)
+    R = reps.f64("k")[0].reshape(W.n_cache, C, ns, W.dk).transpose(2, 0, 1, 3)
+    Am = inputs.to_f64(At_s, W.dtype)[0].transpose(0, 1, 3, 2)
+    Bm = inputs.to_f64(Bc_s, W.dtype)[0].transpose(0, 1, 3, 2)
+    tok = inputs.gen_decode_tokens(1, ns, W.dk, W.dv, step=0, dtype=W.dtype, seed=0, stream=inputs.STREAM["decode"])
+    tq, tk, tv = (inputs.to_f64(tok[n], W.dtype)[0] for n in ("q", "k", "v"))
+    t0 = time.perf_counter()
+    for i in range(ns):
+        oracle.decode_step(tq[i], tk[i], tv[i], float(tok["beta"][0, i]), float(tok["alpha"][0, i]),
+                           np.zeros((W.dv, W.dk)), np.eye(W.dk), Am[i], Bm[i], R[i], W.tau)
+    dt = time.perf_counter() - t0
+    step_s = dt * W.B * W.H / ns
+    out["decode"] = dict(value=W.B / step_s, unit="tokens/s",
+                         sample=f"one step of {ns} (sequence, head) pairs with {W.n_cache} cached chunks each, "
+                                f"{dt:.2f} s, extrapolated to Bs={W.B} x H={W.H} by pair count",
+                         sample_seconds=round(dt, 3), extrapolated_seconds=round(step_s, 2))
+    # Tail-Replay: the replay of the last L tokens and the full-prefix recurrence
+    W = inputs.WORKLOADS["tail_replay"]
+    L = W.replay
+    pairs = TAIL_PAIRS[:1] if small else TAIL_PAIRS
+    nh = max(h for _, h in pairs) + 1
+    x = inputs.gen_tokens(1, W.T, nh, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["tail_replay"],
+                          with_q=False)
+    kk, vv, bb, aa = (np.stack([x.f64(n)[b, :, h] for b, h in pairs]) for n in ("k", "v", "beta", "alpha"))
+    t0 = time.perf_counter()
+    _, S_rep = oracle.gdn_recurrent(None, kk[:, -L:], vv[:, -L:], bb[:, -L:], aa[:, -L:])
+    t1 = time.perf_counter()
+    _, S_pre = oracle.gdn_recurrent(None, kk[:, :-L], vv[:, :-L], bb[:, :-L], aa[:, :-L])
+    _, S_full = oracle.gdn_recurrent(None, kk[:, -L:], vv[:, -L:], bb[:, -L:], aa[:, -L:], S0=S_pre)
+    t2 = time.perf_counter()
+    rep_full = (t1 - t0) * W.B * W.H / len(pairs)
+    rec = dict(value=W.B * L / rep_full, unit="tokens/s (replayed)",
+               sample=f"{len(pairs)} of {W.B * W.H} sequences: replay of the last {L} tokens {t1 - t0:.1f} s, "
+                      f"full {W.T}-token prefix {t2 - t1:.1f} s; replay extrapolated by sequence count",
+               sample_seconds=round(t2 - t0, 2), extrapolated_seconds=round(rep_full, 1),
+               full_prefix_seconds_per_sequence=round((t2 - t1) / len(pairs), 2))
+    if tail_states is not None:
+        # parity of the GPU's rebuilt state against the same-suffix replay, and its distance
+        # from the full-prefix state next to the [TR] bound of the replay (P11): the two
+        # differ by at most (prod of the suffix alphas) ||S_{T-L}||_2
+        S_gpu, S_gpu_full = tail_states
+        cmp = []
+        for i, (b, h) in enumerate(pairs):
+            lb = oracle.tail_replay_bound_log10(aa[i, -L:], S_pre[i])
+            cmp.append(dict(b=b, h=h, rel_err_vs_oracle_replay=rel_err(S_gpu[i], S_rep[i].T),
+                            rel_err_vs_oracle_full_prefix=rel_err(S_gpu[i], S_full[i].T),
+                            gpu_full_prefix_rel_err_vs_oracle=rel_err(S_gpu_full[i], S_full[i].T),
+                            oracle_replay_vs_full_rel=rel_err(S_rep[i], S_full[i]),
+                            p11_bound_log10=round(lb, 1)))
+        rec["parity"] = cmp
+    out["tail_replay"] = rec
+    return out
+
+
+def cpu_baseline(n_query_chunks, tail_states=None):
+    """The oracle on every workload's sample: on all of the host's BLAS threads in this
+    process, then single-threaded in a child process whose thread counts are set before
+    numpy loads.  The headline value is the routed prefill on all threads."""
+    import subprocess
+    multi = oracle_samples(n_query_chunks, tail_states=tail_states)
+    threads = _blas_threads()
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    single = None
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-samples", str(max(64, n_query_chunks // 4))],
+                           env=env, capture_output=True, text=True, timeout=900)
+        if r.returncode == 0:
+            single = json.loads(r.stdout.strip().splitlines()[-1])
+        else:
+            log(f"[cpu_baseline] single-thread run failed: {r.stderr[-500:]}")
+    except Exception as e:  # the baseline is a report; a failed child does not end the bench
+        log(f"[cpu_baseline] single-thread run failed: {e}")
+    head = multi["routed_prefill"]
+    try:
+        cpu_model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except Exception:
+        cpu_model = None
+    return dict(value=head["value"], unit="tokens/s", cores=threads, kind="oracle", sample=head["sample"],
+                sample_seconds=head["sample_seconds"], extrapolated_seconds=head["extrapolated_seconds"],
+                host_cpus=os.cpu_count(), affinity_cpus=len(os.sched_getaffinity(0)), cpu_model=cpu_model,
+                per_workload={"threads": threads, **multi},
+                single_thread=None if single is None else {"threads": single.pop("threads"), **single})
 
 
 # ----------------------------------------------------------------------------- HBM traffic
@@ -716,7 +874,14 @@ def main():
     ap.add_argument("--only", metavar="LINES",
                     help="profiling aid: run only these comma-separated lines (routed_prefill or a secondary "
                          "name) and print their results as one JSON object instead of the bench line")
+    ap.add_argument("--oracle-samples", type=int, metavar="CHUNKS",
+                    help="the oracle leg alone on the CPU (used for the single-thread run): time every "
+                         "workload's oracle sample and print one JSON object")
     args = ap.parse_args()
+    if args.oracle_samples:
+        rec = oracle_samples(args.oracle_samples, small=True)
+        print(json.dumps({"threads": _blas_threads(), **rec}), flush=True)
+        return
     if args.traffic_write:
         traffic_write(*args.traffic_write)
         return
@@ -759,8 +924,19 @@ def main():
             secondary[name] = fn(args, torch, hla, inputs, x)
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"[cpu_baseline] oracle on {args.oracle_chunks} chunks of one head")
-        cpu = cpu_baseline(x, args.oracle_chunks)
+        log(f"[cpu_baseline] oracle samples of every workload ({args.oracle_chunks} chunks of the headline)")
+        cpu = cpu_baseline(args.oracle_chunks, tail_states=_TAIL_STATES.get("states"))
+        # GPU / oracle throughput per workload (all-thread oracle)
+        gpu_rates = {"routed_prefill": head["value"],
+                     "native_prefill": secondary.get("native_prefill", {}).get("tokens_per_s"),
+                     "decode": secondary.get("decode", {}).get("tokens_per_s"),
+                     "tail_replay": secondary.get("tail_replay", {}).get("replay_tokens_per_s")}
+        for name, rate in gpu_rates.items():
+            if rate and name in cpu["per_workload"]:
+                cpu["per_workload"][name]["gpu_speedup"] = round(rate / cpu["per_workload"][name]["value"], 1)
+        parity = cpu["per_workload"]["tail_replay"].pop("parity", None)
+        if parity is not None and "tail_replay" in secondary:
+            secondary["tail_replay"]["vs_oracle"] = parity
         log(f"[cpu_baseline] {cpu['value']:.1f} tokens/s (sample {cpu['sample_seconds']} s)")
 
     W = inputs.WORKLOADS["routed_prefill"]

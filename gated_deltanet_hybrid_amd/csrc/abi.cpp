@@ -54,12 +54,6 @@ bool all_aligned4(P... p) {
   return (aligned4(p) && ...);
 }
 
-// The transitions pass of a prefill hands W | U of every piece to its output pass through
-// the workspace (bf16 only) instead of the output pass inverting the chunk matrix again.
-#ifndef HLA_WU_HANDOFF
-#define HLA_WU_HANDOFF 1
-#endif
-
 // Bytes of the W | U image of every 64-token piece (bf16; float32 takes no hand-off).
 int64_t wu_bytes(const hla_dims_t* d) {
   return d->dtype == HLA_BF16 ? d->B * d->H * n_pieces(d) * hla::aux_chunk_bytes(d->dk, d->dv) : 0;
@@ -79,7 +73,7 @@ PrefillWs prefill_ws(const hla_dims_t* d) {
   w.bc_off = round_up(BHN * d->dk * d->dk * e, 256);
   w.total_ab = w.bc_off + round_up(BHN * d->dk * d->dv * e, 256);
   w.wu_off = w.total_ab;
-  w.st_off = w.wu_off + (HLA_WU_HANDOFF ? round_up(wu_bytes(d), 256) : 0);
+  w.st_off = w.wu_off + round_up(wu_bytes(d), 256);
   w.total = w.st_off + round_up(BHN * d->dk * d->dv * 4, 256);
   return w;
 }
@@ -232,7 +226,7 @@ hipError_t chunk_pass(const hla::ChunkArgs& a, const hla_dims_t* d, bool want_ab
 // them, for float32 or for the Gated DeltaNet-2 pass (which has no UT form), else the
 // workspace region.
 void* wu_internal(const hla_dims_t* d, const hla::ChunkArgs& a, const void* wu, void* region) {
-  return (wu || !HLA_WU_HANDOFF || d->dtype != HLA_BF16 || a.variant != 0) ? nullptr : region;
+  return (wu || d->dtype != HLA_BF16 || a.variant != 0) ? nullptr : region;
 }
 
 // Maps that the library writes for its own scans (never a caller's buffer) carry Bc in the

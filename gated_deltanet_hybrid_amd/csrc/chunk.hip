@@ -144,7 +144,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkArgs a) {
       if (tid < n) {
         const int64_t idx = row0 + (int64_t)tid * a.H;
         bt = a.beta[idx];
-        la = logf(a.alpha[idx]);
+        la = logf(fmaxf(a.alpha[idx], 1.17549435e-38f));  // alpha = 0 (a reset) stays finite
       }
       float x = la;  // inclusive prefix sum over the 64 lanes of wave 0
 #pragma unroll

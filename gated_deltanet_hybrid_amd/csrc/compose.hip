@@ -272,13 +272,7 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
 #pragma unroll
         for (int d = 0; d < NDW; ++d)
           if (f == d * NFA / NDW) {
-#ifdef HLA_SPREAD_MASK
-            __builtin_amdgcn_sched_barrier(HLA_SPREAD_MASK);
-#endif
             issue_one(j + 1, d, nA, nB);
-#ifdef HLA_SPREAD_MASK
-            __builtin_amdgcn_sched_barrier(HLA_SPREAD_MASK);
-#endif
           }
         const bf16x8 af = ring[f % PF];
         if (f + PF < NF) ring[f % PF] = frag(cA, cB, f + PF);
@@ -299,20 +293,6 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
         for (int s = 0; s < SPW; ++s)
           M[s][rt] = Mma<bf16>::mma(af, f < NFA ? bfr[s][f / NRT] : dg[s], M[s][rt]);
       }
-#ifdef HLA_SGB
-      // instruction order of the block: the ring prologue, then per fragment its SPW
-      // products followed by the refill of its ring slot, with the copy instructions
-      // spread evenly in front of the fragments they were placed at
-      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-#pragma unroll
-        for (int d = 0; d < NDW; ++d)
-          if (f == d * NFA / NDW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, SPW, 0);
-        if (f + PF < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-#endif
     } else if (more) {
       issue(j + 1, nA, nB);
     }
@@ -360,13 +340,11 @@ hipError_t launch_compose_bf16(const RouteArgs& a, int dk, int dv, hipStream_t s
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-#ifndef HLA_COMPOSE_SHAPE
-#define HLA_COMPOSE_SHAPE 8, 2, 4
-#endif
-  if (dk == 64 && dv == 64) return launch_compose_bf16_t<64, 64, HLA_COMPOSE_SHAPE>(a, s);
-  if (dk == 64 && dv == 128) return launch_compose_bf16_t<64, 128, HLA_COMPOSE_SHAPE>(a, s);
-  if (dk == 128 && dv == 64) return launch_compose_bf16_t<128, 64, HLA_COMPOSE_SHAPE>(a, s);
-  return launch_compose_bf16_t<128, 128, HLA_COMPOSE_SHAPE>(a, s);
+  // 8 waves of 2 state slices each, a 4-deep ring of fragment reads
+  if (dk == 64 && dv == 64) return launch_compose_bf16_t<64, 64, 8, 2, 4>(a, s);
+  if (dk == 64 && dv == 128) return launch_compose_bf16_t<64, 128, 8, 2, 4>(a, s);
+  if (dk == 128 && dv == 64) return launch_compose_bf16_t<128, 64, 8, 2, 4>(a, s);
+  return launch_compose_bf16_t<128, 128, 8, 2, 4>(a, s);
 }
 
 }  // namespace hla

@@ -130,12 +130,6 @@ __device__ __forceinline__ void live_pass(float* mat, T* cache_out, bool commit,
 // 512 threads per (sequence, head) and a two-deep register prefetch of the cached chunks
 // fit in ~121 VGPRs, so two workgroups share a CU; every phase is a short dependent chain
 // of loads and reductions, and the second workgroup keeps HBM busy meanwhile.
-#ifndef HLA_DECODE_WGS_PER_CU
-#define HLA_DECODE_WGS_PER_CU 1
-#endif
-#ifndef HLA_DECODE_NT
-#define HLA_DECODE_NT 512
-#endif
 template <class T, int DK, int DV, int NT, int WPC, bool G2>
 __global__ __launch_bounds__(NT, WPC) void decode_kernel(DecodeArgs a) {
   constexpr int E = sizeof(T), PAD = 16 / E;
@@ -342,13 +336,6 @@ __global__ __launch_bounds__(NT, WPC) void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
   };
-#if HLA_DECODE_WGS_PER_CU >= 2
-  // with a tighter register bound: one chunk in flight per workgroup
-  for (int j = next_active(nc); j >= 0; j = next_active(j)) {
-    load_chunk(j, ra0, rb0);
-    process(j, ra0, rb0);
-  }
-#else
   int j = next_active(nc);
   if (j >= 0) load_chunk(j, ra0, rb0);
   while (j >= 0) {
@@ -362,7 +349,6 @@ __global__ __launch_bounds__(NT, WPC) void decode_kernel(DecodeArgs a) {
     process(j, ra1, rb1);
     j = jn;
   }
-#endif
   if (tid < DV) a.o[bh * DV + tid] = s_o[tid];
 }
 
@@ -381,11 +367,11 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   {
     TimedLaunch tl(HLA_KERNEL_DECODE, s);
     if (a.variant == 2)
-      hipLaunchKernelGGL((decode_kernel<T, DK, DV, HLA_DECODE_NT, HLA_DECODE_WGS_PER_CU, true>), dim3((unsigned)nb),
-                         dim3(HLA_DECODE_NT), 0, s, a);
+      hipLaunchKernelGGL((decode_kernel<T, DK, DV, 512, 1, true>), dim3((unsigned)nb),
+                         dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((decode_kernel<T, DK, DV, HLA_DECODE_NT, HLA_DECODE_WGS_PER_CU, false>), dim3((unsigned)nb),
-                         dim3(HLA_DECODE_NT), 0, s, a);
+      hipLaunchKernelGGL((decode_kernel<T, DK, DV, 512, 1, false>), dim3((unsigned)nb),
+                         dim3(512), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(a.commit && a.At_cur)) return e;

@@ -26,15 +26,12 @@
 
 namespace hla {
 
-#ifndef HLA_GDN2_SHAPE
-#define HLA_GDN2_SHAPE 2, 4, 8  // columns per thread, row groups, tokens per staged block
-#endif
 namespace {
 template <int CPT_, int RQ_, int TB_>
 struct G2Shape {
   static constexpr int CPT = CPT_, RQ = RQ_, TB = TB_;
 };
-using G2 = G2Shape<HLA_GDN2_SHAPE>;
+using G2 = G2Shape<2, 4, 8>;  // columns per thread, row groups, tokens per staged block
 constexpr int kTB = G2::TB;
 }
 

@@ -170,6 +170,18 @@ def wu_buffer(k, v, beta, alpha, C=CHUNK):
     return torch.empty(n, dtype=torch.uint8, device=k.device) if n else None
 
 
+def _check_wu(wu, d):
+    """The W | U hand-off buffer has no size argument in the C ABI: it must hold
+    hla_workspace_bytes(HLA_FN_WU_HANDOFF) bytes on the inputs' device."""
+    if wu is None:
+        return
+    need = workspace_bytes(FN_WU_HANDOFF, d)
+    if need == 0:
+        raise ValueError("the W | U hand-off takes bfloat16 inputs only")
+    if wu.dtype != torch.uint8 or not wu.is_cuda or not wu.is_contiguous() or wu.numel() < need:
+        raise ValueError(f"wu must be a contiguous CUDA uint8 tensor of at least {need} bytes (see wu_buffer)")
+
+
 def chunk_transitions(k, v, beta, alpha, At=None, Bc=None, C=CHUNK, ws=None, wu=None):
     """Exact affine map (At, Bc) of every C-token chunk: M_end = At M_start + Bc.
     wu (from wu_buffer) also receives every piece's W | U for a later gdn_prefill."""
@@ -179,6 +191,7 @@ def chunk_transitions(k, v, beta, alpha, At=None, Bc=None, C=CHUNK, ws=None, wu=
     Bc = torch.empty((d.B, d.H, N, d.dk, d.dv), dtype=k.dtype, device=k.device) if Bc is None else Bc
     _need(At, (d.B, d.H, N, d.dk, d.dk), k.dtype, "At")
     _need(Bc, (d.B, d.H, N, d.dk, d.dv), k.dtype, "Bc")
+    _check_wu(wu, d)
     if ws is None:
         ws = _workspace(workspace_bytes(FN_CHUNK_TRANSITIONS, d), k.device)
     _check(library().hla_chunk_transitions(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(At),
@@ -209,6 +222,7 @@ def gdn_prefill(q, k, v, beta, alpha, S0=None, chunk_init=None, want_o=True, wan
     _need(S0, (d.B, d.H, d.dk, d.dv), torch.float32, "S0")
     _need(chunk_init, (d.B, d.H, N, d.dk, d.dv), torch.float32, "chunk_init")
     _need(S_final, (d.B, d.H, d.dk, d.dv), torch.float32, "S_final")
+    _check_wu(wu, d)
     if ws is None and (chunk_init is None or C != CHUNK):
         ws = _workspace(workspace_bytes(FN_GDN_PREFILL, d), dev)
     _check(library().hla_gdn_prefill(ctypes.byref(d), _ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(beta),

@@ -17,7 +17,8 @@
  *     stored in the state orientation as the pair (At, Bc) with
  *         M_end = At @ M_start + Bc,   At = A_c^T [dk, dk],   Bc = B_c^T [dk, dv].
  *   - Per-token inputs: q, k [B, ld_T, H, dk]; v [B, ld_T, H, dv]; beta, alpha
- *     [B, ld_T, H] float32.  Only tokens [0, T) of each batch row are read, so a suffix
+ *     [B, ld_T, H] float32, with beta in [0, 1] and alpha in [0, 1] (alpha = 0 clears the
+ *     state: the chunk kernels take log alpha clamped at float32's smallest normal).  Only tokens [0, T) of each batch row are read, so a suffix
  *     view (Tail-Replay) passes base pointers offset to the suffix start and ld_T = the
  *     allocated row length.
  *   - Chunk c covers tokens [c C, min((c + 1) C, T)); N = ceil(T / C); the last chunk may
@@ -101,12 +102,14 @@ typedef enum {
  * diag(beta)(K K^T o decay) is inverted per chunk instead of running the token loop.
  *   k, v, beta, alpha : inputs as in the header notes (q is not needed).
  *   At [B, H, N, dk, dk], Bc [B, H, N, dk, dv] (out, dtype): M_end = At M_start + Bc.
- *   wu     (out, optional, bf16 only): hla_workspace_bytes(HLA_FN_WU_HANDOFF) bytes, or
- *           NULL.  Receives, for every 64-token piece, the UT-transformed keys and values
- *           W = X diag(beta gamma) K and U = X diag(beta) V (X the inverted strictly lower
- *           part plus identity) in the library's own fragment order, so that
- *           hla_gdn_prefill on the same inputs can take them instead of recomputing the
- *           inverse.  The layout is private to this library version.  A non-NULL wu
+ *   wu     (out, optional, bf16 only): a buffer of at least
+ *           hla_workspace_bytes(HLA_FN_WU_HANDOFF) bytes (B H ceil(T / 64) 64 (dk + dv)
+ *           bf16 values; the call has no size argument for it, so a smaller buffer is
+ *           written past its end), or NULL.  Receives, for every 64-token piece, the
+ *           UT-transformed keys and values W = X diag(beta gamma) K and U = X diag(beta) V
+ *           (X the inverted strictly lower part plus identity) in the library's own
+ *           fragment order, so that hla_gdn_prefill on the same inputs can take them
+ *           instead of recomputing the inverse.  The layout is private to this library version.  A non-NULL wu
  *           with float32 inputs is HLA_ERR_UNSUPPORTED.
  *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_CHUNK_TRANSITIONS)
  *           bytes (zero for C = 64; for C > 64 it holds the maps of the 64-token pieces,
@@ -133,8 +136,9 @@ hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const voi
  *   q, k, v, beta, alpha : per-token inputs.
  *   S0         [B, H, dk, dv] float32 or NULL.
  *   chunk_init [B, H, N, dk, dv] float32 or NULL.
- *   wu         (optional, bf16 only): a buffer that hla_chunk_transitions filled from the
- *           same k, v, beta, alpha and dims, or NULL.  Given, the output pass reads W and U
+ *   wu         (optional, bf16 only): a buffer of hla_workspace_bytes(HLA_FN_WU_HANDOFF)
+ *           bytes that hla_chunk_transitions filled from the same k, v, beta, alpha and
+ *           dims, or NULL.  Given, the output pass reads W and U
  *           from it instead of recomputing them; results are identical.
  *   o          [B, T, H, dv] float32 (out) or NULL.
  *   S_final    [B, H, dk, dv] float32 (out) or NULL.  At least one of o, S_final.
@@ -420,8 +424,11 @@ typedef enum {
  * earlier records and starts bracketing every launch of the kernels above with two HIP
  * events recorded on that launch's own stream; hla_timing_enable(0) stops and clears.
  * hla_timing_read() waits for the recorded events of one kernel kind and returns the
- * summed elapsed milliseconds and the number of launches (host pointers).  Timing is
- * process-global: enable it only while one thread issues work.
+ * summed elapsed milliseconds and the number of launches (host pointers).  These two
+ * calls are the one exception to the no-global-state convention above: the switch and the
+ * event records are process-global (host memory and HIP events, never device buffers), so
+ * enable timing only while one thread issues work.  With timing off no entry point reads
+ * or writes that state.
  */
 hla_status_t hla_timing_enable(int32_t on);
 hla_status_t hla_timing_read(int32_t which, double* total_ms, int64_t* launches);

@@ -43,6 +43,7 @@ from .gdn import (  # noqa: F401
     hla_prefill,
     decode_step,
     tail_replay,
+    tail_replay_bound_log10,
     n_eff,
     PARITY_UNPINNED,
 )

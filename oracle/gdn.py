@@ -153,8 +153,12 @@ def router_gates(q, reps, n_rep, C, tau, gates_in=None, Wr=None):
       * l_ij = log-mean-exp over chunk j's representatives r of (qbar_i . r) / sqrt(dk);
       * g_ij = sigmoid(l_ij) for j < i, independent (no normalisation over j);
       * the current chunk has weight 1, future chunks are masked (weight 0);
-      * a history gate below tau is set to zero without renormalisation.  The skip is
-        decided in float32 (the kernel's precision): keep iff float32(g) >= float32(tau).
+      * a history gate below tau is set to zero without renormalisation.  The pages fix
+        no precision for this test; tau crosses the C boundary as a float32 and the gates
+        it is compared with are float32 outputs, so the comparison is taken in float32:
+        keep iff float32(g) >= float32(tau).  A gate within float32 rounding of tau may go
+        either way, which is why exact mask parity is checked on caller gates that both
+        sides read as the same float32 numbers.
     ``gates_in`` [N, N] replaces the computed history gates (entries j < i).
     Returns dict(gates [N,N], mask [N,N] bool (history only), ghat [N,N], active (list of
     ascending index arrays), count [N], n_eff [N]).
@@ -299,3 +303,19 @@ def tail_replay(k, v, beta, alpha, L):
                              beta[..., T - L:], alpha[..., T - L:])
     _, S_full = gdn_recurrent(None, k, v, beta, alpha)
     return S_rep, S_full
+
+
+def tail_replay_bound_log10(alpha_suffix, S_prefix):
+    """log10 of the error bound of a replay from zero ([TR] state rebuild).
+
+    Every token's linear part alpha_t (I - beta_t k_t k_t^T) has 2-norm alpha_t when
+    beta_t is in [0, 1] and k_t has unit length, and the replay differs from the full
+    recurrence only by the state it starts from (zero instead of S_{T-L}).  So
+    ||S_full - S_replay||_2 <= (prod of alpha over the suffix) ||S_{T-L}||_2.  Taken in
+    log10, because the product underflows float64 for long suffixes.
+    alpha_suffix [L]; S_prefix [dv, dk], the state in front of the suffix.
+    """
+    nrm = np.linalg.norm(np.asarray(S_prefix, np.float64), 2)
+    if nrm == 0.0:
+        return -math.inf
+    return float(np.sum(np.log10(np.asarray(alpha_suffix, np.float64))) + math.log10(nrm))

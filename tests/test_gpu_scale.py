@@ -22,9 +22,9 @@ pytestmark = pytest.mark.gpu
 C = 64
 
 
-def assert_close(got, ref, dtype, what):
+def assert_close(got, ref, dtype, what, tol=None):
     """The parity bar, with the measured error printed (run with -s to see it)."""
-    e = _assert_close(got, ref, dtype, what)
+    e = _assert_close(got, ref, dtype, what, tol=tol)
     note(f"    {what}: max|diff|/max|ref| = {e:.2e}")
     return e
 
@@ -110,41 +110,106 @@ def test_route_mix_many_chunks_caller_gates(case):
 
 
 # ----------------------------------------------------------------------------- full sizes
-def test_routed_prefill_full_size_sampled():
-    """B=1, H=16, T=32768, d=128, 512 chunks, bf16, tau=1e-3, planted x8 signal: the three
-    calls the benchmark times, then query chunks {1, 300, 511} of heads {0, 15} against
-    the oracle (transitions token by token, the gate rows, the composition of row i, and
-    the outputs of chunk i from its routed state)."""
-    W = inputs.WORKLOADS["routed_prefill"]
-    note("routed prefill full size")
-    x = inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["routed_prefill"],
-                          plant_period=W.plant_period)
+def _check_router_all_rows(r, b, hh, ref, tau, N):
+    """Every row of one head's router outputs against the oracle: history gates (atol
+    2e-5), the diagonal 1 and the upper triangle 0, the mask (bit-exact away from tau),
+    active lists and counts (bit-exact, from the GPU's own mask) and n_eff."""
+    g = host(r["gates"][b, hh])
+    m = host(r["mask"][b, hh]).astype(bool)
+    idx = host(r["active_idx"][b, hh]).astype(np.int64)
+    cnt = host(r["active_cnt"][b, hh]).astype(np.int64)
+    low = np.tril(np.ones((N, N), bool), -1)
+    np.testing.assert_allclose(g[low], ref["gates"][low], atol=2e-5, rtol=0)
+    assert np.all(np.diag(g) == 1.0) and np.all(g[np.triu(np.ones((N, N), bool), 1)] == 0.0)
+    near = low & (np.abs(ref["gates"] - tau) <= 1e-6)
+    assert np.array_equal(m[low & ~near], ref["mask"][low & ~near])
+    assert not m[~low].any()
+    np.testing.assert_array_equal(cnt, m.sum(axis=1))
+    for i in range(N):
+        act = np.nonzero(m[i])[0]
+        np.testing.assert_array_equal(idx[i, :len(act)], act)
+        assert np.all(idx[i, len(act):] == -1)
+    np.testing.assert_allclose(host(r["n_eff"][b, hh]), ref["n_eff"], rtol=1e-4, atol=1e-5)
+    return int(near.sum())
+
+
+def _router_refs(x, pairs, tau):
+    """The oracle's full gate matrices of several (b, h) sequences, in threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(p):
+        b, hh = p
+        return oracle.router_gates(x.f64("q")[b, :, hh], x.f64("k")[b, :, hh], C, C, tau)
+    with ThreadPoolExecutor(8) as ex:
+        return dict(zip(pairs, ex.map(one, pairs)))
+
+
+def _routed_rows(x, r, o, b, hh, rows, ref, dtype):
+    """Routed states and outputs of query chunks ``rows`` of (b, hh) against the oracle:
+    transitions token by token, the composition of each row alone, the chunk's outputs
+    from its routed state."""
+    qh, kh, vh, bh, ah = seq(x, b, hh)
+    A, Bm = oracle.chunk_transitions(kh, vh, bh, ah, C)
+    T = qh.shape[0]
+    for i in rows:
+        note(f"  head {hh} query chunk {i}")
+        only_i = np.zeros_like(ref["mask"])
+        only_i[i] = ref["mask"][i]
+        S_i = oracle.routed_states(A[:i + 1], Bm[:i + 1], ref["ghat"][:i + 1, :i + 1], only_i[:i + 1, :i + 1])[i]
+        assert_close(host(r["S_routed"][b, hh, i]), S_i.T, dtype, f"S_routed h{hh} i{i}")
+        s, e = i * C, min((i + 1) * C, T)
+        o_i, _ = oracle.gdn_recurrent(qh[s:e], kh[s:e], vh[s:e], bh[s:e], ah[s:e], S0=S_i)
+        assert_close(host(o[b, s:e, hh]), o_i, dtype, f"o h{hh} chunk {i}")
+
+
+def _routed_calls(x, W, N):
     q, k, v, beta, alpha = token_tensors(x)
     h = hla()
-    N = W.N
     At = torch.empty((W.B, W.H, N, W.dk, W.dk), dtype=k.dtype, device="cuda")
     Bc = torch.empty((W.B, W.H, N, W.dk, W.dv), dtype=k.dtype, device="cuda")
     h.chunk_transitions(k, v, beta, alpha, At=At, Bc=Bc)
     r = h.route_mix(q, k, At, Bc, n_rep=C, tau=W.tau)
     o, _ = h.gdn_prefill(q, k, v, beta, alpha, chunk_init=r["S_routed"], want_state=False)
     torch.cuda.synchronize()
-    rows = [1, 300, N - 1]
+    return r, o
+
+
+def test_routed_prefill_full_size_sampled():
+    """B=1, H=16, T=32768, d=128, 512 chunks, bf16, tau=1e-3, planted x8 signal: the three
+    calls the benchmark times.  Every head's 512 x 512 gates, mask, active lists, counts
+    and n_eff against the oracle's; the routed states and outputs of query chunks
+    {1, 300, 511} of heads {0, 15}."""
+    W = inputs.WORKLOADS["routed_prefill"]
+    note("routed prefill full size")
+    x = inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["routed_prefill"],
+                          plant_period=W.plant_period)
+    N = W.N
+    r, o = _routed_calls(x, W, N)
+    refs = _router_refs(x, [(0, hh) for hh in range(W.H)], W.tau)
+    for hh in range(W.H):
+        note(f"  router rows, head {hh}")
+        assert refs[(0, hh)]["mask"][np.tril_indices(N, -1)].all()  # dense at these distributions
+        assert _check_router_all_rows(r, 0, hh, refs[(0, hh)], W.tau, N) == 0
     for hh in (0, W.H - 1):
-        qh, kh, vh, bh, ah = seq(x, 0, hh)
-        A, Bm = oracle.chunk_transitions(kh, vh, bh, ah, C)
-        ref = oracle.router_gates(qh, kh, C, C, W.tau)
-        assert ref["mask"][np.tril_indices(N, -1)].all()  # dense at these distributions
-        for i in rows:
-            note(f"  head {hh} query chunk {i}")
-            check_row(i, host(r["gates"][0, hh, i]), host(r["mask"][0, hh, i]),
-                      host(r["active_idx"][0, hh, i]).astype(int), int(r["active_cnt"][0, hh, i].item()), ref, W.tau)
-            only_i = np.zeros_like(ref["mask"])
-            only_i[i] = ref["mask"][i]
-            S_i = oracle.routed_states(A[:i + 1], Bm[:i + 1], ref["ghat"][:i + 1, :i + 1], only_i[:i + 1, :i + 1])[i]
-            assert_close(host(r["S_routed"][0, hh, i]), S_i.T, W.dtype, f"S_routed h{hh} i{i}")
-            s, e = i * C, min((i + 1) * C, W.T)
-            o_i, _ = oracle.gdn_recurrent(qh[s:e], kh[s:e], vh[s:e], bh[s:e], ah[s:e], S0=S_i)
-            assert_close(host(o[0, s:e, hh]), o_i, W.dtype, f"o h{hh} chunk {i}")
+        _routed_rows(x, r, o, 0, hh, [1, 300, N - 1], refs[(0, hh)], W.dtype)
+
+
+def test_routed_prefill_full_length_slow_decay():
+    """B=1, H=8, T=32768 (512 chunks), bf16, slow decay (median alpha ~ 0.95, so the chunk
+    maps are far from zero and every step of a 511-step chain matters), computed gates:
+    B H is a multiple of 8, so the composition takes its XCD-ordered dispatch.  All router
+    rows of heads {0, 7}; routed states and outputs of query chunks {1, 257, 511}."""
+    W = inputs.Workload("routed_slow", B=1, T=32768, H=8, dk=128, dv=128, C=C, dtype="bf16", tau=1e-3)
+    note("routed prefill full length, slow decay")
+    x = inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=5, stream=inputs.STREAM["routed_prefill"],
+                          alpha_mode="slow")
+    N = W.N
+    r, o = _routed_calls(x, W, N)
+    pairs = [(0, 0), (0, W.H - 1)]
+    refs = _router_refs(x, pairs, W.tau)
+    for b, hh in pairs:
+        _check_router_all_rows(r, b, hh, refs[(b, hh)], W.tau, N)
+        _routed_rows(x, r, o, b, hh, [1, 257, N - 1], refs[(b, hh)], W.dtype)
 
 
 @pytest.mark.parametrize("T,with_s0", [(16 * C + 37, True), (40 * C - 5, False)])
@@ -211,10 +276,28 @@ def test_tail_replay_full_size_sampled():
     ws = torch.empty(h.workspace_bytes(h.FN_GDN_PREFILL, d), dtype=torch.uint8, device="cuda")
     h.gdn_prefill(None, k[:, -L:], v[:, -L:], beta[:, -L:], alpha[:, -L:], want_o=False, S_final=S, ws=ws)
     torch.cuda.synchronize()
-    for b, hh in ((0, 0), (5, 7), (7, 15)):
+    picks = ((0, 0), (5, 7), (7, 15))
+    for b, hh in picks:
         _, kk, vv, bb, aa = seq(x, b, hh)
         _, S_ref = oracle.gdn_recurrent(None, kk, vv, bb, aa)
         assert_close(host(S[b, hh]), S_ref.T, W.dtype, f"S_replay b{b} h{hh}")
+    # [TR]: the rebuilt state against the full 32768-token prefix state.  They differ by at
+    # most (prod of the suffix alphas) ||S_{T-L}||_2 (about 1e-3000 here), so the bf16 bar
+    # plus that bound holds
+    note("tail replay vs full prefix")
+    xp = inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["tail_replay"],
+                           with_q=False, t_range=(0, W.T - L))
+    kk, vv, bb, aa = (np.stack([xp.f64(n)[b, :, hh] for b, hh in picks]) for n in ("k", "v", "beta", "alpha"))
+    _, S_pre = oracle.gdn_recurrent(None, kk, vv, bb, aa)
+    for i, (b, hh) in enumerate(picks):
+        _, ks_, vs_, bs_, as_ = seq(x, b, hh)
+        _, S_full = oracle.gdn_recurrent(None, ks_, vs_, bs_, as_, S0=S_pre[i])
+        lb = oracle.tail_replay_bound_log10(as_, S_pre[i])
+        assert lb < -100
+        bound_rel = 10.0 ** lb / np.max(np.abs(S_full))
+        e = assert_close(host(S[b, hh]), S_full.T, W.dtype, f"S_replay vs full prefix b{b} h{hh}",
+                         tol=2e-2 + bound_rel)
+        note(f"    bound log10 {lb:.0f}, rel err vs full prefix {e:.2e}")
 
 
 def test_decode_full_size_sampled():

@@ -378,10 +378,15 @@ def test_tail_replay_error_bound():
     _, k, v, beta, alpha = _rand_seq(rng, T, 5, 4, slow=True)
     S_rep, S_full = oracle.tail_replay(k, v, beta, alpha, L)
     _, S_pre = oracle.gdn_recurrent(None, k[:T - L], v[:T - L], beta[:T - L], alpha[:T - L])
-    bound = np.prod(alpha[T - L:]) * np.linalg.norm(S_pre, 2)
+    bound = 10.0 ** oracle.tail_replay_bound_log10(alpha[T - L:], S_pre)
     err = np.linalg.norm(S_full - S_rep, 2)
     assert err <= bound * (1 + 1e-12) + 1e-14
     assert err > 0.1 * bound  # the bound is not vacuous here
+    # equality case: one token with k orthogonal to the prefix state's rows (beta = 0), so
+    # the only difference is alpha times the starting state
+    S0 = rng.standard_normal((4, 5))
+    _, S_a = oracle.gdn_recurrent(None, np.zeros((1, 5)), np.zeros((1, 4)), np.zeros(1), np.array([0.3]), S0=S0)
+    assert math.isclose(np.linalg.norm(S_a, 2), 10.0 ** oracle.tail_replay_bound_log10([0.3], S0), rel_tol=1e-12)
     # With L = T the replay is the full prefill.
     S_rep2, S_full2 = oracle.tail_replay(k, v, beta, alpha, T)
     np.testing.assert_array_equal(S_rep2, S_full2)
