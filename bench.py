@@ -113,6 +113,24 @@ def rel_err(got, ref):
     return float(np.max(np.abs(got - ref))) / scale if scale > 0 else float(np.max(np.abs(got)))
 
 
+def timed_kernels(fn, steps, warmup, torch, hla):
+    """timed() with the library's per-kernel HIP-event timing on: (seconds per call, average
+    milliseconds per launch of each kernel kind that ran)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    hla.timing_enable(True)
+    dt = timed(fn, steps, 0, torch)
+    names = (("chunk", hla.KERNEL_CHUNK), ("scan", hla.KERNEL_SCAN), ("prefill", hla.KERNEL_PREFILL))
+    kms = {}
+    for name, kid in names:
+        ms, n = hla.timing_read(kid)
+        if n:
+            kms[name] = round(ms / n, 4)
+    hla.timing_enable(False)
+    return dt, kms
+
+
 def timed(fn, steps, warmup, torch):
     for _ in range(warmup):
         fn()
@@ -391,10 +409,11 @@ def bench_native_prefill(args, torch, hla, inputs):
     ws = torch.empty(hla.workspace_bytes(hla.FN_GDN_PREFILL, d), dtype=torch.uint8, device="cuda")
     o = torch.empty((W.B, W.T, W.H, W.dv), dtype=torch.float32, device="cuda")
     S = torch.empty((W.B, W.H, W.dk, W.dv), dtype=torch.float32, device="cuda")
-    dt = timed(lambda: hla.gdn_prefill(q, k, v, beta, alpha, o=o, S_final=S, ws=ws), 20, 3, torch)
+    dt, kms = timed_kernels(lambda: hla.gdn_prefill(q, k, v, beta, alpha, o=o, S_final=S, ws=ws), 20, 3, torch, hla)
     bytes_alg = W.B * W.T * W.H * (2 * W.dk * 2 + W.dv * 2 + 2 * 4 + W.dv * 4) + W.B * W.H * W.dk * W.dv * 4
     res = dict(workload="native_prefill", B=W.B, T=W.T, H=W.H, ms_per_step=dt * 1e3, tokens_per_s=W.B * W.T / dt,
-               algorithmic_gbs=bytes_alg / dt / 1e9, hbm_frac=round(bytes_alg / dt / 1e9 / PEAK_HBM_GBS, 4))
+               algorithmic_gbs=bytes_alg / dt / 1e9, hbm_frac=round(bytes_alg / dt / 1e9 / PEAK_HBM_GBS, 4),
+               kernel_ms=kms)
     log(f"[native_prefill] {dt*1e3:.3f} ms, {W.B*W.T/dt/1e6:.2f} M tok/s, {bytes_alg/dt/1e9:.0f} GB/s algorithmic")
     return res
 
@@ -606,7 +625,8 @@ def bench_tail_replay(args, torch, hla, inputs):
     S = torch.empty((W.B, W.H, W.dk, W.dv), dtype=torch.float32, device="cuda")
     d_rep = hla.make_dims(W.B, L, W.H, W.T, W.dk, W.dv, hla.HLA_BF16)
     ws_rep = hla._workspace(hla.workspace_bytes(hla.FN_GDN_PREFILL, d_rep), "cuda")
-    dt_rep = timed(lambda: hla.gdn_prefill(None, ks, vs, bs, als, want_o=False, S_final=S, ws=ws_rep), 20, 3, torch)
+    dt_rep, kms = timed_kernels(lambda: hla.gdn_prefill(None, ks, vs, bs, als, want_o=False, S_final=S, ws=ws_rep), 20, 3,
+                                torch, hla)
     d_full = hla.make_dims(W.B, W.T, W.H, W.T, W.dk, W.dv, hla.HLA_BF16)
     ws_full = hla._workspace(hla.workspace_bytes(hla.FN_GDN_PREFILL, d_full), "cuda")
     S2 = torch.empty_like(S)
@@ -617,7 +637,7 @@ def bench_tail_replay(args, torch, hla, inputs):
                ms_full_prefix_state=dt_full * 1e3, speedup_vs_full=dt_full / dt_rep,
                replay_tokens_per_s=W.B * L / dt_rep, algorithmic_gbs=bytes_alg / dt_rep / 1e9,
                hbm_frac=round(bytes_alg / dt_rep / 1e9 / PEAK_HBM_GBS, 4),
-               rel_err_vs_gpu_full_prefix=rel_err(Sh, S2h),
+               rel_err_vs_gpu_full_prefix=rel_err(Sh, S2h), kernel_ms=kms,
                note="rel_err_vs_gpu_full_prefix compares the rebuilt states of all sequences with the GPU's "
                     "full-prefix states; the oracle leg adds both against the oracle and the P11 bound")
     log(f"[tail_replay] replay {dt_rep*1e3:.3f} ms vs full-prefix state {dt_full*1e3:.3f} ms "

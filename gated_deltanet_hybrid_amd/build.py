@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libhla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["chunk.hip", "scan.hip", "route.hip", "compose.hip", "decode.hip", "reps.hip", "gdn2.hip", "compose_bwd.hip", "chunk_bwd.hip", "router_bwd.hip", "abi.cpp", "timing.cpp"]
+SOURCES = ["chunk.hip", "scan.hip", "prefill.hip", "route.hip", "compose.hip", "decode.hip", "reps.hip", "gdn2.hip", "compose_bwd.hip", "chunk_bwd.hip", "router_bwd.hip", "abi.cpp", "timing.cpp"]
 
 # Packed fp32 VALU ops are disabled for the device: the kernels are written with scalar
 # fp32 arithmetic and must not be turned into v_pk_* instructions.
@@ -28,9 +28,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.
           "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
 
 
+# Per-source device flags.  prefill.hip keeps the next piece's operands in small register
+# arrays while the current piece computes; LLVM would otherwise move such arrays into LDS
+# when LDS is free, which turns every prefetch load into a load, a wait and an LDS store.
+SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "-disable-promote-alloca-to-lds"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

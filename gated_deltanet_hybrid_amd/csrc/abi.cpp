@@ -78,6 +78,9 @@ PrefillWs prefill_ws(const hla_dims_t* d) {
   return w;
 }
 
+// Workspace of the native bf16 Gated DeltaNet prefill: one UT record per (b, h, piece).
+int64_t native_ws(const hla_dims_t* d) { return d->B * d->H * n_pieces(d) * hla::ut_record_bytes(d->dk, d->dv); }
+
 // Workspace of hla_route_mix: float32 query-chunk means, then (bf16 only) the reordered
 // copy of At - I that the composition streams.
 int64_t route_qbar_bytes(const hla_dims_t* d) { return round_up(d->B * d->H * n_chunks(d) * d->dk * 4, 256); }
@@ -300,6 +303,18 @@ hla_status_t prefill_body(const hla_dims_t* d, hla::ChunkArgs a, const float* S0
     b.chunk_init = s.states;
     b.chunk_init_t = s.states_t;
     return hip_status(chunk_pass(b, d, false, true, stream));
+  }
+  if (d->dtype == HLA_BF16 && a.variant == 0 && o) {
+    // bf16 Gated DeltaNet with outputs: the per-piece UT records, then one state pass per
+    // (b, h, 32 columns) that carries the state through the pieces and writes the outputs
+    // on the way (wu is not read).  A state-only call (Tail-Replay) takes the chunk maps and
+    // their scan below, which measured faster when no outputs are formed.
+    if (!ws || (int64_t)ws_bytes < native_ws(d)) return HLA_ERR_WORKSPACE;
+    hla::UtArgs f{};
+    f.q = o ? a.q : nullptr; f.k = a.k; f.v = a.v; f.beta = a.beta; f.alpha = a.alpha;
+    f.S0 = S0; f.o = o; f.S_final = S_final; f.rec = ws;
+    f.B = d->B; f.T = d->T; f.H = d->H; f.ld_T = d->ld_T; f.N = N;
+    return hip_status(hla::launch_prefill_native(f, d->dk, d->dv, stream));
   }
   const int64_t need = o ? w.total : w.total_ab;
   if (!ws || (int64_t)ws_bytes < need) return HLA_ERR_WORKSPACE;

@@ -68,6 +68,31 @@ hipError_t launch_scan_segments(const ScanArgs& a, int dk, int dv, hipStream_t s
 // Per segment, the composite map (seg_At, seg_Bc) of its chunks (bf16).
 hipError_t launch_combine_segments(const ScanArgs& a, int dk, int dv, hipStream_t s);
 
+struct UtArgs {
+  const void* q;        // [B,ld_T,H,dk] bf16 (read when o is set)
+  const void* k;        // [B,ld_T,H,dk] bf16
+  const void* v;        // [B,ld_T,H,dv] bf16
+  const float* beta;    // [B,ld_T,H]
+  const float* alpha;   // [B,ld_T,H]
+  const float* S0;      // [B,H,dk,dv] or null (zero)
+  float* o;             // [B,T,H,dv] or null (state only)
+  float* S_final;       // [B,H,dk,dv] or null
+  void* rec;            // workspace: one record of ut_record_bytes per (b, h, piece)
+  int64_t B, T, H, ld_T;
+  int32_t N;            // 64-token pieces
+};
+// One piece's record in the native prefill's workspace, at these byte offsets: -W [64][dk]
+// bf16; U^T in the state pass's lane order [dv/32][2][64][16] bf16; the log decays g [64]
+// float32; P = (Q K^T) o Gamma [64][64] bf16 (lower with the diagonal; written when outputs
+// are wanted).
+constexpr int64_t ut_off_u(int dk) { return (int64_t)128 * dk; }
+constexpr int64_t ut_off_g(int dk, int dv) { return (int64_t)128 * (dk + dv); }
+constexpr int64_t ut_off_p(int dk, int dv) { return ut_off_g(dk, dv) + 256; }
+constexpr int64_t ut_record_bytes(int dk, int dv) { return ut_off_p(dk, dv) + 64 * 64 * 2; }
+// Native bf16 prefill: the per-piece UT pass, then the state pass that carries the state
+// through the pieces (prefill.hip).
+hipError_t launch_prefill_native(const UtArgs& a, int dk, int dv, hipStream_t s);
+
 struct RouteArgs {
   const void* q;        // [B,ld_T,H,dk]
   const void* reps;     // [B,ld_R,H,dk]

@@ -19,6 +19,7 @@ _lib = None
 HLA_F32, HLA_BF16 = 0, 1
 KERNEL_CHUNK, KERNEL_SCAN, KERNEL_GATES, KERNEL_COMPOSE, KERNEL_DECODE, KERNEL_REPS = 0, 1, 2, 3, 4, 5
 KERNEL_BWD_SAVE, KERNEL_BWD_ADJOINT, KERNEL_BWD_REDUCE, KERNEL_BWD_CHUNK, KERNEL_BWD_ROUTER = 6, 7, 8, 9, 10
+KERNEL_PREFILL = 11
 FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX, FN_WU_HANDOFF, FN_CHUNK_REPS = 0, 1, 2, 3, 4
 FN_COMPOSE_BACKWARD, FN_PREFILL_BACKWARD, FN_CHUNK_BACKWARD = 5, 6, 7
 FN_COMPOSE_BACKWARD_MIN, FN_PREFILL_BACKWARD_MIN = 8, 9  # smallest workspaces (query chunks in groups)
@@ -177,7 +178,7 @@ def _check_wu(wu, d):
         return
     need = workspace_bytes(FN_WU_HANDOFF, d)
     if need == 0:
-        raise ValueError("the W | U hand-off takes bfloat16 inputs only")
+        return  # float32 takes no hand-off: the library rejects a buffer (HLA_ERR_UNSUPPORTED)
     if wu.dtype != torch.uint8 or not wu.is_cuda or not wu.is_contiguous() or wu.numel() < need:
         raise ValueError(f"wu must be a contiguous CUDA uint8 tensor of at least {need} bytes (see wu_buffer)")
 

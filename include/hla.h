@@ -138,14 +138,21 @@ hla_status_t hla_chunk_transitions(const hla_dims_t* d, const void* k, const voi
  *   chunk_init [B, H, N, dk, dv] float32 or NULL.
  *   wu         (optional, bf16 only): a buffer of hla_workspace_bytes(HLA_FN_WU_HANDOFF)
  *           bytes that hla_chunk_transitions filled from the same k, v, beta, alpha and
- *           dims, or NULL.  Given, the output pass reads W and U
- *           from it instead of recomputing them; results are identical.
+ *           dims, or NULL.  Given, the routed output pass reads W and U from it instead
+ *           of recomputing them; results are identical.  The native bf16 prefill forms
+ *           W and U inside its single pass and does not read it.
  *   o          [B, T, H, dv] float32 (out) or NULL.
  *   S_final    [B, H, dk, dv] float32 (out) or NULL.  At least one of o, S_final.
  *   ws, ws_bytes: workspace of at least hla_workspace_bytes(HLA_FN_GDN_PREFILL) bytes
  *           (none in routed mode with C = 64; in routed mode with C > 64 every chunk's
  *           64-token pieces start from states scanned from its routed state).  The
  *           native outputs do not depend on C: the prefill runs on 64-token pieces.
+ * Native mode with bf16 inputs and outputs runs in two passes and never forms the chunk
+ * maps (a state-only call scans the chunk maps instead): a parallel pass writes every
+ * piece's UT products (-W, U^T, the log decays and (Q K^T) o decay: B H ceil(T / 64)
+ * (128 (dk + dv) + 8448) bytes of the workspace), then one workgroup per (b, h, 32 state
+ * columns) carries the state through the pieces in order, forming each piece's outputs
+ * and next state on the way; no state goes through HBM.
  * Errors: as hla_chunk_transitions, plus HLA_ERR_WORKSPACE, HLA_ERR_UNSUPPORTED.
  */
 hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, const void* v,
@@ -416,7 +423,8 @@ typedef enum {
   HLA_KERNEL_BWD_REDUCE = 8,  /* backward: per-history-chunk sums (dAt, dBc, gates, dS0)  */
   HLA_KERNEL_BWD_CHUNK = 9,   /* backward: per-chunk reverse token recurrence            */
   HLA_KERNEL_BWD_ROUTER = 10, /* backward: router gates to queries and keys              */
-  HLA_KERNEL_COUNT = 11
+  HLA_KERNEL_PREFILL = 11,    /* one-pass native prefill (bf16): UT, outputs, state scan */
+  HLA_KERNEL_COUNT = 12
 } hla_kernel_t;
 
 /*

@@ -122,13 +122,14 @@ def test_prefill_validation(lib):
     assert pre(ctypes.byref(d), P, P, P, P, P, P, P, None, P, None, None, 0, None) == UNSUPPORTED
     assert pre(ctypes.byref(d), P, P, P, P, P, None, P, None, P, P, None, 0, None) == UNSUPPORTED
     # native mode without enough workspace
-    need = hla.workspace_bytes(hla.FN_GDN_PREFILL, d)
-    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, None, P, P, P, need - 1, None) == WORKSPACE
+    d32 = dims(dtype=0)
+    need = hla.workspace_bytes(hla.FN_GDN_PREFILL, d32)
+    assert pre(ctypes.byref(d32), P, P, P, P, P, None, None, None, P, P, P, need - 1, None) == WORKSPACE
+    assert pre(ctypes.byref(d32), P, P, P, P, P, None, None, None, P, P, None, 0, None) == WORKSPACE
     assert pre(ctypes.byref(d), P, P, P, P, P, None, None, None, P, P, None, 0, None) == WORKSPACE
-    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, None, P, P, PU, need, None) == ALIGN
+    assert pre(ctypes.byref(d), P, P, P, P, P, None, None, None, P, P, PU, 1 << 30, None) == ALIGN
     # the W | U hand-off: 16-byte aligned, bf16 only
     assert pre(ctypes.byref(d), P, P, P, P, P, None, P, PU, P, None, None, 0, None) == ALIGN
-    d32 = dims(dtype=0)
     assert pre(ctypes.byref(d32), P, P, P, P, P, None, P, P, P, None, None, 0, None) == UNSUPPORTED
     assert lib.hla_chunk_transitions(ctypes.byref(d32), P, P, P, P, P, P, P, None, 0, None) == UNSUPPORTED
     assert lib.hla_chunk_transitions(ctypes.byref(d), P, P, P, P, P, P, PU, None, 0, None) == ALIGN
