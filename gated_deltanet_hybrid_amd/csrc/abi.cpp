@@ -358,6 +358,7 @@ const char* hla_status_string(int32_t s) {
     case HLA_ERR_UNSUPPORTED: return "unsupported combination of arguments";
     case HLA_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
     case HLA_ERR_INTERNAL: return "internal error";
+    case HLA_ERR_SCRATCH_LIMIT: return "the problem needs more scratch than the fixed device buffer holds";
     default: return "unknown status";
   }
 }
@@ -446,9 +447,10 @@ hla_status_t hla_gdn2_prefill(const hla_dims_t* d, const void* q, const void* k,
   return prefill_body(d, a, S0, chunk_init, nullptr, o, S_final, ws, ws_bytes, stream);
 }
 
-hla_status_t hla_chunk_reps(const hla_dims_t* d, const void* k, int32_t window, const void* Wq, const void* Wk,
-                            const void* Wv, const void* Wp, const void* Wr, int64_t w_hstride, void* reps, void* ws,
-                            size_t ws_bytes, hipStream_t stream) {
+// Shared checks and arguments of the two representative entry points (all but the scratch).
+static hla_status_t reps_args(const hla_dims_t* d, const void* k, int32_t window, const void* Wq, const void* Wk,
+                              const void* Wv, const void* Wp, const void* Wr, int64_t w_hstride, void* reps,
+                              hla::RepsArgs* a) {
   hla_status_t st = check_dims(d);
   if (st != HLA_OK) return st;
   if (!k || !Wq || !Wk || !Wv || !Wp || !reps) return HLA_ERR_NULL_ARG;
@@ -456,15 +458,38 @@ hla_status_t hla_chunk_reps(const hla_dims_t* d, const void* k, int32_t window, 
   const int64_t wsz = (int64_t)d->dk * d->dk;
   if (w_hstride != 0 && w_hstride < wsz) return HLA_ERR_BAD_SHAPE;
   if ((w_hstride * dtype_bytes(d->dtype)) % 16 != 0) return HLA_ERR_ALIGN;
-  if (!all_aligned(k, Wq, Wk, Wv, Wp, Wr, reps, ws)) return HLA_ERR_ALIGN;
-  const int32_t n_rep = d->C / window;
-  if (!ws || (int64_t)ws_bytes < reps_ws(d, n_rep)) return HLA_ERR_WORKSPACE;
-  hla::RepsArgs a{};
-  a.k = k; a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T;
-  a.C = d->C; a.window = window; a.N = (int32_t)n_chunks(d);
-  a.Wq = Wq; a.Wk = Wk; a.Wv = Wv; a.Wp = Wp; a.Wr = Wr; a.w_hstride = w_hstride;
+  if (!all_aligned(k, Wq, Wk, Wv, Wp, Wr, reps)) return HLA_ERR_ALIGN;
+  *a = hla::RepsArgs{};
+  a->k = k; a->B = d->B; a->T = d->T; a->H = d->H; a->ld_T = d->ld_T;
+  a->C = d->C; a->window = window; a->N = (int32_t)n_chunks(d);
+  a->Wq = Wq; a->Wk = Wk; a->Wv = Wv; a->Wp = Wp; a->Wr = Wr; a->w_hstride = w_hstride;
+  a->reps = reps;
+  return HLA_OK;
+}
+
+hla_status_t hla_chunk_reps(const hla_dims_t* d, const void* k, int32_t window, const void* Wq, const void* Wk,
+                            const void* Wv, const void* Wp, const void* Wr, int64_t w_hstride, void* reps, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  hla::RepsArgs a;
+  const hla_status_t st = reps_args(d, k, window, Wq, Wk, Wv, Wp, Wr, w_hstride, reps, &a);
+  if (st != HLA_OK) return st;
+  if (!aligned16(ws)) return HLA_ERR_ALIGN;
+  if (!ws || (int64_t)ws_bytes < reps_ws(d, d->C / window)) return HLA_ERR_WORKSPACE;
   a.pooled = static_cast<float*>(ws);
-  a.reps = reps;
+  return hip_status(hla::launch_reps(a, d->dtype, d->dk, stream));
+}
+
+hla_status_t hla_chunk_reps_noalloc(const hla_dims_t* d, const void* k, int32_t window, const void* Wq,
+                                    const void* Wk, const void* Wv, const void* Wp, const void* Wr,
+                                    int64_t w_hstride, void* reps, hipStream_t stream) {
+  hla::RepsArgs a;
+  const hla_status_t st = reps_args(d, k, window, Wq, Wk, Wv, Wp, Wr, w_hstride, reps, &a);
+  if (st != HLA_OK) return st;
+  // the size limit is checked before anything touches the GPU
+  if (reps_ws(d, d->C / window) > hla::kRepsScratchBytes) return HLA_ERR_SCRATCH_LIMIT;
+  float* scratch = nullptr;
+  if (hla::reps_scratch(&scratch) != hipSuccess) return HLA_ERR_HIP;
+  a.pooled = scratch;
   return hip_status(hla::launch_reps(a, d->dtype, d->dk, stream));
 }
 

@@ -163,6 +163,10 @@ struct RepsArgs {
 };
 // Learned chunk representatives: window self-attention, mean-pool, projections.
 hipError_t launch_reps(const RepsArgs& a, int dtype, int dk, hipStream_t s);
+// Bytes of the fixed device scratch that hla_chunk_reps_noalloc keeps its window means in.
+constexpr int64_t kRepsScratchBytes = (int64_t)32 << 20;
+// That scratch on the current device (its address looked up once per device, then cached).
+hipError_t reps_scratch(float** out);
 
 struct ComposeBwdArgs {
   const void* At;        // [B,H,N,dk,dk] (dtype)

@@ -20,6 +20,8 @@
 //   project one wavefront per 32 windows: Wp pooled, then Wr^T of that, both as MFMA
 //           products with the float32 operand split into bf16 high and low parts; the
 //           result goes through LDS so rows are stored as 16-byte runs.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
@@ -297,6 +299,34 @@ static hipError_t launch_reps_t(RepsArgs a, hipStream_t s) {
   const int64_t bph = (nrows + 32 * kProjWaves - 1) / (32 * kProjWaves);
   hipLaunchKernelGGL((reps_project_kernel<T, DK>), dim3((unsigned)(BH * bph)), dim3(kProjWaves * 64), 0, s, a);
   return hipGetLastError();
+}
+
+// The window means of hla_chunk_reps_noalloc, for callers that cannot allocate: a fixed
+// array in device memory, one per GPU the library runs on, held until the process ends.
+// Every call on a GPU shares that GPU's copy (calls that overlap on one GPU race); the
+// pooling kernel writes every row of it before the projection reads any, so nothing needs
+// clearing between calls.
+static __device__ __align__(256) float scratch[kRepsScratchBytes / 4];
+
+hipError_t reps_scratch(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // the host-side name of the array is no device address: ask the runtime for this
+    // device's copy, with the device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = static_cast<float*>(addr[dev]);
+  return hipSuccess;
 }
 
 hipError_t launch_reps(const RepsArgs& a, int dtype, int dk, hipStream_t s) {

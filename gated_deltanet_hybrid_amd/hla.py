@@ -25,6 +25,8 @@ FN_COMPOSE_BACKWARD, FN_PREFILL_BACKWARD, FN_CHUNK_BACKWARD = 5, 6, 7
 FN_COMPOSE_BACKWARD_MIN, FN_PREFILL_BACKWARD_MIN = 8, 9  # smallest workspaces (query chunks in groups)
 CHUNK = 64
 MAX_CACHE_SLOTS = 1024
+REPS_SCRATCH_BYTES = 32 << 20  # fixed device scratch of chunk_reps_noalloc
+ERR_SCRATCH_LIMIT = 9
 
 
 class HlaError(RuntimeError):
@@ -54,6 +56,8 @@ _SIGS = {
                                           ctypes.c_size_t, _P]),
     "hla_chunk_reps": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, ctypes.c_int32, _P, _P, _P, _P, _P,
                                         ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]),
+    "hla_chunk_reps_noalloc": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                                ctypes.c_int64, _P, _P]),
     "hla_route_mix": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
                                        _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "hla_compose_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -323,6 +327,28 @@ def chunk_reps(k, W, window=32, C=CHUNK, out=None, ws=None):
     _check(library().hla_chunk_reps(ctypes.byref(d), _ptr(k), window, _ptr(W["Wq"]), _ptr(W["Wk"]), _ptr(W["Wv"]),
                                     _ptr(W["Wp"]), _ptr(W.get("Wr")), 0 if nh == 1 else dk * dk, _ptr(out),
                                     _ptr(ws), 0 if ws is None else ws.numel(), _stream(k.device)), "hla_chunk_reps")
+    return out
+
+
+def chunk_reps_noalloc(k, W, window=32, C=CHUNK, out=None):
+    """chunk_reps for callers that cannot allocate: the library keeps the window means in a
+    fixed device array (REPS_SCRATCH_BYTES per GPU) instead of a workspace.  ``out`` may be
+    given so that the call allocates nothing on the Python side either."""
+    B, T, H, dk, ld_T = _token_view(k, "k")
+    d = make_dims(B, T, H, ld_T, dk, dk, _dtype_code(k), C)
+    N = math.ceil(T / C)
+    n_rep = C // window
+    ws_ = [W[n] for n in ("Wq", "Wk", "Wv", "Wp")] + ([W["Wr"]] if W.get("Wr") is not None else [])
+    nh = ws_[0].shape[0]
+    for t in ws_:
+        if t.shape != (nh, dk, dk) or nh not in (1, H) or t.dtype != k.dtype or not t.is_contiguous():
+            raise ValueError("weights must be contiguous [H or 1, dk, dk] in k's dtype")
+    out = torch.empty((B, N * n_rep, H, dk), dtype=k.dtype, device=k.device) if out is None else out
+    _need(out, (B, N * n_rep, H, dk), k.dtype, "out")
+    _check(library().hla_chunk_reps_noalloc(ctypes.byref(d), _ptr(k), window, _ptr(W["Wq"]), _ptr(W["Wk"]),
+                                            _ptr(W["Wv"]), _ptr(W["Wp"]), _ptr(W.get("Wr")),
+                                            0 if nh == 1 else dk * dk, _ptr(out), _stream(k.device)),
+           "hla_chunk_reps_noalloc")
     return out
 
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define HLA_ABI_VERSION 5
+#define HLA_ABI_VERSION 6
 
 typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype_t;
 
@@ -65,7 +65,8 @@ typedef enum {
   HLA_ERR_HIP = 5,          /* a kernel launch failed                                  */
   HLA_ERR_UNSUPPORTED = 6,  /* a valid but unsupported combination of arguments        */
   HLA_ERR_ALIGN = 7,        /* a base pointer is not 16-byte aligned                   */
-  HLA_ERR_INTERNAL = 8      /* an unexpected host-side failure                         */
+  HLA_ERR_INTERNAL = 8,     /* an unexpected host-side failure                         */
+  HLA_ERR_SCRATCH_LIMIT = 9 /* a no-allocation call exceeds its fixed device scratch    */
 } hla_status_t;
 
 /* Problem sizes.  B batch rows, T tokens processed per row, H heads, ld_T >= T tokens
@@ -218,6 +219,24 @@ hla_status_t hla_chunk_reps(const hla_dims_t* d, const void* k, int32_t window, 
                             const void* Wk, const void* Wv, const void* Wp, const void* Wr,
                             int64_t w_hstride, void* reps, void* ws, size_t ws_bytes,
                             hipStream_t stream);
+
+/*
+ * hla_chunk_reps_noalloc -- hla_chunk_reps for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, kernels and results as hla_chunk_reps, without ws and ws_bytes: the
+ * float32 window means live in a fixed device array of 32 MiB (HLA_REPS_SCRATCH_BYTES)
+ * that the library holds on every GPU it runs on until the process ends; the call itself
+ * allocates nothing.  It holds B H ceil(T / C) (C / window) dk float32 values, so at
+ * dk = 128 up to 65536 (batch row, head, representative) rows.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * Errors: as hla_chunk_reps, and HLA_ERR_SCRATCH_LIMIT (returned before anything reaches
+ * the GPU) when the problem needs more than the fixed array.
+ */
+#define HLA_REPS_SCRATCH_BYTES ((size_t)32 << 20)
+hla_status_t hla_chunk_reps_noalloc(const hla_dims_t* d, const void* k, int32_t window, const void* Wq,
+                                    const void* Wk, const void* Wv, const void* Wp, const void* Wr,
+                                    int64_t w_hstride, void* reps, hipStream_t stream);
 
 /*
  * hla_route_mix -- HLA router gates and the gated composition of chunk transitions.

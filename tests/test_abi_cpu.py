@@ -35,8 +35,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hla_abi_version() == 5
-    for s in range(0, 9):
+    assert lib.hla_abi_version() == 6
+    for s in range(0, 10):
         assert lib.hla_status_string(s)
     assert lib.hla_status_string(99) == b"unknown status"
 
@@ -202,6 +202,25 @@ def test_chunk_reps_validation(lib):
     assert cr(ctypes.byref(d), P, 32, *W, None, 0, P, None, 0, None) == WORKSPACE
     assert lib.hla_workspace_bytes(hla.FN_CHUNK_REPS, ctypes.byref(d), 3, ctypes.byref(ctypes.c_size_t())) == BAD_SHAPE
     assert len(ok) == 13
+
+
+def test_chunk_reps_noalloc_validation(lib):
+    """The no-allocation variant checks what hla_chunk_reps checks, then its fixed scratch
+    limit, all before anything reaches the GPU."""
+    cr = lib.hla_chunk_reps_noalloc
+    W = [P, P, P, P]
+    d = dims(T=256, C=64)
+    # (d, k, window, Wq, Wk, Wv, Wp, Wr, w_hstride, reps, stream)
+    assert cr(ctypes.byref(d), None, 32, *W, None, 0, P, None) == NULL_ARG
+    assert cr(ctypes.byref(d), P, 32, *W, None, 0, None, None) == NULL_ARG
+    assert cr(ctypes.byref(d), P, 24, *W, None, 0, P, None) == BAD_SHAPE
+    assert cr(ctypes.byref(d), P, 32, *W, PU, 0, P, None) == ALIGN
+    # window means of B H N (C / window) rows of dk float32: 8 x 16 x 1024 x 128 x 4 bytes
+    # = 64 MiB > the 32 MiB array; 4 batch rows fit exactly
+    big = dims(B=8, T=32768, H=16, C=64)
+    assert cr(ctypes.byref(big), P, 32, *W, None, 0, P, None) == hla.ERR_SCRATCH_LIMIT
+    assert hla.workspace_bytes(hla.FN_CHUNK_REPS, dims(B=4, T=32768, H=16, C=64), 2) == hla.REPS_SCRATCH_BYTES
+    assert b"scratch" in lib.hla_status_string(hla.ERR_SCRATCH_LIMIT)
 
 
 def test_gdn2_validation(lib):
