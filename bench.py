@@ -11,14 +11,19 @@ state rebuild, the routed prefill's backward pass at T = 8192.  All inputs are s
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
 
-HBM traffic of the composition kernel (the roofline record's ``traffic``), from two counter
-passes over one routed-prefill step plus a 1 GiB calibration copy:
+Hardware counters behind the roofline records come from rocprofv3 passes over one line at a
+time (each counter set a run of its own, after a 1 GiB device copy that calibrates
+FETCH_SIZE / WRITE_SIZE), summarised into profiles/counters.json with a hash of the kernel
+sources; a line reports them only while its sources are unchanged:
 
-    cd /tmp && rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d <f> -o t -- \
-        python3 <repo>/bench.py --traffic-run
-    cd /tmp && rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d <w> -o t -- \
-        python3 <repo>/bench.py --traffic-run
-    python3 bench.py --traffic-write <f>/t_counter_collection.csv <w>/t_counter_collection.csv
+    cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <f> -o c -- \\
+        python3 <repo>/bench.py --counter-run <line>
+    (the same with WRITE_SIZE, and for the MFMA lines SQ_INSTS_VALU_MFMA_MOPS_BF16
+     SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS GRBM_GUI_ACTIVE)
+    python3 bench.py --counter-write <line> <f>/c_counter_collection.csv <w>/c_counter_collection.csv ...
+
+Kernel-time tables (warm-up and timed dispatches apart) come from a kernel trace of
+``--only <line>`` through ``--trace-summary``.
 """
 from __future__ import annotations
 
@@ -74,27 +79,22 @@ def flops_compose(pairs, dk, dv):
     return pairs * 2 * dk * dk * dv
 
 
+def compose_alg_bytes(n_chunks, W):
+    """Algorithmic HBM bytes of one composition launch: every chunk's transition pair
+    (At prepared, Bc; bf16) read once, however many query chunks route to it; the gates
+    (float32) and mask (byte) of every (query, history) chunk pair read; every routed state
+    (float32) written once."""
+    e = 2
+    n_q = W.B * W.H * n_chunks
+    return n_q * (W.dk * W.dk + W.dk * W.dv) * e + n_q * n_chunks * (4 + 1) + n_q * W.dk * W.dv * 4
+
+
 def sha_of(*paths):
     h = hashlib.sha256()
     for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
-
-
-def read_traffic(kernel_key, sources):
-    """HBM bytes per launch from the committed counter summary, or None when the kernel
-    source has changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    try:
-        rec = json.load(open(path)).get(kernel_key)
-    except Exception:
-        return None
-    if not rec or rec.get("source_sha") != sha_of(*sources):
-        return None
-    return rec.get("hbm_bytes_per_launch")
 
 
 # ----------------------------------------------------------------------------- helpers
@@ -140,6 +140,39 @@ def timed(fn, steps, warmup, torch):
         fn()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
+
+
+def gemm_ceiling(torch, n=16384):
+    """TFLOP/s of a plain bf16 GEMM (torch.matmul, n x n x n, standard normal operands) on
+    the same GPU: what the matrix cores sustain on dense random data under the board's
+    power limit, beside the published peak."""
+    a = torch.randn(n, n, device="cuda").bfloat16()
+    b = torch.randn(n, n, device="cuda").bfloat16()
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del a, b, c
+    torch.cuda.empty_cache()
+    return dict(op=f"torch.matmul bf16 {n}x{n}x{n}, N(0,1) operands", ms=round(ms, 3),
+                tflops=round(2 * n ** 3 / (ms / 1e3) / 1e12, 1))
+
+
+def kernel_counters(line, kms, kinds):
+    """Counter figures of the kernels behind the timed kinds {kind: avg ms} of a line."""
+    out = {}
+    for kind, kernel in kinds:
+        if kind in kms:
+            cf = counter_figures(line, kernel, kms[kind] / 1e3)
+            if cf:
+                out[kernel] = cf
+    return out or None
 
 
 # ----------------------------------------------------------------------------- routed prefill
@@ -215,7 +248,9 @@ def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None
         fl_total += W.B * W.H * N * (Cw // C) * 2 * W.dk * W.dk * (W.dk + W.dv)
     comp_avg_s = comp_ms / comp_n / 1e3
     achieved = fl_comp / comp_avg_s / 1e12
-    traffic = read_traffic(TRAFFIC_KEY, TRAFFIC_SOURCES)
+    cf = counter_figures(tag, "compose_bf16_kernel", comp_avg_s, flops=fl_comp,
+                         nbytes=compose_alg_bytes(N, W)) if tag == "routed_prefill" else None
+    traffic = cf["hbm_bytes_per_launch"] if cf and "hbm_bytes_per_launch" in cf else None
     tokens = W.B * W.T
     res = dict(
         value=tokens / dt, ms_per_step=dt * 1e3,
@@ -224,8 +259,13 @@ def bench_routed_prefill(args, torch, hla, inputs, Cw=C, gates_in=None, tau=None
         kernel_ms={kname: round(ms / n, 4) for kname, (ms, n) in per_kernel.items() if n > 0},
         roofline=dict(kernel="compose_bf16_kernel", bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
                       unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic,
-                      flops_per_launch=fl_comp, avg_launch_ms=round(comp_avg_s * 1e3, 4), launches=comp_n),
+                      flops_per_launch=fl_comp, avg_launch_ms=round(comp_avg_s * 1e3, 4), launches=comp_n,
+                      counters=cf),
     )
+    if tag == "routed_prefill":
+        gc = gemm_ceiling(torch)
+        res["roofline"]["library_gemm"] = dict(gc, frac_of_peak=round(gc["tflops"] / PEAK_BF16_TFLOPS, 4),
+                                               compose_vs_gemm=round(achieved / gc["tflops"], 3))
     if pooler is not None:
         rms, rn = per_kernel["reps"]
         r_ach = flops_reps_pool(n_windows, window, W.dk) / (rms / rn / 1e3) / 1e12
@@ -310,7 +350,7 @@ ONLY_LINES = {
 
 
 # ----------------------------------------------------------------------------- decode
-def bench_decode(args, torch, hla, inputs, gdn2=False, skip=False):
+def bench_decode(args, torch, hla, inputs, gdn2=False, skip=False, warm=8):
     """Decode at Bs=256, H=16 with 64 cached chunks per sequence; ``gdn2`` runs the Gated
     DeltaNet-2 live update (channel-wise gates per token) instead of Gated DeltaNet's.
     ``skip``: skip-heavy caller gates (sigmoid(N(-4, 3)) per cached chunk) at tau = 0.1, the
@@ -362,7 +402,7 @@ def bench_decode(args, torch, hla, inputs, gdn2=False, skip=False):
                            Bc_cache=Bc_cache, reps_cache=reps, n_cache=n_cache, tau=tau, o=o, gates_in=g_in)
 
     steps = args.decode_steps
-    for _ in range(8):
+    for _ in range(warm):
         step()
     torch.cuda.synchronize()
     hla.timing_enable(True)
@@ -386,8 +426,12 @@ def bench_decode(args, torch, hla, inputs, gdn2=False, skip=False):
                tokens_per_s=Bs / dt, hbm_gbs=bytes_step / kern_s / 1e9,
                roofline=dict(kernel="decode_kernel", bound="hbm", achieved=round(bytes_step / kern_s / 1e9, 1),
                              peak=PEAK_HBM_GBS, unit="GB/s", frac=round(bytes_step / kern_s / 1e9 / PEAK_HBM_GBS, 4),
-                             bytes_per_launch=bytes_step, avg_launch_ms=round(kern_s * 1e3, 4)),
+                             bytes_per_launch=bytes_step, avg_launch_ms=round(kern_s * 1e3, 4),
+                             traffic=None, counters=None),
                note="no commit while timing; live chunk extends past 64 tokens so every step does the same work")
+    if tag == "decode":
+        cf = counter_figures("decode", "decode_kernel", kern_s, nbytes=bytes_step)
+        res["roofline"].update(counters=cf, traffic=cf["hbm_bytes_per_launch"] if cf else None)
     if skip:
         res.update(active_chunk_frac=n_active / (Bs * H * n_cap), bytes_per_step=bytes_step,
                    dense_bytes_per_step=bytes_dense, bytes_frac_of_dense=bytes_step / bytes_dense,
@@ -400,7 +444,7 @@ def bench_decode(args, torch, hla, inputs, gdn2=False, skip=False):
 
 
 # ----------------------------------------------------------------------------- native prefill
-def bench_native_prefill(args, torch, hla, inputs):
+def bench_native_prefill(args, torch, hla, inputs, steps=20, warmup=3):
     W = inputs.WORKLOADS["native_prefill"]
     x = inputs.gen_tokens(W.B, W.T, W.H, W.dk, W.dv, dtype=W.dtype, seed=0, stream=inputs.STREAM["native_prefill"])
     q, k, v = (to_dev(a, W.dtype, torch) for a in (x.q, x.k, x.v))
@@ -409,11 +453,13 @@ def bench_native_prefill(args, torch, hla, inputs):
     ws = torch.empty(hla.workspace_bytes(hla.FN_GDN_PREFILL, d), dtype=torch.uint8, device="cuda")
     o = torch.empty((W.B, W.T, W.H, W.dv), dtype=torch.float32, device="cuda")
     S = torch.empty((W.B, W.H, W.dk, W.dv), dtype=torch.float32, device="cuda")
-    dt, kms = timed_kernels(lambda: hla.gdn_prefill(q, k, v, beta, alpha, o=o, S_final=S, ws=ws), 20, 3, torch, hla)
+    dt, kms = timed_kernels(lambda: hla.gdn_prefill(q, k, v, beta, alpha, o=o, S_final=S, ws=ws), steps, warmup,
+                            torch, hla)
     bytes_alg = W.B * W.T * W.H * (2 * W.dk * 2 + W.dv * 2 + 2 * 4 + W.dv * 4) + W.B * W.H * W.dk * W.dv * 4
     res = dict(workload="native_prefill", B=W.B, T=W.T, H=W.H, ms_per_step=dt * 1e3, tokens_per_s=W.B * W.T / dt,
                algorithmic_gbs=bytes_alg / dt / 1e9, hbm_frac=round(bytes_alg / dt / 1e9 / PEAK_HBM_GBS, 4),
-               kernel_ms=kms)
+               kernel_ms=kms, counters=kernel_counters("native_prefill", kms,
+                                                       (("chunk", "ut_kernel"), ("prefill", "state_kernel"))))
     log(f"[native_prefill] {dt*1e3:.3f} ms, {W.B*W.T/dt/1e6:.2f} M tok/s, {bytes_alg/dt/1e9:.0f} GB/s algorithmic")
     return res
 
@@ -608,7 +654,7 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, grouped_gib=Non
 
 
 # ----------------------------------------------------------------------------- Tail-Replay
-def bench_tail_replay(args, torch, hla, inputs):
+def bench_tail_replay(args, torch, hla, inputs, steps=20, warmup=3, full_prefix=True):
     """[TR]: the state of a 32768-token prefix rebuilt from its last 3277 tokens alone (a
     suffix view of the allocation, state-only), against the full-prefix state-only prefill
     on the GPU.  Returns the record and the two states of TAIL_PAIRS on the host, for the
@@ -625,8 +671,10 @@ def bench_tail_replay(args, torch, hla, inputs):
     S = torch.empty((W.B, W.H, W.dk, W.dv), dtype=torch.float32, device="cuda")
     d_rep = hla.make_dims(W.B, L, W.H, W.T, W.dk, W.dv, hla.HLA_BF16)
     ws_rep = hla._workspace(hla.workspace_bytes(hla.FN_GDN_PREFILL, d_rep), "cuda")
-    dt_rep, kms = timed_kernels(lambda: hla.gdn_prefill(None, ks, vs, bs, als, want_o=False, S_final=S, ws=ws_rep), 20, 3,
-                                torch, hla)
+    dt_rep, kms = timed_kernels(lambda: hla.gdn_prefill(None, ks, vs, bs, als, want_o=False, S_final=S, ws=ws_rep),
+                                steps, warmup, torch, hla)
+    if not full_prefix:
+        return dict(ms_replay=dt_rep * 1e3, kernel_ms=kms), None
     d_full = hla.make_dims(W.B, W.T, W.H, W.T, W.dk, W.dv, hla.HLA_BF16)
     ws_full = hla._workspace(hla.workspace_bytes(hla.FN_GDN_PREFILL, d_full), "cuda")
     S2 = torch.empty_like(S)
@@ -638,6 +686,7 @@ def bench_tail_replay(args, torch, hla, inputs):
                replay_tokens_per_s=W.B * L / dt_rep, algorithmic_gbs=bytes_alg / dt_rep / 1e9,
                hbm_frac=round(bytes_alg / dt_rep / 1e9 / PEAK_HBM_GBS, 4),
                rel_err_vs_gpu_full_prefix=rel_err(Sh, S2h), kernel_ms=kms,
+               counters=kernel_counters("tail_replay", kms, (("chunk", "chunk_kernel"), ("scan", "scan_bf16_kernel"))),
                note="rel_err_vs_gpu_full_prefix compares the rebuilt states of all sequences with the GPU's "
                     "full-prefix states; the oracle leg adds both against the oracle and the P11 bound")
     log(f"[tail_replay] replay {dt_rep*1e3:.3f} ms vs full-prefix state {dt_full*1e3:.3f} ms "
@@ -806,76 +855,220 @@ def cpu_baseline(n_query_chunks, tail_states=None):
                 single_thread=None if single is None else {"threads": single.pop("threads"), **single})
 
 
-# ----------------------------------------------------------------------------- HBM traffic
-TRAFFIC_KEY = "compose_routed_prefill"
-TRAFFIC_SOURCES = ["gated_deltanet_hybrid_amd/csrc/compose.hip"]
+# ----------------------------------------------------------------------------- counters
+# Hardware counters behind the roofline records, from rocprofv3 passes over short runs of
+# one line each (one counter set per pass, FETCH_SIZE and WRITE_SIZE scaled by their own
+# reading for a 1 GiB device copy), summarised into profiles/counters.json together with a
+# hash of the kernel sources; a line reports them only while the sources are unchanged.
+COUNTER_SOURCES = ["gated_deltanet_hybrid_amd/csrc/" + f for f in
+                   ("common.hpp", "kernels.hpp", "chunk.hip", "scan.hip", "prefill.hip", "route.hip", "compose.hip",
+                    "decode.hip")]
 CALIB_BYTES = 1 << 30
+COUNTER_LINES = ("routed_prefill", "native_prefill", "tail_replay", "decode")
 
 
-def traffic_run(torch, hla, inputs):
-    """One warm-up and one timed routed-prefill step, then a plain 1 GiB device copy (read
-    1 GiB, write 1 GiB) that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
-    args = argparse.Namespace(steps=1, warmup=1)
-    bench_routed_prefill(args, torch, hla, inputs)
+def counter_run(line, torch, hla, inputs):
+    """The line's timed call, once untimed and twice more, then a plain 1 GiB device copy
+    (read 1 GiB, write 1 GiB) twice, which calibrates FETCH_SIZE / WRITE_SIZE."""
+    args = argparse.Namespace(steps=2, warmup=1, decode_steps=2)
+    if line == "routed_prefill":
+        bench_routed_prefill(args, torch, hla, inputs)
+    elif line == "native_prefill":
+        bench_native_prefill(args, torch, hla, inputs, steps=2, warmup=1)
+    elif line == "tail_replay":
+        bench_tail_replay(args, torch, hla, inputs, steps=2, warmup=1, full_prefix=False)
+    elif line == "decode":
+        bench_decode(args, torch, hla, inputs, warm=1)
+    else:
+        sys.exit(f"no counter run for {line}; lines: {', '.join(COUNTER_LINES)}")
     src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(2):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log("[traffic] done")
+    log(f"[counters] {line} done")
 
 
-def _per_dispatch(csv_path, counter):
+def _counter_rows(csv_path):
+    """{(dispatch id, kernel name): {counter: summed value}} of one rocprofv3 counter file."""
     import csv
     per = {}
     for r in csv.DictReader(open(csv_path)):
-        if r["Counter_Name"] != counter:
-            continue
-        key = (r["Dispatch_Id"], r["Kernel_Name"], int(r["Grid_Size"]))
-        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        c = per.setdefault(key, {})
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     return per
 
 
-def _mean_of(per, pred):
-    """Mean counter value over the dispatches whose kernel name passes ``pred`` and whose
-    grid is the largest among those (the calibration copy, not incidental small copies)."""
-    sel = [(g, v) for (_, name, g), v in per.items() if pred(name)]
-    if not sel:
-        return None, 0
-    gmax = max(g for g, _ in sel)
-    vals = [v for g, v in sel if g == gmax]
-    return sum(vals) / len(vals), len(vals)
+_MANGLED_ARGS = (("DF16b", "bf16"), ("f", "float"))
 
 
-def traffic_write(fetch_csv, write_csv):
-    """HBM bytes per composition launch from the two counter passes (KiB per dispatch),
-    each scaled by the same counter's reading for the calibration copy of known size."""
-    is_copy = lambda n: "copy" in n.lower() and "hla::" not in n
-    is_comp = lambda n: "compose_bf16_kernel" in n
-    f, w = _per_dispatch(fetch_csv, "FETCH_SIZE"), _per_dispatch(write_csv, "WRITE_SIZE")
-    f_copy, n_fc = _mean_of(f, is_copy)
-    w_copy, n_wc = _mean_of(w, is_copy)
-    f_comp, n_f = _mean_of(f, is_comp)
-    w_comp, n_w = _mean_of(w, is_comp)
-    if None in (f_copy, w_copy, f_comp, w_comp):
-        sys.exit("traffic: a calibration copy or composition dispatch is missing from the counter files")
-    k_fetch = CALIB_BYTES / (f_copy * 1024.0)
-    k_write = CALIB_BYTES / (w_copy * 1024.0)
-    fetch_b = f_comp * 1024.0 * k_fetch
-    write_b = w_comp * 1024.0 * k_write
-    rec = dict(source_sha=sha_of(*TRAFFIC_SOURCES), hbm_bytes_per_launch=round(fetch_b + write_b),
-               fetch_bytes=round(fetch_b), write_bytes=round(write_b), fetch_kib_raw=round(f_comp, 1),
-               write_kib_raw=round(w_comp, 1), calib_fetch_factor=round(k_fetch, 4),
-               calib_write_factor=round(k_write, 4), calib_copy_bytes=CALIB_BYTES, launches=[n_f, n_w],
-               kernel="compose_bf16_kernel", workload="routed_prefill B=1 H=16 T=32768 d=128 C=64 bf16")
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def kernel_key(name):
+    """A readable key of a library kernel's trace name, template arguments kept:
+    'void hla::ut_kernel<128, 128>(hla::UtArgs)' -> 'ut_kernel<128, 128>', and the mangled
+    names the demangler leaves alone (bf16 template arguments) decoded the same way,
+    '_ZN3hla13decode_kernelIDF16bLi128E...Lb0EEEv...' -> 'decode_kernel<bf16, 128, ..., false>'."""
+    import re
+    if name.startswith("_ZN3hla"):
+        m = re.match(r"_ZN3hla(\d+)", name)
+        n = int(m.group(1))
+        ident = name[m.end():m.end() + n]
+        rest = name[m.end() + n:]
+        args = []
+        if rest.startswith("I"):
+            rest = rest[1:]
+            while rest and not rest.startswith("E"):
+                m2 = re.match(r"L([ib])(\d+)E", rest)
+                if m2:
+                    args.append(m2.group(2) if m2.group(1) == "i" else ("true" if m2.group(2) == "1" else "false"))
+                    rest = rest[m2.end():]
+                    continue
+                for code, txt in _MANGLED_ARGS:
+                    if rest.startswith(code):
+                        args.append(txt)
+                        rest = rest[len(code):]
+                        break
+                else:
+                    args.append("?")
+                    break
+        return ident + (f"<{', '.join(args)}>" if args else "")
+    s = name.replace("void ", "", 1).replace("hla::", "")
+    depth = 0
+    for i, ch in enumerate(s):
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            return s[:i]
+    return s
+
+
+def _short(name):
+    return kernel_key(name).split("<")[0]
+
+
+def counter_write(line, csv_paths):
+    """Per-kernel means over the line's dispatches of every counter in the given passes,
+    HBM bytes scaled by the calibration copy, into profiles/counters.json."""
+    sums, counts, calib = {}, {}, {}
+    for pth in csv_paths:
+        rows = _counter_rows(pth)
+        # the calibration copies are the run's last two runtime copy-buffer dispatches
+        copies = sorted((i, v) for (i, n), v in rows.items() if n.startswith("__amd_rocclr_copyBuffer"))[-2:]
+        if len(copies) != 2:
+            sys.exit(f"{pth}: the two calibration copies are missing")
+        for cn in copies[0][1]:
+            calib[cn] = (copies[0][1][cn] + copies[1][1][cn]) / 2
+        for (_, n), v in rows.items():
+            if "hla" not in n:
+                continue
+            k = kernel_key(n)
+            for cn, cv in v.items():
+                sums.setdefault(k, {}).setdefault(cn, 0.0)
+                sums[k][cn] += cv
+                counts.setdefault(k, {}).setdefault(cn, 0)
+                counts[k][cn] += 1
+    out = {}
+    for k, cs in sums.items():
+        rec = {}
+        for cn, tot in cs.items():
+            mean = tot / counts[k][cn]
+            rec[cn.lower() + "_mean"] = round(mean, 1)
+            if cn in ("FETCH_SIZE", "WRITE_SIZE") and cn in calib:
+                scale = CALIB_BYTES / (calib[cn] * 1024.0)
+                rec[("fetch" if cn == "FETCH_SIZE" else "write") + "_bytes"] = round(mean * 1024.0 * scale)
+                rec[cn.lower() + "_calib_factor"] = round(scale, 4)
+            if cn == "SQ_INSTS_VALU_MFMA_MOPS_BF16":
+                rec["mfma_bf16_flops"] = round(mean * 512)
+        rec["dispatches"] = max(counts[k].values())
+        if "fetch_bytes" in rec and "write_bytes" in rec:
+            rec["hbm_bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
+        out[k] = rec
+    path = os.path.join(ROOT, "profiles", "counters.json")
     allrec = json.load(open(path)) if os.path.exists(path) else {}
-    allrec[TRAFFIC_KEY] = rec
+    allrec[line] = dict(source_sha=sha_of(*COUNTER_SOURCES), kernels=out,
+                        calib_copy_bytes=CALIB_BYTES, calib_raw={k: round(v, 1) for k, v in calib.items()})
     with open(path, "w") as fh:
         json.dump(allrec, fh, indent=1, sort_keys=True)
         fh.write("\n")
-    print(json.dumps(rec, indent=1))
+    print(json.dumps(allrec[line], indent=1))
+
+
+def read_counters(line):
+    """The committed counter summary of a line's kernels, or None when a kernel source has
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(line)
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha") != sha_of(*COUNTER_SOURCES):
+        return None
+    return rec["kernels"]
+
+
+def counter_figures(line, kernel, avg_launch_s, flops=None, nbytes=None):
+    """Counter-derived rates of one kernel next to the algorithmic ones: HBM bytes per launch
+    (FETCH_SIZE + WRITE_SIZE) over the live average launch time, and bf16 MFMA FLOP per launch
+    (512 per SQ_INSTS_VALU_MFMA_MOPS_BF16) over the same time."""
+    ks = read_counters(line)
+    if not ks:
+        return None
+    hits = [n for n in ks if n == kernel or n.split("<")[0] == kernel]
+    if len(hits) != 1:
+        return None
+    k = ks[hits[0]]
+    out = dict(source="profiles/counters.json", kernel=hits[0])
+    if "hbm_bytes" in k:
+        out.update(hbm_bytes_per_launch=k["hbm_bytes"], fetch_bytes=k["fetch_bytes"], write_bytes=k["write_bytes"],
+                   hbm_gbs=round(k["hbm_bytes"] / avg_launch_s / 1e9, 1),
+                   hbm_frac=round(k["hbm_bytes"] / avg_launch_s / 1e9 / PEAK_HBM_GBS, 4))
+        if nbytes:
+            out["hbm_bytes_over_algorithmic"] = round(k["hbm_bytes"] / nbytes, 3)
+    if "mfma_bf16_flops" in k:
+        tf = k["mfma_bf16_flops"] / avg_launch_s / 1e12
+        out.update(mfma_flops_per_launch=k["mfma_bf16_flops"], mfma_tflops=round(tf, 1),
+                   mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4))
+        if flops:
+            out["mfma_flops_over_algorithmic"] = round(k["mfma_bf16_flops"] / flops, 3)
+    if "sq_valu_mfma_busy_cycles_mean" in k and "grbm_gui_active_mean" in k:
+        # busy cycles summed over the chip's SIMDs against the kernel's GPU-active cycles on all of them
+        out["mfma_busy_frac"] = round(k["sq_valu_mfma_busy_cycles_mean"] / (k["grbm_gui_active_mean"] * 256 * 4), 4)
+    for cn in ("sq_valu_mfma_busy_cycles_mean", "sq_busy_cycles_mean", "grbm_gui_active_mean",
+               "sq_lds_bank_conflict_mean", "sq_insts_lds_mean", "sq_waves_mean"):
+        if cn in k:
+            out[cn] = k[cn]
+    return out
+
+
+def trace_summary(csv_path, skip, take, title, command):
+    """Markdown table of a rocprofv3 kernel trace: per kernel, dispatches in time order, the
+    first `skip` as warm-up and the next `take` as the timed ones."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if "hla" not in r["Kernel_Name"]:
+            continue
+        per.setdefault(kernel_key(r["Kernel_Name"]), []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    lines = [f"# {title}", "", "Command, on one MI355X (`<repo>` is the checkout, `<out>` an output folder):", "",
+             f"    {command}", "",
+             f"Per kernel, dispatches in time order: the first {skip} are warm-up, the next {take} the timed ones "
+             "the bench line averages; durations in microseconds.", "",
+             "| kernel | timed | avg (us) | min (us) | max (us) | warm-up avg (us) | other dispatches |",
+             "|---|---|---|---|---|---|---|"]
+    for name, ds in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1][skip:skip + take])):
+        ds.sort()
+        warm, timed, rest = ds[:skip], ds[skip:skip + take], ds[skip + take:]
+        if not timed:
+            continue
+        td = [d / 1e3 for _, d in timed]
+        wa = sum(d for _, d in warm) / len(warm) / 1e3 if warm else float("nan")
+        lines.append(f"| `{name}` | {len(td)} | {sum(td) / len(td):.1f} | {min(td):.1f} | {max(td):.1f} | "
+                     f"{wa:.1f} | {len(rest)} |")
+    print("\n".join(lines))
 
 
 # ----------------------------------------------------------------------------- main
@@ -888,9 +1081,13 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="only the headline routed prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-chunks", type=int, default=512, help="query chunks of the oracle sample (512 = all of head 0)")
-    ap.add_argument("--traffic-run", action="store_true", help="one routed-prefill step plus a calibration copy (under rocprofv3 --pmc)")
-    ap.add_argument("--traffic-write", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/traffic.json from the two counter passes")
+    ap.add_argument("--counter-run", metavar="LINE",
+                    help="run one line's timed call three times and a 1 GiB calibration copy (under rocprofv3 --pmc)")
+    ap.add_argument("--counter-write", nargs="+", metavar=("LINE", "CSV"),
+                    help="summarise the counter passes of LINE (rocprofv3 counter_collection.csv files) into "
+                         "profiles/counters.json")
+    ap.add_argument("--trace-summary", nargs=5, metavar=("CSV", "SKIP", "TAKE", "TITLE", "COMMAND"),
+                    help="markdown table of a rocprofv3 kernel trace, warm-up and timed dispatches apart")
     ap.add_argument("--only", metavar="LINES",
                     help="profiling aid: run only these comma-separated lines (routed_prefill or a secondary "
                          "name) and print their results as one JSON object instead of the bench line")
@@ -902,8 +1099,12 @@ def main():
         rec = oracle_samples(args.oracle_samples, small=True)
         print(json.dumps({"threads": _blas_threads(), **rec}), flush=True)
         return
-    if args.traffic_write:
-        traffic_write(*args.traffic_write)
+    if args.counter_write:
+        counter_write(args.counter_write[0], args.counter_write[1:])
+        return
+    if args.trace_summary:
+        c, sk, tk, title, cmd = args.trace_summary
+        trace_summary(c, int(sk), int(tk), title, cmd)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: every (batch, head) of this path is independent, so --gpus {args.gpus} "
@@ -918,8 +1119,8 @@ def main():
         sys.exit(1)
     hla.library()
     torch.cuda.set_device(0)
-    if args.traffic_run:
-        traffic_run(torch, hla, inputs)
+    if args.counter_run:
+        counter_run(args.counter_run, torch, hla, inputs)
         return
 
     if args.only:

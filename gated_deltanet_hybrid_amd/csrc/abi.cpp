@@ -82,11 +82,14 @@ PrefillWs prefill_ws(const hla_dims_t* d) {
 int64_t native_ws(const hla_dims_t* d) { return d->B * d->H * n_pieces(d) * hla::ut_record_bytes(d->dk, d->dv); }
 
 // Workspace of hla_route_mix: float32 query-chunk means, then (bf16 only) the reordered
-// copy of At - I that the composition streams.
+// copies of At - I and of Bc that the composition streams.
 int64_t route_qbar_bytes(const hla_dims_t* d) { return round_up(d->B * d->H * n_chunks(d) * d->dk * 4, 256); }
+int64_t route_atp_bytes(const hla_dims_t* d) {
+  return d->dtype == HLA_BF16 ? round_up(d->B * d->H * n_chunks(d) * d->dk * d->dk * 2, 256) : 0;
+}
 int64_t route_ws(const hla_dims_t* d) {
-  const int64_t prep = d->dtype == HLA_BF16 ? round_up(d->B * d->H * n_chunks(d) * d->dk * d->dk * 2, 256) : 0;
-  return route_qbar_bytes(d) + prep;
+  const int64_t bcp = d->dtype == HLA_BF16 ? round_up(d->B * d->H * n_chunks(d) * d->dk * d->dv * 2, 256) : 0;
+  return route_qbar_bytes(d) + route_atp_bytes(d) + bcp;
 }
 
 // Workspace of hla_chunk_reps: float32 window means [B,H,N*n_rep,dk].
@@ -513,6 +516,7 @@ hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps,
   a.gates_in = gates_in; a.tau = tau; a.gates = gates; a.mask = mask; a.active_idx = active_idx;
   a.active_cnt = active_cnt; a.n_eff = n_eff; a.S_routed = S_routed; a.qbar = static_cast<float*>(ws);
   a.At_prep = static_cast<char*>(ws) + route_qbar_bytes(d);
+  a.Bc_prep = static_cast<char*>(a.At_prep) + route_atp_bytes(d);
   a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)N; a.C = d->C;
   return hip_status(hla::launch_route(a, d->dtype, d->dk, d->dv, stream));
 }
@@ -607,6 +611,7 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   r.active_cnt = reinterpret_cast<int32_t*>(base + w.acnt_off);
   r.n_eff = nullptr; r.S_routed = nullptr;
   r.qbar = fat(w.route_off); r.At_prep = base + w.route_off + route_qbar_bytes(d);
+  r.Bc_prep = static_cast<char*>(r.At_prep) + route_atp_bytes(d);
   r.B = d->B; r.T = d->T; r.H = d->H; r.ld_T = d->ld_T; r.N = N; r.C = d->C;
   e = hla::launch_route(r, d->dtype, d->dk, d->dv, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;

@@ -19,9 +19,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace hla {
 
 typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
@@ -29,6 +32,15 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 constexpr int kChunk = 64;  // tokens per chunk
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1, so that every
+// index inside the body is a constant (register arrays stay in registers).
+template <int B, int E, class F> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;

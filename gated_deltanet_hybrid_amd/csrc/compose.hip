@@ -13,13 +13,16 @@
 //     the whole chain; its bf16 copy (scaled by g) is the B operand of the next product
 //     without leaving the lane (the k order of the accumulator rows is matched by how At
 //     is read);
-//   * g Bc_j is one more pair of MFMAs per row tile: Bc_j as the A operand against g I;
+//   * g Bc_j is added on the vector ALU, not the matrix cores: Bc_j is stored in the order
+//     of the accumulator elements, so a lane reads the 16 values of one row tile as two
+//     16-byte units and adds g times each with a packed bf16 dot product (v_dot2 of the
+//     pair with (g, 0) or (0, g)) straight into the float32 accumulator;
 //   * (At_j - I, Bc_j) of the next history chunk are copied global -> LDS asynchronously
 //     (global_load_lds, 16 bytes per lane, every instruction a contiguous 1 KiB source)
 //     while the current one is multiplied;
-//   * a prep pass writes (At_j - I) in the exact byte order of its LDS image: every A
-//     fragment is one conflict-free 16-byte LDS read at a lane-constant address plus a
-//     compile-time offset, which leaves registers for a ring of fragment reads in flight;
+//   * a prep pass writes (At_j - I) and Bc_j in the exact byte order of their LDS images:
+//     every fragment is one conflict-free 16-byte LDS read at a lane-constant address plus
+//     a compile-time offset, which leaves registers for a ring of fragment reads in flight;
 //   * gates sit in one register per query chunk (64 history chunks per refill) and are
 //     broadcast with readlane, so the loop touches no other memory;
 //   * each XCD works through its heads one at a time, longest chain first, so the 32
@@ -79,6 +82,46 @@ __global__ __launch_bounds__(256) void prep_at_kernel(const bf16* __restrict__ A
   *reinterpret_cast<bf16x8*>(dst + 8) = swap ? h0 : h1;
 }
 
+// Bc_j in the order of the composition's accumulators.  A lane (column c32 of column tile
+// ct, half hh = lane / 32) holds in row tile rt the rows rt*32 + 8 g + 4 hh + i (g, i =
+// 0..3) as its accumulator elements e = 4 g + i.  Unit (ct, rt, p) of the image is 1 KiB:
+// lane L = 32 hh + c32 at bytes 16 L .. 16 L + 15, holding elements e = 8 p .. 8 p + 7
+// of that lane, so the composition reads them with one conflict-free 16-byte LDS read.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void prep_bc_kernel(const bf16* __restrict__ Bc, bf16* __restrict__ Bp, int64_t n_units) {
+  // one thread per 16-byte unit; consecutive threads take consecutive columns, so each of
+  // the 8 rows a unit gathers is read as one 64-byte run per half wave
+  const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
+  if (t >= n_units) return;
+  constexpr int NRT = DK / 32;
+  const int L = (int)(t & 63), c32 = L & 31, hh = L >> 5;
+  const int64_t u = t >> 6;  // unit over all (b, h, j, ct, rt, p)
+  const int p = (int)(u & 1), rt = (int)((u >> 1) % NRT);
+  const int64_t cu = (u >> 1) / NRT;
+  const int ct = (int)(cu % (DV / 32));
+  const int64_t chunk = cu / (DV / 32);
+  const bf16* src = Bc + chunk * DK * DV + ct * 32 + c32;
+  bf16x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int el = 8 * p + e;
+    out[e] = src[(rt * 32 + (el >> 2) * 8 + hh * 4 + (el & 3)) * DV];
+  }
+  *reinterpret_cast<bf16x8*>(Bp + t * 8) = out;
+}
+
+// Order of the A fragments within one composition step: position q -> fragment index
+// kb * NRT + rt.  Four blocks (R0,K0) (R0,K1) (R1,K0) (R1,K1), R0 / R1 the row tiles
+// [0, NRT/2) and [NRT/2, NRT), K0 / K1 the k-steps [0, NRT) and [NRT, 2 NRT); k-step
+// outer, row tile inner.
+template <int NRT>
+__host__ __device__ constexpr int compose_seq(int q) {
+  constexpr int RH = NRT / 2, HALF = 2 * NRT * RH;
+  const int rbase = q >= HALF ? RH : 0;
+  q %= HALF;
+  return (q / RH) * NRT + rbase + q % RH;
+}
+
 template <int DK, int DV, int NW, int SPW, int PF>
 __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
   constexpr int NCTV = DV / 32;
@@ -128,21 +171,13 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
   for (int s = 0; s < SPW; ++s) qi[s] = i0 + w / NCTV + s * (NW / NCTV);
 
   const bf16* Ag = reinterpret_cast<const bf16*>(a.At_prep) + bh * N * (int64_t)DK * DK;
-  const bf16* Bg = reinterpret_cast<const bf16*>(a.Bc) + bh * N * (int64_t)DK * DV;
+  const bf16* Bg = reinterpret_cast<const bf16*>(a.Bc_prep) + bh * N * (int64_t)DK * DV;
   const float* gts = a.gates + bh * (int64_t)N * N;
   const uint8_t* msk = a.mask + bh * (int64_t)N * N;
   float* Sout = a.S_routed + bh * (int64_t)N * DK * DV;
 
-  // Async copy of (At_j, Bc_j) into LDS, 1 KiB blocks m = w, w + NW, ... per wave.  Bc
-  // block m is UPB = 1024 / (2 DV) whole rows; its lane -> source unit permutation depends
-  // on m only through m mod (units-per-row / UPB), which is fixed per wave because NW is a
-  // multiple of it, so one offset per lane serves every block.
-  constexpr int UB = DV / 8, RPB = 1024 / (2 * DV);  // units per Bc row, rows per block
-  static_assert(NW % (UB / RPB) == 0, "Bc swizzle fixed per wave");
-  const int srcB = [&] {
-    const int r = w * RPB + lane / UB, p = lane % UB;
-    return (lane / UB) * DV * 2 + ((p ^ (r & (UB - 1))) << 4);
-  }();
+  // Async copy of (At_j, Bc_j) into LDS, 1 KiB blocks m = w, w + NW, ... per wave, each a
+  // contiguous block of the prepared images.
   // copy instruction d (0 .. NDW-1) of this wave for history chunk j
   constexpr int NDW = NDA / NW + NDB / NW;
   auto issue_one = [&](int j, int d, bf16* dA, bf16* dB) {
@@ -154,7 +189,7 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
     } else {
       const int m = w + (d - NDA / NW) * NW;
       const char* bs = reinterpret_cast<const char*>(Bg + (int64_t)j * DK * DV);
-      __builtin_amdgcn_global_load_lds(bs + m * 1024 + srcB,
+      __builtin_amdgcn_global_load_lds(bs + m * 1024 + lane * 16,
                                        (lds_void_t*)(reinterpret_cast<char*>(dB) + m * 1024), 16, 0, 0);
     }
   };
@@ -163,18 +198,16 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
     for (int d = 0; d < NDW; ++d) issue_one(j, d, dA, dB);
   };
   auto wait_copies = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-  // fragment reads: row rt*32 + c32, logical half hh of k block kb (At); Bc columns
-  // 32 ct + 16 kd + 8 hh .. (unit 4 ct + 2 kd + hh of the row)
+  // fragment reads: row rt*32 + c32, logical half hh of k block kb (At); the lane's own
+  // unit of Bc image block (ct, rt, p)
   const int rd = c32 * 32 + ((hh ^ (((c32 >> 2) ^ (c32 >> 3)) & 1)) << 4);
-  const int rdB0 = c32 * DV * 2 + (((4 * ct + hh) ^ (c32 & (UB - 1))) << 4);
-  const int rdB1 = c32 * DV * 2 + (((4 * ct + 2 + hh) ^ (c32 & (UB - 1))) << 4);
-  constexpr int NFA = NKS * NRT, NF = NFA + 2 * NRT;
-  auto frag = [&](const bf16* cA, const bf16* cB, int f) -> bf16x8 {
-    if (f < NFA)
-      return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(cA) + rd + (f / NRT) * BLK + (f % NRT) * 1024);
-    const int fb = f - NFA;
-    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(cB) + (fb / NRT ? rdB1 : rdB0) +
-                                            (fb % NRT) * 32 * DV * 2);
+  constexpr int NFA = NKS * NRT;
+  auto frag = [&](const bf16* cA, int f) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(cA) + rd + (f / NRT) * BLK + (f % NRT) * 1024);
+  };
+  auto bc_unit = [&](const bf16* cB, int rt, int p) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(cB) + ((ct * NRT + rt) * 2 + p) * 1024 +
+                                            lane * 16);
   };
 
   f32x16 M[SPW][NRT];
@@ -223,78 +256,116 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
     }
   };
 
-  // diagonal B fragments for g Bc: slot k (plain order) of k-step kd equals the lane's
-  // column in exactly one lane-half; the pattern keeps g's bf16 bits there
-  uint32_t pat[2][4];
+  // One history chunk: multiply with the (At_j - I, Bc_j) in (cA, cB) while the copy of
+  // chunk j + 1 lands in (nA, nB).  The products of a step run in four blocks
+  //   (R0,K0) (R0,K1) (R1,K0) (R1,K1)
+  // (R0 / R1 the upper and lower row tiles of the state slice, K0 / K1 the matching halves
+  // of the k range), and the vector work of the step is spread over them so that it runs
+  // while the matrix cores work on other accumulators:
+  //   (R0,K0): the K1 half of this step's B operand (scale by the gate, round to bf16),
+  //            from rows R1, which the previous step finished and this step has not
+  //            touched yet;
+  //   (R0,K1): g Bc_j added to rows R1, which no product of this step has touched yet;
+  //   (R1,K0): g Bc_j added to rows R0, whose products for this step are issued;
+  //   (R1,K1): the K0 half of the next step's B operand, from rows R0 (now final), into
+  //            registers whose last reader was (R1,K0).
+  constexpr int RH = NRT / 2, KH = NKS / 2, BLK_Q = KH * RH;
+  bf16x8 bfr[SPW][NKS];
+  auto convert = [&](int s, int ks, float gs) { bfr[s][ks] = Mma<bf16>::from_acc(M[s][ks >> 1], ks, gs); };
+  float gnext[SPW];
+  auto read_gates = [&](int j, float* out) {
 #pragma unroll
-  for (int kd = 0; kd < 2; ++kd)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t m = 0;
-      const int k0 = kd * 16 + hh * 8 + 2 * d;
-      if (k0 == c32) m |= 0x0000ffffu;
-      if (k0 + 1 == c32) m |= 0xffff0000u;
-      pat[kd][d] = m;
-    }
+    for (int s = 0; s < SPW; ++s) out[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(greg[s]), j & 63));
+  };
 
-  // one history chunk: multiply with the (At_j - I, Bc_j) in (cA, cB) while the copy of
-  // chunk j + 1 lands in (nA, nB)
   auto step = [&](int j, const bf16* cA, const bf16* cB, bf16* nA, bf16* nB) {
-    if ((j & 63) == 0) load_gates(j >> 6);
-    // read the gates before issuing the next copies, so waiting for the gate loads never
-    // waits for the copies
     float g[SPW];
     bool any = false;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
-      g[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(greg[s]), j & 63));
+      g[s] = gnext[s];
       any |= (g[s] != 0.f);
     }
+    // gates of the next step (a new block of 64 is loaded when it starts)
+    if (((j + 1) & 63) == 0) load_gates((j + 1) >> 6);
+    read_gates(j + 1, gnext);
     const bool more = j + 1 < nsteps;
     if (any) {
-      // the first PF fragment reads are in flight while the B operands are converted
+      // (g, 0) and (0, g) as bf16 pairs: the dot product of a Bc pair with one of them is
+      // g times its first or its second element
+      bf16x2 gp[SPW][2];
+#pragma unroll
+      for (int s = 0; s < SPW; ++s) {
+        const bf16 gb = (bf16)g[s], z = (bf16)0.f;
+        gp[s][0] = bf16x2{gb, z};
+        gp[s][1] = bf16x2{z, gb};
+      }
       bf16x8 ring[PF];
 #pragma unroll
-      for (int p = 0; p < PF; ++p) ring[p] = frag(cA, cB, p);
-      // B operand bf16(g M) straight from the accumulator rows this lane holds
-      bf16x8 bfr[SPW][NKS];
+      for (int p = 0; p < PF; ++p) ring[p] = frag(cA, compose_seq<NRT>(p));
+      bf16x8 bcv[RH][2];  // Bc units of the half being added
+      constexpr int NC = SPW * KH;          // conversions per half
+      constexpr int NB = SPW * RH * 16;     // Bc elements per half
+      static_for<0, NFA>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        constexpr int f = compose_seq<NRT>(q);
+        constexpr int blk = q / BLK_Q, qb = q % BLK_Q;
+        static_for<0, NDW>([&](auto dc) {
+          constexpr int d = decltype(dc)::value;
+          if constexpr (q == d * NFA / NDW) issue_one(j + 1, d, nA, nB);
+        });
+        // Bc units: rows R1 at the start of (R0,K0); unit r of rows R0 at the first position
+        // of (R0,K1) after its R1 unit was last used there, or at the start of (R1,K0)
+        if constexpr (q == 0) {
+#pragma unroll
+          for (int r = 0; r < RH; ++r)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) bcv[r][p] = bc_unit(cB, RH + r, p);
+        }
+        static_for<0, RH>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          constexpr int last = ((r + 1) * SPW * 16 - 1) * BLK_Q / NB;  // last position using unit r
+          if constexpr (q == BLK_Q + last + 1) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) bcv[r][p] = bc_unit(cB, r, p);
+          }
+        });
+        const bf16x8 af = ring[q % PF];
+        if constexpr (q + PF < NFA) ring[q % PF] = frag(cA, compose_seq<NRT>(q + PF));
+        if constexpr (blk == 0 || blk == 3) {
+          static_for<0, NC>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            if constexpr (c * BLK_Q / NC == qb) {
+              if constexpr (blk == 0)
+                convert(c % SPW, KH + c / SPW, g[c % SPW]);
+              else
+                convert(c % SPW, c / SPW, gnext[c % SPW]);
+            }
+          });
+        } else {
+          // g Bc_j into rows R1 (block 1) or R0 (block 2): element x of the half is slice
+          // x % SPW, row tile x / SPW / 16, accumulator element x / SPW % 16
+          constexpr int r0 = blk == 1 ? RH : 0;
+          static_for<0, NB>([&](auto xc) {
+            constexpr int x = decltype(xc)::value;
+            if constexpr (x * BLK_Q / NB == qb) {
+              constexpr int s = x % SPW, e = (x / SPW) % 16, r = x / SPW / 16;
+              const bf16x8 u = bcv[r][e >> 3];
+              const bf16x2 pr = __builtin_shufflevector(u, u, (e & 7) & ~1, ((e & 7) & ~1) + 1);
+              M[s][r0 + r][e] = __builtin_amdgcn_fdot2_f32_bf16(pr, gp[s][e & 1], M[s][r0 + r][e], false);
+            }
+          });
+        }
+        constexpr int rt = f % NRT;
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) M[s][rt] = Mma<bf16>::mma(af, bfr[s][f / NRT], M[s][rt]);
+      });
+    } else {
+      if (more) issue(j + 1, nA, nB);
 #pragma unroll
       for (int s = 0; s < SPW; ++s)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) bfr[s][ks] = Mma<bf16>::from_acc(M[s][ks >> 1], ks, g[s]);
-      bf16x8 dg[SPW];
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        // the copies of chunk j + 1 are spread over the products, so the address unit
-        // drains them in the background instead of stalling every wave at once (after
-        // the last step this copies chunk nsteps <= N - 1 into the idle buffer: in
-        // bounds, never read, and waited for before the kernel ends)
-#pragma unroll
-        for (int d = 0; d < NDW; ++d)
-          if (f == d * NFA / NDW) {
-            issue_one(j + 1, d, nA, nB);
-          }
-        const bf16x8 af = ring[f % PF];
-        if (f + PF < NF) ring[f % PF] = frag(cA, cB, f + PF);
-        const int rt = (f < NFA ? f : f - NFA) % NRT;
-        if (f >= NFA && (f - NFA) % NRT == 0) {
-          const int kd = (f - NFA) / NRT;
-#pragma unroll
-          for (int s = 0; s < SPW; ++s) {
-            const uint32_t gb = (uint32_t)__builtin_bit_cast(unsigned short, (bf16)g[s]);
-            const uint32_t g2 = gb | (gb << 16);
-            uint32_t d4[4];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) d4[d] = pat[kd][d] & g2;
-            dg[s] = __builtin_bit_cast(bf16x8, d4);
-          }
-        }
-#pragma unroll
-        for (int s = 0; s < SPW; ++s)
-          M[s][rt] = Mma<bf16>::mma(af, f < NFA ? bfr[s][f / NRT] : dg[s], M[s][rt]);
-      }
-    } else if (more) {
-      issue(j + 1, nA, nB);
+        for (int ks = 0; ks < KH; ++ks) convert(s, ks, gnext[s]);
     }
 #pragma unroll
     for (int s = 0; s < SPW; ++s)
@@ -307,6 +378,12 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
 
   if (nsteps > 0) {
     issue(0, sA0, sB0);
+    load_gates(0);
+    read_gates(0, gnext);
+#pragma unroll
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+      for (int ks = 0; ks < KH; ++ks) convert(s, ks, gnext[s]);
     wait_copies();
     __syncthreads();
   }
@@ -339,6 +416,20 @@ hipError_t launch_compose_bf16(const RouteArgs& a, int dk, int dv, hipStream_t s
                          reinterpret_cast<bf16*>(a.At_prep), n_pairs);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int64_t n_units = a.B * a.H * (int64_t)a.N * dk * dv / 8;
+    const unsigned nu = (unsigned)((n_units + 255) / 256);
+    const bf16* bc = reinterpret_cast<const bf16*>(a.Bc);
+    bf16* bp = reinterpret_cast<bf16*>(a.Bc_prep);
+    if (dk == 64 && dv == 64)
+      hipLaunchKernelGGL((prep_bc_kernel<64, 64>), dim3(nu), dim3(256), 0, s, bc, bp, n_units);
+    else if (dk == 64 && dv == 128)
+      hipLaunchKernelGGL((prep_bc_kernel<64, 128>), dim3(nu), dim3(256), 0, s, bc, bp, n_units);
+    else if (dk == 128 && dv == 64)
+      hipLaunchKernelGGL((prep_bc_kernel<128, 64>), dim3(nu), dim3(256), 0, s, bc, bp, n_units);
+    else
+      hipLaunchKernelGGL((prep_bc_kernel<128, 128>), dim3(nu), dim3(256), 0, s, bc, bp, n_units);
+    const hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
   }
   // 8 waves of 2 state slices each, a 4-deep ring of fragment reads
   if (dk == 64 && dv == 64) return launch_compose_bf16_t<64, 64, 8, 2, 4>(a, s);

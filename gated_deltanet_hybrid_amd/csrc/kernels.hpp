@@ -112,6 +112,7 @@ struct RouteArgs {
   int32_t C;            // tokens per chunk
   float* qbar;          // workspace [B,H,N,dk] float32
   void* At_prep;        // workspace [B,H,N,dk,dk] bf16: (At - I) reordered for the composition
+  void* Bc_prep;        // workspace [B,H,N,dk,dv] bf16: Bc in the composition's accumulator order
   int64_t B, T, H, ld_T;
   int32_t N;
 };

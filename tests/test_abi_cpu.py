@@ -58,8 +58,10 @@ def test_workspace_sizes(lib):
     d32 = dims(B=2, T=130, H=3, dk=128, dv=64, dtype=0)
     assert hla.workspace_bytes(hla.FN_WU_HANDOFF, d32) == 0
     assert hla.workspace_bytes(hla.FN_GDN_PREFILL, d32) == 2 * ab + st
-    # float32 query-chunk means, then the reordered bf16 copy of At - I
-    assert hla.workspace_bytes(hla.FN_ROUTE_MIX, d) == 2 * 3 * 3 * 128 * 4 + BHN * 128 * 128 * 2
+    # float32 query-chunk means, then the reordered bf16 copies of At - I and of Bc
+    assert hla.workspace_bytes(hla.FN_ROUTE_MIX, d) == 2 * 3 * 3 * 128 * 4 + BHN * 128 * 128 * 2 + BHN * 128 * 64 * 2
+    # float32: the means only
+    assert hla.workspace_bytes(hla.FN_ROUTE_MIX, d32) == 2 * 3 * 3 * 128 * 4
     out = ctypes.c_size_t()
     assert lib.hla_workspace_bytes(99, ctypes.byref(d), 0, ctypes.byref(out)) == UNSUPPORTED
     assert lib.hla_workspace_bytes(0, ctypes.byref(d), 0, None) == NULL_ARG
@@ -75,7 +77,7 @@ def test_workspace_sizes_larger_chunks(lib):
     # the prefill runs on pieces whatever C is
     assert hla.workspace_bytes(hla.FN_GDN_PREFILL, d) == ab + pieces * 64 * 256 * 2 + pieces * 128 * 128 * 4
     assert hla.workspace_bytes(hla.FN_WU_HANDOFF, d) == pieces * 64 * 256 * 2
-    assert hla.workspace_bytes(hla.FN_ROUTE_MIX, d) == 2 * 3 * 128 * 4 + 2 * 3 * 128 * 128 * 2
+    assert hla.workspace_bytes(hla.FN_ROUTE_MIX, d) == 2 * 3 * 128 * 4 + 2 * 2 * 3 * 128 * 128 * 2
 
 
 @pytest.mark.parametrize("kw,code", [
