@@ -307,11 +307,10 @@ hla_status_t prefill_body(const hla_dims_t* d, hla::ChunkArgs a, const float* S0
     b.chunk_init_t = s.states_t;
     return hip_status(chunk_pass(b, d, false, true, stream));
   }
-  if (d->dtype == HLA_BF16 && a.variant == 0 && o) {
-    // bf16 Gated DeltaNet with outputs: the per-piece UT records, then one state pass per
-    // (b, h, 32 columns) that carries the state through the pieces and writes the outputs
-    // on the way (wu is not read).  A state-only call (Tail-Replay) takes the chunk maps and
-    // their scan below, which measured faster when no outputs are formed.
+  if (d->dtype == HLA_BF16 && a.variant == 0) {
+    // bf16 Gated DeltaNet: the per-piece UT records, then one state pass per (b, h) that
+    // carries the state through the pieces and writes the outputs on the way (wu is not
+    // read).
     if (!ws || (int64_t)ws_bytes < native_ws(d)) return HLA_ERR_WORKSPACE;
     hla::UtArgs f{};
     f.q = o ? a.q : nullptr; f.k = a.k; f.v = a.v; f.beta = a.beta; f.alpha = a.alpha;

@@ -81,14 +81,28 @@ struct UtArgs {
   int64_t B, T, H, ld_T;
   int32_t N;            // 64-token pieces
 };
-// One piece's record in the native prefill's workspace, at these byte offsets: -W [64][dk]
-// bf16; U^T in the state pass's lane order [dv/32][2][64][16] bf16; the log decays g [64]
-// float32; P = (Q K^T) o Gamma [64][64] bf16 (lower with the diagonal; written when outputs
-// are wanted).
-constexpr int64_t ut_off_u(int dk) { return (int64_t)128 * dk; }
-constexpr int64_t ut_off_g(int dk, int dv) { return (int64_t)128 * (dk + dv); }
-constexpr int64_t ut_off_p(int dk, int dv) { return ut_off_g(dk, dv) + 256; }
-constexpr int64_t ut_record_bytes(int dk, int dv) { return ut_off_p(dk, dv) + 64 * 64 * 2; }
+// One piece's record in the native prefill's workspace.  Every matrix operand of the state
+// pass is stored as MFMA fragments (32 x 32 x 16 bf16): a fragment is 1 KiB, lane L's 16
+// bytes at 16 L, lane L = 32 h + m holding row m and the 8 k values
+// 16 ks + {4 h .. 4 h + 3, 8 + 4 h .. 8 + 4 h + 3} of its k-step ks -- the k order in which
+// a 32 x 32 accumulator tile (row r of element e = 8 (r / 8) ... ) turns into a B operand
+// in place.  Byte offsets:
+//   -W  fragments [tt 2][ks dk/16], rows t = 32 tt + m, k = key channel;
+//   K^T fragments [rt dk/32][ks 4], rows dk = 32 rt + m, k = token;
+//   U   in the accumulator order of the state pass's E tiles [dv/32][tt 2][64][16] bf16;
+//   gamma_t = exp(g_t) [64] then D_t = exp(g_63 - g_t) [64], float32 (1 KiB reserved);
+//   Q   fragments [tt 2][ks dk/16] (outputs only);
+//   P = (Q K^T) o Gamma fragments [tt 2][ks 4], rows t, k = token s (outputs only).
+constexpr int64_t ut_off_kt(int dk) { return (int64_t)2 * (dk / 16) * 1024; }
+constexpr int64_t ut_off_u(int dk) { return ut_off_kt(dk) + (int64_t)(dk / 32) * 4 * 1024; }
+constexpr int64_t ut_off_gd(int dk, int dv) { return ut_off_u(dk) + (int64_t)(dv / 32) * 4 * 1024; }
+constexpr int64_t ut_off_q(int dk, int dv) { return ut_off_gd(dk, dv) + 1024; }
+constexpr int64_t ut_off_p(int dk, int dv) { return ut_off_q(dk, dv) + (int64_t)2 * (dk / 16) * 1024; }
+// The record is padded to a whole number of 1 KiB blocks per state-pass wave (dv / 32), so
+// that every wave copies the same number of blocks of it.
+constexpr int64_t ut_record_bytes(int dk, int dv) {
+  return (ut_off_p(dk, dv) + 8 * 1024 + (dv / 32) * 1024 - 1) / ((dv / 32) * 1024) * ((dv / 32) * 1024);
+}
 // Native bf16 prefill: the per-piece UT pass, then the state pass that carries the state
 // through the pieces (prefill.hip).
 hipError_t launch_prefill_native(const UtArgs& a, int dk, int dv, hipStream_t s);

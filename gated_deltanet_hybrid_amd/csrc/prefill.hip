@@ -12,21 +12,21 @@
 // Every decay is the exp (or exp2) of a difference of log-decays, never exp(-g).
 //
 // Pass 1, ut_kernel (one workgroup per (b, h, piece), all pieces at once): everything that
-// does not depend on the state -- g, the blocked inverse X, W and U -- into a per-piece
-// record: -W row-major [t][dk] bf16, U^T in the accumulator lane order of the second pass's
-// E^T tiles (bf16), g (float32) and, when outputs are wanted, P = (Q K^T) o Gamma (bf16).  The inverse is a chain of dependent LDS phases, so it
-// runs here, many pieces per CU at once, instead of on the sequential path.
+// does not depend on the state -- the decays, the blocked inverse X, W and U, P -- into a
+// per-piece record whose matrices are stored as the second pass's MFMA fragments.  The
+// inverse is a chain of dependent LDS phases, so it runs here, many pieces per CU at once,
+// instead of on the sequential path.
 //
-// Pass 2, state_kernel (one workgroup per (b, h, 32 state columns)): the state runs through
-// the pieces in order.  Per piece, in the transposed forms whose operands sit in rows of
-// contiguous k:
-//   E^T = U^T - M^T W^T          (U^T seeds the accumulator, -W rows are the B operand)
-//   O   = gamma (Q M) + P E      (P = (Q K^T) o Gamma from the record)
-//   M^T <- gamma_63 M^T + (E^T D) K
-// with the state kept in MFMA accumulators (one 32 x 32 tile of M^T per wave) and exchanged
-// as a bf16 image MT [col][dk] in LDS.  Three barriers per piece; the next piece's operands
-// are loaded into registers while the current one computes, and each output tile is stored
-// at the start of the next piece.
+// Pass 2, state_kernel (one workgroup per (b, h), one wave per 32 state columns): the state
+// runs through the pieces in order, its 32 columns held by one wave in MFMA accumulators
+// (M [dk x 32], four 32 x 32 tiles) for the whole pass.  Per piece:
+//   E = U + (-W) M            (U seeds the accumulators, M's bf16 copy is the B operand)
+//   O = gamma (Q M) + P E     (E's bf16 copy is the B operand)
+//   M <- gamma_63 M + K^T (D E)
+// Every B operand is an accumulator tile rounded to bf16 in place, because the A operands
+// (-W, Q, K^T, P) were stored with their k values in the accumulator's row order; so a
+// wave never exchanges state with another, and the only barrier per piece guards the
+// double-buffered LDS copy of the records (global_load_lds, issued one piece ahead).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
@@ -121,7 +121,10 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
       s_beta[tid] = bt;
       s_g2[tid] = x * kLog2e;
       s_bg[tid] = bt * expf(x);
-      reinterpret_cast<float*>(rec + ut_off_g(DK, DV))[tid] = x;
+      const float x_end = __shfl(x, 63, 64);
+      float* gd = reinterpret_cast<float*>(rec + ut_off_gd(DK, DV));
+      gd[tid] = expf(x);
+      gd[C + tid] = expf(x_end - x);
     }
   }
   // K K^T lower tiles (0,0), (1,0), (1,1) on waves 0-2 and, when outputs are wanted, the
@@ -142,30 +145,52 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
       fb[ks] = *reinterpret_cast<const bf16x8*>(pb + ks * 16);
     }
   }
+  // the Q fragments of the record (outputs only): fragment min(w + 8 j, NQ - 1) of each
+  // wave, loaded here with the other operands and stored in phase C (rows past the end of
+  // a partial piece read its last row: never used)
+  constexpr int NQ = 2 * (DK / 16), NQW = (NQ + 7) / 8;
+  bf16x8 qf[NQW];
+  if (want_p) {
+#pragma unroll
+    for (int j = 0; j < NQW; ++j) {
+      const int fq = min(w + 8 * j, NQ - 1), tt = fq / (DK / 16), ks = fq % (DK / 16);
+      const int t = tt * 32 + c32;
+      qf[j] = Mma<bf16>::load_clayout(reinterpret_cast<const bf16*>(a.q) + (row0 + (t < n ? t : n - 1) * a.H) * DK, ks, hh);
+    }
+  }
   __syncthreads();
 
   // ---- B. L = strictly_lower(diag(beta) (K K^T) o Gamma); P = (Q K^T) o Gamma into the
-  // record (wave 6 writes its zero upper tile); X = 0
+  // record as fragments (wave 6 writes the zero upper tile's two); X = 0
   if (want_p && w >= 3 && w < 6) {
+    // tile (t block tm, s block tn) of P computed as K Q^T: the accumulator holds, for the
+    // lane's token t, the tokens s in the k order of P's fragments
     f32x16 acc = zero16();
 #pragma unroll
-    for (int ks = 0; ks < DK / 16; ++ks) acc = Mma<bf16>::mma(fa[ks], fb[ks], acc);
-    const int s = tn * 32 + c32;
-    const float gs = s_g2[s];
-    float gt[16];
+    for (int ks = 0; ks < DK / 16; ++ks) acc = Mma<bf16>::mma(fb[ks], fa[ks], acc);
+    const float gt = s_g2[tm * 32 + c32];
+    const int t = tm * 32 + c32;
+    float gsv[16];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<float4*>(gt + 4 * r) = *reinterpret_cast<const float4*>(s_g2 + tm * 32 + r * 8 + hh * 4);
-    bf16* po = reinterpret_cast<bf16*>(rec + ut_off_p(DK, DV)) + (tm * 32 + hh * 4) * C + s;
+      *reinterpret_cast<float4*>(gsv + 4 * r) = *reinterpret_cast<const float4*>(s_g2 + tn * 32 + r * 8 + hh * 4);
+    bf16x8 lo, hi;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int t = tm * 32 + acc_row(e, hh);
-      po[((e >> 2) * 8 + (e & 3)) * C] = (bf16)((s <= t) ? __builtin_amdgcn_exp2f(gt[e] - gs) * acc[e] : 0.f);
+      const int sx = tn * 32 + acc_row(e, hh);
+      const bf16 v = (bf16)((sx <= t) ? __builtin_amdgcn_exp2f(gt - gsv[e]) * acc[e] : 0.f);
+      if (e < 8) lo[e] = v; else hi[e - 8] = v;
     }
+    bf16x8* po = reinterpret_cast<bf16x8*>(rec + ut_off_p(DK, DV));
+    po[(tm * 4 + 2 * tn) * 64 + lane] = lo;
+    po[(tm * 4 + 2 * tn + 1) * 64 + lane] = hi;
   } else if (want_p && w == 6) {
-    bf16* po = reinterpret_cast<bf16*>(rec + ut_off_p(DK, DV)) + (hh * 4) * C + 32 + c32;
+    bf16x8 z;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) po[((e >> 2) * 8 + (e & 3)) * C] = (bf16)0.f;
+    for (int e = 0; e < 8; ++e) z[e] = (bf16)0.f;
+    bf16x8* po = reinterpret_cast<bf16x8*>(rec + ut_off_p(DK, DV));
+    po[2 * 64 + lane] = z;
+    po[3 * 64 + lane] = z;
   }
   if (w < 3) {
     // a padded row's product is zeroed below: its beta is 0 (row t) or the row is past the
@@ -190,7 +215,22 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
   for (int i = tid; i < C * PX; i += NT) Xb[i] = 0.f;
   __syncthreads();
 
-  // ---- C. X = (I + L)^-1, blocked by 16: the diagonal blocks by substitution
+  // ---- C. X = (I + L)^-1, blocked by 16: the diagonal blocks by substitution (wave 0);
+  // meanwhile waves 1-7 store the K^T fragments (from K^T in LDS; padded tokens are zero);
+  // every wave stores its Q fragments
+  if (want_p) {
+#pragma unroll
+    for (int j = 0; j < NQW; ++j)
+      reinterpret_cast<bf16x8*>(rec + ut_off_q(DK, DV))[min(w + 8 * j, NQ - 1) * 64 + lane] = qf[j];
+  }
+  if (w > 0) {
+    constexpr int NKT = (DK / 32) * 4;
+    for (int f = w - 1; f < NKT; f += 7) {
+      const int rt = f >> 2, ks = f & 3;
+      reinterpret_cast<bf16x8*>(rec + ut_off_kt(DK))[f * 64 + lane] =
+          Mma<bf16>::load_clayout(KT + (rt * 32 + c32) * PT, ks, hh);
+    }
+  }
   if (tid < 64) {
     const int bi = tid >> 4, cc = tid & 15, base = bi * 16;
     float x[16];
@@ -230,8 +270,9 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
     __syncthreads();
   }
 
-  // ---- F. W tile (tt, db) on wave 2 db + tt -> -W [t][dk];  U^T tile (ct, tt) on wave
-  // 2 ct + tt -> lane order.  X enters as hi + lo bf16 parts (about 16 mantissa bits).
+  // ---- F. W^T tile (dk block db, token block tt) on wave 2 db + tt -> -W fragments (tt,
+  // 2 db) and (tt, 2 db + 1);  U tile (token block tt, column block ct) on wave 2 ct + tt
+  // -> the E accumulator order.  X enters as hi + lo bf16 parts (about 16 mantissa bits).
   auto xfrag = [&](const float* xrow, const float* fac, int ks, bf16x8& hi, bf16x8& lo) {
     const int s0 = ks * 16 + hh * 8;
     float xv[8], fv[8];
@@ -248,32 +289,15 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
     }
   };
   if (w < 2 * NDT) {
+    // W^T = K^T diag(beta gamma) X^T: A = K^T rows (dk), B = X rows (token t), k = s
     const int tt = w & 1, db = w >> 1;
     const float* xrow = Xb + (tt * 32 + c32) * PX;
-    const bf16* brow = KT + (db * 32 + c32) * PT;
+    const bf16* arow = KT + (db * 32 + c32) * PT;
     f32x16 acc = zero16();
 #pragma unroll
     for (int ks = 0; ks < C / 16; ++ks) {
       bf16x8 hi, lo;
       xfrag(xrow, s_bg, ks, hi, lo);
-      const bf16x8 bf = Mma<bf16>::load_plain(brow, ks, hh);
-      acc = Mma<bf16>::mma(hi, bf, acc);
-      acc = Mma<bf16>::mma(lo, bf, acc);
-    }
-    // element (token tt 32 + acc_row(e), key channel db 32 + c32)
-    bf16* wo = reinterpret_cast<bf16*>(rec) + (tt * 32 + hh * 4) * DK + db * 32 + c32;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) wo[((e >> 2) * 8 + (e & 3)) * DK] = (bf16)(-acc[e]);
-  }
-  if (w < 2 * NVT) {
-    const int tt = w & 1, ct = w >> 1;
-    const bf16* arow = VT + (ct * 32 + c32) * PT;
-    const float* xrow = Xb + (tt * 32 + c32) * PX;
-    f32x16 acc = zero16();
-#pragma unroll
-    for (int ks = 0; ks < C / 16; ++ks) {
-      bf16x8 hi, lo;
-      xfrag(xrow, s_beta, ks, hi, lo);
       const bf16x8 af = Mma<bf16>::load_plain(arow, ks, hh);
       acc = Mma<bf16>::mma(af, hi, acc);
       acc = Mma<bf16>::mma(af, lo, acc);
@@ -281,248 +305,385 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
     bf16x8 lo8, hi8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+      lo8[e] = (bf16)(-acc[e]);
+      hi8[e] = (bf16)(-acc[e + 8]);
+    }
+    bf16x8* wo = reinterpret_cast<bf16x8*>(rec);
+    wo[(tt * (DK / 16) + 2 * db) * 64 + lane] = lo8;
+    wo[(tt * (DK / 16) + 2 * db + 1) * 64 + lane] = hi8;
+  }
+  if (w < 2 * NVT) {
+    // U = X diag(beta) V: A = X rows (token t), B = V^T rows (column), k = s
+    const int tt = w & 1, ct = w >> 1;
+    const bf16* brow = VT + (ct * 32 + c32) * PT;
+    const float* xrow = Xb + (tt * 32 + c32) * PX;
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int ks = 0; ks < C / 16; ++ks) {
+      bf16x8 hi, lo;
+      xfrag(xrow, s_beta, ks, hi, lo);
+      const bf16x8 bf = Mma<bf16>::load_plain(brow, ks, hh);
+      acc = Mma<bf16>::mma(hi, bf, acc);
+      acc = Mma<bf16>::mma(lo, bf, acc);
+    }
+    bf16x8 lo8, hi8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
       lo8[e] = (bf16)acc[e];
       hi8[e] = (bf16)acc[e + 8];
     }
-    bf16* uo = reinterpret_cast<bf16*>(rec + ut_off_u(DK)) + ((ct * 2 + tt) * 64 + lane) * 16;
-    *reinterpret_cast<bf16x8*>(uo) = lo8;
-    *reinterpret_cast<bf16x8*>(uo + 8) = hi8;
+    bf16x8* uo = reinterpret_cast<bf16x8*>(rec + ut_off_u(DK)) + ((ct * 2 + tt) * 64 + lane) * 2;
+    uo[0] = lo8;
+    uo[1] = hi8;
   }
 }
 
-template <int DK, int DV, bool WANT_O>
-__global__ __launch_bounds__(512, WANT_O ? 2 : 4) void state_kernel(UtArgs a) {
-  constexpr int C = kChunk;
-  constexpr int NT = 512;
-  constexpr int PK = DK + 8;   // bf16 pitch of [t][dk] and [col][dk] rows
-  constexpr int PT = C + 8;    // bf16 pitch of [d][t] rows
-  constexpr int NDT = DK / 32;
-  constexpr int NCB = DV / 32;
-  constexpr int KU = DK / 8;           // 16-byte units per key row
-  constexpr int KPT = C * KU / NT;     // units of K, Q and -W each thread moves per piece
-  constexpr int NKS = DK / 16;
-  static_assert(KPT >= 1 && C * KU % NT == 0, "units per thread");
 
-  __shared__ __attribute__((aligned(16))) bf16 KT[DK * PT];
-  __shared__ __attribute__((aligned(16))) bf16 Wn[C * PK];
-  __shared__ __attribute__((aligned(16))) bf16 Qp[WANT_O ? C * PK : 8];
-  __shared__ __attribute__((aligned(16))) bf16 MT[2][32 * PK];
-  __shared__ __attribute__((aligned(16))) bf16 ET[32 * PT];
-  __shared__ __attribute__((aligned(16))) bf16 DET[32 * PT];
-  __shared__ __attribute__((aligned(16))) float s_gam[C], s_d[C];
+template <int DK, int DV, int NWB, bool WANT_O>
+__global__ __launch_bounds__(256, 1) void state_kernel(UtArgs a) {
+  constexpr int C = kChunk;
+  constexpr int NCB = DV / 32;        // 32-column slices of the state
+  constexpr int NG = NCB / NWB;       // workgroups per (b, h): NWB slices (waves) each
+  // Four waves per workgroup: the NWB that compute and, when NWB < 4, NH helpers that only
+  // move records into LDS (plain 16-byte loads into registers, then LDS writes: the
+  // asynchronous global -> LDS copy moves fewer bytes per clock and CU than the products
+  // of a piece need).  Without helpers the compute waves copy with global_load_lds.
+  constexpr int NTW = 4, NH = NTW - NWB;
+  constexpr int NRT = DK / 32, NKS = DK / 16;
+  // The part of a piece's record this workgroup stages in LDS, as 1 KiB blocks: -W and K^T
+  // fragments, the U of its own slices, the decays, and (outputs) the Q and P fragments.
+  constexpr int B_WK = (int)(ut_off_u(DK) / 1024), B_U = 4 * NWB, B_GD = 1;
+  constexpr int B_QP = WANT_O ? (int)((ut_record_bytes(DK, DV) - ut_off_q(DK, DV)) / 1024) : 0;
+  constexpr int B_QP_REAL = WANT_O ? 2 * NKS + 8 : 0;
+  constexpr int NB_REAL = B_WK + B_U + B_GD + B_QP_REAL;
+  constexpr int ND = (NB_REAL + NTW - 1) / NTW;  // copy instructions per wave and piece
+  constexpr int NB = ND * NTW;                   // blocks per buffer (the extra ones repeat the decays)
+  constexpr int RB = NB * 1024;
+  static_assert(B_QP >= B_QP_REAL, "record layout");
+  // LDS offsets within a buffer
+  constexpr int L_KT = (int)ut_off_kt(DK), L_U = B_WK * 1024, L_GD = L_U + B_U * 1024, L_Q = L_GD + 1024,
+                L_P = L_Q + 2 * NKS * 1024;
+  // LDS buffers for the records of consecutive pieces: three when they fit and no outputs
+  // are stored (the copy of a piece is issued NBUF - 1 pieces ahead), else two; separate
+  // variables, so the copy into one is not taken to alias reads of another
+  constexpr int NBUF = (NH == 0 && !WANT_O && 3 * RB <= 160 * 1024) ? 3 : 2;
+  static_assert(NBUF * RB <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) char buf0[RB];
+  __shared__ __attribute__((aligned(16))) char buf1[RB];
+  __shared__ __attribute__((aligned(16))) char buf2[NBUF == 3 ? RB : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, c32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  // workgroup -> (b, h, 32-column block); with B H a multiple of 8 the blocks of one (b, h)
-  // share an XCD (workgroups go to the 8 XCDs round robin) and meet its inputs in its L2
+  // workgroup -> (b, h, slice group); with B H a multiple of 8 the groups of one (b, h) go to
+  // the same XCD (workgroups go to the 8 XCDs round robin) and share its records in its L2
   const int64_t id = blockIdx.x;
   int64_t bh;
-  int cb;
+  int sg;
   if ((a.B * a.H) % 8 == 0) {
     const int64_t j = id >> 3;
-    cb = (int)(j % NCB);
-    bh = (j / NCB) * 8 + (id & 7);
+    sg = (int)(j % NG);
+    bh = (j / NG) * 8 + (id & 7);
   } else {
-    cb = (int)(id % NCB);
-    bh = id / NCB;
+    sg = (int)(id % NG);
+    bh = id / NG;
   }
   const int64_t h = bh % a.H, b = bh / a.H;
+  const int cb = sg * NWB + (w < NWB ? w : 0);  // this wave's slice (helpers: unused)
   const int col0 = cb * 32;
   const int N = a.N;
-  const bf16* kg = reinterpret_cast<const bf16*>(a.k);
-  const bf16* qg = reinterpret_cast<const bf16*>(a.q);
-  const int64_t RB = ut_record_bytes(DK, DV);
-  const char* recs = static_cast<const char*>(a.rec) + bh * (int64_t)N * RB;
+  const int64_t RS = ut_record_bytes(DK, DV);
+  const char* recs = static_cast<const char*>(a.rec) + bh * (int64_t)N * RS;
 
-  // ---- roles: E^T tile tt on waves 0, 1; output tile tt on waves 2, 3; M^T tile db (the
-  // block's 32 columns x dk 32 db ..) on wave 4 + db
-  const bool has_e = w < 2;
-  const bool has_o = WANT_O && (w == 2 || w == 3);
-  const bool has_m = w >= 4 && w < 4 + NDT;
-  const int e_tt = w & 1, o_tt = w & 1;
-  const int m_db = w - 4;
+  // The copy of a record into LDS, ND instructions per wave, written out rather than through
+  // the builtin: the compiler would otherwise place a wait for every copy in flight before
+  // the first LDS read of each piece (it cannot tell the buffers apart), which serialises
+  // the copy of the next piece with the current one.  The waits the copies need are the
+  // explicit ones before each barrier below.
+  auto src_block = [&](int m) -> int64_t {  // record offset of LDS block m
+    if (m < B_WK) return (int64_t)m * 1024;
+    if (m < B_WK + B_U) return ut_off_u(DK) + (int64_t)sg * NWB * 4096 + (int64_t)(m - B_WK) * 1024;
+    if (m < B_WK + B_U + B_GD || m >= NB_REAL) return ut_off_gd(DK, DV);
+    return ut_off_q(DK, DV) + (int64_t)(m - B_WK - B_U - B_GD) * 1024;
+  };
+  auto issue_one = [&](int c, char* dst, int i) __attribute__((always_inline)) {
+    const char* src = recs + (int64_t)c * RS + lane * 16;
+    const uint32_t ldst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;
+    const int m = w + i * NTW;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 0"
+                 :: "s"(ldst + m * 1024), "v"(src + src_block(m)) : "memory", "m0");
+  };
+  auto issue = [&](int c, char* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < ND; ++i) issue_one(c, dst, i);
+  };
+  auto frag = [&](const char* base, int off, int f) __attribute__((always_inline)) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(base + off + f * 1024 + lane * 16);
+  };
 
-  // ---- the start state (S0 or zero) and its bf16 image; P's upper tile is zero
-  f32x16 Macc = zero16();
-  if (has_m) {
+  // the state's 32 columns: M [dk x 32] as NRT accumulator tiles (dk = 32 rt + acc_row)
+  f32x16 M[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    M[rt] = zero16();
     if (a.S0) {
-      const float* s0 = a.S0 + bh * (int64_t)DK * DV;
-      const int dk = m_db * 32 + c32;
+      const float* s0 = a.S0 + bh * (int64_t)DK * DV + col0 + c32;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) Macc[e] = s0[dk * DV + col0 + acc_row(e, hh)];
+      for (int e = 0; e < 16; ++e) M[rt][e] = s0[(rt * 32 + acc_row(e, hh)) * DV];
     }
-    bf16* img = MT[0] + m_db * 32 + c32;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) img[acc_row(e, hh) * PK] = (bf16)Macc[e];
   }
-
-  // ---- the next piece's operands, in registers: K units (lane = token, so the transposed
-  // copy is written without bank conflicts), Q and -W units (consecutive threads along a
-  // row), g (threads < 64), the U^T tile in lane order (E waves) and the output tile's rows
-  // of P (output waves, A operand)
-  uint4 rk[KPT], rq[WANT_O ? KPT : 1], rw[KPT], ru[2], rp[WANT_O ? 4 : 1];
-  float rg = 0.f;
-  auto load_piece = [&](int c) {
-    const int64_t t0 = (int64_t)c * C;
-    const int n = (int)((a.T - t0) < C ? (a.T - t0) : C);
-    const int64_t row0 = (b * a.ld_T + t0) * a.H + h;
-    const char* rec = recs + (int64_t)c * RB;
-    // rows past the end of a partial piece load its last row (in bounds, never waited for
-    // here) and are replaced by zeros where they are staged
+  bf16x8 bM[NKS];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int i = tid + NT * j;
-      const int t = i & (C - 1), u = i / C;
-      rk[j] = *reinterpret_cast<const uint4*>(kg + (row0 + (t < n ? t : n - 1) * a.H) * DK + u * 8);
-      const int tr = i / KU, ur = i % KU;
-      rw[j] = reinterpret_cast<const uint4*>(rec)[i];
-      if constexpr (WANT_O)
-        rq[j] = *reinterpret_cast<const uint4*>(qg + (row0 + (tr < n ? tr : n - 1) * a.H) * DK + ur * 8);
-    }
-    if (tid < C) rg = reinterpret_cast<const float*>(rec + ut_off_g(DK, DV))[tid];
-    if (has_e) {
-      const uint4* ur = reinterpret_cast<const uint4*>(rec + ut_off_u(DK)) + ((cb * 2 + e_tt) * 64 + lane) * 2;
-      ru[0] = ur[0];
-      ru[1] = ur[1];
-    }
-    if constexpr (WANT_O) {
-      if (has_o) {
-        const bf16* pr = reinterpret_cast<const bf16*>(rec + ut_off_p(DK, DV)) + (o_tt * 32 + c32) * C + hh * 8;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) rp[ks] = *reinterpret_cast<const uint4*>(pr + ks * 16);
-      }
-    }
-  };
+  for (int ks = 0; ks < NKS; ++ks) bM[ks] = Mma<bf16>::from_acc(M[ks >> 1], ks, 1.f);
 
-  f32x16 Oacc = zero16();
+  // outputs as O^T tiles: lane c32 holds token 32 tt + c32, element e column
+  // col0 + acc_row(e), so each group of four elements is one 16-byte store
+  f32x16 OT[2];
   auto store_o = [&](int c) {
-    // output tile of piece c: token t = 32 o_tt + acc_row(e), column col0 + c32
     const int64_t t0 = (int64_t)c * C;
     const int n = (int)((a.T - t0) < C ? (a.T - t0) : C);
-    float* ob = a.o + ((b * a.T + t0 + o_tt * 32 + hh * 4) * a.H + h) * DV + col0 + c32;
-    const int64_t ostride = a.H * DV;
-    if (n == C) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) __builtin_nontemporal_store(Oacc[e], &ob[((e >> 2) * 8 + (e & 3)) * ostride]);
-    } else {
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = tt * 32 + c32;
+      if (t < n) {
+        float* ob = a.o + ((b * a.T + t0 + t) * a.H + h) * DV + col0 + hh * 4;
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (o_tt * 32 + acc_row(e, hh) < n) __builtin_nontemporal_store(Oacc[e], &ob[((e >> 2) * 8 + (e & 3)) * ostride]);
+        for (int g = 0; g < 4; ++g) {
+          typedef float f4 __attribute__((ext_vector_type(4)));
+          const f4 v = {OT[tt][4 * g], OT[tt][4 * g + 1], OT[tt][4 * g + 2], OT[tt][4 * g + 3]};
+          __builtin_nontemporal_store(v, reinterpret_cast<f4*>(ob + g * 8));
+        }
+      }
     }
   };
 
-  if (N > 0) load_piece(0);
-  for (int c = 0; c < N; ++c) {
-    const int cur = c & 1;
-    const int64_t tc0 = (int64_t)c * C;
-    const int n = (int)((a.T - tc0) < C ? (a.T - tc0) : C);
-    // ---- A. piece c's operands into LDS (K^T, K, Q, -W, decays) and U^T into the E
-    // accumulators; the previous piece's outputs; then piece c + 1's loads
+  // The copy of a later piece is spread over the products of this one (copy instruction i
+  // after product slot i NMF / ND), so the wave never stalls on a burst of memory
+  // instructions while the matrix cores wait.
+  constexpr int NMF = WANT_O ? 2 * NKS + 4 * (NRT + 2) : NKS + 4 * NRT;  // product slots per piece
+  auto piece = [&](const char* cur, int c_ahead, char* ahead) __attribute__((always_inline)) {
+    auto slot = [&](int k) __attribute__((always_inline)) {
+      if (NH == 0 && c_ahead < N) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int i = tid + NT * j;
-      const int t = i & (C - 1), u = i / C;
-      const uint4 kv = t < n ? rk[j] : make_uint4(0u, 0u, 0u, 0u);
-      const bf16* e8 = reinterpret_cast<const bf16*>(&kv);
+        for (int i = 0; i < ND; ++i)
+          if (i * NMF / ND == k) issue_one(c_ahead, ahead, i);
+      }
+    };
+    // E = U + (-W) M and O^T = M^T Q^T, k-step by k-step: four independent accumulator
+    // chains (E and O^T of both token tiles; without outputs, E's k range in two halves
+    // instead), with the A fragments of the next PF k-steps read ahead from LDS.  The
+    // B operand bf16(M) of E serves as the A operand of O^T (its lane holds a column of M),
+    // and the Q fragments (lane = token) as its B operand.
+    constexpr int PF = 3;
+    bf16x8 fu[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) KT[(u * 8 + e) * PT + t] = e8[e];
-      const int tr = i / KU, ur = i % KU;
-      *reinterpret_cast<uint4*>(Wn + tr * PK + ur * 8) = rw[j];
-      if constexpr (WANT_O) *reinterpret_cast<uint4*>(Qp + tr * PK + ur * 8) = tr < n ? rq[j] : make_uint4(0u, 0u, 0u, 0u);
+    for (int tt = 0; tt < 2; ++tt) {
+      const bf16x8* u = reinterpret_cast<const bf16x8*>(cur + L_U) + ((w * 2 + tt) * 64 + lane) * 2;
+      fu[2 * tt] = u[0];
+      fu[2 * tt + 1] = u[1];
     }
-    if (tid < C) {
-      const float g_end = __shfl(rg, 63, 64);
-      s_gam[tid] = expf(rg);
-      s_d[tid] = expf(g_end - rg);
-    }
-    uint4 cp[WANT_O ? 4 : 1];
+    f32x16 E[2], E2[2];
     if constexpr (WANT_O) {
+      bf16x8 rw[2][PF], rq[2][PF];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) cp[ks] = rp[ks];
+      for (int p = 0; p < PF; ++p)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          rw[tt][p] = frag(cur, 0, tt * NKS + p);
+          rq[tt][p] = frag(cur, L_Q, tt * NKS + p);
+        }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          E[tt][e] = (float)fu[2 * tt][e];
+          E[tt][e + 8] = (float)fu[2 * tt + 1][e];
+        }
+        OT[tt] = zero16();
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          E[tt] = Mma<bf16>::mma(rw[tt][ks % PF], bM[ks], E[tt]);
+          OT[tt] = Mma<bf16>::mma(bM[ks], rq[tt][ks % PF], OT[tt]);
+          slot(ks * 2 + tt);
+          if (ks + PF < NKS) {
+            rw[tt][ks % PF] = frag(cur, 0, tt * NKS + ks + PF);
+            rq[tt][ks % PF] = frag(cur, L_Q, tt * NKS + ks + PF);
+          }
+        }
+      }
+    } else {
+      constexpr int KH = NKS / 2;
+      bf16x8 rw[2][2][PF];  // [k half][tt][slot]
+#pragma unroll
+      for (int p = 0; p < PF; ++p)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) rw[hf][tt][p] = frag(cur, 0, tt * NKS + hf * KH + p);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          E[tt][e] = (float)fu[2 * tt][e];
+          E[tt][e + 8] = (float)fu[2 * tt + 1][e];
+        }
+        E2[tt] = zero16();
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < KH; ++k2) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          E[tt] = Mma<bf16>::mma(rw[0][tt][k2 % PF], bM[k2], E[tt]);
+          E2[tt] = Mma<bf16>::mma(rw[1][tt][k2 % PF], bM[KH + k2], E2[tt]);
+          slot(k2 * 2 + tt);
+          if (k2 + PF < KH) {
+            rw[0][tt][k2 % PF] = frag(cur, 0, tt * NKS + k2 + PF);
+            rw[1][tt][k2 % PF] = frag(cur, 0, tt * NKS + KH + k2 + PF);
+          }
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) E[tt][e] += E2[tt][e];
     }
-    f32x16 Eacc;
-    if (has_e) {
-      const bf16* u16 = reinterpret_cast<const bf16*>(ru);
+    const float* gam = reinterpret_cast<const float*>(cur + L_GD);
+    const float* dec = gam + C;
+    const float g_end = gam[C - 1];
+    // B operands from E: bf16(E) (the A operand of E^T P^T) and bf16(D E) for the state
+    // update (D_t per token)
+    bf16x8 bE[4], bDE[4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) Eacc[e] = (float)u16[e];
+    for (int tt = 0; tt < 2; ++tt) {
+      float dv_[16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<float4*>(dv_ + 4 * r) = *reinterpret_cast<const float4*>(dec + tt * 32 + r * 8 + hh * 4);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = E[tt][p * 8 + e];
+          if constexpr (WANT_O) bE[tt * 2 + p][e] = (bf16)x;
+          bDE[tt * 2 + p][e] = (bf16)(x * dv_[p * 8 + e]);
+        }
+      }
     }
     if constexpr (WANT_O) {
-      if (has_o && c > 0) store_o(c - 1);
+      // O = gamma (Q M): gamma of the lane's token
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const float gt = gam[tt * 32 + c32];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) OT[tt][e] *= gt;
+      }
     }
-    if (c + 1 < N) load_piece(c + 1);
-    __syncthreads();
+    // M <- gamma_63 M + K^T (D E);  O^T += E^T P^T: per k-step (token block of 16) NRT + 2
+    // products, fragments two k-steps ahead
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) M[rt][e] *= g_end;
+    bf16x8 rk[2][NRT], rp[2][2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) rk[p][rt] = frag(cur, L_KT, rt * 4 + p);
+      if constexpr (WANT_O) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) rp[p][tt] = frag(cur, L_P, tt * 4 + p);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        M[rt] = Mma<bf16>::mma(rk[ks & 1][rt], bDE[ks], M[rt]);
+        slot((WANT_O ? 2 * NKS : NKS) + ks * (WANT_O ? NRT + 2 : NRT) + rt);
+        if (ks + 2 < 4) rk[ks & 1][rt] = frag(cur, L_KT, rt * 4 + ks + 2);
+      }
+      if constexpr (WANT_O) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          OT[tt] = Mma<bf16>::mma(bE[ks], rp[ks & 1][tt], OT[tt]);
+          slot(2 * NKS + ks * (NRT + 2) + NRT + tt);
+          if (ks + 2 < 4) rp[ks & 1][tt] = frag(cur, L_P, tt * 4 + ks + 2);
+        }
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) bM[ks] = Mma<bf16>::from_acc(M[ks >> 1], ks, 1.f);
+  };
 
-    // ---- G. E^T = U^T - M^T W^T -> ET, DET;  outputs: gamma (Q M);  P = (Q K^T) o Gamma
-    const bf16* Mimg = MT[cur];
-    if (has_e) {
-      const bf16* arow = Mimg + c32 * PK;
-      const bf16* brow = Wn + (e_tt * 32 + c32) * PK;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        Eacc = Mma<bf16>::mma(Mma<bf16>::load_plain(arow, ks, hh), Mma<bf16>::load_plain(brow, ks, hh), Eacc);
-      // element (column acc_row(e), token t = 32 e_tt + c32)
-      const int t = e_tt * 32 + c32;
-      const float dt = s_d[t];
-      bf16* eo = ET + t;
-      bf16* deo = DET + t;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        eo[acc_row(e, hh) * PT] = (bf16)Eacc[e];
-        deo[acc_row(e, hh) * PT] = (bf16)(Eacc[e] * dt);
-      }
-    }
-    if constexpr (WANT_O) {
-      if (has_o) {
-        const bf16* arow = Qp + (o_tt * 32 + c32) * PK;
-        const bf16* brow = Mimg + c32 * PK;
-        f32x16 acc = zero16();
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          acc = Mma<bf16>::mma(Mma<bf16>::load_plain(arow, ks, hh), Mma<bf16>::load_plain(brow, ks, hh), acc);
-        float gm[16];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          *reinterpret_cast<float4*>(gm + 4 * r) = *reinterpret_cast<const float4*>(s_gam + o_tt * 32 + r * 8 + hh * 4);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] *= gm[e];
-        Oacc = acc;
-      }
-    }
-    __syncthreads();
+  // helpers: blocks m = hlp, hlp + NH, ... of a piece's part, all loaded unconditionally
+  // (blocks past the record's part repeat the decays into spare slots, so no load waits
+  // behind a branch)
+  constexpr int NDH = NH > 0 ? (NB_REAL + NH - 1) / NH : 1;
+  static_assert(NH == 0 || NDH * NH <= NB, "helper slots within the buffer");
+  const int hlp = w - NWB;
 
-    // ---- H. outputs: + P E;  state: M^T <- gamma_63 M^T + (E^T D) K
-    if constexpr (WANT_O) {
-      if (has_o) {
-        const bf16* brow = ET + c32 * PT;
-#pragma unroll
-        for (int ks = 0; ks < C / 16; ++ks)
-          Oacc = Mma<bf16>::mma(__builtin_bit_cast(bf16x8, cp[ks]), Mma<bf16>::load_plain(brow, ks, hh), Oacc);
+  // Per piece c: the stores of piece c - 1's outputs are issued, then piece c is computed
+  // from its buffer with the copy of piece c + NBUF - 1 (ND operations per wave) issued
+  // along the way; then the
+  // wave waits for its memory operations up to the copy of piece c + 1 -- with two buffers
+  // all of them, with three all but the ND just issued (the counter retires operations in
+  // issue order) -- and a barrier makes that true for all waves before piece c + 1 reads
+  // its buffer or a copy overwrites the buffer piece c read.
+  static_assert(ND < 64, "vmcnt range");
+  auto step = [&](int c, const char* cur, char* ahead) __attribute__((always_inline)) {
+    const bool ahead_issued = c + NBUF - 1 < N;
+    if (w < NWB) {
+      if constexpr (WANT_O) {
+        if (c > 0) store_o(c - 1);
       }
+      piece(cur, c + NBUF - 1, ahead);
+    } else if (ahead_issued) {
+      // helper: piece c + 1's blocks through registers into LDS
+      uint4 hreg[NDH];
+      const char* src = recs + (int64_t)(c + 1) * RS + lane * 16;
+#pragma unroll
+      for (int i = 0; i < NDH; ++i) hreg[i] = *reinterpret_cast<const uint4*>(src + src_block(hlp + i * NH));
+#pragma unroll
+      for (int i = 0; i < NDH; ++i) *reinterpret_cast<uint4*>(ahead + (hlp + i * NH) * 1024 + lane * 16) = hreg[i];
     }
-    if (has_m) {
-      const float g_end = s_gam[C - 1];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) Macc[e] *= g_end;
-      const bf16* arow = DET + c32 * PT;
-      const bf16* brow = KT + (m_db * 32 + c32) * PT;
-#pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks)
-        Macc = Mma<bf16>::mma(Mma<bf16>::load_plain(arow, ks, hh), Mma<bf16>::load_plain(brow, ks, hh), Macc);
-      bf16* img = MT[cur ^ 1] + m_db * 32 + c32;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) img[acc_row(e, hh) * PK] = (bf16)Macc[e];
-    }
+    // (a plain s_barrier: __syncthreads' release fence would also wait for the copies
+    // issued ahead)
+    if (NBUF == 3 && ahead_issued)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(ND) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  if (N > 0) {
+    issue(0, buf0);  // (every wave, global_load_lds)
+    if (NBUF == 3 && N > 1) issue(1, buf1);
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
+  if constexpr (NBUF == 3) {
+    for (int c = 0; c < N; c += 3) {
+      step(c, buf0, buf2);
+      if (c + 1 < N) step(c + 1, buf1, buf0);
+      if (c + 2 < N) step(c + 2, buf2, buf1);
+    }
+  } else {
+    for (int c = 0; c < N; c += 2) {
+      step(c, buf0, buf1);
+      if (c + 1 < N) step(c + 1, buf1, buf0);
+    }
+  }
+  if (w >= NWB) return;
   if constexpr (WANT_O) {
-    if (has_o && N > 0) store_o(N - 1);
+    if (N > 0) store_o(N - 1);
   }
-  if (has_m && a.S_final) {
-    float* sf = a.S_final + bh * (int64_t)DK * DV;
-    const int dk = m_db * 32 + c32;
+  if (a.S_final) {
+    float* sf = a.S_final + bh * (int64_t)DK * DV + col0 + c32;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sf[dk * DV + col0 + acc_row(e, hh)] = Macc[e];
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sf[(rt * 32 + acc_row(e, hh)) * DV] = M[rt][e];
   }
 }
 
@@ -534,12 +695,26 @@ static hipError_t launch_native_t(const UtArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned nb = (unsigned)(a.B * a.H * (DV / 32));
+  // state pass: the chains' 32-column slices spread over about one workgroup per CU (a
+  // CU streams its piece records at its share of HBM bandwidth, so more CUs per chain
+  // means less time per piece; the slices of a chain share the records through L2)
+  constexpr int NCB = DV / 32;
+  const int64_t chains = a.B * a.H;
   TimedLaunch tl(HLA_KERNEL_PREFILL, s);
-  if (a.o)
-    hipLaunchKernelGGL((state_kernel<DK, DV, true>), dim3(nb), dim3(512), 0, s, a);
+  auto go = [&](auto nwb_c) {
+    constexpr int NWB = decltype(nwb_c)::value;
+    const unsigned nb = (unsigned)(chains * (NCB / NWB));
+    if (a.o)
+      hipLaunchKernelGGL((state_kernel<DK, DV, NWB, true>), dim3(nb), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((state_kernel<DK, DV, NWB, false>), dim3(nb), dim3(256), 0, s, a);
+  };
+  if (chains * NCB <= 256)
+    go(std::integral_constant<int, 1>{});
+  else if (chains * NCB <= 512)
+    go(std::integral_constant<int, 2>{});
   else
-    hipLaunchKernelGGL((state_kernel<DK, DV, false>), dim3(nb), dim3(512), 0, s, a);
+    go(std::integral_constant<int, NCB>{});
   return hipGetLastError();
 }
 
