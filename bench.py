@@ -859,10 +859,13 @@ def cpu_baseline(n_query_chunks, tail_states=None):
 # Hardware counters behind the roofline records, from rocprofv3 passes over short runs of
 # one line each (one counter set per pass, FETCH_SIZE and WRITE_SIZE scaled by their own
 # reading for a 1 GiB device copy), summarised into profiles/counters.json together with a
-# hash of the kernel sources; a line reports them only while the sources are unchanged.
-COUNTER_SOURCES = ["gated_deltanet_hybrid_amd/csrc/" + f for f in
-                   ("common.hpp", "kernels.hpp", "chunk.hip", "scan.hip", "prefill.hip", "route.hip", "compose.hip",
-                    "decode.hip")]
+# hash of the kernel sources of that line; a line reports them only while those sources
+# are unchanged.
+COUNTER_SOURCES = {line: ["gated_deltanet_hybrid_amd/csrc/" + f for f in files] for line, files in (
+    ("routed_prefill", ("chunk.hip", "route.hip", "compose.hip")),
+    ("native_prefill", ("prefill.hip",)),
+    ("tail_replay", ("prefill.hip",)),
+    ("decode", ("decode.hip",)))}
 CALIB_BYTES = 1 << 30
 COUNTER_LINES = ("routed_prefill", "native_prefill", "tail_replay", "decode")
 
@@ -986,7 +989,7 @@ def counter_write(line, csv_paths):
         out[k] = rec
     path = os.path.join(ROOT, "profiles", "counters.json")
     allrec = json.load(open(path)) if os.path.exists(path) else {}
-    allrec[line] = dict(source_sha=sha_of(*COUNTER_SOURCES), kernels=out,
+    allrec[line] = dict(source_sha=sha_of(*COUNTER_SOURCES[line]), sources=COUNTER_SOURCES[line], kernels=out,
                         calib_copy_bytes=CALIB_BYTES, calib_raw={k: round(v, 1) for k, v in calib.items()})
     with open(path, "w") as fh:
         json.dump(allrec, fh, indent=1, sort_keys=True)
@@ -1004,7 +1007,7 @@ def read_counters(line):
         rec = json.load(open(path)).get(line)
     except Exception:
         return None
-    if not rec or rec.get("source_sha") != sha_of(*COUNTER_SOURCES):
+    if not rec or line not in COUNTER_SOURCES or rec.get("source_sha") != sha_of(*COUNTER_SOURCES[line]):
         return None
     return rec["kernels"]
 
