@@ -472,13 +472,17 @@ PEAK_FP32_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2 * 2.4e9 / 1e12
 PEAK_FP32_VALU_UNPACKED_TFLOPS = PEAK_FP32_VALU_TFLOPS / 2
 
 
-def flops_gdn2_pass(n_tokens_heads, dk, dv, outputs):
-    """Token-loop chunk pass per token and head: every column of the map [P | Q] (dk + dv
-    columns) or of the state (dv columns) takes k.(D x) (dk FMA), D x (dk mul), the erase
-    (dk FMA) and the write (dk FMA; none for P columns); outputs add q . x (dk FMA)."""
-    if outputs:
-        return n_tokens_heads * dv * dk * (2 + 1 + 2 + 2 + 2)
-    return n_tokens_heads * (dk * dk * (2 + 1 + 2) + dv * dk * (2 + 1 + 2 + 2))
+def bytes_gdn2_passes(B, T, H, dk, dv, N):
+    """Algorithmic HBM bytes of the two bf16 Gated DeltaNet-2 chunk passes, each input read
+    once and each output written once: the maps pass reads k, v (bf16) and the channel-wise
+    alpha, b (dk) and w (dv) (float32) and writes every chunk's At and Bc (bf16); the
+    outputs pass reads q, k, v, alpha, b, w and every chunk's float32 start state and
+    writes o (float32)."""
+    th, chunks = B * T * H, B * H * N
+    gates = 4 * (2 * dk + dv)
+    maps = th * (2 * dk + 2 * dv + gates) + chunks * 2 * (dk * dk + dk * dv)
+    outs = th * (2 * dk + 2 * dk + 2 * dv + gates + 4 * dv) + chunks * 4 * dk * dv
+    return maps, outs
 
 
 def bench_gdn2_routed(args, torch, hla, inputs, x):
@@ -522,20 +526,18 @@ def bench_gdn2_routed(args, torch, hla, inputs, x):
     ch_ms, ch_n = hla.timing_read(hla.KERNEL_CHUNK)
     cm_ms, cm_n = hla.timing_read(hla.KERNEL_COMPOSE)
     hla.timing_enable(False)
-    th = W.B * W.T * W.H
-    fl_pass = flops_gdn2_pass(th, W.dk, W.dv, False) + flops_gdn2_pass(th, W.dk, W.dv, True)
+    maps_b, outs_b = bytes_gdn2_passes(W.B, W.T, W.H, W.dk, W.dv, N)
     chunk_s = ch_ms / ch_n / 1e3 * 2  # two chunk passes per step
-    ach = fl_pass / chunk_s / 1e12
+    ach = (maps_b + outs_b) / chunk_s / 1e9
     res = dict(workload="routed_prefill under Gated DeltaNet-2 (channel-wise decay, erase and write gates), "
                         "B=1 T=32768 H=16 d=128 C=64",
                ms_per_step=dt * 1e3, tokens_per_s=W.B * W.T / dt, compose_ms=round(cm_ms / cm_n, 4),
                chunk_passes_ms=round(chunk_s * 1e3, 4),
-               chunk_roofline=dict(kernel="gdn2_chunk_kernel (maps + outputs)", bound="alu", achieved=round(ach, 2),
-                                   peak=round(PEAK_FP32_VALU_TFLOPS, 1), unit="TFLOP/s",
-                                   frac=round(ach / PEAK_FP32_VALU_TFLOPS, 4), flops_per_step=fl_pass,
-                                   frac_of_unpacked_peak=round(ach / PEAK_FP32_VALU_UNPACKED_TFLOPS, 4)))
+               chunk_roofline=dict(kernel="gdn2_wy_kernel (maps + outputs)", bound="hbm", achieved=round(ach, 1),
+                                   peak=PEAK_HBM_GBS, unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4),
+                                   bytes_per_step=maps_b + outs_b, maps_bytes=maps_b, outputs_bytes=outs_b))
     log(f"[gdn2_routed_prefill] {dt*1e3:.3f} ms/step, {W.B*W.T/dt/1e6:.3f} M tok/s, chunk passes "
-        f"{chunk_s*1e3:.3f} ms ({ach:.1f} TFLOP/s fp32 VALU), compose {cm_ms/cm_n:.3f} ms")
+        f"{chunk_s*1e3:.3f} ms ({ach:.0f} GB/s of algorithmic bytes), compose {cm_ms/cm_n:.3f} ms")
     del q, k, v, ga, gb, gw, At, Bc, out, o, ws
     torch.cuda.empty_cache()
     return res

@@ -152,6 +152,29 @@ def test_gdn2_native_prefill_many_pieces():
         assert_close(host(S)[0, h], S_ref.T, dtype, f"S h{h}")
 
 
+def test_gdn2_pieces_beyond_one_per_cu():
+    # 2 x 4 x 40 = 320 pieces: more than one workgroup per CU can take at once, so the bf16
+    # passes loop over pieces and prefetch the next piece's inputs; the last piece is ragged
+    dtype, dk, dv, T = "bf16", 128, 128, 40 * C - 5
+    B, H, N = 2, 4, 40
+    note("gdn2 pieces beyond one per CU")
+    x, g = gen((dtype, dk, dv, T), B=B, H=H, seed=97)
+    q, k, v, _, _ = token_tensors(x)
+    rng = np.random.default_rng(98)
+    init = (0.05 * rng.standard_normal((B, H, N, dk, dv))).astype(np.float32)
+    h = hla()
+    At, Bc = h.gdn2_chunk_transitions(k, v, *gates_dev(g))
+    o, _ = h.gdn2_prefill(q, k, v, *gates_dev(g), chunk_init=f32(init), want_state=False)
+    torch.cuda.synchronize()
+    for b, hh in [(0, 0), (1, 3), (1, 1)]:
+        args = seq(x, g, b, hh)
+        A_ref, B_ref = oracle.gdn2_chunk_transitions(*args[1:], C)
+        assert_close(host(At[b, hh]), A_ref.transpose(0, 2, 1), dtype, f"At b{b} h{hh}")
+        assert_close(host(Bc[b, hh]), B_ref.transpose(0, 2, 1), dtype, f"Bc b{b} h{hh}")
+        o_ref = oracle.gdn2_routed_outputs(*args, C, init[b, hh].astype(np.float64).transpose(0, 2, 1))
+        assert_close(host(o)[b, :, hh], o_ref, dtype, f"o b{b} h{hh}")
+
+
 def test_gdn2_collapsed_gates_match_gdn():
     # b = w = beta and a = alpha broadcast: both GPU paths compute the same Gated DeltaNet
     dtype, dk, dv, T = "f32", 64, 64, 150
