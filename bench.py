@@ -340,12 +340,12 @@ SECONDARY = {
     "decode_skip": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs, skip=True),
 }
 
-# lines run only when named with --only: the backward at the full 32768 tokens needs about
-# 200 GiB of workspace in one pass (three per-pair states of the composition backward grow
-# as N^2); the line also times it in query-chunk groups within 64 GiB
+# lines run only when named with --only: the backward at the full 32768 tokens, in one call
+# within a 64 GiB workspace (history segments replayed from checkpoints), and beside it with
+# the about 200 GiB workspace in which every chunk pair has its own state slots
 ONLY_LINES = {
     "routed_prefill_backward_T32K": lambda args, torch, hla, inputs, x: bench_prefill_backward(
-        args, torch, hla, inputs, x, T=inputs.WORKLOADS["routed_prefill"].T, grouped_gib=64),
+        args, torch, hla, inputs, x, T=inputs.WORKLOADS["routed_prefill"].T, ws_gib=64),
 }
 
 
@@ -562,12 +562,14 @@ def flops_router_bwd(pairs, n_rep, dk):
     return pairs * 4 * 2 * n_rep * dk
 
 
-def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, grouped_gib=None):
+def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, ws_gib=None):
     """The routed-prefill backward (hla_prefill_backward) at B=1, T tokens (8192 by default),
     H=16, d=128, C=64, bf16, computed gates at tau = 1e-3: recomputed chunk maps and gates,
     composition replay, chunk outputs reverse, composition adjoint and sums, chunk maps
-    reverse, router backward and the per-token sums.  With `grouped_gib` the step is also
-    timed with a workspace of that many GiB, which runs the query chunks in groups."""
+    reverse, router backward and the per-token sums.  The workspace is the one-pass size
+    (every chunk pair its own state slots) or, with `ws_gib` below that, `ws_gib` GiB, in
+    which the composition backward runs its history steps in segments replayed from
+    checkpoints; the one-pass size is then timed beside it."""
     W = inputs.WORKLOADS["routed_prefill"]
     q, k, v = (to_dev(a[:, :T], W.dtype, torch) for a in (x.q, x.k, x.v))
     beta, alpha = to_dev(x.beta[:, :T], "f32", torch), to_dev(x.alpha[:, :T], "f32", torch)
@@ -575,30 +577,40 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, grouped_gib=Non
     dev = k.device
     N = math.ceil(T / C)
     d = hla.make_dims(W.B, T, W.H, T, W.dk, W.dv, hla.HLA_BF16, C)
-    ws = torch.empty(hla.workspace_bytes(hla.FN_PREFILL_BACKWARD, d), dtype=torch.uint8, device=dev)
-    log(f"[routed_prefill_backward] T={T}: workspace {ws.numel() / 2**30:.2f} GiB")
-    step = lambda: hla.prefill_backward(q, k, v, beta, alpha, dO, tau=W.tau, ws=ws)
-    g = step()
+    one_pass = hla.workspace_bytes(hla.FN_PREFILL_BACKWARD, d)
+    main_bytes = one_pass if ws_gib is None else min(one_pass, int(ws_gib * 2**30))
     # active pairs from the router's own mask (a gate gradient can underflow to zero far
     # back in a long chain, so it does not count them)
     At, Bc = hla.chunk_transitions(k, v, beta, alpha)
     pairs = int(hla.route_mix(q, k, At, Bc, tau=W.tau)["active_cnt"].sum().item())
     del At, Bc
-    torch.cuda.synchronize()
     steps = max(3, args.steps // 4)
-    hla.timing_enable(True)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
     names = (("bwd_chunk", hla.KERNEL_BWD_CHUNK), ("bwd_save", hla.KERNEL_BWD_SAVE),
              ("bwd_adjoint", hla.KERNEL_BWD_ADJOINT), ("bwd_reduce", hla.KERNEL_BWD_REDUCE),
              ("bwd_router", hla.KERNEL_BWD_ROUTER), ("fwd_chunk", hla.KERNEL_CHUNK), ("fwd_gates", hla.KERNEL_GATES),
              ("fwd_compose", hla.KERNEL_COMPOSE))
-    per = {n: hla.timing_read(kid) for n, kid in names}
-    hla.timing_enable(False)
-    ms = {n: tot / steps for n, (tot, cnt) in per.items() if cnt > 0}
+
+    def measure(nbytes):
+        """ms per step, per-kernel ms per step and composition segments per step."""
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        log(f"[routed_prefill_backward] T={T}: workspace {nbytes / 2**30:.2f} GiB")
+        step = lambda: hla.prefill_backward(q, k, v, beta, alpha, dO, tau=W.tau, ws=ws)
+        step()
+        torch.cuda.synchronize()
+        hla.timing_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        dt_ = (time.perf_counter() - t0) / steps
+        per = {n: hla.timing_read(kid) for n, kid in names}
+        hla.timing_enable(False)
+        del ws
+        torch.cuda.empty_cache()
+        ms_ = {n: tot / steps for n, (tot, cnt) in per.items() if cnt > 0}
+        return dt_, ms_, per["bwd_adjoint"][1] // steps  # one adjoint launch per segment
+
+    dt, ms, segments = measure(main_bytes)
     th = W.B * T * W.H
     fl_chunk = flops_chunk_bwd(th, W.dk, W.dv)
     fl_pair = flops_compose(pairs, W.dk, W.dv)
@@ -609,7 +621,7 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, grouped_gib=Non
     # roofline record of the kernel that takes the most time: the chunk reverse (fp32 VALU)
     # or one of the composition passes (bf16 matrix cores)
     kernels = {"bwd_chunk": ("chunk_bwd_kernel (outputs + maps reverse)", "alu", fl_chunk, PEAK_FP32_VALU_TFLOPS),
-               "bwd_save": ("compose_save_kernel (+ prep_bwd_kernel)", "mfma", fl_pair, PEAK_BF16_TFLOPS),
+               "bwd_save": ("compose_replay_kernel (+ prep_bwd_kernel)", "mfma", fl_pair, PEAK_BF16_TFLOPS),
                "bwd_adjoint": ("compose_adjoint_kernel", "mfma", fl_pair, PEAK_BF16_TFLOPS),
                "bwd_reduce": ("compose_grad_reduce_kernel (+ chain_sum_kernel)", "mfma", fl_pair, PEAK_BF16_TFLOPS)}
     dom = max(kernels, key=lambda n: ms[n])
@@ -618,6 +630,7 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, grouped_gib=Non
     res = dict(workload=f"routed prefill backward (GDN + HLA), B={W.B} T={T} H={W.H} d={W.dk} C={C} bf16, "
                         f"computed gates tau={W.tau}",
                ms_per_step=round(dt * 1e3, 3), tokens_per_s=round(W.B * T / dt, 1), active_pairs=pairs,
+               workspace_gib=round(main_bytes / 2**30, 2), history_segments=segments,
                kernel_ms={n: round(v, 3) for n, v in ms.items()},
                roofline=dict(kernel=kname, bound=bound, achieved=round(ach_dom, 2), peak=round(peak, 1),
                              unit="TFLOP/s", frac=round(ach_dom / peak, 4), flops_per_launch=fl_dom,
@@ -626,31 +639,18 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, grouped_gib=Non
                                   unit="TFLOP/s", frac=round(ach / PEAK_FP32_VALU_TFLOPS, 4), flops_per_step=fl_chunk,
                                   frac_of_unpacked_peak=round(ach / PEAK_FP32_VALU_UNPACKED_TFLOPS, 4)),
                composition_mfma=dict(flops_per_pass=fl_pair, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", **mfma),
-               router_tflops=round(flops_router_bwd(pairs, C, W.dk) / (ms["bwd_router"] / 1e3) / 1e12, 2))
-    log(f"[routed_prefill_backward T={T}] {dt*1e3:.3f} ms/step, {W.B*T/dt/1e6:.3f} M tok/s; chunk reverse "
-        f"{ms['bwd_chunk']:.3f} ms ({ach:.1f} TFLOP/s fp32 VALU); save {ms['bwd_save']:.3f}, adjoint "
+               router_tflops=round(flops_router_bwd(pairs, C, W.dk) / (ms["bwd_router"] / 1e3) / 1e12, 2),
+               min_workspace_gib=round(hla.workspace_bytes(hla.FN_PREFILL_BACKWARD_MIN, d) / 2**30, 2))
+    log(f"[routed_prefill_backward T={T}] {dt*1e3:.3f} ms/step, {W.B*T/dt/1e6:.3f} M tok/s in "
+        f"{main_bytes / 2**30:.1f} GiB ({segments} history segments); chunk reverse "
+        f"{ms['bwd_chunk']:.3f} ms ({ach:.1f} TFLOP/s fp32 VALU); replay {ms['bwd_save']:.3f}, adjoint "
         f"{ms['bwd_adjoint']:.3f}, reduce {ms['bwd_reduce']:.3f}, router {ms['bwd_router']:.3f} ms")
-    res["workspace_gib"] = round(ws.numel() / 2**30, 2)
-    if grouped_gib is not None and grouped_gib * 2**30 < ws.numel():
-        del ws, g
-        torch.cuda.empty_cache()
-        ws = torch.empty(int(grouped_gib * 2**30), dtype=torch.uint8, device=dev)
-        g = step()
-        torch.cuda.synchronize()
-        hla.timing_enable(True)
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            step()
-        torch.cuda.synchronize()
-        dtg = (time.perf_counter() - t0) / steps
-        groups = hla.timing_read(hla.KERNEL_BWD_SAVE)[1] // steps  # one save launch per group
-        hla.timing_enable(False)
-        res["grouped"] = dict(workspace_gib=grouped_gib, groups=groups, ms_per_step=round(dtg * 1e3, 3),
-                              tokens_per_s=round(W.B * T / dtg, 1),
-                              min_workspace_gib=round(hla.workspace_bytes(hla.FN_PREFILL_BACKWARD_MIN, d) / 2**30, 2))
-        log(f"[routed_prefill_backward T={T}] in {groups} query-chunk groups within {grouped_gib} GiB: "
-            f"{dtg*1e3:.3f} ms/step")
-    del q, k, v, beta, alpha, dO, ws, g
+    if main_bytes < one_pass:
+        dt1, ms1, _ = measure(one_pass)
+        res["one_pass"] = dict(workspace_gib=round(one_pass / 2**30, 2), ms_per_step=round(dt1 * 1e3, 3),
+                               tokens_per_s=round(W.B * T / dt1, 1), kernel_ms={n: round(v, 3) for n, v in ms1.items()})
+        log(f"[routed_prefill_backward T={T}] one pass in {one_pass / 2**30:.1f} GiB: {dt1*1e3:.3f} ms/step")
+    del q, k, v, beta, alpha, dO
     torch.cuda.empty_cache()
     return res
 

@@ -97,65 +97,67 @@ int64_t reps_ws(const hla_dims_t* d, int32_t n_rep) {
   return round_up(d->B * d->H * n_chunks(d) * n_rep * d->dk * 4, 256);
 }
 
-// Workspace of hla_compose_backward: (At - I) and its transpose in the fragment order, Bc in
-// the lane order, per-wave gate-gradient parts and the final lambda of every chain, then
-// `slots` pair slots per (b, h) (dtype) for each of the state in front of a step, D_j and
-// lambda.  With N (N - 1) / 2 slots every pair has its own and the chains run in one group;
-// with fewer, the chains run in consecutive groups whose pairs fit (at least N - 1 slots,
-// the longest chain's pairs).
+// Workspace of hla_compose_backward with history segments of K steps: (At - I) and its
+// transpose in the fragment order, Bc in the lane order, per-wave gate-gradient parts and
+// every chain's lambda, the float32 checkpoints of every chain at each segment boundary it
+// crosses, then per (b, h) the pair slots of the largest segment (the first: chain i holds
+// min(K, i) pairs) for each of the state in front of a step, D_j and lambda (dtype).  With
+// K = N there is one segment, every pair has its slot and there is no checkpoint.
 struct ComposeBwdWs {
-  int64_t ap_off, apt_off, bl_off, dgp_off, le_off, ms_off, ds_off, ls_off, total;
+  int64_t ap_off, apt_off, bl_off, dgp_off, le_off, ck_off, ms_off, ds_off, ls_off, total;
+  int32_t K;
+  int64_t slots, nck;
 };
-int64_t all_pairs(const hla_dims_t* d) {
-  const int64_t N = n_chunks(d);
-  return N * (N - 1) / 2;
-}
-int64_t min_pairs(const hla_dims_t* d) { return n_chunks(d) > 1 ? n_chunks(d) - 1 : 0; }
 int64_t pair_bytes(const hla_dims_t* d) { return d->B * d->H * d->dk * d->dv * dtype_bytes(d->dtype); }
-ComposeBwdWs compose_bwd_ws(const hla_dims_t* d, int64_t slots) {
+// pair slots per (b, h) of the first segment, and checkpoints per (b, h)
+int64_t seg_slots(int64_t N, int64_t K) {
+  return K >= N - 1 ? N * (N - 1) / 2 : K * (K + 1) / 2 + (N - 1 - K) * K;
+}
+int64_t seg_ckpts(int64_t N, int64_t K) {
+  int64_t n = 0;
+  for (int64_t b = 1; b * K < N; ++b) n += N - 1 - b * K;
+  return n;
+}
+ComposeBwdWs compose_bwd_ws(const hla_dims_t* d, int64_t K) {
   const int64_t N = n_chunks(d), BH = d->B * d->H, e = dtype_bytes(d->dtype);
-  const int64_t at = round_up(BH * N * d->dk * d->dk * e, 256), pr = round_up(slots * pair_bytes(d), 256);
   ComposeBwdWs w;
+  w.K = (int32_t)K;
+  w.slots = seg_slots(N, K);
+  w.nck = seg_ckpts(N, K);
+  const int64_t at = round_up(BH * N * d->dk * d->dk * e, 256), pr = round_up(w.slots * pair_bytes(d), 256);
   w.ap_off = 0;
   w.apt_off = at;
   w.bl_off = 2 * at;
   w.dgp_off = w.bl_off + round_up(BH * N * d->dk * d->dv * e, 256);
   w.le_off = w.dgp_off + round_up(BH * N * N * (d->dv / 32) * 4, 256);
-  w.ms_off = w.le_off + round_up(BH * N * d->dk * d->dv * 4, 256);
+  w.ck_off = w.le_off + round_up(BH * N * d->dk * d->dv * 4, 256);
+  w.ms_off = w.ck_off + round_up(BH * w.nck * d->dk * d->dv * 4, 256);
   w.ds_off = w.ms_off + pr;
   w.ls_off = w.ds_off + pr;
   w.total = w.ls_off + pr;
   return w;
 }
-
-// Pair slots per (b, h) that `bytes` of composition workspace hold (all pairs at most), or
-// -1 when they hold fewer than the longest chain needs.
-int64_t slots_for(const hla_dims_t* d, int64_t bytes) {
-  const int64_t fixed = compose_bwd_ws(d, 0).total, per = 3 * pair_bytes(d);
-  const int64_t slots = bytes < fixed ? -1 : (bytes - fixed) / per;
-  if (slots < min_pairs(d)) return -1;
-  return slots < all_pairs(d) ? slots : all_pairs(d);
+// The smallest composition workspace over the segment lengths.
+int64_t compose_bwd_min(const hla_dims_t* d) {
+  const int64_t N = n_chunks(d);
+  int64_t best = compose_bwd_ws(d, N).total;
+  for (int64_t K = 1; K < N; ++K) best = std::min(best, compose_bwd_ws(d, K).total);
+  return best;
 }
-
-// Consecutive chain groups [i0, i1) whose pairs (i (i - 1) / 2 before chain i) fit `slots`,
-// each as long as it can be.
-std::vector<std::pair<int32_t, int32_t>> chain_groups(int32_t N, int64_t slots) {
-  std::vector<std::pair<int32_t, int32_t>> g;
-  auto before = [](int64_t i) { return i * (i - 1) / 2; };
-  for (int32_t i0 = 0; i0 < N;) {
-    int32_t i1 = i0 + 1;
-    while (i1 < N && before(i1 + 1) - before(i0) <= slots) ++i1;
-    g.emplace_back(i0, i1);
-    i0 = i1;
-  }
-  return g;
+// The longest segment whose workspace fits `bytes` (fewest segments), or -1.
+int64_t seg_len_for(const hla_dims_t* d, int64_t bytes) {
+  for (int64_t K = n_chunks(d); K >= 1; --K)
+    if (compose_bwd_ws(d, K).total <= bytes) return K;
+  return -1;
 }
 
 void set_compose_bwd_ws(hla::ComposeBwdArgs& a, const ComposeBwdWs& w, void* ws) {
   char* base = static_cast<char*>(ws);
   a.Ap = base + w.ap_off; a.ApT = base + w.apt_off; a.Bl = base + w.bl_off;
   a.Msave = base + w.ms_off; a.Dsave = base + w.ds_off; a.Lsave = base + w.ls_off;
+  a.Ckpt = reinterpret_cast<float*>(base + w.ck_off);
   a.dgp = reinterpret_cast<float*>(base + w.dgp_off); a.lam_end = reinterpret_cast<float*>(base + w.le_off);
+  a.K = w.K; a.slots = w.slots; a.nck = w.nck;
 }
 
 // Workspace of hla_chunk_backward: per-workgroup partial sums of the per-token gradients.
@@ -184,13 +186,13 @@ void set_chunk_bwd_ws(hla::ChunkBwdArgs& a, const ChunkBwdWs& w, void* ws) {
 
 // Workspace of hla_prefill_backward: the forward's transitions, route outputs and routed
 // states, the gradients handed between the passes, then the workspaces of the route, the
-// chunk backward and the composition backward (with `slots` pair slots, last, so that
-// what a caller's workspace holds beyond the rest becomes pair slots).
+// chunk backward and the composition backward (with history segments of K steps, last, so
+// that what a caller's workspace holds beyond the rest sets the segment length).
 struct PrefillBwdWs {
   int64_t at_off, bc_off, gates_off, mask_off, aidx_off, acnt_off, sr_off, dsr_off, dat_off, dbc_off, dg_off,
       qbar_off, dqbar_off, dkr_off, route_off, chunk_off, comp_off, total;
 };
-PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d, int64_t slots) {
+PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d, int64_t K) {
   const int64_t N = n_chunks(d), BH = d->B * d->H, BHN = BH * N, e = dtype_bytes(d->dtype);
   PrefillBwdWs w;
   int64_t o = 0;
@@ -215,7 +217,7 @@ PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d, int64_t slots) {
   w.dkr_off = take(d->B * d->T * d->H * d->dk * 4);
   w.route_off = take(route_ws(d));
   w.chunk_off = take(chunk_bwd_ws(d).total);
-  w.comp_off = take(compose_bwd_ws(d, slots).total);
+  w.comp_off = take(compose_bwd_ws(d, K).total);
   w.total = o;
   return w;
 }
@@ -378,8 +380,8 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
       if (n_rep < 1 || d->C % n_rep != 0) return HLA_ERR_BAD_SHAPE;
       *out = (size_t)reps_ws(d, n_rep);
       return HLA_OK;
-    case HLA_FN_COMPOSE_BACKWARD: *out = (size_t)compose_bwd_ws(d, all_pairs(d)).total; return HLA_OK;
-    case HLA_FN_COMPOSE_BACKWARD_MIN: *out = (size_t)compose_bwd_ws(d, min_pairs(d)).total; return HLA_OK;
+    case HLA_FN_COMPOSE_BACKWARD: *out = (size_t)compose_bwd_ws(d, n_chunks(d)).total; return HLA_OK;
+    case HLA_FN_COMPOSE_BACKWARD_MIN: *out = (size_t)compose_bwd_min(d); return HLA_OK;
     case HLA_FN_CHUNK_BACKWARD:
       if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
       *out = (size_t)chunk_bwd_ws(d).total;
@@ -387,7 +389,8 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
     case HLA_FN_PREFILL_BACKWARD:
     case HLA_FN_PREFILL_BACKWARD_MIN:
       if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
-      *out = (size_t)prefill_bwd_ws(d, fn == HLA_FN_PREFILL_BACKWARD ? all_pairs(d) : min_pairs(d)).total;
+      *out = fn == HLA_FN_PREFILL_BACKWARD ? (size_t)prefill_bwd_ws(d, n_chunks(d)).total
+                                           : (size_t)(prefill_bwd_ws(d, 1).comp_off + compose_bwd_min(d));
       return HLA_OK;
     default: return HLA_ERR_UNSUPPORTED;
   }
@@ -520,6 +523,22 @@ hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps,
   return hip_status(hla::launch_route(a, d->dtype, d->dk, d->dv, stream));
 }
 
+// The composition backward's checkpoints from the bf16 composition of the forward: it runs
+// every chain (sharing each staged map among several chains) and keeps each chain's state at
+// the segment boundaries it crosses; its reordered maps go to the backward's Ap and Bl
+// regions, which the backward's prep stage overwrites afterwards.
+static hipError_t compose_checkpoints(hla::ComposeBwdArgs& a, const hla_dims_t* d, hipStream_t stream) {
+  hla::RouteArgs r{};
+  r.At = a.At; r.Bc = a.Bc; r.S0 = a.S0; r.gates = const_cast<float*>(a.gates);
+  r.mask = const_cast<uint8_t*>(a.mask);
+  r.S_routed = a.S_routed ? a.S_routed : a.lam_end;
+  r.At_prep = a.Ap; r.Bc_prep = a.Bl;
+  r.B = d->B; r.T = d->T; r.H = d->H; r.ld_T = d->ld_T; r.N = a.N; r.C = d->C;
+  r.ckpt = a.Ckpt; r.ckpt_K = a.K; r.ckpt_nck = a.nck;
+  a.ckpt_done = 1;
+  return hla::launch_compose_bf16(r, d->dk, d->dv, stream);
+}
+
 hla_status_t hla_compose_backward(const hla_dims_t* d, const void* At, const void* Bc, const float* gates,
                                   const uint8_t* mask, const float* S0, const float* dS_routed, float* dAt,
                                   float* dBc, float* dgates, float* dS0, float* S_routed, void* ws, size_t ws_bytes,
@@ -529,20 +548,32 @@ hla_status_t hla_compose_backward(const hla_dims_t* d, const void* At, const voi
   if (!At || !Bc || !gates || !mask || !dS_routed || !dAt || !dBc || !dgates) return HLA_ERR_NULL_ARG;
   if (!all_aligned(At, Bc, S0, dS_routed, dAt, dBc, dS0, S_routed, ws) || !all_aligned4(gates, dgates))
     return HLA_ERR_ALIGN;
-  const int64_t slots = ws ? slots_for(d, (int64_t)ws_bytes) : -1;
-  if (slots < 0) return HLA_ERR_WORKSPACE;
+  const int64_t K = ws ? seg_len_for(d, (int64_t)ws_bytes) : -1;
+  if (K < 0) return HLA_ERR_WORKSPACE;
   hla::ComposeBwdArgs a{};
   a.At = At; a.Bc = Bc; a.gates = gates; a.mask = mask; a.S0 = S0; a.dS = dS_routed;
   a.dAt = dAt; a.dBc = dBc; a.dgates = dgates; a.dS0 = dS0; a.S_routed = S_routed;
-  set_compose_bwd_ws(a, compose_bwd_ws(d, slots), ws);
+  set_compose_bwd_ws(a, compose_bwd_ws(d, K), ws);
   a.B = d->B; a.H = d->H; a.N = (int32_t)n_chunks(d);
-  for (const auto& g : chain_groups(a.N, slots)) {
-    a.i0 = g.first; a.i1 = g.second; a.accumulate = g.first > 0;
-    const hipError_t e = hla::launch_compose_backward(a, d->dtype, d->dk, d->dv,
-                                                      hla::kComposeBwdSave | hla::kComposeBwdReverse, stream);
+  hipError_t e = hipSuccess;
+  if (a.K < a.N && d->dtype == HLA_BF16) {
+    // checkpoints (and the routed states) from the bf16 composition, with its reordered
+    // maps in the regions the backward's own take over afterwards; without a caller's
+    // S_routed the states land in the lambda buffer, which is free until the adjoint
+    e = compose_checkpoints(a, d, stream);
     if (e != hipSuccess) return HLA_ERR_HIP;
   }
-  return HLA_OK;
+  // the reordered maps (and the checkpoints, if not yet taken), then the segments last to
+  // first
+  e = hla::launch_compose_backward(a, d->dtype, d->dk, d->dv, hla::kComposeBwdPrep, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  if (a.K < a.N) a.S_routed = nullptr;  // written with the checkpoints
+  for (int32_t j0 = (a.N - 1) / a.K * a.K; j0 >= 0; j0 -= a.K) {
+    a.j0 = j0; a.j1 = std::min(j0 + a.K, a.N);
+    e = hla::launch_compose_backward(a, d->dtype, d->dk, d->dv, hla::kComposeBwdSave | hla::kComposeBwdReverse, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+  }
+  return hip_status(hla::launch_compose_backward(a, d->dtype, d->dk, d->dv, hla::kComposeBwdFinish, stream));
 }
 
 hla_status_t hla_chunk_backward(const hla_dims_t* d, const void* q, const void* k, const void* v, const float* beta,
@@ -586,16 +617,16 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
   if (!all_aligned(q, k, v, S0, dS0, ws) || !all_aligned4(beta, alpha, gates_in, dO, dq, dk, dv, dbeta, dalpha, dgates))
     return HLA_ERR_ALIGN;
-  const PrefillBwdWs w0 = prefill_bwd_ws(d, 0);
-  const int64_t slots = ws ? slots_for(d, (int64_t)ws_bytes - w0.comp_off) : -1;
-  if (slots < 0) return HLA_ERR_WORKSPACE;
-  const PrefillBwdWs w = prefill_bwd_ws(d, slots);
+  const PrefillBwdWs w0 = prefill_bwd_ws(d, 1);
+  const int64_t K = ws ? seg_len_for(d, (int64_t)ws_bytes - w0.comp_off) : -1;
+  if (K < 0) return HLA_ERR_WORKSPACE;
+  const PrefillBwdWs w = prefill_bwd_ws(d, K);
   char* base = static_cast<char*>(ws);
   const int32_t N = (int32_t)n_chunks(d);
   auto at = [&](int64_t off) { return static_cast<void*>(base + off); };
   auto fat = [&](int64_t off) { return reinterpret_cast<float*>(base + off); };
   // 1. forward: chunk maps, then gates, mask and lists (the routed states come from the
-  //    composition backward's forward replay in step 2)
+  //    composition backward's forward replay)
   hla::ChunkArgs c{};
   c.q = q; c.k = k; c.v = v; c.beta = beta; c.alpha = alpha;
   c.B = d->B; c.T = d->T; c.H = d->H; c.ld_T = d->ld_T; c.N = N;
@@ -618,7 +649,7 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   hla::ComposeBwdArgs m{};
   m.At = c.At; m.Bc = c.Bc; m.gates = r.gates; m.mask = r.mask; m.S0 = S0; m.dS = fat(w.dsr_off);
   m.dAt = fat(w.dat_off); m.dBc = fat(w.dbc_off); m.dgates = dg; m.dS0 = dS0; m.S_routed = fat(w.sr_off);
-  set_compose_bwd_ws(m, compose_bwd_ws(d, slots), at(w.comp_off));
+  set_compose_bwd_ws(m, compose_bwd_ws(d, K), at(w.comp_off));
   m.B = d->B; m.H = d->H; m.N = N;
   hla::ChunkBwdArgs cb{};
   cb.q = q; cb.k = k; cb.v = v; cb.beta = beta; cb.alpha = alpha;
@@ -628,23 +659,38 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   cb.dAt = m.dAt; cb.dBc = m.dBc;
   set_chunk_bwd_ws(cb, chunk_bwd_ws(d), at(w.chunk_off));
   cb.dq = dq; cb.dk = dk; cb.dv = dv; cb.dbeta = dbeta; cb.dalpha = dalpha;
-  // 2-4 per group of query chunks (one group when the workspace holds every pair):
-  for (const auto& g : chain_groups(N, slots)) {
-    m.i0 = g.first; m.i1 = g.second; m.accumulate = g.first > 0;
-    // 2. composition backward, first stage: replay the group's chains, keeping the step
-    //    states and writing their routed states
-    e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdSave, stream);
-    if (e != hipSuccess) return HLA_ERR_HIP;
-    // 3. outputs part of the chunk backward for the group's chunks: dS~ and the chunk-local
-    //    partial sums
-    cb.c0 = g.first; cb.c1 = g.second;
-    e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdOut, stream);
-    if (e != hipSuccess) return HLA_ERR_HIP;
-    // 4. composition backward, second stage: the group's parts of dAt, dBc, dgates (dS0
-    //    after the last group)
-    e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdReverse, stream);
+  // 2. composition backward, forward replay: with more than one history segment the
+  //    checkpoints and the routed states (from the bf16 composition, or the backward's own
+  //    replay), then the reordered maps; with one segment the routed states come from the
+  //    segment's replay
+  if (m.K < N && d->dtype == HLA_BF16) {
+    e = compose_checkpoints(m, d, stream);
     if (e != hipSuccess) return HLA_ERR_HIP;
   }
+  e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdPrep, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  const int32_t j_last = (N - 1) / m.K * m.K;
+  m.j0 = j_last; m.j1 = N;
+  if (m.K >= N) {
+    e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdSave, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+  }
+  m.S_routed = nullptr;
+  // 3. outputs part of the chunk backward: dS~ and the chunk-local partial sums
+  cb.c0 = 0; cb.c1 = N;
+  e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdOut, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
+  // 4. composition backward per history segment, last to first: replay the segment's steps
+  //    keeping their states (already done for a single segment), then the adjoint and the
+  //    segment's parts of dAt, dBc, dgates; dS0 at the end
+  for (int32_t j0 = j_last; j0 >= 0; j0 -= m.K) {
+    m.j0 = j0; m.j1 = std::min(j0 + m.K, N);
+    const int stages = (m.K >= N ? 0 : hla::kComposeBwdSave) | hla::kComposeBwdReverse;
+    e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, stages, stream);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+  }
+  e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdFinish, stream);
+  if (e != hipSuccess) return HLA_ERR_HIP;
   // then the maps part of the chunk backward
   cb.c0 = 0; cb.c1 = N;
   e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdMap, stream);

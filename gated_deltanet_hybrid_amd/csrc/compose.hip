@@ -34,6 +34,7 @@
 namespace hla {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 // (At_j - I) written in the exact byte order of the composition's LDS image of it, so the
 // copy into LDS is a plain contiguous 1 KiB block per instruction.  The image: the columns
@@ -240,6 +241,23 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
 #pragma unroll
   for (int s = 0; s < SPW; ++s)
     if (qi[s] == 0) write_state(s);
+  // Checkpoint of the chains that cross history step jb = b K (taken before that step), in
+  // the accumulator's lane order: 16 floats per lane and row tile, stored non-temporally.
+  auto keep_state = [&](int jb) {
+    const int b = jb / a.ckpt_K;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      if (qi[s] <= jb || qi[s] >= N) continue;
+      float* ck = a.ckpt + (bh * a.ckpt_nck + ckpt_slot(N, a.ckpt_K, b, qi[s])) * (int64_t)DK * DV;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        f32x4v* dst = reinterpret_cast<f32x4v*>(ck + ((int64_t)(ct * NRT + rt) * 64 + lane) * 16);
+#pragma unroll
+        for (int e = 0; e < 16; e += 4)
+          __builtin_nontemporal_store(f32x4v{M[s][rt][e], M[s][rt][e + 1], M[s][rt][e + 2], M[s][rt][e + 3]}, &dst[e / 4]);
+      }
+    }
+  };
 
   // gates of 64 consecutive history chunks, lane j holds chunk jb*64 + j (0 when skipped)
   float greg[SPW];
@@ -370,6 +388,7 @@ __global__ __launch_bounds__(NW * 64, 1) void compose_bf16_kernel(RouteArgs a) {
 #pragma unroll
     for (int s = 0; s < SPW; ++s)
       if (qi[s] == j + 1 && qi[s] < N) write_state(s);
+    if (a.ckpt && (j + 1) % a.ckpt_K == 0) keep_state(j + 1);
     if (more) {
       wait_copies();
       __syncthreads();

@@ -12,26 +12,32 @@
 //     lambda_{j-1} = lambda_j + g (At_j - I)^T lambda_j,
 // and dS0 sums the final lambda of every chain.  Skipped pairs pass lambda through.
 //
-// Passes (one chain per workgroup in the first two, one wave per 32 state columns):
+// Memory: the sums over the query chunks in pass 3 need, per pair (i, j), the state in front
+// of the step and g lambda_j, so the history steps are cut into segments of K consecutive
+// steps and run one segment at a time, last to first.  A segment's pairs are at most
+// K (N - 1) per (b, h) instead of N (N - 1) / 2; every chain's state at each segment start
+// comes from a checkpoint kept by one forward replay, and each chain's lambda is carried from
+// one segment to the one before it.  With K = N there is one segment and no checkpoint.
+//
+// Passes (one chain per workgroup in 1 and 2, one wave per 32 state columns):
 //   0. prep_bwd_kernel writes (At_j - I) and its transpose with every 16-wide k block in the
 //      order the MFMA fragments read it (one 16-byte load per fragment), and Bc_j in the
-//      accumulator's lane order;
-//   1. compose_save_kernel runs every chain forward (one chain per workgroup; the step's
-//      (At_j - I) staged in LDS and shared by the column waves, the next one loaded while
-//      the current one is multiplied): per active step it forms
-//      D_j = (At_j - I) M_{j-1} + Bc_j on the matrix cores, stores M_{j-1} (row-major, for
-//      pass 3) and D_j (in the accumulator's lane order, for pass 2), and sets M += g D_j;
-//   2. compose_adjoint_kernel runs every chain backward: per active step it stores
-//      g lambda_j, takes the gate gradient <lambda_j, D_j> (per wave, summed over its 32
-//      columns) and updates lambda += (At_j - I)^T (g lambda) on the matrix cores;
-//   3. compose_grad_reduce_kernel, one workgroup per history chunk j, sums over the query
-//      chunks i > j: dAt_j = sum_i (g lambda)_i M_i^T on the matrix cores, dBc_j = sum_i
-//      (g lambda)_i, and the gate gradients of column j;
+//      accumulator's lane order; with more than one segment compose_replay_kernel<.., true>
+//      then runs every chain forward and keeps its state at each segment boundary it crosses;
+//   per segment [j0, j1), last first:
+//   1. compose_replay_kernel<.., false> runs each chain's steps of the segment from its
+//      checkpoint (one chain per workgroup; the step's (At_j - I) staged in LDS and shared by
+//      the column waves, the next one loaded while the current one is multiplied): per
+//      active step it forms D_j = (At_j - I) M_{j-1} + Bc_j on the matrix cores, stores
+//      M_{j-1} (row-major, for pass 3) and D_j (in the accumulator's lane order, for pass 2),
+//      and sets M += g D_j;
+//   2. compose_adjoint_kernel runs each chain's steps of the segment backward: per active
+//      step it stores g lambda_j, takes the gate gradient <lambda_j, D_j> (per wave, summed
+//      over its 32 columns) and updates lambda += (At_j - I)^T (g lambda) on the matrix cores;
+//   3. compose_grad_reduce_kernel, one workgroup per step j of the segment, sums over the
+//      query chunks i > j: dAt_j = sum_i (g lambda)_i M_i^T on the matrix cores, dBc_j =
+//      sum_i (g lambda)_i, and the gate gradients of column j;
 //   4. chain_sum_kernel: dS0 = sum over chains of the final lambda.
-// Passes 1 and 2 take the chains i0 <= i < i1 of one group, and pass 3 sums over that
-// group's chains only (adding to the sums of the earlier groups), so a caller with less
-// memory than every pair's states runs the chains in several groups, each group's pairs
-// stored in the same slots.
 // Every reduction runs in a fixed order (no atomics): results are deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -43,13 +49,15 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int64_t pair_index(int i, int j) { return (int64_t)i * (i - 1) / 2 + j; }
-
-// Slot of pair (i, j) among the pairs of the chains i0 <= i < i1 (per (b, h)), and their count.
+// Slot of pair (i, j), j in the segment [j0, j1) (per (b, h)): the pairs of the chains before
+// chain i come first, chain i' > j0 having min(j1, i') - j0 of them.
 __device__ __forceinline__ int64_t pair_slot(const ComposeBwdArgs& a, int i, int j) {
-  return pair_index(i, j) - pair_index(a.i0, 0);
+  const int64_t m = (int64_t)i - 1 - a.j0, L = a.j1 - a.j0;
+  const int64_t base = m <= 0 ? 0 : (i - 1 <= a.j1 ? m * (m + 1) / 2 : L * (L + 1) / 2 + ((int64_t)i - 1 - a.j1) * L);
+  return base + (j - a.j0);
 }
-__device__ __forceinline__ int64_t group_pairs(const ComposeBwdArgs& a) { return pair_index(a.i1, 0) - pair_index(a.i0, 0); }
+
+__device__ __forceinline__ int64_t ckpt_index(const ComposeBwdArgs& a, int b, int i) { return ckpt_slot(a.N, a.K, b, i); }
 
 // Offset of element e of lane `lane` in the accumulator-lane-order image of one dk x dv
 // matrix: [dv/32 column tiles][dk/32 row tiles][64 lanes][16].
@@ -198,11 +206,13 @@ __device__ __forceinline__ void stage_store(const u32x4 (&r)[NC], T* sA, int tid
   }
 }
 
-// Pass 1: forward over every chain, storing M_{j-1} and D_j of each active step.  One
-// chain per workgroup: (At_j - I) of the next active step is loaded into registers while
-// the current one is multiplied from LDS, then written to the other LDS buffer.
-template <class T, int DK, int DV>
-__global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdArgs a) {
+// Passes 0 and 1: forward over each chain.  CK: every step of the chain, keeping the state in
+// front of each segment boundary it crosses; else the steps of the current segment, from the
+// chain's checkpoint, storing M_{j-1} and D_j of each active step.  One chain per workgroup:
+// (At_j - I) of the next active step is loaded into registers while the current one is
+// multiplied from LDS, then written to the other LDS buffer.
+template <class T, int DK, int DV, bool CK>
+__global__ __launch_bounds__(DV / 32 * 64) void compose_replay_kernel(ComposeBwdArgs a) {
   using MM = Mma<T>;
   constexpr int NRT = DK / 32, NKS = DK / MM::KS, KPT = 32 / MM::KS, NTH = DV / 32 * 64;
   __shared__ __attribute__((aligned(16))) char smem[2 * StagedA<T, DK>::BYTES];
@@ -210,56 +220,74 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
   const int tid = threadIdx.x, lane = tid & 63, ct = tid >> 6, hh = lane >> 5, c32 = lane & 31;
   const int64_t BH = a.B * a.H;
   const int64_t bh = blockIdx.x % BH;
-  const int i = a.i1 - 1 - (int)(blockIdx.x / BH);  // longest chains first
   const int N = a.N;
+  const int i = N - 1 - (int)(blockIdx.x / BH);  // longest chains first
+  const int jb = CK ? 0 : a.j0, je = CK ? i : (a.j1 < i ? a.j1 : i);  // the steps [jb, je)
   const int col = ct * 32 + c32;
-  const int64_t P = group_pairs(a);
-  T* Ms = reinterpret_cast<T*>(a.Msave) + bh * P * DK * DV;
-  T* Ds = reinterpret_cast<T*>(a.Dsave) + bh * P * DK * DV;
+  T* Ms = reinterpret_cast<T*>(a.Msave) + bh * a.slots * DK * DV;
+  T* Ds = reinterpret_cast<T*>(a.Dsave) + bh * a.slots * DK * DV;
+  float* Ck = a.Ckpt + bh * a.nck * DK * DV;
   const T* Apb = reinterpret_cast<const T*>(a.Ap) + bh * N * (int64_t)DK * DK;
   const T* Blb = reinterpret_cast<const T*>(a.Bl) + bh * N * (int64_t)DK * DV;
   const uint8_t* mrow = a.mask + (bh * N + i) * (int64_t)N;
   const float* grow = a.gates + (bh * N + i) * (int64_t)N;
 
   f32x16 M[NRT];
+  if (jb > 0) {  // from the chain's checkpoint at the segment start
+    const float* ck = Ck + ckpt_index(a, jb / a.K, i) * DK * DV;
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
+    for (int rt = 0; rt < NRT; ++rt) M[rt] = load16<float>(ck + lane_off<DK>(ct, rt, lane));
+  } else {
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      M[rt][e] = a.S0 ? a.S0[bh * DK * DV + (int64_t)(rt * 32 + acc_row(e, hh)) * DV + col] : 0.f;
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        M[rt][e] = a.S0 ? a.S0[bh * DK * DV + (int64_t)(rt * 32 + acc_row(e, hh)) * DV + col] : 0.f;
+  }
+  // CK: the state in front of boundaries nb K .. up to step `upto` (boundaries below i only)
+  int nb = 1;
+  auto keep = [&](int upto) {
+    for (; nb * a.K <= upto && nb * a.K < i; ++nb) {
+      float* ck = Ck + ckpt_index(a, nb, i) * DK * DV;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) store16<float>(ck + lane_off<DK>(ct, rt, lane), M[rt], 1.f);
+    }
+  };
 
   auto next_active = [&](int j) {
-    while (j < i && !mrow[j]) ++j;
+    while (j < je && !mrow[j]) ++j;
     return j;
   };
   u32x4 pre[AStage<T, DK, NTH>::NCP];
-  int j = next_active(0);
+  int j = next_active(jb);
   int buf = 0;
-  if (j < i) {
+  if (j < je) {
     stage_load<T, DK, NTH>(pre, Apb + (int64_t)j * DK * DK, tid);
     stage_store<T, DK, NTH>(pre, sbuf(0), tid);
     __syncthreads();
   }
-  while (j < i) {
+  while (j < je) {
     const int jn = next_active(j + 1);
-    if (jn < i) stage_load<T, DK, NTH>(pre, Apb + (int64_t)jn * DK * DK, tid);
+    if (jn < je) stage_load<T, DK, NTH>(pre, Apb + (int64_t)jn * DK * DK, tid);
     const float g = grow[j];
-    const int64_t p = pair_slot(a, i, j);
-    // the opaque lane offset keeps the compiler from holding 64 store addresses in
-    // registers across the whole chain
-    int lofs = hh * 4 * DV + col;
-    asm volatile("" : "+v"(lofs));
-    T* dst = Ms + p * DK * DV + lofs;
+    if constexpr (CK) {
+      keep(j);
+    } else {
+      // the opaque lane offset keeps the compiler from holding 64 store addresses in
+      // registers across the whole chain
+      int lofs = hh * 4 * DV + col;
+      asm volatile("" : "+v"(lofs));
+      T* dst = Ms + pair_slot(a, i, j) * DK * DV + lofs;
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+      for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) dst[(rt * 32 + (e >> 2) * 8 + (e & 3)) * DV] = from_f<T>(M[rt][e]);
+        for (int e = 0; e < 16; ++e) dst[(rt * 32 + (e >> 2) * 8 + (e & 3)) * DV] = from_f<T>(M[rt][e]);
+    }
     typename MM::Frag bf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) bf[ks] = MM::from_acc(M[ks / KPT], ks, 1.f);
     const T* sA = sbuf(buf);
     const T* Bl = Blb + (int64_t)j * DK * DV;
-    T* dd = Ds + p * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       f32x16 D = zero16();
@@ -268,16 +296,17 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
       const f32x16 b = load16<T>(Bl + lane_off<DK>(ct, rt, lane));
 #pragma unroll
       for (int e = 0; e < 16; ++e) D[e] += b[e];
-      store16<T>(dd + lane_off<DK>(ct, rt, lane), D, 1.f);
+      if constexpr (!CK) store16<T>(Ds + pair_slot(a, i, j) * DK * DV + lane_off<DK>(ct, rt, lane), D, 1.f);
 #pragma unroll
       for (int e = 0; e < 16; ++e) M[rt][e] = fmaf(g, D[e], M[rt][e]);
     }
-    if (jn < i) stage_store<T, DK, NTH>(pre, sbuf(buf ^ 1), tid);
+    if (jn < je) stage_store<T, DK, NTH>(pre, sbuf(buf ^ 1), tid);
     __syncthreads();
     buf ^= 1;
     j = jn;
   }
-  if (a.S_routed) {
+  if constexpr (CK) keep(i - 1);
+  if (a.S_routed && je == i) {
     float* so = a.S_routed + (bh * N + i) * (int64_t)DK * DV;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
@@ -286,10 +315,10 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_save_kernel(ComposeBwdAr
   }
 }
 
-// Pass 2: backward over every chain, staged like pass 1 with (At_j - I)^T.  D_j of the next
-// active step is loaded into registers (raw, in the storage type) during the current one,
-// so the gate gradient <lambda_j, D_j> can be taken before the products and lambda can be
-// updated in place.
+// Pass 2: backward over each chain's steps of the segment, staged like pass 1 with
+// (At_j - I)^T.  D_j of the next active step is loaded into registers (raw, in the storage
+// type) during the current one, so the gate gradient <lambda_j, D_j> can be taken before the
+// products and lambda can be updated in place.
 template <class T, int DK, int DV>
 __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBwdArgs a) {
   using MM = Mma<T>;
@@ -300,25 +329,28 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
   const int tid = threadIdx.x, lane = tid & 63, ct = tid >> 6, hh = lane >> 5, c32 = lane & 31;
   const int64_t BH = a.B * a.H;
   const int64_t bh = blockIdx.x % BH;
-  const int i = a.i1 - 1 - (int)(blockIdx.x / BH);
   const int N = a.N;
+  const int i = N - 1 - (int)(blockIdx.x / BH);
+  const int jt = a.j1 < i ? a.j1 : i;  // the chain's steps [j0, jt) in this segment
   const int col = ct * 32 + c32;
-  const int64_t P = group_pairs(a);
   const T* ATb = reinterpret_cast<const T*>(a.ApT) + bh * N * (int64_t)DK * DK;
-  const T* Ds = reinterpret_cast<const T*>(a.Dsave) + bh * P * DK * DV;
-  T* Ls = reinterpret_cast<T*>(a.Lsave) + bh * P * DK * DV;
+  const T* Ds = reinterpret_cast<const T*>(a.Dsave) + bh * a.slots * DK * DV;
+  T* Ls = reinterpret_cast<T*>(a.Lsave) + bh * a.slots * DK * DV;
   const uint8_t* mrow = a.mask + (bh * N + i) * (int64_t)N;
   const float* grow = a.gates + (bh * N + i) * (int64_t)N;
 
+  // lambda after the segment's last step of the chain: the upstream gradient in the segment
+  // that holds the chain's last step, else as the later segment left it
   f32x16 lam[NRT];
-  const float* dS = a.dS + (bh * N + i) * (int64_t)DK * DV;
+  float* le = a.lam_end + (bh * N + i) * (int64_t)DK * DV;
+  const float* l0 = i <= a.j1 ? a.dS + (bh * N + i) * (int64_t)DK * DV : le;
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) lam[rt][e] = dS[(int64_t)(rt * 32 + acc_row(e, hh)) * DV + col];
+    for (int e = 0; e < 16; ++e) lam[rt][e] = l0[(int64_t)(rt * 32 + acc_row(e, hh)) * DV + col];
 
   auto prev_active = [&](int j) {
-    while (j >= 0 && !mrow[j]) --j;
+    while (j >= a.j0 && !mrow[j]) --j;
     return j;
   };
   u32x4 pre[AStage<T, DK, NTH>::NCP];
@@ -330,17 +362,17 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
 #pragma unroll
       for (int c = 0; c < DPC; ++c) dst[rt][c] = reinterpret_cast<const u32x4*>(dd + lane_off<DK>(ct, rt, lane))[c];
   };
-  int j = prev_active(i - 1);
+  int j = prev_active(jt - 1);
   int buf = 0;
-  if (j >= 0) {
+  if (j >= a.j0) {
     stage_load<T, DK, NTH>(pre, ATb + (int64_t)j * DK * DK, tid);
     load_d(dcur, j);
     stage_store<T, DK, NTH>(pre, sbuf(0), tid);
     __syncthreads();
   }
-  while (j >= 0) {
+  while (j >= a.j0) {
     const int jn = prev_active(j - 1);
-    if (jn >= 0) {
+    if (jn >= a.j0) {
       stage_load<T, DK, NTH>(pre, ATb + (int64_t)jn * DK * DK, tid);
       load_d(dnext, jn);
     }
@@ -371,7 +403,7 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
       for (int ks = 0; ks < NKS; ++ks) lam[rt] = MM::mma(lds_frag<T, DK>(sA, rt, ks, hh, c32), bf[ks], lam[rt]);
     part = wave_sum(part);
     if (lane == 0) a.dgp[((bh * N + i) * N + j) * NCT + ct] = part;
-    if (jn >= 0) {
+    if (jn >= a.j0) {
       stage_store<T, DK, NTH>(pre, sbuf(buf ^ 1), tid);
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
@@ -382,14 +414,13 @@ __global__ __launch_bounds__(DV / 32 * 64) void compose_adjoint_kernel(ComposeBw
     buf ^= 1;
     j = jn;
   }
-  float* le = a.lam_end + (bh * N + i) * (int64_t)DK * DV;
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) le[(int64_t)(rt * 32 + acc_row(e, hh)) * DV + col] = lam[rt][e];
 }
 
-// Pass 3: per history chunk j, the sums over the query chunks that keep it.  Each active
+// Pass 3: per history chunk j of the segment, the sums over the query chunks that keep it.  Each active
 // chain's g lambda and M (row-major) are staged in padded LDS rows shared by the four
 // waves; the next active chain's are loaded into registers while the current ones are
 // multiplied, and dBc_j accumulates straight from those registers.
@@ -406,14 +437,13 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, c32 = lane & 31;
   const int64_t BH = a.B * a.H;
   const int64_t bh = blockIdx.x % BH;
-  const int j = (int)(blockIdx.x / BH);  // most query chunks first
+  const int j = a.j0 + (int)(blockIdx.x / BH);  // most query chunks first
   const int N = a.N;
-  const int64_t P = group_pairs(a);
-  const T* Ms = reinterpret_cast<const T*>(a.Msave) + bh * P * DK * DV;
-  const T* Ls = reinterpret_cast<const T*>(a.Lsave) + bh * P * DK * DV;
+  const T* Ms = reinterpret_cast<const T*>(a.Msave) + bh * a.slots * DK * DV;
+  const T* Ls = reinterpret_cast<const T*>(a.Lsave) + bh * a.slots * DK * DV;
   auto active = [&](int i) { return a.mask[(bh * N + i) * (int64_t)N + j] != 0; };
-  auto next_active = [&](int i) {  // the group's chains only
-    while (i < a.i1 && !active(i)) ++i;
+  auto next_active = [&](int i) {
+    while (i < N && !active(i)) ++i;
     return i;
   };
 
@@ -438,10 +468,9 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
     }
   };
 
-  int i = next_active(j + 1 > a.i0 ? j + 1 : a.i0);
-  const bool any = i < a.i1;
-  if (i < a.i1) prefetch(i);
-  while (i < a.i1) {
+  int i = next_active(j + 1);
+  if (i < N) prefetch(i);
+  while (i < N) {
     __syncthreads();  // the previous chain's LDS reads are done
 #pragma unroll
     for (int c = 0; c < NPC; ++c) {
@@ -454,7 +483,7 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
     }
     __syncthreads();
     const int in = next_active(i + 1);
-    if (in < a.i1) prefetch(in);
+    if (in < N) prefetch(in);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int t = w * TPW + u, rt = t / NRT, st = t % NRT;
@@ -465,29 +494,22 @@ __global__ __launch_bounds__(256) void compose_grad_reduce_kernel(ComposeBwdArgs
     }
     i = in;
   }
-  // the first group writes dAt_j and dBc_j, later groups add theirs (if they have a chain)
-  if (!a.accumulate || any) {
-    float* dA = a.dAt + (bh * N + j) * (int64_t)DK * DK;
+  float* dA = a.dAt + (bh * N + j) * (int64_t)DK * DK;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int t = w * TPW + u, rt = t / NRT, st = t % NRT;
+  for (int u = 0; u < TPW; ++u) {
+    const int t = w * TPW + u, rt = t / NRT, st = t % NRT;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float* d = dA + (int64_t)(rt * 32 + acc_row(e, hh)) * DK + st * 32 + c32;
-        *d = a.accumulate ? *d + acc[u][e] : acc[u][e];
-      }
-    }
-    float* dB = a.dBc + (bh * N + j) * (int64_t)DK * DV;
-#pragma unroll
-    for (int c = 0; c < NPC; ++c) {
-      const int64_t e0 = (int64_t)(tid + c * 256) * EPP;
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) dB[e0 + e] = a.accumulate ? dB[e0 + e] + sb[c][e] : sb[c][e];
-    }
+    for (int e = 0; e < 16; ++e) dA[(int64_t)(rt * 32 + acc_row(e, hh)) * DK + st * 32 + c32] = acc[u][e];
   }
-  // gate gradients of column j in the group's rows (zero for skipped, diagonal and future
-  // pairs)
-  for (int ii = a.i0 + tid; ii < a.i1; ii += 256) {
+  float* dB = a.dBc + (bh * N + j) * (int64_t)DK * DV;
+#pragma unroll
+  for (int c = 0; c < NPC; ++c) {
+    const int64_t e0 = (int64_t)(tid + c * 256) * EPP;
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) dB[e0 + e] = sb[c][e];
+  }
+  // gate gradients of column j (zero for skipped, diagonal and future pairs)
+  for (int ii = tid; ii < N; ii += 256) {
     const int64_t o = (bh * N + ii) * N + j;
     float sg = 0.f;
     if (ii > j && a.mask[o]) {
@@ -512,33 +534,44 @@ __global__ __launch_bounds__(256) void chain_sum_kernel(const float* __restrict_
 
 template <class T, int DK, int DV>
 static hipError_t launch_compose_bwd_t(const ComposeBwdArgs& a, int stages, hipStream_t s) {
-  const int64_t BH = a.B * a.H, BHN = BH * a.N, BHG = BH * (a.i1 - a.i0);
-  if (stages & kComposeBwdSave) {
+  const int64_t BH = a.B * a.H, BHN = BH * a.N;
+  const int lo = a.j0 == 0 ? 0 : a.j0 + 1;  // the segment's chains: i > j0 (and chain 0 in the first)
+  const int64_t BHC = BH * (a.N - lo), BHJ = BH * (a.j1 - a.j0);
+  if (stages & kComposeBwdPrep) {
     TimedLaunch tl(HLA_KERNEL_BWD_SAVE, s);
-    if (a.i0 == 0) {  // the reordered maps serve every group
-      const int64_t nt = BHN * (DK / 16) * DK + BHN * (DV / 32) * (DK / 32) * 64;
-      hipLaunchKernelGGL((prep_bwd_kernel<T, DK, DV>), dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, a, BHN);
-    }
-    if (BHG > 0)
-      hipLaunchKernelGGL((compose_save_kernel<T, DK, DV>), dim3((unsigned)BHG), dim3(DV / 32 * 64), 0, s, a);
+    const int64_t nt = BHN * (DK / 16) * DK + BHN * (DV / 32) * (DK / 32) * 64;
+    hipLaunchKernelGGL((prep_bwd_kernel<T, DK, DV>), dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, a, BHN);
+    if (a.K < a.N && !a.ckpt_done)  // the checkpoints of more than one segment
+      hipLaunchKernelGGL((compose_replay_kernel<T, DK, DV, true>), dim3((unsigned)BHN), dim3(DV / 32 * 64), 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !(stages & kComposeBwdReverse)) return e;
-  {
-    TimedLaunch tl(HLA_KERNEL_BWD_ADJOINT, s);
-    if (BHG > 0)
-      hipLaunchKernelGGL((compose_adjoint_kernel<T, DK, DV>), dim3((unsigned)BHG), dim3(DV / 32 * 64), 0, s, a);
+  if (e != hipSuccess) return e;
+  if (stages & kComposeBwdSave) {
+    TimedLaunch tl(HLA_KERNEL_BWD_SAVE, s);
+    if (BHC > 0)
+      hipLaunchKernelGGL((compose_replay_kernel<T, DK, DV, false>), dim3((unsigned)BHC), dim3(DV / 32 * 64), 0, s, a);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  {
-    TimedLaunch tl(HLA_KERNEL_BWD_REDUCE, s);
-    hipLaunchKernelGGL((compose_grad_reduce_kernel<T, DK, DV>), dim3((unsigned)BHN), dim3(256), 0, s, a);
-    if (a.dS0 && a.i1 == a.N) {  // after the last group
-      const int64_t per = (int64_t)DK * DV, total = BH * per;
-      hipLaunchKernelGGL(chain_sum_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.lam_end, a.dS0,
-                         a.N, per, total);
+  if (stages & kComposeBwdReverse) {
+    {
+      TimedLaunch tl(HLA_KERNEL_BWD_ADJOINT, s);
+      if (BHC > 0)
+        hipLaunchKernelGGL((compose_adjoint_kernel<T, DK, DV>), dim3((unsigned)BHC), dim3(DV / 32 * 64), 0, s, a);
     }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    TimedLaunch tl(HLA_KERNEL_BWD_REDUCE, s);
+    if (BHJ > 0)
+      hipLaunchKernelGGL((compose_grad_reduce_kernel<T, DK, DV>), dim3((unsigned)BHJ), dim3(256), 0, s, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((stages & kComposeBwdFinish) && a.dS0) {
+    TimedLaunch tl(HLA_KERNEL_BWD_REDUCE, s);
+    const int64_t per = (int64_t)DK * DV, total = BH * per;
+    hipLaunchKernelGGL(chain_sum_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.lam_end, a.dS0,
+                       a.N, per, total);
   }
   return hipGetLastError();
 }

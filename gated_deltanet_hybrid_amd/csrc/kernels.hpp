@@ -129,7 +129,19 @@ struct RouteArgs {
   void* Bc_prep;        // workspace [B,H,N,dk,dv] bf16: Bc in the composition's accumulator order
   int64_t B, T, H, ld_T;
   int32_t N;
+  // optional (bf16 composition): every chain's state in front of each history step b ckpt_K
+  // (b >= 1) that it crosses, float32 in the accumulator's lane order, at ckpt_slot() of
+  // [B,H,ckpt_nck,dk,dv] (the composition backward's checkpoints)
+  float* ckpt;
+  int32_t ckpt_K;
+  int64_t ckpt_nck;
 };
+// Checkpoint slot (per (b, h)) of chain i at history-segment boundary b K (b >= 1, i > b K):
+// the boundaries before b hold the chains above them, N - 1 - b' K each.
+__host__ __device__ inline int64_t ckpt_slot(int32_t N, int32_t K, int b, int i) {
+  const int64_t bm = b - 1;
+  return bm * (N - 1) - (int64_t)K * bm * (bm + 1) / 2 + ((int64_t)i - (int64_t)b * K - 1);
+}
 hipError_t launch_route(const RouteArgs& a, int dtype, int dk, int dv, hipStream_t s);
 // bf16 gated composition (the routed prefill's hot loop); gates and mask must be final.
 hipError_t launch_compose_bf16(const RouteArgs& a, int dk, int dv, hipStream_t s);
@@ -198,22 +210,35 @@ struct ComposeBwdArgs {
   void* Ap;              // workspace [B,H,N,dk,dk] (dtype): At - I in the fragment order
   void* ApT;             // workspace [B,H,N,dk,dk] (dtype): (At - I)^T in the fragment order
   void* Bl;              // workspace [B,H,N,dk,dv] (dtype): Bc in the accumulator's lane order
-  // per-pair slots of the chain group's pairs ([B,H,slots,dk,dv], dtype each):
+  // per-pair slots of the pairs (i, j) whose step j lies in the current segment
+  // ([B,H,slots,dk,dv], dtype each):
   void* Msave;           // M_{j-1} of pair (i, j)
   void* Dsave;           // D_j of pair (i, j), lane order
   void* Lsave;           // g lambda_j of pair (i, j)
+  float* Ckpt;           // workspace [B,H,nck,dk,dv] float32, lane order: every chain's state in
+                         // front of each segment boundary it crosses
   float* dgp;            // workspace [B,H,N,N,dv/32]: per-wave gate-gradient parts
-  float* lam_end;        // workspace [B,H,N,dk,dv]: final lambda of every chain
+  float* lam_end;        // workspace [B,H,N,dk,dv]: lambda of every chain, carried from one
+                         // segment to the one before it (the final lambda at the end)
   int64_t B, H;
   int32_t N;
-  // the group of chains (query chunks) i0 <= i < i1 this launch takes; its pairs fill the
-  // slots of Msave, Dsave and Lsave.  accumulate: add to dAt, dBc (a group after the first)
-  int32_t i0, i1, accumulate;
+  // the history steps j are cut into segments of K ([j0, j1) the current one), run last to
+  // first; slots and nck are the per-(b, h) counts of pair slots and checkpoints
+  int32_t K, j0, j1;
+  int64_t slots, nck;
+  // the checkpoints were written by the bf16 composition (ckpt of RouteArgs), so the prep
+  // stage does not replay the chains for them
+  int32_t ckpt_done;
 };
-// Backward of the gated composition (see compose_bwd.hip).  `stages`: 1 the forward replay
-// that keeps the step states (and writes S_routed when asked), 2 the adjoint sweep and the
-// sums (dAt, dBc, dgates, dS0).
-constexpr int kComposeBwdSave = 1, kComposeBwdReverse = 2;
+// Backward of the gated composition (see compose_bwd.hip), in stages the caller sequences:
+//   kComposeBwdPrep     the reordered maps, and with more than one segment the checkpoint
+//                       replay (which also writes S_routed when asked);
+//   kComposeBwdSave     the current segment's replay that keeps its step states (and with a
+//                       single segment writes S_routed when asked);
+//   kComposeBwdReverse  the current segment's adjoint sweep and its steps' sums (dAt, dBc,
+//                       dgates);
+//   kComposeBwdFinish   dS0.
+constexpr int kComposeBwdPrep = 1, kComposeBwdSave = 2, kComposeBwdReverse = 4, kComposeBwdFinish = 8;
 hipError_t launch_compose_backward(const ComposeBwdArgs& a, int dtype, int dk, int dv, int stages, hipStream_t s);
 
 struct ChunkBwdArgs {

@@ -22,7 +22,7 @@ KERNEL_BWD_SAVE, KERNEL_BWD_ADJOINT, KERNEL_BWD_REDUCE, KERNEL_BWD_CHUNK, KERNEL
 KERNEL_PREFILL = 11
 FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX, FN_WU_HANDOFF, FN_CHUNK_REPS = 0, 1, 2, 3, 4
 FN_COMPOSE_BACKWARD, FN_PREFILL_BACKWARD, FN_CHUNK_BACKWARD = 5, 6, 7
-FN_COMPOSE_BACKWARD_MIN, FN_PREFILL_BACKWARD_MIN = 8, 9  # smallest workspaces (query chunks in groups)
+FN_COMPOSE_BACKWARD_MIN, FN_PREFILL_BACKWARD_MIN = 8, 9  # smallest workspaces (history segments)
 CHUNK = 64
 MAX_CACHE_SLOTS = 1024
 REPS_SCRATCH_BYTES = 32 << 20  # fixed device scratch of chunk_reps_noalloc
@@ -460,7 +460,8 @@ def prefill_backward(q, k, v, beta, alpha, dO, tau=1e-3, gates_in=None, S0=None,
     upstream gradient dO [B, T, H, dv] float32.  Returns dict(dq, dk, dv, dbeta, dalpha,
     dS0, dgates), float32 (dS0 / dgates None unless wanted).  `ws` (uint8, device) may be
     smaller than workspace_bytes(FN_PREFILL_BACKWARD) down to FN_PREFILL_BACKWARD_MIN's size:
-    the query chunks then run in groups whose per-pair states fit."""
+    the composition backward then runs its history steps in segments replayed from
+    checkpoints."""
     d = _inputs(k, v, beta, alpha, q=q)
     B, T, H, dk, dv = d.B, d.T, d.H, d.dk, d.dv
     N = math.ceil(T / CHUNK)

@@ -345,14 +345,20 @@ hla_status_t hla_gdn2_decode(int64_t Bs, int64_t H, int32_t dk, int32_t dv, int3
  *   S_routed   out [B, H, N, dk, dv] float32 (the routed states, recomputed), or NULL.
  *   ws, ws_bytes: workspace: (At - I), its transpose and Bc reordered for the matrix
  *              cores, and slots for the state in front of an active step, (At_j - I) M
- *              + Bc_j and g lambda (dtype, dk x dv each).  With
- *              hla_workspace_bytes(HLA_FN_COMPOSE_BACKWARD) bytes every pair j < i has
- *              its slots (N (N - 1) / 2 per (b, h), so it grows as N^2) and the query
- *              chunks run in one pass.  A smaller workspace, down to
- *              hla_workspace_bytes(HLA_FN_COMPOSE_BACKWARD_MIN) (N - 1 slots: the
- *              longest chain's pairs), runs consecutive groups of query chunks whose
- *              pairs fit, as few as it can; the results agree up to the order of float32
- *              sums over the groups.
+ *              + Bc_j and g lambda (dtype, dk x dv each) of the pairs whose step j lies in
+ *              one segment of K consecutive history steps, plus float32 checkpoints of
+ *              every chain's state at each segment boundary it crosses.  The call takes
+ *              the longest segments the workspace holds and runs them last to first, each
+ *              chain's steps of a segment replayed from its checkpoint.  With
+ *              hla_workspace_bytes(HLA_FN_COMPOSE_BACKWARD) bytes K = N: one segment,
+ *              every pair j < i has its slots (N (N - 1) / 2 per (b, h), so it grows as
+ *              N^2) and there is no checkpoint.  Any size down to
+ *              hla_workspace_bytes(HLA_FN_COMPOSE_BACKWARD_MIN) (the segment length that
+ *              needs least, about K (N - 1) slots and N^2 / (2 K) checkpoints per (b, h))
+ *              works too.  float32 maps: the checkpoints come from the call's own replay
+ *              and results are bit-identical to one segment's; bf16 maps: they come from
+ *              the bf16 composition of hla_route_mix (several chains share each staged
+ *              map), whose rounding differs, and results agree to bf16 rounding.
  * Computation: bf16 (or float32) matrix-core products with float32 accumulation; sums in a
  * fixed order (deterministic).
  * Errors: HLA_ERR_NULL_ARG, HLA_ERR_BAD_SHAPE, HLA_ERR_BAD_DTYPE, HLA_ERR_ALIGN,
@@ -414,9 +420,10 @@ hla_status_t hla_chunk_backward(const hla_dims_t* d, const void* q, const void* 
  *   dS0 [B, H, dk, dv] float32 out or NULL;  dgates [B, H, N, N] float32 out or NULL.
  *   ws, ws_bytes: workspace; it holds the composition backward's per-pair states.  With
  *              hla_workspace_bytes(HLA_FN_PREFILL_BACKWARD) bytes (growing as N^2 dk dv
- *              per (b, h)) all query chunks run in one pass; any size down to
- *              hla_workspace_bytes(HLA_FN_PREFILL_BACKWARD_MIN) runs them in groups, as
- *              for hla_compose_backward.
+ *              per (b, h)) every chunk pair has its slots; any size down to
+ *              hla_workspace_bytes(HLA_FN_PREFILL_BACKWARD_MIN) runs the composition's
+ *              history steps in segments replayed from checkpoints, as for
+ *              hla_compose_backward.
  * Errors: HLA_ERR_UNSUPPORTED (C != 64) and as hla_gdn_prefill.
  */
 hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void* k, const void* v,

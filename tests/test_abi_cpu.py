@@ -273,17 +273,28 @@ def test_backward_workspace_sizes(lib):
         assert lib.hla_workspace_bytes(fn, ctypes.byref(dims(C=128)), 0, ctypes.byref(out)) == UNSUPPORTED
 
 
+def _comp_ws(BH, N, dk, dv, e, K):
+    """Composition-backward workspace with history segments of K steps: the reordered maps,
+    gate parts and lambdas, float32 checkpoints of every chain i > b K at each boundary b K,
+    and the first segment's pair slots (chain i holds min(K, i)) for M, D and g lambda."""
+    slots = sum(min(K, i) for i in range(1, N))
+    nck = sum(N - 1 - b * K for b in range(1, (N - 1) // K + 1) if b * K < N)
+    return (2 * _r(BH * N * dk * dk * e) + _r(BH * N * dk * dv * e) + _r(BH * N * N * (dv // 32) * 4)
+            + _r(BH * N * dk * dv * 4) + _r(BH * nck * dk * dv * 4) + 3 * _r(BH * slots * dk * dv * e))
+
+
 def test_backward_minimum_workspace(lib):
-    """The smallest workspaces hold the longest chain's pairs (N - 1 slots per (b, h)) of
-    each of the three per-pair arrays; everything else is as for one pass."""
-    for T, N in ((130, 3), (130 + 3 * 64, 6), (64, 1)):
+    """The one-pass workspace is one segment (K = N, no checkpoint); the smallest is the
+    segment length that needs least; the prefill backward adds the same fixed part to both."""
+    for T, N in ((130, 3), (130 + 3 * 64, 6), (64, 1), (40 * 64, 40)):
         d = dims(B=2, T=T, H=3, dk=128, dv=64, dtype=1)
-        BH, P_ = 6, N * (N - 1) // 2
-        slot = BH * 128 * 64 * 2
         full, mn = hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD, d), hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD_MIN, d)
-        assert full - mn == 3 * slot * (P_ - max(N - 1, 0))
+        assert full == _comp_ws(6, N, 128, 64, 2, N)
+        assert mn == min(_comp_ws(6, N, 128, 64, 2, K) for K in range(1, N + 1))
         pf, pm = hla.workspace_bytes(hla.FN_PREFILL_BACKWARD, d), hla.workspace_bytes(hla.FN_PREFILL_BACKWARD_MIN, d)
         assert pf - pm == full - mn
+    # at 40 chunks the segments need far less than every pair's slots
+    assert mn < full / 2
 
 
 def test_compose_backward_validation(lib):
@@ -298,7 +309,7 @@ def test_compose_backward_validation(lib):
         assert f(ctypes.byref(d), *args, P, need, None) == NULL_ARG, i
     args = [P] * 11
     mn = hla.workspace_bytes(hla.FN_COMPOSE_BACKWARD_MIN, d)
-    assert mn < need  # N = 4 chunks: 3 slots per (b, h) instead of 6
+    assert mn < need  # N = 4 chunks: segments of one step
     assert f(ctypes.byref(d), *args, P, mn - 1, None) == WORKSPACE
     assert f(ctypes.byref(d), *args, None, 0, None) == WORKSPACE
     bad = list(args)
