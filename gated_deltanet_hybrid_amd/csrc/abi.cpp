@@ -459,7 +459,7 @@ static hla_status_t reps_args(const hla_dims_t* d, const void* k, int32_t window
   hla_status_t st = check_dims(d);
   if (st != HLA_OK) return st;
   if (!k || !Wq || !Wk || !Wv || !Wp || !reps) return HLA_ERR_NULL_ARG;
-  if (window != 8 && window != 16 && window != 32) return HLA_ERR_BAD_SHAPE;
+  if (window != 8 && window != 16 && window != 32 && window != 64) return HLA_ERR_BAD_SHAPE;
   const int64_t wsz = (int64_t)d->dk * d->dk;
   if (w_hstride != 0 && w_hstride < wsz) return HLA_ERR_BAD_SHAPE;
   if ((w_hstride * dtype_bytes(d->dtype)) % 16 != 0) return HLA_ERR_ALIGN;

@@ -58,8 +58,8 @@ __global__ __launch_bounds__(kPoolWaves * 64) void reps_pool_kernel(RepsArgs a) 
   constexpr int NKS = DK / MM::KS;         // k-steps over the features
   constexpr int NKT = 32 / MM::KS;         // k-steps over the 32 tokens of a tile
   constexpr int TPK = 32 / MM::KS;         // k-steps per 32-row accumulator tile
-  constexpr int NWT = 32 / WIN;            // windows per tile
-  static_assert(32 % WIN == 0, "window divides the 32-token tile");
+  constexpr int NWT = WIN <= 32 ? 32 / WIN : 1;  // windows per 32-token tile
+  static_assert(32 % WIN == 0 || WIN == 64, "window divides the 32-token tile, or spans two");
   __shared__ __attribute__((aligned(16))) T sW[STAGE ? 3 * DK * PW : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, c32 = lane & 31;
@@ -90,6 +90,122 @@ __global__ __launch_bounds__(kPoolWaves * 64) void reps_pool_kernel(RepsArgs a) 
     else return MM::load_plain(wsrc(m) + (int64_t)row * DK, ks, hh);
   };
   const float qscale = 1.f / sqrtf((float)DK);
+
+  if constexpr (WIN == 64) {
+    // One wavefront per 64-token window: two 32-token tiles a (keys) and b (queries).
+    // S^T_ab = K_a Q_b^T; the softmax of query column t runs over the rows of S^T_0b and
+    // S^T_1b (and the partner lane half); O_b = sum_a P_ab V_a, and the window mean is the
+    // sum over the rows of O_0 and O_1 over the valid tokens.
+    const int64_t nwin = (int64_t)a.N * (a.C / 64);
+    for (int64_t tw = (int64_t)grp * kPoolWaves + w; tw < nwin; tw += (int64_t)a.groups * kPoolWaves) {
+      const int64_t t0 = tw * 64;
+      const int64_t cend = ((t0 / a.C) + 1) * a.C < a.T ? ((t0 / a.C) + 1) * a.C : a.T;
+      const int nv = (int)(cend - t0 < 0 ? 0 : (cend - t0 < 64 ? cend - t0 : 64));  // valid tokens
+      float* prow = a.pooled + (bh * nrows + tw) * DK;
+      if (nv == 0) {
+        for (int i = lane; i < DK; i += 64) prow[i] = 0.f;
+        continue;
+      }
+      // X fragments of tile a: lane column = token 32 a + c32 (zero beyond the valid tokens).
+      // Each use loads them again (from L1 / L2): the opaque token keeps the compiler from
+      // holding both tiles in registers across the whole window.
+      auto load_x = [&](int at, typename MM::Frag (&xf)[NKS]) {
+        int tok = 32 * at + c32;
+        asm volatile("" : "+v"(tok));
+        const T* xr = reinterpret_cast<const T*>(a.k) + ((b * a.ld_T + t0 + (tok < nv ? tok : 0)) * a.H + h) * DK;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          xf[ks] = MM::load_plain(xr, ks, hh);
+          if (tok >= nv) xf[ks] = typename MM::Frag{};
+        }
+      };
+      // W X_a^T [feature][token] as operand fragments over the features (m: 0 = Wq, 1 = Wk)
+      auto proj = [&](int m, const typename MM::Frag (&xf)[NKS], typename MM::Frag (&out)[NKS], float scale) {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+          f32x16 acc = zero16();
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) acc = MM::mma(wfrag(m, ft * 32 + c32, ks), xf[ks], acc);
+#pragma unroll
+          for (int j = 0; j < TPK; ++j) out[ft * TPK + j] = MM::from_acc(acc, ft * TPK + j, scale);
+        }
+      };
+      typename MM::Frag pf[2][2][NKT];  // [a][b]: P_ab as A fragments over the keys of tile a
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt) {
+        // S^T_ab for both key tiles (K_a formed again for each query tile: fewer registers)
+        f32x16 p[2];
+        {
+          typename MM::Frag qf[NKS];
+          {
+            typename MM::Frag xf[NKS];
+            load_x(bt, xf);
+            proj(0, xf, qf, qscale);
+          }
+#pragma unroll
+          for (int at = 0; at < 2; ++at) {
+            typename MM::Frag xf[NKS], kf[NKS];
+            load_x(at, xf);
+            proj(1, xf, kf, 1.f);
+            p[at] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) p[at] = MM::mma(kf[ks], qf[ks], p[at]);
+          }
+        }
+        // softmax of query column t over the valid keys s of both key tiles
+        float mx = -INFINITY;
+#pragma unroll
+        for (int at = 0; at < 2; ++at)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (32 * at + acc_row(e, hh) < nv) mx = fmaxf(mx, p[at][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float sum = 0.f;
+#pragma unroll
+        for (int at = 0; at < 2; ++at)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            p[at][e] = 32 * at + acc_row(e, hh) < nv ? __expf(p[at][e] - mx) : 0.f;
+            sum += p[at][e];
+          }
+        sum += __shfl_xor(sum, 32, 64);
+        const float inv = sum > 0.f ? 1.f / sum : 0.f;
+#pragma unroll
+        for (int at = 0; at < 2; ++at) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) p[at][e] *= inv;
+#pragma unroll
+          for (int ks = 0; ks < NKT; ++ks) pf[at][bt][ks] = MM::from_acc(p[at], ks, 1.f);
+        }
+      }
+      // V_a per feature tile, O_b = sum_a P_ab V_a, then the mean over the valid query rows
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        f32x16 o[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int at = 0; at < 2; ++at) {
+          typename MM::Frag xf[NKS];
+          load_x(at, xf);
+          f32x16 v = zero16();
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) v = MM::mma(xf[ks], wfrag(2, ft * 32 + c32, ks), v);
+#pragma unroll
+          for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+            for (int ks = 0; ks < NKT; ++ks) o[bt] = MM::mma(pf[at][bt][ks], MM::from_acc(v, ks, 1.f), o[bt]);
+        }
+        float sacc = 0.f;
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (32 * bt + acc_row(e, hh) < nv) sacc += o[bt][e];
+        sacc += __shfl_xor(sacc, 32, 64);
+        if (hh == 0) prow[ft * 32 + c32] = sacc / (float)nv;
+      }
+    }
+    return;
+  }
 
   for (int64_t tt = (int64_t)grp * kPoolWaves + w; tt < ntiles; tt += (int64_t)a.groups * kPoolWaves) {
     const int64_t t0 = tt * 32;
@@ -290,6 +406,7 @@ static hipError_t launch_reps_t(RepsArgs a, hipStream_t s) {
     switch (a.window) {
       case 8: hipLaunchKernelGGL((reps_pool_kernel<T, DK, 8>), grid, block, 0, s, a); break;
       case 16: hipLaunchKernelGGL((reps_pool_kernel<T, DK, 16>), grid, block, 0, s, a); break;
+      case 64: hipLaunchKernelGGL((reps_pool_kernel<T, DK, 64>), grid, block, 0, s, a); break;
       default: hipLaunchKernelGGL((reps_pool_kernel<T, DK, 32>), grid, block, 0, s, a); break;
     }
   }

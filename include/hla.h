@@ -201,7 +201,7 @@ hla_status_t hla_gdn2_prefill(const hla_dims_t* d, const void* q, const void* k,
  * (Wr q) . (Wp pooled).  A window cut by the end of the sequence pools the tokens it has;
  * a window with no tokens gets a zero row.
  *   k      : [B, ld_T, H, dk] keys (dims d; dv is not used).
- *   window : 8, 16 or 32 tokens (C / window representatives per chunk).
+ *   window : 8, 16, 32 or 64 tokens (C / window representatives per chunk).
  *   Wq, Wk, Wv, Wp : [dk, dk] weights in the dims' dtype, row-major [out, in] (a row
  *           vector x maps to W x); head h's matrices start w_hstride elements after head
  *           h-1's (w_hstride = 0: one set shared by all heads; else >= dk*dk).

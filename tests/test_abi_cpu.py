@@ -195,7 +195,7 @@ def test_chunk_reps_validation(lib):
     assert cr(ctypes.byref(d), None, 32, *W, None, 0, P, P, need, None) == NULL_ARG
     assert cr(ctypes.byref(d), P, 32, P, P, None, P, None, 0, P, P, need, None) == NULL_ARG
     assert cr(ctypes.byref(d), P, 32, *W, None, 0, None, P, need, None) == NULL_ARG
-    for bad_window in (0, 4, 24, 64):
+    for bad_window in (0, 4, 24, 48, 128):
         assert cr(ctypes.byref(d), P, bad_window, *W, None, 0, P, P, need, None) == BAD_SHAPE
     assert cr(ctypes.byref(d), P, 32, *W, None, 100, P, P, need, None) == BAD_SHAPE  # overlapping heads
     assert cr(ctypes.byref(d), P, 32, *W, None, 128 * 128 + 4, P, P, need, None) == ALIGN  # 8-byte head step

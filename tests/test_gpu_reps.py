@@ -30,6 +30,9 @@ CASES = [
     ("bf16", 128, 32, 64, 33, False, False),
     ("f32", 64, 32, 64, 200, False, True),
     ("f32", 128, 16, 64, 130, True, True),
+    ("bf16", 128, 64, 128, 3 * 128 - 40, False, True),
+    ("bf16", 64, 64, 64, 4 * 64 - 23, True, False),
+    ("f32", 128, 64, 64, 2 * 64 + 9, False, True),
 ]
 IDS = [f"{c[0]}-dk{c[1]}-w{c[2]}-C{c[3]}-T{c[4]}{'-shared' if c[5] else ''}{'-Wr' if c[6] else ''}" for c in CASES]
 
