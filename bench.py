@@ -529,13 +529,22 @@ def bench_gdn2_routed(args, torch, hla, inputs, x):
     maps_b, outs_b = bytes_gdn2_passes(W.B, W.T, W.H, W.dk, W.dv, N)
     chunk_s = ch_ms / ch_n / 1e3 * 2  # two chunk passes per step
     ach = (maps_b + outs_b) / chunk_s / 1e9
+    # HBM bytes of the two passes from the committed counters (FETCH_SIZE + WRITE_SIZE, copy
+    # calibrated), when they were taken on the current sources
+    ks = read_counters("gdn2_routed_prefill") or {}
+    kp = [ks.get(f"gdn2_wy_kernel<{W.dk}, {W.dv}, {o}>") for o in ("false", "true")]
+    traffic = sum(k["hbm_bytes"] for k in kp) if all(k and "hbm_bytes" in k for k in kp) else None
     res = dict(workload="routed_prefill under Gated DeltaNet-2 (channel-wise decay, erase and write gates), "
                         "B=1 T=32768 H=16 d=128 C=64",
                ms_per_step=dt * 1e3, tokens_per_s=W.B * W.T / dt, compose_ms=round(cm_ms / cm_n, 4),
                chunk_passes_ms=round(chunk_s * 1e3, 4),
                chunk_roofline=dict(kernel="gdn2_wy_kernel (maps + outputs)", bound="hbm", achieved=round(ach, 1),
                                    peak=PEAK_HBM_GBS, unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4),
-                                   bytes_per_step=maps_b + outs_b, maps_bytes=maps_b, outputs_bytes=outs_b))
+                                   traffic=traffic, bytes_per_step=maps_b + outs_b, maps_bytes=maps_b,
+                                   outputs_bytes=outs_b))
+    if traffic:
+        res["chunk_roofline"].update(counter_hbm_gbs=round(traffic / chunk_s / 1e9, 1),
+                                     traffic_over_algorithmic=round(traffic / (maps_b + outs_b), 3))
     log(f"[gdn2_routed_prefill] {dt*1e3:.3f} ms/step, {W.B*W.T/dt/1e6:.3f} M tok/s, chunk passes "
         f"{chunk_s*1e3:.3f} ms ({ach:.0f} GB/s of algorithmic bytes), compose {cm_ms/cm_n:.3f} ms")
     del q, k, v, ga, gb, gw, At, Bc, out, o, ws
@@ -867,9 +876,10 @@ COUNTER_SOURCES = {line: ["gated_deltanet_hybrid_amd/csrc/" + f for f in files] 
     ("routed_prefill", ("chunk.hip", "route.hip", "compose.hip")),
     ("native_prefill", ("prefill.hip",)),
     ("tail_replay", ("prefill.hip",)),
-    ("decode", ("decode.hip",)))}
+    ("decode", ("decode.hip",)),
+    ("gdn2_routed_prefill", ("gdn2.hip", "route.hip", "compose.hip")))}
 CALIB_BYTES = 1 << 30
-COUNTER_LINES = ("routed_prefill", "native_prefill", "tail_replay", "decode")
+COUNTER_LINES = ("routed_prefill", "native_prefill", "tail_replay", "decode", "gdn2_routed_prefill")
 
 
 def counter_run(line, torch, hla, inputs):
@@ -884,6 +894,8 @@ def counter_run(line, torch, hla, inputs):
         bench_tail_replay(args, torch, hla, inputs, steps=2, warmup=1, full_prefix=False)
     elif line == "decode":
         bench_decode(args, torch, hla, inputs, warm=1)
+    elif line == "gdn2_routed_prefill":
+        bench_gdn2_routed(args, torch, hla, inputs, routed_inputs(inputs))
     else:
         sys.exit(f"no counter run for {line}; lines: {', '.join(COUNTER_LINES)}")
     src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")

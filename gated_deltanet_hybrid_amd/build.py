@@ -60,6 +60,40 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+# Host code only (the C ABI's argument checks, workspace sizing and launch set-up) under
+# AddressSanitizer and UndefinedBehaviorSanitizer; every flag is scoped to the host pass.
+HOST_SOURCES = ("abi.cpp", "timing.cpp")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(out: str) -> str:
+    """A copy of libhla.so whose host code is built with ASan and UBSan, linked against the
+    shared sanitizer runtime (preload it to load the library), with the device objects that
+    build_library compiled.  Returns the library's path."""
+    objs = []
+    san_dir = os.path.join(os.path.dirname(os.path.abspath(out)), "san_objs")
+    os.makedirs(san_dir, exist_ok=True)
+    for src in SOURCES:
+        if src in HOST_SOURCES:
+            obj = os.path.join(san_dir, os.path.splitext(src)[0] + ".o")
+            cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *SAN_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        else:
+            obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+            if not os.path.exists(obj):
+                raise RuntimeError(f"{obj} is missing: run build_library first")
+        objs.append(obj)
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *SAN_FLAGS, "-Xarch_host", "-shared-libsan",
+           "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     build_library(verbose=True)
     sys.exit(0)

@@ -13,7 +13,8 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhla.so")
+# HLA_LIBRARY names another build of the same library (for instance the host-sanitized one)
+_LIB_PATH = os.environ.get("HLA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhla.so")
 _lib = None
 
 HLA_F32, HLA_BF16 = 0, 1
