@@ -588,11 +588,6 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, ws_gib=None):
     d = hla.make_dims(W.B, T, W.H, T, W.dk, W.dv, hla.HLA_BF16, C)
     one_pass = hla.workspace_bytes(hla.FN_PREFILL_BACKWARD, d)
     main_bytes = one_pass if ws_gib is None else min(one_pass, int(ws_gib * 2**30))
-    # active pairs from the router's own mask (a gate gradient can underflow to zero far
-    # back in a long chain, so it does not count them)
-    At, Bc = hla.chunk_transitions(k, v, beta, alpha)
-    pairs = int(hla.route_mix(q, k, At, Bc, tau=W.tau)["active_cnt"].sum().item())
-    del At, Bc
     steps = max(3, args.steps // 4)
     names = (("bwd_chunk", hla.KERNEL_BWD_CHUNK), ("bwd_save", hla.KERNEL_BWD_SAVE),
              ("bwd_adjoint", hla.KERNEL_BWD_ADJOINT), ("bwd_reduce", hla.KERNEL_BWD_REDUCE),
@@ -620,6 +615,12 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, ws_gib=None):
         return dt_, ms_, per["bwd_adjoint"][1] // steps  # one adjoint launch per segment
 
     dt, ms, segments = measure(main_bytes)
+    # active pairs from the router's own mask (a gate gradient can underflow to zero far
+    # back in a long chain, so it does not count them); after the timed calls, so that in a
+    # kernel trace every kernel's first dispatch is the warm-up call's
+    At, Bc = hla.chunk_transitions(k, v, beta, alpha)
+    pairs = int(hla.route_mix(q, k, At, Bc, tau=W.tau)["active_cnt"].sum().item())
+    del At, Bc
     th = W.B * T * W.H
     fl_chunk = flops_chunk_bwd(th, W.dk, W.dv)
     fl_pair = flops_compose(pairs, W.dk, W.dv)
@@ -1051,8 +1052,9 @@ def counter_figures(line, kernel, avg_launch_s, flops=None, nbytes=None):
         if flops:
             out["mfma_flops_over_algorithmic"] = round(k["mfma_bf16_flops"] / flops, 3)
     if "sq_valu_mfma_busy_cycles_mean" in k and "grbm_gui_active_mean" in k:
-        # busy cycles summed over the chip's SIMDs against the kernel's GPU-active cycles on all of them
-        out["mfma_busy_frac"] = round(k["sq_valu_mfma_busy_cycles_mean"] / (k["grbm_gui_active_mean"] * 256 * 4), 4)
+        # busy cycles summed over the chip's 1024 SIMDs against the kernel's GPU-active cycles on all
+        # of them (GRBM_GUI_ACTIVE is summed over the 8 XCDs: one eighth of it is the kernel's cycles)
+        out["mfma_busy_frac"] = round(k["sq_valu_mfma_busy_cycles_mean"] / (k["grbm_gui_active_mean"] / 8 * 256 * 4), 4)
     for cn in ("sq_valu_mfma_busy_cycles_mean", "sq_busy_cycles_mean", "grbm_gui_active_mean",
                "sq_lds_bank_conflict_mean", "sq_insts_lds_mean", "sq_waves_mean"):
         if cn in k:
@@ -1060,10 +1062,13 @@ def counter_figures(line, kernel, avg_launch_s, flops=None, nbytes=None):
     return out
 
 
-def trace_summary(csv_path, skip, take, title, command):
-    """Markdown table of a rocprofv3 kernel trace: per kernel, dispatches in time order, the
-    first `skip` as warm-up and the next `take` as the timed ones."""
+def trace_summary(csv_path, skip, take, title, command, per_call=""):
+    """Markdown table of a rocprofv3 kernel trace: per kernel, calls in time order, the first
+    `skip` as warm-up and the next `take` as the timed ones.  A call is one dispatch, or m
+    consecutive dispatches for kernels listed in `per_call` as "kernel=m;..." (a kernel
+    launched once per history segment); its time is then the sum over them."""
     import csv
+    mult = dict((k, int(m)) for k, m in (e.rsplit("=", 1) for e in per_call.split(";") if e))
     per = {}
     for r in csv.DictReader(open(csv_path)):
         if "hla" not in r["Kernel_Name"]:
@@ -1072,19 +1077,27 @@ def trace_summary(csv_path, skip, take, title, command):
             (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     lines = [f"# {title}", "", "Command, on one MI355X (`<repo>` is the checkout, `<out>` an output folder):", "",
              f"    {command}", "",
-             f"Per kernel, dispatches in time order: the first {skip} are warm-up, the next {take} the timed ones "
-             "the bench line averages; durations in microseconds.", "",
-             "| kernel | timed | avg (us) | min (us) | max (us) | warm-up avg (us) | other dispatches |",
-             "|---|---|---|---|---|---|---|"]
-    for name, ds in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1][skip:skip + take])):
+             f"Per kernel, calls in time order: the first {skip} are warm-up, the next {take} the timed ones "
+             "the bench line averages; durations in microseconds."]
+    if mult:
+        lines.append("Kernels launched several times per call (once per history segment) are summed over "
+                     "the call's launches: " + ", ".join(f"`{k}` x {m}" for k, m in mult.items()) + ".")
+    lines += ["", "| kernel | timed | avg (us) | min (us) | max (us) | warm-up avg (us) | other dispatches |",
+              "|---|---|---|---|---|---|---|"]
+    rows = []
+    for name, ds in per.items():
         ds.sort()
-        warm, timed, rest = ds[:skip], ds[skip:skip + take], ds[skip + take:]
+        m = mult.get(name, 1)
+        calls = [sum(d for _, d in ds[i:i + m]) for i in range(0, m * (skip + take), m) if i + m <= len(ds)]
+        warm, timed = calls[:skip], calls[skip:skip + take]
+        rest = len(ds) - m * (len(warm) + len(timed))
         if not timed:
             continue
-        td = [d / 1e3 for _, d in timed]
-        wa = sum(d for _, d in warm) / len(warm) / 1e3 if warm else float("nan")
-        lines.append(f"| `{name}` | {len(td)} | {sum(td) / len(td):.1f} | {min(td):.1f} | {max(td):.1f} | "
-                     f"{wa:.1f} | {len(rest)} |")
+        td = [d / 1e3 for d in timed]
+        wa = sum(warm) / len(warm) / 1e3 if warm else float("nan")
+        rows.append((sum(td), f"| `{name}` | {len(td)} | {sum(td) / len(td):.1f} | {min(td):.1f} | {max(td):.1f} | "
+                              f"{wa:.1f} | {rest} |"))
+    lines += [r for _, r in sorted(rows, key=lambda x: -x[0])]
     print("\n".join(lines))
 
 
@@ -1103,7 +1116,7 @@ def main():
     ap.add_argument("--counter-write", nargs="+", metavar=("LINE", "CSV"),
                     help="summarise the counter passes of LINE (rocprofv3 counter_collection.csv files) into "
                          "profiles/counters.json")
-    ap.add_argument("--trace-summary", nargs=5, metavar=("CSV", "SKIP", "TAKE", "TITLE", "COMMAND"),
+    ap.add_argument("--trace-summary", nargs="+", metavar="CSV SKIP TAKE TITLE COMMAND [PER_CALL]",
                     help="markdown table of a rocprofv3 kernel trace, warm-up and timed dispatches apart")
     ap.add_argument("--only", metavar="LINES",
                     help="profiling aid: run only these comma-separated lines (routed_prefill or a secondary "
@@ -1120,8 +1133,10 @@ def main():
         counter_write(args.counter_write[0], args.counter_write[1:])
         return
     if args.trace_summary:
-        c, sk, tk, title, cmd = args.trace_summary
-        trace_summary(c, int(sk), int(tk), title, cmd)
+        if len(args.trace_summary) not in (5, 6):
+            sys.exit("--trace-summary takes CSV SKIP TAKE TITLE COMMAND [PER_CALL]")
+        c, sk, tk, title, cmd = args.trace_summary[:5]
+        trace_summary(c, int(sk), int(tk), title, cmd, *args.trace_summary[5:])
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: every (batch, head) of this path is independent, so --gpus {args.gpus} "
