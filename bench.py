@@ -698,7 +698,7 @@ def bench_tail_replay(args, torch, hla, inputs, steps=20, warmup=3, full_prefix=
                replay_tokens_per_s=W.B * L / dt_rep, algorithmic_gbs=bytes_alg / dt_rep / 1e9,
                hbm_frac=round(bytes_alg / dt_rep / 1e9 / PEAK_HBM_GBS, 4),
                rel_err_vs_gpu_full_prefix=rel_err(Sh, S2h), kernel_ms=kms,
-               counters=kernel_counters("tail_replay", kms, (("chunk", "chunk_kernel"), ("scan", "scan_bf16_kernel"))),
+               counters=kernel_counters("tail_replay", kms, (("chunk", "ut_kernel"), ("prefill", "state_kernel"))),
                note="rel_err_vs_gpu_full_prefix compares the rebuilt states of all sequences with the GPU's "
                     "full-prefix states; the oracle leg adds both against the oracle and the P11 bound")
     log(f"[tail_replay] replay {dt_rep*1e3:.3f} ms vs full-prefix state {dt_full*1e3:.3f} ms "
