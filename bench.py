@@ -307,14 +307,15 @@ def bench_routed_skip(args, torch, hla, inputs, x):
                 compose_ms=r["roofline"]["avg_launch_ms"], compose_tflops_active=r["roofline"]["achieved"])
 
 
-def bench_routed_learned_reps(args, torch, hla, inputs, x):
-    """C = 64 with learned window representatives (window 32, seeded weights)."""
+def bench_routed_learned_reps(args, torch, hla, inputs, x, window=32):
+    """C = 64 with learned window representatives (seeded weights), C / window per chunk."""
     W = inputs.WORKLOADS["routed_prefill"]
     pooler = inputs.gen_pooler_weights(W.H, W.dk, dtype=W.dtype, seed=0, stream=inputs.STREAM["routed_prefill"])
-    r, _ = bench_routed_prefill(_sub(args), torch, hla, inputs, Cw=C, x=x, tag="routed_prefill_learned_reps",
-                                pooler=pooler, window=32)
+    tag = "routed_prefill_learned_reps" + ("" if window == 32 else f"_w{window}")
+    r, _ = bench_routed_prefill(_sub(args), torch, hla, inputs, Cw=C, x=x, tag=tag, pooler=pooler, window=window)
     return dict(
-        workload="routed_prefill C=64, learned representatives (window 32, 2 per chunk), seeded weights",
+        workload=f"routed_prefill C=64, learned representatives (window {window}, {C // window} per chunk), "
+                 "seeded weights",
         C=C, tau=W.tau, ms_per_step=r["ms_per_step"], tokens_per_s=r["value"], mfma_util_pct=r["mfma_util_pct"],
         active_pairs=r["active_pairs"], kernel_ms=r["kernel_ms"], reps_pool=r["reps_pool"])
 
@@ -331,6 +332,8 @@ SECONDARY = {
     "routed_prefill_C256": bench_routed_c256,
     "routed_prefill_skip": bench_routed_skip,
     "routed_prefill_learned_reps": bench_routed_learned_reps,
+    "routed_prefill_learned_reps_w64": lambda args, torch, hla, inputs, x: bench_routed_learned_reps(
+        args, torch, hla, inputs, x, window=64),
     "gdn2_routed_prefill": lambda args, torch, hla, inputs, x: bench_gdn2_routed(args, torch, hla, inputs, x),
     "routed_prefill_backward": lambda args, torch, hla, inputs, x: bench_prefill_backward(args, torch, hla, inputs, x),
     "decode": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs),

@@ -178,3 +178,12 @@ def test_backward_twice():
         return dict(r)
 
     twice(run, "routed prefill backward")
+
+    # the smallest workspace: history segments replayed from checkpoints
+    d = h.make_dims(B, T, H, T, d, d, 1, C)
+    ws = torch.empty(h.workspace_bytes(h.FN_PREFILL_BACKWARD_MIN, d), dtype=torch.uint8, device="cuda")
+
+    def run_seg(_):
+        return dict(h.prefill_backward(q, k, v, beta, alpha, dO, tau=1e-3, S0=S0, ws=ws))
+
+    twice(run_seg, "routed prefill backward in history segments")
