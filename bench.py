@@ -633,7 +633,7 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, ws_gib=None):
             for n in ("bwd_save", "bwd_adjoint", "bwd_reduce")}
     # roofline record of the kernel that takes the most time: the chunk reverse (fp32 VALU)
     # or one of the composition passes (bf16 matrix cores)
-    kernels = {"bwd_chunk": ("chunk_bwd_kernel (outputs + maps reverse)", "alu", fl_chunk, PEAK_FP32_VALU_TFLOPS),
+    kernels = {"bwd_chunk": ("chunk_bwd_kernel (outputs reverse, fp32 VALU) + chunk_bwd_map_ut_kernel (maps reverse through the UT form, fp32 MFMA)", "alu", fl_chunk, PEAK_FP32_VALU_TFLOPS),
                "bwd_save": ("compose_replay_kernel (+ prep_bwd_kernel)", "mfma", fl_pair, PEAK_BF16_TFLOPS),
                "bwd_adjoint": ("compose_adjoint_kernel", "mfma", fl_pair, PEAK_BF16_TFLOPS),
                "bwd_reduce": ("compose_grad_reduce_kernel (+ chain_sum_kernel)", "mfma", fl_pair, PEAK_BF16_TFLOPS)}

@@ -254,6 +254,402 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// The chunk-map part of the reverse through the UT form, on the matrix cores (bf16 inputs,
+// float32 arithmetic).
+//
+// [HLA] Methodology paragraph 1: a piece's map is At = gamma_63 I - K^T D W and
+// Bc = K^T D U, with (for the piece's tokens t, s)
+//     A0 = strictly_lower((K K^T) o Gamma),  L = diag(beta) A0,  X = (I + L)^-1,
+//     W = X diag(beta gamma) K,  U = X diag(beta) V,  D = diag(exp(g_63 - g_s)).
+// Given dAt and dBc (float32) the reverse is, in this order,
+//     dY = -K dAt,  dKB = K dBc,  dD_s = dY_s . W_s + dKB_s . U_s,  dW = D dY,  dU = D dKB,
+//     dK  = D (-W dAt^T + U dBc^T),                                (K in K^T D W, K^T D U)
+//     F = X^T dU,  G = X^T dW,  dV = diag(beta) F,  dK += diag(beta gamma) G,
+//     T1 = X^T dX = F (diag(beta) V)^T + G (diag(beta gamma) K)^T,  H = -T1 X^T (s < t),
+//     dK += H' K + H'^T K,  H'_ts = beta_t Gamma_ts H_ts,
+//     dbeta_t = F_t . v_t + gamma_t G_t . k_t + sum_s H_ts A0_ts,
+//     dg_t = beta_t gamma_t G_t . k_t + sum_s Psi_ts - sum_s Psi_st - dD_t D_t
+//            (+ sum_s dD_s D_s + tr(dAt) gamma_63 at t = 63),   Psi_ts = beta_t H_ts A0_ts,
+//     dlog alpha_s = sum_{t >= s} dg_t,  dalpha = dlog alpha / alpha.
+// One workgroup of 8 waves per (b, h, piece); every product is a 32 x 32 tile of
+// v_mfma_f32_32x32x2_f32 with its operands read from LDS (dAt, dBc from global memory), and
+// wave w owns tile w of the 64 x dk and of the 64 x dv results.  The workgroup writes its
+// per-token sums into the first chunk-map slot of the partial sums.
+namespace {
+// C (32 x 32) += A B over KD k values: fa(k) = A[m0 + lane % 32][k], fb(k) = B[k][n0 + lane % 32]
+template <int KD, class FA, class FB>
+__device__ __forceinline__ f32x16 mm32(f32x16 acc, int hh, FA fa, FB fb) {
+#pragma unroll 8
+  for (int ks = 0; ks < KD / 2; ++ks) {
+    const int k = 2 * ks + hh;
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa(k), fb(k), acc, 0, 0, 0);
+  }
+  return acc;
+}
+}  // namespace
+
+template <int DK, int DV>
+__global__ __launch_bounds__(512, 1) void chunk_bwd_map_ut_kernel(ChunkBwdArgs a) {
+  constexpr int C = kChunk, NT = 512;
+  constexpr int PX = C + 4;                // float32 pitch of the 64 x 64 matrices
+  constexpr int PK = DK + 8, PV = DV + 8;  // bf16 pitch of the k and v rows
+  constexpr int PW = DK + 4, PU = DV + 4;  // float32 pitch of W (dW, G) and U (dU, F)
+  constexpr int NKT = 2 * (DK / 32), NVT = 2 * (DV / 32);  // 32 x 32 tiles of 64 x dk, 64 x dv
+  constexpr int NB_OUT = DV / 32, NB_ALL = NB_OUT + (DK + DV) / 32;
+  static_assert(NKT <= 8 && NVT <= 8, "one tile of each kind per wave");
+  __shared__ __attribute__((aligned(16))) float A0[C * PX];  // lower: Gamma o K K^T; upper blocks: scratch
+  __shared__ __attribute__((aligned(16))) float Xb[C * PX];
+  __shared__ __attribute__((aligned(16))) float Tb[C * PX];  // T1, then H
+  __shared__ __attribute__((aligned(16))) bf16 Ks[C * PK];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[C * PV];
+  __shared__ __attribute__((aligned(16))) float Wb[C * PW];  // W, then dW, then G
+  __shared__ __attribute__((aligned(16))) float Ub[C * PU];  // U, then dU, then F
+  __shared__ float s_beta[C], s_alpha[C], s_g2[C], s_gam[C], s_D[C], s_dD[C];
+  __shared__ float s_red[C][8];
+  __shared__ float s_row[3][C];  // sum_s Psi_ts, sum_t Psi_ts (by s), sum_s H_ts A0_ts
+  __shared__ float s_tr;
+
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, c32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t id = blockIdx.x;
+  const int c = a.c0 + (int)(id % (a.c1 - a.c0));
+  const int64_t bh = id / (a.c1 - a.c0);
+  const int64_t h = bh % a.H, b = bh / a.H;
+  const int64_t t0 = (int64_t)c * C;
+  const int n = (int)((a.T - t0) < C ? (a.T - t0) : C);
+  const int64_t row0 = (b * a.ld_T + t0) * a.H + h;  // token-row of (b, t0, h)
+  const int64_t cc = bh * a.N + c;
+  const float* dAt = a.dAt + cc * (int64_t)DK * DK;
+  const float* dBc = a.dBc + cc * (int64_t)DK * DV;
+
+  // ---- 0. k, v rows (zero past the end), per-token gates and decays
+  {
+    const bf16* kg = reinterpret_cast<const bf16*>(a.k);
+    const bf16* vg = reinterpret_cast<const bf16*>(a.v);
+    for (int i = tid; i < C * (DK / 8); i += NT) {
+      const int t = i / (DK / 8), u = i % (DK / 8);
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (t < n) x = *reinterpret_cast<const uint4*>(kg + (row0 + (int64_t)t * a.H) * DK + u * 8);
+      *reinterpret_cast<uint4*>(Ks + t * PK + u * 8) = x;
+    }
+    for (int i = tid; i < C * (DV / 8); i += NT) {
+      const int t = i / (DV / 8), u = i % (DV / 8);
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (t < n) x = *reinterpret_cast<const uint4*>(vg + (row0 + (int64_t)t * a.H) * DV + u * 8);
+      *reinterpret_cast<uint4*>(Vs + t * PV + u * 8) = x;
+    }
+    for (int i = tid; i < C * PX; i += NT) Xb[i] = 0.f;
+    if (tid < C) {
+      const int64_t r = row0 + (int64_t)tid * a.H;
+      const float be = tid < n ? a.beta[r] : 0.f, al = tid < n ? a.alpha[r] : 1.f;
+      float x = logf(fmaxf(al, 1.17549435e-38f));  // alpha = 0 (a reset) stays finite
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {  // inclusive prefix sum over wave 0
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      const float x_end = __shfl(x, 63, 64);
+      s_beta[tid] = be;
+      s_alpha[tid] = al;
+      s_g2[tid] = x * 1.4426950408889634f;
+      s_gam[tid] = expf(x);
+      s_D[tid] = expf(x_end - x);
+    }
+    if (w == 2) {  // tr(dAt)
+      float tr = 0.f;
+      for (int i = lane; i < DK; i += 64) tr += dAt[(int64_t)i * DK + i];
+      tr = wave_sum(tr);
+      if (lane == 0) s_tr = tr;
+    }
+  }
+  __syncthreads();
+
+  // ---- 1. A0 = strictly_lower(Gamma o K K^T): tiles (0,0), (1,0), (1,1) on waves 0-2
+  // (bf16 products of the bf16 keys, float32 sums); wave 3 zeroes tile (0,1)
+  if (w < 3) {
+    const int tm = w == 0 ? 0 : 1, tn = w == 2 ? 1 : 0;
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int ks = 0; ks < DK / 16; ++ks)
+      acc = Mma<bf16>::mma(Mma<bf16>::load_plain(Ks + (tm * 32 + c32) * PK, ks, hh),
+                           Mma<bf16>::load_plain(Ks + (tn * 32 + c32) * PK, ks, hh), acc);
+    const int s = tn * 32 + c32;
+    const float gs = s_g2[s];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int t = tm * 32 + acc_row(e, hh);
+      A0[t * PX + s] = s < t ? __builtin_amdgcn_exp2f(s_g2[t] - gs) * acc[e] : 0.f;
+    }
+  } else if (w == 3) {
+    for (int i = lane; i < 32 * 32; i += 64) A0[(i >> 5) * PX + 32 + (i & 31)] = 0.f;
+  }
+  __syncthreads();
+
+  // ---- 2. X = (I + L)^-1 with L = diag(beta) A0, blocked by 16: the diagonal blocks by
+  // substitution, then the blocks below them by sub-diagonal from Z = -X_ii L_im (kept in
+  // A0's unused blocks above the diagonal)
+  if (tid < 64) {
+    const int bi = tid >> 4, cl = tid & 15, base = bi * 16;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = (r == cl) ? 1.f : 0.f;
+      const float br = s_beta[base + r];
+#pragma unroll
+      for (int q2 = 0; q2 < r; ++q2) s -= br * A0[(base + r) * PX + base + q2] * x[q2];
+      x[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Xb[(base + r) * PX + base + cl] = x[r];
+  }
+  __syncthreads();
+  for (int e = tid; e < 6 * 256; e += NT) {
+    const int bz = e >> 8, r = (e >> 4) & 15, cl = e & 15;
+    const int i = bz < 1 ? 1 : (bz < 3 ? 2 : 3), m = bz - i * (i - 1) / 2;
+    float z = 0.f;
+#pragma unroll
+    for (int q2 = 0; q2 < 16; ++q2)
+      z -= Xb[(i * 16 + r) * PX + i * 16 + q2] * s_beta[i * 16 + q2] * A0[(i * 16 + q2) * PX + m * 16 + cl];
+    A0[(m * 16 + r) * PX + i * 16 + cl] = z;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    for (int e = tid; e < (4 - d) * 256; e += NT) {
+      const int k = e >> 8, i = k + d, r = (e >> 4) & 15, cl = e & 15;
+      float x = 0.f;
+      for (int m = k; m < i; ++m)
+#pragma unroll
+        for (int q2 = 0; q2 < 16; ++q2) x += A0[(m * 16 + r) * PX + i * 16 + q2] * Xb[(m * 16 + q2) * PX + k * 16 + cl];
+      Xb[(i * 16 + r) * PX + k * 16 + cl] = x;
+    }
+    __syncthreads();
+  }
+
+  // wave w's tiles: (rows tk * 32, columns ck * 32) of the 64 x dk results and (tv, cv) of
+  // the 64 x dv ones
+  const bool hk = w < NKT, hv = w < NVT;
+  const int tk = w & 1, ck = w >> 1, tv = w & 1, cv = w >> 1;
+  const int rk0 = tk * 32, rv0 = tv * 32;  // first row of the tiles
+  auto tok = [&](int r0, int e) { return r0 + acc_row(e, hh); };
+
+  // ---- 3. W = X diag(beta gamma) K and U = X diag(beta) V
+  if (hk) {
+    const float* xr = Xb + (rk0 + c32) * PX;
+    const bf16* kc = Ks + ck * 32 + c32;
+    const f32x16 acc = mm32<C>(zero16(), hh, [&](int k) { return xr[k] * s_beta[k] * s_gam[k]; },
+                               [&](int k) { return (float)kc[k * PK]; });
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Wb[tok(rk0, e) * PW + ck * 32 + c32] = acc[e];
+  }
+  if (hv) {
+    const float* xr = Xb + (rv0 + c32) * PX;
+    const bf16* vc = Vs + cv * 32 + c32;
+    const f32x16 acc = mm32<C>(zero16(), hh, [&](int k) { return xr[k] * s_beta[k]; },
+                               [&](int k) { return (float)vc[k * PV]; });
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Ub[tok(rv0, e) * PU + cv * 32 + c32] = acc[e];
+  }
+  __syncthreads();
+
+  // ---- 4. dY = -K dAt, dKB = K dBc, dK_ab = D (-W dAt^T + U dBc^T), dD
+  f32x16 dkab = zero16(), dy = zero16(), dkb = zero16();
+  if (hk) {
+    const bf16* kr = Ks + (rk0 + c32) * PK;
+    const float* wr = Wb + (rk0 + c32) * PW;
+    const float* ur = Ub + (rk0 + c32) * PU;
+    const int nc = ck * 32 + c32;
+    dy = mm32<DK>(dy, hh, [&](int k) { return -(float)kr[k]; }, [&](int k) { return dAt[(int64_t)k * DK + nc]; });
+    dkab = mm32<DK>(dkab, hh, [&](int k) { return -wr[k]; }, [&](int k) { return dAt[(int64_t)nc * DK + k]; });
+    dkab = mm32<DV>(dkab, hh, [&](int k) { return ur[k]; }, [&](int k) { return dBc[(int64_t)nc * DV + k]; });
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dkab[e] *= s_D[tok(rk0, e)];
+  }
+  if (hv) {
+    const bf16* kr = Ks + (rv0 + c32) * PK;
+    const int nc = cv * 32 + c32;
+    dkb = mm32<DK>(dkb, hh, [&](int k) { return (float)kr[k]; }, [&](int k) { return dBc[(int64_t)k * DV + nc]; });
+  }
+  // dD_t = dY_t . W_t + dKB_t . U_t: each tile's 32 columns summed over the lanes of a half
+  if (hk) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = lane_group_sum<32>(dy[e] * Wb[tok(rk0, e) * PW + ck * 32 + c32]);
+      if (c32 == 0) s_red[tok(rk0, e)][ck] = p;
+    }
+  }
+  if (hv) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = lane_group_sum<32>(dkb[e] * Ub[tok(rv0, e) * PU + cv * 32 + c32]);
+      if (c32 == 0) s_red[tok(rv0, e)][DK / 32 + cv] = p;
+    }
+  }
+  __syncthreads();  // W, U and the partial sums are complete
+  if (tid < C) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < DK / 32 + DV / 32; ++j) s += s_red[tid][j];
+    s_dD[tid] = s;
+  }
+  if (hk) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Wb[tok(rk0, e) * PW + ck * 32 + c32] = s_D[tok(rk0, e)] * dy[e];  // dW
+  }
+  if (hv) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Ub[tok(rv0, e) * PU + cv * 32 + c32] = s_D[tok(rv0, e)] * dkb[e];  // dU
+  }
+  __syncthreads();
+
+  // ---- 5. G = X^T dW, F = X^T dU
+  f32x16 gt = zero16(), ft = zero16();
+  if (hk) {
+    const float* xc = Xb + rk0 + c32;
+    const float* dw = Wb + ck * 32 + c32;
+    gt = mm32<C>(gt, hh, [&](int k) { return xc[k * PX]; }, [&](int k) { return dw[k * PW]; });
+  }
+  if (hv) {
+    const float* xc = Xb + rv0 + c32;
+    const float* du = Ub + cv * 32 + c32;
+    ft = mm32<C>(ft, hh, [&](int k) { return xc[k * PX]; }, [&](int k) { return du[k * PU]; });
+  }
+  __syncthreads();  // dW, dU are dead
+  if (hk) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Wb[tok(rk0, e) * PW + ck * 32 + c32] = gt[e];
+  }
+  if (hv) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Ub[tok(rv0, e) * PU + cv * 32 + c32] = ft[e];
+  }
+  __syncthreads();
+
+  // ---- 6. T1 = F (diag(beta) V)^T + G (diag(beta gamma) K)^T: tile (tm, tn) on wave tm + 2 tn
+  if (w < 4) {
+    const int tm = w & 1, tn = w >> 1, s = tn * 32 + c32;
+    const float* fr = Ub + (tm * 32 + c32) * PU;
+    const float* gr = Wb + (tm * 32 + c32) * PW;
+    const bf16* vr = Vs + s * PV;
+    const bf16* kr = Ks + s * PK;
+    const f32x16 a1 = mm32<DV>(zero16(), hh, [&](int k) { return fr[k]; }, [&](int k) { return (float)vr[k]; });
+    const f32x16 a2 = mm32<DK>(zero16(), hh, [&](int k) { return gr[k]; }, [&](int k) { return (float)kr[k]; });
+    const float bs = s_beta[s], gs = s_gam[s];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Tb[(tm * 32 + acc_row(e, hh)) * PX + s] = bs * (a1[e] + gs * a2[e]);
+  }
+  __syncthreads();
+  // ---- 7. H = -T1 X^T, kept below the diagonal
+  f32x16 ht = zero16();
+  if (w < 4) {
+    const int tm = w & 1, tn = w >> 1, s = tn * 32 + c32;
+    const float* tr = Tb + (tm * 32 + c32) * PX;
+    const float* xr = Xb + s * PX;
+    ht = mm32<C>(ht, hh, [&](int k) { return tr[k]; }, [&](int k) { return xr[k]; });
+  }
+  __syncthreads();
+  if (w < 4) {
+    const int tm = w & 1, tn = w >> 1, s = tn * 32 + c32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int t = tm * 32 + acc_row(e, hh);
+      Tb[t * PX + s] = s < t ? -ht[e] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- 8. dK = dK_ab + diag(beta gamma) G + H' K + H'^T K;  dV = diag(beta) F
+  const int64_t pslot = (cc * NB_ALL + NB_OUT) * (int64_t)C;  // first chunk-map slot
+  if (hk) {
+    const int t = rk0 + c32;
+    const float* hr = Tb + t * PX;  // row t of H
+    const float* hc = Tb + t;       // column t of H
+    const bf16* kc = Ks + ck * 32 + c32;
+    const float bt = s_beta[t], g2t = s_g2[t];
+    f32x16 acc = mm32<C>(zero16(), hh,
+                         [&](int k) { return k < t ? hr[k] * bt * __builtin_amdgcn_exp2f(g2t - s_g2[k]) : 0.f; },
+                         [&](int k) { return (float)kc[k * PK]; });
+    acc = mm32<C>(acc, hh,
+                  [&](int k) { return k > t ? hc[k * PX] * s_beta[k] * __builtin_amdgcn_exp2f(s_g2[k] - g2t) : 0.f; },
+                  [&](int k) { return (float)kc[k * PK]; });
+    float* pk = a.part_k + pslot * DK + ck * 32 + c32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int te = tok(rk0, e);
+      if (te < n) pk[(int64_t)te * DK] = acc[e] + dkab[e] + s_beta[te] * s_gam[te] * gt[e];
+    }
+  }
+  if (hv) {
+    float* pv = a.part_v + (cc * 2 + 1) * (int64_t)C * DV + cv * 32 + c32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int te = tok(rv0, e);
+      if (te < n) pv[(int64_t)te * DV] = s_beta[te] * ft[e];
+    }
+  }
+  // ---- 9. the per-token dots: F_t . v_t, G_t . k_t (by tiles), the sums of Psi and of
+  // H o A0 (threads 0-127), then dbeta, dg and the reverse cumulative sum for dalpha
+  if (hv) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int te = tok(rv0, e);
+      const float p = lane_group_sum<32>(ft[e] * (float)Vs[te * PV + cv * 32 + c32]);
+      if (c32 == 0) s_red[te][cv] = p;
+    }
+  }
+  if (hk) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int te = tok(rk0, e);
+      const float p = lane_group_sum<32>(gt[e] * (float)Ks[te * PK + ck * 32 + c32]);
+      if (c32 == 0) s_red[te][4 + ck] = p;
+    }
+  }
+  if (tid < C) {
+    const int t = tid;
+    float ps = 0.f, ha = 0.f;
+    for (int s = 0; s < t; ++s) {
+      const float x = Tb[t * PX + s] * A0[t * PX + s];
+      ha += x;
+    }
+    ps = s_beta[t] * ha;
+    s_row[0][t] = ps;
+    s_row[2][t] = ha;
+  } else if (tid < 2 * C) {
+    const int s = tid - C;
+    float pc = 0.f;
+    for (int t = s + 1; t < C; ++t) pc += s_beta[t] * Tb[t * PX + s] * A0[t * PX + s];
+    s_row[1][s] = pc;
+  }
+  __syncthreads();
+  if (tid < C) {
+    const int t = tid;
+    float fv = 0.f, gk = 0.f;
+#pragma unroll
+    for (int j = 0; j < DV / 32; ++j) fv += s_red[t][j];
+#pragma unroll
+    for (int j = 0; j < DK / 32; ++j) gk += s_red[t][4 + j];
+    const float be = s_beta[t], ga = s_gam[t], dd = s_dD[t] * s_D[t];
+    const float dbeta = fv + ga * gk + s_row[2][t];
+    float dg = be * ga * gk + s_row[0][t] - s_row[1][t] - dd;
+    const float ddsum = wave_sum(dd);
+    if (t == C - 1) dg += ddsum + s_tr * ga;
+    // dlog alpha_t = sum_{u >= t} dg_u: inclusive suffix sum over the wave
+    float x = dg;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(x, off, 64);
+      if (lane + off < 64) x += y;
+    }
+    if (t < n) {
+      float* ps = a.part_s + (pslot + t) * 2;
+      ps[0] = dbeta;
+      ps[1] = x / fmaxf(s_alpha[t], 1.17549435e-38f);
+    }
+  }
+}
+
 // dq, dk, dv, dbeta, dalpha of every token: the workgroups' partial sums in a fixed order,
 // plus the router's parts (dqbar of the token's chunk divided by its token count, and the
 // per-token key gradient) when given.  One thread per (b, t, h, row).
@@ -271,7 +667,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_finalize_kernel(ChunkBwdArgs a)
   const int c = (int)(t / C), u = (int)(t % C);
   const int64_t bh = b * a.H + h;
   const int64_t base = (bh * a.N + c) * NB_ALL;
-  const int b0 = a.have_out ? 0 : NB_OUT, b1 = a.have_map ? NB_ALL : NB_OUT;
+  const int b0 = a.have_out ? 0 : NB_OUT, b1 = a.have_map ? (a.map_ut ? NB_OUT + 1 : NB_ALL) : NB_OUT;
   // every partial sum is read once, here: non-temporal loads, all of a thread's in flight
   if (e < DK) {
     float sk = 0.f;
@@ -314,9 +710,13 @@ static hipError_t launch_chunk_bwd_t(const ChunkBwdArgs& a, int stages, hipStrea
     TimedLaunch tl(HLA_KERNEL_BWD_CHUNK, s);
     if (stages & kChunkBwdOut)
       hipLaunchKernelGGL((chunk_bwd_kernel<T, DK, DV, true>), dim3((unsigned)(BHN * (DV / 32))), dim3(NT), 0, s, a);
-    if (stages & kChunkBwdMap)
-      hipLaunchKernelGGL((chunk_bwd_kernel<T, DK, DV, false>), dim3((unsigned)(BHN * ((DK + DV) / 32))), dim3(NT), 0,
-                         s, a);
+    if (stages & kChunkBwdMap) {
+      if (a.map_ut)
+        hipLaunchKernelGGL((chunk_bwd_map_ut_kernel<DK, DV>), dim3((unsigned)BHN), dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((chunk_bwd_kernel<T, DK, DV, false>), dim3((unsigned)(BHN * ((DK + DV) / 32))), dim3(NT),
+                           0, s, a);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(stages & kChunkBwdFinalize)) return e;
@@ -335,7 +735,10 @@ static hipError_t launch_chunk_bwd_d(const ChunkBwdArgs& a, int dk, int dv, int 
 }
 
 hipError_t launch_chunk_backward(const ChunkBwdArgs& a, int dtype, int dk, int dv, int stages, hipStream_t s) {
-  return dtype == 1 ? launch_chunk_bwd_d<bf16>(a, dk, dv, stages, s) : launch_chunk_bwd_d<float>(a, dk, dv, stages, s);
+  // bf16: the chunk-map part through the UT form on the matrix cores
+  ChunkBwdArgs b = a;
+  b.map_ut = dtype == 1;
+  return dtype == 1 ? launch_chunk_bwd_d<bf16>(b, dk, dv, stages, s) : launch_chunk_bwd_d<float>(b, dk, dv, stages, s);
 }
 
 }  // namespace hla

@@ -70,11 +70,25 @@ CHUNK_CASES = [("f32", 64, 128, 3 * C + 17), ("bf16", 128, 128, 150), ("bf16", 1
 @pytest.mark.parametrize("parts", ["out", "map", "both"])
 @pytest.mark.parametrize("case", CHUNK_CASES, ids=[f"{c[0]}-dk{c[1]}-dv{c[2]}-T{c[3]}" for c in CHUNK_CASES])
 def test_chunk_backward(case, parts):
+    _check_chunk_backward(case, parts, "slow")
+
+
+@pytest.mark.parametrize("parts", ["map", "both"])
+@pytest.mark.parametrize("case,alpha_mode", [(("bf16", 128, 128, 3 * C - 5), "workload"),
+                                             (("bf16", 64, 128, 2 * C + 7), "slow")],
+                         ids=["bf16-dk128-dv128-workload-decay", "bf16-dk64-dv128-slow"])
+def test_chunk_backward_map_ut(case, alpha_mode, parts):
+    # the bf16 chunk-map reverse runs through the UT form: under the workloads' fast decay
+    # (pairwise factors far below float32's range) and with dk != dv
+    _check_chunk_backward(case, parts, alpha_mode)
+
+
+def _check_chunk_backward(case, parts, alpha_mode):
     dtype, dk, dv, T = case
-    note(f"chunk backward {case} {parts}")
+    note(f"chunk backward {case} {parts} {alpha_mode}")
     B, H = 2, 2
     N = -(-T // C)
-    x = inputs.gen_tokens(B, T, H, dk, dv, dtype=dtype, seed=41, alpha_mode="slow")
+    x = inputs.gen_tokens(B, T, H, dk, dv, dtype=dtype, seed=41, **({"alpha_mode": "slow"} if alpha_mode == "slow" else {}))
     q, k, v, beta, alpha = (dev(x.q, dtype), dev(x.k, dtype), dev(x.v, dtype), f32(x.beta), f32(x.alpha))
     want_out, want_map = parts in ("out", "both"), parts in ("map", "both")
     init = inputs.gen_cotangent((B, H, N, dk, dv), seed=42, name="S0", scale=0.5) if want_out else None
