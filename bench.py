@@ -473,6 +473,8 @@ def bench_native_prefill(args, torch, hla, inputs, steps=20, warmup=3):
 # without packed-fp32 instructions, so its own ceiling is half that; records give both.
 PEAK_FP32_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2 * 2.4e9 / 1e12
 PEAK_FP32_VALU_UNPACKED_TFLOPS = PEAK_FP32_VALU_TFLOPS / 2
+# dense fp32 matrix-core peak, as published
+PEAK_FP32_MFMA_TFLOPS = 157.3
 
 
 def bytes_gdn2_passes(B, T, H, dk, dv, N):
@@ -559,13 +561,22 @@ def bench_gdn2_routed(args, torch, hla, inputs, x):
 BWD_T = 8192
 
 
-def flops_chunk_bwd(n_tokens_heads, dk, dv):
-    """Algorithmic work of the per-chunk reverse, per token and head: every column runs the
-    forward step once (k . x and the update, 4 dk) and its reverse (k . dx, dx . x_prev, the
-    two-term key gradient and the dx update, 10 dk); the dv state columns add q dO and the
-    query gradient (4 dk).  Map columns: dk + dv; state columns: dv.  The checkpoint replay
-    the kernel adds (a second forward step) is not counted."""
-    return n_tokens_heads * dk * (dv * 18 + (dk + dv) * 14)
+def flops_chunk_bwd(n_pieces_heads, dk, dv):
+    """Algorithmic work of the per-piece reverse through the UT form ([HLA] Methodology
+    paragraph 1), per (piece, head), as matrix products at 2 m n k, each product with a
+    triangular factor (A0, P, dP, X, H) at half: both parts recompute A0 (C^2 dk), W and U
+    (C^2 (dk + dv)) and end in the common tail (G and F: C^2 (dk + dv); T1: 2 C^2 (dk + dv);
+    H: C^3; H'K and H'^T K: 2 C^2 dk).  The maps part adds dY, dKB and dK_ab (4 C dk^2 +
+    4 C dk dv); the outputs part adds P (C^2 dk), E (2 C dk dv), dE and dP (2 C^2 dv), dQ
+    (2 C dk dv + C^2 dk), dK_P (C^2 dk), dM0 (4 C dk dv) and dW (2 C dk dv).  The blocked
+    inverse and the per-token sums are not counted."""
+    c = C
+    tail = c * c * (dk + dv) + 2 * c * c * (dk + dv) + c ** 3 + 2 * c * c * dk
+    common = c * c * dk + c * c * (dk + dv) + tail
+    maps = common + 4 * c * dk * dk + 4 * c * dk * dv
+    outs = common + c * c * dk + 2 * c * dk * dv + 2 * c * c * dv + 2 * c * dk * dv + c * c * dk + c * c * dk \
+        + 4 * c * dk * dv + 2 * c * dk * dv
+    return n_pieces_heads * (maps + outs)
 
 
 def flops_router_bwd(pairs, n_rep, dk):
@@ -624,16 +635,16 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, ws_gib=None):
     At, Bc = hla.chunk_transitions(k, v, beta, alpha)
     pairs = int(hla.route_mix(q, k, At, Bc, tau=W.tau)["active_cnt"].sum().item())
     del At, Bc
-    th = W.B * T * W.H
-    fl_chunk = flops_chunk_bwd(th, W.dk, W.dv)
+    fl_chunk = flops_chunk_bwd(W.B * N * W.H, W.dk, W.dv)
     fl_pair = flops_compose(pairs, W.dk, W.dv)
     ach = fl_chunk / (ms["bwd_chunk"] / 1e3) / 1e12
     mfma = {n: dict(achieved=round(fl_pair / (ms[n] / 1e3) / 1e12, 1),
                     frac=round(fl_pair / (ms[n] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4))
             for n in ("bwd_save", "bwd_adjoint", "bwd_reduce")}
-    # roofline record of the kernel that takes the most time: the chunk reverse (fp32 VALU)
-    # or one of the composition passes (bf16 matrix cores)
-    kernels = {"bwd_chunk": ("chunk_bwd_kernel (outputs reverse, fp32 VALU) + chunk_bwd_map_ut_kernel (maps reverse through the UT form, fp32 MFMA)", "alu", fl_chunk, PEAK_FP32_VALU_TFLOPS),
+    # roofline record of the kernel that takes the most time: the chunk reverse (fp32 matrix
+    # cores) or one of the composition passes (bf16 matrix cores)
+    kernels = {"bwd_chunk": ("chunk_bwd_out_ut_kernel + chunk_bwd_map_ut_kernel (reverse through the UT form)",
+                             "mfma", fl_chunk, PEAK_FP32_MFMA_TFLOPS),
                "bwd_save": ("compose_replay_kernel (+ prep_bwd_kernel)", "mfma", fl_pair, PEAK_BF16_TFLOPS),
                "bwd_adjoint": ("compose_adjoint_kernel", "mfma", fl_pair, PEAK_BF16_TFLOPS),
                "bwd_reduce": ("compose_grad_reduce_kernel (+ chain_sum_kernel)", "mfma", fl_pair, PEAK_BF16_TFLOPS)}
@@ -648,15 +659,14 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, ws_gib=None):
                roofline=dict(kernel=kname, bound=bound, achieved=round(ach_dom, 2), peak=round(peak, 1),
                              unit="TFLOP/s", frac=round(ach_dom / peak, 4), flops_per_launch=fl_dom,
                              avg_launch_ms=round(ms[dom], 4)),
-               chunk_reverse=dict(bound="alu", achieved=round(ach, 2), peak=round(PEAK_FP32_VALU_TFLOPS, 1),
-                                  unit="TFLOP/s", frac=round(ach / PEAK_FP32_VALU_TFLOPS, 4), flops_per_step=fl_chunk,
-                                  frac_of_unpacked_peak=round(ach / PEAK_FP32_VALU_UNPACKED_TFLOPS, 4)),
+               chunk_reverse=dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_FP32_MFMA_TFLOPS,
+                                  unit="TFLOP/s", frac=round(ach / PEAK_FP32_MFMA_TFLOPS, 4), flops_per_step=fl_chunk),
                composition_mfma=dict(flops_per_pass=fl_pair, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", **mfma),
                router_tflops=round(flops_router_bwd(pairs, C, W.dk) / (ms["bwd_router"] / 1e3) / 1e12, 2),
                min_workspace_gib=round(hla.workspace_bytes(hla.FN_PREFILL_BACKWARD_MIN, d) / 2**30, 2))
     log(f"[routed_prefill_backward T={T}] {dt*1e3:.3f} ms/step, {W.B*T/dt/1e6:.3f} M tok/s in "
         f"{main_bytes / 2**30:.1f} GiB ({segments} history segments); chunk reverse "
-        f"{ms['bwd_chunk']:.3f} ms ({ach:.1f} TFLOP/s fp32 VALU); replay {ms['bwd_save']:.3f}, adjoint "
+        f"{ms['bwd_chunk']:.3f} ms ({ach:.1f} TFLOP/s fp32 MFMA); replay {ms['bwd_save']:.3f}, adjoint "
         f"{ms['bwd_adjoint']:.3f}, reduce {ms['bwd_reduce']:.3f}, router {ms['bwd_router']:.3f} ms")
     if main_bytes < one_pass:
         dt1, ms1, _ = measure(one_pass)

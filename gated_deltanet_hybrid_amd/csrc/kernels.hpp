@@ -252,8 +252,8 @@ struct ChunkBwdArgs {
   int32_t c0, c1;           // the chunks c0 <= c < c1 that the outputs and maps parts take
   int32_t have_out;         // reverse of the outputs from chunk_init
   int32_t have_map;         // reverse of the chunk maps
-  int32_t map_ut;           // the chunk-map part runs through the UT form (one partial-sum
-                            // slot per piece) rather than by state columns (set by the launcher)
+  int32_t ut;               // both parts run through the UT form (one partial-sum slot per
+                            // piece and part) rather than by state columns (set by the launcher)
   const float* chunk_init;  // [B,H,N,dk,dv] start state of every chunk (have_out)
   const float* dO;          // [B,T,H,dv] upstream gradient of the outputs (have_out)
   const float* dAt;         // [B,H,N,dk,dk] upstream gradient of At (have_map)

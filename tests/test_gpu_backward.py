@@ -73,13 +73,14 @@ def test_chunk_backward(case, parts):
     _check_chunk_backward(case, parts, "slow")
 
 
-@pytest.mark.parametrize("parts", ["map", "both"])
+@pytest.mark.parametrize("parts", ["out", "map", "both"])
 @pytest.mark.parametrize("case,alpha_mode", [(("bf16", 128, 128, 3 * C - 5), "workload"),
-                                             (("bf16", 64, 128, 2 * C + 7), "slow")],
-                         ids=["bf16-dk128-dv128-workload-decay", "bf16-dk64-dv128-slow"])
-def test_chunk_backward_map_ut(case, alpha_mode, parts):
-    # the bf16 chunk-map reverse runs through the UT form: under the workloads' fast decay
-    # (pairwise factors far below float32's range) and with dk != dv
+                                             (("bf16", 64, 128, 2 * C + 7), "slow"),
+                                             (("bf16", 128, 64, C + 1), "workload")],
+                         ids=["bf16-dk128-dv128-workload-decay", "bf16-dk64-dv128-slow", "bf16-dk128-dv64-workload-decay"])
+def test_chunk_backward_ut(case, alpha_mode, parts):
+    # the bf16 reverse runs through the UT form: under the workloads' fast decay (pairwise
+    # factors far below float32's range), with dk != dv, and a last piece of one token
     _check_chunk_backward(case, parts, alpha_mode)
 
 
