@@ -336,6 +336,8 @@ SECONDARY = {
         args, torch, hla, inputs, x, window=64),
     "gdn2_routed_prefill": lambda args, torch, hla, inputs, x: bench_gdn2_routed(args, torch, hla, inputs, x),
     "routed_prefill_backward": lambda args, torch, hla, inputs, x: bench_prefill_backward(args, torch, hla, inputs, x),
+    "gdn2_routed_prefill_backward": lambda args, torch, hla, inputs, x: bench_gdn2_prefill_backward(
+        args, torch, hla, inputs, x),
     "decode": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs),
     "gdn2_decode": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs, gdn2=True),
     "native_prefill": lambda args, torch, hla, inputs, x: bench_native_prefill(args, torch, hla, inputs),
@@ -674,6 +676,67 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, ws_gib=None):
                                tokens_per_s=round(W.B * T / dt1, 1), kernel_ms={n: round(v, 3) for n, v in ms1.items()})
         log(f"[routed_prefill_backward T={T}] one pass in {one_pass / 2**30:.1f} GiB: {dt1*1e3:.3f} ms/step")
     del q, k, v, beta, alpha, dO
+    torch.cuda.empty_cache()
+    return res
+
+
+def flops_gdn2_chunk_bwd(n_tokens_heads, dk, dv):
+    """Algorithmic work of the Gated DeltaNet-2 per-chunk reverse, per token and head and per
+    row of a state column: the forward step once (a o x, k . x' and the update: 7 flops) and
+    its reverse (k . dx and (b o k) . dx: 5; the key, decay and erase-gate parts and the dx
+    update: 12); the dv state columns add q dO and the query part (3).  Map columns: dk + dv;
+    state columns: dv.  The checkpoint replay and the column sums are not counted."""
+    return n_tokens_heads * dk * (dv * 27 + (dk + dv) * 24)
+
+
+def bench_gdn2_prefill_backward(args, torch, hla, inputs, x, T=BWD_T):
+    """The Gated DeltaNet-2 routed-prefill backward (hla_gdn2_prefill_backward) at B=1,
+    T tokens (8192 by default), H=16, d=128, C=64, bf16, channel-wise gates, computed router
+    gates at tau = 1e-3, with the one-pass workspace: recomputed GDN-2 chunk maps and gates,
+    the composition replay, adjoint and sums (shared with Gated DeltaNet), the GDN-2 chunk
+    reverse per state column (float32 VALU) and the router backward."""
+    W = inputs.WORKLOADS["routed_prefill"]
+    log(f"[gdn2_routed_prefill_backward] generating channel-wise gates B={W.B} T={T} H={W.H}")
+    g = inputs.gen_gdn2_gates(W.B, T, W.H, W.dk, W.dv, seed=0, stream=inputs.STREAM["routed_prefill"])
+    ga, gb, gw = (to_dev(g[n], "f32", torch) for n in ("a", "b", "w"))
+    del g
+    # the first T tokens as their own [B, T, H, d] arrays, like the gates
+    q, k, v = (to_dev(a[:, :T].copy(), W.dtype, torch) for a in (x.q, x.k, x.v))
+    dO = to_dev(inputs.gen_cotangent((W.B, T, W.H, W.dv), seed=0, name="dO"), "f32", torch)
+    dev = k.device
+    d = hla.make_dims(W.B, T, W.H, T, W.dk, W.dv, hla.HLA_BF16, C)
+    ws = torch.empty(hla.workspace_bytes(hla.FN_GDN2_PREFILL_BACKWARD, d), dtype=torch.uint8, device=dev)
+    step = lambda: hla.gdn2_prefill_backward(q, k, v, ga, gb, gw, dO, tau=W.tau, ws=ws)
+    steps = max(3, args.steps // 4)
+    step()
+    torch.cuda.synchronize()
+    hla.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    names = (("bwd_chunk", hla.KERNEL_BWD_CHUNK), ("bwd_save", hla.KERNEL_BWD_SAVE),
+             ("bwd_adjoint", hla.KERNEL_BWD_ADJOINT), ("bwd_reduce", hla.KERNEL_BWD_REDUCE),
+             ("bwd_router", hla.KERNEL_BWD_ROUTER), ("fwd_chunk", hla.KERNEL_CHUNK), ("fwd_gates", hla.KERNEL_GATES))
+    per = {n: hla.timing_read(kid) for n, kid in names}
+    hla.timing_enable(False)
+    ms = {n: tot / steps for n, (tot, cnt) in per.items() if cnt > 0}
+    fl = flops_gdn2_chunk_bwd(W.B * T * W.H, W.dk, W.dv)
+    ach = fl / (ms["bwd_chunk"] / 1e3) / 1e12
+    res = dict(workload=f"Gated DeltaNet-2 routed prefill backward, B={W.B} T={T} H={W.H} d={W.dk} C={C} bf16, "
+                        f"channel-wise gates, computed gates tau={W.tau}",
+               ms_per_step=round(dt * 1e3, 3), tokens_per_s=round(W.B * T / dt, 1),
+               workspace_gib=round(ws.numel() / 2**30, 2), kernel_ms={n: round(v, 3) for n, v in ms.items()},
+               chunk_reverse=dict(kernel="gdn2_chunk_bwd_kernel (outputs and maps, per state column)", bound="alu",
+                                  achieved=round(ach, 2), peak=round(PEAK_FP32_VALU_TFLOPS, 1), unit="TFLOP/s",
+                                  frac=round(ach / PEAK_FP32_VALU_TFLOPS, 4),
+                                  frac_of_unpacked_peak=round(ach / PEAK_FP32_VALU_UNPACKED_TFLOPS, 4),
+                                  flops_per_step=fl))
+    log(f"[gdn2_routed_prefill_backward T={T}] {dt*1e3:.3f} ms/step, {W.B*T/dt/1e6:.3f} M tok/s; chunk reverse "
+        f"{ms['bwd_chunk']:.3f} ms ({ach:.1f} TFLOP/s fp32 VALU); replay {ms['bwd_save']:.3f}, adjoint "
+        f"{ms['bwd_adjoint']:.3f}, reduce {ms['bwd_reduce']:.3f}, router {ms['bwd_router']:.3f} ms")
+    del ws, q, k, v, ga, gb, gw, dO
     torch.cuda.empty_cache()
     return res
 

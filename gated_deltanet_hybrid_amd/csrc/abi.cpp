@@ -184,6 +184,36 @@ void set_chunk_bwd_ws(hla::ChunkBwdArgs& a, const ChunkBwdWs& w, void* ws) {
   a.part_v = reinterpret_cast<float*>(base + w.v_off);
 }
 
+// Workspace of hla_gdn2_chunk_backward: per-workgroup column sums of the per-token
+// gradients (16 state columns per workgroup).
+struct Gdn2ChunkBwdWs {
+  int64_t k_off, a_off, b_off, q_off, v_off, w_off, total;
+};
+Gdn2ChunkBwdWs gdn2_chunk_bwd_ws(const hla_dims_t* d) {
+  const int64_t BHN = d->B * d->H * n_pieces(d), C = kPiece, NC = hla::kGdn2BwdCols;
+  const int64_t nb_out = d->dv / NC, nb_all = nb_out + (d->dk + d->dv) / NC;
+  const int64_t vec = round_up(BHN * nb_all * C * d->dk * 4, 256), per_v = round_up(BHN * 2 * C * d->dv * 4, 256);
+  Gdn2ChunkBwdWs w;
+  w.k_off = 0;
+  w.a_off = vec;
+  w.b_off = 2 * vec;
+  w.q_off = 3 * vec;
+  w.v_off = w.q_off + round_up(BHN * nb_out * C * d->dk * 4, 256);
+  w.w_off = w.v_off + per_v;
+  w.total = w.w_off + per_v;
+  return w;
+}
+
+void set_gdn2_chunk_bwd_ws(hla::Gdn2BwdArgs& a, const Gdn2ChunkBwdWs& w, void* ws) {
+  char* base = static_cast<char*>(ws);
+  a.part_k = reinterpret_cast<float*>(base + w.k_off);
+  a.part_a = reinterpret_cast<float*>(base + w.a_off);
+  a.part_b = reinterpret_cast<float*>(base + w.b_off);
+  a.part_q = reinterpret_cast<float*>(base + w.q_off);
+  a.part_v = reinterpret_cast<float*>(base + w.v_off);
+  a.part_w = reinterpret_cast<float*>(base + w.w_off);
+}
+
 // Workspace of hla_prefill_backward: the forward's transitions, route outputs and routed
 // states, the gradients handed between the passes, then the workspaces of the route, the
 // chunk backward and the composition backward (with history segments of K steps, last, so
@@ -192,7 +222,8 @@ struct PrefillBwdWs {
   int64_t at_off, bc_off, gates_off, mask_off, aidx_off, acnt_off, sr_off, dsr_off, dat_off, dbc_off, dg_off,
       qbar_off, dqbar_off, dkr_off, route_off, chunk_off, comp_off, total;
 };
-PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d, int64_t K) {
+// (hla_gdn2_prefill_backward: the same with the Gated DeltaNet-2 chunk backward's region)
+PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d, int64_t K, int variant = 0) {
   const int64_t N = n_chunks(d), BH = d->B * d->H, BHN = BH * N, e = dtype_bytes(d->dtype);
   PrefillBwdWs w;
   int64_t o = 0;
@@ -216,7 +247,7 @@ PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d, int64_t K) {
   w.dqbar_off = take(BHN * d->dk * 4);
   w.dkr_off = take(d->B * d->T * d->H * d->dk * 4);
   w.route_off = take(route_ws(d));
-  w.chunk_off = take(chunk_bwd_ws(d).total);
+  w.chunk_off = take(variant == 2 ? gdn2_chunk_bwd_ws(d).total : chunk_bwd_ws(d).total);
   w.comp_off = take(compose_bwd_ws(d, K).total);
   w.total = o;
   return w;
@@ -388,9 +419,18 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
       return HLA_OK;
     case HLA_FN_PREFILL_BACKWARD:
     case HLA_FN_PREFILL_BACKWARD_MIN:
+    case HLA_FN_GDN2_PREFILL_BACKWARD:
+    case HLA_FN_GDN2_PREFILL_BACKWARD_MIN: {
       if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
-      *out = fn == HLA_FN_PREFILL_BACKWARD ? (size_t)prefill_bwd_ws(d, n_chunks(d)).total
-                                           : (size_t)(prefill_bwd_ws(d, 1).comp_off + compose_bwd_min(d));
+      const int variant = (fn == HLA_FN_GDN2_PREFILL_BACKWARD || fn == HLA_FN_GDN2_PREFILL_BACKWARD_MIN) ? 2 : 0;
+      const bool one_pass = fn == HLA_FN_PREFILL_BACKWARD || fn == HLA_FN_GDN2_PREFILL_BACKWARD;
+      *out = one_pass ? (size_t)prefill_bwd_ws(d, n_chunks(d), variant).total
+                      : (size_t)(prefill_bwd_ws(d, 1, variant).comp_off + compose_bwd_min(d));
+      return HLA_OK;
+    }
+    case HLA_FN_GDN2_CHUNK_BACKWARD:
+      if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
+      *out = (size_t)gdn2_chunk_bwd_ws(d).total;
       return HLA_OK;
     default: return HLA_ERR_UNSUPPORTED;
   }
@@ -605,36 +645,42 @@ hla_status_t hla_chunk_backward(const hla_dims_t* d, const void* q, const void* 
   return hip_status(hla::launch_chunk_backward(a, d->dtype, d->dk, d->dv, stages, stream));
 }
 
-hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void* k, const void* v,
-                                  const float* beta, const float* alpha, const float* S0, const float* gates_in,
-                                  float tau, const float* dO, float* dq, float* dk, float* dv, float* dbeta,
-                                  float* dalpha, float* dS0, float* dgates, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
-  hla_status_t st = check_dims(d);
-  if (st != HLA_OK) return st;
-  if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !beta || !alpha || !dO || !dq || !dk || !dv || !dbeta || !dalpha) return HLA_ERR_NULL_ARG;
-  if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
-  if (!all_aligned(q, k, v, S0, dS0, ws) || !all_aligned4(beta, alpha, gates_in, dO, dq, dk, dv, dbeta, dalpha, dgates))
-    return HLA_ERR_ALIGN;
-  const PrefillBwdWs w0 = prefill_bwd_ws(d, 1);
+}  // extern "C"
+
+// What the routed-prefill backward hands the per-chunk reverse of its recurrence.
+struct ChunkBwdBufs {
+  const float* S_routed;  // [B,H,N,dk,dv] each chunk's routed start state (the forward's)
+  float* dS_routed;       // out: its gradient (outputs part)
+  const float* dAt;       // gradients of the chunk maps (maps part)
+  const float* dBc;
+  void* ws;               // the chunk reverse's own workspace region
+  const float* dqbar;     // router parts for the per-token sums, or null
+  const float* dk_router;
+};
+
+// The routed-prefill backward of either recurrence (C = 64, raw-key representatives):
+// `maps(At, Bc)` recomputes the forward's chunk maps, `chunk_bwd(bufs, stages)` runs the
+// per-chunk reverse (stages kChunkBwdOut, kChunkBwdMap, kChunkBwdFinalize).  The router, the
+// composition and their reverses are the same for both ([HLA] Methodology paragraphs 2-4).
+template <class Maps, class ChunkBwd>
+static hla_status_t prefill_backward_body(const hla_dims_t* d, int variant, const void* q, const void* k,
+                                          const float* S0, const float* gates_in, float tau, float* dS0, float* dgates,
+                                          void* ws, size_t ws_bytes, hipStream_t stream, Maps maps,
+                                          ChunkBwd chunk_bwd) {
+  const PrefillBwdWs w0 = prefill_bwd_ws(d, 1, variant);
   const int64_t K = ws ? seg_len_for(d, (int64_t)ws_bytes - w0.comp_off) : -1;
   if (K < 0) return HLA_ERR_WORKSPACE;
-  const PrefillBwdWs w = prefill_bwd_ws(d, K);
+  const PrefillBwdWs w = prefill_bwd_ws(d, K, variant);
   char* base = static_cast<char*>(ws);
   const int32_t N = (int32_t)n_chunks(d);
   auto at = [&](int64_t off) { return static_cast<void*>(base + off); };
   auto fat = [&](int64_t off) { return reinterpret_cast<float*>(base + off); };
   // 1. forward: chunk maps, then gates, mask and lists (the routed states come from the
   //    composition backward's forward replay)
-  hla::ChunkArgs c{};
-  c.q = q; c.k = k; c.v = v; c.beta = beta; c.alpha = alpha;
-  c.B = d->B; c.T = d->T; c.H = d->H; c.ld_T = d->ld_T; c.N = N;
-  c.At = at(w.at_off); c.Bc = at(w.bc_off);
-  hipError_t e = hla::launch_chunk(c, d->dtype, d->dk, d->dv, true, false, stream);
+  hipError_t e = maps(at(w.at_off), at(w.bc_off));
   if (e != hipSuccess) return HLA_ERR_HIP;
   hla::RouteArgs r{};
-  r.q = q; r.reps = k; r.n_rep = kPiece; r.ld_R = d->ld_T; r.At = c.At; r.Bc = c.Bc; r.S0 = S0;
+  r.q = q; r.reps = k; r.n_rep = kPiece; r.ld_R = d->ld_T; r.At = at(w.at_off); r.Bc = at(w.bc_off); r.S0 = S0;
   r.gates_in = gates_in; r.tau = tau; r.gates = fat(w.gates_off);
   r.mask = reinterpret_cast<uint8_t*>(base + w.mask_off);
   r.active_idx = reinterpret_cast<int32_t*>(base + w.aidx_off);
@@ -647,18 +693,11 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   if (e != hipSuccess) return HLA_ERR_HIP;
   float* dg = dgates ? dgates : fat(w.dg_off);
   hla::ComposeBwdArgs m{};
-  m.At = c.At; m.Bc = c.Bc; m.gates = r.gates; m.mask = r.mask; m.S0 = S0; m.dS = fat(w.dsr_off);
+  m.At = r.At; m.Bc = r.Bc; m.gates = r.gates; m.mask = r.mask; m.S0 = S0; m.dS = fat(w.dsr_off);
   m.dAt = fat(w.dat_off); m.dBc = fat(w.dbc_off); m.dgates = dg; m.dS0 = dS0; m.S_routed = fat(w.sr_off);
   set_compose_bwd_ws(m, compose_bwd_ws(d, K), at(w.comp_off));
   m.B = d->B; m.H = d->H; m.N = N;
-  hla::ChunkBwdArgs cb{};
-  cb.q = q; cb.k = k; cb.v = v; cb.beta = beta; cb.alpha = alpha;
-  cb.B = d->B; cb.T = d->T; cb.H = d->H; cb.ld_T = d->ld_T; cb.N = N;
-  cb.have_out = 1; cb.have_map = 1;
-  cb.chunk_init = m.S_routed; cb.dO = dO; cb.dchunk_init = fat(w.dsr_off);
-  cb.dAt = m.dAt; cb.dBc = m.dBc;
-  set_chunk_bwd_ws(cb, chunk_bwd_ws(d), at(w.chunk_off));
-  cb.dq = dq; cb.dk = dk; cb.dv = dv; cb.dbeta = dbeta; cb.dalpha = dalpha;
+  ChunkBwdBufs cb{fat(w.sr_off), fat(w.dsr_off), m.dAt, m.dBc, at(w.chunk_off), nullptr, nullptr};
   // 2. composition backward, forward replay: with more than one history segment the
   //    checkpoints and the routed states (from the bf16 composition, or the backward's own
   //    replay), then the reordered maps; with one segment the routed states come from the
@@ -677,8 +716,7 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   }
   m.S_routed = nullptr;
   // 3. outputs part of the chunk backward: dS~ and the chunk-local partial sums
-  cb.c0 = 0; cb.c1 = N;
-  e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdOut, stream);
+  e = chunk_bwd(cb, hla::kChunkBwdOut);
   if (e != hipSuccess) return HLA_ERR_HIP;
   // 4. composition backward per history segment, last to first: replay the segment's steps
   //    keeping their states (already done for a single segment), then the adjoint and the
@@ -692,8 +730,7 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
   e = hla::launch_compose_backward(m, d->dtype, d->dk, d->dv, hla::kComposeBwdFinish, stream);
   if (e != hipSuccess) return HLA_ERR_HIP;
   // then the maps part of the chunk backward
-  cb.c0 = 0; cb.c1 = N;
-  e = hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdMap, stream);
+  e = chunk_bwd(cb, hla::kChunkBwdMap);
   if (e != hipSuccess) return HLA_ERR_HIP;
   // 5. router (computed gates only), then the per-token sums
   if (!gates_in && N > 1) {
@@ -706,7 +743,118 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
     cb.dqbar = rb.dqbar;
     cb.dk_router = rb.dk_router;
   }
-  return hip_status(hla::launch_chunk_backward(cb, d->dtype, d->dk, d->dv, hla::kChunkBwdFinalize, stream));
+  return hip_status(chunk_bwd(cb, hla::kChunkBwdFinalize));
+}
+
+extern "C" {
+
+hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                                  const float* beta, const float* alpha, const float* S0, const float* gates_in,
+                                  float tau, const float* dO, float* dq, float* dk, float* dv, float* dbeta,
+                                  float* dalpha, float* dS0, float* dgates, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !beta || !alpha || !dO || !dq || !dk || !dv || !dbeta || !dalpha) return HLA_ERR_NULL_ARG;
+  if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
+  if (!all_aligned(q, k, v, S0, dS0, ws) || !all_aligned4(beta, alpha, gates_in, dO, dq, dk, dv, dbeta, dalpha, dgates))
+    return HLA_ERR_ALIGN;
+  const int32_t N = (int32_t)n_chunks(d);
+  auto maps = [&](void* At, void* Bc) {
+    hla::ChunkArgs c{};
+    c.q = q; c.k = k; c.v = v; c.beta = beta; c.alpha = alpha;
+    c.B = d->B; c.T = d->T; c.H = d->H; c.ld_T = d->ld_T; c.N = N;
+    c.At = At; c.Bc = Bc;
+    return hla::launch_chunk(c, d->dtype, d->dk, d->dv, true, false, stream);
+  };
+  auto chunk_bwd = [&](const ChunkBwdBufs& p, int stages) {
+    hla::ChunkBwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.alpha = alpha;
+    a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = N;
+    a.c0 = 0; a.c1 = N;
+    a.have_out = 1; a.have_map = 1;
+    a.chunk_init = p.S_routed; a.dO = dO; a.dchunk_init = p.dS_routed; a.dAt = p.dAt; a.dBc = p.dBc;
+    set_chunk_bwd_ws(a, chunk_bwd_ws(d), p.ws);
+    a.dqbar = p.dqbar; a.dk_router = p.dk_router;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dalpha = dalpha;
+    return hla::launch_chunk_backward(a, d->dtype, d->dk, d->dv, stages, stream);
+  };
+  return prefill_backward_body(d, 0, q, k, S0, gates_in, tau, dS0, dgates, ws, ws_bytes, stream, maps, chunk_bwd);
+}
+
+}  // extern "C"
+
+static hla::Gdn2BwdArgs gdn2_bwd_args(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                                      const float* a_decay, const float* b_erase, const float* w_write, float* dq,
+                                      float* dk, float* dv, float* da, float* db, float* dw) {
+  hla::Gdn2BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.ga = a_decay; a.gb = b_erase; a.gw = w_write;
+  a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.N = (int32_t)n_pieces(d);
+  a.c0 = 0; a.c1 = a.N;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.da = da; a.db = db; a.dw = dw;
+  return a;
+}
+
+extern "C" {
+
+hla_status_t hla_gdn2_chunk_backward(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                                     const float* a_decay, const float* b_erase, const float* w_write,
+                                     const float* chunk_init, const float* dO, const float* dAt, const float* dBc,
+                                     float* dq, float* dk, float* dv, float* da, float* db, float* dw,
+                                     float* dchunk_init, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
+  const bool have_out = chunk_init || dO, have_map = dAt || dBc;
+  if (!have_out && !have_map) return HLA_ERR_NULL_ARG;
+  if (have_out && (!chunk_init || !dO || !q || !dchunk_init)) return HLA_ERR_NULL_ARG;
+  if (have_map && (!dAt || !dBc)) return HLA_ERR_NULL_ARG;
+  if (!k || !v || !a_decay || !b_erase || !w_write || !dq || !dk || !dv || !da || !db || !dw) return HLA_ERR_NULL_ARG;
+  if (!all_aligned(q, k, v, chunk_init, dAt, dBc, dchunk_init, ws) ||
+      !all_aligned4(a_decay, b_erase, w_write, dO, dq, dk, dv, da, db, dw))
+    return HLA_ERR_ALIGN;
+  const Gdn2ChunkBwdWs w = gdn2_chunk_bwd_ws(d);
+  if (!ws || (int64_t)ws_bytes < w.total) return HLA_ERR_WORKSPACE;
+  hla::Gdn2BwdArgs a = gdn2_bwd_args(d, q, k, v, a_decay, b_erase, w_write, dq, dk, dv, da, db, dw);
+  a.have_out = have_out; a.have_map = have_map;
+  a.chunk_init = chunk_init; a.dO = dO; a.dAt = dAt; a.dBc = dBc; a.dchunk_init = dchunk_init;
+  set_gdn2_chunk_bwd_ws(a, w, ws);
+  const int stages = (have_out ? hla::kChunkBwdOut : 0) | (have_map ? hla::kChunkBwdMap : 0) | hla::kChunkBwdFinalize;
+  return hip_status(hla::launch_gdn2_chunk_backward(a, d->dtype, d->dk, d->dv, stages, stream));
+}
+
+hla_status_t hla_gdn2_prefill_backward(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                                       const float* a_decay, const float* b_erase, const float* w_write,
+                                       const float* S0, const float* gates_in, float tau, const float* dO, float* dq,
+                                       float* dk, float* dv, float* da, float* db, float* dw, float* dS0,
+                                       float* dgates, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !a_decay || !b_erase || !w_write || !dO || !dq || !dk || !dv || !da || !db || !dw)
+    return HLA_ERR_NULL_ARG;
+  if (std::isnan(tau)) return HLA_ERR_BAD_SHAPE;
+  if (!all_aligned(q, k, v, S0, dS0, ws) ||
+      !all_aligned4(a_decay, b_erase, w_write, gates_in, dO, dq, dk, dv, da, db, dw, dgates))
+    return HLA_ERR_ALIGN;
+  const int32_t N = (int32_t)n_chunks(d);
+  auto maps = [&](void* At, void* Bc) {
+    hla::ChunkArgs c{};
+    c.k = k; c.v = v; c.ga = a_decay; c.gb = b_erase; c.gw = w_write; c.variant = 2;
+    c.B = d->B; c.T = d->T; c.H = d->H; c.ld_T = d->ld_T; c.N = N;
+    c.At = At; c.Bc = Bc;
+    return hla::launch_gdn2_chunk(c, d->dtype, d->dk, d->dv, false, stream);
+  };
+  auto chunk_bwd = [&](const ChunkBwdBufs& p, int stages) {
+    hla::Gdn2BwdArgs a = gdn2_bwd_args(d, q, k, v, a_decay, b_erase, w_write, dq, dk, dv, da, db, dw);
+    a.have_out = 1; a.have_map = 1;
+    a.chunk_init = p.S_routed; a.dO = dO; a.dchunk_init = p.dS_routed; a.dAt = p.dAt; a.dBc = p.dBc;
+    set_gdn2_chunk_bwd_ws(a, gdn2_chunk_bwd_ws(d), p.ws);
+    a.dqbar = p.dqbar; a.dk_router = p.dk_router;
+    return hla::launch_gdn2_chunk_backward(a, d->dtype, d->dk, d->dv, stages, stream);
+  };
+  return prefill_backward_body(d, 2, q, k, S0, gates_in, tau, dS0, dgates, ws, ws_bytes, stream, maps, chunk_bwd);
 }
 
 // Shared checks of the two decode entry points (everything but the per-token gates).

@@ -278,6 +278,45 @@ struct ChunkBwdArgs {
 constexpr int kChunkBwdOut = 1, kChunkBwdMap = 2, kChunkBwdFinalize = 4;
 hipError_t launch_chunk_backward(const ChunkBwdArgs& a, int dtype, int dk, int dv, int stages, hipStream_t s);
 
+// Backward of the Gated DeltaNet-2 per-chunk work: the outputs from chunk_init and the
+// chunk maps, token by token per state column (channel-wise decay ga, erase gate gb and
+// write gate gw in place of alpha and beta), then the per-token sums.  Stages as for
+// launch_chunk_backward.
+struct Gdn2BwdArgs {
+  const void* q;            // [B,ld_T,H,dk] (dtype)
+  const void* k;
+  const void* v;            // [B,ld_T,H,dv]
+  const float* ga;          // [B,ld_T,H,dk] decay
+  const float* gb;          // [B,ld_T,H,dk] erase gate
+  const float* gw;          // [B,ld_T,H,dv] write gate
+  int64_t B, T, H, ld_T;
+  int32_t N;                // 64-token chunks
+  int32_t c0, c1;           // the chunks c0 <= c < c1 that the outputs and maps parts take
+  int32_t have_out, have_map;
+  const float* chunk_init;  // [B,H,N,dk,dv] (have_out)
+  const float* dO;          // [B,T,H,dv] (have_out)
+  const float* dAt;         // [B,H,N,dk,dk] (have_map)
+  const float* dBc;         // [B,H,N,dk,dv]
+  float* dchunk_init;       // out [B,H,N,dk,dv] (have_out)
+  // workspace: per-workgroup column sums (16 state columns per workgroup)
+  float* part_k;            // [B,H,N,(dv + dk + dv)/16,64,dk]
+  float* part_a;            // same
+  float* part_b;            // same
+  float* part_q;            // [B,H,N,dv/16,64,dk]
+  float* part_v;            // [B,H,N,2,64,dv]: outputs part, maps part
+  float* part_w;            // same
+  const float* dqbar;       // [B,H,N,dk] router parts added by the finalize pass, or null
+  const float* dk_router;   // [B,T,H,dk]
+  float* dq;                // out [B,T,H,dk]
+  float* dk;                // out [B,T,H,dk]
+  float* dv;                // out [B,T,H,dv]
+  float* da;                // out [B,T,H,dk]
+  float* db;                // out [B,T,H,dk]
+  float* dw;                // out [B,T,H,dv]
+};
+constexpr int kGdn2BwdCols = 16;  // state columns per workgroup of the Gated DeltaNet-2 reverse
+hipError_t launch_gdn2_chunk_backward(const Gdn2BwdArgs& a, int dtype, int dk, int dv, int stages, hipStream_t s);
+
 struct RouterBwdArgs {
   const void* q;         // [B,ld_T,H,dk] (dtype)
   const void* k;         // [B,ld_T,H,dk]: the representatives (raw keys, n_rep = 64)

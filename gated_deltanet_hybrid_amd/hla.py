@@ -24,6 +24,7 @@ KERNEL_PREFILL = 11
 FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX, FN_WU_HANDOFF, FN_CHUNK_REPS = 0, 1, 2, 3, 4
 FN_COMPOSE_BACKWARD, FN_PREFILL_BACKWARD, FN_CHUNK_BACKWARD = 5, 6, 7
 FN_COMPOSE_BACKWARD_MIN, FN_PREFILL_BACKWARD_MIN = 8, 9  # smallest workspaces (history segments)
+FN_GDN2_CHUNK_BACKWARD, FN_GDN2_PREFILL_BACKWARD, FN_GDN2_PREFILL_BACKWARD_MIN = 10, 11, 12
 CHUNK = 64
 MAX_CACHE_SLOTS = 1024
 REPS_SCRATCH_BYTES = 32 << 20  # fixed device scratch of chunk_reps_noalloc
@@ -67,6 +68,11 @@ _SIGS = {
                                             _P, _P, _P, ctypes.c_size_t, _P]),
     "hla_prefill_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
                                               _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "hla_gdn2_chunk_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                 _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "hla_gdn2_prefill_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P,
+                                                   ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                   ctypes.c_size_t, _P]),
     "hla_timing_enable": (ctypes.c_int32, [ctypes.c_int32]),
     "hla_timing_read": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "hla_gdn_decode": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -483,6 +489,69 @@ def prefill_backward(q, k, v, beta, alpha, dO, tau=1e-3, gates_in=None, S0=None,
                                           _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dalpha"]),
                                           _ptr(out["dS0"]), _ptr(out["dgates"]), _ptr(ws),
                                           0 if ws is None else ws.numel(), _stream(dev)), "hla_prefill_backward")
+    return out
+
+
+def _gdn2_grads(B, T, H, dk, dv, dev):
+    f32 = dict(dtype=torch.float32, device=dev)
+    return dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
+                dv=torch.empty((B, T, H, dv), **f32), da=torch.empty((B, T, H, dk), **f32),
+                db=torch.empty((B, T, H, dk), **f32), dw=torch.empty((B, T, H, dv), **f32))
+
+
+def gdn2_chunk_backward(q, k, v, a_decay, b_erase, w_write, chunk_init=None, dO=None, dAt=None, dBc=None, ws=None):
+    """chunk_backward for the Gated DeltaNet-2 recurrence.  Returns dict(dq, dk, dv, da, db,
+    dw, dchunk_init (or None)), all float32."""
+    B, T, H, dk, ld_T = _token_view(k, "k")
+    dv = v.shape[-1]
+    d = make_dims(B, T, H, ld_T, dk, dv, _dtype_code(k), CHUNK)
+    _gdn2_gates(d, a_decay, b_erase, w_write)
+    N = math.ceil(T / CHUNK)
+    dev = k.device
+    _need(chunk_init, (B, H, N, dk, dv), torch.float32, "chunk_init")
+    _need(dO, (B, T, H, dv), torch.float32, "dO")
+    _need(dAt, (B, H, N, dk, dk), torch.float32, "dAt")
+    _need(dBc, (B, H, N, dk, dv), torch.float32, "dBc")
+    out = _gdn2_grads(B, T, H, dk, dv, dev)
+    out["dchunk_init"] = (torch.empty((B, H, N, dk, dv), dtype=torch.float32, device=dev)
+                          if chunk_init is not None else None)
+    if ws is None:
+        ws = _workspace(workspace_bytes(FN_GDN2_CHUNK_BACKWARD, d), dev)
+    _check(library().hla_gdn2_chunk_backward(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a_decay),
+                                             _ptr(b_erase), _ptr(w_write), _ptr(chunk_init), _ptr(dO), _ptr(dAt),
+                                             _ptr(dBc), *(_ptr(out[n]) for n in ("dq", "dk", "dv", "da", "db", "dw")),
+                                             _ptr(out["dchunk_init"]), _ptr(ws), 0 if ws is None else ws.numel(),
+                                             _stream(dev)), "hla_gdn2_chunk_backward")
+    return out
+
+
+def gdn2_prefill_backward(q, k, v, a_decay, b_erase, w_write, dO, tau=1e-3, gates_in=None, S0=None, want_dS0=True,
+                          want_dgates=True, ws=None):
+    """prefill_backward for the Gated DeltaNet-2 routed prefill.  Returns dict(dq, dk, dv,
+    da, db, dw, dS0, dgates), float32 (dS0 / dgates None unless wanted); `ws` may be as
+    small as workspace_bytes(FN_GDN2_PREFILL_BACKWARD_MIN)."""
+    B, T, H, dk, ld_T = _token_view(k, "k")
+    dv = v.shape[-1]
+    d = make_dims(B, T, H, ld_T, dk, dv, _dtype_code(k), CHUNK)
+    _gdn2_gates(d, a_decay, b_erase, w_write)
+    N = math.ceil(T / CHUNK)
+    dev = k.device
+    _need(dO, (B, T, H, dv), torch.float32, "dO")
+    _need(S0, (B, H, dk, dv), torch.float32, "S0")
+    _need(gates_in, (B, H, N, N), torch.float32, "gates_in")
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = _gdn2_grads(B, T, H, dk, dv, dev)
+    out["dS0"] = torch.empty((B, H, dk, dv), **f32) if want_dS0 else None
+    out["dgates"] = torch.empty((B, H, N, N), **f32) if want_dgates else None
+    if ws is None:
+        ws = _workspace(workspace_bytes(FN_GDN2_PREFILL_BACKWARD, d), dev)
+    _check(library().hla_gdn2_prefill_backward(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a_decay),
+                                               _ptr(b_erase), _ptr(w_write), _ptr(S0), _ptr(gates_in),
+                                               ctypes.c_float(tau), _ptr(dO),
+                                               *(_ptr(out[n]) for n in ("dq", "dk", "dv", "da", "db", "dw")),
+                                               _ptr(out["dS0"]), _ptr(out["dgates"]), _ptr(ws),
+                                               0 if ws is None else ws.numel(), _stream(dev)),
+           "hla_gdn2_prefill_backward")
     return out
 
 

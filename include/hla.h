@@ -92,7 +92,10 @@ typedef enum {
   HLA_FN_PREFILL_BACKWARD = 6, /* workspace of hla_prefill_backward (one pass) */
   HLA_FN_CHUNK_BACKWARD = 7,   /* workspace of hla_chunk_backward */
   HLA_FN_COMPOSE_BACKWARD_MIN = 8, /* smallest workspace hla_compose_backward accepts */
-  HLA_FN_PREFILL_BACKWARD_MIN = 9  /* smallest workspace hla_prefill_backward accepts */
+  HLA_FN_PREFILL_BACKWARD_MIN = 9, /* smallest workspace hla_prefill_backward accepts */
+  HLA_FN_GDN2_CHUNK_BACKWARD = 10, /* workspace of hla_gdn2_chunk_backward */
+  HLA_FN_GDN2_PREFILL_BACKWARD = 11, /* workspace of hla_gdn2_prefill_backward (one pass) */
+  HLA_FN_GDN2_PREFILL_BACKWARD_MIN = 12 /* smallest workspace hla_gdn2_prefill_backward accepts */
 } hla_fn_t;
 
 /*
@@ -431,6 +434,38 @@ hla_status_t hla_prefill_backward(const hla_dims_t* d, const void* q, const void
                                   const float* gates_in, float tau, const float* dO, float* dq,
                                   float* dk, float* dv, float* dbeta, float* dalpha, float* dS0,
                                   float* dgates, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hla_gdn2_chunk_backward, hla_gdn2_prefill_backward -- hla_chunk_backward and
+ * hla_prefill_backward for the Gated DeltaNet-2 recurrence (the formula of
+ * hla_gdn2_chunk_transitions: S' = S diag(a_t), S = S' - (S' k_t)(b_t o k_t)^T +
+ * (w_t o v_t) k_t^T, o_t = S q_t; [GDN2] the Gated DeltaNet-2 abstract).  The per-token
+ * gates a_decay, b_erase [B, ld_T, H, dk] and w_write [B, ld_T, H, dv] (float32) take the
+ * place of alpha and beta, and their gradients da, db [B, T, H, dk] and dw [B, T, H, dv]
+ * (float32 out) the place of dalpha and dbeta.  The reverse of a chunk runs token by token
+ * per state column in float32, from the state in front of every 8-token block: per token
+ *     du = k . dx,  dp = -(b o k) . dx,  dv[col] += w[col] du,  dw[col] += v[col] du,
+ *     dk += dx o (u - b p) + dp x',  db += -p k o dx,  dx' = dx + dp k,  da += dx' o x,
+ *     dx <- a o dx'
+ * (x the column before the token, x' = a o x, p = k . x', u = w[col] v[col]).  The
+ * routed prefill's router, composition and their reverses are those of
+ * hla_prefill_backward, unchanged.  Every other argument, output, mode, workspace rule
+ * (HLA_FN_GDN2_CHUNK_BACKWARD, HLA_FN_GDN2_PREFILL_BACKWARD, down to
+ * HLA_FN_GDN2_PREFILL_BACKWARD_MIN with history segments) and error is as for the Gated
+ * DeltaNet calls.
+ */
+hla_status_t hla_gdn2_chunk_backward(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                                     const float* a_decay, const float* b_erase, const float* w_write,
+                                     const float* chunk_init, const float* dO, const float* dAt,
+                                     const float* dBc, float* dq, float* dk, float* dv, float* da,
+                                     float* db, float* dw, float* dchunk_init, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+hla_status_t hla_gdn2_prefill_backward(const hla_dims_t* d, const void* q, const void* k, const void* v,
+                                       const float* a_decay, const float* b_erase,
+                                       const float* w_write, const float* S0, const float* gates_in,
+                                       float tau, const float* dO, float* dq, float* dk, float* dv,
+                                       float* da, float* db, float* dw, float* dS0, float* dgates,
+                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes that entry point `fn` needs for dims `d`; n_rep is the number of
  * representatives per chunk for HLA_FN_CHUNK_REPS (C / window; it must divide C) and is

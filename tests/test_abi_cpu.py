@@ -375,3 +375,73 @@ def test_prefill_backward_validation(lib):
     a = list(full)
     a[0] = PU
     assert call(a) == ALIGN
+
+
+def test_gdn2_backward_workspace_sizes(lib):
+    """Column sums of 16-column workgroups: dk, da and db over every slot, dq over the
+    outputs' slots, dv and dw per part; the prefill backward differs from Gated DeltaNet's
+    by the chunk reverse's region only."""
+    d = dims(B=2, T=130, H=3, dk=128, dv=64, dtype=1)  # N = 3
+    BHN, nb_out, nb_all = 6 * 3, 64 // 16, 64 // 16 + (128 + 64) // 16
+    vec = _r(BHN * nb_all * 64 * 128 * 4)
+    g2 = 3 * vec + _r(BHN * nb_out * 64 * 128 * 4) + 2 * _r(BHN * 2 * 64 * 64 * 4)
+    assert hla.workspace_bytes(hla.FN_GDN2_CHUNK_BACKWARD, d) == g2
+    g1 = hla.workspace_bytes(hla.FN_CHUNK_BACKWARD, d)
+    for one, two in ((hla.FN_PREFILL_BACKWARD, hla.FN_GDN2_PREFILL_BACKWARD),
+                     (hla.FN_PREFILL_BACKWARD_MIN, hla.FN_GDN2_PREFILL_BACKWARD_MIN)):
+        assert hla.workspace_bytes(two, d) - hla.workspace_bytes(one, d) == g2 - g1
+    out = ctypes.c_size_t()
+    for fn in (hla.FN_GDN2_CHUNK_BACKWARD, hla.FN_GDN2_PREFILL_BACKWARD, hla.FN_GDN2_PREFILL_BACKWARD_MIN):
+        assert lib.hla_workspace_bytes(fn, ctypes.byref(dims(C=128)), 0, ctypes.byref(out)) == UNSUPPORTED
+
+
+def test_gdn2_chunk_backward_validation(lib):
+    d = dims()
+    f = lib.hla_gdn2_chunk_backward
+    need = hla.workspace_bytes(hla.FN_GDN2_CHUNK_BACKWARD, d)
+    # (d, q, k, v, a, b, w, chunk_init, dO, dAt, dBc, dq, dk, dv, da, db, dw, dinit, ws, ws_bytes, s)
+    full = [P] * 17
+    assert f(ctypes.byref(d), *full, None, 0, None) == WORKSPACE
+    assert f(ctypes.byref(d), *full, P, need - 1, None) == WORKSPACE
+    neither = list(full)
+    neither[6:10] = [None] * 4
+    assert f(ctypes.byref(d), *neither, P, need, None) == NULL_ARG
+    half = list(full)
+    half[7] = None                                                   # chunk_init without dO
+    assert f(ctypes.byref(d), *half, P, need, None) == NULL_ARG
+    for i in (1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 15):
+        a = list(full)
+        a[i] = None
+        assert f(ctypes.byref(d), *a, P, need, None) == NULL_ARG, i
+    a = list(full)
+    a[4] = P + 2  # the erase gate needs 4 bytes
+    assert f(ctypes.byref(d), *a, P, need, None) == ALIGN
+    a = list(full)
+    a[1] = PU
+    assert f(ctypes.byref(d), *a, P, need, None) == ALIGN
+    assert f(ctypes.byref(dims(C=128)), *full, P, need, None) == UNSUPPORTED
+
+
+def test_gdn2_prefill_backward_validation(lib):
+    d = dims()
+    f = lib.hla_gdn2_prefill_backward
+    need = hla.workspace_bytes(hla.FN_GDN2_PREFILL_BACKWARD, d)
+    # (d, q, k, v, a, b, w, S0, gates_in, tau, dO, dq, dk, dv, da, db, dw, dS0, dgates, ws, ws_bytes, s)
+    def call(args, tau=1e-3, ws=P, nb=need, dd=d):
+        return f(ctypes.byref(dd), *args[:8], ctypes.c_float(tau), *args[8:], ws, nb, None)
+    full = [P] * 17  # q .. gates_in (8), then dO .. dgates (9)
+    for i in (0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13, 14):
+        a = list(full)
+        a[i] = None
+        assert call(a) == NULL_ARG, i
+    opt = list(full)
+    opt[6] = opt[7] = opt[15] = opt[16] = None  # S0, gates_in, dS0, dgates are optional
+    mn = hla.workspace_bytes(hla.FN_GDN2_PREFILL_BACKWARD_MIN, d)
+    assert mn < need
+    assert call(opt, nb=mn - 1) == WORKSPACE
+    assert call(opt, ws=None, nb=need) == WORKSPACE
+    assert call(full, tau=float("nan")) == BAD_SHAPE
+    assert call(full, dd=dims(C=256)) == UNSUPPORTED
+    a = list(full)
+    a[5] = P + 2
+    assert call(a) == ALIGN
