@@ -21,12 +21,14 @@ Sources (cited by page title and section):
 Orientation: the math state S has shape [dv, dk] and acts on keys (o = S q).  Chunk
 transitions act on the right: S_end = S_start @ A + B with A [dk, dk], B [dv, dk].
 
-Gradients (``oracle.grad``, and ``oracle.grad_gdn2`` for the Gated DeltaNet-2 recurrence)
-are those of the same forward, taken by torch.autograd on a float64 CPU restatement of it.
+Gradients (``oracle.grad``, ``oracle.grad_gdn2`` for the Gated DeltaNet-2 recurrence and
+``oracle.grad_reps`` for the learned representatives) are those of the same forward, taken
+by torch.autograd on a float64 CPU restatement of it.
 
 Parity status: every function is pinned by tests/test_oracle_pins.py (gradients by
-tests/test_oracle_grad_pins.py and tests/test_oracle_grad_gdn2_pins.py) except the
-readings listed in ``PARITY_UNPINNED`` (no printed number can confirm them).
+tests/test_oracle_grad_pins.py, tests/test_oracle_grad_gdn2_pins.py and
+tests/test_oracle_grad_reps_pins.py) except the readings listed in ``PARITY_UNPINNED`` (no
+printed number can confirm them).
 """
 from .gdn import (  # noqa: F401
     gdn_recurrent,
@@ -62,6 +64,7 @@ from .gdn2 import (  # noqa: F401
     gdn2_hla_prefill,
     gdn2_decode_step,
 )
+from .grad_reps import window_reps_backward  # noqa: F401
 from .grad_gdn2 import (  # noqa: F401
     gdn2_chunk_outputs_backward,
     gdn2_chunk_transitions_backward,
