@@ -121,7 +121,8 @@ def timed_kernels(fn, steps, warmup, torch, hla):
     torch.cuda.synchronize()
     hla.timing_enable(True)
     dt = timed(fn, steps, 0, torch)
-    names = (("chunk", hla.KERNEL_CHUNK), ("scan", hla.KERNEL_SCAN), ("prefill", hla.KERNEL_PREFILL))
+    names = (("chunk", hla.KERNEL_CHUNK), ("scan", hla.KERNEL_SCAN), ("prefill", hla.KERNEL_PREFILL),
+             ("bwd_reps", hla.KERNEL_BWD_REPS))
     kms = {}
     for name, kid in names:
         ms, n = hla.timing_read(kid)
@@ -320,6 +321,44 @@ def bench_routed_learned_reps(args, torch, hla, inputs, x, window=32):
         active_pairs=r["active_pairs"], kernel_ms=r["kernel_ms"], reps_pool=r["reps_pool"])
 
 
+def flops_reps_bwd(n_tokens_heads, dk):
+    """Algorithmic matrix work of the learned-representative backward per token and head:
+    the recomputed projections Q, K, V (3 x 2 dk^2), dX = dQ Wq + dK Wk + dV Wv (3 x 2 dk^2)
+    and the weight gradients dQ^T X, dK^T X, dV^T X (3 x 2 dk^2); the window attention and the
+    per-window vectors are not counted."""
+    return n_tokens_heads * 18 * dk * dk
+
+
+def bench_reps_backward(args, torch, hla, inputs, x, window=32):
+    """hla_chunk_reps_backward at the long-context shape (B=1, T=32768, H=16, dk=128, bf16,
+    per-head seeded weights with the folded query projection, window 32): from a seeded
+    gradient of every representative row to dk and the five weight gradients."""
+    W = inputs.WORKLOADS["routed_prefill"]
+    pooler = inputs.gen_pooler_weights(W.H, W.dk, dtype=W.dtype, seed=0, stream=inputs.STREAM["routed_prefill"])
+    Wd = {n: to_dev(a, W.dtype, torch) for n, a in pooler.items()}
+    k = to_dev(x.k, W.dtype, torch)
+    N = math.ceil(W.T / C)
+    dreps = to_dev(inputs.gen_cotangent((W.B, N * (C // window), W.H, W.dk), seed=0, name="dreps"), "f32", torch)
+    d = hla.make_dims(W.B, W.T, W.H, W.T, W.dk, W.dk, hla.HLA_BF16, C)
+    ws = torch.empty(hla.workspace_bytes(hla.FN_CHUNK_REPS_BACKWARD, d, 1), dtype=torch.uint8, device=k.device)
+    step = lambda: hla.chunk_reps_backward(k, Wd, dreps, window=window, ws=ws)
+    steps = max(3, args.steps // 2)
+    dt, kms = timed_kernels(step, steps, 2, torch, hla)
+    ms = kms.get("bwd_reps", dt * 1e3)
+    fl = flops_reps_bwd(W.B * W.T * W.H, W.dk)
+    ach = fl / (ms / 1e3) / 1e12
+    res = dict(workload=f"learned-representative backward, B={W.B} T={W.T} H={W.H} dk={W.dk} bf16, window {window}, "
+                        "per-head weights with the folded query projection",
+               ms_per_step=round(dt * 1e3, 3), kernel_ms=round(ms, 3), workspace_gib=round(ws.numel() / 2**30, 2),
+               roofline=dict(kernel="reps_bwd_tile_kernel + reps_bwd_reduce_kernel", bound="mfma",
+                             achieved=round(ach, 2), peak=PEAK_FP32_MFMA_TFLOPS, unit="TFLOP/s",
+                             frac=round(ach / PEAK_FP32_MFMA_TFLOPS, 4), flops_per_call=fl))
+    log(f"[learned_reps_backward] {dt*1e3:.3f} ms/call, kernels {ms:.3f} ms ({ach:.1f} TFLOP/s fp32 MFMA)")
+    del ws, k, dreps, Wd
+    torch.cuda.empty_cache()
+    return res
+
+
 def routed_inputs(inputs):
     W = inputs.WORKLOADS["routed_prefill"]
     log(f"[routed_prefill] generating inputs B={W.B} T={W.T} H={W.H} d={W.dk}")
@@ -338,6 +377,7 @@ SECONDARY = {
     "routed_prefill_backward": lambda args, torch, hla, inputs, x: bench_prefill_backward(args, torch, hla, inputs, x),
     "gdn2_routed_prefill_backward": lambda args, torch, hla, inputs, x: bench_gdn2_prefill_backward(
         args, torch, hla, inputs, x),
+    "learned_reps_backward": bench_reps_backward,
     "decode": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs),
     "gdn2_decode": lambda args, torch, hla, inputs, x: bench_decode(args, torch, hla, inputs, gdn2=True),
     "native_prefill": lambda args, torch, hla, inputs, x: bench_native_prefill(args, torch, hla, inputs),
@@ -1238,7 +1278,7 @@ def main():
         if unknown:
             print(f"unknown lines {unknown}; known: routed_prefill, {', '.join(extra)}", file=sys.stderr)
             sys.exit(2)
-        x = routed_inputs(inputs) if any(n.startswith(("routed", "gdn2_routed")) for n in names) else None
+        x = routed_inputs(inputs) if any(n.startswith(("routed", "gdn2_routed", "learned")) for n in names) else None
         out = {}
         for n in names:
             out[n] = bench_routed_prefill(args, torch, hla, inputs, x=x)[0] if n == "routed_prefill" else \

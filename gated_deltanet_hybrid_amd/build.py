@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libhla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["chunk.hip", "scan.hip", "prefill.hip", "route.hip", "compose.hip", "decode.hip", "reps.hip", "gdn2.hip", "compose_bwd.hip", "chunk_bwd.hip", "gdn2_bwd.hip", "router_bwd.hip", "abi.cpp", "timing.cpp"]
+SOURCES = ["chunk.hip", "scan.hip", "prefill.hip", "route.hip", "compose.hip", "decode.hip", "reps.hip", "reps_bwd.hip", "gdn2.hip", "compose_bwd.hip", "chunk_bwd.hip", "gdn2_bwd.hip", "router_bwd.hip", "abi.cpp", "timing.cpp"]
 
 # Packed fp32 VALU ops are disabled for the device: the kernels are written with scalar
 # fp32 arithmetic and must not be turned into v_pk_* instructions.

@@ -97,6 +97,14 @@ int64_t reps_ws(const hla_dims_t* d, int32_t n_rep) {
   return round_up(d->B * d->H * n_chunks(d) * n_rep * d->dk * 4, 256);
 }
 
+// Workspace of hla_router_backward: the query-chunk means and their gradients.
+int64_t router_bwd_ws(const hla_dims_t* d) { return 2 * round_up(d->B * d->H * n_chunks(d) * d->dk * 4, 256); }
+// Workspace of hla_chunk_reps_backward: every 64-token tile's weight gradients (4 matrices,
+// 5 with Wr).
+int64_t reps_bwd_ws(const hla_dims_t* d, bool with_wr) {
+  return round_up(d->B * d->H * ((d->T + 63) / 64) * (with_wr ? 5 : 4) * (int64_t)d->dk * d->dk * 4, 256);
+}
+
 // Workspace of hla_compose_backward with history segments of K steps: (At - I) and its
 // transpose in the fragment order, Bc in the lane order, per-wave gate-gradient parts and
 // every chain's lambda, the float32 checkpoints of every chain at each segment boundary it
@@ -428,6 +436,14 @@ hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep,
                       : (size_t)(prefill_bwd_ws(d, 1, variant).comp_off + compose_bwd_min(d));
       return HLA_OK;
     }
+    case HLA_FN_ROUTER_BACKWARD:
+      if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
+      *out = (size_t)router_bwd_ws(d);
+      return HLA_OK;
+    case HLA_FN_CHUNK_REPS_BACKWARD:
+      if (d->C % kPiece != 0) return HLA_ERR_UNSUPPORTED;
+      *out = (size_t)reps_bwd_ws(d, n_rep != 0);
+      return HLA_OK;
     case HLA_FN_GDN2_CHUNK_BACKWARD:
       if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
       *out = (size_t)gdn2_chunk_bwd_ws(d).total;
@@ -536,6 +552,47 @@ hla_status_t hla_chunk_reps_noalloc(const hla_dims_t* d, const void* k, int32_t 
   if (hla::reps_scratch(&scratch) != hipSuccess) return HLA_ERR_HIP;
   a.pooled = scratch;
   return hip_status(hla::launch_reps(a, d->dtype, d->dk, stream));
+}
+
+hla_status_t hla_chunk_reps_backward(const hla_dims_t* d, const void* k, int32_t window, const void* Wq,
+                                     const void* Wk, const void* Wv, const void* Wp, const void* Wr, int64_t w_hstride,
+                                     const float* dreps, float* dk, float* dWq, float* dWk, float* dWv, float* dWp,
+                                     float* dWr, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hla::RepsArgs f;
+  hla_status_t st = reps_args(d, k, window, Wq, Wk, Wv, Wp, Wr, w_hstride, const_cast<float*>(dreps), &f);
+  if (st != HLA_OK) return st;
+  if (d->C % kPiece != 0) return HLA_ERR_UNSUPPORTED;
+  if (!dk || !dWq || !dWk || !dWv || !dWp || (Wr && !dWr)) return HLA_ERR_NULL_ARG;
+  if (!all_aligned(ws) || !all_aligned4(dk, dWq, dWk, dWv, dWp, dWr)) return HLA_ERR_ALIGN;
+  if (!ws || (int64_t)ws_bytes < reps_bwd_ws(d, Wr != nullptr)) return HLA_ERR_WORKSPACE;
+  hla::RepsBwdArgs a{};
+  a.k = k; a.B = d->B; a.T = d->T; a.H = d->H; a.ld_T = d->ld_T; a.window = window;
+  a.Wq = Wq; a.Wk = Wk; a.Wv = Wv; a.Wp = Wp; a.Wr = Wr; a.w_hstride = w_hstride;
+  a.dreps = dreps; a.R = n_chunks(d) * (d->C / window); a.dk = dk;
+  a.part = static_cast<float*>(ws);
+  a.dW[0] = dWq; a.dW[1] = dWk; a.dW[2] = dWv; a.dW[3] = dWp; a.dW[4] = Wr ? dWr : nullptr;
+  return hip_status(hla::launch_reps_backward(a, d->dtype, d->dk, stream));
+}
+
+hla_status_t hla_router_backward(const hla_dims_t* d, const void* q, const void* reps, int32_t n_rep, int64_t ld_R,
+                                 const float* gates, const float* dgates, float* dq, float* dreps, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  hla_status_t st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (d->C != kPiece) return HLA_ERR_UNSUPPORTED;
+  if (!q || !reps || !gates || !dgates || !dq || !dreps) return HLA_ERR_NULL_ARG;
+  const int64_t N = n_chunks(d);
+  if (n_rep < 1 || n_rep > kPiece || ld_R < (N - 1) * (int64_t)n_rep) return HLA_ERR_BAD_SHAPE;
+  if (!all_aligned(q, reps, ws) || !all_aligned4(gates, dgates, dq, dreps)) return HLA_ERR_ALIGN;
+  if (!ws || (int64_t)ws_bytes < router_bwd_ws(d)) return HLA_ERR_WORKSPACE;
+  hla::RouterBwdArgs rb{};
+  rb.q = q; rb.reps = reps; rb.gates = gates; rb.dgates = dgates;
+  rb.qbar = static_cast<float*>(ws);
+  rb.dqbar = reinterpret_cast<float*>(static_cast<char*>(ws) + router_bwd_ws(d) / 2);
+  rb.dreps = dreps; rb.dq_tok = dq;
+  rb.B = d->B; rb.T = d->T; rb.H = d->H; rb.ld_T = d->ld_T; rb.N = (int32_t)N;
+  rb.n_rep = n_rep; rb.ld_R = ld_R; rb.R_out = N * n_rep;
+  return hip_status(hla::launch_router_backward(rb, d->dtype, d->dk, stream));
 }
 
 hla_status_t hla_route_mix(const hla_dims_t* d, const void* q, const void* reps, int32_t n_rep, int64_t ld_R,
@@ -735,13 +792,14 @@ static hla_status_t prefill_backward_body(const hla_dims_t* d, int variant, cons
   // 5. router (computed gates only), then the per-token sums
   if (!gates_in && N > 1) {
     hla::RouterBwdArgs rb{};
-    rb.q = q; rb.k = k; rb.gates = r.gates; rb.dgates = dg;
-    rb.qbar = fat(w.qbar_off); rb.dqbar = fat(w.dqbar_off); rb.dk_router = fat(w.dkr_off);
+    rb.q = q; rb.reps = k; rb.gates = r.gates; rb.dgates = dg;
+    rb.qbar = fat(w.qbar_off); rb.dqbar = fat(w.dqbar_off); rb.dreps = fat(w.dkr_off);
     rb.B = d->B; rb.T = d->T; rb.H = d->H; rb.ld_T = d->ld_T; rb.N = N;
+    rb.n_rep = kPiece; rb.ld_R = d->ld_T; rb.R_out = d->T;  // the raw keys, rows = tokens
     e = hla::launch_router_backward(rb, d->dtype, d->dk, stream);
     if (e != hipSuccess) return HLA_ERR_HIP;
     cb.dqbar = rb.dqbar;
-    cb.dk_router = rb.dk_router;
+    cb.dk_router = rb.dreps;
   }
   return hip_status(chunk_bwd(cb, hla::kChunkBwdFinalize));
 }

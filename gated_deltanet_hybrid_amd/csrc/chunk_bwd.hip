@@ -286,17 +286,6 @@ __global__ __launch_bounds__(chunk_bwd_threads<DK>()) void chunk_bwd_kernel(Chun
 // 64 x dk and of the 64 x dv results.  Each workgroup writes its per-token sums into one
 // partial-sum slot of its part.
 namespace {
-// C (32 x 32) += A B over KD k values: fa(k) = A[m0 + lane % 32][k], fb(k) = B[k][n0 + lane % 32]
-template <int KD, class FA, class FB>
-__device__ __forceinline__ f32x16 mm32(f32x16 acc, int hh, FA fa, FB fb) {
-#pragma unroll 8
-  for (int ks = 0; ks < KD / 2; ++ks) {
-    const int k = 2 * ks + hh;
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa(k), fb(k), acc, 0, 0, 0);
-  }
-  return acc;
-}
-
 // The workgroup's LDS for the UT reverse, and the lane's coordinates.
 template <int DK, int DV>
 struct UtRev {

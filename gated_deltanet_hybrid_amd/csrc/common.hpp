@@ -52,6 +52,19 @@ __device__ __forceinline__ f32x16 zero16() {
 // Row of accumulator element a for lane half h.
 __device__ __forceinline__ int acc_row(int a, int h) { return (a >> 2) * 8 + h * 4 + (a & 3); }
 
+// One 32 x 32 float32 tile on the matrix cores (v_mfma_f32_32x32x2_f32): C += A B over KD
+// k values, with fa(k) = A[m0 + lane % 32][k] and fb(k) = B[k][n0 + lane % 32] for the lane's
+// k = 2 ks + lane / 32; the result is in the accumulator layout (row acc_row(e, lane / 32)).
+template <int KD, class FA, class FB>
+__device__ __forceinline__ f32x16 mm32(f32x16 acc, int hh, FA fa, FB fb) {
+#pragma unroll 8
+  for (int ks = 0; ks < KD / 2; ++ks) {
+    const int k = 2 * ks + hh;
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa(k), fb(k), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 template <class T> struct Mma;
 
 template <> struct Mma<bf16> {

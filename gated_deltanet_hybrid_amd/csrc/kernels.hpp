@@ -190,6 +190,28 @@ struct RepsArgs {
 };
 // Learned chunk representatives: window self-attention, mean-pool, projections.
 hipError_t launch_reps(const RepsArgs& a, int dtype, int dk, hipStream_t s);
+// Backward of the learned representatives: from the gradient of every representative row,
+// the gradient of the keys the windows pooled and of the weights.
+struct RepsBwdArgs {
+  const void* k;          // [B,ld_T,H,dk]
+  int64_t B, T, H, ld_T;
+  int32_t window;         // 8, 16, 32 or 64 (windows never cross a 64-token tile)
+  const void* Wq;         // [*, dk, dk] (out, in) in dtype; head h at + h * w_hstride
+  const void* Wk;
+  const void* Wv;
+  const void* Wp;
+  const void* Wr;         // folded query projection, or null
+  int64_t w_hstride;      // 0: one set shared by all heads
+  const float* dreps;     // [B,R,H,dk]: row t0 / window is the window starting at token t0
+  int64_t R;              // rows per batch of dreps
+  float* dk;              // out [B,T,H,dk]
+  float* part;            // workspace [B,H,ceil(T/64),NM,dk,dk]: each tile's weight gradients
+                          // (NM = 4 without Wr: q, k, v, p; 5 with it: q, k, v, p, r)
+  float* dW[5];           // out [Hw,dk,dk] float32: dWq, dWk, dWv, dWp, dWr (Hw = H, or 1
+                          // when shared)
+};
+hipError_t launch_reps_backward(const RepsBwdArgs& a, int dtype, int dk, hipStream_t s);
+
 // Bytes of the fixed device scratch that hla_chunk_reps_noalloc keeps its window means in.
 constexpr int64_t kRepsScratchBytes = (int64_t)32 << 20;
 // That scratch on the current device (its address looked up once per device, then cached).
@@ -319,16 +341,20 @@ hipError_t launch_gdn2_chunk_backward(const Gdn2BwdArgs& a, int dtype, int dk, i
 
 struct RouterBwdArgs {
   const void* q;         // [B,ld_T,H,dk] (dtype)
-  const void* k;         // [B,ld_T,H,dk]: the representatives (raw keys, n_rep = 64)
+  const void* reps;      // [B,ld_R,H,dk] (dtype): chunk j's representatives are rows
+                         // [j n_rep, (j + 1) n_rep) (the raw keys: n_rep = 64, ld_R = ld_T)
   const float* gates;    // [B,H,N,N]
   const float* dgates;   // [B,H,N,N] gradient of the gates (zero for skipped pairs)
   float* qbar;           // workspace [B,H,N,dk]
   float* dqbar;          // out [B,H,N,dk]
-  float* dk_router;      // out [B,T,H,dk]
+  float* dreps;          // out [B,R_out,H,dk]: gradient of every representative row below R_out
+  float* dq_tok;         // out [B,T,H,dk] dqbar of each token's chunk over its token count, or null
   int64_t B, T, H, ld_T;
   int32_t N;
+  int32_t n_rep;         // 1 .. 64
+  int64_t ld_R, R_out;
 };
-// Backward of the router gates to the query-chunk means and the keys.
+// Backward of the router gates to the query-chunk means and the representatives.
 hipError_t launch_router_backward(const RouterBwdArgs& a, int dtype, int dk, hipStream_t s);
 
 }  // namespace hla

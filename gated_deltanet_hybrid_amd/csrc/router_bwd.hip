@@ -1,16 +1,18 @@
-// Backward of the HLA router gates (raw-key representatives, n_rep = C = 64).
+// Backward of the HLA router gates (C = 64; the raw keys, n_rep = 64, or learned
+// representatives, n_rep of them per chunk).
 //
 // [HLA] Overview and Methodology paragraph 2: qbar_i = mean of q over query chunk i,
-// s_ijr = qbar_i . k_{jC+r} / sqrt(dk) over history chunk j's keys, l_ij = log-mean-exp
-// over r of s_ijr, g_ij = sigmoid(l_ij).  Given dg_ij (zero for skipped pairs):
+// s_ijr = qbar_i . r_{j n_rep + r} / sqrt(dk) over history chunk j's representatives,
+// l_ij = log-mean-exp over r of s_ijr, g_ij = sigmoid(l_ij).  Given dg_ij (zero for skipped
+// pairs):
 //     dl_ij = dg_ij g_ij (1 - g_ij),   p_ijr = softmax over r of s_ijr,
-//     dqbar_i  = sum_{j<i} dl_ij sum_r p_ijr k_{jC+r} / sqrt(dk),
-//     dk_{jC+r} = sum_{i>j} dl_ij p_ijr qbar_i / sqrt(dk),
+//     dqbar_i  = sum_{j<i} dl_ij sum_r p_ijr r_{j n_rep + r} / sqrt(dk),
+//     dr_{j n_rep + r} = sum_{i>j} dl_ij p_ijr qbar_i / sqrt(dk),
 // and every token of chunk i receives dqbar_i / n_i (added by the chunk backward's
-// finalize pass).
+// finalize pass, or written per token here).
 //
-// Lane r owns key r of a history chunk, so the softmax over a chunk's 64 keys is a wave
-// reduction.
+// Lane r owns representative r of a history chunk (lanes r >= n_rep take no part), so the
+// softmax over a chunk's representatives is a wave reduction.
 #include <math.h>
 
 #include "common.hpp"
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(64 * kRouterQG) void router_dq_kernel(RouterBwdArgs
   const int i = i0 + w;
   const int64_t h = bh % a.H, b = bh / a.H;
   const T* q = reinterpret_cast<const T*>(a.q);
-  const T* k = reinterpret_cast<const T*>(a.k);
+  const T* k = reinterpret_cast<const T*>(a.reps);
   const float rs = 1.f / sqrtf((float)DK);
   if (i < a.N) {
     const int64_t t0 = (int64_t)i * C;
@@ -81,11 +83,16 @@ __global__ __launch_bounds__(64 * kRouterQG) void router_dq_kernel(RouterBwdArgs
   for (int e = 0; e < DK; ++e) acc[e] = 0.f;
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   u32x4 pre[NU];
+  // history chunk j's representative rows (every one exists: j < N - 1); rows r >= n_rep
+  // are zero and take no part
   auto load_keys = [&](int j) {
 #pragma unroll
     for (int m = 0; m < NU; ++m) {
       const int u = tid + m * NTH, r = u / UPR, cu = u % UPR;
-      pre[m] = *reinterpret_cast<const u32x4*>(k + ((b * a.ld_T + (int64_t)j * C + r) * a.H + h) * DK + cu * EPP);
+      pre[m] = u32x4{0u, 0u, 0u, 0u};
+      if (r < a.n_rep)
+        pre[m] = *reinterpret_cast<const u32x4*>(
+            k + ((b * a.ld_R + (int64_t)j * a.n_rep + r) * a.H + h) * DK + cu * EPP);
     }
   };
   if (jmax > 0) load_keys(0);
@@ -105,7 +112,7 @@ __global__ __launch_bounds__(64 * kRouterQG) void router_dq_kernel(RouterBwdArgs
       const float g = a.gates[o], dl = a.dgates[o] * g * (1.f - g);
       if (dl != 0.f) {  // uniform over the wave
         const float* kr = s_key + lane * PK;
-        const float sc = dot_rows<DK>(s_qb[w], kr) * rs;
+        const float sc = lane < a.n_rep ? dot_rows<DK>(s_qb[w], kr) * rs : -INFINITY;
         const float mx = wave_max_valu(sc);
         const float p = __expf(sc - mx);
         const float cr = dl * (p / wave_sum_valu(p)) * rs;
@@ -130,9 +137,9 @@ __global__ __launch_bounds__(64 * kRouterQG) void router_dq_kernel(RouterBwdArgs
   }
 }
 
-// Key side: dk of every token of history chunk j (zero for the last chunk, which no query
-// chunk reads).  Lane r keeps key r's gradient; the query means (from router_dq_kernel)
-// are wave-uniform loads, so a pair needs no barrier.
+// Representative side: the gradient of every representative row of chunk j (zero for the
+// last chunk, which no query chunk reads).  Lane r keeps row r's gradient; the query means
+// (from router_dq_kernel) are wave-uniform loads, so a pair needs no barrier.
 template <class T, int DK>
 __global__ __launch_bounds__(64) void router_dk_kernel(RouterBwdArgs a) {
   constexpr int C = kChunk, PK = DK + 4;
@@ -141,13 +148,14 @@ __global__ __launch_bounds__(64) void router_dk_kernel(RouterBwdArgs a) {
   const int64_t bh = blockIdx.x / a.N;
   const int j = (int)(blockIdx.x % a.N);
   const int64_t h = bh % a.H, b = bh / a.H;
-  const int64_t t0 = (int64_t)j * C;
-  const int nj = (int)((a.T - t0) < C ? (a.T - t0) : C);
-  const T* k = reinterpret_cast<const T*>(a.k);
+  const int64_t r0 = (int64_t)j * a.n_rep;  // first row of chunk j
+  const int nj = (int)((a.R_out - r0) < a.n_rep ? (a.R_out - r0) : a.n_rep);  // its rows below R_out
+  const T* k = reinterpret_cast<const T*>(a.reps);
   const float rs = 1.f / sqrtf((float)DK);
+  const bool read = j + 1 < a.N;  // a history chunk: all n_rep rows exist
   for (int idx = lane; idx < C * DK; idx += 64) {
     const int r = idx / DK, e = idx % DK;
-    s_key[r * PK + e] = r < nj ? to_f<T>(k[((b * a.ld_T + t0 + r) * a.H + h) * DK + e]) : 0.f;
+    s_key[r * PK + e] = (read && r < a.n_rep) ? to_f<T>(k[((b * a.ld_R + r0 + r) * a.H + h) * DK + e]) : 0.f;
   }
   __syncthreads();
   const float* kr = s_key + lane * PK;
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(64) void router_dk_kernel(RouterBwdArgs a) {
     const float g = a.gates[o], dl = a.dgates[o] * g * (1.f - g);
     if (dl == 0.f) continue;  // uniform over the wave
     const float* qb = a.qbar + (bh * a.N + i) * DK;
-    const float sc = dot_rows<DK>(qb, kr) * rs;
+    const float sc = lane < a.n_rep ? dot_rows<DK>(qb, kr) * rs : -INFINITY;
     const float mx = wave_max_valu(sc);
     const float p = __expf(sc - mx);
     const float cr = dl * (p / wave_sum_valu(p)) * rs;
@@ -167,10 +175,26 @@ __global__ __launch_bounds__(64) void router_dk_kernel(RouterBwdArgs a) {
     for (int e = 0; e < DK; ++e) acc[e] = fmaf(cr, qb[e], acc[e]);
   }
   if (lane < nj) {
-    float* out = a.dk_router + ((b * a.T + t0 + lane) * a.H + h) * DK;
+    float* out = a.dreps + ((b * a.R_out + r0 + lane) * a.H + h) * DK;
 #pragma unroll
     for (int e = 0; e < DK; ++e) out[e] = acc[e];
   }
+}
+
+// dqbar of each token's chunk over the chunk's token count, per token.
+template <int DK>
+__global__ __launch_bounds__(256) void router_spread_kernel(RouterBwdArgs a) {
+  constexpr int C = kChunk;
+  const int64_t id = blockIdx.x * (int64_t)256 + threadIdx.x;
+  if (id >= a.B * a.T * a.H * DK) return;
+  const int e = (int)(id % DK);
+  const int64_t bth = id / DK;
+  const int64_t h = bth % a.H, bt = bth / a.H;
+  const int64_t t = bt % a.T, b = bt / a.T;
+  const int c = (int)(t / C);
+  const int64_t t0 = (int64_t)c * C;
+  const int nc = (int)((a.T - t0) < C ? (a.T - t0) : C);
+  a.dq_tok[id] = a.dqbar[((b * a.H + h) * a.N + c) * DK + e] / (float)nc;
 }
 
 template <class T, int DK>
@@ -180,6 +204,10 @@ static hipError_t launch_router_bwd_t(const RouterBwdArgs& a, hipStream_t s) {
   TimedLaunch tl(HLA_KERNEL_BWD_ROUTER, s);
   hipLaunchKernelGGL((router_dq_kernel<T, DK>), dim3(nq), dim3(64 * kRouterQG), 0, s, a);
   hipLaunchKernelGGL((router_dk_kernel<T, DK>), dim3(nk), dim3(64), 0, s, a);
+  if (a.dq_tok) {
+    const int64_t total = a.B * a.T * a.H * DK;
+    hipLaunchKernelGGL((router_spread_kernel<DK>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

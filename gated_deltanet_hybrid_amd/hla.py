@@ -20,11 +20,12 @@ _lib = None
 HLA_F32, HLA_BF16 = 0, 1
 KERNEL_CHUNK, KERNEL_SCAN, KERNEL_GATES, KERNEL_COMPOSE, KERNEL_DECODE, KERNEL_REPS = 0, 1, 2, 3, 4, 5
 KERNEL_BWD_SAVE, KERNEL_BWD_ADJOINT, KERNEL_BWD_REDUCE, KERNEL_BWD_CHUNK, KERNEL_BWD_ROUTER = 6, 7, 8, 9, 10
-KERNEL_PREFILL = 11
+KERNEL_PREFILL, KERNEL_BWD_REPS = 11, 12
 FN_CHUNK_TRANSITIONS, FN_GDN_PREFILL, FN_ROUTE_MIX, FN_WU_HANDOFF, FN_CHUNK_REPS = 0, 1, 2, 3, 4
 FN_COMPOSE_BACKWARD, FN_PREFILL_BACKWARD, FN_CHUNK_BACKWARD = 5, 6, 7
 FN_COMPOSE_BACKWARD_MIN, FN_PREFILL_BACKWARD_MIN = 8, 9  # smallest workspaces (history segments)
 FN_GDN2_CHUNK_BACKWARD, FN_GDN2_PREFILL_BACKWARD, FN_GDN2_PREFILL_BACKWARD_MIN = 10, 11, 12
+FN_ROUTER_BACKWARD, FN_CHUNK_REPS_BACKWARD = 13, 14
 CHUNK = 64
 MAX_CACHE_SLOTS = 1024
 REPS_SCRATCH_BYTES = 32 << 20  # fixed device scratch of chunk_reps_noalloc
@@ -73,6 +74,11 @@ _SIGS = {
     "hla_gdn2_prefill_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P,
                                                    ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                    ctypes.c_size_t, _P]),
+    "hla_router_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
+                                             _P, _P, ctypes.c_size_t, _P]),
+    "hla_chunk_reps_backward": (ctypes.c_int32, [ctypes.POINTER(Dims), _P, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                                 ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                                 _P]),
     "hla_timing_enable": (ctypes.c_int32, [ctypes.c_int32]),
     "hla_timing_read": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "hla_gdn_decode": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -356,6 +362,58 @@ def chunk_reps_noalloc(k, W, window=32, C=CHUNK, out=None):
                                             _ptr(W["Wv"]), _ptr(W["Wp"]), _ptr(W.get("Wr")),
                                             0 if nh == 1 else dk * dk, _ptr(out), _stream(k.device)),
            "hla_chunk_reps_noalloc")
+    return out
+
+
+def chunk_reps_backward(k, W, dreps, window=32, C=CHUNK, ws=None):
+    """Reverse of chunk_reps: dreps [B, N * C/window, H, dk] float32 (the gradient of its
+    output rows) -> dict(dk [B, T, H, dk], dWq, dWk, dWv, dWp, dWr (None without Wr)),
+    float32, the weight gradients shaped like the weights ([H or 1, dk, dk])."""
+    B, T, H, dk, ld_T = _token_view(k, "k")
+    d = make_dims(B, T, H, ld_T, dk, dk, _dtype_code(k), C)
+    N = math.ceil(T / C)
+    n_rep = C // window
+    names = ("Wq", "Wk", "Wv", "Wp") + (("Wr",) if W.get("Wr") is not None else ())
+    nh = W["Wq"].shape[0]
+    for n in names:
+        t = W[n]
+        if t.shape != (nh, dk, dk) or nh not in (1, H) or t.dtype != k.dtype or not t.is_contiguous():
+            raise ValueError("weights must be contiguous [H or 1, dk, dk] in k's dtype")
+    _need(dreps, (B, N * n_rep, H, dk), torch.float32, "dreps")
+    f32 = dict(dtype=torch.float32, device=k.device)
+    out = {"dk": torch.empty((B, T, H, dk), **f32)}
+    for n in ("Wq", "Wk", "Wv", "Wp", "Wr"):
+        out["d" + n] = torch.empty((nh, dk, dk), **f32) if n in names else None
+    if ws is None:
+        ws = _workspace(workspace_bytes(FN_CHUNK_REPS_BACKWARD, d, 1 if "Wr" in names else 0), k.device)
+    _check(library().hla_chunk_reps_backward(ctypes.byref(d), _ptr(k), window, _ptr(W["Wq"]), _ptr(W["Wk"]),
+                                             _ptr(W["Wv"]), _ptr(W["Wp"]), _ptr(W.get("Wr")),
+                                             0 if nh == 1 else dk * dk, _ptr(dreps), _ptr(out["dk"]),
+                                             *(_ptr(out["d" + n]) for n in ("Wq", "Wk", "Wv", "Wp", "Wr")),
+                                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(k.device)),
+           "hla_chunk_reps_backward")
+    return out
+
+
+def router_backward(q, reps, n_rep, gates, dgates, ws=None):
+    """Gradients of the history gates (as route_mix computed them from q and reps) to the
+    queries and the representatives: dgates [B, H, N, N] float32 -> dict(dq [B, T, H, dk],
+    dreps [B, N * n_rep, H, dk]), float32."""
+    B, T, H, dk, ld_T = _token_view(q, "q")
+    Br, _, Hr, dr, ld_R = _token_view(reps, "reps")
+    if (Br, Hr, dr) != (B, H, dk) or reps.dtype != q.dtype:
+        raise ValueError("reps must be [B, R, H, dk] in q's dtype")
+    d = make_dims(B, T, H, ld_T, dk, dk, _dtype_code(q), CHUNK)
+    N = math.ceil(T / CHUNK)
+    _need(gates, (B, H, N, N), torch.float32, "gates")
+    _need(dgates, (B, H, N, N), torch.float32, "dgates")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = dict(dq=torch.empty((B, T, H, dk), **f32), dreps=torch.empty((B, N * n_rep, H, dk), **f32))
+    if ws is None:
+        ws = _workspace(workspace_bytes(FN_ROUTER_BACKWARD, d), q.device)
+    _check(library().hla_router_backward(ctypes.byref(d), _ptr(q), _ptr(reps), n_rep, ld_R, _ptr(gates),
+                                         _ptr(dgates), _ptr(out["dq"]), _ptr(out["dreps"]), _ptr(ws),
+                                         0 if ws is None else ws.numel(), _stream(q.device)), "hla_router_backward")
     return out
 
 

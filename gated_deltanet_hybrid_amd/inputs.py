@@ -32,7 +32,7 @@ import numpy as np
 SEGMENT = 4096
 _TENSOR_ID = {"q": 1, "k": 2, "v": 3, "beta": 4, "alpha": 5, "gates": 6, "At": 7, "Bc": 8, "S0": 9,
               "Wq": 10, "Wk": 11, "Wv": 12, "Wp": 13, "Wr": 14, "ga": 15, "gb": 16, "gw": 17,
-              "dO": 18, "dS": 19}
+              "dO": 18, "dS": 19, "dreps": 20, "dgates": 21}
 
 
 # --------------------------------------------------------------------------- rounding

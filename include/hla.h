@@ -95,7 +95,10 @@ typedef enum {
   HLA_FN_PREFILL_BACKWARD_MIN = 9, /* smallest workspace hla_prefill_backward accepts */
   HLA_FN_GDN2_CHUNK_BACKWARD = 10, /* workspace of hla_gdn2_chunk_backward */
   HLA_FN_GDN2_PREFILL_BACKWARD = 11, /* workspace of hla_gdn2_prefill_backward (one pass) */
-  HLA_FN_GDN2_PREFILL_BACKWARD_MIN = 12 /* smallest workspace hla_gdn2_prefill_backward accepts */
+  HLA_FN_GDN2_PREFILL_BACKWARD_MIN = 12, /* smallest workspace hla_gdn2_prefill_backward accepts */
+  HLA_FN_ROUTER_BACKWARD = 13,   /* workspace of hla_router_backward */
+  HLA_FN_CHUNK_REPS_BACKWARD = 14 /* workspace of hla_chunk_reps_backward; n_rep says whether Wr
+                                     is given (0: no, 1: yes) */
 } hla_fn_t;
 
 /*
@@ -467,9 +470,65 @@ hla_status_t hla_gdn2_prefill_backward(const hla_dims_t* d, const void* q, const
                                        float* da, float* db, float* dw, float* dS0, float* dgates,
                                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * hla_router_backward -- gradients of the history gates to the queries and to the
+ * representatives (learned ones, or the raw keys), for callers that compose the learned-
+ * representative backward themselves: hla_prefill_backward with the forward's gates as
+ * gates_in returns dgates; this call takes them on to dq and dreps, and
+ * hla_chunk_reps_backward takes dreps on to the keys and the pooler's weights.
+ * [HLA] Overview, Methodology paragraph 2: with qbar_i the mean of q over chunk i,
+ * s_ijr = qbar_i . r_{j n_rep + r} / sqrt(dk), g_ij = sigmoid(log-mean-exp_r s_ijr):
+ *     dl_ij = dg_ij g_ij (1 - g_ij),  p_ijr = softmax_r s_ijr,
+ *     dq_t = (1 / n_i) sum_{j<i} dl_ij sum_r p_ijr r_{j n_rep + r} / sqrt(dk)  (t in chunk i),
+ *     dr_{j n_rep + r} = sum_{i>j} dl_ij p_ijr qbar_i / sqrt(dk).
+ *   d      : dims (C = 64).
+ *   q      : [B, ld_T, H, dk] (dtype);  reps: [B, ld_R, H, dk] (dtype), chunk j's rows
+ *           [j n_rep, (j + 1) n_rep), 1 <= n_rep <= 64, ld_R >= (N - 1) n_rep.
+ *   gates, dgates : [B, H, N, N] float32: the gates hla_route_mix wrote and their gradient
+ *           (entries j < i are read; a skipped pair's gradient is zero).
+ *   dq     : [B, T, H, dk] float32 out (the router's part of the query gradient).
+ *   dreps  : [B, N n_rep, H, dk] float32 out (the last chunk's rows are zero).
+ *   ws, ws_bytes : hla_workspace_bytes(HLA_FN_ROUTER_BACKWARD) bytes.
+ * Errors: HLA_ERR_NULL_ARG, HLA_ERR_BAD_SHAPE (n_rep, ld_R), HLA_ERR_ALIGN (q, reps, ws
+ *         16 bytes; the float32 arrays 4), HLA_ERR_WORKSPACE, HLA_ERR_UNSUPPORTED (C != 64),
+ *         HLA_ERR_HIP.
+ */
+hla_status_t hla_router_backward(const hla_dims_t* d, const void* q, const void* reps, int32_t n_rep,
+                                 int64_t ld_R, const float* gates, const float* dgates, float* dq,
+                                 float* dreps, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hla_chunk_reps_backward -- reverse of hla_chunk_reps: from dreps, the gradient of every
+ * representative row, the gradients of the keys and of the weights.
+ * [HLA] Methodology paragraph 2 (the forward of hla_chunk_reps).  Per window of n >= 1
+ * tokens X, with P the window's attention, c_s its column sums, m = (1/n) sum_s c_s V_s
+ * and z = Wp m:
+ *     dz = Wr dr (dr without Wr),  dWr += z dr^T,  dm = Wp^T dz,  dWp += dz m^T,
+ *     dV_s = c_s dm / n,  e_s = V_s . dm / n,  dS_ts = P_ts (e_s - sum_s' P_ts' e_s'),
+ *     dQ = dS K / sqrt(dk),  dK = dS^T Q / sqrt(dk),
+ *     dX = dQ Wq + dK Wk + dV Wv,  dWq += dQ^T X,  dWk += dK^T X,  dWv += dV^T X;
+ * an empty window passes nothing.  The weight gradients sum over every window of every
+ * batch row (and head, with shared weights) in a fixed order.
+ *   k, window, Wq, Wk, Wv, Wp, Wr, w_hstride : as for hla_chunk_reps (C a multiple of 64).
+ *   dreps  : [B, N (C / window), H, dk] float32, rows as hla_chunk_reps writes them.
+ *   dk     : [B, T, H, dk] float32 out.
+ *   dWq, dWk, dWv, dWp : [Hw, dk, dk] float32 out, Hw = H (w_hstride != 0) or 1 (shared),
+ *           each head's matrix dk * dk elements after the previous one.
+ *   dWr    : same, out; required exactly when Wr is given.
+ *   ws, ws_bytes : hla_workspace_bytes(HLA_FN_CHUNK_REPS_BACKWARD, d, Wr ? 1 : 0) bytes
+ *           (every 64-token tile's weight gradients).
+ * Errors: as hla_chunk_reps, and HLA_ERR_UNSUPPORTED (C not a multiple of 64).
+ */
+hla_status_t hla_chunk_reps_backward(const hla_dims_t* d, const void* k, int32_t window, const void* Wq,
+                                     const void* Wk, const void* Wv, const void* Wp, const void* Wr,
+                                     int64_t w_hstride, const float* dreps, float* dk, float* dWq,
+                                     float* dWk, float* dWv, float* dWp, float* dWr, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes that entry point `fn` needs for dims `d`; n_rep is the number of
- * representatives per chunk for HLA_FN_CHUNK_REPS (C / window; it must divide C) and is
- * ignored otherwise.  `out` is a host pointer. */
+ * representatives per chunk for HLA_FN_CHUNK_REPS (C / window; it must divide C), whether
+ * Wr is given (0 or 1) for HLA_FN_CHUNK_REPS_BACKWARD, and ignored otherwise.  `out` is a
+ * host pointer. */
 hla_status_t hla_workspace_bytes(int32_t fn, const hla_dims_t* d, int32_t n_rep, size_t* out);
 
 /* Kernel kinds that hla_timing_read() reports. */
@@ -486,7 +545,8 @@ typedef enum {
   HLA_KERNEL_BWD_CHUNK = 9,   /* backward: per-chunk reverse token recurrence            */
   HLA_KERNEL_BWD_ROUTER = 10, /* backward: router gates to queries and keys              */
   HLA_KERNEL_PREFILL = 11,    /* one-pass native prefill (bf16): UT, outputs, state scan */
-  HLA_KERNEL_COUNT = 12
+  HLA_KERNEL_BWD_REPS = 12,   /* backward: learned representatives (tiles and reduction)  */
+  HLA_KERNEL_COUNT = 13
 } hla_kernel_t;
 
 /*

@@ -445,3 +445,57 @@ def test_gdn2_prefill_backward_validation(lib):
     a = list(full)
     a[5] = P + 2
     assert call(a) == ALIGN
+
+
+def test_reps_and_router_backward_workspace_sizes(lib):
+    d = dims(B=2, T=130, H=3, dk=128, dv=64, dtype=1)  # 3 tiles of 64 tokens, N = 3
+    assert hla.workspace_bytes(hla.FN_ROUTER_BACKWARD, d) == 2 * _r(2 * 3 * 3 * 128 * 4)
+    assert hla.workspace_bytes(hla.FN_CHUNK_REPS_BACKWARD, d, 0) == _r(2 * 3 * 3 * 4 * 128 * 128 * 4)
+    assert hla.workspace_bytes(hla.FN_CHUNK_REPS_BACKWARD, d, 1) == _r(2 * 3 * 3 * 5 * 128 * 128 * 4)
+    out = ctypes.c_size_t()
+    assert lib.hla_workspace_bytes(hla.FN_ROUTER_BACKWARD, ctypes.byref(dims(C=128)), 0, ctypes.byref(out)) == \
+        UNSUPPORTED
+
+
+def test_router_backward_validation(lib):
+    d = dims()
+    f = lib.hla_router_backward
+    need = hla.workspace_bytes(hla.FN_ROUTER_BACKWARD, d)
+    N = -(-d.T // 64)
+    # (d, q, reps, n_rep, ld_R, gates, dgates, dq, dreps, ws, ws_bytes, s)
+    def call(q=P, reps=P, n_rep=2, ld_R=N * 2, gates=P, dg=P, dq=P, dr=P, ws=P, nb=need, dd=d):
+        return f(ctypes.byref(dd), q, reps, n_rep, ld_R, gates, dg, dq, dr, ws, nb, None)
+    for kw in ({"q": None}, {"reps": None}, {"gates": None}, {"dg": None}, {"dq": None}, {"dr": None}):
+        assert call(**kw) == NULL_ARG, kw
+    assert call(n_rep=0) == BAD_SHAPE
+    assert call(n_rep=65) == BAD_SHAPE
+    assert call(ld_R=(N - 1) * 2 - 1) == BAD_SHAPE
+    assert call(reps=PU) == ALIGN
+    assert call(gates=P + 2) == ALIGN
+    assert call(nb=need - 1) == WORKSPACE
+    assert call(ws=None, nb=0) == WORKSPACE
+    assert call(dd=dims(C=128)) == UNSUPPORTED
+
+
+def test_chunk_reps_backward_validation(lib):
+    d = dims()
+    f = lib.hla_chunk_reps_backward
+    need = hla.workspace_bytes(hla.FN_CHUNK_REPS_BACKWARD, d, 1)
+    # (d, k, window, Wq, Wk, Wv, Wp, Wr, w_hstride, dreps, dk, dWq, dWk, dWv, dWp, dWr, ws, ws_bytes, s)
+    def call(ptrs, window=32, hs=0, ws=P, nb=need, dd=d):
+        p = list(ptrs)
+        return f(ctypes.byref(dd), p[0], window, *p[1:6], hs, *p[6:13], ws, nb, None)
+    full = [P] * 13  # k, Wq, Wk, Wv, Wp, Wr, then dreps, dk, dWq, dWk, dWv, dWp, dWr
+    for i in (0, 1, 2, 3, 4, 6, 7, 8, 9, 10, 11, 12):
+        a = list(full)
+        a[i] = None
+        assert call(a) == NULL_ARG, i
+    no_wr = list(full)
+    no_wr[5] = no_wr[12] = None  # dWr is needed exactly when Wr is given
+    assert call(no_wr, nb=hla.workspace_bytes(hla.FN_CHUNK_REPS_BACKWARD, d, 0) - 1) == WORKSPACE
+    assert call(full, window=24) == BAD_SHAPE
+    assert call(full, hs=100) == BAD_SHAPE
+    a = list(full)
+    a[7] = P + 2
+    assert call(a) == ALIGN
+    assert call(full, nb=need - 1) == WORKSPACE
