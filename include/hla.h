@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define HLA_ABI_VERSION 6
+#define HLA_ABI_VERSION 7
 
 typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype_t;
 
@@ -184,8 +184,10 @@ hla_status_t hla_gdn_prefill(const hla_dims_t* d, const void* q, const void* k, 
  *   Every other argument, output, mode, workspace size and error is as for
  *           hla_chunk_transitions and hla_gdn_prefill, which have no wu argument here (the
  *           W | U hand-off belongs to Gated DeltaNet's UT form).
- * The chunk pass runs each 64-token piece's tokens in float32, so its cost is
- * O(C dk (dk + dv)) vector arithmetic per piece rather than matrix-core work.
+ * With bf16 inputs the chunk pass runs the chunkwise WY form on the matrix cores (every
+ * per-channel decay factor it forms is taken against a reference token of its 16 x 16
+ * block, and log a_t is floored at -11 per token); with float32 inputs it runs each
+ * 64-token piece's tokens in float32 on the vector units.
  */
 hla_status_t hla_gdn2_chunk_transitions(const hla_dims_t* d, const void* k, const void* v,
                                         const float* a_decay, const float* b_erase,

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hla_abi_version() == 6
+    assert lib.hla_abi_version() == 7
     for s in range(0, 10):
         assert lib.hla_status_string(s)
     assert lib.hla_status_string(99) == b"unknown status"
