@@ -187,3 +187,38 @@ def test_backward_twice():
         return dict(h.prefill_backward(q, k, v, beta, alpha, dO, tau=1e-3, S0=S0, ws=ws))
 
     twice(run_seg, "routed prefill backward in history segments")
+
+
+def test_gdn2_backward_twice():
+    B, H, T, d = 1, 8, 6 * C - 13, 128
+    x = inputs.gen_tokens(B, T, H, d, d, dtype="bf16", seed=75, alpha_mode="slow")
+    q, k, v, _, _ = token_tensors(x)
+    g = inputs.gen_gdn2_gates(B, T, H, d, d, seed=76, alpha_mode="slow")
+    ga, gb, gw = (f32(g[n]) for n in ("a", "b", "w"))
+    dO = f32(inputs.gen_cotangent((B, T, H, d), seed=77))
+    h = hla()
+
+    def run(_):
+        return dict(h.gdn2_prefill_backward(q, k, v, ga, gb, gw, dO, tau=1e-3))
+
+    twice(run, "gated deltanet-2 routed prefill backward")
+
+
+def test_reps_and_router_backward_twice():
+    B, H, T, d = 1, 4, 7 * C - 9, 128
+    x = inputs.gen_tokens(B, T, H, d, d, dtype="bf16", seed=78)
+    q, k, v, beta, alpha = token_tensors(x)
+    Wd = {n: dev(a, "bf16") for n, a in inputs.gen_pooler_weights(H, d, dtype="bf16", seed=79).items()}
+    h = hla()
+    N = math.ceil(T / C)
+    reps = h.chunk_reps(k, Wd, window=32)
+    At, Bc = h.chunk_transitions(k, v, beta, alpha)
+    fw = h.route_mix(q, reps, At, Bc, n_rep=2, tau=1e-3)
+    dG = f32(inputs.gen_cotangent((B, H, N, N), seed=80, name="dgates")) * fw["mask"].float()
+
+    def run(_):
+        r = h.router_backward(q, reps, 2, fw["gates"], dG)
+        p = h.chunk_reps_backward(k, Wd, r["dreps"], window=32)
+        return dict(dq=r["dq"], dreps=r["dreps"], **{n: t for n, t in p.items() if t is not None})
+
+    twice(run, "router and learned-representative backward")
