@@ -193,12 +193,12 @@ void set_chunk_bwd_ws(hla::ChunkBwdArgs& a, const ChunkBwdWs& w, void* ws) {
 }
 
 // Workspace of hla_gdn2_chunk_backward: per-workgroup column sums of the per-token
-// gradients (16 state columns per workgroup).
+// gradients (gdn2_bwd_cols state columns per workgroup).
 struct Gdn2ChunkBwdWs {
   int64_t k_off, a_off, b_off, q_off, v_off, w_off, total;
 };
 Gdn2ChunkBwdWs gdn2_chunk_bwd_ws(const hla_dims_t* d) {
-  const int64_t BHN = d->B * d->H * n_pieces(d), C = kPiece, NC = hla::kGdn2BwdCols;
+  const int64_t BHN = d->B * d->H * n_pieces(d), C = kPiece, NC = hla::gdn2_bwd_cols(d->dtype);
   const int64_t nb_out = d->dv / NC, nb_all = nb_out + (d->dk + d->dv) / NC;
   const int64_t vec = round_up(BHN * nb_all * C * d->dk * 4, 256), per_v = round_up(BHN * 2 * C * d->dv * 4, 256);
   Gdn2ChunkBwdWs w;

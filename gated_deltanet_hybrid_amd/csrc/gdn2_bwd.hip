@@ -17,7 +17,8 @@
 //     dx' = dx + dp k_t,   da_t += dx' o x,   dq_t += dO_t[col] x_after,   dx <- a_t o dx'.
 // dk, da, db and dq are sums over every column; dv_t[col] and dw_t[col] come from one.
 //
-// Layout: one workgroup per (b, h, chunk, block of 16 columns); a thread holds 8 rows of one
+// Layout: one workgroup per (b, h, chunk, block of 32 columns, 16 for float32 inputs, whose
+// keys and queries take twice the LDS); a thread holds 8 rows of one
 // column, the column's dk / 8 threads adjacent lanes (a dot product is a sum over 8 rows
 // plus log2(dk / 8) DPP lane moves).  A forward pass keeps the state in front of every
 // 8-token block in registers, and each block is replayed from its checkpoint before it is
@@ -36,14 +37,15 @@ constexpr int kTB = 8;    // tokens per checkpoint block
 constexpr int kKF = 2;    // tokens per flush of the column sums
 }  // namespace
 
-template <int DK>
+template <class T, int DK>
 constexpr int gdn2_bwd_threads() {
-  return kGdn2BwdCols * (DK / kRows);
+  return gdn2_bwd_cols(sizeof(T) == 2 ? 1 : 0) * (DK / kRows);
 }
 
 template <class T, int DK, int DV, bool OUT>
-__global__ __launch_bounds__(gdn2_bwd_threads<DK>()) void gdn2_chunk_bwd_kernel(Gdn2BwdArgs a) {
-  constexpr int C = kChunk, R = kRows, RG = DK / R, NCOL = kGdn2BwdCols, NTH = NCOL * RG, NWV = NTH / 64;
+__global__ __launch_bounds__((gdn2_bwd_threads<T, DK>())) void gdn2_chunk_bwd_kernel(Gdn2BwdArgs a) {
+  constexpr int C = kChunk, R = kRows, RG = DK / R, NCOL = gdn2_bwd_cols(sizeof(T) == 2 ? 1 : 0);
+  constexpr int NTH = NCOL * RG, NWV = NTH / 64;
   constexpr int NB_OUT = DV / NCOL, NB_MAP = (DK + DV) / NCOL, NB = OUT ? NB_OUT : NB_MAP, NB_ALL = NB_OUT + NB_MAP;
   constexpr int NV = OUT ? 4 : 3;  // column sums per token: dk, da, db (, dq)
   static_assert(RG == 8 || RG == 16, "dk of 64 or 128");
@@ -253,9 +255,9 @@ __global__ __launch_bounds__(gdn2_bwd_threads<DK>()) void gdn2_chunk_bwd_kernel(
 // dq, dk, dv, da, db, dw of every token: the workgroups' partial sums in a fixed order, plus
 // the router's parts (dqbar of the token's chunk divided by its token count, and the
 // per-token key gradient) when given.  One thread per (b, t, h, row).
-template <int DK, int DV>
+template <int DK, int DV, int NCOL>
 __global__ __launch_bounds__(256) void gdn2_chunk_bwd_finalize_kernel(Gdn2BwdArgs a) {
-  constexpr int C = kChunk, NCOL = kGdn2BwdCols, NB_OUT = DV / NCOL, NB_ALL = NB_OUT + (DK + DV) / NCOL;
+  constexpr int C = kChunk, NB_OUT = DV / NCOL, NB_ALL = NB_OUT + (DK + DV) / NCOL;
   constexpr int W = DK > DV ? DK : DV;
   const int64_t id = blockIdx.x * (int64_t)256 + threadIdx.x;
   const int64_t total = a.B * a.T * a.H * W;
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(256) void gdn2_chunk_bwd_finalize_kernel(Gdn2BwdArg
 template <class T, int DK, int DV>
 static hipError_t launch_gdn2_bwd_t(const Gdn2BwdArgs& a, int stages, hipStream_t s) {
   const int64_t BHN = a.B * a.H * (int64_t)(a.c1 - a.c0);
-  constexpr int NT = gdn2_bwd_threads<DK>(), NCOL = kGdn2BwdCols;
+  constexpr int NT = gdn2_bwd_threads<T, DK>(), NCOL = gdn2_bwd_cols(sizeof(T) == 2 ? 1 : 0);
   if ((stages & (kChunkBwdOut | kChunkBwdMap)) && BHN > 0) {
     TimedLaunch tl(HLA_KERNEL_BWD_CHUNK, s);
     if (stages & kChunkBwdOut)
@@ -328,8 +330,8 @@ static hipError_t launch_gdn2_bwd_t(const Gdn2BwdArgs& a, int stages, hipStream_
   if (e != hipSuccess || !(stages & kChunkBwdFinalize)) return e;
   constexpr int W = DK > DV ? DK : DV;
   const int64_t total = a.B * a.T * a.H * W;
-  hipLaunchKernelGGL((gdn2_chunk_bwd_finalize_kernel<DK, DV>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                     a);
+  hipLaunchKernelGGL((gdn2_chunk_bwd_finalize_kernel<DK, DV, NCOL>), dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, s, a);
   return hipGetLastError();
 }
 

@@ -320,11 +320,12 @@ struct Gdn2BwdArgs {
   const float* dAt;         // [B,H,N,dk,dk] (have_map)
   const float* dBc;         // [B,H,N,dk,dv]
   float* dchunk_init;       // out [B,H,N,dk,dv] (have_out)
-  // workspace: per-workgroup column sums (16 state columns per workgroup)
-  float* part_k;            // [B,H,N,(dv + dk + dv)/16,64,dk]
+  // workspace: per-workgroup column sums (NC = gdn2_bwd_cols(dtype) state columns per
+  // workgroup)
+  float* part_k;            // [B,H,N,(dv + dk + dv)/NC,64,dk]
   float* part_a;            // same
   float* part_b;            // same
-  float* part_q;            // [B,H,N,dv/16,64,dk]
+  float* part_q;            // [B,H,N,dv/NC,64,dk]
   float* part_v;            // [B,H,N,2,64,dv]: outputs part, maps part
   float* part_w;            // same
   const float* dqbar;       // [B,H,N,dk] router parts added by the finalize pass, or null
@@ -336,7 +337,9 @@ struct Gdn2BwdArgs {
   float* db;                // out [B,T,H,dk]
   float* dw;                // out [B,T,H,dv]
 };
-constexpr int kGdn2BwdCols = 16;  // state columns per workgroup of the Gated DeltaNet-2 reverse
+// State columns per workgroup of the Gated DeltaNet-2 reverse: 32 for bf16 inputs (dtype 1),
+// 16 for float32 ones (their keys and queries take twice the LDS).
+constexpr int gdn2_bwd_cols(int dtype) { return dtype == 1 ? 32 : 16; }
 hipError_t launch_gdn2_chunk_backward(const Gdn2BwdArgs& a, int dtype, int dk, int dv, int stages, hipStream_t s);
 
 struct RouterBwdArgs {

@@ -378,11 +378,11 @@ def test_prefill_backward_validation(lib):
 
 
 def test_gdn2_backward_workspace_sizes(lib):
-    """Column sums of 16-column workgroups: dk, da and db over every slot, dq over the
-    outputs' slots, dv and dw per part; the prefill backward differs from Gated DeltaNet's
-    by the chunk reverse's region only."""
+    """Column sums of workgroups of 32 state columns (bf16; 16 for float32): dk, da and db
+    over every slot, dq over the outputs' slots, dv and dw per part; the prefill backward
+    differs from Gated DeltaNet's by the chunk reverse's region only."""
     d = dims(B=2, T=130, H=3, dk=128, dv=64, dtype=1)  # N = 3
-    BHN, nb_out, nb_all = 6 * 3, 64 // 16, 64 // 16 + (128 + 64) // 16
+    BHN, nb_out, nb_all = 6 * 3, 64 // 32, 64 // 32 + (128 + 64) // 32
     vec = _r(BHN * nb_all * 64 * 128 * 4)
     g2 = 3 * vec + _r(BHN * nb_out * 64 * 128 * 4) + 2 * _r(BHN * 2 * 64 * 64 * 4)
     assert hla.workspace_bytes(hla.FN_GDN2_CHUNK_BACKWARD, d) == g2
@@ -390,6 +390,10 @@ def test_gdn2_backward_workspace_sizes(lib):
     for one, two in ((hla.FN_PREFILL_BACKWARD, hla.FN_GDN2_PREFILL_BACKWARD),
                      (hla.FN_PREFILL_BACKWARD_MIN, hla.FN_GDN2_PREFILL_BACKWARD_MIN)):
         assert hla.workspace_bytes(two, d) - hla.workspace_bytes(one, d) == g2 - g1
+    d32 = dims(B=2, T=130, H=3, dk=128, dv=64, dtype=0)
+    nb_out, nb_all = 64 // 16, 64 // 16 + (128 + 64) // 16
+    assert hla.workspace_bytes(hla.FN_GDN2_CHUNK_BACKWARD, d32) == 3 * _r(BHN * nb_all * 64 * 128 * 4) + \
+        _r(BHN * nb_out * 64 * 128 * 4) + 2 * _r(BHN * 2 * 64 * 64 * 4)
     out = ctypes.c_size_t()
     for fn in (hla.FN_GDN2_CHUNK_BACKWARD, hla.FN_GDN2_PREFILL_BACKWARD, hla.FN_GDN2_PREFILL_BACKWARD_MIN):
         assert lib.hla_workspace_bytes(fn, ctypes.byref(dims(C=128)), 0, ctypes.byref(out)) == UNSUPPORTED
