@@ -56,11 +56,18 @@ __global__ __launch_bounds__(256) void qbar_kernel(RouteArgs a) {
 // chunk's rows are prefetched into registers while the current one is scored.  Queries
 // are the columns, so pooling over representatives is lane-local plus one exchange
 // between the lane halves.
-constexpr int kGateSeg = 32;  // history chunks per workgroup: 2x the workgroups of 64, fewer rounds each
+// History chunks per workgroup of gate_kernel: about 64 rounds of 32 representatives each
+// (32 chunks of the raw 64 keys; 8 chunks of 256 keys, so that C = 256, with 4x fewer
+// chunks, still fills the GPU), and at most 32 chunks.
+__host__ __device__ inline int gate_seg(int n_rep) {
+  const int nkt = (n_rep + 31) / 32;
+  const int s = 64 / nkt;
+  return s < 1 ? 1 : (s > 32 ? 32 : s);
+}
 template <class T, int DK>
 __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
   using MM = Mma<T>;
-  constexpr int JSEG = kGateSeg;
+  const int JSEG = gate_seg(a.n_rep);
   constexpr int PAD = 16 / sizeof(T), UPR = DK / PAD;
   constexpr int RT = 32;                  // representatives staged per round
   constexpr int PR = DK + PAD;            // LDS row pitch (elements)
@@ -397,7 +404,8 @@ static hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
     TimedLaunch tl(HLA_KERNEL_GATES, s);
     if (!a.gates_in && a.N > 1) {
       hipLaunchKernelGGL((qbar_kernel<T, DK>), dim3((unsigned)(BH * a.N)), dim3(256), 0, s, a);
-      const int64_t nqt = (a.N + 31) / 32, nqg = (nqt + 3) / 4, njs = (a.N + kGateSeg - 1) / kGateSeg;
+      const int64_t nqt = (a.N + 31) / 32, nqg = (nqt + 3) / 4, seg = gate_seg(a.n_rep);
+      const int64_t njs = (a.N + seg - 1) / seg;
       hipLaunchKernelGGL((gate_kernel<T, DK>), dim3((unsigned)(BH * nqg * njs)), dim3(256), 0, s, a);
     }
     hipLaunchKernelGGL(lists_kernel, dim3((unsigned)(BH * a.N)), dim3(64), 0, s, a);

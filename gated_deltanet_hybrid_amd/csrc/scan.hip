@@ -170,9 +170,20 @@ __global__ __launch_bounds__(DK / 32 * 64 + (LANES ? 64 : 0)) void scan_bf16_ker
 
   const int lane = threadIdx.x & 63, hh = lane >> 5, c32 = lane & 31;
   const int rt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t id = blockIdx.x;
-  const int ct = (int)(id % NCT);
-  const int64_t rest = id / NCT;
+  // block -> (column tile, scan): consecutive blocks go to the 8 XCDs in turn, and the NCT
+  // column tiles of one scan all read its At, so when the scans come in multiples of 8 the
+  // tiles of a scan take block indices equal mod 8: one XCD, one L2 for its At
+  const int64_t id = blockIdx.x, nscan = gridDim.x / NCT;
+  int ct;
+  int64_t rest;
+  if (nscan % 8 == 0) {
+    const int64_t r = id >> 3;
+    ct = (int)(r % NCT);
+    rest = (r / NCT) * 8 + (id & 7);
+  } else {
+    ct = (int)(id % NCT);
+    rest = id / NCT;
+  }
   const int N = a.N;
   int64_t bh = rest;
   int NS = 1, g = 0, c0 = 0, nsub = N;
