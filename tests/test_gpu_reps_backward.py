@@ -150,3 +150,44 @@ def test_learned_reps_prefill_backward_chain():
             assert_close(host(g1[n])[0, :, hh], r1[n], dtype, n)
         for n in NAMES:
             assert_close(host(g3["d" + n])[hh], r3["d" + n], dtype, "d" + n)
+
+
+def test_learned_reps_gdn2_prefill_backward_chain():
+    """The same three-call chain under the Gated DeltaNet-2 recurrence: its routed-prefill
+    backward with the forward's gates, then the (shared) router and pooler backward."""
+    dtype, dk, dv, B, H, T, window, C = "bf16", 128, 64, 1, 2, 4 * 64 - 21, 16, 64
+    note("learned-representative gated deltanet-2 prefill backward chain")
+    n_rep = C // window
+    x = inputs.gen_tokens(B, T, H, dk, dv, dtype=dtype, seed=211, alpha_mode="slow")
+    q, k, v, _, _ = token_tensors(x)
+    gg = inputs.gen_gdn2_gates(B, T, H, dk, dv, seed=212, alpha_mode="slow")
+    ga, gb, gw = (f32(gg[n]) for n in ("a", "b", "w"))
+    Wd, W64 = _weights(H, dk, dtype, True, True, seed=213)  # one weight set shared by the heads
+    dO = inputs.gen_cotangent((B, T, H, dv), seed=214, name="dO")
+    h = hla()
+    reps = h.chunk_reps(k, Wd, window=window)
+    At, Bc = h.gdn2_chunk_transitions(k, v, ga, gb, gw)
+    fw = h.route_mix(q, reps, At, Bc, n_rep=n_rep, tau=1e-3)
+    g1 = h.gdn2_prefill_backward(q, k, v, ga, gb, gw, f32(dO), tau=1e-3, gates_in=fw["gates"])
+    g2 = h.router_backward(q, reps, n_rep, fw["gates"], g1["dgates"])
+    g3 = h.chunk_reps_backward(k, Wd, g2["dreps"], window=window)
+    torch.cuda.synchronize()
+    Wh = [W64[n][0] for n in NAMES]
+    dW = {n: 0.0 for n in NAMES}
+    for hh in range(H):
+        qq, kk, vv = (x.f64(n)[0, :, hh] for n in ("q", "k", "v"))
+        aa, bb, ww = (gg[n][0, :, hh].astype(np.float64) for n in ("a", "b", "w"))
+        reps_o = oracle.window_reps(kk, C, window, *Wh[:4]) @ Wh[4]
+        gates_o = oracle.router_gates(qq, reps_o, n_rep, C, 1e-3)["gates"]
+        r1 = oracle.gdn2_hla_prefill_backward(qq, kk, vv, aa, bb, ww, C, 1e-3, dO[0, :, hh].astype(np.float64),
+                                              gates_in=gates_o)
+        r2 = oracle.router_backward(qq, reps_o, n_rep, C, r1["dgates"])
+        r3 = oracle.window_reps_backward(kk, C, window, *Wh[:4], r2["dreps"], Wr=Wh[4])
+        assert_close(host(g1["dq"] + g2["dq"])[0, :, hh], r1["dq"] + r2["dq"], dtype, "dq")
+        assert_close(host(g1["dk"] + g3["dk"])[0, :, hh], r1["dk"] + r3["dk"], dtype, "dk")
+        for n in ("dv", "da", "db", "dw"):
+            assert_close(host(g1[n])[0, :, hh], r1[n], dtype, n)
+        for n in NAMES:
+            dW[n] = dW[n] + r3["d" + n]
+    for n in NAMES:
+        assert_close(host(g3["d" + n])[0], dW[n], dtype, "d" + n + " (shared)")
