@@ -627,6 +627,20 @@ def flops_router_bwd(pairs, n_rep, dk):
     return pairs * 4 * 2 * n_rep * dk
 
 
+def state_traffic(pairs, dk, dv, ms):
+    """The per-pair state bytes each composition-backward pass moves by design (bf16 dk x dv
+    matrices: the replay writes M_{j-1} and D_j, the adjoint reads D_j and writes g lambda_j,
+    the reduce reads M_{j-1} and g lambda_j), and the HBM rate they make per pass: context
+    for the matrix-core fractions, since these passes are bound by that traffic."""
+    per = pairs * dk * dv * 2
+    out = {}
+    for name, n in (("bwd_save", 2), ("bwd_adjoint", 2), ("bwd_reduce", 2)):
+        if name in ms:
+            gbs = n * per / (ms[name] / 1e3) / 1e9
+            out[name] = dict(bytes=n * per, achieved=round(gbs, 1), frac=round(gbs / PEAK_HBM_GBS, 4))
+    return dict(unit="GB/s", peak=PEAK_HBM_GBS, **out)
+
+
 def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, ws_gib=None):
     """The routed-prefill backward (hla_prefill_backward) at B=1, T tokens (8192 by default),
     H=16, d=128, C=64, bf16, computed gates at tau = 1e-3: recomputed chunk maps and gates,
@@ -704,6 +718,7 @@ def bench_prefill_backward(args, torch, hla, inputs, x, T=BWD_T, ws_gib=None):
                chunk_reverse=dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_FP32_MFMA_TFLOPS,
                                   unit="TFLOP/s", frac=round(ach / PEAK_FP32_MFMA_TFLOPS, 4), flops_per_step=fl_chunk),
                composition_mfma=dict(flops_per_pass=fl_pair, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", **mfma),
+               composition_state_traffic=state_traffic(pairs, W.dk, W.dv, ms),
                router_tflops=round(flops_router_bwd(pairs, C, W.dk) / (ms["bwd_router"] / 1e3) / 1e12, 2),
                min_workspace_gib=round(hla.workspace_bytes(hla.FN_PREFILL_BACKWARD_MIN, d) / 2**30, 2))
     log(f"[routed_prefill_backward T={T}] {dt*1e3:.3f} ms/step, {W.B*T/dt/1e6:.3f} M tok/s in "
