@@ -99,10 +99,21 @@ int64_t reps_ws(const hla_dims_t* d, int32_t n_rep) {
 
 // Workspace of hla_router_backward: the query-chunk means and their gradients.
 int64_t router_bwd_ws(const hla_dims_t* d) { return 2 * round_up(d->B * d->H * n_chunks(d) * d->dk * 4, 256); }
-// Workspace of hla_chunk_reps_backward: every 64-token tile's weight gradients (4 matrices,
-// 5 with Wr).
-int64_t reps_bwd_ws(const hla_dims_t* d, bool with_wr) {
-  return round_up(d->B * d->H * ((d->T + 63) / 64) * (with_wr ? 5 : 4) * (int64_t)d->dk * d->dk * 4, 256);
+// Workspace of hla_chunk_reps_backward: dWq, dWk, dWv of every workgroup of the tile kernel
+// (8 consecutive 64-token tiles of a (b, h) row), then four vectors (dz, m, z, dr') per
+// window, sized for the smallest window (8 per tile).
+int64_t reps_bwd_rows(const hla_dims_t* d) { return (d->T + 63) / 64 * 8; }
+int64_t reps_bwd_part_bytes(const hla_dims_t* d) {
+  const int64_t groups = ((d->T + 63) / 64 + 7) / 8;
+  return round_up(d->B * d->H * groups * 3 * (int64_t)d->dk * d->dk * 4, 256);
+}
+int64_t reps_bwd_vec_bytes(const hla_dims_t* d) {
+  return round_up(4 * d->B * reps_bwd_rows(d) * d->H * d->dk * 4, 256);
+}
+// then dWp and dWr of every chunk of 256 windows of one (b, h)
+int64_t reps_bwd_ws(const hla_dims_t* d, bool) {
+  const int64_t chunks = d->B * d->H * ((reps_bwd_rows(d) + 255) / 256);
+  return reps_bwd_part_bytes(d) + reps_bwd_vec_bytes(d) + round_up(2 * chunks * (int64_t)d->dk * d->dk * 4, 256);
 }
 
 // Workspace of hla_compose_backward with history segments of K steps: (At - I) and its
@@ -570,6 +581,9 @@ hla_status_t hla_chunk_reps_backward(const hla_dims_t* d, const void* k, int32_t
   a.Wq = Wq; a.Wk = Wk; a.Wv = Wv; a.Wp = Wp; a.Wr = Wr; a.w_hstride = w_hstride;
   a.dreps = dreps; a.R = n_chunks(d) * (d->C / window); a.dk = dk;
   a.part = static_cast<float*>(ws);
+  a.wvec = reinterpret_cast<float*>(static_cast<char*>(ws) + reps_bwd_part_bytes(d));
+  a.part2 = reinterpret_cast<float*>(static_cast<char*>(ws) + reps_bwd_part_bytes(d) + reps_bwd_vec_bytes(d));
+  a.RW = reps_bwd_rows(d);
   a.dW[0] = dWq; a.dW[1] = dWk; a.dW[2] = dWv; a.dW[3] = dWp; a.dW[4] = Wr ? dWr : nullptr;
   return hip_status(hla::launch_reps_backward(a, d->dtype, d->dk, stream));
 }

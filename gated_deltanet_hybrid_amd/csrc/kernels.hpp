@@ -205,8 +205,12 @@ struct RepsBwdArgs {
   const float* dreps;     // [B,R,H,dk]: row t0 / window is the window starting at token t0
   int64_t R;              // rows per batch of dreps
   float* dk;              // out [B,T,H,dk]
-  float* part;            // workspace [B,H,ceil(T/64),NM,dk,dk]: each tile's weight gradients
-                          // (NM = 4 without Wr: q, k, v, p; 5 with it: q, k, v, p, r)
+  float* part;            // workspace [B,H,ceil(ceil(T/64)/8),3,dk,dk]: dWq, dWk, dWv of each
+                          // workgroup of the tile kernel (8 tiles of 64 tokens)
+  float* wvec;            // workspace [4,B,RW,H,dk]: each window's dz, m, z and dr', row
+                          // t0 / window for the window starting at token t0
+  int64_t RW;             // rows per batch of wvec: ceil(T/64) 8 (the most, at window 8)
+  float* part2;           // workspace: dWp (and dWr) of every chunk of 256 windows of a (b, h)
   float* dW[5];           // out [Hw,dk,dk] float32: dWq, dWk, dWv, dWp, dWr (Hw = H, or 1
                           // when shared)
 };

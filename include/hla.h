@@ -518,7 +518,8 @@ hla_status_t hla_router_backward(const hla_dims_t* d, const void* q, const void*
  *           each head's matrix dk * dk elements after the previous one.
  *   dWr    : same, out; required exactly when Wr is given.
  *   ws, ws_bytes : hla_workspace_bytes(HLA_FN_CHUNK_REPS_BACKWARD, d, Wr ? 1 : 0) bytes
- *           (every 64-token tile's weight gradients).
+ *           (dWq, dWk and dWv of every 8 consecutive 64-token tiles, and four dk-vectors per
+ *           window).
  * Errors: as hla_chunk_reps, and HLA_ERR_UNSUPPORTED (C not a multiple of 64).
  */
 hla_status_t hla_chunk_reps_backward(const hla_dims_t* d, const void* k, int32_t window, const void* Wq,

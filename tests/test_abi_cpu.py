@@ -454,8 +454,17 @@ def test_gdn2_prefill_backward_validation(lib):
 def test_reps_and_router_backward_workspace_sizes(lib):
     d = dims(B=2, T=130, H=3, dk=128, dv=64, dtype=1)  # 3 tiles of 64 tokens, N = 3
     assert hla.workspace_bytes(hla.FN_ROUTER_BACKWARD, d) == 2 * _r(2 * 3 * 3 * 128 * 4)
-    assert hla.workspace_bytes(hla.FN_CHUNK_REPS_BACKWARD, d, 0) == _r(2 * 3 * 3 * 4 * 128 * 128 * 4)
-    assert hla.workspace_bytes(hla.FN_CHUNK_REPS_BACKWARD, d, 1) == _r(2 * 3 * 3 * 5 * 128 * 128 * 4)
+    # the pooler: dWq, dWk, dWv per workgroup of 8 tiles (one group at 3 tiles, 2 at 9), then
+    # four vectors per window, sized for windows of 8 (8 per tile), then dWp and dWr per chunk
+    # of 256 windows of a (b, h)
+    for T, groups in ((130, 1), (9 * 64 - 5, 2), (40 * 64, 5)):
+        dd = dims(B=2, T=T, H=3, dk=128, dv=64, dtype=1)
+        ntl = -(-T // 64)
+        chunks = 2 * 3 * (-(-ntl * 8 // 256))
+        want = _r(2 * 3 * groups * 3 * 128 * 128 * 4) + _r(4 * 2 * ntl * 8 * 3 * 128 * 4) + \
+            _r(2 * chunks * 128 * 128 * 4)
+        for wr in (0, 1):
+            assert hla.workspace_bytes(hla.FN_CHUNK_REPS_BACKWARD, dd, wr) == want
     out = ctypes.c_size_t()
     assert lib.hla_workspace_bytes(hla.FN_ROUTER_BACKWARD, ctypes.byref(dims(C=128)), 0, ctypes.byref(out)) == \
         UNSUPPORTED
