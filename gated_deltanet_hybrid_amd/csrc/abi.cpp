@@ -97,8 +97,12 @@ int64_t reps_ws(const hla_dims_t* d, int32_t n_rep) {
   return round_up(d->B * d->H * n_chunks(d) * n_rep * d->dk * 4, 256);
 }
 
-// Workspace of hla_router_backward: the query-chunk means and their gradients.
-int64_t router_bwd_ws(const hla_dims_t* d) { return 2 * round_up(d->B * d->H * n_chunks(d) * d->dk * 4, 256); }
+// Workspace of hla_router_backward: the query-chunk means, their gradients, then the
+// per-segment parts of those gradients.
+int64_t router_bwd_means(const hla_dims_t* d) { return round_up(d->B * d->H * n_chunks(d) * d->dk * 4, 256); }
+int64_t router_bwd_ws(const hla_dims_t* d) {
+  return 2 * router_bwd_means(d) + hla::router_bwd_part_bytes(d->B, d->H, n_chunks(d), d->dk);
+}
 // Workspace of hla_chunk_reps_backward: dWq, dWk, dWv of every workgroup of the tile kernel
 // (8 consecutive 64-token tiles of a (b, h) row), then four vectors (dz, m, z, dr') per
 // window, sized for the smallest window (8 per tile).
@@ -239,7 +243,7 @@ void set_gdn2_chunk_bwd_ws(hla::Gdn2BwdArgs& a, const Gdn2ChunkBwdWs& w, void* w
 // that what a caller's workspace holds beyond the rest sets the segment length).
 struct PrefillBwdWs {
   int64_t at_off, bc_off, gates_off, mask_off, aidx_off, acnt_off, sr_off, dsr_off, dat_off, dbc_off, dg_off,
-      qbar_off, dqbar_off, dkr_off, route_off, chunk_off, comp_off, total;
+      qbar_off, dqbar_off, dkr_off, rpart_off, route_off, chunk_off, comp_off, total;
 };
 // (hla_gdn2_prefill_backward: the same with the Gated DeltaNet-2 chunk backward's region)
 PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d, int64_t K, int variant = 0) {
@@ -265,6 +269,7 @@ PrefillBwdWs prefill_bwd_ws(const hla_dims_t* d, int64_t K, int variant = 0) {
   w.qbar_off = take(BHN * d->dk * 4);
   w.dqbar_off = take(BHN * d->dk * 4);
   w.dkr_off = take(d->B * d->T * d->H * d->dk * 4);
+  w.rpart_off = take(hla::router_bwd_part_bytes(d->B, d->H, N, d->dk));
   w.route_off = take(route_ws(d));
   w.chunk_off = take(variant == 2 ? gdn2_chunk_bwd_ws(d).total : chunk_bwd_ws(d).total);
   w.comp_off = take(compose_bwd_ws(d, K).total);
@@ -602,7 +607,8 @@ hla_status_t hla_router_backward(const hla_dims_t* d, const void* q, const void*
   hla::RouterBwdArgs rb{};
   rb.q = q; rb.reps = reps; rb.gates = gates; rb.dgates = dgates;
   rb.qbar = static_cast<float*>(ws);
-  rb.dqbar = reinterpret_cast<float*>(static_cast<char*>(ws) + router_bwd_ws(d) / 2);
+  rb.dqbar = reinterpret_cast<float*>(static_cast<char*>(ws) + router_bwd_means(d));
+  rb.part = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * router_bwd_means(d));
   rb.dreps = dreps; rb.dq_tok = dq;
   rb.B = d->B; rb.T = d->T; rb.H = d->H; rb.ld_T = d->ld_T; rb.N = (int32_t)N;
   rb.n_rep = n_rep; rb.ld_R = ld_R; rb.R_out = N * n_rep;
@@ -807,7 +813,7 @@ static hla_status_t prefill_backward_body(const hla_dims_t* d, int variant, cons
   if (!gates_in && N > 1) {
     hla::RouterBwdArgs rb{};
     rb.q = q; rb.reps = k; rb.gates = r.gates; rb.dgates = dg;
-    rb.qbar = fat(w.qbar_off); rb.dqbar = fat(w.dqbar_off); rb.dreps = fat(w.dkr_off);
+    rb.qbar = fat(w.qbar_off); rb.dqbar = fat(w.dqbar_off); rb.dreps = fat(w.dkr_off); rb.part = fat(w.rpart_off);
     rb.B = d->B; rb.T = d->T; rb.H = d->H; rb.ld_T = d->ld_T; rb.N = N;
     rb.n_rep = kPiece; rb.ld_R = d->ld_T; rb.R_out = d->T;  // the raw keys, rows = tokens
     e = hla::launch_router_backward(rb, d->dtype, d->dk, stream);

@@ -360,7 +360,20 @@ struct RouterBwdArgs {
   int32_t N;
   int32_t n_rep;         // 1 .. 64
   int64_t ld_R, R_out;
+  float* part;           // workspace of router_bwd_part_bytes: dqbar per history segment
 };
+// History chunks per workgroup of the router backward's query-side pass: about 1024
+// workgroups over (b, h, group of 128 query chunks, segment), between 4 and 32 chunks.
+__host__ __device__ inline int router_bwd_seg(int64_t BH, int64_t N) {
+  const int64_t nqg = ((N + 31) / 32 + 3) / 4;
+  const int64_t s = (N * BH * nqg + 1023) / 1024;
+  return (int)(s < 4 ? 4 : (s > 32 ? 32 : s));
+}
+// Workspace bytes of the router backward's parts: dqbar per history segment.
+inline int64_t router_bwd_part_bytes(int64_t B, int64_t H, int64_t N, int dk) {
+  const int64_t seg = router_bwd_seg(B * H, N), njs = (N + seg - 1) / seg;
+  return (njs * B * H * N * dk * 4 + 255) / 256 * 256;
+}
 // Backward of the router gates to the query-chunk means and the representatives.
 hipError_t launch_router_backward(const RouterBwdArgs& a, int dtype, int dk, hipStream_t s);
 

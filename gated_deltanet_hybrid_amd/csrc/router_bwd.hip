@@ -11,8 +11,19 @@
 // and every token of chunk i receives dqbar_i / n_i (added by the chunk backward's
 // finalize pass, or written per token here).
 //
-// Lane r owns representative r of a history chunk (lanes r >= n_rep take no part), so the
-// softmax over a chunk's representatives is a wave reduction.
+// Both sums run on the matrix cores in the forward gate pass's orientation: S^T (a history
+// chunk's representatives x 32 query chunks, one query per lane column) from representative
+// rows and query means (float32 split into bf16 high and low parts on the bf16 path, so the
+// scores keep float32 accuracy), the softmax down each lane's column, and
+// Z^T = (dl p / sqrt(dk))^T in the accumulators.  Then
+//   query side (router_dq_kernel): dqbar (32 queries x dk per wave) += Z R_j, with Z^T taken
+//     straight from the accumulators (their row order serves as the k order of the next
+//     product) and R_j staged feature-major in LDS; one workgroup per (b, h, 128 query
+//     chunks, segment of history chunks), each segment's sum a part that
+//     router_dq_sum_kernel adds in a fixed order;
+//   representative side (router_dr_kernel): one wave per history chunk j, dR_j (n_rep x dk)
+//     += Z Qbar over tiles of 32 query chunks i > j, Z transposed through LDS, written once.
+// No atomics: the results are bitwise reproducible.
 #include <math.h>
 
 #include "common.hpp"
@@ -21,164 +32,350 @@
 
 namespace hla {
 
-// Query-chunk side: qbar_i, then dqbar_i.  A workgroup takes 4 consecutive query chunks,
-// one per wave; the keys of each history chunk j are staged once in LDS rows padded by 16
-// bytes (row r read by lane r in 16-byte pieces, so each 16-lane phase hits distinct
-// banks) and the next chunk's keys are loaded into registers while the current ones are
-// used.
-constexpr int kRouterQG = 4;
+namespace {
+constexpr int kRT = 64;  // representative rows of a history chunk, padded (n_rep <= 64)
 
-// q . k over DK with eight independent partial sums (no long dependent chain); k is a
-// 16-byte aligned LDS row, q a per-wave (LDS) or wave-uniform (global) vector.
-template <int DK>
-__device__ __forceinline__ float dot_rows(const float* q, const float* k) {
-  float p[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) p[u] = 0.f;
-#pragma unroll
-  for (int e = 0; e < DK; e += 8) {
-    const float4 k0 = *reinterpret_cast<const float4*>(k + e), k1 = *reinterpret_cast<const float4*>(k + e + 4);
-    p[0] = fmaf(q[e], k0.x, p[0]);
-    p[1] = fmaf(q[e + 1], k0.y, p[1]);
-    p[2] = fmaf(q[e + 2], k0.z, p[2]);
-    p[3] = fmaf(q[e + 3], k0.w, p[3]);
-    p[4] = fmaf(q[e + 4], k1.x, p[4]);
-    p[5] = fmaf(q[e + 5], k1.y, p[5]);
-    p[6] = fmaf(q[e + 6], k1.z, p[6]);
-    p[7] = fmaf(q[e + 7], k1.w, p[7]);
-  }
-  return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+// x ~= hi + lo with both parts in bf16 (about 16 significant bits together): element e of
+// the fragments fh (high parts) and fl (low parts)
+__device__ __forceinline__ void split_bf16(float x, bf16x8& fh, bf16x8& fl, int e) {
+  const bf16 hi = (bf16)x;
+  fh[e] = hi;
+  fl[e] = (bf16)(x - (float)hi);
 }
 
+// softmax over a history chunk's representatives of the scores in sc (rows = representatives
+// rt * 32 + acc_row(e, hh), this lane's column = one query), scaled by w: sc <- w p.
+__device__ __forceinline__ void column_softmax(f32x16 (&sc)[2], int n_rep, int hh, float scale, float w) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float v = rt * 32 + acc_row(e, hh) < n_rep ? sc[rt][e] * scale : -INFINITY;
+      sc[rt][e] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  float sum = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sc[rt][e] = __expf(sc[rt][e] - mx);  // 0 past n_rep
+      sum += sc[rt][e];
+    }
+  sum += __shfl_xor(sum, 32, 64);
+  const float z = w / sum;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[rt][e] *= z;
+}
+
+// dl_ij = dg_ij g_ij (1 - g_ij) of one (query chunk, history chunk) pair
+__device__ __forceinline__ float pair_weight(const RouterBwdArgs& a, int64_t bh, int i, int j) {
+  const int64_t o = (bh * a.N + i) * (int64_t)a.N + j;
+  const float g = a.gates[o];
+  return a.dgates[o] * g * (1.f - g);
+}
+}  // namespace
+
+// qbar_i, the mean of q over query chunk i: one thread per (b, h, i, feature).
 template <class T, int DK>
-__global__ __launch_bounds__(64 * kRouterQG) void router_dq_kernel(RouterBwdArgs a) {
-  constexpr int C = kChunk, QG = kRouterQG, NTH = 64 * QG, PK = DK + 4;
-  constexpr int EPP = 16 / (int)sizeof(T), UPR = DK / EPP, NU = C * UPR / NTH;  // 16-byte units
-  static_assert(NU * NTH == C * UPR, "key staging split");
-  __shared__ __attribute__((aligned(16))) float s_key[C * PK];
-  __shared__ __attribute__((aligned(16))) float s_qb[QG][DK];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int ng = (a.N + QG - 1) / QG;
-  const int64_t bh = blockIdx.x / ng;
-  const int i0 = (ng - 1 - (int)(blockIdx.x % ng)) * QG;  // longest histories first
-  const int i = i0 + w;
-  const int64_t h = bh % a.H, b = bh / a.H;
+__global__ __launch_bounds__(256) void router_qbar_kernel(RouterBwdArgs a) {
+  const int64_t id = blockIdx.x * (int64_t)256 + threadIdx.x;
+  if (id >= a.B * a.H * a.N * DK) return;
+  const int e = (int)(id % DK);
+  const int64_t bhi = id / DK;
+  const int i = (int)(bhi % a.N);
+  const int64_t bh = bhi / a.N, h = bh % a.H, b = bh / a.H;
+  const int64_t t0 = (int64_t)i * kChunk;
+  const int ni = (int)((a.T - t0) < kChunk ? (a.T - t0) : kChunk);
   const T* q = reinterpret_cast<const T*>(a.q);
-  const T* k = reinterpret_cast<const T*>(a.reps);
-  const float rs = 1.f / sqrtf((float)DK);
-  if (i < a.N) {
-    const int64_t t0 = (int64_t)i * C;
-    const int ni = (int)((a.T - t0) < C ? (a.T - t0) : C);
-    for (int e = lane; e < DK; e += 64) {
-      float sq = 0.f;
-      for (int t = 0; t < ni; ++t) sq += to_f<T>(q[((b * a.ld_T + t0 + t) * a.H + h) * DK + e]);
-      sq /= (float)ni;
-      s_qb[w][e] = sq;
-      a.qbar[(bh * a.N + i) * DK + e] = sq;
+  float s = 0.f;
+  for (int t = 0; t < ni; ++t) s += to_f<T>(q[((b * a.ld_T + t0 + t) * a.H + h) * DK + e]);
+  a.qbar[id] = s / (float)ni;
+}
+
+// Query side.  Wave w of workgroup (b, h, qg, js) owns query chunks (4 qg + w) 32 + lane % 32
+// and sums over history chunks j in [js seg, (js + 1) seg) below the group's last query
+// chunk.  Chunk j + 1's rows are prefetched into registers while chunk j is used.
+template <class T, int DK>
+__global__ __launch_bounds__(256) void router_dq_kernel(RouterBwdArgs a) {
+  using MM = Mma<T>;
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int EPP = 16 / (int)sizeof(T), PR = DK + EPP, UPR = DK / EPP, NU = kRT * UPR / 256;
+  constexpr int PRT = kRT + 8;  // feature-major rows of the bf16 copy
+  constexpr int NKS = DK / MM::KS, NDT = DK / 32, NZK = BF ? 2 : 16;  // k-steps per 32 representatives
+  static_assert(NU * 256 == kRT * UPR, "staging split");
+  __shared__ __attribute__((aligned(16))) T sR[2][kRT * PR];
+  __shared__ __attribute__((aligned(16))) T sRT[2][BF ? DK * PRT : 1];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, c32 = lane & 31;
+  const int seg = router_bwd_seg(a.B * a.H, a.N);
+  const int nqg = ((a.N + 31) / 32 + 3) / 4, njs = (a.N + seg - 1) / seg;
+  int64_t id = blockIdx.x;
+  const int js = (int)(id % njs);
+  id /= njs;
+  const int qg = (int)(id % nqg);
+  const int64_t bh = id / nqg, h = bh % a.H, b = bh / a.H;
+  const int imax = ((qg + 1) * 128 < a.N ? (qg + 1) * 128 : a.N) - 1;  // the group's last query chunk
+  const int j_lo = js * seg, j_hi = j_lo + seg < imax ? j_lo + seg : imax;  // pairs j < i <= imax
+  if (j_lo >= j_hi) return;  // no pair here; router_dq_sum_kernel reads no part of it
+  const int qi = (qg * 4 + w) * 32 + c32;
+  const float scale = 1.f / sqrtf((float)DK);
+
+  // B operand of the scores: this lane's query mean
+  typename MM::Frag bhi[NKS], blo[BF ? NKS : 1];
+  {
+    const float* qb = a.qbar + (bh * a.N + (qi < a.N ? qi : 0)) * DK;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if constexpr (BF) {
+        bf16x8 fh, fl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split_bf16(qi < a.N ? qb[ks * 16 + hh * 8 + e] : 0.f, fh, fl, e);
+        bhi[ks] = fh;
+        blo[ks] = fl;
+      } else {
+        bhi[ks] = qi < a.N ? qb[ks * 2 + hh] : 0.f;
+      }
     }
   }
-  const int jmax = (i0 + QG - 1 < a.N - 1 ? i0 + QG - 1 : a.N - 1);  // history chunks 0 .. jmax-1
-  float acc[DK];
-#pragma unroll
-  for (int e = 0; e < DK; ++e) acc[e] = 0.f;
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 pre[NU];
-  // history chunk j's representative rows (every one exists: j < N - 1); rows r >= n_rep
-  // are zero and take no part
-  auto load_keys = [&](int j) {
+  const T* reps = reinterpret_cast<const T*>(a.reps);
+  uint4 pf[NU];
+  auto load_chunk = [&](int j) {
 #pragma unroll
     for (int m = 0; m < NU; ++m) {
-      const int u = tid + m * NTH, r = u / UPR, cu = u % UPR;
-      pre[m] = u32x4{0u, 0u, 0u, 0u};
+      const int u = tid + 256 * m, r = u / UPR, cu = u % UPR;
+      pf[m] = make_uint4(0u, 0u, 0u, 0u);
       if (r < a.n_rep)
-        pre[m] = *reinterpret_cast<const u32x4*>(
-            k + ((b * a.ld_R + (int64_t)j * a.n_rep + r) * a.H + h) * DK + cu * EPP);
+        pf[m] = *reinterpret_cast<const uint4*>(reps + ((b * a.ld_R + (int64_t)j * a.n_rep + r) * a.H + h) * DK +
+                                                cu * EPP);
     }
   };
-  if (jmax > 0) load_keys(0);
-  for (int j = 0; j < jmax; ++j) {
-    __syncthreads();  // earlier reads of s_key (and the s_qb writes) are done
+  auto store_chunk = [&](int buf) {
 #pragma unroll
     for (int m = 0; m < NU; ++m) {
-      const int u = tid + m * NTH, r = u / UPR, cu = u % UPR;
-      const T* v = reinterpret_cast<const T*>(&pre[m]);
+      const int u = tid + 256 * m, r = u / UPR, cu = u % UPR;
+      *reinterpret_cast<uint4*>(&sR[buf][r * PR + cu * EPP]) = pf[m];
+      if constexpr (BF) {
+        const bf16* v = reinterpret_cast<const bf16*>(&pf[m]);
 #pragma unroll
-      for (int e = 0; e < EPP; ++e) s_key[r * PK + cu * EPP + e] = to_f<T>(v[e]);
+        for (int e = 0; e < 8; ++e) sRT[buf][(cu * 8 + e) * PRT + r] = v[e];
+      }
     }
-    __syncthreads();
-    if (j + 1 < jmax) load_keys(j + 1);
-    if (i < a.N && j < i) {
-      const int64_t o = (bh * a.N + i) * (int64_t)a.N + j;
-      const float g = a.gates[o], dl = a.dgates[o] * g * (1.f - g);
-      if (dl != 0.f) {  // uniform over the wave
-        const float* kr = s_key + lane * PK;
-        const float sc = lane < a.n_rep ? dot_rows<DK>(s_qb[w], kr) * rs : -INFINITY;
-        const float mx = wave_max_valu(sc);
-        const float p = __expf(sc - mx);
-        const float cr = dl * (p / wave_sum_valu(p)) * rs;
+  };
+
+  f32x16 dq[NDT];
 #pragma unroll
-        for (int e = 0; e < DK; e += 4) {
-          const float4 kv = *reinterpret_cast<const float4*>(kr + e);
-          acc[e] = fmaf(cr, kv.x, acc[e]);
-          acc[e + 1] = fmaf(cr, kv.y, acc[e + 1]);
-          acc[e + 2] = fmaf(cr, kv.z, acc[e + 2]);
-          acc[e + 3] = fmaf(cr, kv.w, acc[e + 3]);
+  for (int dt = 0; dt < NDT; ++dt) dq[dt] = zero16();
+  load_chunk(j_lo);
+  store_chunk(0);
+  __syncthreads();
+  for (int j = j_lo; j < j_hi; ++j) {
+    const int buf = (j - j_lo) & 1;
+    if (j + 1 < j_hi) load_chunk(j + 1);
+    const float dl = (qi < a.N && j < qi) ? pair_weight(a, bh, qi, j) : 0.f;
+    f32x16 sc[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      sc[rt] = zero16();
+      if (rt * 32 < a.n_rep) {
+        const T* arow = &sR[buf][(rt * 32 + c32) * PR];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const auto af = MM::load_plain(arow, ks, hh);
+          sc[rt] = MM::mma(af, bhi[ks], sc[rt]);
+          if constexpr (BF) sc[rt] = MM::mma(af, blo[ks], sc[rt]);
+        }
+      }
+    }
+    column_softmax(sc, a.n_rep, hh, scale, dl * scale);
+    // dqbar += Z R_j: A = Z (lane = query; slot k = accumulator row), B = R_j in that k order
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      if (rt * 32 >= a.n_rep) break;
+#pragma unroll
+      for (int kk = 0; kk < NZK; ++kk) {
+        typename MM::Frag zh, zl;
+        if constexpr (BF) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) split_bf16(sc[rt][kk * 8 + e], zh, zl, e);
+        } else {
+          zh = sc[rt][kk];
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          typename MM::Frag rb;
+          if constexpr (BF)
+            rb = MM::load_clayout(&sRT[buf][(dt * 32 + c32) * PRT + rt * 32], kk, hh);
+          else
+            rb = sR[buf][(rt * 32 + Mma<float>::clayout_k(kk, hh)) * PR + dt * 32 + c32];
+          dq[dt] = MM::mma(zh, rb, dq[dt]);
+          if constexpr (BF) dq[dt] = MM::mma(zl, rb, dq[dt]);
+        }
+      }
+    }
+    if (j + 1 < j_hi) store_chunk(buf ^ 1);  // buf ^ 1 was last read before the previous barrier
+    __syncthreads();
+  }
+  // this segment's part of dqbar for the wave's 32 query chunks (rows = queries)
+  float* pdq = a.part + ((int64_t)js * a.B * a.H + bh) * a.N * DK;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int q = (qg * 4 + w) * 32 + acc_row(e, hh);
+      if (q < a.N) pdq[(int64_t)q * DK + dt * 32 + c32] = dq[dt][e];
+    }
+}
+
+// dqbar_i = the sum of the parts of the segments that start below i, in segment order.
+template <int DK>
+__global__ __launch_bounds__(256) void router_dq_sum_kernel(RouterBwdArgs a) {
+  const int64_t nq = a.B * a.H * a.N * DK;
+  const int64_t id = blockIdx.x * (int64_t)256 + threadIdx.x;
+  if (id >= nq) return;
+  const int seg = router_bwd_seg(a.B * a.H, a.N);
+  const int i = (int)((id / DK) % a.N);
+  const int nseg = (i + seg - 1) / seg;
+  float s = 0.f;
+  for (int g = 0; g < nseg; ++g) s += a.part[g * nq + id];
+  a.dqbar[id] = s;
+}
+
+// Representative side.  Wave w of workgroup (b, h, g) owns history chunk j = 4 g + w; the
+// workgroup walks the tiles of 32 query chunks that hold an i > 4 g, staging each tile's
+// means in LDS in both orientations.  Rows of the last chunk (no query reads it) are zero.
+template <class T, int DK>
+__global__ __launch_bounds__(256) void router_dr_kernel(RouterBwdArgs a) {
+  using MM = Mma<T>;
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int PQ = DK + 16 / (int)sizeof(T), PQT = 32 + 16 / (int)sizeof(T), PZ = 32 + 4;
+  constexpr int NKS = DK / MM::KS, NDT = DK / 32, NQK = 32 / MM::KS;
+  __shared__ __attribute__((aligned(16))) T sQh[32 * PQ];
+  __shared__ __attribute__((aligned(16))) T sQl[BF ? 32 * PQ : 1];
+  __shared__ __attribute__((aligned(16))) T sQTh[DK * PQT];
+  __shared__ __attribute__((aligned(16))) T sQTl[BF ? DK * PQT : 1];
+  __shared__ __attribute__((aligned(16))) float sZ[4][kRT * PZ];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, c32 = lane & 31;
+  const int ng = (a.N + 3) / 4;
+  const int64_t bh = blockIdx.x / ng, h = bh % a.H, b = bh / a.H;
+  const int g = (int)(blockIdx.x % ng);
+  const int j = g * 4 + w;
+  const bool hist = j < a.N - 1;  // some query chunk i > j reads chunk j
+  const int nrt = (a.n_rep + 31) / 32;
+  const float scale = 1.f / sqrtf((float)DK);
+  const T* reps = reinterpret_cast<const T*>(a.reps);
+  auto rep_row = [&](int rt) -> const T* {  // this lane's representative row of tile rt, or null
+    const int r = rt * 32 + c32;
+    return (hist && r < a.n_rep) ? reps + ((b * a.ld_R + (int64_t)j * a.n_rep + r) * a.H + h) * DK : nullptr;
+  };
+  // A operand of the scores on the bf16 path: the chunk's rows, kept in registers
+  typename MM::Frag ra[2][BF ? NKS : 1];
+  if constexpr (BF) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const T* row = rep_row(rt);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (row) {
+          ra[rt][ks] = MM::load_plain(row, ks, hh);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ra[rt][ks][e] = (bf16)0.f;
         }
       }
     }
   }
-  if (i < a.N) {
-    float* out = a.dqbar + (bh * a.N + i) * DK;
+  f32x16 dr[2][NDT];
 #pragma unroll
-    for (int e = 0; e < DK; ++e) {
-      const float v = wave_sum_valu(acc[e]);
-      if (lane == (e & 63)) out[e] = v;
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) dr[rt][dt] = zero16();
+  const int nqt = (a.N + 31) / 32;
+  for (int t = (g * 4 + 1) / 32; t < nqt; ++t) {
+    __syncthreads();  // the previous tile's reads of sQ*, sZ are done
+    for (int x = tid; x < 32 * DK; x += 256) {
+      const int r = x / DK, d = x % DK, i = t * 32 + r;
+      const float v = i < a.N ? a.qbar[(bh * a.N + i) * DK + d] : 0.f;
+      if constexpr (BF) {
+        const bf16 vh = (bf16)v, vl = (bf16)(v - (float)vh);
+        sQh[r * PQ + d] = vh;
+        sQl[r * PQ + d] = vl;
+        sQTh[d * PQT + r] = vh;
+        sQTl[d * PQT + r] = vl;
+      } else {
+        sQh[r * PQ + d] = v;
+        sQTh[d * PQT + r] = v;
+      }
+    }
+    __syncthreads();
+    const int qi = t * 32 + c32;
+    const float dl = (hist && qi < a.N && qi > j) ? pair_weight(a, bh, qi, j) : 0.f;
+    f32x16 sc[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      sc[rt] = zero16();
+      if (rt >= nrt) continue;
+      const T* row = rep_row(rt);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        typename MM::Frag af;
+        if constexpr (BF)
+          af = ra[rt][ks];
+        else
+          af = row ? MM::load_plain(row, ks, hh) : 0.f;
+        sc[rt] = MM::mma(af, MM::load_plain(&sQh[c32 * PQ], ks, hh), sc[rt]);
+        if constexpr (BF) sc[rt] = MM::mma(af, MM::load_plain(&sQl[c32 * PQ], ks, hh), sc[rt]);
+      }
+    }
+    column_softmax(sc, a.n_rep, hh, scale, dl * scale);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      if (rt >= nrt) break;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sZ[w][(rt * 32 + acc_row(e, hh)) * PZ + c32] = sc[rt][e];
+    }
+    __syncthreads();
+    // dR_j += Z Qbar: A = Z (lane = representative, k = query), B = Qbar (k = query, lane = feature)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      if (rt >= nrt) break;
+      const float* zrow = &sZ[w][(rt * 32 + c32) * PZ];
+#pragma unroll
+      for (int ks = 0; ks < NQK; ++ks) {
+        typename MM::Frag zh, zl;
+        if constexpr (BF) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) split_bf16(zrow[ks * 16 + hh * 8 + e], zh, zl, e);
+        } else {
+          zh = zrow[ks * 2 + hh];
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const auto qh = MM::load_plain(&sQTh[(dt * 32 + c32) * PQT], ks, hh);
+          dr[rt][dt] = MM::mma(zh, qh, dr[rt][dt]);
+          if constexpr (BF) {
+            dr[rt][dt] = MM::mma(zh, MM::load_plain(&sQTl[(dt * 32 + c32) * PQT], ks, hh), dr[rt][dt]);
+            dr[rt][dt] = MM::mma(zl, qh, dr[rt][dt]);
+          }
+        }
+      }
     }
   }
-}
-
-// Representative side: the gradient of every representative row of chunk j (zero for the
-// last chunk, which no query chunk reads).  Lane r keeps row r's gradient; the query means
-// (from router_dq_kernel) are wave-uniform loads, so a pair needs no barrier.
-template <class T, int DK>
-__global__ __launch_bounds__(64) void router_dk_kernel(RouterBwdArgs a) {
-  constexpr int C = kChunk, PK = DK + 4;
-  __shared__ __attribute__((aligned(16))) float s_key[C * PK];
-  const int lane = threadIdx.x;
-  const int64_t bh = blockIdx.x / a.N;
-  const int j = (int)(blockIdx.x % a.N);
-  const int64_t h = bh % a.H, b = bh / a.H;
-  const int64_t r0 = (int64_t)j * a.n_rep;  // first row of chunk j
-  const int nj = (int)((a.R_out - r0) < a.n_rep ? (a.R_out - r0) : a.n_rep);  // its rows below R_out
-  const T* k = reinterpret_cast<const T*>(a.reps);
-  const float rs = 1.f / sqrtf((float)DK);
-  const bool read = j + 1 < a.N;  // a history chunk: all n_rep rows exist
-  for (int idx = lane; idx < C * DK; idx += 64) {
-    const int r = idx / DK, e = idx % DK;
-    s_key[r * PK + e] = (read && r < a.n_rep) ? to_f<T>(k[((b * a.ld_R + r0 + r) * a.H + h) * DK + e]) : 0.f;
-  }
-  __syncthreads();
-  const float* kr = s_key + lane * PK;
-  float acc[DK];
+  if (j >= a.N) return;
 #pragma unroll
-  for (int e = 0; e < DK; ++e) acc[e] = 0.f;
-  for (int i = j + 1; i < a.N; ++i) {
-    const int64_t o = (bh * a.N + i) * (int64_t)a.N + j;
-    const float g = a.gates[o], dl = a.dgates[o] * g * (1.f - g);
-    if (dl == 0.f) continue;  // uniform over the wave
-    const float* qb = a.qbar + (bh * a.N + i) * DK;
-    const float sc = lane < a.n_rep ? dot_rows<DK>(qb, kr) * rs : -INFINITY;
-    const float mx = wave_max_valu(sc);
-    const float p = __expf(sc - mx);
-    const float cr = dl * (p / wave_sum_valu(p)) * rs;
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int e = 0; e < DK; ++e) acc[e] = fmaf(cr, qb[e], acc[e]);
-  }
-  if (lane < nj) {
-    float* out = a.dreps + ((b * a.R_out + r0 + lane) * a.H + h) * DK;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int e = 0; e < DK; ++e) out[e] = acc[e];
-  }
+      for (int e = 0; e < 16; ++e) {
+        const int r = rt * 32 + acc_row(e, hh);
+        const int64_t row = (int64_t)j * a.n_rep + r;
+        if (r < a.n_rep && row < a.R_out)
+          a.dreps[((b * a.R_out + row) * a.H + h) * DK + dt * 32 + c32] = dr[rt][dt][e];
+      }
 }
 
 // dqbar of each token's chunk over the chunk's token count, per token.
@@ -199,11 +396,15 @@ __global__ __launch_bounds__(256) void router_spread_kernel(RouterBwdArgs a) {
 
 template <class T, int DK>
 static hipError_t launch_router_bwd_t(const RouterBwdArgs& a, hipStream_t s) {
-  const int64_t BH = a.B * a.H;
-  const unsigned nq = (unsigned)(BH * ((a.N + kRouterQG - 1) / kRouterQG)), nk = (unsigned)(BH * a.N);
+  const int64_t BH = a.B * a.H, nq = BH * a.N * DK;
+  const int seg = router_bwd_seg(BH, a.N);
+  const int64_t nqg = ((a.N + 31) / 32 + 3) / 4, njs = (a.N + seg - 1) / seg, ng = (a.N + 3) / 4;
+  const unsigned gq = (unsigned)((nq + 255) / 256);
   TimedLaunch tl(HLA_KERNEL_BWD_ROUTER, s);
-  hipLaunchKernelGGL((router_dq_kernel<T, DK>), dim3(nq), dim3(64 * kRouterQG), 0, s, a);
-  hipLaunchKernelGGL((router_dk_kernel<T, DK>), dim3(nk), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((router_qbar_kernel<T, DK>), dim3(gq), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((router_dq_kernel<T, DK>), dim3((unsigned)(BH * nqg * njs)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((router_dr_kernel<T, DK>), dim3((unsigned)(BH * ng)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((router_dq_sum_kernel<DK>), dim3(gq), dim3(256), 0, s, a);
   if (a.dq_tok) {
     const int64_t total = a.B * a.T * a.H * DK;
     hipLaunchKernelGGL((router_spread_kernel<DK>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);

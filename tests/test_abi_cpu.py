@@ -453,7 +453,16 @@ def test_gdn2_prefill_backward_validation(lib):
 
 def test_reps_and_router_backward_workspace_sizes(lib):
     d = dims(B=2, T=130, H=3, dk=128, dv=64, dtype=1)  # 3 tiles of 64 tokens, N = 3
-    assert hla.workspace_bytes(hla.FN_ROUTER_BACKWARD, d) == 2 * _r(2 * 3 * 3 * 128 * 4)
+    # the router: query means and their gradients, then one part of the gradients per segment
+    # of history chunks (about 1024 workgroups over b, h, 128-chunk query groups, segments;
+    # 4 to 32 chunks a segment)
+    for B, T, H in ((2, 130, 3), (1, 8192, 16), (1, 32768, 16), (2, 700 * 64, 4)):
+        dd = dims(B=B, T=T, H=H, dk=128, dv=64, dtype=1)
+        N = -(-T // 64)
+        nqg = -(-(-(-N // 32)) // 4)
+        seg = min(32, max(4, -(-(N * B * H * nqg) // 1024)))
+        means = _r(B * H * N * 128 * 4)
+        assert hla.workspace_bytes(hla.FN_ROUTER_BACKWARD, dd) == 2 * means + _r(-(-N // seg) * B * H * N * 128 * 4)
     # the pooler: dWq, dWk, dWv per workgroup of 8 tiles (one group at 3 tiles, 2 at 9), then
     # four vectors per window, sized for windows of 8 (8 per tile), then dWp and dWr per chunk
     # of 256 windows of a (b, h)
