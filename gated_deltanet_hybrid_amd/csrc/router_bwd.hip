@@ -91,9 +91,15 @@ __global__ __launch_bounds__(256) void router_qbar_kernel(RouterBwdArgs a) {
   const int64_t bh = bhi / a.N, h = bh % a.H, b = bh / a.H;
   const int64_t t0 = (int64_t)i * kChunk;
   const int ni = (int)((a.T - t0) < kChunk ? (a.T - t0) : kChunk);
-  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* q = reinterpret_cast<const T*>(a.q) + ((b * a.ld_T + t0) * a.H + h) * DK + e;
+  // all 64 loads issued together (rows past the chunk's end re-read its last row and count
+  // zero), summed in token order
+  float v[kChunk];
+#pragma unroll
+  for (int t = 0; t < kChunk; ++t) v[t] = to_f<T>(q[(int64_t)(t < ni ? t : ni - 1) * a.H * DK]);
   float s = 0.f;
-  for (int t = 0; t < ni; ++t) s += to_f<T>(q[((b * a.ld_T + t0 + t) * a.H + h) * DK + e]);
+#pragma unroll
+  for (int t = 0; t < kChunk; ++t) s += t < ni ? v[t] : 0.f;
   a.qbar[id] = s / (float)ni;
 }
 
@@ -169,53 +175,98 @@ __global__ __launch_bounds__(256) void router_dq_kernel(RouterBwdArgs a) {
   f32x16 dq[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) dq[dt] = zero16();
+  // dl of this lane's pair with history chunk j (zero unless j < qi < N); every load in bounds
+  auto weight = [&](int j) {
+    const float v = pair_weight(a, bh, qi < a.N ? qi : a.N - 1, j);
+    return (qi < a.N && j < qi) ? v : 0.f;
+  };
+  // One history chunk: scores, softmax, dqbar += Z R_j.  TWO: a second tile of 32
+  // representatives (n_rep > 32).  Fragments are loaded in blocks ahead of their products,
+  // and the high and low parts of the query means feed separate accumulators, so that
+  // independent products are in flight while the LDS loads return.
+  auto round = [&](int buf, float dl, auto TWO) {
+    constexpr bool two = decltype(TWO)::value;
+    constexpr int KB = BF ? NKS : 16;
+    f32x16 sc[2], sl[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) sc[rt] = sl[rt] = zero16();
+    const T* r0 = &sR[buf][c32 * PR];
+    const T* r1 = &sR[buf][(32 + c32) * PR];
+#pragma unroll
+    for (int k0 = 0; k0 < NKS; k0 += KB) {
+      typename MM::Frag a0[KB], a1[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        a0[u] = MM::load_plain(r0, k0 + u, hh);
+        if constexpr (two) a1[u] = MM::load_plain(r1, k0 + u, hh);
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        sc[0] = MM::mma(a0[u], bhi[k0 + u], sc[0]);
+        if constexpr (two) sc[1] = MM::mma(a1[u], bhi[k0 + u], sc[1]);
+        if constexpr (BF) {
+          sl[0] = MM::mma(a0[u], blo[k0 + u], sl[0]);
+          if constexpr (two) sl[1] = MM::mma(a1[u], blo[k0 + u], sl[1]);
+        }
+      }
+    }
+    if constexpr (BF) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[rt][e] += sl[rt][e];
+    }
+    column_softmax(sc, a.n_rep, hh, scale, dl * scale);
+    // dqbar += Z R_j: A = Z (lane = query; slot k = accumulator row), B = R_j in that k order
+    constexpr int KK = BF ? NZK : 4;
+#pragma unroll
+    for (int rt = 0; rt < (two ? 2 : 1); ++rt) {
+#pragma unroll
+      for (int k0 = 0; k0 < NZK; k0 += KK) {
+        typename MM::Frag rb[KK][NDT];
+#pragma unroll
+        for (int u = 0; u < KK; ++u)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            if constexpr (BF)
+              rb[u][dt] = MM::load_clayout(&sRT[buf][(dt * 32 + c32) * PRT + rt * 32], k0 + u, hh);
+            else
+              rb[u][dt] = sR[buf][(rt * 32 + Mma<float>::clayout_k(k0 + u, hh)) * PR + dt * 32 + c32];
+          }
+#pragma unroll
+        for (int u = 0; u < KK; ++u) {
+          typename MM::Frag zh, zl;
+          if constexpr (BF) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) split_bf16(sc[rt][(k0 + u) * 8 + e], zh, zl, e);
+          } else {
+            zh = sc[rt][k0 + u];
+          }
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) dq[dt] = MM::mma(zh, rb[u][dt], dq[dt]);
+          if constexpr (BF) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) dq[dt] = MM::mma(zl, rb[u][dt], dq[dt]);
+          }
+        }
+      }
+    }
+  };
   load_chunk(j_lo);
+  float dl_next = weight(j_lo);
   store_chunk(0);
   __syncthreads();
   for (int j = j_lo; j < j_hi; ++j) {
     const int buf = (j - j_lo) & 1;
-    if (j + 1 < j_hi) load_chunk(j + 1);
-    const float dl = (qi < a.N && j < qi) ? pair_weight(a, bh, qi, j) : 0.f;
-    f32x16 sc[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      sc[rt] = zero16();
-      if (rt * 32 < a.n_rep) {
-        const T* arow = &sR[buf][(rt * 32 + c32) * PR];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const auto af = MM::load_plain(arow, ks, hh);
-          sc[rt] = MM::mma(af, bhi[ks], sc[rt]);
-          if constexpr (BF) sc[rt] = MM::mma(af, blo[ks], sc[rt]);
-        }
-      }
+    const float dl = dl_next;
+    if (j + 1 < j_hi) {  // chunk j + 1 and its weights: in flight during this round
+      load_chunk(j + 1);
+      dl_next = weight(j + 1);
     }
-    column_softmax(sc, a.n_rep, hh, scale, dl * scale);
-    // dqbar += Z R_j: A = Z (lane = query; slot k = accumulator row), B = R_j in that k order
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      if (rt * 32 >= a.n_rep) break;
-#pragma unroll
-      for (int kk = 0; kk < NZK; ++kk) {
-        typename MM::Frag zh, zl;
-        if constexpr (BF) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) split_bf16(sc[rt][kk * 8 + e], zh, zl, e);
-        } else {
-          zh = sc[rt][kk];
-        }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          typename MM::Frag rb;
-          if constexpr (BF)
-            rb = MM::load_clayout(&sRT[buf][(dt * 32 + c32) * PRT + rt * 32], kk, hh);
-          else
-            rb = sR[buf][(rt * 32 + Mma<float>::clayout_k(kk, hh)) * PR + dt * 32 + c32];
-          dq[dt] = MM::mma(zh, rb, dq[dt]);
-          if constexpr (BF) dq[dt] = MM::mma(zl, rb, dq[dt]);
-        }
-      }
-    }
+    if (a.n_rep > 32)
+      round(buf, dl, std::true_type{});
+    else
+      round(buf, dl, std::false_type{});
     if (j + 1 < j_hi) store_chunk(buf ^ 1);  // buf ^ 1 was last read before the previous barrier
     __syncthreads();
   }
@@ -258,6 +309,7 @@ __global__ __launch_bounds__(256) void router_dr_kernel(RouterBwdArgs a) {
   __shared__ __attribute__((aligned(16))) T sQTh[DK * PQT];
   __shared__ __attribute__((aligned(16))) T sQTl[BF ? DK * PQT : 1];
   __shared__ __attribute__((aligned(16))) float sZ[4][kRT * PZ];
+  __shared__ __attribute__((aligned(16))) T sRw[4][BF ? kRT * (DK + 8) : 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, c32 = lane & 31;
   const int ng = (a.N + 3) / 4;
   const int64_t bh = blockIdx.x / ng, h = bh % a.H, b = bh / a.H;
@@ -271,21 +323,16 @@ __global__ __launch_bounds__(256) void router_dr_kernel(RouterBwdArgs a) {
     const int r = rt * 32 + c32;
     return (hist && r < a.n_rep) ? reps + ((b * a.ld_R + (int64_t)j * a.n_rep + r) * a.H + h) * DK : nullptr;
   };
-  // A operand of the scores on the bf16 path: the chunk's rows, kept in registers
-  typename MM::Frag ra[2][BF ? NKS : 1];
+  // A operand of the scores on the bf16 path: the wave's own chunk rows, staged in LDS once
+  // (zero past n_rep, and for a chunk no query reads)
+  constexpr int UPR = DK / 8, PR = DK + 8;
   if constexpr (BF) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const T* row = rep_row(rt);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if (row) {
-          ra[rt][ks] = MM::load_plain(row, ks, hh);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ra[rt][ks][e] = (bf16)0.f;
-        }
-      }
+    for (int u = lane; u < kRT * UPR; u += 64) {
+      const int r = u / UPR, cu = u % UPR;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (hist && r < a.n_rep)
+        v = *reinterpret_cast<const uint4*>(reps + ((b * a.ld_R + (int64_t)j * a.n_rep + r) * a.H + h) * DK + cu * 8);
+      *reinterpret_cast<uint4*>(&sRw[w][r * PR + cu * 8]) = v;
     }
   }
   f32x16 dr[2][NDT];
@@ -293,12 +340,114 @@ __global__ __launch_bounds__(256) void router_dr_kernel(RouterBwdArgs a) {
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) dr[rt][dt] = zero16();
-  const int nqt = (a.N + 31) / 32;
-  for (int t = (g * 4 + 1) / 32; t < nqt; ++t) {
+  // the next tile's query means (one slice per thread) and this lane's pair weight, loaded
+  // a tile ahead; every load in bounds
+  constexpr int NQV = 32 * DK / 256;
+  const int nqt = (a.N + 31) / 32, jc = j < a.N - 1 ? j : a.N - 1;
+  float qv[NQV], dl_next = 0.f;
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int m = 0; m < NQV; ++m) {
+      const int x = tid + 256 * m, r = x / DK, d = x % DK, i = t * 32 + r;
+      const float v = a.qbar[(bh * a.N + (i < a.N ? i : a.N - 1)) * DK + d];
+      qv[m] = i < a.N ? v : 0.f;
+    }
+    const int qi = t * 32 + c32;
+    const float v = pair_weight(a, bh, qi < a.N ? qi : a.N - 1, jc);
+    dl_next = (hist && qi < a.N && qi > j) ? v : 0.f;
+  };
+  // One tile: scores, softmax, Z^T to LDS, dR_j += Z Qbar (TWO: n_rep > 32).  As in the
+  // query-side pass, fragments are loaded in blocks ahead of their products and the two
+  // parts of the means feed separate accumulators.
+  auto tile = [&](float dl, auto TWO) {
+    constexpr bool two = decltype(TWO)::value;
+    constexpr int KB = BF ? 4 : 16;
+    f32x16 sc[2], sl[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) sc[rt] = sl[rt] = zero16();
+    const T* row0 = rep_row(0);
+    const T* row1 = rep_row(1);
+#pragma unroll
+    for (int k0 = 0; k0 < NKS; k0 += KB) {
+      typename MM::Frag qh[KB], ql[KB];
+      typename MM::Frag ra0[BF ? KB : 1], ra1[BF ? KB : 1];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        qh[u] = MM::load_plain(&sQh[c32 * PQ], k0 + u, hh);
+        if constexpr (BF) {
+          ql[u] = MM::load_plain(&sQl[c32 * PQ], k0 + u, hh);
+          ra0[u] = MM::load_plain(&sRw[w][c32 * PR], k0 + u, hh);
+          if constexpr (two) ra1[u] = MM::load_plain(&sRw[w][(32 + c32) * PR], k0 + u, hh);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        typename MM::Frag a0, a1;
+        if constexpr (BF) {
+          a0 = ra0[u];
+          if constexpr (two) a1 = ra1[u];
+        } else {
+          a0 = row0 ? MM::load_plain(row0, k0 + u, hh) : 0.f;
+          if constexpr (two) a1 = row1 ? MM::load_plain(row1, k0 + u, hh) : 0.f;
+        }
+        sc[0] = MM::mma(a0, qh[u], sc[0]);
+        if constexpr (two) sc[1] = MM::mma(a1, qh[u], sc[1]);
+        if constexpr (BF) {
+          sl[0] = MM::mma(a0, ql[u], sl[0]);
+          if constexpr (two) sl[1] = MM::mma(a1, ql[u], sl[1]);
+        }
+      }
+    }
+    if constexpr (BF) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[rt][e] += sl[rt][e];
+    }
+    column_softmax(sc, a.n_rep, hh, scale, dl * scale);
+#pragma unroll
+    for (int rt = 0; rt < (two ? 2 : 1); ++rt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sZ[w][(rt * 32 + acc_row(e, hh)) * PZ + c32] = sc[rt][e];
+    __syncthreads();
+    // dR_j += Z Qbar: A = Z (lane = representative, k = query), B = Qbar (k = query, lane = feature)
+#pragma unroll
+    for (int ks = 0; ks < NQK; ++ks) {
+      typename MM::Frag bh_[NDT], bl_[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        bh_[dt] = MM::load_plain(&sQTh[(dt * 32 + c32) * PQT], ks, hh);
+        if constexpr (BF) bl_[dt] = MM::load_plain(&sQTl[(dt * 32 + c32) * PQT], ks, hh);
+      }
+#pragma unroll
+      for (int rt = 0; rt < (two ? 2 : 1); ++rt) {
+        const float* zrow = &sZ[w][(rt * 32 + c32) * PZ];
+        typename MM::Frag zh, zl;
+        if constexpr (BF) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) split_bf16(zrow[ks * 16 + hh * 8 + e], zh, zl, e);
+        } else {
+          zh = zrow[ks * 2 + hh];
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) dr[rt][dt] = MM::mma(zh, bh_[dt], dr[rt][dt]);
+        if constexpr (BF) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) dr[rt][dt] = MM::mma(zh, bl_[dt], dr[rt][dt]);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) dr[rt][dt] = MM::mma(zl, bh_[dt], dr[rt][dt]);
+        }
+      }
+    }
+  };
+  const int t_lo = (g * 4 + 1) / 32;
+  if (t_lo < nqt) load_tile(t_lo);
+  for (int t = t_lo; t < nqt; ++t) {
     __syncthreads();  // the previous tile's reads of sQ*, sZ are done
-    for (int x = tid; x < 32 * DK; x += 256) {
-      const int r = x / DK, d = x % DK, i = t * 32 + r;
-      const float v = i < a.N ? a.qbar[(bh * a.N + i) * DK + d] : 0.f;
+#pragma unroll
+    for (int m = 0; m < NQV; ++m) {
+      const int x = tid + 256 * m, r = x / DK, d = x % DK;
+      const float v = qv[m];
       if constexpr (BF) {
         const bf16 vh = (bf16)v, vl = (bf16)(v - (float)vh);
         sQh[r * PQ + d] = vh;
@@ -310,59 +459,13 @@ __global__ __launch_bounds__(256) void router_dr_kernel(RouterBwdArgs a) {
         sQTh[d * PQT + r] = v;
       }
     }
+    const float dl = dl_next;
+    if (t + 1 < nqt) load_tile(t + 1);  // in flight during this tile
     __syncthreads();
-    const int qi = t * 32 + c32;
-    const float dl = (hist && qi < a.N && qi > j) ? pair_weight(a, bh, qi, j) : 0.f;
-    f32x16 sc[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      sc[rt] = zero16();
-      if (rt >= nrt) continue;
-      const T* row = rep_row(rt);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        typename MM::Frag af;
-        if constexpr (BF)
-          af = ra[rt][ks];
-        else
-          af = row ? MM::load_plain(row, ks, hh) : 0.f;
-        sc[rt] = MM::mma(af, MM::load_plain(&sQh[c32 * PQ], ks, hh), sc[rt]);
-        if constexpr (BF) sc[rt] = MM::mma(af, MM::load_plain(&sQl[c32 * PQ], ks, hh), sc[rt]);
-      }
-    }
-    column_softmax(sc, a.n_rep, hh, scale, dl * scale);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      if (rt >= nrt) break;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sZ[w][(rt * 32 + acc_row(e, hh)) * PZ + c32] = sc[rt][e];
-    }
-    __syncthreads();
-    // dR_j += Z Qbar: A = Z (lane = representative, k = query), B = Qbar (k = query, lane = feature)
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      if (rt >= nrt) break;
-      const float* zrow = &sZ[w][(rt * 32 + c32) * PZ];
-#pragma unroll
-      for (int ks = 0; ks < NQK; ++ks) {
-        typename MM::Frag zh, zl;
-        if constexpr (BF) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) split_bf16(zrow[ks * 16 + hh * 8 + e], zh, zl, e);
-        } else {
-          zh = zrow[ks * 2 + hh];
-        }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const auto qh = MM::load_plain(&sQTh[(dt * 32 + c32) * PQT], ks, hh);
-          dr[rt][dt] = MM::mma(zh, qh, dr[rt][dt]);
-          if constexpr (BF) {
-            dr[rt][dt] = MM::mma(zh, MM::load_plain(&sQTl[(dt * 32 + c32) * PQT], ks, hh), dr[rt][dt]);
-            dr[rt][dt] = MM::mma(zl, qh, dr[rt][dt]);
-          }
-        }
-      }
-    }
+    if (nrt > 1)
+      tile(dl, std::true_type{});
+    else
+      tile(dl, std::false_type{});
   }
   if (j >= a.N) return;
 #pragma unroll
