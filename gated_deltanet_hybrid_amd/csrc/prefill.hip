@@ -51,8 +51,10 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
 
   __shared__ __attribute__((aligned(16))) bf16 KT[DK * PT];
   __shared__ __attribute__((aligned(16))) bf16 VT[DV * PT];
-  __shared__ __attribute__((aligned(16))) float Lb[C * PX];
-  __shared__ __attribute__((aligned(16))) float Xb[C * PX];
+  // L and X, and before them (phase A) the row-major staging copies of K and V
+  __shared__ __attribute__((aligned(16))) float LX[2 * C * PX];
+  float* const Lb = LX;
+  float* const Xb = LX + C * PX;
   __shared__ __attribute__((aligned(16))) float s_beta[C], s_g2[C], s_bg[C];
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, c32 = lane & 31;
@@ -68,20 +70,53 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
   const bf16* vg = reinterpret_cast<const bf16*>(a.v);
   char* rec = static_cast<char*>(a.rec) + id * ut_record_bytes(DK, DV);
 
-  // ---- A. keys and values transposed into LDS; the K K^T operands of waves 0-2 into
-  // registers; per-token decays (wave 0)
+  // ---- A. keys and values: rows loaded whole (a wave reads 4 tokens' rows, 8 cache lines
+  // per instruction, instead of one 16-byte column unit of 64 tokens), staged row-major in
+  // the space of L and X, then turned into the [d][t] images KT and VT inside LDS; the K K^T
+  // operands of waves 0-5 from the staged rows; per-token decays (wave 0)
+  constexpr int RK = DK + 8, RV = DV + 8;  // bf16 pitch of the staged rows
+  static_assert(C * (RK + RV) * 2 <= 2 * C * PX * 4, "staging fits in L and X");
+  bf16* const Ks = reinterpret_cast<bf16*>(LX);
+  bf16* const Vs = Ks + C * RK;
+  // K K^T lower tiles (0,0), (1,0), (1,1) on waves 0-2 and, when outputs are wanted, the
+  // same tiles of Q K^T on waves 3-5: both operands are rows (8 consecutive dk per lane); the
+  // Q rows of waves 3-5 come from global memory with the other loads, the K rows later from
+  // the staged copy (zero past the end)
+  const bool want_p = a.q != nullptr;
+  const int job = w < 3 ? w : w - 3;
+  const int tm = job == 0 ? 0 : 1, tn = job == 2 ? 1 : 0;
+  bf16x8 fa[DK / 16], fb[DK / 16];
+  if (want_p && w >= 3 && w < 6) {
+    const int ta = tm * 32 + c32;
+    const bf16* pa = reinterpret_cast<const bf16*>(a.q) + (row0 + (ta < n ? ta : n - 1) * a.H) * DK + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < DK / 16; ++ks) fa[ks] = *reinterpret_cast<const bf16x8*>(pa + ks * 16);
+  }
+  // the Q fragments of the record (outputs only): fragment min(w + 8 j, NQ - 1) of each
+  // wave, loaded here with the other operands and stored in phase C (rows past the end of
+  // a partial piece read its last row: never used)
+  constexpr int NQ = 2 * (DK / 16), NQW = (NQ + 7) / 8;
+  bf16x8 qf[NQW];
+  if (want_p) {
+#pragma unroll
+    for (int j = 0; j < NQW; ++j) {
+      const int fq = min(w + 8 * j, NQ - 1), tt = fq / (DK / 16), ks = fq % (DK / 16);
+      const int t = tt * 32 + c32;
+      qf[j] = Mma<bf16>::load_clayout(reinterpret_cast<const bf16*>(a.q) + (row0 + (t < n ? t : n - 1) * a.H) * DK, ks, hh);
+    }
+  }
   {
     // every load first (rows past the end of a partial piece read its last row, in bounds),
-    // then the zero padding where the values are used, so no load waits for another
+    // then the zero padding where the values are stored, so no load waits for another
     uint4 rk[KPT], rv[VPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int i = tid + NT * j, t = i & (C - 1), u = i / C;
+      const int i = tid + NT * j, t = i / (DK / 8), u = i % (DK / 8);
       rk[j] = *reinterpret_cast<const uint4*>(kg + (row0 + (t < n ? t : n - 1) * a.H) * DK + u * 8);
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int i = tid + NT * j, t = i & (C - 1), u = i / C;
+      const int i = tid + NT * j, t = i / (DV / 8), u = i % (DV / 8);
       rv[j] = *reinterpret_cast<const uint4*>(vg + (row0 + (t < n ? t : n - 1) * a.H) * DV + u * 8);
     }
     float bt = 0.f, ra = 1.f;
@@ -92,19 +127,13 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int i = tid + NT * j, t = i & (C - 1), u = i / C;
-      const uint4 kv = t < n ? rk[j] : make_uint4(0u, 0u, 0u, 0u);
-      const bf16* e8 = reinterpret_cast<const bf16*>(&kv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) KT[(u * 8 + e) * PT + t] = e8[e];
+      const int i = tid + NT * j, t = i / (DK / 8), u = i % (DK / 8);
+      *reinterpret_cast<uint4*>(Ks + t * RK + u * 8) = t < n ? rk[j] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int i = tid + NT * j, t = i & (C - 1), u = i / C;
-      const uint4 vv = t < n ? rv[j] : make_uint4(0u, 0u, 0u, 0u);
-      const bf16* e8 = reinterpret_cast<const bf16*>(&vv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) VT[(u * 8 + e) * PT + t] = e8[e];
+      const int i = tid + NT * j, t = i / (DV / 8), u = i % (DV / 8);
+      *reinterpret_cast<uint4*>(Vs + t * RV + u * 8) = t < n ? rv[j] : make_uint4(0u, 0u, 0u, 0u);
     }
     if (tid < C) {
       float x = 0.f;
@@ -127,36 +156,35 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
       gd[C + tid] = expf(x_end - x);
     }
   }
-  // K K^T lower tiles (0,0), (1,0), (1,1) on waves 0-2 and, when outputs are wanted, the
-  // same tiles of Q K^T on waves 3-5: both operands are rows (8 consecutive dk per lane)
-  // straight from global memory
-  const bool want_p = a.q != nullptr;
-  const int job = w < 3 ? w : w - 3;
-  const int tm = job == 0 ? 0 : 1, tn = job == 2 ? 1 : 0;
-  bf16x8 fa[DK / 16], fb[DK / 16];
-  if (w < 3 || (want_p && w < 6)) {
-    const int ta = tm * 32 + c32, tb = tn * 32 + c32;
-    const bf16* ag = w < 3 ? kg : reinterpret_cast<const bf16*>(a.q);
-    const bf16* pa = ag + (row0 + (ta < n ? ta : n - 1) * a.H) * DK + hh * 8;
-    const bf16* pb = kg + (row0 + (tb < n ? tb : n - 1) * a.H) * DK + hh * 8;
+  __syncthreads();
+  // the [d][t] images: unit (channel d, tokens 8 g .. 8 g + 7), lanes along d, so that the
+  // eight 2-byte reads of a unit are consecutive across the wave
 #pragma unroll
-    for (int ks = 0; ks < DK / 16; ++ks) {
-      fa[ks] = *reinterpret_cast<const bf16x8*>(pa + ks * 16);
-      fb[ks] = *reinterpret_cast<const bf16x8*>(pb + ks * 16);
-    }
+  for (int j = 0; j < KPT; ++j) {
+    const int i = tid + NT * j, d = i % DK, g = i / DK;
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = Ks[(g * 8 + e) * RK + d];
+    *reinterpret_cast<bf16x8*>(KT + d * PT + g * 8) = x;
   }
-  // the Q fragments of the record (outputs only): fragment min(w + 8 j, NQ - 1) of each
-  // wave, loaded here with the other operands and stored in phase C (rows past the end of
-  // a partial piece read its last row: never used)
-  constexpr int NQ = 2 * (DK / 16), NQW = (NQ + 7) / 8;
-  bf16x8 qf[NQW];
-  if (want_p) {
 #pragma unroll
-    for (int j = 0; j < NQW; ++j) {
-      const int fq = min(w + 8 * j, NQ - 1), tt = fq / (DK / 16), ks = fq % (DK / 16);
-      const int t = tt * 32 + c32;
-      qf[j] = Mma<bf16>::load_clayout(reinterpret_cast<const bf16*>(a.q) + (row0 + (t < n ? t : n - 1) * a.H) * DK, ks, hh);
+  for (int j = 0; j < VPT; ++j) {
+    const int i = tid + NT * j, d = i % DV, g = i / DV;
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = Vs[(g * 8 + e) * RV + d];
+    *reinterpret_cast<bf16x8*>(VT + d * PT + g * 8) = x;
+  }
+  // the K operands of the K K^T (waves 0-2) and Q K^T (waves 3-5) tiles from the staged rows
+  if (w < 3 || (want_p && w < 6)) {
+    const bf16* pb = Ks + (tn * 32 + c32) * RK + hh * 8;
+    if (w < 3) {
+      const bf16* pa = Ks + (tm * 32 + c32) * RK + hh * 8;
+#pragma unroll
+      for (int ks = 0; ks < DK / 16; ++ks) fa[ks] = *reinterpret_cast<const bf16x8*>(pa + ks * 16);
     }
+#pragma unroll
+    for (int ks = 0; ks < DK / 16; ++ks) fb[ks] = *reinterpret_cast<const bf16x8*>(pb + ks * 16);
   }
   __syncthreads();
 
@@ -617,43 +645,41 @@ __global__ __launch_bounds__(256, 1) void state_kernel(UtArgs a) {
     for (int ks = 0; ks < NKS; ++ks) bM[ks] = Mma<bf16>::from_acc(M[ks >> 1], ks, 1.f);
   };
 
-  // helpers: blocks m = hlp, hlp + NH, ... of a piece's part, all loaded unconditionally
-  // (blocks past the record's part repeat the decays into spare slots, so no load waits
-  // behind a branch)
+  // Helper waves (NH > 0): blocks m = hlp, hlp + NH, ... of a piece's part, all loaded
+  // unconditionally (blocks past the record's part repeat the decays into spare slots, so no
+  // load waits behind a branch).  A piece's blocks are loaded into registers two pieces
+  // ahead and written into LDS one piece ahead, so each load has a whole piece step to
+  // arrive before its LDS write waits for it.
   constexpr int NDH = NH > 0 ? (NB_REAL + NH - 1) / NH : 1;
   static_assert(NH == 0 || NDH * NH <= NB, "helper slots within the buffer");
   const int hlp = w - NWB;
 
   // Per piece c: the stores of piece c - 1's outputs are issued, then piece c is computed
-  // from its buffer with the copy of piece c + NBUF - 1 (ND operations per wave) issued
-  // along the way; then the
-  // wave waits for its memory operations up to the copy of piece c + 1 -- with two buffers
-  // all of them, with three all but the ND just issued (the counter retires operations in
-  // issue order) -- and a barrier makes that true for all waves before piece c + 1 reads
-  // its buffer or a copy overwrites the buffer piece c read.
+  // from its buffer; the copy of piece c + 1 into the other buffer is either spread over the
+  // products by the computing waves (no helpers: global_load_lds, issued NBUF - 1 pieces
+  // ahead) or made by the helpers.  Then every wave waits for its LDS operations (and,
+  // without helpers, for its copies up to piece c + 1: with two buffers all of them, with
+  // three all but the ND just issued, since the counter retires operations in issue order),
+  // and a barrier makes that true for all waves before piece c + 1 reads its buffer or a
+  // copy overwrites the buffer piece c read.  With helpers the computing waves issue no
+  // loads and the helpers' loads of piece c + 2 stay in flight across the barrier.
   static_assert(ND < 64, "vmcnt range");
-  auto step = [&](int c, const char* cur, char* ahead) __attribute__((always_inline)) {
-    const bool ahead_issued = c + NBUF - 1 < N;
-    if (w < NWB) {
-      if constexpr (WANT_O) {
-        if (c > 0) store_o(c - 1);
-      }
-      piece(cur, c + NBUF - 1, ahead);
-    } else if (ahead_issued) {
-      // helper: piece c + 1's blocks through registers into LDS
-      uint4 hreg[NDH];
-      const char* src = recs + (int64_t)(c + 1) * RS + lane * 16;
-#pragma unroll
-      for (int i = 0; i < NDH; ++i) hreg[i] = *reinterpret_cast<const uint4*>(src + src_block(hlp + i * NH));
-#pragma unroll
-      for (int i = 0; i < NDH; ++i) *reinterpret_cast<uint4*>(ahead + (hlp + i * NH) * 1024 + lane * 16) = hreg[i];
-    }
-    // (a plain s_barrier: __syncthreads' release fence would also wait for the copies
+  auto barrier_after = [&](int c) __attribute__((always_inline)) {
+    // (a plain s_barrier: __syncthreads' release fence would also wait for the loads
     // issued ahead)
-    if (NBUF == 3 && ahead_issued)
+    if constexpr (NH > 0)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (NBUF == 3 && c + NBUF - 1 < N)
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(ND) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  auto step = [&](int c, const char* cur, char* ahead) __attribute__((always_inline)) {
+    if constexpr (WANT_O) {
+      if (c > 0) store_o(c - 1);
+    }
+    piece(cur, c + NBUF - 1, ahead);
+    barrier_after(c);
   };
   if (N > 0) {
     issue(0, buf0);  // (every wave, global_load_lds)
@@ -662,6 +688,33 @@ __global__ __launch_bounds__(256, 1) void state_kernel(UtArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
+  if constexpr (NH > 0) {
+    if (w >= NWB) {
+      // (a vector type, not uint4: the loop-carried array must stay in registers)
+      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+      u32x4 hreg[NDH];
+      if (N > 1) {
+        const char* src = recs + RS + lane * 16;
+#pragma unroll
+        for (int i = 0; i < NDH; ++i) hreg[i] = *reinterpret_cast<const u32x4*>(src + src_block(hlp + i * NH));
+      }
+      for (int c = 0; c < N; ++c) {
+        char* ahead = (c & 1) ? buf0 : buf1;
+        if (c + 1 < N) {
+#pragma unroll
+          for (int i = 0; i < NDH; ++i) *reinterpret_cast<u32x4*>(ahead + (hlp + i * NH) * 1024 + lane * 16) = hreg[i];
+        }
+        if (c + 2 < N) {
+          const char* src = recs + (int64_t)(c + 2) * RS + lane * 16;
+#pragma unroll
+          for (int i = 0; i < NDH; ++i) hreg[i] = *reinterpret_cast<const u32x4*>(src + src_block(hlp + i * NH));
+        }
+        barrier_after(c);
+      }
+      return;
+    }
+  }
+  static_assert(NH == 0 || NBUF == 2, "helpers fill two buffers");
   if constexpr (NBUF == 3) {
     for (int c = 0; c < N; c += 3) {
       step(c, buf0, buf2);
