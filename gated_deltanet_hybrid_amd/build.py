@@ -31,7 +31,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.
 # Per-source device flags.  prefill.hip keeps the next piece's operands in small register
 # arrays while the current piece computes; LLVM would otherwise move such arrays into LDS
 # when LDS is free, which turns every prefetch load into a load, a wait and an LDS store.
-SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "-disable-promote-alloca-to-lds"]}
+# Its state pass also scales and converts the MFMA accumulators (the state, E and O^T) with
+# vector instructions every piece: with the accumulators in ordinary VGPRs (they fit, 239
+# registers at one wave per SIMD) those need no accumulator-register moves (about 256 per
+# piece otherwise).
+SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "-disable-promote-alloca-to-lds", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
