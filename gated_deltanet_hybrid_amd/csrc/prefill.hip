@@ -70,54 +70,49 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
   const bf16* vg = reinterpret_cast<const bf16*>(a.v);
   char* rec = static_cast<char*>(a.rec) + id * ut_record_bytes(DK, DV);
 
-  // ---- A. keys and values: rows loaded whole (a wave reads 4 tokens' rows, 8 cache lines
-  // per instruction, instead of one 16-byte column unit of 64 tokens), staged row-major in
-  // the space of L and X, then turned into the [d][t] images KT and VT inside LDS; the K K^T
-  // operands of waves 0-5 from the staged rows; per-token decays (wave 0)
+  // ---- A. keys, values and queries: rows loaded whole (a wave reads 4 tokens' rows, 8
+  // cache lines per instruction, instead of one 16-byte column unit of 64 tokens), staged
+  // row-major in LDS (K and V in the space of L and X, Q in that of K^T), then K and V turned
+  // into the [d][t] images KT and VT inside LDS; the K K^T and Q K^T operands and the
+  // record's Q fragments from the staged rows; per-token decays (wave 0)
   constexpr int RK = DK + 8, RV = DV + 8;  // bf16 pitch of the staged rows
   static_assert(C * (RK + RV) * 2 <= 2 * C * PX * 4, "staging fits in L and X");
   bf16* const Ks = reinterpret_cast<bf16*>(LX);
   bf16* const Vs = Ks + C * RK;
   // K K^T lower tiles (0,0), (1,0), (1,1) on waves 0-2 and, when outputs are wanted, the
-  // same tiles of Q K^T on waves 3-5: both operands are rows (8 consecutive dk per lane); the
-  // Q rows of waves 3-5 come from global memory with the other loads, the K rows later from
-  // the staged copy (zero past the end)
+  // same tiles of Q K^T on waves 3-5: both operands are rows (8 consecutive dk per lane),
+  // read from the staged copies (K zero past the end)
   const bool want_p = a.q != nullptr;
   const int job = w < 3 ? w : w - 3;
   const int tm = job == 0 ? 0 : 1, tn = job == 2 ? 1 : 0;
   bf16x8 fa[DK / 16], fb[DK / 16];
-  if (want_p && w >= 3 && w < 6) {
-    const int ta = tm * 32 + c32;
-    const bf16* pa = reinterpret_cast<const bf16*>(a.q) + (row0 + (ta < n ? ta : n - 1) * a.H) * DK + hh * 8;
-#pragma unroll
-    for (int ks = 0; ks < DK / 16; ++ks) fa[ks] = *reinterpret_cast<const bf16x8*>(pa + ks * 16);
-  }
-  // the Q fragments of the record (outputs only): fragment min(w + 8 j, NQ - 1) of each
-  // wave, loaded here with the other operands and stored in phase C (rows past the end of
-  // a partial piece read its last row: never used)
   constexpr int NQ = 2 * (DK / 16), NQW = (NQ + 7) / 8;
-  bf16x8 qf[NQW];
-  if (want_p) {
-#pragma unroll
-    for (int j = 0; j < NQW; ++j) {
-      const int fq = min(w + 8 * j, NQ - 1), tt = fq / (DK / 16), ks = fq % (DK / 16);
-      const int t = tt * 32 + c32;
-      qf[j] = Mma<bf16>::load_clayout(reinterpret_cast<const bf16*>(a.q) + (row0 + (t < n ? t : n - 1) * a.H) * DK, ks, hh);
-    }
-  }
+  // Q rows (outputs only) are staged row-major in the space of the K^T image, which is
+  // free until K is transposed at the end of phase A
+  static_assert(C * RK <= DK * PT, "Q staging fits in K^T");
+  bf16* const Qs = KT;
   {
     // every load first (rows past the end of a partial piece read its last row, in bounds),
     // then the zero padding where the values are stored, so no load waits for another
-    uint4 rk[KPT], rv[VPT];
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // (not uint4: kept in registers)
+    u32x4 rk[KPT], rv[VPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int i = tid + NT * j, t = i / (DK / 8), u = i % (DK / 8);
-      rk[j] = *reinterpret_cast<const uint4*>(kg + (row0 + (t < n ? t : n - 1) * a.H) * DK + u * 8);
+      rk[j] = *reinterpret_cast<const u32x4*>(kg + (row0 + (t < n ? t : n - 1) * a.H) * DK + u * 8);
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int i = tid + NT * j, t = i / (DV / 8), u = i % (DV / 8);
-      rv[j] = *reinterpret_cast<const uint4*>(vg + (row0 + (t < n ? t : n - 1) * a.H) * DV + u * 8);
+      rv[j] = *reinterpret_cast<const u32x4*>(vg + (row0 + (t < n ? t : n - 1) * a.H) * DV + u * 8);
+    }
+    u32x4 rq[KPT];
+    if (want_p) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int i = tid + NT * j, t = i / (DK / 8), u = i % (DK / 8);
+        rq[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(a.q) + (row0 + (t < n ? t : n - 1) * a.H) * DK + u * 8);
+      }
     }
     float bt = 0.f, ra = 1.f;
     if (tid < C) {
@@ -128,12 +123,20 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int i = tid + NT * j, t = i / (DK / 8), u = i % (DK / 8);
-      *reinterpret_cast<uint4*>(Ks + t * RK + u * 8) = t < n ? rk[j] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<u32x4*>(Ks + t * RK + u * 8) = t < n ? rk[j] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int i = tid + NT * j, t = i / (DV / 8), u = i % (DV / 8);
-      *reinterpret_cast<uint4*>(Vs + t * RV + u * 8) = t < n ? rv[j] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<u32x4*>(Vs + t * RV + u * 8) = t < n ? rv[j] : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (want_p) {
+      // (rows past the end hold the last row: their results are never used)
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int i = tid + NT * j, t = i / (DK / 8), u = i % (DK / 8);
+        *reinterpret_cast<u32x4*>(Qs + t * RK + u * 8) = rq[j];
+      }
     }
     if (tid < C) {
       float x = 0.f;
@@ -158,15 +161,8 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
   }
   __syncthreads();
   // the [d][t] images: unit (channel d, tokens 8 g .. 8 g + 7), lanes along d, so that the
-  // eight 2-byte reads of a unit are consecutive across the wave
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int i = tid + NT * j, d = i % DK, g = i / DK;
-    bf16x8 x;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = Ks[(g * 8 + e) * RK + d];
-    *reinterpret_cast<bf16x8*>(KT + d * PT + g * 8) = x;
-  }
+  // eight 2-byte reads of a unit are consecutive across the wave; V's first, and the Q
+  // operands read from their staging before K's image overwrites it
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int i = tid + NT * j, d = i % DV, g = i / DV;
@@ -174,6 +170,20 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = Vs[(g * 8 + e) * RV + d];
     *reinterpret_cast<bf16x8*>(VT + d * PT + g * 8) = x;
+  }
+  if (want_p) {
+    if (w >= 3 && w < 6) {
+      const bf16* pa = Qs + (tm * 32 + c32) * RK + hh * 8;
+#pragma unroll
+      for (int ks = 0; ks < DK / 16; ++ks) fa[ks] = *reinterpret_cast<const bf16x8*>(pa + ks * 16);
+    }
+    // the record's Q fragments, stored here (fragment min(w + 8 j, NQ - 1) of each wave)
+#pragma unroll
+    for (int j = 0; j < NQW; ++j) {
+      const int fq = min(w + 8 * j, NQ - 1), tt = fq / (DK / 16), ks = fq % (DK / 16);
+      reinterpret_cast<bf16x8*>(rec + ut_off_q(DK, DV))[fq * 64 + lane] =
+          Mma<bf16>::load_clayout(Qs + (tt * 32 + c32) * RK, ks, hh);
+    }
   }
   // the K operands of the K K^T (waves 0-2) and Q K^T (waves 3-5) tiles from the staged rows
   if (w < 3 || (want_p && w < 6)) {
@@ -185,6 +195,15 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
     }
 #pragma unroll
     for (int ks = 0; ks < DK / 16; ++ks) fb[ks] = *reinterpret_cast<const bf16x8*>(pb + ks * 16);
+  }
+  if (want_p) __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = tid + NT * j, d = i % DK, g = i / DK;
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = Ks[(g * 8 + e) * RK + d];
+    *reinterpret_cast<bf16x8*>(KT + d * PT + g * 8) = x;
   }
   __syncthreads();
 
@@ -244,13 +263,7 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
   __syncthreads();
 
   // ---- C. X = (I + L)^-1, blocked by 16: the diagonal blocks by substitution (wave 0);
-  // meanwhile waves 1-7 store the K^T fragments (from K^T in LDS; padded tokens are zero);
-  // every wave stores its Q fragments
-  if (want_p) {
-#pragma unroll
-    for (int j = 0; j < NQW; ++j)
-      reinterpret_cast<bf16x8*>(rec + ut_off_q(DK, DV))[min(w + 8 * j, NQ - 1) * 64 + lane] = qf[j];
-  }
+  // meanwhile waves 1-7 store the K^T fragments (from K^T in LDS; padded tokens are zero)
   if (w > 0) {
     constexpr int NKT = (DK / 32) * 4;
     for (int f = w - 1; f < NKT; f += 7) {
