@@ -24,6 +24,7 @@ CASES = [
     ("bf16", 128, 128, 200, "slow"),
     ("bf16", 64, 128, 130, "slow"),
     ("bf16", 128, 64, 70, "slow"),
+    ("bf16", 64, 64, 150, "config"),
 ]
 IDS = [f"{c[0]}-dk{c[1]}-dv{c[2]}-T{c[3]}-{c[4]}" for c in CASES]
 
