@@ -314,68 +314,71 @@ __global__ __launch_bounds__(512, 4) void ut_kernel(UtArgs a) {
   // ---- F. W^T tile (dk block db, token block tt) on wave 2 db + tt -> -W fragments (tt,
   // 2 db) and (tt, 2 db + 1);  U tile (token block tt, column block ct) on wave 2 ct + tt
   // -> the E accumulator order.  X enters as hi + lo bf16 parts (about 16 mantissa bits).
-  auto xfrag = [&](const float* xrow, const float* fac, int ks, bf16x8& hi, bf16x8& lo) {
-    const int s0 = ks * 16 + hh * 8;
-    float xv[8], fv[8];
-    *reinterpret_cast<float4*>(xv) = *reinterpret_cast<const float4*>(xrow + s0);
-    *reinterpret_cast<float4*>(xv + 4) = *reinterpret_cast<const float4*>(xrow + s0 + 4);
-    *reinterpret_cast<float4*>(fv) = *reinterpret_cast<const float4*>(fac + s0);
-    *reinterpret_cast<float4*>(fv + 4) = *reinterpret_cast<const float4*>(fac + s0 + 4);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = xv[e] * fv[e];
-      const bf16 hv = (bf16)x;
-      hi[e] = hv;
-      lo[e] = (bf16)(x - (float)hv);
-    }
-  };
-  if (w < 2 * NDT) {
-    // W^T = K^T diag(beta gamma) X^T: A = K^T rows (dk), B = X rows (token t), k = s
-    const int tt = w & 1, db = w >> 1;
+  // A wave's W tile and U tile share the token block tt, so X's rows are read once per
+  // k-step for both, and the two accumulator chains interleave on the matrix cores.
+  const bool do_w = w < 2 * NDT, do_u = w < 2 * NVT;
+  if (do_w || do_u) {
+    // W^T = K^T diag(beta gamma) X^T: A = K^T rows (dk block jb), B = X rows (token t), k = s;
+    // U = X diag(beta) V: A = X rows (token t), B = V^T rows (column block jb), k = s
+    const int tt = w & 1, jb = w >> 1;
     const float* xrow = Xb + (tt * 32 + c32) * PX;
-    const bf16* arow = KT + (db * 32 + c32) * PT;
-    f32x16 acc = zero16();
+    const bf16* arow = KT + (jb * 32 + c32) * PT;  // (read only by W's waves)
+    const bf16* brow = VT + (jb * 32 + c32) * PT;  // (read only by U's waves)
+    f32x16 acc_w = zero16(), acc_u = zero16();
 #pragma unroll
     for (int ks = 0; ks < C / 16; ++ks) {
-      bf16x8 hi, lo;
-      xfrag(xrow, s_bg, ks, hi, lo);
-      const bf16x8 af = Mma<bf16>::load_plain(arow, ks, hh);
-      acc = Mma<bf16>::mma(af, hi, acc);
-      acc = Mma<bf16>::mma(af, lo, acc);
-    }
-    bf16x8 lo8, hi8;
+      const int s0 = ks * 16 + hh * 8;
+      float xv[8], gv[8], bv[8];
+      *reinterpret_cast<float4*>(xv) = *reinterpret_cast<const float4*>(xrow + s0);
+      *reinterpret_cast<float4*>(xv + 4) = *reinterpret_cast<const float4*>(xrow + s0 + 4);
+      *reinterpret_cast<float4*>(gv) = *reinterpret_cast<const float4*>(s_bg + s0);
+      *reinterpret_cast<float4*>(gv + 4) = *reinterpret_cast<const float4*>(s_bg + s0 + 4);
+      *reinterpret_cast<float4*>(bv) = *reinterpret_cast<const float4*>(s_beta + s0);
+      *reinterpret_cast<float4*>(bv + 4) = *reinterpret_cast<const float4*>(s_beta + s0 + 4);
+      // X enters as hi + lo bf16 parts (about 16 mantissa bits)
+      bf16x8 hw, lw, hu, lu;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo8[e] = (bf16)(-acc[e]);
-      hi8[e] = (bf16)(-acc[e + 8]);
+      for (int e = 0; e < 8; ++e) {
+        const float x_w = xv[e] * gv[e], x_u = xv[e] * bv[e];
+        hw[e] = (bf16)x_w;
+        lw[e] = (bf16)(x_w - (float)hw[e]);
+        hu[e] = (bf16)x_u;
+        lu[e] = (bf16)(x_u - (float)hu[e]);
+      }
+      bf16x8 af, bf;
+      if (do_w) {
+        af = Mma<bf16>::load_plain(arow, ks, hh);
+        acc_w = Mma<bf16>::mma(af, hw, acc_w);
+      }
+      if (do_u) {
+        bf = Mma<bf16>::load_plain(brow, ks, hh);
+        acc_u = Mma<bf16>::mma(hu, bf, acc_u);
+      }
+      if (do_w) acc_w = Mma<bf16>::mma(af, lw, acc_w);
+      if (do_u) acc_u = Mma<bf16>::mma(lu, bf, acc_u);
     }
-    bf16x8* wo = reinterpret_cast<bf16x8*>(rec);
-    wo[(tt * (DK / 16) + 2 * db) * 64 + lane] = lo8;
-    wo[(tt * (DK / 16) + 2 * db + 1) * 64 + lane] = hi8;
-  }
-  if (w < 2 * NVT) {
-    // U = X diag(beta) V: A = X rows (token t), B = V^T rows (column), k = s
-    const int tt = w & 1, ct = w >> 1;
-    const bf16* brow = VT + (ct * 32 + c32) * PT;
-    const float* xrow = Xb + (tt * 32 + c32) * PX;
-    f32x16 acc = zero16();
+    if (do_w) {
+      bf16x8 lo8, hi8;
 #pragma unroll
-    for (int ks = 0; ks < C / 16; ++ks) {
-      bf16x8 hi, lo;
-      xfrag(xrow, s_beta, ks, hi, lo);
-      const bf16x8 bf = Mma<bf16>::load_plain(brow, ks, hh);
-      acc = Mma<bf16>::mma(hi, bf, acc);
-      acc = Mma<bf16>::mma(lo, bf, acc);
+      for (int e = 0; e < 8; ++e) {
+        lo8[e] = (bf16)(-acc_w[e]);
+        hi8[e] = (bf16)(-acc_w[e + 8]);
+      }
+      bf16x8* wo = reinterpret_cast<bf16x8*>(rec);
+      wo[(tt * (DK / 16) + 2 * jb) * 64 + lane] = lo8;
+      wo[(tt * (DK / 16) + 2 * jb + 1) * 64 + lane] = hi8;
     }
-    bf16x8 lo8, hi8;
+    if (do_u) {
+      bf16x8 lo8, hi8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo8[e] = (bf16)acc[e];
-      hi8[e] = (bf16)acc[e + 8];
+      for (int e = 0; e < 8; ++e) {
+        lo8[e] = (bf16)acc_u[e];
+        hi8[e] = (bf16)acc_u[e + 8];
+      }
+      bf16x8* uo = reinterpret_cast<bf16x8*>(rec + ut_off_u(DK)) + ((jb * 2 + tt) * 64 + lane) * 2;
+      uo[0] = lo8;
+      uo[1] = hi8;
     }
-    bf16x8* uo = reinterpret_cast<bf16x8*>(rec + ut_off_u(DK)) + ((ct * 2 + tt) * 64 + lane) * 2;
-    uo[0] = lo8;
-    uo[1] = hi8;
   }
 }
 
